@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the NVFP4 linear layer.
+
+This module draws random numbers and nothing else: it holds none of the
+layer's arithmetic (no amax, no scale rule, no quantize, no GEMM).  Both the
+HIP path and the CPU oracle consume what it returns.  Rounding of draws to
+bf16 and to E4M3 is done by torch's own dtype conversions.
+
+Recipe (numpy PCG64):
+  * activations: ``default_rng(seed)``; X drawn in float64, then the
+    workload's modifications (outliers, zero blocks, heavy tails), then the
+    MoE routing, in that order; X is cast to float32 and rounded to bf16
+    (round to nearest even) by torch.
+  * weights: tensor ``layer`` of expert ``e`` uses ``default_rng([seed,
+    1 + layer, e])``: packed E2M1 codes are uniform random bytes (two
+    independent uniform nibbles), block scales are uniform float64 draws in
+    [lo, hi] cast to float32 and rounded to E4M3 by torch, weight_scale_2 is
+    a float32 constant or a uniform draw.
+Weight layout: codes (N, K/2) uint8, scales (N, K/16) uint8 (E4M3 bits),
+row n = output feature n, packed along K.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+
+# ------------------------------------------------------------------ shapes
+# The five workloads: a tiny case, a decode projection, a prefill
+# projection, a routed-expert MoE pair of projections and a large-magnitude
+# prefill stress case.
+WORKLOADS = {
+    "tiny_m1_k256_n256": dict(kind="linear", M=1, K=256, N=256, seed=0, x="normal",
+                              sf=(0.5, 2.0), ws2=0.01),
+    "decode_m1_k7168_n1536": dict(kind="linear", M=1, K=7168, N=1536, seed=1,
+                                  x="outliers", sf=(0.25, 4.0), ws2=0.005),
+    "prefill_m512_k7168_n4096": dict(kind="linear", M=512, K=7168, N=4096, seed=2,
+                                     x="zero_blocks", sf=(0.25, 4.0), ws2=0.005),
+    "moe_t64_e256_top8": dict(kind="moe", tokens=64, experts=256, topk=8, K1=7168,
+                              N1=4096, K2=2048, N2=7168, granularity=8, seed=3,
+                              sf=(0.25, 4.0), ws2=(0.002, 0.01)),
+    "stress_m2048_k7168_n7168": dict(kind="linear", M=2048, K=7168, N=7168, seed=4,
+                                     x="student_t", sf=(0.125, 8.0), ws2=0.003),
+}
+
+
+def to_bf16_bits(x64: np.ndarray) -> np.ndarray:
+    """float64 -> float32 -> bf16 (RNE, torch) -> raw uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_e4m3_bits(v64: np.ndarray) -> np.ndarray:
+    """Positive float64 draws -> float32 -> E4M3 (torch RNE) -> uint8 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(v64, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+# ------------------------------------------------------------------ pieces
+def draw_activation(rng: np.random.Generator, M: int, K: int, kind: str) -> np.ndarray:
+    """float64 activations of the given kind (before bf16 rounding)."""
+    if kind == "student_t":
+        x = rng.standard_t(2.0, size=(M, K))
+        x *= 1000.0 / np.max(np.abs(x))
+        return x
+    x = rng.standard_normal((M, K))
+    if kind == "normal":
+        pass
+    elif kind == "outliers":
+        # round(0.1%) of all entries, without replacement, multiplied by 100
+        n_out = int(round(0.001 * M * K))
+        idx = rng.choice(M * K, n_out, replace=False)
+        x.reshape(-1)[idx] *= 100.0
+    elif kind == "zero_blocks":
+        # round(1%) of the 16-element blocks, without replacement, set to +0
+        nblk = M * (K // 16)
+        n_zero = int(round(0.01 * nblk))
+        idx = rng.choice(nblk, n_zero, replace=False)
+        x.reshape(-1, 16)[idx] = 0.0
+    else:
+        raise ValueError(kind)
+    return x
+
+
+def draw_weight(seed: int, layer: int, expert: int, N: int, K: int, sf_lo: float,
+                sf_hi: float, ws2=None):
+    """Packed codes (N, K/2), E4M3 scale bits (N, K/16) and a float32 ws2."""
+    rng = np.random.default_rng([seed, 1 + layer, expert])
+    codes = np.frombuffer(rng.bytes(N * (K // 2)), dtype=np.uint8).reshape(N, K // 2).copy()
+    scales = to_e4m3_bits(rng.uniform(sf_lo, sf_hi, size=(N, K // 16)))
+    if isinstance(ws2, tuple):
+        w2 = np.float32(rng.uniform(ws2[0], ws2[1]))
+    else:
+        w2 = np.float32(ws2)
+    return codes, scales, w2
+
+
+@dataclass
+class LinearInputs:
+    name: str
+    x: np.ndarray          # (M, K) bf16 bits, uint16
+    w_codes: np.ndarray    # (N, K/2) uint8
+    w_scales: np.ndarray   # (N, K/16) uint8
+    ws2: np.float32
+    M: int
+    K: int
+    N: int
+
+
+def make_linear(M: int, K: int, N: int, seed: int, x: str = "normal",
+                sf=(0.25, 4.0), ws2: float = 0.005, name: str = "custom") -> LinearInputs:
+    rng = np.random.default_rng(seed)
+    xb = to_bf16_bits(draw_activation(rng, M, K, x))
+    wc, wsc, w2 = draw_weight(seed, 0, 0, N, K, sf[0], sf[1], ws2)
+    return LinearInputs(name, xb, wc, wsc, w2, M, K, N)
+
+
+@dataclass
+class MoEInputs:
+    name: str
+    x: np.ndarray              # (T, K1) bf16 bits
+    pair_expert: np.ndarray    # (P,) int32, sorted by (expert, token)
+    pair_token: np.ndarray     # (P,) int32 = row_index for L1
+    offsets: np.ndarray        # (E+1,) int32
+    T: int
+    E: int
+    topk: int
+    K1: int
+    N1: int
+    K2: int
+    N2: int
+    granularity: int
+    seed: int
+    sf: tuple
+    ws2_range: tuple
+    _cache: dict = field(default_factory=dict, repr=False)
+
+    @property
+    def active_experts(self) -> np.ndarray:
+        return np.nonzero(np.diff(self.offsets) > 0)[0]
+
+    def weight(self, layer: int, e: int):
+        """(codes, scales, ws2) of expert e; layer 0 = L1 (gate/up), 1 = L2."""
+        key = (layer, e)
+        if key not in self._cache:
+            N, K = (self.N1, self.K1) if layer == 0 else (self.N2, self.K2)
+            self._cache[key] = draw_weight(self.seed, layer, e, N, K, self.sf[0],
+                                           self.sf[1], self.ws2_range)
+        return self._cache[key]
+
+    def drop_cache(self):
+        self._cache.clear()
+
+
+def make_moe(tokens=64, experts=256, topk=8, K1=7168, N1=4096, K2=2048, N2=7168,
+             granularity=8, seed=3, sf=(0.25, 4.0), ws2=(0.002, 0.01),
+             name="custom_moe") -> MoEInputs:
+    rng = np.random.default_rng(seed)
+    xb = to_bf16_bits(draw_activation(rng, tokens, K1, "normal"))
+    tok, exp_ = [], []
+    for t in range(tokens):
+        chosen = rng.choice(experts, topk, replace=False)
+        for e in chosen:
+            tok.append(t)
+            exp_.append(int(e))
+    tok = np.asarray(tok, np.int64)
+    exp_ = np.asarray(exp_, np.int64)
+    order = np.lexsort((tok, exp_))       # sort by expert, then token
+    pair_expert = exp_[order].astype(np.int32)
+    pair_token = tok[order].astype(np.int32)
+    counts = np.bincount(pair_expert, minlength=experts)
+    offsets = np.zeros(experts + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return MoEInputs(name, xb, pair_expert, pair_token, offsets, tokens, experts, topk,
+                     K1, N1, K2, N2, granularity, seed, tuple(sf), tuple(ws2))
+
+
+def make(name: str):
+    """Build the named workload at its full size."""
+    c = dict(WORKLOADS[name])
+    kind = c.pop("kind")
+    if kind == "linear":
+        return make_linear(c["M"], c["K"], c["N"], c["seed"], c["x"], c["sf"], c["ws2"],
+                           name=name)
+    return make_moe(c["tokens"], c["experts"], c["topk"], c["K1"], c["N1"], c["K2"],
+                    c["N2"], c["granularity"], c["seed"], c["sf"], c["ws2"], name=name)

@@ -1,0 +1,368 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself -- the tables and constants printed on the pages, torch's own FP8
+conversion, exact rational arithmetic, closed forms and invariants."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden
+from oracle import oracle, bruteforce
+from moe_amax_gsa_amd import workloads as W
+
+
+def consts():
+    return {k: float(v) for k, v in golden("gsa_constants.txt")}
+
+
+# ----------------------------------------------------------------- E2M1
+def test_e2m1_decode_matches_page_table():
+    table = {int(b, 2): float(v) for b, v in golden("e2m1_table.txt")}
+    for code in range(16):
+        mag = table[code & 7]
+        want = -mag if code & 8 else mag
+        got = oracle.e2m1_value(code)
+        assert got == want, (code, got, want)
+        assert math.copysign(1.0, got) == (-1.0 if code & 8 else 1.0)
+
+
+def test_e2m1_rejects_raw_integer_decode():
+    # The page's wrong decode: (nibble & 7) taken as an integer.
+    for code in range(1, 8):
+        assert oracle.e2m1_value(code) != float(code & 7)
+    assert oracle.e2m1_value(0b001) == 0.5 and oracle.e2m1_value(0b111) == 6.0
+
+
+def test_e2m1_nearest_grid_midpoints_and_saturation():
+    grid = [float(v) for _, v in golden("e2m1_table.txt")]
+    for i, g in enumerate(grid):
+        assert oracle.e2m1_nearest(g) == i
+    for i in range(7):
+        lo, hi = grid[i], grid[i + 1]
+        mid = np.float32((lo + hi) / 2)
+        even = i if i % 2 == 0 else i + 1  # tie goes to the even mantissa bit
+        assert oracle.e2m1_nearest(float(mid)) == even
+        assert oracle.e2m1_nearest(float(np.nextafter(mid, np.float32(0)))) == i
+        assert oracle.e2m1_nearest(float(np.nextafter(mid, np.float32(10)))) == i + 1
+    for q in [6.0, 6.5, 7.0, 100.0, 3.4e38]:
+        assert oracle.e2m1_nearest(q) == 7
+    qs = np.linspace(0, 8, 4001, dtype=np.float32)
+    idx = [oracle.e2m1_nearest(float(q)) for q in qs]
+    assert all(a <= b for a, b in zip(idx, idx[1:]))  # monotone
+
+
+# ----------------------------------------------------------------- E4M3
+def _torch_e4m3_value(b):
+    return torch.tensor([b], dtype=torch.uint8).view(torch.float8_e4m3fn).float().item()
+
+
+def test_e4m3_decode_all_patterns_match_torch():
+    for b in range(256):
+        got = oracle.e4m3_value(b)
+        want = _torch_e4m3_value(b)
+        if math.isnan(want):
+            assert math.isnan(got), b
+        else:
+            assert got == want, (b, got, want)
+    assert oracle.e4m3_value(0x7E) == consts()["e4m3_max"]
+
+
+def test_e4m3_encode_matches_torch_rne():
+    rng = np.random.default_rng(123)
+    finite = np.array([oracle.e4m3_value(c) for c in range(0x7F)], np.float64)
+    mids = (finite[:-1] + finite[1:]) / 2
+    vals = np.concatenate([
+        finite, mids, np.nextafter(mids.astype(np.float32), 0).astype(np.float64),
+        np.nextafter(mids.astype(np.float32), 1e9).astype(np.float64),
+        rng.uniform(0, 448, 3000), np.exp(rng.uniform(np.log(1e-6), np.log(448), 3000)),
+        [0.0, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11],
+    ]).astype(np.float32)
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(v)) for v in vals], np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(vals[i]), int(got[i]), int(want[i])) for i in bad[:5]]
+
+
+def test_e4m3_encode_saturates_instead_of_nan():
+    for v in [448.0, 449.0, 463.9, 464.0, 470.0, 1e4, 3.0e38]:
+        assert oracle.e4m3_encode(v) == 0x7E
+    assert oracle.e4m3_encode(2.0 ** -10) == 0  # tie between 0 and 2^-9 -> even
+
+
+# ----------------------------------------------------------------- gsa
+def test_amax_is_max_abs_and_gsa_closed_form():
+    c = consts()
+    rng = np.random.default_rng(5)
+    for dist in ["normal", "outliers", "student_t"]:
+        xb = W.to_bf16_bits(W.draw_activation(rng, 7, 96, dist))
+        xf = W.bf16_bits_to_f32(xb)
+        a = oracle.amax(xb)
+        assert a == np.max(np.abs(xf))
+        assert oracle.amax(np.ascontiguousarray(xf)) == a
+        g = oracle.amax_gsa(xb)
+        # page formula max|x| / (6 * 448), evaluated in double, stored in float32
+        assert g == np.float32(float(a) / (c["e2m1_max"] * c["e4m3_max"]))
+        assert c["e2m1_max"] * c["e4m3_max"] == c["gsa_divisor"]
+
+
+def test_gsa_zero_tensor_uses_floor():
+    c = consts()
+    z = np.zeros((3, 32), np.uint16)
+    assert oracle.amax(z) == 0.0
+    assert oracle.amax_gsa(z) == np.float32(float(np.float32(c["amax_floor"])) / c["gsa_divisor"])
+    neg0 = np.full((1, 16), 0x8000, np.uint16)  # -0.0
+    assert oracle.amax(neg0) == 0.0
+
+
+@pytest.mark.parametrize("dist", ["normal", "outliers", "student_t", "zero_blocks"])
+def test_amax_block_gets_max_scale(dist):
+    """Runtime gsa makes x/gsa <= 6*448: the block holding max|x| gets the
+    largest finite scale (448) and that element the largest code (6)."""
+    rng = np.random.default_rng(11)
+    xb = W.to_bf16_bits(W.draw_activation(rng, 9, 256, dist))
+    g = oracle.amax_gsa(xb)
+    codes, scales = oracle.quantize(xb, g)
+    xf = W.bf16_bits_to_f32(xb)
+    i = int(np.argmax(np.abs(xf)))
+    m, k = divmod(i, 256)
+    assert scales[m, k // 16] == 0x7E
+    code = (codes[m, k // 2] >> (4 * (k & 1))) & 0xF
+    assert code & 7 == 7
+    assert np.all(scales <= 0x7E)
+    assert float(np.max(np.abs(xf))) / float(g) <= 2688.0 * (1 + 2 ** -22)
+
+
+def test_too_small_gsa_saturates_scales():
+    """A gsa far below max|x|/2688 (the checkpoint-input_scale bug the pages
+    record) clamps every large block scale to 448: no NaN code appears."""
+    rng = np.random.default_rng(2)
+    xb = W.to_bf16_bits(W.draw_activation(rng, 4, 128, "normal") * 7956.0)
+    g = np.float32(0.000251)
+    codes, scales = oracle.quantize(xb, g)
+    assert np.all(scales <= 0x7E) and np.any(scales == 0x7E)
+    xhat = oracle.dequantize(codes, scales, g)
+    assert np.max(np.abs(xhat)) <= 6 * 448 * float(g) * (1 + 1e-12)
+
+
+# ----------------------------------------------------------------- quantize
+def _pack(codes_full):
+    return (codes_full[:, 0::2] | (codes_full[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _unpack(codes):
+    return bruteforce.unpack(codes)
+
+
+@pytest.mark.parametrize("log2_gsa", [-12, -3, 0])
+def test_exact_round_trip_of_representable_values(log2_gsa):
+    rng = np.random.default_rng(100 + log2_gsa)
+    M, K = 6, 128
+    nb = K // 16
+    sf = rng.integers(1, 0x7F, size=(M, nb)).astype(np.uint8)  # any nonzero finite scale
+    codes_full = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    # at least one magnitude-6 code per block so the block max maps to 6
+    pos = rng.integers(0, 16, size=(M, nb))
+    for m in range(M):
+        for b in range(nb):
+            codes_full[m, b * 16 + pos[m, b]] |= 0x7
+    gsa = np.float32(2.0 ** log2_gsa)
+    table = {int(b, 2): float(v) for b, v in golden("e2m1_table.txt")}
+    x = np.empty((M, K), np.float64)
+    for m in range(M):
+        for k in range(K):
+            c = codes_full[m, k]
+            v = table[c & 7] * _torch_e4m3_value(int(sf[m, k // 16])) * float(gsa)
+            x[m, k] = -v if c & 8 else v
+    xb = W.to_bf16_bits(x)
+    assert np.array_equal(W.bf16_bits_to_f32(xb).astype(np.float64), x)  # exact in bf16
+    xb[codes_full == 8] = 0x8000  # -0.0 keeps its sign bit
+    codes, scales = oracle.quantize(xb, gsa)
+    assert np.array_equal(scales, sf)
+    assert np.array_equal(codes, _pack(codes_full))
+
+
+def _check_nearest_and_bounds(xf, codes, scales, gsa):
+    M, K = xf.shape
+    cf = _unpack(codes)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    sdec = np.array([oracle.e4m3_value(int(b)) for b in range(256)])[scales]
+    s32 = (sdec.astype(np.float32) * np.float32(gsa)).astype(np.float32)
+    s_el = np.repeat(s32, 16, axis=1)
+    mag = cf & 7
+    sign = cf >> 3
+    assert np.array_equal(sign.astype(bool), np.signbit(xf))
+    nz = np.repeat(sdec, 16, axis=1) != 0
+    assert np.all(mag[~nz] == 0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = (np.abs(xf).astype(np.float32) / s_el).astype(np.float64)
+    d = np.abs(q[..., None] - grid[None, None, :])
+    best = d.min(axis=-1)
+    chosen = np.take_along_axis(d, mag[..., None].astype(np.int64), axis=-1)[..., 0]
+    assert np.all(chosen[nz] == best[nz])                  # nearest grid point
+    ties = (np.sum(d == best[..., None], axis=-1) > 1) & nz
+    assert np.all(mag[ties] % 2 == 0)                       # ties to even
+    # error bound: half a grid step inside [0, 6], |x| - 6s beyond
+    xhat = oracle.dequantize(codes, scales, gsa)
+    half = np.array([0.25, 0.25, 0.25, 0.25, 0.5, 0.5, 1.0, 1.0])[mag]
+    err = np.abs(xf.astype(np.float64) - xhat)
+    s64 = s_el.astype(np.float64)
+    lim = np.where(np.abs(xf) > 6 * s64, np.abs(xf) - 6 * s64, half * s64)
+    # slack: s is rounded to float32 here, the dequantized value uses it unrounded
+    assert np.all(err[nz] <= lim[nz] + 2.0 ** -20 * np.abs(xf[nz]))
+
+
+@pytest.mark.parametrize("dist", ["normal", "outliers", "zero_blocks", "student_t"])
+def test_quantize_nearest_code_and_error_bound(dist):
+    rng = np.random.default_rng(7)
+    xb = W.to_bf16_bits(W.draw_activation(rng, 16, 512, dist))
+    g = oracle.amax_gsa(xb)
+    codes, scales = oracle.quantize(xb, g)
+    _check_nearest_and_bounds(W.bf16_bits_to_f32(xb), codes, scales, g)
+
+
+def test_quantize_fp32_input_same_as_bf16():
+    rng = np.random.default_rng(8)
+    xb = W.to_bf16_bits(W.draw_activation(rng, 5, 64, "normal"))
+    xf = np.ascontiguousarray(W.bf16_bits_to_f32(xb))
+    g = oracle.amax_gsa(xb)
+    assert oracle.amax_gsa(xf) == g
+    c1, s1 = oracle.quantize(xb, g)
+    c2, s2 = oracle.quantize(xf, g)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_quantize_zero_tensor_and_signed_zero():
+    z = np.zeros((2, 32), np.uint16)
+    z[1, 3] = 0x8000
+    g = oracle.amax_gsa(z)
+    codes, scales = oracle.quantize(z, g)
+    assert np.all(scales == 0)
+    cf = _unpack(codes)
+    assert cf[1, 3] == 0x8 and np.sum(cf != 0) == 1
+
+
+def test_underflowing_block_scale_is_zero():
+    # one block of tiny values next to a block holding 1000: its scale rounds to 0
+    x = np.zeros((1, 32))
+    x[0, :16] = 1e-4 * np.linspace(-1, 1, 16)
+    x[0, 20] = 1000.0
+    xb = W.to_bf16_bits(x)
+    g = oracle.amax_gsa(xb)
+    codes, scales = oracle.quantize(xb, g)
+    assert scales[0, 0] == 0 and scales[0, 1] == 0x7E
+    cf = _unpack(codes)
+    assert np.all(cf[0, :16] & 7 == 0)
+    assert np.array_equal(cf[0, :16] >> 3, np.signbit(W.bf16_bits_to_f32(xb)[0, :16]).astype(int))
+
+
+def test_round_trip_cosine_on_normal_data():
+    """The pages report a quantize/dequantize cosine of about 0.995 on random
+    data; a N(0,1) tensor must land near it."""
+    rng = np.random.default_rng(9)
+    xb = W.to_bf16_bits(rng.standard_normal((64, 4096)))
+    g = oracle.amax_gsa(xb)
+    codes, scales = oracle.quantize(xb, g)
+    xf = W.bf16_bits_to_f32(xb).astype(np.float64).ravel()
+    xh = oracle.dequantize(codes, scales, g).ravel()
+    cos = xf @ xh / np.linalg.norm(xf) / np.linalg.norm(xh)
+    assert 0.990 <= cos <= 0.998, cos
+
+
+# ----------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("M,N,K,seed", [(1, 3, 16, 0), (2, 5, 32, 1), (4, 8, 64, 2),
+                                        (3, 2, 48, 3)])
+def test_linear_equals_exact_rational_bruteforce(M, N, K, seed):
+    inp = W.make_linear(M, K, N, seed, "normal", (0.125, 8.0), 0.0071)
+    g = oracle.amax_gsa(inp.x)
+    ac, asf = oracle.quantize(inp.x, g)
+    y = oracle.linear(ac, asf, g, inp.w_codes, inp.w_scales, inp.ws2)
+    ye = bruteforce.linear_exact(ac, asf, g, inp.w_codes, inp.w_scales, inp.ws2)
+    for m in range(M):
+        for n in range(N):
+            assert y[m, n] == float(ye[m][n]), (m, n, y[m, n], float(ye[m][n]))
+
+
+def test_linear_integer_special_case():
+    """All block scales 1.0 and gsa = ws2 = 1: every product lut*lut is a
+    multiple of 1/4, so y = (2a) @ (2w)^T / 4 exactly in integers."""
+    rng = np.random.default_rng(4)
+    M, N, K = 5, 7, 96
+    ac = rng.integers(0, 256, (M, K // 2)).astype(np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    ones_a = np.full((M, K // 16), 0x38, np.uint8)
+    ones_w = np.full((N, K // 16), 0x38, np.uint8)
+    assert _torch_e4m3_value(0x38) == 1.0
+    y = oracle.linear(ac, ones_a, 1.0, wc, ones_w, 1.0)
+    twice = np.array([0, 1, 2, 3, 4, 6, 8, 12], np.int64)
+    a2 = twice[_unpack(ac) & 7] * np.where(_unpack(ac) & 8, -1, 1)
+    w2 = twice[_unpack(wc) & 7] * np.where(_unpack(wc) & 8, -1, 1)
+    exact = (a2 @ w2.T).astype(np.float64) / 4.0
+    assert np.array_equal(y, exact)
+
+
+def test_linear_matches_numpy_matmul_of_dequantized():
+    inp = W.make_linear(6, 256, 40, 12, "outliers", (0.25, 4.0), 0.005)
+    g = oracle.amax_gsa(inp.x)
+    ac, asf = oracle.quantize(inp.x, g)
+    y = oracle.linear(ac, asf, g, inp.w_codes, inp.w_scales, inp.ws2)
+    A = oracle.dequantize(ac, asf, 1.0)
+    Wd = oracle.dequantize(inp.w_codes, inp.w_scales, 1.0)
+    ref = float(g) * float(inp.ws2) * (A @ Wd.T)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    ms = np.array([0, 5, 3]); ns = np.array([39, 0, 17])
+    assert np.array_equal(oracle.linear_at(ac, asf, g, inp.w_codes, inp.w_scales, inp.ws2,
+                                           ms, ns), y[ms, ns])
+
+
+def test_grouped_linear_equals_bruteforce_per_group():
+    moe = W.make_moe(tokens=5, experts=4, topk=2, K1=32, N1=6, K2=16, N2=3, granularity=1,
+                     seed=21)
+    g = oracle.amax_gsa(moe.x)
+    ac, asf = oracle.quantize(moe.x, g)
+    G = moe.E
+    wc = np.stack([moe.weight(0, e)[0] for e in range(G)])
+    wsf = np.stack([moe.weight(0, e)[1] for e in range(G)])
+    ws2 = np.array([moe.weight(0, e)[2] for e in range(G)], np.float32)
+    P = moe.offsets[-1]
+    y = oracle.grouped_linear(ac, asf, g, moe.pair_token, moe.offsets, wc, wsf, ws2, P)
+    assert P == 10 and not np.any(np.isnan(y))
+    for r in range(P):
+        e = moe.pair_expert[r]
+        t = moe.pair_token[r]
+        assert moe.offsets[e] <= r < moe.offsets[e + 1]
+        ye = bruteforce.linear_exact(ac[t:t + 1], asf[t:t + 1], g, wc[e], wsf[e], ws2[e])
+        assert np.array_equal(y[r], np.array([float(v) for v in ye[0]]))
+
+
+def test_moe_routing_is_sorted_and_complete():
+    moe = W.make_moe(tokens=64, experts=256, topk=8, K1=32, N1=16, K2=16, N2=16)
+    P = moe.T * moe.topk
+    assert moe.offsets[0] == 0 and moe.offsets[-1] == P
+    keys = moe.pair_expert.astype(np.int64) * 1000 + moe.pair_token
+    assert np.all(np.diff(keys) > 0)
+    for t in range(moe.T):
+        assert np.sum(moe.pair_token == t) == moe.topk
+
+
+# ----------------------------------------------------------------- SwiGLU
+def test_deinterleave_mapping_matches_fixture():
+    rows = [tuple(int(v) for v in r) for r in golden("deinterleave_g8_n32.txt")]
+    l1 = np.zeros((1, 32), np.float32)
+    for hcol, gcol, ucol in rows:
+        l1[:] = 0
+        l1[0, gcol] = 3.0
+        l1[0, ucol] = 2.0
+        h = oracle.swiglu_deinterleave(l1, 8)
+        want = 3.0 / (1 + math.exp(-3.0)) * 2.0
+        assert h[0, hcol] == pytest.approx(want, rel=1e-15)
+        assert np.sum(h != 0) == 1
+
+
+def test_swiglu_matches_torch_silu():
+    rng = np.random.default_rng(3)
+    l1 = (rng.standard_normal((4, 64)) * 4).astype(np.float32)
+    h = oracle.swiglu_deinterleave(l1, 8)
+    t = torch.from_numpy(l1.astype(np.float64)).reshape(4, 4, 2, 8)
+    ref = (torch.nn.functional.silu(t[:, :, 0]) * t[:, :, 1]).reshape(4, 32).numpy()
+    assert np.max(np.abs(h - ref)) <= 1e-14 * np.max(np.abs(ref))
