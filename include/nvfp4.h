@@ -1,0 +1,161 @@
+/*
+ * nvfp4.h -- C ABI of the NVFP4 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer runs in three steps on one GPU:
+ *   1. amax -> gsa:  gsa = max(max_i |x_i|, 1e-8) / (6 * 448)
+ *   2. quantize:     per 16-element block an E4M3 scale and 16 E2M1 codes
+ *   3. linear:       y = gsa * ws2 * sum_k (lut[a]*sfa) * (lut[w]*sfw)
+ *
+ * Sources (pages of the nvfp4-megamoe-kernel repository on sweetapi.com):
+ *   - commit 107d62d, single_shot_inference.py, commit message on computing
+ *     gsa at runtime: gsa = max|x| / (6.0 * 448.0) keeps x/gsa <= 2688;
+ *   - deleted PERFORMANCE_AUDIT.md, section "P0 -- Per-call .item() D2H
+ *     sync": amax is clamped from below at 1e-8 and must stay on the GPU;
+ *   - commit 107d62d, dsv4/ops/quantize.py, commit message: the amax is its
+ *     own kernel (a single-pass kernel that synchronised only within a block
+ *     raced across blocks), the quantize reads gsa from a device buffer;
+ *   - commit 0d1cd1e, dsv4/kernels/indexer, commit message: E2M1 code table
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6} with bias 1, sign in bit 3;
+ *   - commit db07d17, dsv4, commit messages: checkpoint weights are
+ *     (N, K/2) uint8 (byte-identical to float4_e2m1fn_x2) with (N, K/16)
+ *     E4M3 scales, and w = lut[w] * weight_scale * weight_scale_2;
+ *   - dsv4/_archive/layers/linear.py (finalize_weights, _run_impl) and
+ *     archived_plans/CORRECTNESS_BACKLOG.md section 7: the GEMM computes
+ *     (A*SFA) @ (B*SFB) and the epilogue multiplies by gsa * gsb with
+ *     gsb = weight_scale_2;
+ *   - dsv4/_archive/layers/grouped_linear.py, _run_impl: one gsa shared by
+ *     every group, one weight global scale per group;
+ *   - README.md, "MoE kernel (FusedSwiGLUScaledGroupedGemmKernel)": L1
+ *     gate/up weights interleaved at granularity 8, even subtiles gate, odd
+ *     subtiles up, SwiGLU between the two expert projections.
+ *
+ * Data layout (all row-major, all buffers in device memory unless noted):
+ *   x       (M, K) bf16 or fp32 activations; K % 16 == 0.
+ *   codes   (M, K/2) uint8; byte j of a row holds element 2j in bits 0..3
+ *           and element 2j+1 in bits 4..7; bit 3 of a code is its sign.
+ *   scales  (M, K/16) uint8, E4M3 (OCP FP8 E4M3FN) bit patterns.
+ *   gsa     one float32.
+ *   weights codes (N, K/2) and scales (N, K/16), row n = output feature n;
+ *           grouped weights are G such matrices stacked contiguously.
+ *   ws2     one float32 per weight matrix (weight_scale_2).
+ *   y       (M, N) float32 or bf16 (round to nearest even).
+ *
+ * Quantize rule for one 16-element block (binary32, correctly rounded):
+ *   sf = E4M3_rne_satfinite(bamax / (gsa * 6));  s = dec(sf) * gsa;
+ *   code = sign(x) | nearest_even_E2M1(|x| / s), magnitude 0 when sf == 0.
+ *
+ * Conventions:
+ *   - The caller owns every buffer.  No entry point allocates, frees,
+ *     synchronises or reads device memory on the host; all work is
+ *     enqueued on `stream` (a hipStream_t; NULL is the null stream), so
+ *     every call can be captured in a HIP graph.
+ *   - Return value: NVFP4_OK (0) or a negative status; on any status other
+ *     than NVFP4_ERR_LAUNCH nothing was enqueued.  nvfp4_status_string()
+ *     names a status.
+ *   - Stateless and reentrant; the workspace is scratch that the call may
+ *     overwrite (its size comes from nvfp4_workspace_bytes; no initial
+ *     contents are required).  Calls that share a workspace must be ordered
+ *     on one stream.
+ *   - Inputs must be finite.  A caller-supplied gsa must be positive and
+ *     finite.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_OK 0
+#define NVFP4_ERR_NULL (-1)      /* a required pointer is NULL            */
+#define NVFP4_ERR_SHAPE (-2)     /* a size is negative, zero where it may  */
+                                 /* not be, or K % 16 != 0                  */
+#define NVFP4_ERR_DTYPE (-3)     /* unknown dtype enum                     */
+#define NVFP4_ERR_WORKSPACE (-4) /* workspace NULL or smaller than needed  */
+#define NVFP4_ERR_ALIGN (-5)     /* a pointer is not aligned as required   */
+#define NVFP4_ERR_LAUNCH (-6)    /* the HIP runtime reported an error      */
+
+#define NVFP4_DTYPE_BF16 0
+#define NVFP4_DTYPE_FP32 1
+
+/* Operation ids for nvfp4_workspace_bytes. */
+#define NVFP4_OP_AMAX_GSA 0
+#define NVFP4_OP_QUANTIZE 1
+#define NVFP4_OP_LINEAR 2
+#define NVFP4_OP_GROUPED_LINEAR 3
+
+/* Bytes of workspace an operation needs for the given sizes (0 if none).
+ * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored. */
+size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
+
+/* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
+ * x: numel elements of x_dtype (16-byte aligned); gsa: device float32.
+ * A true grid reduction: the first kernel writes one partial maximum per
+ * workgroup into ws, a second single-workgroup kernel reduces the partials
+ * and writes gsa.  Inputs of at most 65536 elements are reduced by one
+ * workgroup in a single kernel.  numel == 0 gives gsa = 1e-8 / 2688. */
+int nvfp4_amax_gsa(const void *x, int x_dtype, int64_t numel, float *gsa, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* Step 2: quantize x (M, K) with the device gsa into codes (M, K/2) and
+ * scales (M, K/16).  x 16-byte aligned, codes 8-byte aligned.  M == 0 is a
+ * no-op.  gsa is read on the device; it need not come from step 1 (any
+ * positive finite value works, a too small one saturates the scales at 448). */
+int nvfp4_quantize_from_buffer(const void *x, int x_dtype, int64_t M, int64_t K,
+                               const float *gsa, uint8_t *codes, uint8_t *scales,
+                               void *stream);
+
+/* Step 3: y (M, N) = gsa * ws2 * dequant(A) @ dequant(W)^T, FP32 accumulation.
+ * A is codes (M, K/2) + scales (M, K/16) from step 2; W is codes (N, K/2) +
+ * scales (N, K/16); gsa and ws2 are device float32 scalars.  Code buffers
+ * 8-byte aligned.  M <= 16 runs a weight-streaming kernel on FP4 matrix
+ * cores; larger M runs a tiled kernel that dequantizes both operands
+ * exactly to f16 (every E2M1 x E4M3 product fits) and accumulates on f16
+ * matrix cores in FP32.  M == 0 or N == 0 is a no-op.  ws is unused (may be
+ * NULL). */
+int nvfp4_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa,
+                 const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
+                 void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* Grouped linear (MoE experts, or any set of G weight matrices sharing one
+ * activation gsa).  Output row r, 0 <= r < M_total, belongs to group g when
+ * group_offsets[g] <= r < group_offsets[g+1] (device int32[G+1],
+ * non-decreasing); its activation row is row_index[r] (device
+ * int32[M_total]) or r when row_index is NULL (then a_rows >= M_total).
+ * A has a_rows rows (codes (a_rows, K/2), scales (a_rows, K/16)).
+ * y[r] = gsa * ws2[g] * dequant(A[row]) @ dequant(W_g)^T with W_g = codes
+ * (N, K/2) at w_codes + g*N*K/2 and scales (N, K/16) at w_scales + g*N*K/16;
+ * ws2 is a device float32[G].  The group sizes are read on the device only.
+ * Rows of y outside every group, rows at or beyond M_total, and rows whose
+ * row_index lies outside [0, a_rows) are not written. */
+int nvfp4_grouped_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa,
+                         int64_t a_rows, const int32_t *row_index,
+                         const int32_t *group_offsets, int G, int64_t M_total,
+                         const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
+                         void *y, int y_dtype, int64_t N, int64_t K, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* SwiGLU between the two expert projections, unfused: l1 (M, N_inter) fp32
+ * holds gate/up column groups of `granularity` columns interleaved (group
+ * q = j / granularity is gate when q is even, up when odd, gate group 2p
+ * pairs with up group 2p+1); h (M, N_inter/2) fp32 receives
+ * h[m, p*granularity + i] = silu(gate) * up, silu(g) = g / (1 + exp(-g)).
+ * N_inter % (2*granularity) == 0. */
+int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_inter,
+                              int granularity, void *stream);
+
+/* Static name of a status code. */
+const char *nvfp4_status_string(int status);
+
+/* Library ABI version (increments on any signature change). */
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

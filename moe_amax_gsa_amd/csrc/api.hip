@@ -1,0 +1,145 @@
+// api.hip -- the C ABI declared in include/nvfp4.h: argument validation,
+// workspace sizing and dispatch to the gfx950 kernels.  Nothing here touches
+// device memory from the host; every launch goes to the caller's stream.
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+#include "launch.hpp"
+
+#define NVFP4_API extern "C" __attribute__((visibility("default")))
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t I32_MAX = 2147483647;
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline bool dtype_ok(int d) { return d == NVFP4_DTYPE_BF16 || d == NVFP4_DTYPE_FP32; }
+inline int launched(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
+
+size_t amax_ws_bytes(int64_t numel) {
+  if (numel <= AMAX_SMALL_NUMEL) return 0;
+  return (size_t)amax_parts_for(numel) * sizeof(uint32_t);
+}
+
+// Shape checks shared by the linear entry points.
+int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (M > I32_MAX || N > I32_MAX || K > I32_MAX) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+NVFP4_API int nvfp4_abi_version(void) { return 1; }
+
+NVFP4_API const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "unsupported shape (negative size, K <= 0 or K % 16 != 0, or too large)";
+    case NVFP4_ERR_DTYPE: return "unknown dtype";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_ALIGN: return "pointer not aligned as required";
+    case NVFP4_ERR_LAUNCH: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G) {
+  (void)N;
+  (void)K;
+  (void)G;
+  switch (op) {
+    case NVFP4_OP_AMAX_GSA: return M > 0 ? amax_ws_bytes(M) : 0;
+    default: return 0;
+  }
+}
+
+NVFP4_API int nvfp4_amax_gsa(const void* x, int x_dtype, int64_t numel, float* gsa, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype)) return NVFP4_ERR_DTYPE;
+  if (numel < 0) return NVFP4_ERR_SHAPE;
+  if (gsa == nullptr || (numel > 0 && x == nullptr)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(gsa, 4)) return NVFP4_ERR_ALIGN;
+  const size_t need = amax_ws_bytes(numel);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+  }
+  return launched(launch_amax_gsa(x, x_dtype == NVFP4_DTYPE_BF16, numel, gsa, ws,
+                                  (hipStream_t)stream));
+}
+
+NVFP4_API int nvfp4_quantize_from_buffer(const void* x, int x_dtype, int64_t M, int64_t K,
+                                         const float* gsa, uint8_t* codes, uint8_t* scales,
+                                         void* stream) {
+  if (!dtype_ok(x_dtype)) return NVFP4_ERR_DTYPE;
+  if (M < 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (M > 0 && (M * (K / 16) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (x == nullptr || gsa == nullptr || codes == nullptr || scales == nullptr)
+    return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gsa, 4)) return NVFP4_ERR_ALIGN;
+  return launched(launch_quantize(x, x_dtype == NVFP4_DTYPE_BF16, M, K, gsa, codes, scales,
+                                  (hipStream_t)stream));
+}
+
+NVFP4_API int nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                           void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* ws,
+                           size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  int st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !gsa || !w_codes || !w_scales || !ws2 || !y) return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 8) || !aligned(w_codes, 8) || !aligned(gsa, 4) || !aligned(ws2, 4) ||
+      !aligned(y, y_dtype == NVFP4_DTYPE_FP32 ? 4 : 2))
+    return NVFP4_ERR_ALIGN;
+  const bool ybf = y_dtype == NVFP4_DTYPE_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= GEMV_MAX_M)
+    return launched(launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s));
+  return launched(launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s));
+}
+
+NVFP4_API int nvfp4_grouped_linear(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const float* gsa, int64_t a_rows, const int32_t* row_index,
+                                   const int32_t* group_offsets, int G, int64_t M_total,
+                                   const uint8_t* w_codes, const uint8_t* w_scales,
+                                   const float* ws2, void* y, int y_dtype, int64_t N, int64_t K,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  int st = check_gemm_shape(M_total, N, K);
+  if (st != NVFP4_OK) return st;
+  if (G < 1 || G > 65535 || a_rows < 0 || a_rows > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (row_index == nullptr && a_rows < M_total) return NVFP4_ERR_SHAPE;
+  if (M_total == 0 || N == 0) return NVFP4_OK;
+  if (a_rows == 0) return NVFP4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !gsa || !group_offsets || !w_codes || !w_scales || !ws2 || !y)
+    return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 8) || !aligned(w_codes, 8) || !aligned(gsa, 4) || !aligned(ws2, 4) ||
+      !aligned(group_offsets, 4) || !aligned(row_index, 4) ||
+      !aligned(y, y_dtype == NVFP4_DTYPE_FP32 ? 4 : 2))
+    return NVFP4_ERR_ALIGN;
+  return launched(launch_grouped_gemv(a_codes, a_scales, gsa, a_rows, row_index, group_offsets, G,
+                                      M_total, w_codes, w_scales, ws2, y,
+                                      y_dtype == NVFP4_DTYPE_BF16, N, K, (hipStream_t)stream));
+}
+
+NVFP4_API int nvfp4_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t N_inter,
+                                        int granularity, void* stream) {
+  if (M < 0 || granularity < 1 || N_inter < 0 || N_inter % (2 * (int64_t)granularity) != 0)
+    return NVFP4_ERR_SHAPE;
+  if ((M * (N_inter / 2) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N_inter == 0) return NVFP4_OK;
+  if (l1 == nullptr || h == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned(l1, 4) || !aligned(h, 4)) return NVFP4_ERR_ALIGN;
+  return launched(launch_swiglu_deinterleave(l1, h, M, N_inter, granularity, (hipStream_t)stream));
+}

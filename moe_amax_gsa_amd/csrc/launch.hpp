@@ -1,0 +1,43 @@
+// launch.hpp -- internal launchers behind the C ABI (not exported).
+// Each launcher assumes its arguments were validated by the ABI layer and
+// returns the HIP status of its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// amax -> gsa
+constexpr int64_t AMAX_SMALL_NUMEL = 65536;  // one workgroup, one kernel
+constexpr int AMAX_MAX_PARTS = 1024;         // phase-1 workgroups at most
+int amax_parts_for(int64_t numel);
+hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, void* ws,
+                           hipStream_t s);
+
+// quantize from a device gsa
+hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const float* gsa,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+// SwiGLU de-interleave
+hipError_t launch_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t NI, int gran,
+                                      hipStream_t s);
+
+// Weight-streaming linear for few rows (FP4 matrix cores).
+constexpr int64_t GEMV_MAX_M = 16;
+hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+// Grouped weight-streaming linear (device-side group sizes).
+hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                               int64_t a_rows, const int32_t* row_index, const int32_t* offsets,
+                               int G, int64_t M_total, const uint8_t* w_codes,
+                               const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
+                               int64_t N, int64_t K, hipStream_t s);
+
+// Tiled GEMM for many rows (dequantize to f16, f16 matrix cores).
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+}  // namespace nvfp4

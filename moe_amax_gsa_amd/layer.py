@@ -1,0 +1,121 @@
+"""NVFP4 linear layers over the C ABI: device buffers, allocated once.
+
+``Nvfp4Linear`` runs the single-projection path (the pages' Nvfp4Linear:
+amax -> gsa, quantize from the gsa buffer, block-scaled GEMM; see
+dsv4/_archive/layers/linear.py, _run_impl).  ``Nvfp4MoE`` runs the routed
+expert pair (L1 gate/up with granularity-8 interleave, SwiGLU, re-quantize,
+L2), as README.md's MoE kernel section describes, unfused.  Both keep gsa
+on the device: no host synchronisation, no per-call host-to-device copy
+(deleted PERFORMANCE_AUDIT.md, P0; docs/PERFORMANCE_AUDIT.md, P2).
+
+Torch is used for memory and streams only; all arithmetic runs in
+libnvfp4.so.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import nvfp4 as C
+
+
+def _f32_scalar(v, device) -> torch.Tensor:
+    if isinstance(v, torch.Tensor):
+        return v.to(device=device, dtype=torch.float32).reshape(1).contiguous()
+    return torch.tensor([float(v)], dtype=torch.float32, device=device)
+
+
+class Nvfp4Linear:
+    """y = Nvfp4Linear(x): x (M, K) bf16/fp32 -> y (M, N) fp32 (or bf16)."""
+
+    def __init__(self, w_codes: torch.Tensor, w_scales: torch.Tensor, ws2, max_tokens: int,
+                 out_dtype=torch.float32, x_dtype=torch.bfloat16):
+        assert w_codes.dtype == torch.uint8 and w_scales.dtype == torch.uint8
+        self.device = w_codes.device
+        self.N, self.K = w_codes.shape[0], w_codes.shape[1] * 2
+        self.w_codes = w_codes.contiguous()
+        self.w_scales = w_scales.contiguous()
+        self.ws2 = _f32_scalar(ws2, self.device)
+        self.max_tokens = max_tokens
+        dev = self.device
+        self.gsa = torch.zeros(1, dtype=torch.float32, device=dev)
+        nws = C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, max_tokens * self.K)
+        self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+        self.codes = torch.empty(max_tokens, self.K // 2, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(max_tokens, self.K // 16, dtype=torch.uint8, device=dev)
+        self.y = torch.empty(max_tokens, self.N, dtype=out_dtype, device=dev)
+
+    def quantize(self, x: torch.Tensor, stream=None):
+        M = x.shape[0]
+        C.nvfp4_amax_gsa(x, self.gsa, self.ws, stream)
+        C.nvfp4_quantize_from_buffer(x, self.gsa, self.codes[:M], self.scales[:M], stream)
+        return self.codes[:M], self.scales[:M], self.gsa
+
+    def run_from_quantized(self, codes, scales, gsa, stream=None) -> torch.Tensor:
+        M = codes.shape[0]
+        y = self.y[:M]
+        C.nvfp4_linear(codes, scales, gsa, self.w_codes, self.w_scales, self.ws2, y, None, stream)
+        return y
+
+    def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        assert x.shape[0] <= self.max_tokens and x.shape[1] == self.K
+        codes, scales, gsa = self.quantize(x, stream)
+        return self.run_from_quantized(codes, scales, gsa, stream)
+
+    __call__ = forward
+
+
+class Nvfp4MoE:
+    """Routed experts: y2 (P, N2) for the P (token, expert) pairs in expert order.
+
+    x (T, K1) bf16; row_index (P,) int32 = token of each pair; offsets (E+1,)
+    int32 = first pair of each expert.  L1 weights (E, N1, K1/2) hold
+    gate/up column groups interleaved at ``granularity``; L2 weights
+    (E, N2, N1/4) consume the SwiGLU output of width N1/2.
+    """
+
+    def __init__(self, w1_codes, w1_scales, w1_ws2, w2_codes, w2_scales, w2_ws2, max_pairs: int,
+                 max_tokens: int, granularity: int = 8):
+        dev = w1_codes.device
+        self.device = dev
+        self.E, self.N1, self.K1 = w1_codes.shape[0], w1_codes.shape[1], w1_codes.shape[2] * 2
+        self.N2, self.K2 = w2_codes.shape[1], w2_codes.shape[2] * 2
+        assert self.K2 * 2 == self.N1, "L2 input width must be half the L1 output width"
+        self.granularity = granularity
+        self.w1_codes, self.w1_scales = w1_codes.contiguous(), w1_scales.contiguous()
+        self.w2_codes, self.w2_scales = w2_codes.contiguous(), w2_scales.contiguous()
+        self.w1_ws2 = w1_ws2.to(device=dev, dtype=torch.float32).contiguous()
+        self.w2_ws2 = w2_ws2.to(device=dev, dtype=torch.float32).contiguous()
+        self.gsa1 = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.gsa2 = torch.zeros(1, dtype=torch.float32, device=dev)
+        nws = max(C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, max_tokens * self.K1),
+                  C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, max_pairs * self.K2), 16)
+        self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        self.x_codes = torch.empty(max_tokens, self.K1 // 2, dtype=torch.uint8, device=dev)
+        self.x_scales = torch.empty(max_tokens, self.K1 // 16, dtype=torch.uint8, device=dev)
+        self.y1 = torch.empty(max_pairs, self.N1, dtype=torch.float32, device=dev)
+        self.h = torch.empty(max_pairs, self.K2, dtype=torch.float32, device=dev)
+        self.h_codes = torch.empty(max_pairs, self.K2 // 2, dtype=torch.uint8, device=dev)
+        self.h_scales = torch.empty(max_pairs, self.K2 // 16, dtype=torch.uint8, device=dev)
+        self.y2 = torch.empty(max_pairs, self.N2, dtype=torch.float32, device=dev)
+
+    def forward(self, x, row_index, offsets, stream=None) -> torch.Tensor:
+        T, P = x.shape[0], row_index.shape[0]
+        xc, xs = self.x_codes[:T], self.x_scales[:T]
+        C.nvfp4_amax_gsa(x, self.gsa1, self.ws, stream)
+        C.nvfp4_quantize_from_buffer(x, self.gsa1, xc, xs, stream)
+        y1 = self.y1[:P]
+        C.nvfp4_grouped_linear(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
+                               self.w1_scales, self.w1_ws2, y1, None, stream)
+        h = self.h[:P]
+        C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream)
+        hc, hs = self.h_codes[:P], self.h_scales[:P]
+        C.nvfp4_amax_gsa(h, self.gsa2, self.ws, stream)
+        C.nvfp4_quantize_from_buffer(h, self.gsa2, hc, hs, stream)
+        y2 = self.y2[:P]
+        C.nvfp4_grouped_linear(hc, hs, self.gsa2, None, offsets, self.w2_codes, self.w2_scales,
+                               self.w2_ws2, y2, None, stream)
+        return y2
+
+    __call__ = forward

@@ -1,0 +1,149 @@
+"""Python binding of the NVFP4 C ABI (include/nvfp4.h) -- marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU; it passes their data pointers, sizes
+and the current HIP stream, and raises on a negative status.  Every step of
+the computation runs in the HIP library; there is no fallback.  Importing
+this module loads libnvfp4.so and fails loudly when it has not been built
+(``python -m moe_amax_gsa_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loaded first: the library binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+OK = 0
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+OP_AMAX_GSA = 0
+OP_QUANTIZE = 1
+OP_LINEAR = 2
+OP_GROUPED_LINEAR = 3
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_amax_gsa_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+lib.nvfp4_abi_version.restype = _I
+lib.nvfp4_abi_version.argtypes = []
+lib.nvfp4_status_string.restype = ctypes.c_char_p
+lib.nvfp4_status_string.argtypes = [_I]
+lib.nvfp4_workspace_bytes.restype = _SZ
+lib.nvfp4_workspace_bytes.argtypes = [_I, _I64, _I64, _I64, _I]
+lib.nvfp4_amax_gsa.restype = _I
+lib.nvfp4_amax_gsa.argtypes = [_P, _I, _I64, _P, _P, _SZ, _P]
+lib.nvfp4_quantize_from_buffer.restype = _I
+lib.nvfp4_quantize_from_buffer.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P]
+lib.nvfp4_linear.restype = _I
+lib.nvfp4_linear.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_grouped_linear.restype = _I
+lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
+                                     _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_swiglu_deinterleave.restype = _I
+lib.nvfp4_swiglu_deinterleave.argtypes = [_P, _P, _I64, _I64, _I, _P]
+
+
+class Nvfp4Error(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise Nvfp4Error(f"{what}: {lib.nvfp4_status_string(status).decode()} ({status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def nvfp4_abi_version() -> int:
+    return lib.nvfp4_abi_version()
+
+
+def nvfp4_workspace_bytes(op: int, M: int, N: int = 0, K: int = 0, G: int = 0) -> int:
+    return lib.nvfp4_workspace_bytes(op, M, N, K, G)
+
+
+def nvfp4_amax_gsa(x: torch.Tensor, gsa: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """gsa[0] = max(max|x|, 1e-8) / 2688 on the device (x bf16 or fp32)."""
+    _check(lib.nvfp4_amax_gsa(_ptr(x), _dtype(x), x.numel(), _ptr(gsa), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream)), "nvfp4_amax_gsa")
+
+
+def nvfp4_quantize_from_buffer(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
+                               scales: torch.Tensor, stream=None) -> None:
+    """x (M, K) -> codes (M, K/2) uint8, scales (M, K/16) uint8 with device gsa."""
+    M, K = x.shape
+    _check(lib.nvfp4_quantize_from_buffer(_ptr(x), _dtype(x), M, K, _ptr(gsa), _ptr(codes),
+                                          _ptr(scales), _stream(stream)),
+           "nvfp4_quantize_from_buffer")
+
+
+def nvfp4_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,
+                 w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
+                 y: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """y (M, N) = gsa * ws2 * dequant(A) @ dequant(W)^T."""
+    M = a_codes.shape[0]
+    K = a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    _check(lib.nvfp4_linear(_ptr(a_codes), _ptr(a_scales), _ptr(gsa), _ptr(w_codes),
+                            _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y), M, N, K, _ptr(ws),
+                            0 if ws is None else ws.numel() * ws.element_size(),
+                            _stream(stream)), "nvfp4_linear")
+
+
+def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,
+                         row_index: Optional[torch.Tensor], group_offsets: torch.Tensor,
+                         w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
+                         y: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """w_codes (G, N, K/2), w_scales (G, N, K/16), ws2 (G,), y (M_total, N)."""
+    G, N = w_codes.shape[0], w_codes.shape[1]
+    K = w_codes.shape[2] * 2
+    _check(lib.nvfp4_grouped_linear(_ptr(a_codes), _ptr(a_scales), _ptr(gsa), a_codes.shape[0],
+                                    _ptr(row_index), _ptr(group_offsets), G, y.shape[0],
+                                    _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(y),
+                                    _dtype(y), N, K, _ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream)), "nvfp4_grouped_linear")
+
+
+def nvfp4_swiglu_deinterleave(l1: torch.Tensor, h: torch.Tensor, granularity: int = 8,
+                              stream=None) -> None:
+    """h (M, N/2) = silu(gate) * up from granularity-interleaved l1 (M, N), fp32."""
+    M, NI = l1.shape
+    _check(lib.nvfp4_swiglu_deinterleave(_ptr(l1), _ptr(h), M, NI, granularity,
+                                         _stream(stream)), "nvfp4_swiglu_deinterleave")

@@ -190,3 +190,39 @@ def make(name: str):
                            name=name)
     return make_moe(c["tokens"], c["experts"], c["topk"], c["K1"], c["N1"], c["K2"],
                     c["N2"], c["granularity"], c["seed"], c["sf"], c["ws2"], name=name)
+
+
+# ------------------------------------------------------------------ upload
+def bf16_to_torch(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bits -> torch bfloat16 tensor on device (bit copy)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+def moe_weights_to(moe: MoEInputs, device, experts=None, keep_host: bool = False):
+    """Stacked expert weights on the device: (w1_codes, w1_scales, w1_ws2,
+    w2_codes, w2_scales, w2_ws2).  Experts outside ``experts`` (default:
+    the experts that receive at least one token) are left zero -- the
+    grouped kernels never read an empty group's weights."""
+    E = moe.E
+    if experts is None:
+        experts = moe.active_experts
+    w1c = torch.zeros(E, moe.N1, moe.K1 // 2, dtype=torch.uint8, device=device)
+    w1s = torch.zeros(E, moe.N1, moe.K1 // 16, dtype=torch.uint8, device=device)
+    w2c = torch.zeros(E, moe.N2, moe.K2 // 2, dtype=torch.uint8, device=device)
+    w2s = torch.zeros(E, moe.N2, moe.K2 // 16, dtype=torch.uint8, device=device)
+    w1_ws2 = np.zeros(E, np.float32)
+    w2_ws2 = np.zeros(E, np.float32)
+    for e in experts:
+        c, s, w = moe.weight(0, int(e))
+        w1c[e].copy_(torch.from_numpy(c))
+        w1s[e].copy_(torch.from_numpy(s))
+        w1_ws2[e] = w
+        c, s, w = moe.weight(1, int(e))
+        w2c[e].copy_(torch.from_numpy(c))
+        w2s[e].copy_(torch.from_numpy(s))
+        w2_ws2[e] = w
+        if not keep_host:
+            moe.drop_cache()
+    return (w1c, w1s, torch.from_numpy(w1_ws2).to(device), w2c, w2s,
+            torch.from_numpy(w2_ws2).to(device))

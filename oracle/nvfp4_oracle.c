@@ -238,11 +238,11 @@ void oracle_linear(const uint8_t *a_codes, const uint8_t *a_scales, float gsa,
                    const uint8_t *w_codes, const uint8_t *w_scales, float ws2,
                    int64_t M, int64_t N, int64_t K, double *y)
 {
-    #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t m = 0; m < M; ++m)
-        for (int64_t n = 0; n < N; ++n)
-            y[m * N + n] = (double)gsa * (double)ws2 *
-                           dot_row(a_codes, a_scales, m, w_codes, w_scales, n, K);
+    #pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < M * N; ++i) {
+        int64_t m = i / N, n = i % N;
+        y[i] = (double)gsa * (double)ws2 * dot_row(a_codes, a_scales, m, w_codes, w_scales, n, K);
+    }
 }
 
 /* The same outputs at a list of (m, n) positions only. */

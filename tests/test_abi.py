@@ -1,0 +1,81 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/nvfp4.h declares, and rejects bad arguments with a
+negative status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+LIB = os.path.join(ROOT, "moe_amax_gsa_amd", "libnvfp4.so")
+
+
+@pytest.fixture(scope="module")
+def C():
+    if not os.path.exists(LIB):
+        from moe_amax_gsa_amd import build
+        build.build(verbose=False)
+    from moe_amax_gsa_amd import nvfp4
+    return nvfp4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ["nvfp4_amax_gsa", "nvfp4_quantize_from_buffer", "nvfp4_linear",
+              "nvfp4_grouped_linear"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(C):
+    lib = ctypes.CDLL(C.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert C.nvfp4_abi_version() == 1
+
+
+def test_status_strings(C):
+    for st in [0, -1, -2, -3, -4, -5, -6]:
+        assert C.lib.nvfp4_status_string(st)
+    assert C.lib.nvfp4_status_string(-99) == b"unknown status"
+
+
+def test_validation_errors_return_before_any_launch(C):
+    L = C.lib
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation
+    # bad dtype, negative size, K % 16, null pointers, workspace
+    assert L.nvfp4_amax_gsa(fake, 7, 10, fake, None, 0, None) == -3
+    assert L.nvfp4_amax_gsa(fake, 0, -1, fake, None, 0, None) == -2
+    assert L.nvfp4_amax_gsa(fake, 0, 10, None, None, 0, None) == -1
+    assert L.nvfp4_amax_gsa(ctypes.c_void_p(4097), 0, 10, fake, None, 0, None) == -5
+    big = 10 ** 7
+    need = C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, big)
+    assert need > 0
+    assert L.nvfp4_amax_gsa(fake, 0, big, fake, None, 0, None) == -4
+    assert L.nvfp4_amax_gsa(fake, 0, big, fake, fake, need - 4, None) == -4
+    assert C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, 1000) == 0
+    assert L.nvfp4_quantize_from_buffer(fake, 0, 4, 15, fake, fake, fake, None) == -2
+    assert L.nvfp4_quantize_from_buffer(fake, 0, 4, 0, fake, fake, fake, None) == -2
+    assert L.nvfp4_quantize_from_buffer(fake, 2, 4, 16, fake, fake, fake, None) == -3
+    assert L.nvfp4_quantize_from_buffer(fake, 0, 4, 16, None, fake, fake, None) == -1
+    assert L.nvfp4_quantize_from_buffer(fake, 0, 0, 16, None, None, None, None) == 0  # no-op
+    args = [fake] * 7
+    assert L.nvfp4_linear(*args, 0, 2, 3, 24, None, 0, None) == -2
+    assert L.nvfp4_linear(*args, 5, 2, 3, 32, None, 0, None) == -3
+    assert L.nvfp4_linear(fake, fake, None, fake, fake, fake, fake, 1, 2, 3, 32, None, 0,
+                          None) == -1
+    assert L.nvfp4_linear(*args, 1, 0, 3, 32, None, 0, None) == 0  # M == 0: no-op
+    # grouped: no row_index needs a_rows >= M_total; G must be positive
+    assert L.nvfp4_grouped_linear(fake, fake, fake, 4, None, fake, 2, 8, fake, fake, fake, fake,
+                                  1, 16, 32, None, 0, None) == -2
+    assert L.nvfp4_grouped_linear(fake, fake, fake, 8, None, fake, 0, 8, fake, fake, fake, fake,
+                                  1, 16, 32, None, 0, None) == -2
+    assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 24, 8, None) == -2
+    assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 32, 0, None) == -2

@@ -1,0 +1,404 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: gsa, codes and scales bit-exact; linear outputs within
+max|y - y_ref| / max|y_ref| <= 1e-3 of the oracle's FP64 accumulation of the
+same dequantized operands (stepwise: the oracle consumes the GPU's own
+quantized activations, checked bit-exact first); integer-valued special
+cases bit-exact.  Full-size workloads are checked on sampled outputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from moe_amax_gsa_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+REL_TOL = 1e-3
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def C():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    from moe_amax_gsa_amd import nvfp4
+    return nvfp4
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def x_dev(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return W.bf16_to_torch(bits, DEV)
+    return to_dev(W.bf16_bits_to_f32(bits))
+
+
+def x_host(bits: np.ndarray, dtype: str) -> np.ndarray:
+    return bits if dtype == "bf16" else np.ascontiguousarray(W.bf16_bits_to_f32(bits))
+
+
+def gpu_gsa(C, x):
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, x.numel()))
+    ws = torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV)  # garbage: no init needed
+    C.nvfp4_amax_gsa(x, gsa, ws)
+    return gsa
+
+
+def gpu_quantize(C, x, gsa):
+    M, K = x.shape
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    C.nvfp4_quantize_from_buffer(x, gsa, codes, scales)
+    return codes, scales
+
+
+def rel_err(y, ref):
+    return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def f32(t: torch.Tensor) -> np.float32:
+    return np.float32(t.cpu().numpy()[0])
+
+
+# ---------------------------------------------------------------- amax / gsa
+AMAX_CASES = [
+    (1, "bf16", "last"), (7, "bf16", "first"), (1000, "fp32", "last"), (65536, "bf16", "mid"),
+    (65537, "bf16", "last"), (100003, "fp32", "last"), (2 ** 20 + 5, "bf16", "last"),
+    (2048 * 7168, "bf16", "last"), (3 * 2 ** 20 + 3, "fp32", "first"), (4096, "bf16", "zero"),
+    (70000, "bf16", "negzero"),
+]
+
+
+@pytest.mark.parametrize("n,dtype,plant", AMAX_CASES)
+def test_amax_gsa_bitexact(C, n, dtype, plant):
+    say("amax", n, dtype, plant)
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n)
+    if plant == "zero":
+        x[:] = 0.0
+    elif plant == "negzero":
+        x[:] = -0.0
+    else:
+        pos = {"last": n - 1, "first": 0, "mid": n // 2}[plant]
+        x[pos] = -50.0  # a negative maximum
+    bits = W.to_bf16_bits(x)
+    g = gpu_gsa(C, x_dev(bits, dtype))
+    want = oracle.amax_gsa(x_host(bits, dtype))
+    assert f32(g) == want
+
+
+def test_amax_race_repeat(C):
+    """Large grid, maximum planted in the last workgroup's range, many runs."""
+    n = 2 ** 24 + 3
+    say("amax race", n)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(n)
+    x[-2] = 123.0
+    bits = W.to_bf16_bits(x)
+    xd = x_dev(bits, "bf16")
+    want = oracle.amax_gsa(bits)
+    for _ in range(20):
+        assert f32(gpu_gsa(C, xd)) == want
+
+
+# ---------------------------------------------------------------- quantize
+QUANT_CASES = [
+    (1, 16, "normal", "bf16"), (3, 48, "normal", "fp32"), (7, 256, "outliers", "bf16"),
+    (33, 1040, "zero_blocks", "fp32"), (16, 7168, "student_t", "bf16"), (300, 512, "normal", "bf16"),
+    (5, 2048, "student_t", "fp32"),
+]
+
+
+@pytest.mark.parametrize("M,K,dist,dtype", QUANT_CASES)
+def test_quantize_bitexact(C, M, K, dist, dtype):
+    say("quantize", M, K, dist, dtype)
+    rng = np.random.default_rng(M * 7 + K)
+    bits = W.to_bf16_bits(W.draw_activation(rng, M, K, dist))
+    xd = x_dev(bits, dtype)
+    g = gpu_gsa(C, xd)
+    assert f32(g) == oracle.amax_gsa(x_host(bits, dtype))
+    codes, scales = gpu_quantize(C, xd, g)
+    oc, os_ = oracle.quantize(x_host(bits, dtype), f32(g))
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+def test_quantize_small_gsa_saturates(C):
+    """A caller gsa far too small (the pages' input_scale bug) saturates
+    block scales at 448 on both sides."""
+    say("quantize saturation")
+    rng = np.random.default_rng(3)
+    bits = W.to_bf16_bits(rng.standard_normal((8, 256)) * 7956.0)
+    xd = x_dev(bits, "bf16")
+    g = torch.tensor([0.000251], dtype=torch.float32, device=DEV)
+    codes, scales = gpu_quantize(C, xd, g)
+    oc, os_ = oracle.quantize(bits, f32(g))
+    assert np.array_equal(scales.cpu().numpy(), os_) and np.any(os_ == 0x7E)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+def test_quantize_signed_zero_and_underflow(C):
+    say("quantize zeros")
+    x = np.zeros((2, 64))
+    x[0, :16] = 1e-4 * np.linspace(-1, 1, 16)
+    x[0, 20] = 1000.0
+    bits = W.to_bf16_bits(x)
+    bits[1, 5] = 0x8000
+    xd = x_dev(bits, "bf16")
+    g = gpu_gsa(C, xd)
+    codes, scales = gpu_quantize(C, xd, g)
+    oc, os_ = oracle.quantize(bits, f32(g))
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+# ---------------------------------------------------------------- linear
+def run_linear(C, inp: W.LinearInputs, y_dtype=torch.float32, dtype="bf16"):
+    xd = x_dev(inp.x, dtype)
+    g = gpu_gsa(C, xd)
+    codes, scales = gpu_quantize(C, xd, g)
+    wc, ws = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=DEV)
+    y = torch.full((inp.M, inp.N), float("nan"), dtype=y_dtype, device=DEV)
+    C.nvfp4_linear(codes, scales, g, wc, ws, ws2, y)
+    return g, codes, scales, y
+
+
+LINEAR_CASES = [
+    (1, 16, 16), (1, 17, 48), (2, 40, 256), (3, 33, 272), (5, 130, 1024), (16, 64, 512),
+    (17, 40, 256), (33, 130, 1040), (130, 300, 512), (129, 257, 2064), (256, 256, 7168),
+]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_CASES)
+def test_linear_parity(C, M, N, K):
+    say("linear", M, N, K)
+    inp = W.make_linear(M, K, N, seed=M + N + K, x="outliers", sf=(0.125, 8.0), ws2=0.0037)
+    g, codes, scales, y = run_linear(C, inp)
+    oc, os_ = oracle.quantize(inp.x, f32(g))
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    ref = oracle.linear(oc, os_, f32(g), inp.w_codes, inp.w_scales, inp.ws2)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(yg))
+    assert rel_err(yg, ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 7168), (3, 100, 256), (40, 96, 1024), (200, 160, 7168)])
+def test_linear_integer_case_bitexact(C, M, N, K):
+    """All block scales 1.0, gsa = ws2 = 1: outputs are multiples of 1/4 below
+    2^22, exact in FP32 on any summation order -- catches nibble order,
+    scale indexing and tail bugs that a tolerance would hide."""
+    say("linear integer", M, N, K)
+    rng = np.random.default_rng(K + M)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asf = np.full((M, K // 16), 0x38, np.uint8)
+    wsf = np.full((N, K // 16), 0x38, np.uint8)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(to_dev(ac), to_dev(asf), one, to_dev(wc), to_dev(wsf), one, y)
+    ref = oracle.linear(ac, asf, 1.0, wc, wsf, 1.0)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_linear_bf16_output_is_rounded_fp32(C, M):
+    say("linear bf16 out", M)
+    inp = W.make_linear(M, 512, 96, seed=5)
+    _, codes, scales, y32 = run_linear(C, inp)
+    wc, ws = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=DEV)
+    g = gpu_gsa(C, x_dev(inp.x, "bf16"))
+    y16 = torch.empty(M, 96, dtype=torch.bfloat16, device=DEV)
+    C.nvfp4_linear(codes, scales, g, wc, ws, ws2, y16)
+    assert torch.equal(y16.cpu(), y32.cpu().to(torch.bfloat16))
+
+
+def test_linear_deterministic(C):
+    say("linear determinism")
+    inp = W.make_linear(300, 2048, 200, seed=9)
+    outs = [run_linear(C, inp)[3].cpu() for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+# ---------------------------------------------------------------- grouped / MoE
+def moe_small(**kw):
+    base = dict(tokens=9, experts=6, topk=2, K1=256, N1=64, K2=32, N2=40, granularity=8,
+                seed=17)
+    base.update(kw)
+    base["K2"] = base["N1"] // 2
+    return W.make_moe(**base)
+
+
+def run_moe_stepwise(C, moe, sample=None):
+    """Run the layer; check every step against the oracle on the GPU's own
+    input to that step.  sample: number of sampled outputs per GEMM (None =
+    all)."""
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
+    P = int(moe.offsets[-1])
+    w = W.moe_weights_to(moe, DEV, keep_host=True)
+    layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=moe.granularity)
+    xd = W.bf16_to_torch(moe.x, DEV)
+    ri = to_dev(moe.pair_token)
+    off = to_dev(moe.offsets)
+    y2 = layer(xd, ri, off).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    g1 = f32(layer.gsa1)
+    assert g1 == oracle.amax_gsa(moe.x)
+    oc1, os1 = oracle.quantize(moe.x, g1)
+    assert np.array_equal(layer.x_codes[:moe.T].cpu().numpy(), oc1)
+    assert np.array_equal(layer.x_scales[:moe.T].cpu().numpy(), os1)
+    y1 = layer.y1[:P].cpu().numpy().astype(np.float64)
+    h = layer.h[:P].cpu().numpy()
+    hc = layer.h_codes[:P].cpu().numpy()
+    hs = layer.h_scales[:P].cpu().numpy()
+    g2 = f32(layer.gsa2)
+    rng = np.random.default_rng(0)
+    for layer_id, yg, Ncols in [(0, y1, moe.N1), (1, y2, moe.N2)]:
+        ref_max = 0.0
+        err_max = 0.0
+        for e in moe.active_experts:
+            r0, r1 = int(moe.offsets[e]), int(moe.offsets[e + 1])
+            wc, wsf, w2 = moe.weight(layer_id, int(e))
+            rows = np.arange(r0, r1)
+            if layer_id == 0:
+                ac, asf, g = oc1[moe.pair_token[rows]], os1[moe.pair_token[rows]], g1
+            else:
+                ac, asf, g = hc[rows], hs[rows], g2
+            if sample is None:
+                ref = oracle.linear(ac, asf, g, wc, wsf, w2)
+                got = yg[rows]
+            else:
+                ms = rng.integers(0, len(rows), sample)
+                ns = rng.integers(0, Ncols, sample)
+                ns[:2] = [0, Ncols - 1]
+                ref = oracle.linear_at(ac, asf, g, wc, wsf, w2, ms, ns)
+                got = yg[rows[ms], ns]
+            ref_max = max(ref_max, float(np.max(np.abs(ref))))
+            err_max = max(err_max, float(np.max(np.abs(got - ref))))
+        assert err_max / ref_max <= REL_TOL, (layer_id, err_max / ref_max)
+        if layer_id == 0:
+            # SwiGLU on the GPU's own L1 output (tolerance only: exp rounding)
+            href = oracle.swiglu_deinterleave(layer.y1[:P].cpu().numpy(), moe.granularity)
+            assert np.max(np.abs(h - href)) <= 1e-6 * np.max(np.abs(href))
+            # re-quantize of the GPU's own h: bit-exact
+            assert g2 == oracle.amax_gsa(h)
+            oc2, os2 = oracle.quantize(h, g2)
+            assert np.array_equal(hc, oc2) and np.array_equal(hs, os2)
+
+
+def test_moe_small_stepwise(C):
+    say("moe small")
+    run_moe_stepwise(C, moe_small())
+
+
+def test_moe_small_skewed_groups(C):
+    """One expert takes many rows (more than one pass of the grouped kernel),
+    several experts are empty."""
+    say("moe skewed")
+    run_moe_stepwise(C, moe_small(tokens=40, experts=3, topk=2, K1=512, N1=64, N2=24, seed=4))
+
+
+def test_grouped_row_index_bounds(C):
+    """Row indices outside the activation rows and rows past the last group
+    are left unwritten."""
+    say("grouped bounds")
+    rng = np.random.default_rng(2)
+    K, N, G = 64, 32, 2
+    ac = rng.integers(0, 256, (3, K // 2), dtype=np.uint8)
+    asf = np.full((3, K // 16), 0x38, np.uint8)
+    wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    wsf = np.full((G, N, K // 16), 0x38, np.uint8)
+    offsets = np.array([0, 2, 4], np.int32)
+    row_index = np.array([0, 7, 2, -1, 1, 1], np.int32)  # rows 1, 3 invalid; rows 4, 5 ungrouped
+    one = torch.ones(G, dtype=torch.float32, device=DEV)
+    y = torch.full((6, N), -7.0, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(to_dev(ac), to_dev(asf), one[:1], to_dev(row_index), to_dev(offsets),
+                           to_dev(wc), to_dev(wsf), one, y)
+    yh = y.cpu().numpy().astype(np.float64)
+    assert np.all(yh[[1, 3, 4, 5]] == -7.0)
+    for r, g in [(0, 0), (2, 1)]:
+        ref = oracle.linear(ac[row_index[r]:row_index[r] + 1], asf[:1], 1.0, wc[g], wsf[g], 1.0)
+        assert np.array_equal(yh[r], ref[0])
+
+
+def test_swiglu_parity(C):
+    say("swiglu")
+    rng = np.random.default_rng(1)
+    l1 = (rng.standard_normal((37, 96)) * 5).astype(np.float32)
+    h = torch.empty(37, 48, dtype=torch.float32, device=DEV)
+    C.nvfp4_swiglu_deinterleave(to_dev(l1), h, 8)
+    href = oracle.swiglu_deinterleave(l1, 8)
+    assert np.max(np.abs(h.cpu().numpy() - href)) <= 1e-6 * np.max(np.abs(href))
+
+
+# ---------------------------------------------------------------- full workloads
+def sample_positions(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, n)
+    ns = rng.integers(0, N, n)
+    ms[:4] = [0, 0, M - 1, M - 1]
+    ns[:4] = [0, N - 1, 0, N - 1]
+    return ms, ns
+
+
+@pytest.mark.parametrize("name", ["tiny_m1_k256_n256", "decode_m1_k7168_n1536",
+                                  "prefill_m512_k7168_n4096", "stress_m2048_k7168_n7168"])
+def test_workload_linear(C, name):
+    say("workload", name)
+    inp = W.make(name)
+    g, codes, scales, y = run_linear(C, inp)
+    assert f32(g) == oracle.amax_gsa(inp.x)
+    oc, os_ = oracle.quantize(inp.x, f32(g))
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(yg))
+    if inp.M * inp.N <= 1 << 16:
+        ref = oracle.linear(oc, os_, f32(g), inp.w_codes, inp.w_scales, inp.ws2)
+        assert rel_err(yg, ref) <= REL_TOL
+    else:
+        ms, ns = sample_positions(inp.M, inp.N, 4096, 1)
+        ref = oracle.linear_at(oc, os_, f32(g), inp.w_codes, inp.w_scales, inp.ws2, ms, ns)
+        assert rel_err(yg[ms, ns], ref) <= REL_TOL
+
+
+def test_workload_moe(C):
+    say("workload moe_t64_e256_top8")
+    run_moe_stepwise(C, W.make("moe_t64_e256_top8"), sample=64)
+
+
+def test_graph_capture_replays_match_eager(C):
+    """The whole step (amax, quantize, linear) captured once and replayed,
+    with eager work in between; every replay equals the eager result."""
+    say("graph capture")
+    from moe_amax_gsa_amd.layer import Nvfp4Linear
+    inp = W.make_linear(1, 7168, 1536, seed=1, x="outliers")
+    layer = Nvfp4Linear(to_dev(inp.w_codes), to_dev(inp.w_scales), inp.ws2, max_tokens=1)
+    x = W.bf16_to_torch(inp.x, DEV)
+    eager = layer(x).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer(x)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = layer(x)
+    for i in range(4):
+        layer.y.fill_(float("nan"))
+        layer.gsa.fill_(0.0)
+        _ = torch.randn(1000, device=DEV).sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
