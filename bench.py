@@ -4,15 +4,26 @@
 
 A step is one pass of the layer's hot path over one batch of synthetic,
 seeded input already resident in HBM: amax -> gsa, quantize from the gsa
-buffer, and the block-scaled linear (and, for the MoE workload, SwiGLU,
-re-quantize and the second grouped linear).  The headline line is the
-decode projection (M=1, K=7168, N=1536): decode weight-stream GB/s =
-algorithmic bytes of the linear (weight codes + weight scales + activation
-codes + scales + output) / step time.  Weight copies are rotated over more
-than 512 MB so the 256 MB Infinity Cache cannot serve repeats.  The other
-workloads are reported under "workloads" in the same JSON line.
+buffer and the block-scaled linear (for the MoE workload also SwiGLU,
+re-quantize and the second grouped linear).  Timing: W untimed eager steps,
+then the K steps are captured once in a HIP graph (launch cost off the
+critical path, as a decode loop runs), replayed once untimed, and replayed
+once more bracketed by synchronisation and events: ms_per_step = that
+replay / K.  Weight copies rotate over more than 512 MB so the 256 MB
+Infinity Cache cannot serve repeats.
 
-Prints ONE JSON line.
+Headline: the decode projection (M=1, K=7168, N=1536), step = one
+nvfp4_linear_run call (amax, gsa, quantize and the weight-streaming linear
+in one kernel for a one-row activation).  value = algorithmic bytes of the
+step (weight codes + weight scales + bf16 activation + activation codes and
+scales + fp32 output) / step time.  The same step as three ABI calls and the
+other workloads are reported under "workloads".
+
+roofline: the dominant kernel's duration measured with events around each
+launch, queued behind a bounded spin kernel so that the host never gaps the
+GPU between them.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -31,6 +42,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2516.6  # dense f16/bf16 matrix cores: 256 CU * 4096 flop/clk * 2.4 GHz
 ROTATE_BYTES = 512 << 20
+HEAD = "decode_m1_k7168_n1536"
 
 
 def parse():
@@ -38,7 +50,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default=None, help="run one workload")
+    p.add_argument("--only", default=None, help="extra workload to run (default: all)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     return p.parse_args()
@@ -48,50 +60,100 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-class Timer:
-    """Events on the current (launch) stream."""
+# ------------------------------------------------------------------ timing
+def graph_ms_per_step(step, steps: int, warmup: int) -> float:
+    """step(i) enqueues step i.  W eager warmup steps, then K steps captured
+    in one graph, one untimed replay, one timed replay."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
-    def __init__(self):
-        self.a = torch.cuda.Event(enable_timing=True)
-        self.b = torch.cuda.Event(enable_timing=True)
 
-    def start(self):
-        self.a.record()
+_SPIN_CYCLES_PER_MS = None
 
-    def stop(self) -> float:
-        self.b.record()
-        self.b.synchronize()
-        return self.a.elapsed_time(self.b)
+
+def _spin_cycles_per_ms() -> float:
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        n = 1_000_000
+        torch.cuda._sleep(n)  # warm-up
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = n / max(a.elapsed_time(b), 1e-3)
+    return _SPIN_CYCLES_PER_MS
+
+
+def kernel_us(launch, iters: int, pre=None) -> float:
+    """Mean duration of launch(i), from events recorded on the launch stream
+    around each launch.  A bounded spin kernel (torch.cuda._sleep) holds the
+    GPU while the host enqueues everything, so the launches run back to back
+    and each event pair brackets one kernel."""
+    if pre is not None:
+        pre(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    torch.cuda._sleep(int(_spin_cycles_per_ms() * (2.0 + 0.1 * iters)))
+    for i in range(iters):
+        if pre is not None:
+            pre(i)
+        evs[i][0].record()
+        launch(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return 1e3 * sum(x.elapsed_time(y) for x, y in evs) / iters
 
 
 # ------------------------------------------------------------------ linear
 class LinearBench:
-    """One workload of the single-projection path with rotated weight copies."""
+    """One single-projection workload with rotated weight copies."""
 
     def __init__(self, C, inp, dev):
         from moe_amax_gsa_amd import workloads as W
         self.C, self.inp = C, inp
         M, K, N = inp.M, inp.K, inp.N
         wbytes = inp.w_codes.nbytes + inp.w_scales.nbytes
-        self.ncopies = max(1, min(256, -(-ROTATE_BYTES // wbytes)))
+        self.ncopies = max(1, min(512, -(-ROTATE_BYTES // wbytes)))
         wc = torch.from_numpy(inp.w_codes).to(dev)
         wsf = torch.from_numpy(inp.w_scales).to(dev)
         self.w = [(wc, wsf)] + [(wc.clone(), wsf.clone()) for _ in range(self.ncopies - 1)]
         self.x = W.bf16_to_torch(inp.x, dev)
         self.ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=dev)
         self.gsa = torch.zeros(1, dtype=torch.float32, device=dev)
-        nws = max(16, C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, M * K))
+        nws = max(16, C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, N, K))
         self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
         self.codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
         self.scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
         self.y = torch.empty(M, N, dtype=torch.float32, device=dev)
         self.flops = 2.0 * M * N * K
-        # algorithmic bytes of the linear: W codes + W scales + A codes + A scales + y
-        self.linear_bytes = wbytes + M * K // 2 + M * K // 16 + M * N * 4
-        # quantize pass: read x, write codes + scales
-        self.quant_bytes = M * K * 2 + M * K // 2 + M * K // 16
+        a_bytes = M * K // 2 + M * K // 16
+        # nvfp4_linear: weights + quantized activation + fp32 output
+        self.linear_bytes = wbytes + a_bytes + M * N * 4
+        # a whole step: weights + bf16 activation + quantized activation written + output
+        self.step_bytes = wbytes + M * K * 2 + a_bytes + M * N * 4
+        self.quant_bytes = M * K * 2 + a_bytes
 
-    def quantize(self):
+    def quantize(self, i=0):
         C = self.C
         C.nvfp4_amax_gsa(self.x, self.gsa, self.ws)
         C.nvfp4_quantize_from_buffer(self.x, self.gsa, self.codes, self.scales)
@@ -100,78 +162,35 @@ class LinearBench:
         wc, wsf = self.w[i % self.ncopies]
         self.C.nvfp4_linear(self.codes, self.scales, self.gsa, wc, wsf, self.ws2, self.y)
 
-    def step(self, i):
+    def step3(self, i):  # the three ABI calls
         self.quantize()
         self.linear(i)
 
-
-def time_steps(fn, steps, warmup) -> float:
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    t = Timer()
-    t.start()
-    for i in range(steps):
-        fn(i)
-    ms = t.stop()
-    torch.cuda.synchronize()
-    return ms / steps
+    def run(self, i):  # nvfp4_linear_run
+        wc, wsf = self.w[i % self.ncopies]
+        self.C.nvfp4_linear_run(self.x, self.gsa, self.codes, self.scales, wc, wsf, self.ws2,
+                                self.y, self.ws)
 
 
-def time_kernel(pre, kern, steps) -> float:
-    """Average duration of kern(i) measured by events around each launch."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        pre(i)
-        evs[i][0].record()
-        kern(i)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps
-
-
-# ------------------------------------------------------------------ oracle
-def cpu_baseline(inp, budget_s=12.0):
-    """The oracle's step (amax, quantize, linear) on host cores for the same
-    workload, repeated within a time budget."""
-    from oracle import oracle
-    threads = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    oracle._load()
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        g = oracle.amax_gsa(inp.x)
-        c, s = oracle.quantize(inp.x, g)
-        oracle.linear(c, s, g, inp.w_codes, inp.w_scales, inp.ws2)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 1000:
-            break
-    return el / n, n, int(os.environ.get("OMP_NUM_THREADS", threads))
-
-
-# ------------------------------------------------------------------ main
-def bench_linear(C, name, dev, steps, warmup):
+def bench_linear(C, name, dev, steps, warmup, kiters):
     from moe_amax_gsa_amd import workloads as W
     inp = W.make(name)
     b = LinearBench(C, inp, dev)
-    ms = time_steps(b.step, steps, warmup)
-    lin_ms = time_kernel(lambda i: b.quantize(), b.linear, steps)
-    q_ms = time_kernel(lambda i: None, lambda i: b.quantize(), steps)
-    r = {
-        "ms_per_step": ms,
-        "linear_us": lin_ms * 1e3,
-        "quant_us": q_ms * 1e3,
-        "rotated_weight_copies": b.ncopies,
-        "linear_GBps": b.linear_bytes / (lin_ms * 1e-3) / 1e9,
-        "linear_TFLOPs": b.flops / (lin_ms * 1e-3) / 1e12,
-        "step_GBps": b.linear_bytes / (ms * 1e-3) / 1e9,
-        "step_TFLOPs": b.flops / (ms * 1e-3) / 1e12,
-    }
+    r = {"rotated_weight_copies": b.ncopies}
+    r["step_us"] = 1e3 * graph_ms_per_step(b.run, steps, warmup)
+    r["step3_us"] = 1e3 * graph_ms_per_step(b.step3, steps, warmup)
+    r["linear_us"] = kernel_us(b.linear, kiters, pre=b.quantize)
+    r["run_us"] = kernel_us(b.run, kiters)
+    r["quant_us"] = kernel_us(lambda i: b.quantize(), kiters)
+    r["step_GBps"] = b.step_bytes / (r["step_us"] * 1e-6) / 1e9
+    r["step_TFLOPs"] = b.flops / (r["step_us"] * 1e-6) / 1e12
+    r["linear_GBps"] = b.linear_bytes / (r["linear_us"] * 1e-6) / 1e9
+    r["linear_TFLOPs"] = b.flops / (r["linear_us"] * 1e-6) / 1e12
     r["linear_frac_hbm"] = r["linear_GBps"] / HBM_PEAK_GBS
     r["linear_frac_mfma"] = r["linear_TFLOPs"] / MFMA_F16_PEAK_TFLOPS
+    r["step_bytes"] = b.step_bytes
+    r["linear_bytes"] = b.linear_bytes
+    r["flops"] = b.flops
     return inp, b, r
 
 
@@ -190,27 +209,49 @@ def bench_moe(C, dev, steps, warmup):
                   moe.N2 * moe.K2 // 2 + moe.N2 * moe.K2 // 16)
     wbytes = nact * per_expert
     flops = 2.0 * P * (moe.N1 * moe.K1 + moe.N2 * moe.K2)
-    ms = time_steps(lambda i: layer(x, ri, off), steps, warmup)
-    return {"ms_per_step": ms, "active_experts": nact, "weight_bytes": wbytes,
-            "step_GBps": wbytes / (ms * 1e-3) / 1e9,
-            "step_frac_hbm": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "step_TFLOPs": flops / (ms * 1e-3) / 1e12}
+    us = 1e3 * graph_ms_per_step(lambda i: layer(x, ri, off), steps, warmup)
+    return {"step_us": us, "active_experts": nact, "weight_bytes": wbytes,
+            "step_GBps": wbytes / (us * 1e-6) / 1e9,
+            "step_frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "step_TFLOPs": flops / (us * 1e-6) / 1e12}
 
 
+# ------------------------------------------------------------------ oracle
+def cpu_baseline(inp, budget_s=12.0):
+    """The oracle's step (amax, quantize, FP64 linear) for the same workload
+    on the host cores, repeated within a time budget."""
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    from oracle import oracle
+    oracle._load()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        g = oracle.amax_gsa(inp.x)
+        c, s = oracle.quantize(inp.x, g)
+        oracle.linear(c, s, g, inp.w_codes, inp.w_scales, inp.ws2)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    return el / n, n, int(os.environ["OMP_NUM_THREADS"])
+
+
+# ------------------------------------------------------------------ main
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
-              "sharded across GPUs in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU (got --gpus {args.gpus}): the layer is not sharded "
+              "across GPUs in this build", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench needs a GPU"
     from moe_amax_gsa_amd import nvfp4 as C
     dev = torch.device("cuda:0")
-    head = "decode_m1_k7168_n1536"
+    kiters = 50
 
-    log("headline", head)
-    inp, b, r = bench_linear(C, head, dev, args.steps, args.warmup)
-    workloads = {head: r}
+    log("headline", HEAD)
+    inp, b, r = bench_linear(C, HEAD, dev, args.steps, args.warmup, kiters)
+    workloads = {HEAD: r}
     if not args.no_extra:
         for name, steps in [("tiny_m1_k256_n256", args.steps),
                             ("prefill_m512_k7168_n4096", max(20, args.steps // 4)),
@@ -218,22 +259,23 @@ def main():
             if args.only and args.only != name:
                 continue
             log("workload", name)
-            workloads[name] = bench_linear(C, name, dev, steps, min(args.warmup, 10))[2]
+            workloads[name] = bench_linear(C, name, dev, steps, min(args.warmup, 10),
+                                           min(kiters, steps))[2]
         if not args.only or args.only == "moe_t64_e256_top8":
             log("workload moe_t64_e256_top8")
             workloads["moe_t64_e256_top8"] = bench_moe(C, dev, max(10, args.steps // 10),
-                                                      min(args.warmup, 5))
+                                                      min(args.warmup, 3))
 
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         per_step_s, nrep, cores = cpu_baseline(inp)
-        cpu = {"value": b.linear_bytes / per_step_s / 1e9, "unit": "GB/s", "cores": cores,
+        cpu = {"value": b.step_bytes / per_step_s / 1e9, "unit": "GB/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"{nrep} full oracle steps (amax, quantize, FP64 linear) of {head}, "
+               "sample": f"{nrep} whole oracle steps (amax, quantize, FP64 linear) of {HEAD}, "
                          f"{per_step_s * 1e3:.1f} ms each"}
 
-    ms = r["ms_per_step"]
+    run_gbps = b.step_bytes / (r["run_us"] * 1e-6) / 1e9
     line = {
         "metric": "NVFP4 linear decode weight-stream GB/s (M=1, K=7168, N=1536)",
         "value": r["step_GBps"],
@@ -241,21 +283,23 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": r["step_us"] * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1 x e2m1 (E4M3 block scales), fp32 accumulate",
+        "dtype": "e2m1 x e2m1, e4m3 block scales, f32 accumulate",
         "data": "synthetic, seeded",
-        "config": {"workload": head, "M": 1, "K": 7168, "N": 1536,
-                   "step": "amax_gsa + quantize_from_buffer + linear",
-                   "bytes_per_step": b.linear_bytes},
-        "roofline": {"bound": "hbm", "achieved": r["linear_GBps"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": r["linear_GBps"] / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gemv_fp4_kernel", "kernel_us": r["linear_us"]},
+        "config": {"workload": HEAD, "M": 1, "K": 7168, "N": 1536,
+                   "step": "nvfp4_linear_run (amax, gsa, quantize, linear)",
+                   "bytes_per_step": b.step_bytes},
+        "roofline": {"bound": "hbm", "achieved": run_gbps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": run_gbps / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemv_fp4_kernel (fused run mode)", "kernel_us": r["run_us"],
+                     "bytes_per_launch": b.step_bytes},
         "cpu_baseline": cpu,
         "workloads": workloads,
-        "context": "pages' whole-model decode on B200: ~1.45 s/token (not comparable)",
+        "context": "the pages' whole-model decode on B200 took about 1.45 s per token "
+                   "(61 layers; not comparable to one projection)",
     }
     print(json.dumps(line))
 

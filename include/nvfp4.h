@@ -86,9 +86,11 @@ extern "C" {
 #define NVFP4_OP_QUANTIZE 1
 #define NVFP4_OP_LINEAR 2
 #define NVFP4_OP_GROUPED_LINEAR 3
+#define NVFP4_OP_LINEAR_RUN 4
 
 /* Bytes of workspace an operation needs for the given sizes (0 if none).
- * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored. */
+ * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored;
+ * for NVFP4_OP_LINEAR_RUN, the activation is (M, K). */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
 
 /* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
@@ -120,6 +122,23 @@ int nvfp4_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *g
                  const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
                  void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* The whole layer on a bf16/fp32 activation, as Nvfp4Linear.run does
+ * (dsv4/_archive/layers/linear.py, _run_impl): steps 1, 2 and 3 with the
+ * same results as calling nvfp4_amax_gsa, nvfp4_quantize_from_buffer and
+ * nvfp4_linear in turn -- gsa, codes (M, K/2) and scales (M, K/16) are
+ * written as those calls would write them, and y (M, N).
+ * For a few rows (M <= 16, K % 256 == 0, M*K <= 16384, 16-byte aligned x
+ * and weights) it is ONE kernel: every workgroup reads the whole activation,
+ * computes its exact maximum by itself (no reduction across workgroups, so
+ * no workgroup waits on another), quantizes it into LDS and streams its
+ * weight rows.  Otherwise the separate kernels run in order (then ws must
+ * hold nvfp4_workspace_bytes(NVFP4_OP_LINEAR_RUN, M, N, K, 1) bytes).
+ * N == 0 only quantizes. */
+int nvfp4_linear_run(const void *x, int x_dtype, float *gsa, uint8_t *codes, uint8_t *scales,
+                     const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2, void *y,
+                     int y_dtype, int64_t M, int64_t N, int64_t K, void *ws, size_t ws_bytes,
+                     void *stream);
 
 /* Grouped linear (MoE experts, or any set of G weight matrices sharing one
  * activation gsa).  Output row r, 0 <= r < M_total, belongs to group g when

@@ -53,6 +53,7 @@ NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, 
   (void)G;
   switch (op) {
     case NVFP4_OP_AMAX_GSA: return M > 0 ? amax_ws_bytes(M) : 0;
+    case NVFP4_OP_LINEAR_RUN: return (M > 0 && K > 0) ? amax_ws_bytes(M * K) : 0;
     default: return 0;
   }
 }
@@ -105,6 +106,40 @@ NVFP4_API int nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, cons
   if (M <= GEMV_MAX_M)
     return launched(launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s));
   return launched(launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s));
+}
+
+NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* codes,
+                               uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* ws2, void* y, int y_dtype, int64_t M, int64_t N,
+                               int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  int st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  if (M > 0 && (M * (K / 16) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!x || !gsa || !codes || !scales || !w_codes || !w_scales || !ws2 || (N > 0 && !y))
+    return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gsa, 4) || !aligned(w_codes, 8) ||
+      !aligned(ws2, 4) || !aligned(y, y_dtype == NVFP4_DTYPE_FP32 ? 4 : 2))
+    return NVFP4_ERR_ALIGN;
+  const bool xbf = x_dtype == NVFP4_DTYPE_BF16, ybf = y_dtype == NVFP4_DTYPE_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  if (N > 0 && gemv_run_supported(M, K, x, w_codes, w_scales))
+    return launched(launch_gemv_run(x, xbf, gsa, codes, scales, w_codes, w_scales, ws2, y, ybf, M,
+                                    N, K, s));
+  // general case: the three steps as separate kernels
+  const size_t need = amax_ws_bytes(M * K);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+  hipError_t e = launch_amax_gsa(x, xbf, M * K, gsa, ws, s);
+  if (e == hipSuccess) e = launch_quantize(x, xbf, M, K, gsa, codes, scales, s);
+  if (e == hipSuccess && N > 0) {
+    if (M <= GEMV_MAX_M)
+      e = launch_gemv(codes, scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s);
+    else
+      e = launch_gemm(codes, scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s);
+  }
+  return launched(e);
 }
 
 NVFP4_API int nvfp4_grouped_linear(const uint8_t* a_codes, const uint8_t* a_scales,

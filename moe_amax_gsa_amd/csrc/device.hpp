@@ -69,3 +69,135 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 }  // namespace nvfp4
+
+namespace nvfp4 {
+
+// ---- |x| maximum as an ordered integer (bf16: 15 bits, fp32: 31 bits).
+// For non-negative finite floats the bit pattern orders like the value, so
+// the integer max is the exact, order-free maximum.
+template <bool BF16>
+__device__ __forceinline__ uint32_t absbits_vec(uint4 v) {
+  if (BF16) {
+    uint32_t a = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+    uint32_t b = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
+    uint32_t c = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
+    uint32_t d = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
+    return max(max(a, b), max(c, d));
+  }
+  return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+}
+
+// Max of |x| bits over elements tid, tid + nthreads, ... (16-byte vectors,
+// scalar tail).  x must be 16-byte aligned.
+template <bool BF16>
+__device__ __forceinline__ uint32_t thread_absmax(const void* __restrict__ x, int64_t numel,
+                                                  int64_t tid, int64_t nthreads) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  const uint4* __restrict__ xv = (const uint4*)x;
+  const int64_t nvec = numel / EPV;
+  uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+  int64_t i = tid;
+  for (; i + 3 * nthreads < nvec; i += 4 * nthreads) {
+    uint4 v0 = xv[i], v1 = xv[i + nthreads], v2 = xv[i + 2 * nthreads], v3 = xv[i + 3 * nthreads];
+    m0 = max(m0, absbits_vec<BF16>(v0));
+    m1 = max(m1, absbits_vec<BF16>(v1));
+    m2 = max(m2, absbits_vec<BF16>(v2));
+    m3 = max(m3, absbits_vec<BF16>(v3));
+  }
+  for (; i < nvec; i += nthreads) m0 = max(m0, absbits_vec<BF16>(xv[i]));
+  for (int64_t e = nvec * EPV + tid; e < numel; e += nthreads) {
+    uint32_t b = BF16 ? (uint32_t)((const uint16_t*)x)[e] & 0x7FFFu
+                      : ((const uint32_t*)x)[e] & 0x7FFFFFFFu;
+    m1 = max(m1, b);
+  }
+  return max(max(m0, m1), max(m2, m3));
+}
+
+// gsa = max(amax, 1e-8) / (6 * 448).
+__device__ __forceinline__ float gsa_from_amax(float amax) {
+#pragma clang fp contract(off)
+  if (!(amax >= 1e-8f)) amax = 1e-8f;
+  return amax / 2688.0f;
+}
+
+// gsa = max(amax, 1e-8) / (6 * 448) from the maximum's bits.
+template <bool BF16>
+__device__ __forceinline__ float gsa_from_bits(uint32_t bits) {
+  return gsa_from_amax(BF16 ? __uint_as_float(bits << 16) : __uint_as_float(bits));
+}
+
+// Load the 16 elements of block b (elements 16b .. 16b+15 of a row-major
+// tensor whose row length is a multiple of 16) as floats.
+template <bool BF16>
+__device__ __forceinline__ void load_block16(const void* __restrict__ x, int64_t b, float v[16]) {
+  if (BF16) {
+    const uint4* p = (const uint4*)x + 2 * b;
+    const uint4 u0 = p[0], u1 = p[1];
+    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const uint4* p = (const uint4*)x + 4 * b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = p[i];
+      v[4 * i] = __uint_as_float(u.x);
+      v[4 * i + 1] = __uint_as_float(u.y);
+      v[4 * i + 2] = __uint_as_float(u.z);
+      v[4 * i + 3] = __uint_as_float(u.w);
+    }
+  }
+}
+
+__device__ __forceinline__ float block_absmax16(const float v[16]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+// Quantize one 16-element block held in registers: E4M3 scale byte and 16
+// E2M1 codes packed in two words (code 2i in the low nibble of byte i).
+// One IEEE fp32 operation per step, no contraction:
+//   sf = E4M3(bamax / (gsa * 6)), s = dec(sf) * gsa, code = sign | E2M1(|x| / s).
+__device__ __forceinline__ void quantize_vals16(const float v[16], float gsa, uint32_t& lo,
+                                                uint32_t& hi, uint32_t& sf) {
+#pragma clang fp contract(off)
+  const float bamax = block_absmax16(v);
+  const float six_gsa = gsa * 6.0f;
+  const float sf_raw = bamax / six_gsa;
+  sf = e4m3_encode(sf_raw);
+  const float sdec = e4m3_decode(sf);
+  const float sc = sdec * gsa;
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t mag = sdec != 0.0f ? e2m1_magnitude(fabsf(v[i]) / sc) : 0u;
+    const uint32_t code = ((__float_as_uint(v[i]) >> 31) << 3) | mag;
+    if (i < 8)
+      lo |= code << (4 * i);
+    else
+      hi |= code << (4 * (i - 8));
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void quantize_block16(const void* __restrict__ x, int64_t b, float gsa,
+                                                 uint32_t& lo, uint32_t& hi, uint32_t& sf) {
+  float v[16];
+  load_block16<BF16>(x, b, v);
+  quantize_vals16(v, gsa, lo, hi, sf);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations (lgkmcnt 0) but leaves vector-memory loads in flight, unlike
+// __syncthreads(), whose release fence also drains them.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace nvfp4

@@ -20,19 +20,48 @@
 // Lane geometry of the 16x16x128 FP4 MFMA (lane l, 64 lanes): A row / B
 // column l % 16, K slice l / 16 of 32 codes (16 bytes); result lane l holds
 // rows 4*(l/16) .. +3 of column l % 16.  A workgroup owns 16 weight rows; its
-// waves split the K dimension in 256-element super-chunks (128 bytes per row,
-// two MFMAs), and a lane's 32 bytes of a super-chunk are K slice j of MFMA 0
-// (first 16 bytes) and MFMA 1 (next 16).  Slice j of MFMA h spans blocks
-// 16c + 4j + 2h and +1, so A row i (slot s = i % 8) takes the half s % 2 of
-// slice s / 2.  Result row i of MFMA h is block 16c + 8(j%2) + 4(r/2) + 2h +
-// (r%2) for lane slice j and register r, whose two scale bytes sit in one
-// 8-byte word per row at byte 16c + 8(j%2).
+// waves split K in groups of S super-chunks of 256 elements (128 bytes per
+// row, two MFMAs each) and issue a whole group's weight loads before using
+// any.  A lane's 32 bytes of a super-chunk are K slice j of MFMA 0 (first 16
+// bytes) and MFMA 1 (next 16).  Slice j of MFMA h spans blocks 16c + 4j + 2h
+// and +1, so A row i (slot s = i % 8) takes the half s % 2 of slice s / 2.
+// Result row i of MFMA h is block 16c + 8(j%2) + 4(r/2) + 2h + (r%2) for lane
+// slice j and register r, whose two scale bytes sit in one 8-byte word per
+// row at byte 16c + 8(j%2).
+//
+// Fused mode (nvfp4_linear_run): for a few activation rows the whole step
+// amax -> gsa -> quantize -> linear is one kernel.  Every workgroup loads the
+// entire (small) activation, computes its exact maximum itself -- there is no
+// reduction across workgroups, so no workgroup ever waits for another -- and
+// quantizes it into LDS while its first weight loads are in flight.
+// Workgroup (0, 0) also writes gsa, codes and scales to memory.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace nvfp4 {
 
 typedef __attribute__((ext_vector_type(8))) int v8i;
+
+constexpr int GEMV_MAX_WAVES = 8;
+enum { MODE_PLAIN = 0, MODE_GROUPED = 1, MODE_RUN = 2 };
+
+struct GemvArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* gsa;
+  const int32_t* row_index;
+  const int32_t* offsets;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* ws2;
+  void* y;
+  int y_bf16, M, N, K, a_rows;
+  // MODE_RUN: the activation and where workgroup (0, 0) stores its quantization
+  const void* x;
+  float* gsa_out;
+  uint8_t* codes_out;
+  uint8_t* scales_out;
+};
 
 __device__ __forceinline__ float4_t mfma_fp4(v8i a, v8i b) {
   const float4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -41,8 +70,8 @@ __device__ __forceinline__ float4_t mfma_fp4(v8i a, v8i b) {
 }
 
 // 32 code bytes of a row at byte offset off, zero outside [0, rowbytes) or
-// when !ok.  FAST: the whole super-chunk is inside the row and 16-byte
-// aligned.  Otherwise 8-byte pieces (rows are 8-byte aligned since K % 16 == 0).
+// when !ok.  FAST: whole super-chunks inside rows, 16-byte aligned.
+// Otherwise 8-byte pieces (rows are 8-byte aligned since K % 16 == 0).
 template <bool FAST>
 __device__ __forceinline__ void load32(const uint8_t* row, int64_t off, int64_t rowbytes, bool ok,
                                        uint4& a, uint4& b) {
@@ -95,36 +124,51 @@ __device__ __forceinline__ void fp8x8_to_f32(uint2 s, float f[8]) {
   f[7] = __builtin_amdgcn_cvt_f32_fp8((int)s.y, 3);
 }
 
-// MP activation-row pairs per pass (up to 2*MP rows); pairs past the last
-// row of the pass are skipped.  GROUPED: blockIdx.y is the group; its rows
-// come from offsets[], its activation rows from row_index[] (or identity).
-template <int NW, int MP, bool FAST, bool GROUPED>
-__global__ __launch_bounds__(NW * 64) void gemv_fp4_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-    const float* __restrict__ gsa_p, const int32_t* __restrict__ row_index,
-    const int32_t* __restrict__ offsets, const uint8_t* __restrict__ w_codes,
-    const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
-    int y_bf16, int M, int N, int K, int a_rows) {
-  constexpr int ROWS = 2 * MP;
-  static_assert(NW * 64 >= ROWS * 16, "final reduction needs ROWS*16 threads");
-  __shared__ float red[NW][ROWS][16];
+// Weight codes and scales of S super-chunks (group cg) for this lane.  FAST:
+// unconditional loads of a clamped, always valid chunk -- chunks past the
+// end are skipped by the (wave-uniform) compute loop.  A branch around the
+// loads would make the compiler drain every outstanding load at its merge.
+template <int S, bool FAST>
+__device__ __forceinline__ void load_w_group(const uint8_t* wrow, const uint8_t* wsrow, int cg,
+                                             int nsc, int j, int64_t cbytes, int64_t sbytes,
+                                             uint4 wb0[S], uint4 wb1[S], uint2 wsb[S]) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = FAST ? min(cg * S + s, nsc - 1) : cg * S + s;
+    const bool ok = FAST || c < nsc;
+    load32<FAST>(wrow, (int64_t)c * 128 + 32 * j, cbytes, ok, wb0[s], wb1[s]);
+    wsb[s] = load8<FAST>(wsrow, (int64_t)c * 16 + 8 * (j & 1), sbytes, ok);
+  }
+}
 
+// S super-chunks per wave group; MP activation-row pairs per pass (pairs
+// past the last row are skipped); BPT activation blocks per thread in
+// MODE_RUN (the activation is held in registers between its amax and its
+// quantization).
+template <int S, int MP, bool FAST, int MODE, bool XBF16, int BPT>
+__global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const GemvArgs args) {
+  constexpr int ROWS = 2 * MP;
+  __shared__ float red[GEMV_MAX_WAVES][ROWS][16];
+  __shared__ float amax_red[GEMV_MAX_WAVES];
+  extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];
+
+  const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, j = lane >> 4;
+  const int M = args.M, N = args.N, K = args.K;
   const int n0 = blockIdx.x * 16;
-  const int g = GROUPED ? (int)blockIdx.y : 0;
+  const int g = MODE == MODE_GROUPED ? (int)blockIdx.y : 0;
   int r_begin = 0, r_end = M;
-  if (GROUPED) {
-    r_begin = max(offsets[g], 0);
-    r_end = min(offsets[g + 1], M);
+  if (MODE == MODE_GROUPED) {
+    r_begin = max(args.offsets[g], 0);
+    r_end = min(args.offsets[g + 1], M);
     if (r_begin >= r_end) return;  // uniform over the workgroup
   }
   const int64_t cbytes = K / 2, sbytes = K / 16;
   const int64_t n_here = (n0 + col < N) ? n0 + col : n0;  // clamp: results discarded
-  const uint8_t* wrow = w_codes + ((int64_t)g * N + n_here) * cbytes;
-  const uint8_t* wsrow = w_scales + ((int64_t)g * N + n_here) * sbytes;
+  const uint8_t* wrow = args.w_codes + ((int64_t)g * N + n_here) * cbytes;
+  const uint8_t* wsrow = args.w_scales + ((int64_t)g * N + n_here) * sbytes;
   const int nsc = (K + 255) / 256;
-  const float gscale = gsa_p[0] * ws2_p[g];
 
   // A operand: lane row i = col -> local row 2p + (i / 8), slot s = i % 8,
   // carries data only when s / 2 == j, in half s % 2.
@@ -133,7 +177,68 @@ __global__ __launch_bounds__(NW * 64) void gemv_fp4_kernel(
   // Result: lane rows 4j .. 4j+3 belong to local row 2p + j / 2.
   const int c_mloc = j >> 1;
 
+  const uint8_t* lds_codes = act_lds;
+  const uint8_t* lds_scales = act_lds + (size_t)M * cbytes;
+
   for (int r0 = r_begin; r0 < r_end; r0 += ROWS) {
+    // MODE_RUN: the activation blocks this thread quantizes, loaded first so
+    // that waiting for them does not wait for the weight loads issued next.
+    const int64_t nblk = (int64_t)M * (K / 16);
+    float xv[BPT][16];
+    bool xok[BPT];
+    if (MODE == MODE_RUN) {
+      // unconditional loads (index clamped): a branch here would make the
+      // compiler wait for them before issuing the weight loads below
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        const int64_t b = threadIdx.x + (int64_t)q * blockDim.x;
+        xok[q] = b < nblk;
+        load_block16<XBF16>(args.x, xok[q] ? b : nblk - 1, xv[q]);
+      }
+    }
+
+    // first weight group of this wave
+    int cg = wave;
+    uint4 wb0[S], wb1[S];
+    uint2 wsb[S];
+    load_w_group<S, FAST>(wrow, wsrow, cg, nsc, j, cbytes, sbytes, wb0, wb1, wsb);
+
+    float gsa_v;
+    if (MODE == MODE_RUN) {
+      float m = 0.f;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q)
+        if (xok[q]) m = fmaxf(m, block_absmax16(xv[q]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) amax_red[wave] = m;
+      lds_barrier();
+      float mm = 0.f;
+      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, amax_red[w]);
+      gsa_v = gsa_from_amax(mm);
+      const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        const int64_t b = threadIdx.x + (int64_t)q * blockDim.x;
+        if (xok[q]) {
+          uint32_t lo, hi, sf;
+          quantize_vals16(xv[q], gsa_v, lo, hi, sf);
+          ((uint2*)act_lds)[b] = make_uint2(lo, hi);
+          act_lds[(size_t)M * cbytes + b] = (uint8_t)sf;
+          if (writer) {
+            ((uint2*)args.codes_out)[b] = make_uint2(lo, hi);
+            args.scales_out[b] = (uint8_t)sf;
+          }
+        }
+      }
+      if (writer && threadIdx.x == 0) args.gsa_out[0] = gsa_v;
+      lds_barrier();
+    } else {
+      gsa_v = args.gsa[0];
+    }
+    const float gscale = gsa_v * args.ws2[g];
+
+    // activation rows of this pass
     const uint8_t* ac[MP];
     const uint8_t* as[MP];
     bool aok[MP], sok[MP];
@@ -144,54 +249,85 @@ __global__ __launch_bounds__(NW * 64) void gemv_fp4_kernel(
       aok[p] = a_has && ra < r_end;
       sok[p] = rc < r_end;
       int64_t rowa = ra < r_end ? ra : r0, rowc = rc < r_end ? rc : r0;
-      if (GROUPED && row_index != nullptr) {
-        rowa = row_index[rowa];
-        rowc = row_index[rowc];
+      if (MODE == MODE_GROUPED && args.row_index != nullptr) {
+        rowa = args.row_index[rowa];
+        rowc = args.row_index[rowc];
         // an index outside the activation rows reads nothing (its row is
         // not written either)
-        if (rowa < 0 || rowa >= a_rows) { rowa = 0; aok[p] = false; }
-        if (rowc < 0 || rowc >= a_rows) { rowc = 0; sok[p] = false; }
+        if (rowa < 0 || rowa >= args.a_rows) {
+          rowa = 0;
+          aok[p] = false;
+        }
+        if (rowc < 0 || rowc >= args.a_rows) {
+          rowc = 0;
+          sok[p] = false;
+        }
       }
-      ac[p] = a_codes + rowa * cbytes;
-      as[p] = a_scales + rowc * sbytes;
+      if (MODE == MODE_RUN) {
+        ac[p] = lds_codes + rowa * cbytes;
+        as[p] = lds_scales + rowc * sbytes;
+      } else {
+        ac[p] = args.a_codes + rowa * cbytes;
+        as[p] = args.a_scales + rowc * sbytes;
+      }
     }
+
     float acc[MP];
 #pragma unroll
     for (int p = 0; p < MP; ++p) acc[p] = 0.f;
 
-    for (int c = wave; c < nsc; c += NW) {
-      const int64_t boff = (int64_t)c * 128 + 32 * j;
-      const int64_t soff = (int64_t)c * 16 + 8 * (j & 1);
-      uint4 w0, w1;
-      load32<FAST>(wrow, boff, cbytes, true, w0, w1);
-      const uint2 sw = load8<FAST>(wsrow, soff, sbytes, true);
-      const v8i B0 = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, 0, 0, 0, 0};
-      const v8i B1 = {(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w, 0, 0, 0, 0};
-      float fw[8];
-      fp8x8_to_f32(sw, fw);
+    while (cg * S < nsc) {  // wave-uniform
 #pragma unroll
       for (int p = 0; p < MP; ++p) {
         if (r0 + 2 * p >= r_end) break;  // uniform
-        uint4 a0, a1;
-        load32<FAST>(ac[p], boff, cbytes, aok[p], a0, a1);
-        const v8i A0 = a_half == 0 ? v8i{(int)a0.x, (int)a0.y, 0, 0, 0, 0, 0, 0}
-                                   : v8i{0, 0, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
-        const v8i A1 = a_half == 0 ? v8i{(int)a1.x, (int)a1.y, 0, 0, 0, 0, 0, 0}
-                                   : v8i{0, 0, (int)a1.z, (int)a1.w, 0, 0, 0, 0};
-        const uint2 sa = load8<FAST>(as[p], soff, sbytes, sok[p]);
-        float fa[8];
-        fp8x8_to_f32(sa, fa);
-        const float4_t c0 = mfma_fp4(A0, B0);
-        const float4_t c1 = mfma_fp4(A1, B1);
+        uint4 a0[S], a1[S];
+        uint2 sa[S];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t0 = 4 * (r >> 1) + (r & 1);  // scale byte for MFMA 0
-          const int t1 = t0 + 2;                  // and for MFMA 1
-          acc[p] = fmaf(c0[r], fa[t0] * fw[t0], acc[p]);
-          acc[p] = fmaf(c1[r], fa[t1] * fw[t1], acc[p]);
+        for (int s = 0; s < S; ++s) {
+          const int c = cg * S + s;
+          const bool ok = c < nsc;
+          const int64_t boff = (int64_t)c * 128 + 32 * j;
+          const int64_t soff = (int64_t)c * 16 + 8 * (j & 1);
+          if (MODE == MODE_RUN) {  // LDS, K % 256 == 0
+            if (aok[p] && ok) {
+              a0[s] = *(const uint4*)(ac[p] + boff);
+              a1[s] = *(const uint4*)(ac[p] + boff + 16);
+            } else {
+              a0[s] = a1[s] = make_uint4(0u, 0u, 0u, 0u);
+            }
+            sa[s] = (sok[p] && ok) ? *(const uint2*)(as[p] + soff) : make_uint2(0u, 0u);
+          } else {
+            load32<FAST>(ac[p], boff, cbytes, aok[p] && ok, a0[s], a1[s]);
+            sa[s] = load8<FAST>(as[p], soff, sbytes, sok[p] && ok);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          if (cg * S + s >= nsc) break;  // wave-uniform: past the last chunk
+          const v8i A0 = a_half == 0 ? v8i{(int)a0[s].x, (int)a0[s].y, 0, 0, 0, 0, 0, 0}
+                                     : v8i{0, 0, (int)a0[s].z, (int)a0[s].w, 0, 0, 0, 0};
+          const v8i A1 = a_half == 0 ? v8i{(int)a1[s].x, (int)a1[s].y, 0, 0, 0, 0, 0, 0}
+                                     : v8i{0, 0, (int)a1[s].z, (int)a1[s].w, 0, 0, 0, 0};
+          const v8i B0 = {(int)wb0[s].x, (int)wb0[s].y, (int)wb0[s].z, (int)wb0[s].w, 0, 0, 0, 0};
+          const v8i B1 = {(int)wb1[s].x, (int)wb1[s].y, (int)wb1[s].z, (int)wb1[s].w, 0, 0, 0, 0};
+          float fa[8], fw[8];
+          fp8x8_to_f32(sa[s], fa);
+          fp8x8_to_f32(wsb[s], fw);
+          const float4_t c0 = mfma_fp4(A0, B0);
+          const float4_t c1 = mfma_fp4(A1, B1);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t0 = 4 * (r >> 1) + (r & 1);  // scale byte for MFMA 0
+            const int t1 = t0 + 2;                  // and for MFMA 1
+            acc[p] = fmaf(c0[r], fa[t0] * fw[t0], acc[p]);
+            acc[p] = fmaf(c1[r], fa[t1] * fw[t1], acc[p]);
+          }
         }
       }
+      cg += NW;
+      if (cg * S < nsc) load_w_group<S, FAST>(wrow, wsrow, cg, nsc, j, cbytes, sbytes, wb0, wb1, wsb);
     }
+
     // lanes of slices j and j^1 hold the same (row, column): add them
 #pragma unroll
     for (int p = 0; p < MP; ++p) {
@@ -199,20 +335,21 @@ __global__ __launch_bounds__(NW * 64) void gemv_fp4_kernel(
       if ((j & 1) == 0) red[wave][2 * p + c_mloc][col] = acc[p];
     }
     __syncthreads();
-    if (threadIdx.x < ROWS * 16) {
-      const int rl = threadIdx.x >> 4, cc = threadIdx.x & 15;
+    // ROWS*16 outputs; the workgroup may have fewer threads (one wave for short K)
+    for (int e = threadIdx.x; e < ROWS * 16; e += blockDim.x) {
+      const int rl = e >> 4, cc = e & 15;
       float s = 0.f;
-#pragma unroll
       for (int w = 0; w < NW; ++w) s += red[w][rl][cc];
       const int r = r0 + rl, n = n0 + cc;
       bool ok = r < r_end && n < N;
-      if (GROUPED && row_index != nullptr && ok) ok = row_index[r] >= 0 && row_index[r] < a_rows;
+      if (MODE == MODE_GROUPED && args.row_index != nullptr && ok)
+        ok = args.row_index[r] >= 0 && args.row_index[r] < args.a_rows;
       if (ok) {
         const float v = s * gscale;
-        if (y_bf16)
-          ((uint16_t*)y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v);
+        if (args.y_bf16)
+          ((uint16_t*)args.y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v);
         else
-          ((float*)y)[(int64_t)r * N + n] = v;
+          ((float*)args.y)[(int64_t)r * N + n] = v;
       }
     }
     __syncthreads();
@@ -221,32 +358,53 @@ __global__ __launch_bounds__(NW * 64) void gemv_fp4_kernel(
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-template <bool GROUPED>
-static hipError_t launch_impl(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
-                              const int32_t* row_index, const int32_t* offsets, int G,
-                              const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                              void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
-                              int64_t a_rows, hipStream_t s) {
-  constexpr int NW = 4, MP = 8;
-  const bool fast = (K % 256 == 0) && aligned16(a_codes) && aligned16(a_scales) &&
-                    aligned16(w_codes) && aligned16(w_scales);
-  dim3 grid((unsigned)((N + 15) / 16), GROUPED ? (unsigned)G : 1u);
+constexpr int S_GROUP = 4;
+
+static int waves_for(int64_t K) {
+  const int64_t nsc = (K + 255) / 256;
+  int64_t nw = (nsc + S_GROUP - 1) / S_GROUP;
+  if (nw < 1) nw = 1;
+  if (nw > GEMV_MAX_WAVES) nw = GEMV_MAX_WAVES;
+  return (int)nw;
+}
+
+template <int MP, int MODE>
+static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hipStream_t s) {
   if (fast)
-    gemv_fp4_kernel<NW, MP, true, GROUPED><<<grid, NW * 64, 0, s>>>(
-        a_codes, a_scales, gsa, row_index, offsets, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0,
-        (int)M, (int)N, (int)K, (int)a_rows);
+    gemv_fp4_kernel<S_GROUP, MP, true, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
   else
-    gemv_fp4_kernel<NW, MP, false, GROUPED><<<grid, NW * 64, 0, s>>>(
-        a_codes, a_scales, gsa, row_index, offsets, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0,
-        (int)M, (int)N, (int)K, (int)a_rows);
+    gemv_fp4_kernel<S_GROUP, MP, false, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_rows(const GemvArgs& a, int64_t rows_per_pass, bool fast, dim3 grid,
+                              int nw, hipStream_t s) {
+  if (rows_per_pass <= 2) return launch_mp<1, MODE>(a, fast, grid, nw, s);
+  if (rows_per_pass <= 4) return launch_mp<2, MODE>(a, fast, grid, nw, s);
+  return launch_mp<8, MODE>(a, fast, grid, nw, s);
 }
 
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
                        void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  return launch_impl<false>(a_codes, a_scales, gsa, nullptr, nullptr, 1, w_codes, w_scales, ws2, y,
-                            y_bf16, M, N, K, M, s);
+  GemvArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.gsa = gsa;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.ws2 = ws2;
+  a.y = y;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.a_rows = (int)M;
+  const bool fast = (K % 256 == 0) && aligned16(a_codes) && aligned16(a_scales) &&
+                    aligned16(w_codes) && aligned16(w_scales);
+  dim3 grid((unsigned)((N + 15) / 16), 1u);
+  return launch_rows<MODE_PLAIN>(a, M, fast, grid, waves_for(K), s);
 }
 
 hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
@@ -254,8 +412,82 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
                                int G, int64_t M_total, const uint8_t* w_codes,
                                const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
                                int64_t N, int64_t K, hipStream_t s) {
-  return launch_impl<true>(a_codes, a_scales, gsa, row_index, offsets, G, w_codes, w_scales, ws2,
-                           y, y_bf16, M_total, N, K, a_rows, s);
+  GemvArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.gsa = gsa;
+  a.row_index = row_index;
+  a.offsets = offsets;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.ws2 = ws2;
+  a.y = y;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.M = (int)M_total;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.a_rows = (int)a_rows;
+  const bool fast = (K % 256 == 0) && aligned16(a_codes) && aligned16(a_scales) &&
+                    aligned16(w_codes) && aligned16(w_scales);
+  dim3 grid((unsigned)((N + 15) / 16), (unsigned)G);
+  // rows per pass from the mean group size (groups larger than a pass make
+  // more passes over the same weight tile, which then comes from L2)
+  const int64_t mean_rows = (M_total + G - 1) / G;
+  return launch_rows<MODE_GROUPED>(a, mean_rows <= 2 ? 4 : 2 * mean_rows, fast, grid,
+                                   waves_for(K), s);
+}
+
+bool gemv_run_supported(int64_t M, int64_t K, const void* x, const uint8_t* w_codes,
+                        const uint8_t* w_scales) {
+  const int64_t nblk = M * (K / 16);
+  return M >= 1 && M <= GEMV_RUN_MAX_M && K % 256 == 0 && nblk <= 2 * GEMV_MAX_WAVES * 64 &&
+         M * (K / 2 + K / 16) <= GEMV_RUN_MAX_LDS && aligned16(x) && aligned16(w_codes) &&
+         aligned16(w_scales);
+}
+
+template <int MP, bool XBF16, int BPT>
+static hipError_t launch_run_t(const GemvArgs& a, dim3 grid, int nw, size_t lds, hipStream_t s) {
+  gemv_fp4_kernel<S_GROUP, MP, true, MODE_RUN, XBF16, BPT><<<grid, nw * 64, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int MP>
+static hipError_t launch_run_mp(const GemvArgs& a, bool xbf16, int bpt, dim3 grid, int nw,
+                                size_t lds, hipStream_t s) {
+  if (xbf16)
+    return bpt == 1 ? launch_run_t<MP, true, 1>(a, grid, nw, lds, s)
+                    : launch_run_t<MP, true, 2>(a, grid, nw, lds, s);
+  return bpt == 1 ? launch_run_t<MP, false, 1>(a, grid, nw, lds, s)
+                  : launch_run_t<MP, false, 2>(a, grid, nw, lds, s);
+}
+
+hipError_t launch_gemv_run(const void* x, bool x_bf16, float* gsa, uint8_t* codes,
+                           uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                           const float* ws2, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
+                           hipStream_t s) {
+  GemvArgs a{};
+  a.x = x;
+  a.gsa_out = gsa;
+  a.codes_out = codes;
+  a.scales_out = scales;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.ws2 = ws2;
+  a.y = y;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.a_rows = (int)M;
+  const int64_t nblk = M * (K / 16);
+  int nw = waves_for(K);
+  while ((int64_t)nw * 64 * 2 < nblk && nw < GEMV_MAX_WAVES) ++nw;  // two blocks per thread at most
+  const int bpt = nblk <= (int64_t)nw * 64 ? 1 : 2;
+  const size_t lds = (size_t)(M * (K / 2 + K / 16));
+  dim3 grid((unsigned)((N + 15) / 16), 1u);
+  if (M <= 2) return launch_run_mp<1>(a, x_bf16, bpt, grid, nw, lds, s);
+  if (M <= 4) return launch_run_mp<2>(a, x_bf16, bpt, grid, nw, lds, s);
+  return launch_run_mp<8>(a, x_bf16, bpt, grid, nw, lds, s);
 }
 
 }  // namespace nvfp4

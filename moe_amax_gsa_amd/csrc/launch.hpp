@@ -35,6 +35,16 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
                                const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
                                int64_t N, int64_t K, hipStream_t s);
 
+// amax -> gsa -> quantize -> linear in one kernel for a few activation rows.
+constexpr int64_t GEMV_RUN_MAX_M = 16;
+constexpr int64_t GEMV_RUN_MAX_LDS = 65536;  // activation codes + scales held in LDS
+bool gemv_run_supported(int64_t M, int64_t K, const void* x, const uint8_t* w_codes,
+                        const uint8_t* w_scales);
+hipError_t launch_gemv_run(const void* x, bool x_bf16, float* gsa, uint8_t* codes,
+                           uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                           const float* ws2, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
+                           hipStream_t s);
+
 // Tiled GEMM for many rows (dequantize to f16, f16 matrix cores).
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,

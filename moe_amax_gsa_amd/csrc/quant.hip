@@ -23,47 +23,6 @@ namespace nvfp4 {
 constexpr int AMAX_THREADS = 256;
 constexpr int SMALL_THREADS = 1024;
 
-// |x| as an ordered integer: for non-negative finite floats the bit pattern
-// orders like the value, so the max over bits is the exact, order-free max.
-template <bool BF16>
-__device__ __forceinline__ uint32_t absbits_vec(uint4 v) {
-  uint32_t m;
-  if (BF16) {
-    uint32_t a = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
-    uint32_t b = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
-    uint32_t c = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
-    uint32_t d = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
-    m = max(max(a, b), max(c, d));
-  } else {
-    m = max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
-  }
-  return m;
-}
-
-template <bool BF16>
-__device__ uint32_t thread_absmax(const void* __restrict__ x, int64_t numel, int64_t tid,
-                                  int64_t nthreads) {
-  constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
-  const uint4* __restrict__ xv = (const uint4*)x;
-  const int64_t nvec = numel / EPV;
-  uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
-  int64_t i = tid;
-  for (; i + 3 * nthreads < nvec; i += 4 * nthreads) {
-    uint4 v0 = xv[i], v1 = xv[i + nthreads], v2 = xv[i + 2 * nthreads], v3 = xv[i + 3 * nthreads];
-    m0 = max(m0, absbits_vec<BF16>(v0));
-    m1 = max(m1, absbits_vec<BF16>(v1));
-    m2 = max(m2, absbits_vec<BF16>(v2));
-    m3 = max(m3, absbits_vec<BF16>(v3));
-  }
-  for (; i < nvec; i += nthreads) m0 = max(m0, absbits_vec<BF16>(xv[i]));
-  for (int64_t e = nvec * EPV + tid; e < numel; e += nthreads) {
-    uint32_t b = BF16 ? (uint32_t)((const uint16_t*)x)[e] & 0x7FFFu
-                      : ((const uint32_t*)x)[e] & 0x7FFFFFFFu;
-    m1 = max(m1, b);
-  }
-  return max(max(m0, m1), max(m2, m3));
-}
-
 // Block-wide max; every thread gets the result.
 template <int THREADS>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
@@ -76,13 +35,6 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
 #pragma unroll
   for (int w = 0; w < THREADS / 64; ++w) r = max(r, red[w]);
   return r;
-}
-
-template <bool BF16>
-__device__ __forceinline__ float gsa_from_bits(uint32_t bits) {
-  float amax = BF16 ? __uint_as_float(bits << 16) : __uint_as_float(bits);
-  if (!(amax >= 1e-8f)) amax = 1e-8f;
-  return amax / 2688.0f;  // 6 * 448
 }
 
 // Phase 1: one partial maximum per workgroup.
@@ -158,46 +110,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                                                        uint8_t* __restrict__ scales) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblk) return;
-  float v[16];
-  if (BF16) {
-    const uint4* p = (const uint4*)x + 2 * b;
-    uint4 u0 = p[0], u1 = p[1];
-    uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
-    const uint4* p = (const uint4*)x + 4 * b;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 u = p[i];
-      v[4 * i] = __uint_as_float(u.x);
-      v[4 * i + 1] = __uint_as_float(u.y);
-      v[4 * i + 2] = __uint_as_float(u.z);
-      v[4 * i + 3] = __uint_as_float(u.w);
-    }
-  }
-  const float gsa = gsa_p[0];
-  float bamax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, fabsf(v[i]));
-  const float six_gsa = gsa * 6.0f;
-  const float sf_raw = bamax / six_gsa;
-  const uint32_t sf = e4m3_encode(sf_raw);
-  const float sdec = e4m3_decode(sf);
-  const float sc = sdec * gsa;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t mag = sdec != 0.0f ? e2m1_magnitude(fabsf(v[i]) / sc) : 0u;
-    uint32_t code = ((__float_as_uint(v[i]) >> 31) << 3) | mag;
-    if (i < 8)
-      lo |= code << (4 * i);
-    else
-      hi |= code << (4 * (i - 8));
-  }
+  uint32_t lo, hi, sf;
+  quantize_block16<BF16>(x, b, gsa_p[0], lo, hi, sf);
   ((uint2*)codes)[b] = make_uint2(lo, hi);
   scales[b] = (uint8_t)sf;
 }

@@ -40,7 +40,7 @@ class Nvfp4Linear:
         self.max_tokens = max_tokens
         dev = self.device
         self.gsa = torch.zeros(1, dtype=torch.float32, device=dev)
-        nws = C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, max_tokens * self.K)
+        nws = C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, max_tokens, self.N, self.K)
         self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
         self.codes = torch.empty(max_tokens, self.K // 2, dtype=torch.uint8, device=dev)
         self.scales = torch.empty(max_tokens, self.K // 16, dtype=torch.uint8, device=dev)
@@ -59,9 +59,19 @@ class Nvfp4Linear:
         return y
 
     def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        """The three steps as three calls of the C ABI."""
         assert x.shape[0] <= self.max_tokens and x.shape[1] == self.K
         codes, scales, gsa = self.quantize(x, stream)
         return self.run_from_quantized(codes, scales, gsa, stream)
+
+    def run(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        """The same result through nvfp4_linear_run (one kernel for few rows)."""
+        M = x.shape[0]
+        assert M <= self.max_tokens and x.shape[1] == self.K
+        y = self.y[:M]
+        C.nvfp4_linear_run(x, self.gsa, self.codes[:M], self.scales[:M], self.w_codes,
+                           self.w_scales, self.ws2, y, self.ws, stream)
+        return y
 
     __call__ = forward
 

@@ -25,6 +25,7 @@ OP_AMAX_GSA = 0
 OP_QUANTIZE = 1
 OP_LINEAR = 2
 OP_GROUPED_LINEAR = 3
+OP_LINEAR_RUN = 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_amax_gsa_amd.build`")
@@ -48,6 +49,9 @@ lib.nvfp4_quantize_from_buffer.restype = _I
 lib.nvfp4_quantize_from_buffer.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P]
 lib.nvfp4_linear.restype = _I
 lib.nvfp4_linear.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_linear_run.restype = _I
+lib.nvfp4_linear_run.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ,
+                                 _P]
 lib.nvfp4_grouped_linear.restype = _I
 lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
                                      _I64, _I64, _P, _SZ, _P]
@@ -123,6 +127,20 @@ def nvfp4_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tenso
                             _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y), M, N, K, _ptr(ws),
                             0 if ws is None else ws.numel() * ws.element_size(),
                             _stream(stream)), "nvfp4_linear")
+
+
+def nvfp4_linear_run(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
+                     scales: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                     ws2: torch.Tensor, y: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """amax -> gsa -> quantize -> linear on x (M, K); writes gsa, codes, scales, y."""
+    M, K = x.shape
+    N = w_codes.shape[0]
+    _check(lib.nvfp4_linear_run(_ptr(x), _dtype(x), _ptr(gsa), _ptr(codes), _ptr(scales),
+                                _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y),
+                                M, N, K, _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream)), "nvfp4_linear_run")
 
 
 def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,

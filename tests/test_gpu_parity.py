@@ -231,6 +231,38 @@ def test_linear_deterministic(C):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+RUN_CASES = [
+    (1, 256, 64, "bf16"), (1, 7168, 1536, "bf16"), (1, 7168, 100, "fp32"), (2, 2048, 48, "bf16"),
+    (3, 4096, 40, "fp32"), (5, 512, 33, "bf16"), (16, 1024, 64, "bf16"),  # one kernel
+    (1, 272, 40, "bf16"), (4, 7168, 40, "bf16"), (20, 512, 64, "fp32"),    # separate kernels
+]
+
+
+@pytest.mark.parametrize("M,K,N,dtype", RUN_CASES)
+def test_linear_run_matches_the_three_steps(C, M, K, N, dtype):
+    """nvfp4_linear_run writes what amax_gsa + quantize_from_buffer + linear
+    write: gsa/codes/scales bit-exact with the oracle, y within 1e-3."""
+    say("linear_run", M, K, N, dtype)
+    inp = W.make_linear(M, K, N, seed=3 * M + K + N, x="outliers", sf=(0.125, 8.0), ws2=0.004)
+    xd = x_dev(inp.x, dtype)
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, N, K))
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    C.nvfp4_linear_run(xd, gsa, codes, scales, to_dev(inp.w_codes), to_dev(inp.w_scales),
+                       torch.tensor([inp.ws2], dtype=torch.float32, device=DEV), y, ws)
+    g = f32(gsa)
+    assert g == oracle.amax_gsa(x_host(inp.x, dtype))
+    oc, os_ = oracle.quantize(x_host(inp.x, dtype), g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    ref = oracle.linear(oc, os_, g, inp.w_codes, inp.w_scales, inp.ws2)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(yg))
+    assert rel_err(yg, ref) <= REL_TOL
+
+
 # ---------------------------------------------------------------- grouped / MoE
 def moe_small(**kw):
     base = dict(tokens=9, experts=6, topk=2, K1=256, N1=64, K2=32, N2=40, granularity=8,
@@ -387,18 +419,19 @@ def test_graph_capture_replays_match_eager(C):
     layer = Nvfp4Linear(to_dev(inp.w_codes), to_dev(inp.w_scales), inp.ws2, max_tokens=1)
     x = W.bf16_to_torch(inp.x, DEV)
     eager = layer(x).clone()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        layer(x)  # warm-up on the capture stream
-    torch.cuda.current_stream().wait_stream(s)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        out = layer(x)
-    for i in range(4):
-        layer.y.fill_(float("nan"))
-        layer.gsa.fill_(0.0)
-        _ = torch.randn(1000, device=DEV).sum()  # eager work between replays
-        graph.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(out, eager), i
+    for fn in [layer.forward, layer.run]:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(x)  # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            out = fn(x)
+        for i in range(4):
+            layer.y.fill_(float("nan"))
+            layer.gsa.fill_(0.0)
+            _ = torch.randn(1000, device=DEV).sum()  # eager work between replays
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), (fn.__name__, i)
