@@ -124,6 +124,11 @@ NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* 
     return NVFP4_ERR_ALIGN;
   const bool xbf = x_dtype == NVFP4_DTYPE_BF16, ybf = y_dtype == NVFP4_DTYPE_BF16;
   hipStream_t s = (hipStream_t)stream;
+  // decode shapes: one kernel, 4 weight rows per workgroup, every workgroup
+  // quantizes the activation itself
+  if (N > 0 && gemv_narrow_run_supported(M, K, x, w_codes, w_scales))
+    return launched(launch_narrow_run(x, xbf, gsa, codes, scales, w_codes, w_scales, ws2, y, ybf,
+                                      M, N, K, s));
   if (N > 0 && gemv_run_supported(M, K, x, w_codes, w_scales))
     return launched(launch_gemv_run(x, xbf, gsa, codes, scales, w_codes, w_scales, ws2, y, ybf, M,
                                     N, K, s));

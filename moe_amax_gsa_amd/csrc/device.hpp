@@ -49,13 +49,17 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 }
 
 // E2M1 magnitude index of q >= 0: nearest of {0,.5,1,1.5,2,3,4,6}, ties to
-// the even mantissa bit, beyond 6 -> 6.  Each comparison is one grid
-// midpoint; the strict/non-strict choice at a midpoint sends the tie to the
-// neighbour whose mantissa bit is 0.
+// the even mantissa bit, beyond 6 -> 6.  Below 1 the grid is uniform with
+// step 1/2, so the index is rint(2q) (0, 1 or 2; rint ties to even).  From
+// 1 up it is a float with one mantissa bit: round the fp32 mantissa to one
+// bit at bit 22 (ties to even), then index = 2 + 2*exponent + mantissa bit,
+// saturated at 7.  Equal to the midpoint-threshold form for every fp32 q >= 0.
 __device__ __forceinline__ uint32_t e2m1_magnitude(float q) {
-  return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
-         (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) +
-         (uint32_t)(q > 5.0f);
+  if (q < 1.0f) return (uint32_t)__builtin_rintf(q * 2.0f);
+  uint32_t u = __float_as_uint(q);
+  u += 0x1FFFFFu + ((u >> 22) & 1u);
+  const uint32_t mag = 2u + 2u * ((u >> 23) - 127u) + ((u >> 22) & 1u);
+  return mag < 7u ? mag : 7u;
 }
 
 // ---- wave64 reductions (DPP-friendly xor shuffles)
@@ -182,6 +186,85 @@ __device__ __forceinline__ void quantize_vals16(const float v[16], float gsa, ui
       lo |= code << (4 * i);
     else
       hi |= code << (4 * (i - 8));
+  }
+}
+
+// Half-block layout: thread h owns elements 8h .. 8h+7 (one 16-byte bf16
+// load); half-blocks 2b and 2b+1 form block b and sit in adjacent lanes.
+template <bool BF16>
+__device__ __forceinline__ void load_half8(const void* __restrict__ x, int64_t h, float v[8]) {
+  if (BF16) {
+    const uint4 u = ((const uint4*)x)[h];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const uint4* p = (const uint4*)x + 2 * h;
+    const uint4 a = p[0], b = p[1];
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+}
+
+// The same split in two steps: raw 16-byte words first (bf16: one word,
+// fp32: two), floats later -- so that a kernel can issue other loads
+// before it waits for these.
+template <bool BF16>
+__device__ __forceinline__ void load_half8_raw(const void* __restrict__ x, int64_t h, uint4 r[2]) {
+  if (BF16) {
+    r[0] = ((const uint4*)x)[h];
+    r[1] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    const uint4* p = (const uint4*)x + 2 * h;
+    r[0] = p[0];
+    r[1] = p[1];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack_half8(const uint4 r[2], float v[8]) {
+  if (BF16) {
+    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    v[0] = __uint_as_float(r[0].x); v[1] = __uint_as_float(r[0].y);
+    v[2] = __uint_as_float(r[0].z); v[3] = __uint_as_float(r[0].w);
+    v[4] = __uint_as_float(r[1].x); v[5] = __uint_as_float(r[1].y);
+    v[6] = __uint_as_float(r[1].z); v[7] = __uint_as_float(r[1].w);
+  }
+}
+
+__device__ __forceinline__ float half_absmax8(const float v[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+// Codes of one half-block given its block's maximum: the same steps as
+// quantize_vals16 (both lanes of a block compute the same scale).
+__device__ __forceinline__ void quantize_half8(const float v[8], float bamax, float gsa,
+                                               uint32_t& codes, uint32_t& sf) {
+#pragma clang fp contract(off)
+  const float six_gsa = gsa * 6.0f;
+  const float sf_raw = bamax / six_gsa;
+  sf = e4m3_encode(sf_raw);
+  const float sdec = e4m3_decode(sf);
+  const float sc = sdec * gsa;
+  codes = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t mag = sdec != 0.0f ? e2m1_magnitude(fabsf(v[i]) / sc) : 0u;
+    codes |= (((__float_as_uint(v[i]) >> 31) << 3) | mag) << (4 * i);
   }
 }
 

@@ -124,6 +124,14 @@ __device__ __forceinline__ void fp8x8_to_f32(uint2 s, float f[8]) {
   f[7] = __builtin_amdgcn_cvt_f32_fp8((int)s.y, 3);
 }
 
+// Streaming 16-byte load: weights are read once per call, so they need not
+// stay in the vector L1.
+__device__ __forceinline__ uint4 ldg_nt16(const uint8_t* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Weight codes and scales of S super-chunks (group cg) for this lane.  FAST:
 // unconditional loads of a clamped, always valid chunk -- chunks past the
 // end are skipped by the (wave-uniform) compute loop.  A branch around the
@@ -136,7 +144,12 @@ __device__ __forceinline__ void load_w_group(const uint8_t* wrow, const uint8_t*
   for (int s = 0; s < S; ++s) {
     const int c = FAST ? min(cg * S + s, nsc - 1) : cg * S + s;
     const bool ok = FAST || c < nsc;
-    load32<FAST>(wrow, (int64_t)c * 128 + 32 * j, cbytes, ok, wb0[s], wb1[s]);
+    if (FAST) {
+      wb0[s] = ldg_nt16(wrow + (int64_t)c * 128 + 32 * j);
+      wb1[s] = ldg_nt16(wrow + (int64_t)c * 128 + 32 * j + 16);
+    } else {
+      load32<FAST>(wrow, (int64_t)c * 128 + 32 * j, cbytes, ok, wb0[s], wb1[s]);
+    }
     wsb[s] = load8<FAST>(wsrow, (int64_t)c * 16 + 8 * (j & 1), sbytes, ok);
   }
 }
@@ -195,6 +208,7 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
         xok[q] = b < nblk;
         load_block16<XBF16>(args.x, xok[q] ? b : nblk - 1, xv[q]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // activation loads before weight loads
     }
 
     // first weight group of this wave
@@ -356,6 +370,270 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
   }
 }
 
+// ---------------------------------------------------------------- narrow
+// Few activation rows and few weight rows per workgroup: 4 weight rows per
+// workgroup so that a decode-sized N spreads its weight stream over every
+// CU.  The K dimension is split four ways inside each MFMA: B column
+// n' = 4q + r holds weight row r at chunk 4*set + q (a "stream" q of 128
+// K-elements), A row i = 4q + t holds activation block 4h + t of the same
+// chunk in MFMA h (two MFMAs cover the chunk's 8 blocks), so result row
+// 4q + t against column 4q + r is the exact block sum S_b for row r; the
+// other 3/4 of the results are cross terms and are discarded (their scale
+// factor is 0).  Result lane l holds rows 4*(l/16) + t, t = 0..3, of column
+// l % 16: it is useful when l/16 == (l%16)/4, i.e. l = 20q + r.  A
+// 512-element set is 256 contiguous bytes per weight row.
+//
+// Memory order per workgroup: (RUN: the activation) -> the 4 rows' weight
+// scales and (otherwise) the activation rows, staged into LDS by coalesced
+// 16-byte loads -> each wave's weight codes for S sets.  Loads complete in
+// order, so staging waits only for the small loads issued before the codes.
+//
+// GROUPED: blockIdx.y is the group; its rows come from offsets[], their
+// activation rows from row_index[] (or identity), MR rows per pass.
+// RUN: the workgroup quantizes the whole (small) activation itself -- amax
+// over every element, gsa, codes and scales into LDS, HPT half-blocks per
+// thread -- while its weight loads are in flight.  No workgroup depends on
+// another; workgroup 0 also writes gsa, codes and scales out.
+template <int S, int MR, int MODE, bool XBF16, int HPT>
+__global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const GemvArgs args) {
+  constexpr bool RUN = MODE == MODE_RUN, GROUPED = MODE == MODE_GROUPED;
+  __shared__ float red[GEMV_MAX_WAVES][MR][4];
+  __shared__ float amax_red[GEMV_MAX_WAVES];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int NW = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, j = lane >> 4;
+  const int M = args.M, N = args.N, K = args.K;
+  const int n0 = blockIdx.x * 4;
+  const int g = GROUPED ? (int)blockIdx.y : 0;
+  int r_begin = 0, r_end = M;
+  if (GROUPED) {
+    r_begin = max(args.offsets[g], 0);
+    r_end = min(args.offsets[g + 1], M);
+    if (r_begin >= r_end) return;  // uniform over the workgroup
+  }
+  const int q = col >> 2, r = col & 3;  // B column: stream, weight row; A row: stream, slot
+  const bool useful = j == q;           // result rows of this lane are stream j
+  const int64_t cbytes = K / 2, sbytes = K / 16;
+  const int nch = K / 128;
+  const int nset = nch / 4;  // K % 512 == 0
+  const uint8_t* wbase = args.w_codes + (int64_t)g * N * cbytes;
+  const uint8_t* wsbase = args.w_scales + (int64_t)g * N * sbytes;
+  const uint8_t* wrow = wbase + (int64_t)min(n0 + r, N - 1) * cbytes;
+  // A row slot t = r carries block 4h + t of its chunk in MFMA h: slice 2h + t/2
+  const int dj = j - (r >> 1);
+  const bool a_has = dj == 0 || dj == 2;
+  const int a_h = dj >> 1, a_half = r & 1;
+
+  // LDS: weight scales of the 4 rows, then activation codes and scales
+  uint8_t* wsl = lds;                                   // [4][sbytes]
+  uint8_t* acl = lds + 4 * sbytes;                      // [rows][cbytes]
+  uint8_t* asl = acl + (int64_t)(RUN ? M : MR) * cbytes;  // [rows][sbytes]
+  uint8_t* trash = asl + (int64_t)(RUN ? M : MR) * sbytes;  // 16 bytes
+
+  const int64_t nhalf = (int64_t)M * (K / 8);
+  uint4 xr[HPT][2];
+  bool xok[HPT];
+  if (RUN) {
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+      const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
+      xok[u] = h < nhalf;
+      load_half8_raw<XBF16>(args.x, xok[u] ? h : 0, xr[u]);
+    }
+  }
+  float gsa_v = RUN ? 0.f : args.gsa[0];
+  bool quantized = !RUN;
+
+  for (int r0 = r_begin; r0 < r_end; r0 += MR) {
+    // activation rows of this pass (clamped to valid rows; flags mask them)
+    int64_t arow[MR];
+    bool mok[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const int rr = r0 + m;
+      mok[m] = rr < r_end;
+      int64_t ar = mok[m] ? rr : r0;
+      if (GROUPED && args.row_index != nullptr) {
+        ar = args.row_index[ar];
+        if (ar < 0 || ar >= args.a_rows) {
+          ar = 0;
+          mok[m] = false;
+        }
+      }
+      arow[m] = ar;
+    }
+    // staging loads: 16-byte pieces, one per thread while they last
+    const int ws16 = (int)(sbytes / 16);  // pieces per weight-scale row
+    const int nws = (r0 == r_begin) ? 4 * ws16 : 0;  // weight scales once
+    const int ac16 = (int)(cbytes / 16), as16 = (int)(sbytes / 16);
+    const int nac = RUN ? 0 : MR * ac16, nas = RUN ? 0 : MR * as16;
+    const int nstage = nws + nac + nas;
+    // Four staging pieces per thread (the host keeps nstage <= 4 * threads).
+    // Addresses are selected, not branched on, and every load is issued (a
+    // valid dummy address when the piece does not exist): a branch around a
+    // load makes the compiler wait for it before the next one.
+    auto src_of = [&](int p) -> const uint8_t* {
+      const int wr = (p >= ws16) + (p >= 2 * ws16) + (p >= 3 * ws16);  // p / ws16 for p < 4*ws16
+      const uint8_t* src_w =
+          wsbase + (int64_t)min(n0 + wr, N - 1) * sbytes + (int64_t)(p - wr * ws16) * 16;
+      const uint8_t* src = (p < nws) ? src_w : wsbase;
+      if (!RUN) {
+        const int pa = p - nws, ps = p - nws - nac;
+        int ma = 0, ms = 0;
+#pragma unroll
+        for (int m = 1; m < MR; ++m) {
+          ma += pa >= m * ac16;
+          ms += ps >= m * as16;
+        }
+        int64_t rowa = arow[0], rows_ = arow[0];
+#pragma unroll
+        for (int m = 1; m < MR; ++m) {
+          rowa = ma == m ? arow[m] : rowa;
+          rows_ = ms == m ? arow[m] : rows_;
+        }
+        const uint8_t* src_a = args.a_codes + rowa * cbytes + (int64_t)(pa - ma * ac16) * 16;
+        const uint8_t* src_s = args.a_scales + rows_ * sbytes + (int64_t)(ps - ms * as16) * 16;
+        src = (p >= nws && p < nws + nac) ? src_a : src;
+        src = (p >= nws + nac && p < nstage) ? src_s : src;
+      }
+      return src;
+    };
+    const int tid = threadIdx.x, bd = blockDim.x;
+    const uint4 st0 = *(const uint4*)src_of(tid);
+    const uint4 st1 = *(const uint4*)src_of(tid + bd);
+    const uint4 st2 = *(const uint4*)src_of(tid + 2 * bd);
+    const uint4 st3 = *(const uint4*)src_of(tid + 3 * bd);
+    __builtin_amdgcn_sched_barrier(0);
+
+    int sg = wave;
+    uint4 wv[S];
+    auto load_group = [&](int gg) {
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) {  // unconditional loads of clamped sets
+        const int set = min(gg * S + s2, nset - 1);
+        wv[s2] = ldg_nt16(wrow + (int64_t)(4 * set + q) * 64 + 16 * j);
+      }
+    };
+    load_group(sg);
+
+    // unconditional stores: pieces that do not exist go to a trash slot
+    auto dst_of = [&](int p) -> uint8_t* {
+      uint8_t* dst = p < nws ? wsl + p * 16
+                             : (p < nws + nac ? acl + (p - nws) * 16 : asl + (p - nws - nac) * 16);
+      return p < nstage ? dst : trash;
+    };
+    *(uint4*)dst_of(tid) = st0;
+    *(uint4*)dst_of(tid + bd) = st1;
+    *(uint4*)dst_of(tid + 2 * bd) = st2;
+    *(uint4*)dst_of(tid + 3 * bd) = st3;
+
+    if (!quantized) {  // RUN: quantize the activation into LDS
+      float xv[HPT][8];
+#pragma unroll
+      for (int u = 0; u < HPT; ++u) unpack_half8<XBF16>(xr[u], xv[u]);
+      float m = 0.f;
+#pragma unroll
+      for (int u = 0; u < HPT; ++u)
+        if (xok[u]) m = fmaxf(m, half_absmax8(xv[u]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) amax_red[wave] = m;
+      lds_barrier();
+      float mm = 0.f;
+      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, amax_red[w]);
+      gsa_v = gsa_from_amax(mm);
+      const bool writer = blockIdx.x == 0;
+#pragma unroll
+      for (int u = 0; u < HPT; ++u) {
+        const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
+        float bm = xok[u] ? half_absmax8(xv[u]) : 0.f;
+        bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+        uint32_t c, sf;
+        quantize_half8(xv[u], bm, gsa_v, c, sf);
+        if (xok[u]) {
+          ((uint32_t*)acl)[h] = c;
+          if ((h & 1) == 0) asl[h >> 1] = (uint8_t)sf;
+          if (writer) {
+            ((uint32_t*)args.codes_out)[h] = c;
+            if ((h & 1) == 0) args.scales_out[h >> 1] = (uint8_t)sf;
+          }
+        }
+      }
+      if (writer && threadIdx.x == 0) args.gsa_out[0] = gsa_v;
+      quantized = true;
+    }
+    lds_barrier();
+
+    // LDS row of each activation row of the pass
+    const int64_t lrow0 = RUN ? r0 : 0;
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+
+    while (sg * S < nset) {  // wave-uniform
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int set = sg * S + s2;
+        if (set >= nset) break;  // wave-uniform
+        const v8i B = {(int)wv[s2].x, (int)wv[s2].y, (int)wv[s2].z, (int)wv[s2].w, 0, 0, 0, 0};
+        float fw[8];
+        fp8x8_to_f32(*(const uint2*)(wsl + r * sbytes + (4 * set + j) * 8), fw);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          if (r0 + m >= r_end) break;  // uniform
+          const uint8_t* ar = acl + (lrow0 + m) * cbytes;
+          const uint8_t* sr = asl + (lrow0 + m) * sbytes;
+          const uint4 a4 = (a_has && mok[m]) ? *(const uint4*)(ar + (4 * set + q) * 64 + 16 * j)
+                                            : make_uint4(0u, 0u, 0u, 0u);
+          const uint2 sa = (useful && mok[m]) ? *(const uint2*)(sr + (4 * set + j) * 8)
+                                             : make_uint2(0u, 0u);
+          const v8i Am = a_half == 0 ? v8i{(int)a4.x, (int)a4.y, 0, 0, 0, 0, 0, 0}
+                                     : v8i{0, 0, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
+          const v8i Z = {0, 0, 0, 0, 0, 0, 0, 0};
+          const float4_t c0 = mfma_fp4(a_h == 0 ? Am : Z, B);
+          const float4_t c1 = mfma_fp4(a_h == 1 ? Am : Z, B);
+          float fa[8];
+          fp8x8_to_f32(sa, fa);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            acc[m] = fmaf(c0[t], fa[t] * fw[t], acc[m]);
+            acc[m] = fmaf(c1[t], fa[4 + t] * fw[4 + t], acc[m]);
+          }
+        }
+      }
+      sg += NW;
+      if (sg * S < nset) load_group(sg);
+    }
+    // row r's partial sums sit in lanes 20q + r: gather them in lanes 0..3
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float v = useful ? acc[m] : 0.f;
+      const int src = 20 * (lane >> 2) + (lane & 3);  // lanes 0..15 read the 16 useful lanes
+      float t = __shfl(v, src & 63, 64);
+      t += __shfl_down(t, 4, 64);
+      t += __shfl_down(t, 8, 64);
+      if (lane < 4) red[wave][m][lane] = t;
+    }
+    __syncthreads();
+    const float gscale = gsa_v * args.ws2[g];
+    for (int e = threadIdx.x; e < MR * 4; e += blockDim.x) {
+      const int m = e >> 2, rr = e & 3;
+      float sum = 0.f;
+      for (int w = 0; w < NW; ++w) sum += red[w][m][rr];
+      const int row = r0 + m, n = n0 + rr;
+      if (row < r_end && mok[m] && n < N) {
+        const float v = sum * gscale;
+        if (args.y_bf16)
+          ((uint16_t*)args.y)[(int64_t)row * N + n] = (uint16_t)f32_to_bf16_rne(v);
+        else
+          ((float*)args.y)[(int64_t)row * N + n] = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int S_GROUP = 4;
@@ -385,6 +663,108 @@ static hipError_t launch_rows(const GemvArgs& a, int64_t rows_per_pass, bool fas
   return launch_mp<8, MODE>(a, fast, grid, nw, s);
 }
 
+constexpr int NARROW_S = 2;
+
+
+
+static int narrow_waves(int64_t K) {
+  const int64_t nset = K / 512;
+  int64_t nw = (nset + NARROW_S - 1) / NARROW_S;
+  return (int)(nw < 1 ? 1 : (nw > GEMV_MAX_WAVES ? GEMV_MAX_WAVES : nw));
+}
+
+// staging pieces (16 bytes) a workgroup of nw waves must hold, 4 per thread
+static bool narrow_stage_fits(int64_t K, int64_t rows, int nw) {
+  const int64_t pieces = 4 * (K / 256) + rows * (K / 32 + K / 256);
+  return pieces <= 4 * (int64_t)nw * 64;
+}
+
+static size_t narrow_lds(int64_t K, int64_t rows) {
+  return (size_t)(4 * (K / 16) + rows * (K / 2 + K / 16) + 16);  // + 16-byte trash slot
+}
+
+static int narrow_waves_for(int64_t K, int64_t rows) {
+  int nw = narrow_waves(K);
+  while (!narrow_stage_fits(K, rows, nw) && nw < GEMV_MAX_WAVES) ++nw;
+  return nw;
+}
+
+static hipError_t launch_narrow(const GemvArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.N + 3) / 4));
+  const int MR = a.M <= 1 ? 1 : (a.M <= 2 ? 2 : 4);
+  const int th = narrow_waves_for(a.K, MR) * 64;
+  const size_t lds = narrow_lds(a.K, MR);
+  if (MR == 1)
+    gemv_narrow_kernel<NARROW_S, 1, MODE_PLAIN, true, 1><<<grid, th, lds, s>>>(a);
+  else if (MR == 2)
+    gemv_narrow_kernel<NARROW_S, 2, MODE_PLAIN, true, 1><<<grid, th, lds, s>>>(a);
+  else
+    gemv_narrow_kernel<NARROW_S, 4, MODE_PLAIN, true, 1><<<grid, th, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+bool gemv_narrow_supported(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales) {
+  return M >= 1 && M <= 4 && K % 512 == 0 && K <= 16384 && aligned16(a_codes) &&
+         aligned16(a_scales) && aligned16(w_codes) && aligned16(w_scales) &&
+         narrow_stage_fits(K, 4, GEMV_MAX_WAVES);
+}
+
+// RUN mode: enough threads for at most 4 activation half-blocks each.
+bool gemv_narrow_run_supported(int64_t M, int64_t K, const void* x, const uint8_t* w_codes,
+                               const uint8_t* w_scales) {
+  return M >= 1 && M <= 4 && K % 512 == 0 && K <= 16384 &&
+         M * (K / 8) <= 4 * GEMV_MAX_WAVES * 64 && aligned16(x) && aligned16(w_codes) &&
+         aligned16(w_scales);
+}
+
+template <int MR, bool XBF16>
+static hipError_t launch_narrow_run_t(const GemvArgs& a, int nw, int hpt, size_t lds,
+                                      hipStream_t s) {
+  dim3 grid((unsigned)((a.N + 3) / 4));
+  if (hpt == 1)
+    gemv_narrow_kernel<NARROW_S, MR, MODE_RUN, XBF16, 1><<<grid, nw * 64, lds, s>>>(a);
+  else if (hpt == 2)
+    gemv_narrow_kernel<NARROW_S, MR, MODE_RUN, XBF16, 2><<<grid, nw * 64, lds, s>>>(a);
+  else
+    gemv_narrow_kernel<NARROW_S, MR, MODE_RUN, XBF16, 4><<<grid, nw * 64, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* codes,
+                             uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                             const float* ws2, void* y, bool y_bf16, int64_t M, int64_t N,
+                             int64_t K, hipStream_t s) {
+  GemvArgs a{};
+  a.x = x;
+  a.gsa_out = gsa;
+  a.codes_out = codes;
+  a.scales_out = scales;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.ws2 = ws2;
+  a.y = y;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.a_rows = (int)M;
+  const int64_t nhalf = M * (K / 8);
+  int nw = narrow_waves_for(K, 0);
+  while ((int64_t)nw * 64 * 4 < nhalf && nw < GEMV_MAX_WAVES) ++nw;
+  const int64_t per = ((int64_t)nw * 64);
+  const int hpt = nhalf <= per ? 1 : (nhalf <= 2 * per ? 2 : 4);
+  const size_t lds = narrow_lds(K, M);
+  if (x_bf16) {
+    if (M <= 1) return launch_narrow_run_t<1, true>(a, nw, hpt, lds, s);
+    if (M <= 2) return launch_narrow_run_t<2, true>(a, nw, hpt, lds, s);
+    return launch_narrow_run_t<4, true>(a, nw, hpt, lds, s);
+  }
+  if (M <= 1) return launch_narrow_run_t<1, false>(a, nw, hpt, lds, s);
+  if (M <= 2) return launch_narrow_run_t<2, false>(a, nw, hpt, lds, s);
+  return launch_narrow_run_t<4, false>(a, nw, hpt, lds, s);
+}
+
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
                        void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
@@ -401,6 +781,8 @@ hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   a.N = (int)N;
   a.K = (int)K;
   a.a_rows = (int)M;
+  if (gemv_narrow_supported(M, K, a_codes, a_scales, w_codes, w_scales))
+    return launch_narrow(a, s);
   const bool fast = (K % 256 == 0) && aligned16(a_codes) && aligned16(a_scales) &&
                     aligned16(w_codes) && aligned16(w_scales);
   dim3 grid((unsigned)((N + 15) / 16), 1u);
@@ -429,10 +811,10 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
   a.a_rows = (int)a_rows;
   const bool fast = (K % 256 == 0) && aligned16(a_codes) && aligned16(a_scales) &&
                     aligned16(w_codes) && aligned16(w_scales);
-  dim3 grid((unsigned)((N + 15) / 16), (unsigned)G);
   // rows per pass from the mean group size (groups larger than a pass make
   // more passes over the same weight tile, which then comes from L2)
   const int64_t mean_rows = (M_total + G - 1) / G;
+  dim3 grid((unsigned)((N + 15) / 16), (unsigned)G);
   return launch_rows<MODE_GROUPED>(a, mean_rows <= 2 ? 4 : 2 * mean_rows, fast, grid,
                                    waves_for(K), s);
 }

@@ -14,6 +14,11 @@ int amax_parts_for(int64_t numel);
 hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, void* ws,
                            hipStream_t s);
 
+// amax -> gsa -> quantize in one workgroup (at most 4096 blocks)
+bool amax_quantize_small_ok(int64_t M, int64_t K);
+hipError_t launch_amax_quantize_small(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
+                                      uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // quantize from a device gsa
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const float* gsa,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
@@ -44,6 +49,17 @@ hipError_t launch_gemv_run(const void* x, bool x_bf16, float* gsa, uint8_t* code
                            uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
                            const float* ws2, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                            hipStream_t s);
+
+// The narrow weight-streaming kernel handles these (4 weight rows per workgroup).
+bool gemv_narrow_supported(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales);
+
+bool gemv_narrow_run_supported(int64_t M, int64_t K, const void* x, const uint8_t* w_codes,
+                               const uint8_t* w_scales);
+hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* codes,
+                             uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                             const float* ws2, void* y, bool y_bf16, int64_t M, int64_t N,
+                             int64_t K, hipStream_t s);
 
 // Tiled GEMM for many rows (dequantize to f16, f16 matrix cores).
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,

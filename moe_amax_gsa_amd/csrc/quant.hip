@@ -100,32 +100,111 @@ hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, 
 }
 
 // ---------------------------------------------------------------- quantize
-// One thread per 16-element block.  Row-major (M, K) with K % 16 == 0 makes
-// block b of the flattened tensor start at element 16b, its codes at byte 8b
-// and its scale at byte b.
+// One thread per half-block (8 elements: one 16-byte bf16 load, so a wave
+// reads 1 KB contiguous); the two halves of a block are adjacent lanes and
+// exchange their maxima with one shuffle.  Row-major (M, K) with K % 16 == 0
+// makes half-block h start at element 8h, its 4 code bytes at byte 4h and
+// its block's scale at byte h/2.
 template <bool BF16>
-__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t nblk,
+__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t nhalf,
                                                        const float* __restrict__ gsa_p,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblk) return;
-  uint32_t lo, hi, sf;
-  quantize_block16<BF16>(x, b, gsa_p[0], lo, hi, sf);
-  ((uint2*)codes)[b] = make_uint2(lo, hi);
-  scales[b] = (uint8_t)sf;
+  const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = h < nhalf;  // nhalf is even, so both lanes of a block agree
+  float v[8];
+  load_half8<BF16>(x, ok ? h : 0, v);
+  const float gsa = gsa_p[0];
+  float m = half_absmax8(v);
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  uint32_t c, sf;
+  quantize_half8(v, m, gsa, c, sf);
+  if (ok) {
+    ((uint32_t*)codes)[h] = c;
+    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sf;
+  }
 }
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const float* gsa,
                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  const int64_t nblk = M * (K / 16);
-  if (nblk == 0) return hipSuccess;
-  const int64_t grid = (nblk + 255) / 256;
+  const int64_t nhalf = M * (K / 8);
+  if (nhalf == 0) return hipSuccess;
+  const int64_t grid = (nhalf + 255) / 256;
   if (bf16)
-    quantize_kernel<true><<<(unsigned)grid, 256, 0, s>>>(x, nblk, gsa, codes, scales);
+    quantize_kernel<true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales);
   else
-    quantize_kernel<false><<<(unsigned)grid, 256, 0, s>>>(x, nblk, gsa, codes, scales);
+    quantize_kernel<false><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- small
+// amax -> gsa -> quantize of a small tensor by ONE workgroup: the block
+// barrier then spans every element, so the maximum is complete before any
+// block is quantized.  Each thread holds HPT half-blocks in registers
+// between the two phases.
+template <bool BF16, int HPT>
+__global__ __launch_bounds__(SMALL_THREADS) void amax_quantize_small_kernel(
+    const void* __restrict__ x, int64_t nhalf, float* __restrict__ gsa_out,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ float red[SMALL_THREADS / 64];
+  float v[HPT][8];
+  bool ok[HPT];
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < HPT; ++q) {
+    const int64_t h = threadIdx.x + (int64_t)q * SMALL_THREADS;
+    ok[q] = h < nhalf;
+    load_half8<BF16>(x, ok[q] ? h : 0, v[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < HPT; ++q)
+    if (ok[q]) m = fmaxf(m, half_absmax8(v[q]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float mm = 0.f;
+#pragma unroll
+  for (int w = 0; w < SMALL_THREADS / 64; ++w) mm = fmaxf(mm, red[w]);
+  const float gsa = gsa_from_amax(mm);
+  if (threadIdx.x == 0) gsa_out[0] = gsa;
+#pragma unroll
+  for (int q = 0; q < HPT; ++q) {
+    const int64_t h = threadIdx.x + (int64_t)q * SMALL_THREADS;
+    float bm = ok[q] ? half_absmax8(v[q]) : 0.f;
+    bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+    uint32_t c, sf;
+    quantize_half8(v[q], bm, gsa, c, sf);
+    if (ok[q]) {
+      ((uint32_t*)codes)[h] = c;
+      if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sf;
+    }
+  }
+}
+
+bool amax_quantize_small_ok(int64_t M, int64_t K) {
+  return M * (K / 8) <= 8 * SMALL_THREADS;
+}
+
+template <bool BF16>
+static hipError_t launch_small_t(const void* x, int64_t nhalf, float* gsa, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s) {
+  if (nhalf <= SMALL_THREADS)
+    amax_quantize_small_kernel<BF16, 1><<<1, SMALL_THREADS, 0, s>>>(x, nhalf, gsa, codes, scales);
+  else if (nhalf <= 2 * SMALL_THREADS)
+    amax_quantize_small_kernel<BF16, 2><<<1, SMALL_THREADS, 0, s>>>(x, nhalf, gsa, codes, scales);
+  else if (nhalf <= 4 * SMALL_THREADS)
+    amax_quantize_small_kernel<BF16, 4><<<1, SMALL_THREADS, 0, s>>>(x, nhalf, gsa, codes, scales);
+  else
+    amax_quantize_small_kernel<BF16, 8><<<1, SMALL_THREADS, 0, s>>>(x, nhalf, gsa, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_quantize_small(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
+                                      uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t nhalf = M * (K / 8);
+  return bf16 ? launch_small_t<true>(x, nhalf, gsa, codes, scales, s)
+              : launch_small_t<false>(x, nhalf, gsa, codes, scales, s);
 }
 
 // ---------------------------------------------------------------- SwiGLU

@@ -177,6 +177,8 @@ def run_linear(C, inp: W.LinearInputs, y_dtype=torch.float32, dtype="bf16"):
 LINEAR_CASES = [
     (1, 16, 16), (1, 17, 48), (2, 40, 256), (3, 33, 272), (5, 130, 1024), (16, 64, 512),
     (17, 40, 256), (33, 130, 1040), (130, 300, 512), (129, 257, 2064), (256, 256, 7168),
+    (1, 7, 128), (2, 33, 384), (4, 130, 1152),                 # 16-row kernel, ragged K
+    (1, 7, 512), (2, 33, 1024), (4, 130, 2048), (3, 64, 7168),  # 4-row kernel
 ]
 
 
