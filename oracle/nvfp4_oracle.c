@@ -27,8 +27,8 @@
  *   [MOE]   README.md, "MoE kernel (FusedSwiGLUScaledGroupedGemmKernel)":
  *           granularity-8 interleaved L1 weights, even subtiles gate, odd up.
  *
- * Readings where the pages are silent are listed in the design doc; each function
- * below states the one it takes.
+ * Where the pages are silent, each function below states the reading it
+ * takes.
  *
  * Floating point: every float operation is a single IEEE binary32 operation,
  * correctly rounded (build with -O2 -fno-fast-math -ffp-contract=off), in
