@@ -53,13 +53,6 @@ __device__ __forceinline__ half2_t scale_pair2(uint32_t two) {
   return half2_t{f0, f1};
 }
 
-// Streaming 16-byte load (weights are read by few workgroups).
-__device__ __forceinline__ uint4 ldg_nt16_g(const uint8_t* p) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 __device__ __forceinline__ half2_t scale_pair(uint32_t byte) {
   const _Float16 f = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
   return half2_t{f, f};
@@ -169,98 +162,107 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(
       }
 }
 
-// ---------------------------------------------------------------- split-K
-// Workgroup tile (32*WM) x (32*WN), four waves that each compute the whole
-// tile over every fourth 64-element K step -- each wave then dequantizes
-// WM + WN fragments per WM*WN MFMAs (4 + 4 for 16 at 4 x 4), which keeps the
-// exact f16 dequantization within the VALU slots beside the matrix cores --
-// then an LDS reduction of the four partial tiles.  Codes and scales of the
-// next K step are loaded while the current one computes (two register sets,
-// the loop unrolled by two so that the sets are named, not indexed).
-template <int WM, int WN>
-struct FragSet {
-  uint4 ca[WM], cb[WN];
-  uint32_t sa[WM], sb[WN];
+// ------------------------------------------------------- LDS-staged tiles
+// Workgroup tile (32 WM) x (32 WN), four waves.  Codes and scales are staged
+// through LDS in 256-element K chunks: a chunk is one 128-byte line of codes
+// and 16 scale bytes per row, fetched whole (eight lanes per line) straight
+// into LDS, STAGES chunks in flight.  Each wave computes the whole tile over
+// 64-element step w of every chunk -- so a wave dequantizes WM + WN
+// fragments per WM * WN MFMAs -- and the four partial tiles are summed
+// through LDS at the end.  Code lines sit in LDS with their 16-byte pieces
+// rotated by the row (piece c of row r at slot c ^ (r & 7)), so the
+// MFMA-layout reads of eight consecutive rows hit eight different bank
+// groups.
+// 16 bytes per lane from base + voff straight into LDS at byte address
+// lds_wave_base + 16 * lane (base and lds_wave_base uniform over the wave).
+// Issued as inline assembly so that the compiler does not fence every later
+// LDS read behind it (it cannot tell the stages apart); the kernel waits
+// for these loads itself with explicit vmcnt counts.  M0 carries the LDS
+// address; the compiler reserves M0, so its value is saved and restored
+// here, and one wait state separates the M0 write from the load.
+__device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t voff,
+                                           uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_wave_base), "v"(voff), "s"(base)
+      : "memory");
+}
+
+// LDS byte address of a pointer into dynamic shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+template <int WM, int WN, int STAGES>
+struct LdsTile {
+  static constexpr int TM = 32 * WM, TN = 32 * WN, ROWS = TM + TN;
+  static constexpr int CODE_BYTES = ROWS * 128, SCALE_BYTES = ROWS * 16;
+  static constexpr int STAGE_BYTES = CODE_BYTES + SCALE_BYTES;
+  static constexpr int CODE_LOADS = ROWS / 32;         // 16-byte loads per lane per chunk
+  static constexpr int SCALE_WAVES = ROWS / 64;        // waves that fetch scales
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 };
 
-template <int WM, int WN>
-__device__ __forceinline__ void load_set(FragSet<WM, WN>& f, const uint8_t* __restrict__ a_codes,
-                                         const uint8_t* __restrict__ a_scales,
-                                         const uint8_t* __restrict__ w_codes,
-                                         const uint8_t* __restrict__ w_scales,
-                                         const uint32_t (&aoff)[WM], const uint32_t (&asoff)[WM],
-                                         const uint32_t (&boff)[WN], const uint32_t (&bsoff)[WN],
-                                         int ks, int h) {
-  const uint32_t co = (uint32_t)ks * 32 + 16 * h, so = (uint32_t)ks * 4 + 2 * h;
-#pragma unroll
-  for (int i = 0; i < WM; ++i) {
-    f.ca[i] = *(const uint4*)(a_codes + (aoff[i] + co));
-    f.sa[i] = *(const uint16_t*)(a_scales + (asoff[i] + so));
-  }
-#pragma unroll
-  for (int i = 0; i < WN; ++i) {
-    f.cb[i] = ldg_nt16_g(w_codes + (boff[i] + co));
-    f.sb[i] = *(const uint16_t*)(w_scales + (bsoff[i] + so));
-  }
-}
-
-template <int WM, int WN>
-__device__ __forceinline__ void compute_set(const FragSet<WM, WN>& f, f32x16 (&acc)[WM][WN]) {
-  half2_t sfa[WM], sfb[WN];
-#pragma unroll
-  for (int i = 0; i < WM; ++i) sfa[i] = scale_pair2(f.sa[i]);
-#pragma unroll
-  for (int i = 0; i < WN; ++i) sfb[i] = scale_pair2(f.sb[i]);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    half8_t A[WM], B[WN];
-#pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const uint32_t w = s == 0 ? f.ca[i].x : s == 1 ? f.ca[i].y : s == 2 ? f.ca[i].z : f.ca[i].w;
-      const _Float16 sc = s < 2 ? sfa[i][0] : sfa[i][1];
-      A[i] = dequant8(w, half2_t{sc, sc});
-    }
-#pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      const uint32_t w = s == 0 ? f.cb[i].x : s == 1 ? f.cb[i].y : s == 2 ? f.cb[i].z : f.cb[i].w;
-      const _Float16 sc = s < 2 ? sfb[i][0] : sfb[i][1];
-      B[i] = dequant8(w, half2_t{sc, sc});
-    }
-#pragma unroll
-    for (int a = 0; a < WM; ++a)
-#pragma unroll
-      for (int b = 0; b < WN; ++b) acc[a][b] = mfma_f16(A[a], B[b], acc[a][b]);
-    // one substep's operands live at a time
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-template <int WM, int WN, int WPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_splitk4_kernel(
+template <int WM, int WN, int STAGES, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
     int y_bf16, int M, int N, int K) {
-  constexpr int TM = 32 * WM, TN = 32 * WN, LDT = TN + 4;
-  extern __shared__ __attribute__((aligned(16))) float red[];  // [4 waves][16][LDT]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  using T = LdsTile<WM, WN, STAGES>;
+  constexpr int TM = T::TM, TN = T::TN, LDT = TN + 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, h = lane >> 5;
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
-  const int64_t cbytes = K / 2, sbytes = K / 16;
-  // 32-bit byte offsets of each fragment row (the host checks the sizes fit)
-  uint32_t aoff[WM], asoff[WM], boff[WN], bsoff[WN];
+  const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t cbytes = (uint32_t)K / 2, sbytes = (uint32_t)K / 16;
+  const int nch = K / 256;
+
+  // this lane's source offsets for its code loads: load i of wave w fills
+  // LDS rows 8(4i + w) .. +7, lane l the row 8(4i + w) + l/8, slot l % 8,
+  // which holds piece (l % 8) ^ (l / 8) of that row's line
+  uint32_t csrc[T::CODE_LOADS];
 #pragma unroll
-  for (int i = 0; i < WM; ++i) {
-    const uint32_t ra = (uint32_t)min(m0 + i * 32 + r32, M - 1);  // clamped: results discarded
-    aoff[i] = ra * (uint32_t)cbytes;
-    asoff[i] = ra * (uint32_t)sbytes;
+  for (int i = 0; i < T::CODE_LOADS; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    const uint32_t piece = (uint32_t)((lane & 7) ^ (lane >> 3));
+    if (row < TM) {
+      const uint32_t ra = (uint32_t)min(m0 + row, M - 1);  // clamped rows: results discarded
+      csrc[i] = ra * cbytes + piece * 16;
+    } else {
+      const uint32_t rb = (uint32_t)min(n0 + row - TM, N - 1);
+      csrc[i] = rb * cbytes + piece * 16;
+    }
   }
+  // scales: wave w < SCALE_WAVES fetches rows 64w + lane (16 bytes each);
+  // rows below TM are activation rows (TM is a multiple of 64)
+  static_assert(TM % 64 == 0, "scale rows of one wave must not straddle A and B");
+  const int srow = 64 * min(wave, T::SCALE_WAVES - 1) + lane;
+  const uint32_t ssrc = srow < TM ? (uint32_t)min(m0 + srow, M - 1) * sbytes
+                                  : (uint32_t)min(n0 + srow - TM, N - 1) * sbytes;
+
+  auto issue = [&](int chunk, int stage) {
+    const uint32_t st = smem_base + stage * T::STAGE_BYTES;
 #pragma unroll
-  for (int i = 0; i < WN; ++i) {
-    const uint32_t rb = (uint32_t)min(n0 + i * 32 + r32, N - 1);
-    boff[i] = rb * (uint32_t)cbytes;
-    bsoff[i] = rb * (uint32_t)sbytes;
-  }
+    for (int i = 0; i < T::CODE_LOADS; ++i) {
+      const uint8_t* base = (32 * i < TM) ? a_codes : w_codes;  // the same for the whole load
+      load_lds16(base, csrc[i] + (uint32_t)chunk * 128, st + 1024 * (4 * i + wave));
+    }
+    const uint32_t sdst = st + T::CODE_BYTES + 1024 * wave;
+    if (wave < TM / 64)
+      load_lds16(a_scales, ssrc + (uint32_t)chunk * 16, sdst);
+    else if (wave < T::SCALE_WAVES)
+      load_lds16(w_scales, ssrc + (uint32_t)chunk * 16, sdst);
+  };
+
   f32x16 acc[WM][WN];
 #pragma unroll
   for (int a = 0; a < WM; ++a)
@@ -269,26 +271,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // wave w takes K steps w, w + 4, ...: `mine` of them, in pairs and then
-  // an odd one, so the loop has a single exit and the accumulators stay put
-  const int nks = K / 64;
-  const int mine = wave < nks ? (nks - 1 - wave) / 4 + 1 : 0;
-  FragSet<WM, WN> X, Yb;
-  int ks = min(wave, nks - 1);
-  load_set<WM, WN>(X, a_codes, a_scales, w_codes, w_scales, aoff, asoff, boff, bsoff, ks, h);
-  for (int p = 0; p < mine / 2; ++p) {
-    load_set<WM, WN>(Yb, a_codes, a_scales, w_codes, w_scales, aoff, asoff, boff, bsoff,
-                     min(ks + 4, nks - 1), h);
-    compute_set<WM, WN>(X, acc);
-    load_set<WM, WN>(X, a_codes, a_scales, w_codes, w_scales, aoff, asoff, boff, bsoff,
-                     min(ks + 8, nks - 1), h);
-    compute_set<WM, WN>(Yb, acc);
-    ks += 8;
+  // LDS read offsets of this lane's fragments within a stage
+  const uint32_t piece = (uint32_t)(2 * wave + h);
+  const uint32_t slot = (piece ^ (uint32_t)(r32 & 7)) * 16;
+
+#pragma unroll
+  for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, nch - 1), s0);
+
+  for (int c = 0; c < nch; ++c) {
+    // chunks c+1 .. c+STAGES-2 may still be in flight (fewest loads per wave)
+    constexpr int PER_CHUNK = T::CODE_LOADS + (T::SCALE_WAVES == 4 ? 1 : 0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * PER_CHUNK) : "memory");
+    lds_barrier();
+    issue(min(c + STAGES - 1, nch - 1), (c + STAGES - 1) % STAGES);
+
+    const uint8_t* st = smem + (c % STAGES) * T::STAGE_BYTES;
+    uint4 fa[WM], fb[WN];
+    uint32_t sa[WM], sb[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int row = 32 * i + r32;
+      fa[i] = *(const uint4*)(st + row * 128 + slot);
+      sa[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * 16 + 4 * wave + 2 * h);
+    }
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int row = TM + 32 * i + r32;
+      fb[i] = *(const uint4*)(st + row * 128 + slot);
+      sb[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * 16 + 4 * wave + 2 * h);
+    }
+    half2_t sfa[WM], sfb[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) sfa[i] = scale_pair2(sa[i]);
+#pragma unroll
+    for (int i = 0; i < WN; ++i) sfb[i] = scale_pair2(sb[i]);
+    half8_t A[2][WM], B[2][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) A[0][i] = dequant8(fa[i].x, half2_t{sfa[i][0], sfa[i][0]});
+#pragma unroll
+    for (int i = 0; i < WN; ++i) B[0][i] = dequant8(fb[i].x, half2_t{sfb[i][0], sfb[i][0]});
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const int cur = sub & 1, nxt = cur ^ 1;
+      if (sub < 3) {
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          const uint32_t w = sub == 0 ? fa[i].y : sub == 1 ? fa[i].z : fa[i].w;
+          const _Float16 sc = sub == 0 ? sfa[i][0] : sfa[i][1];
+          A[nxt][i] = dequant8(w, half2_t{sc, sc});
+        }
+#pragma unroll
+        for (int i = 0; i < WN; ++i) {
+          const uint32_t w = sub == 0 ? fb[i].y : sub == 1 ? fb[i].z : fb[i].w;
+          const _Float16 sc = sub == 0 ? sfb[i][0] : sfb[i][1];
+          B[nxt][i] = dequant8(w, half2_t{sc, sc});
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b) acc[a][b] = mfma_f16(A[cur][a], B[cur][b], acc[a][b]);
+      if (sub < 3) {
+        // one MFMA, then a share of the next substep's dequantization
+#pragma unroll
+        for (int g = 0; g < WM * WN; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (8 * (WM + WN) + WM * WN - 1) / (WM * WN), 0);
+        }
+      }
+    }
   }
-  if (mine & 1) compute_set<WM, WN>(X, acc);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // reduce the four partial tiles one 16-row slab at a time (result
   // registers 8q..8q+7 of MFMA tile row a hold rows 32a + 16q + [0, 16))
+  float* red = (float*)smem;
   const float gscale = gsa_p[0] * ws2_p[0];
   float* slab = red + (size_t)wave * 16 * LDT;
 #pragma unroll
@@ -301,7 +359,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
         for (int r = 8 * q; r < 8 * q + 8; ++r)
           slab[(8 * ((r >> 2) & 1) + 4 * h + (r & 3)) * LDT + b * 32 + r32] = acc[a][b][r];
       __syncthreads();
-      // wave w sums rows [4w, 4w + 4) of the slab
       for (int e = lane; e < 4 * TN; e += 64) {
         const int rr = wave * 4 + e / TN, cc = e % TN;
         const float v = red[(0 * 16 + rr) * LDT + cc] + red[(1 * 16 + rr) * LDT + cc] +
@@ -320,16 +377,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   }
 }
 
-template <int WM, int WN, int WPE>
-hipError_t launch_splitk4(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
-                          const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                          void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  constexpr int TM = 32 * WM, TN = 32 * WN;
-  const size_t lds = (size_t)4 * 16 * (TN + 4) * sizeof(float);
-  const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
-  gemm_splitk4_kernel<WM, WN, WPE><<<grid, 256, lds, s>>>(a_codes, a_scales, gsa, w_codes,
-                                                          w_scales, ws2, y, y_bf16 ? 1 : 0,
-                                                          (int)M, (int)N, (int)K);
+template <int WM, int WN, int STAGES, int WPE>
+hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
+                      bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  using T = LdsTile<WM, WN, STAGES>;
+  static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM));
+  gemm_lds_kernel<WM, WN, STAGES, WPE><<<grid, 256, T::LDS_BYTES, s>>>(
+      a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -338,16 +398,11 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                        void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   const bool fast = (K % 64 == 0) && (((uintptr_t)a_codes | (uintptr_t)w_codes) & 15u) == 0 &&
                     (((uintptr_t)a_scales | (uintptr_t)w_scales) & 1u) == 0;
-  // split-K tiles address rows with 32-bit byte offsets
-  const bool big = fast && K >= 256 && M * (K / 2) < (1ll << 31) && N * (K / 2) < (1ll << 31);
-  if (big) {
-    const int64_t tiles44 = ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles44 >= 512)
-      return launch_splitk4<4, 4, 1>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M,
-                                     N, K, s);
-    return launch_splitk4<4, 2, 2>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M,
-                                   N, K, s);
-  }
+  // the staged kernel takes whole 256-element chunks and 32-bit row offsets
+  const bool big = fast && K % 256 == 0 && K >= 256 && M * (K / 2) < (1ll << 31) && N * (K / 2) < (1ll << 31);
+  if (big)  // 128 x 64 tiles, two workgroups per CU, two stages
+    return launch_lds<4, 2, 2, 2>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M, N,
+                                  K, s);
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
   if (fast)
     gemm_f16_kernel<true><<<grid, 256, 0, s>>>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,

@@ -179,6 +179,7 @@ LINEAR_CASES = [
     (17, 40, 256), (33, 130, 1040), (130, 300, 512), (129, 257, 2064), (256, 256, 7168),
     (1, 7, 128), (2, 33, 384), (4, 130, 1152),                 # 16-row kernel, ragged K
     (1, 7, 512), (2, 33, 1024), (4, 130, 2048), (3, 64, 7168),  # 4-row kernel
+    (128, 64, 256), (200, 100, 768), (129, 65, 1280), (600, 333, 1536),  # LDS-staged tiles
 ]
 
 
