@@ -19,17 +19,24 @@ step (weight codes + weight scales + bf16 activation + activation codes and
 scales + fp32 output) / step time.  The same step as three ABI calls and the
 other workloads are reported under "workloads".
 
-roofline: the dominant kernel's duration measured with events around each
-launch, queued behind a bounded spin kernel so that the host never gaps the
-GPU between them.
+roofline: the dominant kernel's average duration, from events around a
+graph of K back-to-back launches of that kernel alone (at M=1 the whole step
+is that one kernel).  traffic: HBM bytes per launch from the rocprofv3
+FETCH_SIZE and WRITE_SIZE summary kept under profiles/, scaled by what the
+same counters read for a copy of known size; reported only while the kernel
+sources still hash to the value recorded there.
+
+    python bench.py --pmc-probe     (the program those counter runs profile)
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,6 +60,8 @@ def parse():
     p.add_argument("--only", default=None, help="extra workload to run (default: all)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
+    p.add_argument("--pmc-probe", action="store_true",
+                   help="run only a 256 MiB copy and the headline kernel (for counter runs)")
     return p.parse_args()
 
 
@@ -84,44 +93,40 @@ def graph_ms_per_step(step, steps: int, warmup: int) -> float:
     return a.elapsed_time(b) / steps
 
 
-_SPIN_CYCLES_PER_MS = None
-
-
-def _spin_cycles_per_ms() -> float:
-    global _SPIN_CYCLES_PER_MS
-    if _SPIN_CYCLES_PER_MS is None:
-        n = 1_000_000
-        torch.cuda._sleep(n)  # warm-up
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        torch.cuda._sleep(n)
-        b.record()
-        torch.cuda.synchronize()
-        _SPIN_CYCLES_PER_MS = n / max(a.elapsed_time(b), 1e-3)
-    return _SPIN_CYCLES_PER_MS
-
-
 def kernel_us(launch, iters: int, pre=None) -> float:
-    """Mean duration of launch(i), from events recorded on the launch stream
-    around each launch.  A bounded spin kernel (torch.cuda._sleep) holds the
-    GPU while the host enqueues everything, so the launches run back to back
-    and each event pair brackets one kernel."""
+    """Average duration of launch(i) alone: `iters` launches captured back to
+    back in a graph (after pre(0), which prepares the inputs), replayed once
+    untimed and once between events on the replay stream."""
     if pre is not None:
         pre(0)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    torch.cuda._sleep(int(_spin_cycles_per_ms() * (2.0 + 0.1 * iters)))
-    for i in range(iters):
-        if pre is not None:
-            pre(i)
-        evs[i][0].record()
-        launch(i)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    return 1e3 * sum(x.elapsed_time(y) for x, y in evs) / iters
+    return 1e3 * graph_ms_per_step(launch, iters, 2)
+
+
+KERNEL_SOURCES = ["device.hpp", "launch.hpp", "api.hip", "gemv.hip", "gemm.hip", "quant.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "moe_amax_gsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(path: str):
+    """Bytes per launch recorded by the counter runs, or None when the file
+    is missing or the kernel sources changed since the counters were taken."""
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 # ------------------------------------------------------------------ linear
@@ -180,7 +185,6 @@ def bench_linear(C, name, dev, steps, warmup, kiters):
     r["step_us"] = 1e3 * graph_ms_per_step(b.run, steps, warmup)
     r["step3_us"] = 1e3 * graph_ms_per_step(b.step3, steps, warmup)
     r["linear_us"] = kernel_us(b.linear, kiters, pre=b.quantize)
-    r["run_us"] = kernel_us(b.run, kiters)
     r["quant_us"] = kernel_us(lambda i: b.quantize(), kiters)
     r["step_GBps"] = b.step_bytes / (r["step_us"] * 1e-6) / 1e9
     r["step_TFLOPs"] = b.flops / (r["step_us"] * 1e-6) / 1e12
@@ -237,6 +241,26 @@ def cpu_baseline(inp, budget_s=12.0):
     return el / n, n, int(os.environ["OMP_NUM_THREADS"])
 
 
+# ------------------------------------------------------------------ probe
+def pmc_probe(C, dev, launches=20):
+    """A 256 MiB device copy (three times, to calibrate the byte counters),
+    then `launches` launches of the headline step on rotated weights."""
+    from moe_amax_gsa_amd import workloads as W
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    b = LinearBench(C, W.make(HEAD), dev)
+    for i in range(launches):
+        b.run(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": HEAD, "copy_bytes": src.numel(), "copies": 3,
+                      "launches": launches, "bytes_per_launch": b.step_bytes,
+                      "source_hash": kernel_source_hash()}))
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -247,6 +271,9 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     from moe_amax_gsa_amd import nvfp4 as C
     dev = torch.device("cuda:0")
+    if args.pmc_probe:
+        pmc_probe(C, dev)
+        return
     kiters = 50
 
     log("headline", HEAD)
@@ -275,7 +302,11 @@ def main():
                "sample": f"{nrep} whole oracle steps (amax, quantize, FP64 linear) of {HEAD}, "
                          f"{per_step_s * 1e3:.1f} ms each"}
 
-    run_gbps = b.step_bytes / (r["run_us"] * 1e-6) / 1e9
+    # at M=1 the step is one launch of the fused kernel: its average
+    # duration is the step time of the graph of K launches
+    kern_us = r["step_us"]
+    run_gbps = b.step_bytes / (kern_us * 1e-6) / 1e9
+    traffic = recorded_traffic(os.path.join(ROOT, "profiles", "traffic_gemv_narrow_run_decode_m1_k7168_n1536.md"))
     line = {
         "metric": "NVFP4 linear decode weight-stream GB/s (M=1, K=7168, N=1536)",
         "value": r["step_GBps"],
@@ -287,15 +318,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1 x e2m1, e4m3 block scales, f32 accumulate",
+        "dtype": "e2m1 codes with e4m3 block scales, exact f16 operands, f32 accumulate",
         "data": "synthetic, seeded",
         "config": {"workload": HEAD, "M": 1, "K": 7168, "N": 1536,
                    "step": "nvfp4_linear_run (amax, gsa, quantize, linear)",
                    "bytes_per_step": b.step_bytes},
         "roofline": {"bound": "hbm", "achieved": run_gbps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": run_gbps / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gemv_fp4_kernel (fused run mode)", "kernel_us": r["run_us"],
-                     "bytes_per_launch": b.step_bytes},
+                     "frac": run_gbps / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gemv_narrow_kernel, run mode (amax, gsa, quantize and linear "
+                               "for one activation row in one launch)",
+                     "kernel_us": kern_us, "bytes_per_launch": b.step_bytes},
         "cpu_baseline": cpu,
         "workloads": workloads,
         "context": "the pages' whole-model decode on B200 took about 1.45 s per token "
