@@ -128,15 +128,17 @@ int nvfp4_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *g
  * same results as calling nvfp4_amax_gsa, nvfp4_quantize_from_buffer and
  * nvfp4_linear in turn -- gsa, codes (M, K/2) and scales (M, K/16) are
  * written as those calls would write them, and y (M, N).
- * For up to 4 rows (K % 128 == 0, 16-byte aligned buffers) it is two
- * kernels: one workgroup computes amax, gsa and the quantization (its block
- * barrier spans the whole tensor), then the weight-streaming kernel.  For up
- * to 16 rows (K % 256 == 0, M*K <= 16384) it is ONE kernel: every workgroup
- * reads the whole activation, computes its exact maximum by itself (no
- * reduction across workgroups, so no workgroup waits on another), quantizes
- * it into LDS and streams its weight rows.  Otherwise the separate kernels
- * run in order (then ws must hold nvfp4_workspace_bytes(
- * NVFP4_OP_LINEAR_RUN, M, N, K, 1) bytes).
+ * When x, w_codes and w_scales are 16-byte aligned it is ONE kernel for
+ *   - up to 4 rows with K % 512 == 0, K <= 16384 and M*K <= 16384 (4 weight
+ *     rows per workgroup), or
+ *   - up to 16 rows with K % 256 == 0, M*K/16 <= 1024 and
+ *     M*(K/2 + K/16) <= 65536 (16 weight rows per workgroup):
+ * every workgroup reads the whole activation, computes its exact maximum by
+ * itself (no reduction across workgroups, so no workgroup waits on
+ * another), quantizes it into LDS and streams its weight rows; workgroup 0
+ * also writes gsa, codes and scales.  Otherwise the separate kernels run in
+ * order (then ws must hold nvfp4_workspace_bytes(NVFP4_OP_LINEAR_RUN, M, N,
+ * K, 1) bytes).
  * N == 0 only quantizes. */
 int nvfp4_linear_run(const void *x, int x_dtype, float *gsa, uint8_t *codes, uint8_t *scales,
                      const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2, void *y,
