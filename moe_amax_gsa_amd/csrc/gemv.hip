@@ -383,58 +383,55 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
 // l % 16: it is useful when l/16 == (l%16)/4, i.e. l = 20q + r.  A
 // 512-element set is 256 contiguous bytes per weight row.
 //
-// Memory order per workgroup: (RUN: the activation) -> the 4 rows' weight
-// scales and (otherwise) the activation rows, staged into LDS by coalesced
-// 16-byte loads -> each wave's weight codes for S sets.  Loads complete in
-// order, so staging waits only for the small loads issued before the codes.
-//
-// GROUPED: blockIdx.y is the group; its rows come from offsets[], their
-// activation rows from row_index[] (or identity), MR rows per pass.
+// Every lane loads what its MFMAs and scale products need straight into
+// registers -- 16 weight-code bytes, the 8 weight-scale bytes of its
+// (row, chunk) and, for already quantized activations, 16 code bytes and 8
+// scale bytes -- for S sets at a time, the next group's loads in flight
+// while the current one computes.  No staging, no barrier before compute.
 // RUN: the workgroup quantizes the whole (small) activation itself -- amax
 // over every element, gsa, codes and scales into LDS, HPT half-blocks per
 // thread -- while its weight loads are in flight.  No workgroup depends on
 // another; workgroup 0 also writes gsa, codes and scales out.
-template <int S, int MR, int MODE, bool XBF16, int HPT>
+template <int S, int MR, bool RUN, bool XBF16, int HPT>
 __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const GemvArgs args) {
-  constexpr bool RUN = MODE == MODE_RUN, GROUPED = MODE == MODE_GROUPED;
   __shared__ float red[GEMV_MAX_WAVES][MR][4];
   __shared__ float amax_red[GEMV_MAX_WAVES];
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // RUN: codes, scales
   const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, j = lane >> 4;
   const int M = args.M, N = args.N, K = args.K;
   const int n0 = blockIdx.x * 4;
-  const int g = GROUPED ? (int)blockIdx.y : 0;
-  int r_begin = 0, r_end = M;
-  if (GROUPED) {
-    r_begin = max(args.offsets[g], 0);
-    r_end = min(args.offsets[g + 1], M);
-    if (r_begin >= r_end) return;  // uniform over the workgroup
-  }
   const int q = col >> 2, r = col & 3;  // B column: stream, weight row; A row: stream, slot
   const bool useful = j == q;           // result rows of this lane are stream j
   const int64_t cbytes = K / 2, sbytes = K / 16;
-  const int nch = K / 128;
-  const int nset = nch / 4;  // K % 512 == 0
-  const uint8_t* wbase = args.w_codes + (int64_t)g * N * cbytes;
-  const uint8_t* wsbase = args.w_scales + (int64_t)g * N * sbytes;
-  const uint8_t* wrow = wbase + (int64_t)min(n0 + r, N - 1) * cbytes;
+  const int nset = K / 512;
+  const int64_t wr = min(n0 + r, N - 1);  // clamped: results of missing rows are not stored
+  const uint8_t* wrow = args.w_codes + wr * cbytes;
+  const uint8_t* wsrow = args.w_scales + wr * sbytes;
   // A row slot t = r carries block 4h + t of its chunk in MFMA h: slice 2h + t/2
   const int dj = j - (r >> 1);
   const bool a_has = dj == 0 || dj == 2;
   const int a_h = dj >> 1, a_half = r & 1;
+  uint8_t* acl = lds;                       // [M][cbytes]
+  uint8_t* asl = lds + (int64_t)M * cbytes;  // [M][sbytes]
 
-  // LDS: weight scales of the 4 rows, then activation codes and scales
-  uint8_t* wsl = lds;                                   // [4][sbytes]
-  uint8_t* acl = lds + 4 * sbytes;                      // [rows][cbytes]
-  uint8_t* asl = acl + (int64_t)(RUN ? M : MR) * cbytes;  // [rows][sbytes]
-  uint8_t* trash = asl + (int64_t)(RUN ? M : MR) * sbytes;  // 16 bytes
+  // activation rows (clamped; mok masks the missing ones)
+  bool mok[MR];
+  const uint8_t* arc[MR];
+  const uint8_t* ars[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    mok[m] = m < M;
+    const int64_t ar = mok[m] ? m : 0;
+    arc[m] = (RUN ? acl : args.a_codes) + ar * cbytes;
+    ars[m] = (RUN ? asl : args.a_scales) + ar * sbytes;
+  }
 
   const int64_t nhalf = (int64_t)M * (K / 8);
   uint4 xr[HPT][2];
   bool xok[HPT];
-  if (RUN) {
+  if (RUN) {  // the activation first: its loads complete before the weights'
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
       const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
@@ -442,195 +439,132 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const 
       load_half8_raw<XBF16>(args.x, xok[u] ? h : 0, xr[u]);
     }
   }
-  float gsa_v = RUN ? 0.f : args.gsa[0];
-  bool quantized = !RUN;
 
-  for (int r0 = r_begin; r0 < r_end; r0 += MR) {
-    // activation rows of this pass (clamped to valid rows; flags mask them)
-    int64_t arow[MR];
-    bool mok[MR];
+  int sg = wave;
+  uint4 wv[S];
+  uint2 fwv[S];
+  uint4 av[S][MR];
+  uint2 sav[S][MR];
+  auto load_group = [&](int gg) {
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const int rr = r0 + m;
-      mok[m] = rr < r_end;
-      int64_t ar = mok[m] ? rr : r0;
-      if (GROUPED && args.row_index != nullptr) {
-        ar = args.row_index[ar];
-        if (ar < 0 || ar >= args.a_rows) {
-          ar = 0;
-          mok[m] = false;
-        }
-      }
-      arow[m] = ar;
-    }
-    // staging loads: 16-byte pieces, one per thread while they last
-    const int ws16 = (int)(sbytes / 16);  // pieces per weight-scale row
-    const int nws = (r0 == r_begin) ? 4 * ws16 : 0;  // weight scales once
-    const int ac16 = (int)(cbytes / 16), as16 = (int)(sbytes / 16);
-    const int nac = RUN ? 0 : MR * ac16, nas = RUN ? 0 : MR * as16;
-    const int nstage = nws + nac + nas;
-    // Four staging pieces per thread (the host keeps nstage <= 4 * threads).
-    // Addresses are selected, not branched on, and every load is issued (a
-    // valid dummy address when the piece does not exist): a branch around a
-    // load makes the compiler wait for it before the next one.
-    auto src_of = [&](int p) -> const uint8_t* {
-      const int wr = (p >= ws16) + (p >= 2 * ws16) + (p >= 3 * ws16);  // p / ws16 for p < 4*ws16
-      const uint8_t* src_w =
-          wsbase + (int64_t)min(n0 + wr, N - 1) * sbytes + (int64_t)(p - wr * ws16) * 16;
-      const uint8_t* src = (p < nws) ? src_w : wsbase;
+    for (int s2 = 0; s2 < S; ++s2) {  // unconditional loads of clamped sets
+      const int set = min(gg * S + s2, nset - 1);
+      wv[s2] = ldg_nt16(wrow + (int64_t)(4 * set + q) * 64 + 16 * j);
+      fwv[s2] = *(const uint2*)(wsrow + (4 * set + j) * 8);
       if (!RUN) {
-        const int pa = p - nws, ps = p - nws - nac;
-        int ma = 0, ms = 0;
-#pragma unroll
-        for (int m = 1; m < MR; ++m) {
-          ma += pa >= m * ac16;
-          ms += ps >= m * as16;
-        }
-        int64_t rowa = arow[0], rows_ = arow[0];
-#pragma unroll
-        for (int m = 1; m < MR; ++m) {
-          rowa = ma == m ? arow[m] : rowa;
-          rows_ = ms == m ? arow[m] : rows_;
-        }
-        const uint8_t* src_a = args.a_codes + rowa * cbytes + (int64_t)(pa - ma * ac16) * 16;
-        const uint8_t* src_s = args.a_scales + rows_ * sbytes + (int64_t)(ps - ms * as16) * 16;
-        src = (p >= nws && p < nws + nac) ? src_a : src;
-        src = (p >= nws + nac && p < nstage) ? src_s : src;
-      }
-      return src;
-    };
-    const int tid = threadIdx.x, bd = blockDim.x;
-    const uint4 st0 = *(const uint4*)src_of(tid);
-    const uint4 st1 = *(const uint4*)src_of(tid + bd);
-    const uint4 st2 = *(const uint4*)src_of(tid + 2 * bd);
-    const uint4 st3 = *(const uint4*)src_of(tid + 3 * bd);
-    __builtin_amdgcn_sched_barrier(0);
-
-    int sg = wave;
-    uint4 wv[S];
-    auto load_group = [&](int gg) {
-#pragma unroll
-      for (int s2 = 0; s2 < S; ++s2) {  // unconditional loads of clamped sets
-        const int set = min(gg * S + s2, nset - 1);
-        wv[s2] = ldg_nt16(wrow + (int64_t)(4 * set + q) * 64 + 16 * j);
-      }
-    };
-    load_group(sg);
-
-    // unconditional stores: pieces that do not exist go to a trash slot
-    auto dst_of = [&](int p) -> uint8_t* {
-      uint8_t* dst = p < nws ? wsl + p * 16
-                             : (p < nws + nac ? acl + (p - nws) * 16 : asl + (p - nws - nac) * 16);
-      return p < nstage ? dst : trash;
-    };
-    *(uint4*)dst_of(tid) = st0;
-    *(uint4*)dst_of(tid + bd) = st1;
-    *(uint4*)dst_of(tid + 2 * bd) = st2;
-    *(uint4*)dst_of(tid + 3 * bd) = st3;
-
-    if (!quantized) {  // RUN: quantize the activation into LDS
-      float xv[HPT][8];
-#pragma unroll
-      for (int u = 0; u < HPT; ++u) unpack_half8<XBF16>(xr[u], xv[u]);
-      float m = 0.f;
-#pragma unroll
-      for (int u = 0; u < HPT; ++u)
-        if (xok[u]) m = fmaxf(m, half_absmax8(xv[u]));
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      if (lane == 0) amax_red[wave] = m;
-      lds_barrier();
-      float mm = 0.f;
-      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, amax_red[w]);
-      gsa_v = gsa_from_amax(mm);
-      const bool writer = blockIdx.x == 0;
-#pragma unroll
-      for (int u = 0; u < HPT; ++u) {
-        const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
-        float bm = xok[u] ? half_absmax8(xv[u]) : 0.f;
-        bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
-        uint32_t c, sf;
-        quantize_half8(xv[u], bm, gsa_v, c, sf);
-        if (xok[u]) {
-          ((uint32_t*)acl)[h] = c;
-          if ((h & 1) == 0) asl[h >> 1] = (uint8_t)sf;
-          if (writer) {
-            ((uint32_t*)args.codes_out)[h] = c;
-            if ((h & 1) == 0) args.scales_out[h >> 1] = (uint8_t)sf;
-          }
-        }
-      }
-      if (writer && threadIdx.x == 0) args.gsa_out[0] = gsa_v;
-      quantized = true;
-    }
-    lds_barrier();
-
-    // LDS row of each activation row of the pass
-    const int64_t lrow0 = RUN ? r0 : 0;
-    float acc[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
-
-    while (sg * S < nset) {  // wave-uniform
-#pragma unroll
-      for (int s2 = 0; s2 < S; ++s2) {
-        const int set = sg * S + s2;
-        if (set >= nset) break;  // wave-uniform
-        const v8i B = {(int)wv[s2].x, (int)wv[s2].y, (int)wv[s2].z, (int)wv[s2].w, 0, 0, 0, 0};
-        float fw[8];
-        fp8x8_to_f32(*(const uint2*)(wsl + r * sbytes + (4 * set + j) * 8), fw);
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          if (r0 + m >= r_end) break;  // uniform
-          const uint8_t* ar = acl + (lrow0 + m) * cbytes;
-          const uint8_t* sr = asl + (lrow0 + m) * sbytes;
-          const uint4 a4 = (a_has && mok[m]) ? *(const uint4*)(ar + (4 * set + q) * 64 + 16 * j)
-                                            : make_uint4(0u, 0u, 0u, 0u);
-          const uint2 sa = (useful && mok[m]) ? *(const uint2*)(sr + (4 * set + j) * 8)
-                                             : make_uint2(0u, 0u);
-          const v8i Am = a_half == 0 ? v8i{(int)a4.x, (int)a4.y, 0, 0, 0, 0, 0, 0}
-                                     : v8i{0, 0, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
-          const v8i Z = {0, 0, 0, 0, 0, 0, 0, 0};
-          const float4_t c0 = mfma_fp4(a_h == 0 ? Am : Z, B);
-          const float4_t c1 = mfma_fp4(a_h == 1 ? Am : Z, B);
-          float fa[8];
-          fp8x8_to_f32(sa, fa);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            acc[m] = fmaf(c0[t], fa[t] * fw[t], acc[m]);
-            acc[m] = fmaf(c1[t], fa[4 + t] * fw[4 + t], acc[m]);
-          }
+          av[s2][m] = *(const uint4*)(arc[m] + (int64_t)(4 * set + q) * 64 + 16 * j);
+          sav[s2][m] = *(const uint2*)(ars[m] + (4 * set + j) * 8);
         }
       }
-      sg += NW;
-      if (sg * S < nset) load_group(sg);
     }
-    // row r's partial sums sit in lanes 20q + r: gather them in lanes 0..3
+  };
+  load_group(sg);
+
+  float gsa_v = RUN ? 0.f : args.gsa[0];
+  if (RUN) {  // quantize the activation into LDS
+    float xv[HPT][8];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const float v = useful ? acc[m] : 0.f;
-      const int src = 20 * (lane >> 2) + (lane & 3);  // lanes 0..15 read the 16 useful lanes
-      float t = __shfl(v, src & 63, 64);
-      t += __shfl_down(t, 4, 64);
-      t += __shfl_down(t, 8, 64);
-      if (lane < 4) red[wave][m][lane] = t;
-    }
-    __syncthreads();
-    const float gscale = gsa_v * args.ws2[g];
-    for (int e = threadIdx.x; e < MR * 4; e += blockDim.x) {
-      const int m = e >> 2, rr = e & 3;
-      float sum = 0.f;
-      for (int w = 0; w < NW; ++w) sum += red[w][m][rr];
-      const int row = r0 + m, n = n0 + rr;
-      if (row < r_end && mok[m] && n < N) {
-        const float v = sum * gscale;
-        if (args.y_bf16)
-          ((uint16_t*)args.y)[(int64_t)row * N + n] = (uint16_t)f32_to_bf16_rne(v);
-        else
-          ((float*)args.y)[(int64_t)row * N + n] = v;
+    for (int u = 0; u < HPT; ++u) unpack_half8<XBF16>(xr[u], xv[u]);
+    float mx = 0.f;
+#pragma unroll
+    for (int u = 0; u < HPT; ++u)
+      if (xok[u]) mx = fmaxf(mx, half_absmax8(xv[u]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) amax_red[wave] = mx;
+    lds_barrier();
+    float mm = 0.f;
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, amax_red[w]);
+    gsa_v = gsa_from_amax(mm);
+    const bool writer = blockIdx.x == 0;
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+      const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
+      float bm = xok[u] ? half_absmax8(xv[u]) : 0.f;
+      bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+      uint32_t c, sf;
+      quantize_half8(xv[u], bm, gsa_v, c, sf);
+      if (xok[u]) {
+        ((uint32_t*)acl)[h] = c;
+        if ((h & 1) == 0) asl[h >> 1] = (uint8_t)sf;
+        if (writer) {
+          ((uint32_t*)args.codes_out)[h] = c;
+          if ((h & 1) == 0) args.scales_out[h >> 1] = (uint8_t)sf;
+        }
       }
     }
-    __syncthreads();
+    if (writer && threadIdx.x == 0) args.gsa_out[0] = gsa_v;
+    lds_barrier();
+  }
+
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+  while (sg * S < nset) {  // wave-uniform
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int set = sg * S + s2;
+      if (set >= nset) break;  // wave-uniform
+      const v8i B = {(int)wv[s2].x, (int)wv[s2].y, (int)wv[s2].z, (int)wv[s2].w, 0, 0, 0, 0};
+      float fw[8];
+      fp8x8_to_f32(fwv[s2], fw);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        if (m >= M) break;  // uniform
+        uint4 a4;
+        uint2 sa;
+        if (RUN) {
+          a4 = *(const uint4*)(arc[m] + (int64_t)(4 * set + q) * 64 + 16 * j);
+          sa = *(const uint2*)(ars[m] + (4 * set + j) * 8);
+        } else {
+          a4 = av[s2][m];
+          sa = sav[s2][m];
+        }
+        a4 = a_has ? a4 : make_uint4(0u, 0u, 0u, 0u);
+        sa = useful ? sa : make_uint2(0u, 0u);
+        const v8i Am = a_half == 0 ? v8i{(int)a4.x, (int)a4.y, 0, 0, 0, 0, 0, 0}
+                                   : v8i{0, 0, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
+        const v8i Z = {0, 0, 0, 0, 0, 0, 0, 0};
+        const float4_t c0 = mfma_fp4(a_h == 0 ? Am : Z, B);
+        const float4_t c1 = mfma_fp4(a_h == 1 ? Am : Z, B);
+        float fa[8];
+        fp8x8_to_f32(sa, fa);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[m] = fmaf(c0[t], fa[t] * fw[t], acc[m]);
+          acc[m] = fmaf(c1[t], fa[4 + t] * fw[4 + t], acc[m]);
+        }
+      }
+    }
+    sg += NW;
+    if (sg * S < nset) load_group(sg);
+  }
+  // row r's partial sums sit in lanes 20q + r: gather them in lanes 0..3
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const float v = useful ? acc[m] : 0.f;
+    const int src = 20 * (lane >> 2) + (lane & 3);  // lanes 0..15 read the 16 useful lanes
+    float t = __shfl(v, src & 63, 64);
+    t += __shfl_down(t, 4, 64);
+    t += __shfl_down(t, 8, 64);
+    if (lane < 4) red[wave][m][lane] = t;
+  }
+  __syncthreads();
+  const float gscale = gsa_v * args.ws2[0];
+  for (int e = threadIdx.x; e < MR * 4; e += blockDim.x) {
+    const int m = e >> 2, rr = e & 3;
+    float sum = 0.f;
+    for (int w = 0; w < NW; ++w) sum += red[w][m][rr];
+    const int n = n0 + rr;
+    if (m < M && n < N) {
+      const float v = sum * gscale;
+      if (args.y_bf16)
+        ((uint16_t*)args.y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+      else
+        ((float*)args.y)[(int64_t)m * N + n] = v;
+    }
   }
 }
 
@@ -665,49 +599,28 @@ static hipError_t launch_rows(const GemvArgs& a, int64_t rows_per_pass, bool fas
 
 constexpr int NARROW_S = 2;
 
-
-
 static int narrow_waves(int64_t K) {
   const int64_t nset = K / 512;
   int64_t nw = (nset + NARROW_S - 1) / NARROW_S;
   return (int)(nw < 1 ? 1 : (nw > GEMV_MAX_WAVES ? GEMV_MAX_WAVES : nw));
 }
 
-// staging pieces (16 bytes) a workgroup of nw waves must hold, 4 per thread
-static bool narrow_stage_fits(int64_t K, int64_t rows, int nw) {
-  const int64_t pieces = 4 * (K / 256) + rows * (K / 32 + K / 256);
-  return pieces <= 4 * (int64_t)nw * 64;
-}
-
-static size_t narrow_lds(int64_t K, int64_t rows) {
-  return (size_t)(4 * (K / 16) + rows * (K / 2 + K / 16) + 16);  // + 16-byte trash slot
-}
-
-static int narrow_waves_for(int64_t K, int64_t rows) {
-  int nw = narrow_waves(K);
-  while (!narrow_stage_fits(K, rows, nw) && nw < GEMV_MAX_WAVES) ++nw;
-  return nw;
-}
-
 static hipError_t launch_narrow(const GemvArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.N + 3) / 4));
-  const int MR = a.M <= 1 ? 1 : (a.M <= 2 ? 2 : 4);
-  const int th = narrow_waves_for(a.K, MR) * 64;
-  const size_t lds = narrow_lds(a.K, MR);
-  if (MR == 1)
-    gemv_narrow_kernel<NARROW_S, 1, MODE_PLAIN, true, 1><<<grid, th, lds, s>>>(a);
-  else if (MR == 2)
-    gemv_narrow_kernel<NARROW_S, 2, MODE_PLAIN, true, 1><<<grid, th, lds, s>>>(a);
+  const int th = narrow_waves(a.K) * 64;
+  if (a.M <= 1)
+    gemv_narrow_kernel<NARROW_S, 1, false, true, 1><<<grid, th, 0, s>>>(a);
+  else if (a.M <= 2)
+    gemv_narrow_kernel<NARROW_S, 2, false, true, 1><<<grid, th, 0, s>>>(a);
   else
-    gemv_narrow_kernel<NARROW_S, 4, MODE_PLAIN, true, 1><<<grid, th, lds, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, 4, false, true, 1><<<grid, th, 0, s>>>(a);
   return hipGetLastError();
 }
 
 bool gemv_narrow_supported(int64_t M, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                            const uint8_t* w_codes, const uint8_t* w_scales) {
   return M >= 1 && M <= 4 && K % 512 == 0 && K <= 16384 && aligned16(a_codes) &&
-         aligned16(a_scales) && aligned16(w_codes) && aligned16(w_scales) &&
-         narrow_stage_fits(K, 4, GEMV_MAX_WAVES);
+         aligned16(a_scales) && aligned16(w_codes) && aligned16(w_scales);
 }
 
 // RUN mode: enough threads for at most 4 activation half-blocks each.
@@ -723,11 +636,11 @@ static hipError_t launch_narrow_run_t(const GemvArgs& a, int nw, int hpt, size_t
                                       hipStream_t s) {
   dim3 grid((unsigned)((a.N + 3) / 4));
   if (hpt == 1)
-    gemv_narrow_kernel<NARROW_S, MR, MODE_RUN, XBF16, 1><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 1><<<grid, nw * 64, lds, s>>>(a);
   else if (hpt == 2)
-    gemv_narrow_kernel<NARROW_S, MR, MODE_RUN, XBF16, 2><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 2><<<grid, nw * 64, lds, s>>>(a);
   else
-    gemv_narrow_kernel<NARROW_S, MR, MODE_RUN, XBF16, 4><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 4><<<grid, nw * 64, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -750,11 +663,11 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
   a.K = (int)K;
   a.a_rows = (int)M;
   const int64_t nhalf = M * (K / 8);
-  int nw = narrow_waves_for(K, 0);
+  int nw = narrow_waves(K);
   while ((int64_t)nw * 64 * 4 < nhalf && nw < GEMV_MAX_WAVES) ++nw;
   const int64_t per = ((int64_t)nw * 64);
   const int hpt = nhalf <= per ? 1 : (nhalf <= 2 * per ? 2 : 4);
-  const size_t lds = narrow_lds(K, M);
+  const size_t lds = (size_t)(M * (K / 2 + K / 16));
   if (x_bf16) {
     if (M <= 1) return launch_narrow_run_t<1, true>(a, nw, hpt, lds, s);
     if (M <= 2) return launch_narrow_run_t<2, true>(a, nw, hpt, lds, s);
