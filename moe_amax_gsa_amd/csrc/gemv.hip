@@ -371,9 +371,9 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
 }
 
 // ---------------------------------------------------------------- narrow
-// Few activation rows and few weight rows per workgroup: 4 weight rows per
-// workgroup so that a decode-sized N spreads its weight stream over every
-// CU.  The K dimension is split four ways inside each MFMA: B column
+// Few activation rows and few weight rows per workgroup: RQ quads of 4
+// weight rows per workgroup (8 rows at decode sizes) so that a decode-sized
+// N spreads its weight stream over every CU.  The K dimension is split four ways inside each MFMA: B column
 // n' = 4q + r holds weight row r at chunk 4*set + q (a "stream" q of 128
 // K-elements), A row i = 4q + t holds activation block 4h + t of the same
 // chunk in MFMA h (two MFMAs cover the chunk's 8 blocks), so result row
@@ -392,23 +392,28 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
 // over every element, gsa, codes and scales into LDS, HPT half-blocks per
 // thread -- while its weight loads are in flight.  No workgroup depends on
 // another; workgroup 0 also writes gsa, codes and scales out.
-template <int S, int MR, bool RUN, bool XBF16, int HPT>
+template <int S, int MR, bool RUN, bool XBF16, int HPT, int RQ>
 __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const GemvArgs args) {
-  __shared__ float red[GEMV_MAX_WAVES][MR][4];
+  __shared__ float red[GEMV_MAX_WAVES][MR][4 * RQ];
   __shared__ float amax_red[GEMV_MAX_WAVES];
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // RUN: codes, scales
   const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, j = lane >> 4;
   const int M = args.M, N = args.N, K = args.K;
-  const int n0 = blockIdx.x * 4;
+  const int n0 = blockIdx.x * 4 * RQ;  // RQ quads of 4 weight rows
   const int q = col >> 2, r = col & 3;  // B column: stream, weight row; A row: stream, slot
   const bool useful = j == q;           // result rows of this lane are stream j
   const int64_t cbytes = K / 2, sbytes = K / 16;
   const int nset = K / 512;
-  const int64_t wr = min(n0 + r, N - 1);  // clamped: results of missing rows are not stored
-  const uint8_t* wrow = args.w_codes + wr * cbytes;
-  const uint8_t* wsrow = args.w_scales + wr * sbytes;
+  const uint8_t* wrow[RQ];
+  const uint8_t* wsrow[RQ];
+#pragma unroll
+  for (int rq = 0; rq < RQ; ++rq) {
+    const int64_t wr = min(n0 + 4 * rq + r, N - 1);  // clamped: missing rows are not stored
+    wrow[rq] = args.w_codes + wr * cbytes;
+    wsrow[rq] = args.w_scales + wr * sbytes;
+  }
   // A row slot t = r carries block 4h + t of its chunk in MFMA h: slice 2h + t/2
   const int dj = j - (r >> 1);
   const bool a_has = dj == 0 || dj == 2;
@@ -441,16 +446,19 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const 
   }
 
   int sg = wave;
-  uint4 wv[S];
-  uint2 fwv[S];
+  uint4 wv[S][RQ];
+  uint2 fwv[S][RQ];
   uint4 av[S][MR];
   uint2 sav[S][MR];
   auto load_group = [&](int gg) {
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {  // unconditional loads of clamped sets
       const int set = min(gg * S + s2, nset - 1);
-      wv[s2] = ldg_nt16(wrow + (int64_t)(4 * set + q) * 64 + 16 * j);
-      fwv[s2] = *(const uint2*)(wsrow + (4 * set + j) * 8);
+#pragma unroll
+      for (int rq = 0; rq < RQ; ++rq) {
+        wv[s2][rq] = ldg_nt16(wrow[rq] + (int64_t)(4 * set + q) * 64 + 16 * j);
+        fwv[s2][rq] = *(const uint2*)(wsrow[rq] + (4 * set + j) * 8);
+      }
       if (!RUN) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
@@ -499,17 +507,19 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const 
     lds_barrier();
   }
 
-  float acc[MR];
+  float acc[MR][RQ];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int rq = 0; rq < RQ; ++rq) acc[m][rq] = 0.f;
   while (sg * S < nset) {  // wave-uniform
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {
       const int set = sg * S + s2;
       if (set >= nset) break;  // wave-uniform
-      const v8i B = {(int)wv[s2].x, (int)wv[s2].y, (int)wv[s2].z, (int)wv[s2].w, 0, 0, 0, 0};
-      float fw[8];
-      fp8x8_to_f32(fwv[s2], fw);
+      float fw[RQ][8];
+#pragma unroll
+      for (int rq = 0; rq < RQ; ++rq) fp8x8_to_f32(fwv[s2][rq], fw[rq]);
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         if (m >= M) break;  // uniform
@@ -527,14 +537,20 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const 
         const v8i Am = a_half == 0 ? v8i{(int)a4.x, (int)a4.y, 0, 0, 0, 0, 0, 0}
                                    : v8i{0, 0, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
         const v8i Z = {0, 0, 0, 0, 0, 0, 0, 0};
-        const float4_t c0 = mfma_fp4(a_h == 0 ? Am : Z, B);
-        const float4_t c1 = mfma_fp4(a_h == 1 ? Am : Z, B);
+        const v8i A0 = a_h == 0 ? Am : Z, A1 = a_h == 1 ? Am : Z;
         float fa[8];
         fp8x8_to_f32(sa, fa);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[m] = fmaf(c0[t], fa[t] * fw[t], acc[m]);
-          acc[m] = fmaf(c1[t], fa[4 + t] * fw[4 + t], acc[m]);
+        for (int rq = 0; rq < RQ; ++rq) {
+          const v8i B = {(int)wv[s2][rq].x, (int)wv[s2][rq].y, (int)wv[s2][rq].z,
+                         (int)wv[s2][rq].w, 0, 0, 0, 0};
+          const float4_t c0 = mfma_fp4(A0, B);
+          const float4_t c1 = mfma_fp4(A1, B);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            acc[m][rq] = fmaf(c0[t], fa[t] * fw[rq][t], acc[m][rq]);
+            acc[m][rq] = fmaf(c1[t], fa[4 + t] * fw[rq][4 + t], acc[m][rq]);
+          }
         }
       }
     }
@@ -543,18 +559,20 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const 
   }
   // row r's partial sums sit in lanes 20q + r: gather them in lanes 0..3
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const float v = useful ? acc[m] : 0.f;
-    const int src = 20 * (lane >> 2) + (lane & 3);  // lanes 0..15 read the 16 useful lanes
-    float t = __shfl(v, src & 63, 64);
-    t += __shfl_down(t, 4, 64);
-    t += __shfl_down(t, 8, 64);
-    if (lane < 4) red[wave][m][lane] = t;
-  }
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int rq = 0; rq < RQ; ++rq) {
+      const float v = useful ? acc[m][rq] : 0.f;
+      const int src = 20 * (lane >> 2) + (lane & 3);  // lanes 0..15 read the 16 useful lanes
+      float t = __shfl(v, src & 63, 64);
+      t += __shfl_down(t, 4, 64);
+      t += __shfl_down(t, 8, 64);
+      if (lane < 4) red[wave][m][4 * rq + lane] = t;
+    }
   __syncthreads();
   const float gscale = gsa_v * args.ws2[0];
-  for (int e = threadIdx.x; e < MR * 4; e += blockDim.x) {
-    const int m = e >> 2, rr = e & 3;
+  for (int e = threadIdx.x; e < MR * 4 * RQ; e += blockDim.x) {
+    const int m = e / (4 * RQ), rr = e % (4 * RQ);
     float sum = 0.f;
     for (int w = 0; w < NW; ++w) sum += red[w][m][rr];
     const int n = n0 + rr;
@@ -605,15 +623,19 @@ static int narrow_waves(int64_t K) {
   return (int)(nw < 1 ? 1 : (nw > GEMV_MAX_WAVES ? GEMV_MAX_WAVES : nw));
 }
 
+// 8 weight rows (two quads) per workgroup: half as many workgroups quantize
+// the activation in RUN mode, and a decode-sized N still spreads over the CUs
+constexpr int NARROW_RQ = 2;
+
 static hipError_t launch_narrow(const GemvArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)((a.N + 3) / 4));
+  dim3 grid((unsigned)((a.N + 4 * NARROW_RQ - 1) / (4 * NARROW_RQ)));
   const int th = narrow_waves(a.K) * 64;
   if (a.M <= 1)
-    gemv_narrow_kernel<NARROW_S, 1, false, true, 1><<<grid, th, 0, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, 1, false, true, 1, NARROW_RQ><<<grid, th, 0, s>>>(a);
   else if (a.M <= 2)
-    gemv_narrow_kernel<NARROW_S, 2, false, true, 1><<<grid, th, 0, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, 2, false, true, 1, NARROW_RQ><<<grid, th, 0, s>>>(a);
   else
-    gemv_narrow_kernel<NARROW_S, 4, false, true, 1><<<grid, th, 0, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, 4, false, true, 1, NARROW_RQ><<<grid, th, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -634,13 +656,13 @@ bool gemv_narrow_run_supported(int64_t M, int64_t K, const void* x, const uint8_
 template <int MR, bool XBF16>
 static hipError_t launch_narrow_run_t(const GemvArgs& a, int nw, int hpt, size_t lds,
                                       hipStream_t s) {
-  dim3 grid((unsigned)((a.N + 3) / 4));
+  dim3 grid((unsigned)((a.N + 4 * NARROW_RQ - 1) / (4 * NARROW_RQ)));
   if (hpt == 1)
-    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 1><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 1, NARROW_RQ><<<grid, nw * 64, lds, s>>>(a);
   else if (hpt == 2)
-    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 2><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 2, NARROW_RQ><<<grid, nw * 64, lds, s>>>(a);
   else
-    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 4><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 4, NARROW_RQ><<<grid, nw * 64, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -162,6 +162,71 @@ def test_quantize_signed_zero_and_underflow(C):
     assert np.array_equal(codes.cpu().numpy(), oc)
 
 
+def near_tie_activation(M=4, K=4096, seed=11):
+    """fp32 activation whose quantize decisions sit at rounding ties.
+
+    gsa is 2^-8 (one element is 10.5 = 2688 * 2^-8).  Even blocks have an
+    exact scale (block max 6 gsa dec(c)) and elements within 40 ulp of every
+    E2M1 decision point t * s, t in {.25, .75, 1.25, 1.75, 2.5, 3.5, 5};
+    odd blocks have a block max within 40 ulp of 6 gsa times the midpoint of
+    two neighbouring E4M3 values.  The oracle decides every code."""
+    rng = np.random.default_rng(seed)
+    gsa = 2.0 ** -8
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    x = np.zeros((M * K // 16, 16), np.float32)
+    for b in range(x.shape[0]):
+        c = 1 + b % 126
+        sc = oracle.e4m3_value(c) * gsa
+        if b % 2 == 0:
+            x[b, 0] = np.float32(6.0 * sc)
+            for i in range(1, 16):
+                t = ties[(b + i) % len(ties)]
+                k = int(rng.integers(-40, 41))
+                x[b, i] = np.float32(t * sc * (1.0 + k * 2.0 ** -23))
+        else:
+            mid = 0.5 * (oracle.e4m3_value(c - 1) + oracle.e4m3_value(c))
+            bm = np.float32(6.0 * gsa * mid)
+            bm = (bm.view(np.uint32) + np.uint32(int(rng.integers(0, 41)))).view(np.float32) \
+                if b % 4 == 1 else (bm.view(np.uint32) - np.uint32(int(rng.integers(0, 41)))).view(np.float32)
+            x[b, 0] = bm
+            x[b, 1:] = (rng.uniform(-0.9, 0.9, 15) * bm).astype(np.float32)
+        x[b] *= np.where(rng.random(16) < 0.5, -1.0, 1.0).astype(np.float32)
+    x = x.reshape(M, K)
+    x[0, 0] = np.float32(10.5)
+    assert np.max(np.abs(x)) == np.float32(10.5)
+    return np.ascontiguousarray(x)
+
+
+def test_quantize_near_rounding_ties(C):
+    """Codes and scales at and around every rounding tie, through
+    quantize_from_buffer and through the one-launch decode path."""
+    say("quantize near ties")
+    x = near_tie_activation()
+    M, K = x.shape
+    xd = to_dev(x)
+    g = gpu_gsa(C, xd)
+    assert f32(g) == np.float32(2.0 ** -8) == oracle.amax_gsa(x)
+    oc, os_ = oracle.quantize(x, np.float32(2.0 ** -8))
+    codes, scales = gpu_quantize(C, xd, g)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    # the fused path quantizes inside every workgroup: same bits
+    N = 64
+    inp = W.make_linear(1, K, N, seed=5)
+    wc, ws = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=DEV)
+    gsa2 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes2 = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales2 = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_run(xd, gsa2, codes2, scales2, wc, ws, ws2, y)
+    assert f32(gsa2) == np.float32(2.0 ** -8)
+    assert np.array_equal(scales2.cpu().numpy(), os_)
+    assert np.array_equal(codes2.cpu().numpy(), oc)
+    ref = oracle.linear(oc, os_, np.float32(2.0 ** -8), inp.w_codes, inp.w_scales, inp.ws2)
+    assert rel_err(y.cpu().numpy().astype(np.float64), ref) <= REL_TOL
+
+
 # ---------------------------------------------------------------- linear
 def run_linear(C, inp: W.LinearInputs, y_dtype=torch.float32, dtype="bf16"):
     xd = x_dev(inp.x, dtype)
