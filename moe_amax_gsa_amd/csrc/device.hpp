@@ -62,6 +62,42 @@ __device__ __forceinline__ uint32_t e2m1_magnitude(float q) {
   return mag < 7u ? mag : 7u;
 }
 
+// gfx950's converters give the same codes as the two encoders above:
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds fp32 to E2M1 to nearest,
+// ties to even, saturating at 6, keeping the sign (-0 -> 0x8); it packs
+// its two inputs into one byte, the first in the low nibble.
+// v_cvt_scalef32_pk_fp8_f32 with scale 1 rounds to E4M3 to nearest even
+// (NaN above 448, so the input is clamped first).  Both were compared with
+// the encoders above on every input they see here (every non-negative
+// finite fp32; every fp32 in [0, 448]).
+typedef short short2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t e4m3_encode_hw(float v) {
+  const short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2_t{0, 0}, fminf(v, 448.0f),
+                                                              0.0f, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0] & 0xFFu;
+}
+
+// Eight signed quotients v[i] / sc, each correctly rounded, as E2M1 codes
+// (code i in bits 4i .. 4i+3).  sc > 0.
+__device__ __forceinline__ uint32_t e2m1_codes8_hw(const float v[8], float sc) {
+#pragma clang fp contract(off)
+  uint32_t c = 0;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[0] / sc, v[1] / sc, 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[2] / sc, v[3] / sc, 1.0f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[4] / sc, v[5] / sc, 1.0f, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v[6] / sc, v[7] / sc, 1.0f, 3);
+  return c;
+}
+
+// Signs only (the codes of a block whose scale rounded to 0).
+__device__ __forceinline__ uint32_t e2m1_signs8(const float v[8]) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c |= ((__float_as_uint(v[i]) >> 31) << 3) << (4 * i);
+  return c;
+}
+
 // ---- wave64 reductions (DPP-friendly xor shuffles)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -173,20 +209,16 @@ __device__ __forceinline__ void quantize_vals16(const float v[16], float gsa, ui
   const float bamax = block_absmax16(v);
   const float six_gsa = gsa * 6.0f;
   const float sf_raw = bamax / six_gsa;
-  sf = e4m3_encode(sf_raw);
+  sf = e4m3_encode_hw(sf_raw);
   const float sdec = e4m3_decode(sf);
   const float sc = sdec * gsa;
-  lo = 0;
-  hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t mag = sdec != 0.0f ? e2m1_magnitude(fabsf(v[i]) / sc) : 0u;
-    const uint32_t code = ((__float_as_uint(v[i]) >> 31) << 3) | mag;
-    if (i < 8)
-      lo |= code << (4 * i);
-    else
-      hi |= code << (4 * (i - 8));
+  if (sdec == 0.0f) {  // every magnitude rounds to 0; signs stay
+    lo = e2m1_signs8(v);
+    hi = e2m1_signs8(v + 8);
+    return;
   }
+  lo = e2m1_codes8_hw(v, sc);
+  hi = e2m1_codes8_hw(v + 8, sc);
 }
 
 // Half-block layout: thread h owns elements 8h .. 8h+7 (one 16-byte bf16
@@ -257,15 +289,10 @@ __device__ __forceinline__ void quantize_half8(const float v[8], float bamax, fl
 #pragma clang fp contract(off)
   const float six_gsa = gsa * 6.0f;
   const float sf_raw = bamax / six_gsa;
-  sf = e4m3_encode(sf_raw);
+  sf = e4m3_encode_hw(sf_raw);
   const float sdec = e4m3_decode(sf);
   const float sc = sdec * gsa;
-  codes = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t mag = sdec != 0.0f ? e2m1_magnitude(fabsf(v[i]) / sc) : 0u;
-    codes |= (((__float_as_uint(v[i]) >> 31) << 3) | mag) << (4 * i);
-  }
+  codes = sdec == 0.0f ? e2m1_signs8(v) : e2m1_codes8_hw(v, sc);
 }
 
 template <bool BF16>

@@ -392,10 +392,10 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
 // over every element, gsa, codes and scales into LDS, HPT half-blocks per
 // thread -- while its weight loads are in flight.  No workgroup depends on
 // another; workgroup 0 also writes gsa, codes and scales out.
-template <int S, int MR, bool RUN, bool XBF16, int HPT, int RQ>
-__global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_narrow_kernel(const GemvArgs args) {
-  __shared__ float red[GEMV_MAX_WAVES][MR][4 * RQ];
-  __shared__ float amax_red[GEMV_MAX_WAVES];
+template <int S, int MR, bool RUN, bool XBF16, int HPT, int RQ, int MAXW>
+__global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs args) {
+  __shared__ float red[MAXW][MR][4 * RQ];
+  __shared__ float amax_red[MAXW];
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // RUN: codes, scales
   const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -615,12 +615,15 @@ static hipError_t launch_rows(const GemvArgs& a, int64_t rows_per_pass, bool fas
   return launch_mp<8, MODE>(a, fast, grid, nw, s);
 }
 
-constexpr int NARROW_S = 2;
+// One activation row: one 512-element set per wave and up to 16 waves (the
+// quantize in RUN mode spreads over more threads); more rows: two sets per
+// wave and up to 8 waves (their registers do not fit 16 waves).
+constexpr int NARROW_MAXW1 = 16;
 
-static int narrow_waves(int64_t K) {
+static int narrow_waves(int64_t K, int S, int maxw) {
   const int64_t nset = K / 512;
-  int64_t nw = (nset + NARROW_S - 1) / NARROW_S;
-  return (int)(nw < 1 ? 1 : (nw > GEMV_MAX_WAVES ? GEMV_MAX_WAVES : nw));
+  int64_t nw = (nset + S - 1) / S;
+  return (int)(nw < 1 ? 1 : (nw > maxw ? maxw : nw));
 }
 
 // 8 weight rows (two quads) per workgroup: half as many workgroups quantize
@@ -629,13 +632,16 @@ constexpr int NARROW_RQ = 2;
 
 static hipError_t launch_narrow(const GemvArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.N + 4 * NARROW_RQ - 1) / (4 * NARROW_RQ)));
-  const int th = narrow_waves(a.K) * 64;
-  if (a.M <= 1)
-    gemv_narrow_kernel<NARROW_S, 1, false, true, 1, NARROW_RQ><<<grid, th, 0, s>>>(a);
-  else if (a.M <= 2)
-    gemv_narrow_kernel<NARROW_S, 2, false, true, 1, NARROW_RQ><<<grid, th, 0, s>>>(a);
-  else
-    gemv_narrow_kernel<NARROW_S, 4, false, true, 1, NARROW_RQ><<<grid, th, 0, s>>>(a);
+  if (a.M <= 1) {
+    const int th = narrow_waves(a.K, 1, NARROW_MAXW1) * 64;
+    gemv_narrow_kernel<1, 1, false, true, 1, NARROW_RQ, NARROW_MAXW1><<<grid, th, 0, s>>>(a);
+  } else {
+    const int th = narrow_waves(a.K, 2, GEMV_MAX_WAVES) * 64;
+    if (a.M <= 2)
+      gemv_narrow_kernel<2, 2, false, true, 1, NARROW_RQ, GEMV_MAX_WAVES><<<grid, th, 0, s>>>(a);
+    else
+      gemv_narrow_kernel<2, 4, false, true, 1, NARROW_RQ, GEMV_MAX_WAVES><<<grid, th, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -653,16 +659,16 @@ bool gemv_narrow_run_supported(int64_t M, int64_t K, const void* x, const uint8_
          aligned16(w_scales);
 }
 
-template <int MR, bool XBF16>
+template <int S, int MR, bool XBF16, int MAXW>
 static hipError_t launch_narrow_run_t(const GemvArgs& a, int nw, int hpt, size_t lds,
                                       hipStream_t s) {
   dim3 grid((unsigned)((a.N + 4 * NARROW_RQ - 1) / (4 * NARROW_RQ)));
   if (hpt == 1)
-    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 1, NARROW_RQ><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<S, MR, true, XBF16, 1, NARROW_RQ, MAXW><<<grid, nw * 64, lds, s>>>(a);
   else if (hpt == 2)
-    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 2, NARROW_RQ><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<S, MR, true, XBF16, 2, NARROW_RQ, MAXW><<<grid, nw * 64, lds, s>>>(a);
   else
-    gemv_narrow_kernel<NARROW_S, MR, true, XBF16, 4, NARROW_RQ><<<grid, nw * 64, lds, s>>>(a);
+    gemv_narrow_kernel<S, MR, true, XBF16, 4, NARROW_RQ, MAXW><<<grid, nw * 64, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -685,19 +691,21 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
   a.K = (int)K;
   a.a_rows = (int)M;
   const int64_t nhalf = M * (K / 8);
-  int nw = narrow_waves(K);
-  while ((int64_t)nw * 64 * 4 < nhalf && nw < GEMV_MAX_WAVES) ++nw;
+  const bool one = M <= 1;
+  const int maxw = one ? NARROW_MAXW1 : GEMV_MAX_WAVES;
+  int nw = narrow_waves(K, one ? 1 : 2, maxw);
+  while ((int64_t)nw * 64 * 4 < nhalf && nw < maxw) ++nw;
   const int64_t per = ((int64_t)nw * 64);
   const int hpt = nhalf <= per ? 1 : (nhalf <= 2 * per ? 2 : 4);
   const size_t lds = (size_t)(M * (K / 2 + K / 16));
   if (x_bf16) {
-    if (M <= 1) return launch_narrow_run_t<1, true>(a, nw, hpt, lds, s);
-    if (M <= 2) return launch_narrow_run_t<2, true>(a, nw, hpt, lds, s);
-    return launch_narrow_run_t<4, true>(a, nw, hpt, lds, s);
+    if (one) return launch_narrow_run_t<1, 1, true, NARROW_MAXW1>(a, nw, hpt, lds, s);
+    if (M <= 2) return launch_narrow_run_t<2, 2, true, GEMV_MAX_WAVES>(a, nw, hpt, lds, s);
+    return launch_narrow_run_t<2, 4, true, GEMV_MAX_WAVES>(a, nw, hpt, lds, s);
   }
-  if (M <= 1) return launch_narrow_run_t<1, false>(a, nw, hpt, lds, s);
-  if (M <= 2) return launch_narrow_run_t<2, false>(a, nw, hpt, lds, s);
-  return launch_narrow_run_t<4, false>(a, nw, hpt, lds, s);
+  if (one) return launch_narrow_run_t<1, 1, false, NARROW_MAXW1>(a, nw, hpt, lds, s);
+  if (M <= 2) return launch_narrow_run_t<2, 2, false, GEMV_MAX_WAVES>(a, nw, hpt, lds, s);
+  return launch_narrow_run_t<2, 4, false, GEMV_MAX_WAVES>(a, nw, hpt, lds, s);
 }
 
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
