@@ -373,8 +373,8 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
 // ---------------------------------------------------------------- narrow
 // Few activation rows and few weight rows per workgroup: RQ quads of 4
 // weight rows per workgroup (8 rows at decode sizes) so that a decode-sized
-// N spreads its weight stream over every CU.  The K dimension is split four ways inside each MFMA: B column
-// n' = 4q + r holds weight row r at chunk 4*set + q (a "stream" q of 128
+// N spreads its weight stream over every CU.  The K dimension is split four
+// ways inside each MFMA: B column n' = 4q + r holds weight row r at chunk 4*set + q (a "stream" q of 128
 // K-elements), A row i = 4q + t holds activation block 4h + t of the same
 // chunk in MFMA h (two MFMAs cover the chunk's 8 blocks), so result row
 // 4q + t against column 4q + r is the exact block sum S_b for row r; the
@@ -590,20 +590,20 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int S_GROUP = 4;
 
-static int waves_for(int64_t K) {
+static int waves_for(int64_t K, int S = S_GROUP) {
   const int64_t nsc = (K + 255) / 256;
-  int64_t nw = (nsc + S_GROUP - 1) / S_GROUP;
+  int64_t nw = (nsc + S - 1) / S;
   if (nw < 1) nw = 1;
   if (nw > GEMV_MAX_WAVES) nw = GEMV_MAX_WAVES;
   return (int)nw;
 }
 
-template <int MP, int MODE>
+template <int MP, int MODE, int S = S_GROUP>
 static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hipStream_t s) {
   if (fast)
-    gemv_fp4_kernel<S_GROUP, MP, true, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
+    gemv_fp4_kernel<S, MP, true, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
   else
-    gemv_fp4_kernel<S_GROUP, MP, false, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
+    gemv_fp4_kernel<S, MP, false, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -758,6 +758,11 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
   // more passes over the same weight tile, which then comes from L2)
   const int64_t mean_rows = (M_total + G - 1) / G;
   dim3 grid((unsigned)((N + 15) / 16), (unsigned)G);
+  if (mean_rows <= 2 && K >= 4096) {
+    // long K, few rows: two super-chunks per wave in flight instead of four
+    // (109 instead of 157 registers, so two workgroups share a CU)
+    return launch_mp<2, MODE_GROUPED, 2>(a, fast, grid, waves_for(K, 2), s);
+  }
   return launch_rows<MODE_GROUPED>(a, mean_rows <= 2 ? 4 : 2 * mean_rows, fast, grid,
                                    waves_for(K), s);
 }
