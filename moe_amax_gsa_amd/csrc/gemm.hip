@@ -199,23 +199,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-template <int WM, int WN, int STAGES>
+template <int WM, int WN, int STAGES, int KW>
 struct LdsTile {
   static constexpr int TM = 32 * WM, TN = 32 * WN, ROWS = TM + TN;
-  static constexpr int CODE_BYTES = ROWS * 128, SCALE_BYTES = ROWS * 16;
+  static constexpr int THREADS = 64 * KW;
+  static constexpr int CHUNK = 64 * KW;             // K elements per chunk, 64 per wave
+  static constexpr int CB = CHUNK / 2, SB = CHUNK / 16;  // code, scale bytes per row
+  static constexpr int PPR = CB / 16;               // 16-byte pieces per code row
+  static constexpr int RPL = 1024 / CB;             // code rows per wave load
+  static constexpr int SRL = 1024 / SB;             // scale rows per wave load
+  static constexpr int CODE_BYTES = ROWS * CB, SCALE_BYTES = ROWS * SB;
   static constexpr int STAGE_BYTES = CODE_BYTES + SCALE_BYTES;
-  static constexpr int CODE_LOADS = ROWS / 32;         // 16-byte loads per lane per chunk
-  static constexpr int SCALE_WAVES = ROWS / 64;        // waves that fetch scales
+  static constexpr int CODE_LOADS = ROWS / (RPL * KW);  // 16-byte loads per lane per chunk
+  static constexpr int SCALE_LOADS = ROWS / SRL;        // waves that fetch scales
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(ROWS % (RPL * KW) == 0 && TM % (RPL * KW) == 0, "loads must not straddle A/B");
+  static_assert(ROWS % SRL == 0 && TM % SRL == 0 && SCALE_LOADS <= KW, "scale loads");
+  static_assert(KW * 16 * (TN + 4) * 4 <= LDS_BYTES, "reduction slabs fit in the stages");
 };
 
-template <int WM, int WN, int STAGES, int WPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_lds_kernel(
+template <int WM, int WN, int STAGES, int WPE, int KW>
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
     int y_bf16, int M, int N, int K) {
-  using T = LdsTile<WM, WN, STAGES>;
+  using T = LdsTile<WM, WN, STAGES, KW>;
   constexpr int TM = T::TM, TN = T::TN, LDT = TN + 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -224,43 +233,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const uint32_t cbytes = (uint32_t)K / 2, sbytes = (uint32_t)K / 16;
-  const int nch = K / 256;
+  const int nch = K / T::CHUNK;
 
-  // this lane's source offsets for its code loads: load i of wave w fills
-  // LDS rows 8(4i + w) .. +7, lane l the row 8(4i + w) + l/8, slot l % 8,
-  // which holds piece (l % 8) ^ (l / 8) of that row's line
+  // code load i of wave w fills LDS rows RPL (KW i + w) .. + RPL-1: lane l
+  // the row RPL (KW i + w) + l / PPR, slot l % PPR, which holds piece
+  // (l % PPR) ^ (row & 7) of that row's chunk
   uint32_t csrc[T::CODE_LOADS];
 #pragma unroll
   for (int i = 0; i < T::CODE_LOADS; ++i) {
-    const int row = 8 * (4 * i + wave) + (lane >> 3);
-    const uint32_t piece = (uint32_t)((lane & 7) ^ (lane >> 3));
-    if (row < TM) {
-      const uint32_t ra = (uint32_t)min(m0 + row, M - 1);  // clamped rows: results discarded
-      csrc[i] = ra * cbytes + piece * 16;
-    } else {
-      const uint32_t rb = (uint32_t)min(n0 + row - TM, N - 1);
-      csrc[i] = rb * cbytes + piece * 16;
-    }
+    const int row = T::RPL * (KW * i + wave) + lane / T::PPR;
+    const uint32_t piece = (uint32_t)((lane % T::PPR) ^ (row & 7));
+    if (row < TM)
+      csrc[i] = (uint32_t)min(m0 + row, M - 1) * cbytes + piece * 16;  // clamped: discarded
+    else
+      csrc[i] = (uint32_t)min(n0 + row - TM, N - 1) * cbytes + piece * 16;
   }
-  // scales: wave w < SCALE_WAVES fetches rows 64w + lane (16 bytes each);
-  // rows below TM are activation rows (TM is a multiple of 64)
-  static_assert(TM % 64 == 0, "scale rows of one wave must not straddle A and B");
-  const int srow = 64 * min(wave, T::SCALE_WAVES - 1) + lane;
-  const uint32_t ssrc = srow < TM ? (uint32_t)min(m0 + srow, M - 1) * sbytes
-                                  : (uint32_t)min(n0 + srow - TM, N - 1) * sbytes;
+  // scale load of wave w < SCALE_LOADS: rows SRL w + l / (SB/16), piece l % (SB/16)
+  const int srow = T::SRL * min(wave, T::SCALE_LOADS - 1) + lane / (T::SB / 16);
+  const uint32_t spiece = (uint32_t)(lane % (T::SB / 16)) * 16;
+  const uint32_t ssrc = (srow < TM ? (uint32_t)min(m0 + srow, M - 1) * sbytes
+                                   : (uint32_t)min(n0 + srow - TM, N - 1) * sbytes) + spiece;
 
   auto issue = [&](int chunk, int stage) {
     const uint32_t st = smem_base + stage * T::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < T::CODE_LOADS; ++i) {
-      const uint8_t* base = (32 * i < TM) ? a_codes : w_codes;  // the same for the whole load
-      load_lds16(base, csrc[i] + (uint32_t)chunk * 128, st + 1024 * (4 * i + wave));
+      const uint8_t* base = (T::RPL * KW * i < TM) ? a_codes : w_codes;  // the same for the load
+      load_lds16(base, csrc[i] + (uint32_t)chunk * T::CB, st + 1024 * (KW * i + wave));
     }
     const uint32_t sdst = st + T::CODE_BYTES + 1024 * wave;
-    if (wave < TM / 64)
-      load_lds16(a_scales, ssrc + (uint32_t)chunk * 16, sdst);
-    else if (wave < T::SCALE_WAVES)
-      load_lds16(w_scales, ssrc + (uint32_t)chunk * 16, sdst);
+    if (wave < TM / T::SRL)
+      load_lds16(a_scales, ssrc + (uint32_t)chunk * T::SB, sdst);
+    else if (wave < T::SCALE_LOADS)
+      load_lds16(w_scales, ssrc + (uint32_t)chunk * T::SB, sdst);
   };
 
   f32x16 acc[WM][WN];
@@ -271,7 +276,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // LDS read offsets of this lane's fragments within a stage
+  // LDS read offsets of this lane's fragments within a stage (wave = the
+  // 64-element step of the chunk)
   const uint32_t piece = (uint32_t)(2 * wave + h);
   const uint32_t slot = (piece ^ (uint32_t)(r32 & 7)) * 16;
 
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 
   for (int c = 0; c < nch; ++c) {
     // chunks c+1 .. c+STAGES-2 may still be in flight (fewest loads per wave)
-    constexpr int PER_CHUNK = T::CODE_LOADS + (T::SCALE_WAVES == 4 ? 1 : 0);
+    constexpr int PER_CHUNK = T::CODE_LOADS + (T::SCALE_LOADS == KW ? 1 : 0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * PER_CHUNK) : "memory");
     lds_barrier();
     issue(min(c + STAGES - 1, nch - 1), (c + STAGES - 1) % STAGES);
@@ -291,14 +297,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       const int row = 32 * i + r32;
-      fa[i] = *(const uint4*)(st + row * 128 + slot);
-      sa[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * 16 + 4 * wave + 2 * h);
+      fa[i] = *(const uint4*)(st + row * T::CB + slot);
+      sa[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
     }
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
       const int row = TM + 32 * i + r32;
-      fb[i] = *(const uint4*)(st + row * 128 + slot);
-      sb[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * 16 + 4 * wave + 2 * h);
+      fb[i] = *(const uint4*)(st + row * T::CB + slot);
+      sb[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
     }
     half2_t sfa[WM], sfb[WN];
 #pragma unroll
@@ -344,8 +350,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // reduce the four partial tiles one 16-row slab at a time (result
-  // registers 8q..8q+7 of MFMA tile row a hold rows 32a + 16q + [0, 16))
+  // reduce the KW partial tiles one 16-row slab at a time (result registers
+  // 8q..8q+7 of MFMA tile row a hold rows 32a + 16q + [0, 16))
   float* red = (float*)smem;
   const float gscale = gsa_p[0] * ws2_p[0];
   float* slab = red + (size_t)wave * 16 * LDT;
@@ -359,10 +365,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
         for (int r = 8 * q; r < 8 * q + 8; ++r)
           slab[(8 * ((r >> 2) & 1) + 4 * h + (r & 3)) * LDT + b * 32 + r32] = acc[a][b][r];
       __syncthreads();
-      for (int e = lane; e < 4 * TN; e += 64) {
-        const int rr = wave * 4 + e / TN, cc = e % TN;
-        const float v = red[(0 * 16 + rr) * LDT + cc] + red[(1 * 16 + rr) * LDT + cc] +
-                        red[(2 * 16 + rr) * LDT + cc] + red[(3 * 16 + rr) * LDT + cc];
+      for (int e = threadIdx.x; e < 16 * TN; e += T::THREADS) {
+        const int rr = e / TN, cc = e % TN;
+        float v = red[rr * LDT + cc];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += red[(w * 16 + rr) * LDT + cc];
         const int row = m0 + a * 32 + q * 16 + rr, col = n0 + cc;
         if (row < M && col < N) {
           const float o = v * gscale;
@@ -377,18 +384,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   }
 }
 
-template <int WM, int WN, int STAGES, int WPE>
+template <int WM, int WN, int STAGES, int WPE, int KW>
 hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  using T = LdsTile<WM, WN, STAGES>;
+  using T = LdsTile<WM, WN, STAGES, KW>;
   static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE>,
+      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW>,
       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM));
-  gemm_lds_kernel<WM, WN, STAGES, WPE><<<grid, 256, T::LDS_BYTES, s>>>(
+  gemm_lds_kernel<WM, WN, STAGES, WPE, KW><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
       a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
@@ -401,8 +408,8 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   // the staged kernel takes whole 256-element chunks and 32-bit row offsets
   const bool big = fast && K % 256 == 0 && K >= 256 && M * (K / 2) < (1ll << 31) && N * (K / 2) < (1ll << 31);
   if (big)  // 128 x 64 tiles, two workgroups per CU, two stages
-    return launch_lds<4, 2, 2, 2>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M, N,
-                                  K, s);
+    return launch_lds<4, 2, 2, 2, 4>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M,
+                                     N, K, s);
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
   if (fast)
     gemm_f16_kernel<true><<<grid, 256, 0, s>>>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,
