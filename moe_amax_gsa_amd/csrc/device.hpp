@@ -306,6 +306,32 @@ __device__ __forceinline__ void quantize_block16(const void* __restrict__ x, int
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations (lgkmcnt 0) but leaves vector-memory loads in flight, unlike
 // __syncthreads(), whose release fence also drains them.
+// 16 bytes per lane from base + voff straight into LDS at byte address
+// lds_wave_base + 16 * lane (base and lds_wave_base uniform over the wave).
+// Issued as inline assembly so that the compiler does not fence every later
+// LDS read behind it (it cannot tell the stages apart); the kernel waits
+// for these loads itself with explicit vmcnt counts.  M0 carries the LDS
+// address; the compiler reserves M0, so its value is saved and restored
+// here, and one wait state separates the M0 write from the load.
+__device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t voff,
+                                           uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_wave_base), "v"(voff), "s"(base)
+      : "memory");
+}
+
+// LDS byte address of a pointer into dynamic shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -370,6 +370,188 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
   }
 }
 
+// ---------------------------------------------------------------- stream
+// Many independent (group, 16 weight rows) tiles -- the routed-expert
+// projections: every wave owns the whole K range of its 16 weight rows, so
+// no partial sums cross waves, and it keeps the next S super-chunks of its
+// weights in flight while it computes the current ones (two register
+// buffers, used alternately, so the loop never waits for a load it has just
+// issued).  The STREAM_WAVES waves of a workgroup take consecutive tiles of
+// one group and share its activation rows, 2 * MP per pass, which the
+// workgroup copies into LDS with direct global -> LDS loads once per pass:
+// the compute loop reads activations from LDS, never from behind the weight
+// stream.  Lane geometry and block-masked A rows as in gemv_fp4_kernel.
+// Requires K % 256 == 0 and 16-byte aligned operands.
+constexpr int STREAM_WAVES = 4;
+
+template <int S, int MP, int WPE = 1>
+__global__ __launch_bounds__(STREAM_WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(WPE))) void gemv_stream_kernel(const GemvArgs args) {
+  constexpr int ROWS = 2 * MP;
+  extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // codes, then scales
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, j = lane >> 4;
+  const int N = args.N, K = args.K;
+  const int g = blockIdx.y;
+  int r_begin = 0, r_end = args.M;
+  if (args.offsets != nullptr) {
+    r_begin = max(args.offsets[g], 0);
+    r_end = min(args.offsets[g + 1], args.M);
+  }
+  if (r_begin >= r_end) return;  // uniform over the workgroup
+
+  const int n0 = (blockIdx.x * STREAM_WAVES + wave) * 16;
+  const bool tile_ok = n0 < N;  // wave-uniform; a wave past the end only stages
+  const int64_t cbytes = K / 2, sbytes = K / 16;
+  const int64_t n_here = (n0 + col < N) ? n0 + col : N - 1;  // clamp: results discarded
+  const uint8_t* wrow = args.w_codes + ((int64_t)g * N + n_here) * cbytes;
+  const uint8_t* wsrow = args.w_scales + ((int64_t)g * N + n_here) * sbytes;
+  const int nsc = K / 256;
+  const int ngr = (nsc + S - 1) / S;
+
+  const int a_mloc = col >> 3, a_half = col & 1;
+  const bool a_has = ((col & 7) >> 1) == j;
+  const int c_mloc = j >> 1;
+
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(act_lds));
+  const uint8_t* lds_codes = act_lds;
+  const uint8_t* lds_scales = act_lds + ROWS * cbytes;
+  const int cpr = (int)(cbytes / 16), spr = (int)(sbytes / 16);  // 16-byte pieces per row
+
+  for (int r0 = r_begin; r0 < r_end; r0 += ROWS) {
+    // source row of each pass row (lane l < ROWS holds row l); -1: not a row
+    int my_src = -1;
+    if (lane < ROWS && r0 + lane < r_end) {
+      my_src = args.row_index != nullptr ? args.row_index[r0 + lane] : r0 + lane;
+      if (my_src < 0 || my_src >= args.a_rows) my_src = -1;
+    }
+
+    // first weight group in flight before the activation copy
+    uint4 xa0[S], xa1[S], xb0[S], xb1[S];
+    uint2 xsa[S], xsb[S];
+    if (tile_ok) load_w_group<S, true>(wrow, wsrow, 0, nsc, j, cbytes, sbytes, xa0, xa1, xsa);
+
+    // copy the pass rows' codes and scales into LDS (a row that is not a row
+    // copies row 0; its fragments are masked below)
+    __syncthreads();  // the previous pass has finished reading LDS
+    const int ncp = ROWS * cpr, nsp = ROWS * spr;
+    for (int base = wave * 64; base < ncp; base += STREAM_WAVES * 64) {
+      const int e = base + lane;
+      const int rl = e / cpr, q = e - rl * cpr;
+      const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
+      if (e < ncp)
+        load_lds16(args.a_codes, (uint32_t)((int64_t)max(src, 0) * cbytes + 16 * q),
+                   lds0 + 16 * (uint32_t)base);
+    }
+    for (int base = wave * 64; base < nsp; base += STREAM_WAVES * 64) {
+      const int e = base + lane;
+      const int rl = e / spr, q = e - rl * spr;
+      const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
+      if (e < nsp)
+        load_lds16(args.a_scales, (uint32_t)((int64_t)max(src, 0) * sbytes + 16 * q),
+                   lds0 + (uint32_t)(ROWS * cbytes) + 16 * (uint32_t)base);
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // fragment masks of the pass rows
+    bool aok[MP], sok[MP];
+#pragma unroll
+    for (int p = 0; p < MP; ++p) {
+      const int srca = __shfl(my_src, 2 * p + a_mloc, 64);
+      const int srcc = __shfl(my_src, 2 * p + c_mloc, 64);
+      aok[p] = a_has && srca >= 0;
+      sok[p] = srcc >= 0;
+    }
+    const int npairs = min(MP, (r_end - r0 + 1) / 2);
+
+    float acc[MP];
+#pragma unroll
+    for (int p = 0; p < MP; ++p) acc[p] = 0.f;
+
+    // tail: the last group may hold fewer than S chunks
+    auto compute = [&](const uint4 (&w0)[S], const uint4 (&w1)[S], const uint2 (&ws)[S], int cg,
+                       bool tail) {
+      float fw[S][8];
+#pragma unroll
+      for (int s = 0; s < S; ++s) fp8x8_to_f32(ws[s], fw[s]);
+#pragma unroll
+      for (int p = 0; p < MP; ++p) {
+        if (p >= npairs) break;  // uniform
+        const uint8_t* ac = lds_codes + (2 * p + a_mloc) * cbytes;
+        const uint8_t* as = lds_scales + (2 * p + c_mloc) * sbytes;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int c = cg * S + s;
+          if (tail && c >= nsc) break;  // uniform: past the last chunk
+          uint2 q0 = make_uint2(0u, 0u), q1 = make_uint2(0u, 0u), sa = make_uint2(0u, 0u);
+          if (aok[p]) {
+            q0 = *(const uint2*)(ac + (int64_t)c * 128 + 32 * j + 8 * a_half);
+            q1 = *(const uint2*)(ac + (int64_t)c * 128 + 32 * j + 8 * a_half + 16);
+          }
+          if (sok[p]) sa = *(const uint2*)(as + (int64_t)c * 16 + 8 * (j & 1));
+          const v8i A0 = a_half == 0 ? v8i{(int)q0.x, (int)q0.y, 0, 0, 0, 0, 0, 0}
+                                     : v8i{0, 0, (int)q0.x, (int)q0.y, 0, 0, 0, 0};
+          const v8i A1 = a_half == 0 ? v8i{(int)q1.x, (int)q1.y, 0, 0, 0, 0, 0, 0}
+                                     : v8i{0, 0, (int)q1.x, (int)q1.y, 0, 0, 0, 0};
+          const v8i B0 = {(int)w0[s].x, (int)w0[s].y, (int)w0[s].z, (int)w0[s].w, 0, 0, 0, 0};
+          const v8i B1 = {(int)w1[s].x, (int)w1[s].y, (int)w1[s].z, (int)w1[s].w, 0, 0, 0, 0};
+          float fa[8];
+          fp8x8_to_f32(sa, fa);
+          const float4_t c0 = mfma_fp4(A0, B0);
+          const float4_t c1 = mfma_fp4(A1, B1);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t0 = 4 * (r >> 1) + (r & 1);  // scale byte for MFMA 0
+            const int t1 = t0 + 2;                  // and for MFMA 1
+            acc[p] = fmaf(c0[r], fa[t0] * fw[s][t0], acc[p]);
+            acc[p] = fmaf(c1[r], fa[t1] * fw[s][t1], acc[p]);
+          }
+        }
+      }
+    };
+
+    if (tile_ok) {
+      // Groups alternate between the two buffers, the loads of group cg + 1
+      // issued before group cg is computed.  A counted loop of two groups
+      // per trip with no exit inside keeps each buffer in its registers (an
+      // exit inside makes the compiler copy a buffer at the back edge, which
+      // waits for its loads).
+      const int trips = (ngr - 1) / 2;
+      for (int t = 0; t < trips; ++t) {
+        load_w_group<S, true>(wrow, wsrow, 2 * t + 1, nsc, j, cbytes, sbytes, xb0, xb1, xsb);
+        compute(xa0, xa1, xsa, 2 * t, false);
+        load_w_group<S, true>(wrow, wsrow, 2 * t + 2, nsc, j, cbytes, sbytes, xa0, xa1, xsa);
+        compute(xb0, xb1, xsb, 2 * t + 1, false);
+      }
+      if ((ngr & 1) == 0) {
+        load_w_group<S, true>(wrow, wsrow, ngr - 1, nsc, j, cbytes, sbytes, xb0, xb1, xsb);
+        compute(xa0, xa1, xsa, ngr - 2, false);
+        compute(xb0, xb1, xsb, ngr - 1, true);
+      } else {
+        compute(xa0, xa1, xsa, ngr - 1, true);
+      }
+
+      const float gscale = args.gsa[0] * args.ws2[g];
+#pragma unroll
+      for (int p = 0; p < MP; ++p) {
+        // lanes of slices j and j^1 hold the same (row, column): add them
+        const float v = acc[p] + __shfl_xor(acc[p], 16, 64);
+        const int rl = 2 * p + c_mloc, r = r0 + rl, n = n0 + col;
+        const bool ok = (j & 1) == 0 && r < r_end && n < N && __shfl(my_src, rl, 64) >= 0;
+        if (ok) {
+          if (args.y_bf16)
+            ((uint16_t*)args.y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v * gscale);
+          else
+            ((float*)args.y)[(int64_t)r * N + n] = v * gscale;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- narrow
 // Few activation rows and few weight rows per workgroup: RQ quads of 4
 // weight rows per workgroup (8 rows at decode sizes) so that a decode-sized
@@ -589,6 +771,7 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int S_GROUP = 4;
+constexpr int S_STREAM = 2;
 
 static int waves_for(int64_t K, int S = S_GROUP) {
   const int64_t nsc = (K + 255) / 256;
@@ -605,6 +788,40 @@ static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hip
   else
     gemv_fp4_kernel<S, MP, false, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int S, int MP, int WPE = 1>
+static hipError_t launch_stream_t(const GemvArgs& a, int G, size_t lds, hipStream_t s) {
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_stream_kernel<S, MP, WPE>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)((a.N + 16 * STREAM_WAVES - 1) / (16 * STREAM_WAVES)), (unsigned)G);
+  gemv_stream_kernel<S, MP, WPE><<<grid, STREAM_WAVES * 64, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+// Rows per pass of the streaming kernel: enough for most groups (a group
+// with more rows streams its weights once more per extra pass), within
+// STREAM_MAX_LDS bytes of staged activation.  0: K too long to stage.
+constexpr int64_t STREAM_MAX_LDS = 64 * 1024;
+
+static int stream_pairs(int64_t mean_rows, int64_t K) {
+  const int64_t row_bytes = K / 2 + K / 16;
+  int mp = mean_rows <= 4 ? 4 : 8;
+  while (mp > 0 && 2 * mp * row_bytes > STREAM_MAX_LDS) mp /= 2;
+  return mp;
+}
+
+// at most 256 registers (two workgroups of four waves per CU) where that
+// does not spill
+static hipError_t launch_stream(const GemvArgs& a, int G, int mp, hipStream_t s) {
+  const size_t lds = (size_t)(2 * mp) * (size_t)(a.K / 2 + a.K / 16);
+  if (mp >= 8) return launch_stream_t<S_STREAM, 8, 1>(a, G, lds, s);
+  if (mp >= 4) return launch_stream_t<S_STREAM, 4, 2>(a, G, lds, s);
+  if (mp >= 2) return launch_stream_t<S_STREAM, 2, 2>(a, G, lds, s);
+  return launch_stream_t<S_STREAM, 1, 2>(a, G, lds, s);
 }
 
 template <int MODE>
@@ -757,6 +974,11 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
   // rows per pass from the mean group size (groups larger than a pass make
   // more passes over the same weight tile, which then comes from L2)
   const int64_t mean_rows = (M_total + G - 1) / G;
+  if (fast) {
+    // activation copy offsets are 32-bit
+    const int mp = stream_pairs(mean_rows, K);
+    if (mp > 0 && a_rows * (K / 2) < ((int64_t)1 << 31)) return launch_stream(a, G, mp, s);
+  }
   dim3 grid((unsigned)((N + 15) / 16), (unsigned)G);
   if (mean_rows <= 2 && K >= 4096) {
     // long K, few rows: two super-chunks per wave in flight instead of four

@@ -432,6 +432,46 @@ def test_grouped_row_index_bounds(C):
         assert np.array_equal(yh[r], ref[0])
 
 
+@pytest.mark.parametrize("K,N", [(256, 72), (768, 64), (1280, 40), (2048, 136)])
+def test_grouped_stream_shapes(C, K, N):
+    """Grouped linear on 16-byte aligned operands with K % 256 == 0: group
+    sizes 0 .. 19 (several passes of rows), invalid row indices, K giving one,
+    two and three weight groups per wave with a partial last group, N with
+    partial tiles.  Every written row against the oracle; invalid rows and
+    rows past the last group stay unwritten."""
+    say(f"grouped stream K={K} N={N}")
+    rng = np.random.default_rng(K + N)
+    sizes = [3, 0, 1, 19, 2, 0, 5, 9]
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    P = int(offsets[-1])
+    a_rows = 11
+    row_index = rng.integers(0, a_rows, P + 3).astype(np.int32)
+    row_index[[4, 10, 20]] = [-1, a_rows, 1 << 20]  # invalid: not written
+    ac = rng.integers(0, 256, (a_rows, K // 2), dtype=np.uint8)
+    asf = rng.integers(0x20, 0x48, (a_rows, K // 16), dtype=np.uint8)
+    wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    wsf = rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8)
+    ws2 = rng.uniform(0.002, 0.01, G).astype(np.float32)
+    gsa = np.float32(0.37)
+    y = torch.full((P + 3, N), -7.0, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(to_dev(ac), to_dev(asf), to_dev(np.array([gsa], np.float32)),
+                           to_dev(row_index), to_dev(offsets), to_dev(wc), to_dev(wsf),
+                           to_dev(ws2), y)
+    yh = y.cpu().numpy().astype(np.float64)
+    assert np.all(yh[P:] == -7.0)
+    for g in range(G):
+        for r in range(offsets[g], offsets[g + 1]):
+            src = int(row_index[r])
+            if src < 0 or src >= a_rows:
+                assert np.all(yh[r] == -7.0), r
+                continue
+            ref = oracle.linear(ac[src:src + 1], asf[src:src + 1], float(gsa), wc[g], wsf[g],
+                                float(ws2[g]))[0]
+            err = np.max(np.abs(yh[r] - ref)) / max(np.max(np.abs(ref)), 1e-30)
+            assert err <= REL_TOL, (g, r, err)
+
+
 def test_swiglu_parity(C):
     say("swiglu")
     rng = np.random.default_rng(1)
