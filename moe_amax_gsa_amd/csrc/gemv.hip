@@ -370,25 +370,51 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
   }
 }
 
-// ---------------------------------------------------------------- stream
+// ---------------------------------------------------------------- ring
 // Many independent (group, 16 weight rows) tiles -- the routed-expert
-// projections: every wave owns the whole K range of its 16 weight rows, so
-// no partial sums cross waves, and it keeps the next S super-chunks of its
-// weights in flight while it computes the current ones (two register
-// buffers, used alternately, so the loop never waits for a load it has just
-// issued).  The STREAM_WAVES waves of a workgroup take consecutive tiles of
-// one group and share its activation rows, 2 * MP per pass, which the
-// workgroup copies into LDS with direct global -> LDS loads once per pass:
-// the compute loop reads activations from LDS, never from behind the weight
-// stream.  Lane geometry and block-masked A rows as in gemv_fp4_kernel.
-// Requires K % 256 == 0 and 16-byte aligned operands.
-constexpr int STREAM_WAVES = 4;
+// projections.  Every wave owns the whole K range of its 16 weight rows, so
+// no partial sums cross waves.  The W waves of a workgroup take consecutive
+// tiles of one group and share its activation rows, 2 * MP per pass, which
+// the workgroup copies into LDS with direct global -> LDS loads once per
+// pass.  The weight stream goes through LDS as well: an HBM read in which
+// every load instruction covers whole 128-byte lines of 8 rows runs about a
+// fifth faster than one covering half lines of 16 rows, which is what
+// loading a 16-row MFMA operand straight into registers amounts to.  Each
+// wave owns a private ring of D slots of one super-chunk (16 rows x 128
+// bytes), each filled by two direct global -> LDS loads, and copies all of
+// its tile's weight scales into LDS once.  Piece p of a row r sits at slot
+// p ^ (r & 7), so the MFMA-layout reads of eight rows hit eight bank groups.
+// The wave waits for a slot with an explicit vmcnt (no other vector memory
+// instruction is issued inside its loop) and refills it after computing it.
+constexpr int RING_SLOT = 16 * 128;  // bytes of one super-chunk of 16 rows
 
-template <int S, int MP, int WPE = 1>
-__global__ __launch_bounds__(STREAM_WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(WPE))) void gemv_stream_kernel(const GemvArgs args) {
+// wait until at most n vector memory instructions of this wave are in flight
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: __asm__ volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: __asm__ volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: __asm__ volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: __asm__ volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: __asm__ volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: __asm__ volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: __asm__ volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: __asm__ volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 12: __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 13: __asm__ volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    default: __asm__ volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+  }
+}
+
+template <int MP, int D, int W>
+__global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) {
+  static_assert(2 * (D - 1) <= 14, "wait_vm range");
   constexpr int ROWS = 2 * MP;
-  extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // codes, then scales
+  constexpr int SLOT = RING_SLOT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -402,42 +428,82 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_stream_kernel(const GemvArgs
   }
   if (r_begin >= r_end) return;  // uniform over the workgroup
 
-  const int n0 = (blockIdx.x * STREAM_WAVES + wave) * 16;
+  const int n0 = (blockIdx.x * W + wave) * 16;
   const bool tile_ok = n0 < N;  // wave-uniform; a wave past the end only stages
   const int64_t cbytes = K / 2, sbytes = K / 16;
-  const int64_t n_here = (n0 + col < N) ? n0 + col : N - 1;  // clamp: results discarded
-  const uint8_t* wrow = args.w_codes + ((int64_t)g * N + n_here) * cbytes;
-  const uint8_t* wsrow = args.w_scales + ((int64_t)g * N + n_here) * sbytes;
   const int nsc = K / 256;
-  const int ngr = (nsc + S - 1) / S;
 
   const int a_mloc = col >> 3, a_half = col & 1;
   const bool a_has = ((col & 7) >> 1) == j;
   const int c_mloc = j >> 1;
 
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(act_lds));
-  const uint8_t* lds_codes = act_lds;
-  const uint8_t* lds_scales = act_lds + ROWS * cbytes;
+  // LDS: activation rows (codes, then scales), then per wave its weight
+  // scales (16 rows x K/16 bytes) and its ring of D slots
+  const uint32_t act_bytes = (uint32_t)(ROWS * (cbytes + sbytes));
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  const uint32_t wave_off = act_bytes + (uint32_t)wave * (uint32_t)(K + D * SLOT);
+  const uint32_t ws_lds = lds0 + wave_off, ring_lds = ws_lds + (uint32_t)K;
+  const uint8_t* lds_codes = lds;
+  const uint8_t* lds_scales = lds + ROWS * cbytes;
+  const uint8_t* ws_area = lds + wave_off;
+  const uint8_t* ring = lds + wave_off + K;
   const int cpr = (int)(cbytes / 16), spr = (int)(sbytes / 16);  // 16-byte pieces per row
 
+  // weight rows of the tile relative to row n0 (clamped: results discarded)
+  const int64_t tile_row0 = (int64_t)g * N + (tile_ok ? n0 : 0);
+  const uint8_t* wbase = args.w_codes + tile_row0 * cbytes;
+  const uint8_t* wsbase = args.w_scales + tile_row0 * sbytes;
+  // ring loads: lane l of load i takes row 8i + l/8, piece (l % 8) ^ (row % 8)
+  uint32_t ring_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const int rc = (tile_ok && n0 + r < N) ? r : max(N - 1 - n0, 0);
+    ring_off[i] = (uint32_t)(rc * cbytes + 16 * ((lane & 7) ^ (r & 7)));
+  }
+  auto issue_slot = [&](int c) {
+    const uint32_t slot = ring_lds + (uint32_t)(c % D) * SLOT;
+    load_lds16(wbase, ring_off[0] + 128u * (uint32_t)c, slot);
+    load_lds16(wbase, ring_off[1] + 128u * (uint32_t)c, slot + 1024u);
+  };
+
   for (int r0 = r_begin; r0 < r_end; r0 += ROWS) {
-    // source row of each pass row (lane l < ROWS holds row l); -1: not a row
     int my_src = -1;
     if (lane < ROWS && r0 + lane < r_end) {
       my_src = args.row_index != nullptr ? args.row_index[r0 + lane] : r0 + lane;
       if (my_src < 0 || my_src >= args.a_rows) my_src = -1;
     }
-
-    // first weight group in flight before the activation copy
-    uint4 xa0[S], xa1[S], xb0[S], xb1[S];
-    uint2 xsa[S], xsb[S];
-    if (tile_ok) load_w_group<S, true>(wrow, wsrow, 0, nsc, j, cbytes, sbytes, xa0, xa1, xsa);
-
-    // copy the pass rows' codes and scales into LDS (a row that is not a row
-    // copies row 0; its fragments are masked below)
+    // fragment masks of the pass rows -- this first use of the row indices
+    // also waits for their loads before any direct-to-LDS load is issued
+    // (the compiler does not count those)
+    bool aok[MP], sok[MP];
+#pragma unroll
+    for (int p = 0; p < MP; ++p) {
+      const int srca = __shfl(my_src, 2 * p + a_mloc, 64);
+      const int srcc = __shfl(my_src, 2 * p + c_mloc, 64);
+      aok[p] = a_has && srca >= 0;
+      sok[p] = srcc >= 0;
+    }
+    const int npairs = min(MP, (r_end - r0 + 1) / 2);
     __syncthreads();  // the previous pass has finished reading LDS
+
+    if (tile_ok) {
+      // the tile's weight scales (once), then the first D slots
+      if (r0 == r_begin) {
+        for (int e0 = 0; e0 < 16 * spr; e0 += 64) {
+          const int e = e0 + lane;
+          const int r = e / spr, q = e - r * spr;
+          const int rc = (n0 + r < N) ? r : N - 1 - n0;
+          if (e < 16 * spr)
+            load_lds16(wsbase, (uint32_t)(rc * sbytes + 16 * q), ws_lds + 16u * (uint32_t)e0);
+        }
+      }
+      for (int c = 0; c < D && c < nsc; ++c) issue_slot(c);
+    }
+    // the pass rows' activation codes and scales (a missing row copies row 0
+    // and is masked below)
     const int ncp = ROWS * cpr, nsp = ROWS * spr;
-    for (int base = wave * 64; base < ncp; base += STREAM_WAVES * 64) {
+    for (int base = wave * 64; base < ncp; base += W * 64) {
       const int e = base + lane;
       const int rl = e / cpr, q = e - rl * cpr;
       const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
@@ -445,7 +511,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_stream_kernel(const GemvArgs
         load_lds16(args.a_codes, (uint32_t)((int64_t)max(src, 0) * cbytes + 16 * q),
                    lds0 + 16 * (uint32_t)base);
     }
-    for (int base = wave * 64; base < nsp; base += STREAM_WAVES * 64) {
+    for (int base = wave * 64; base < nsp; base += W * 64) {
       const int e = base + lane;
       const int rl = e / spr, q = e - rl * spr;
       const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
@@ -456,88 +522,62 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_stream_kernel(const GemvArgs
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // fragment masks of the pass rows
-    bool aok[MP], sok[MP];
-#pragma unroll
-    for (int p = 0; p < MP; ++p) {
-      const int srca = __shfl(my_src, 2 * p + a_mloc, 64);
-      const int srcc = __shfl(my_src, 2 * p + c_mloc, 64);
-      aok[p] = a_has && srca >= 0;
-      sok[p] = srcc >= 0;
-    }
-    const int npairs = min(MP, (r_end - r0 + 1) / 2);
 
     float acc[MP];
 #pragma unroll
     for (int p = 0; p < MP; ++p) acc[p] = 0.f;
 
-    // tail: the last group may hold fewer than S chunks
-    auto compute = [&](const uint4 (&w0)[S], const uint4 (&w1)[S], const uint2 (&ws)[S], int cg,
-                       bool tail) {
-      float fw[S][8];
+    if (tile_ok) {
+      for (int c = 0; c < nsc; ++c) {
+        // slots c + 1 .. c + D - 1 may still be in flight
+        wait_vm(2 * min(D - 1, nsc - 1 - c));
+        const uint8_t* sl = ring + (c % D) * SLOT + col * 128;
+        const uint4 w0 = *(const uint4*)(sl + 16 * ((2 * j) ^ (col & 7)));
+        const uint4 w1 = *(const uint4*)(sl + 16 * ((2 * j + 1) ^ (col & 7)));
+        const uint2 wsc = *(const uint2*)(ws_area + col * sbytes + (int64_t)c * 16 + 8 * (j & 1));
+        float fw[8];
+        fp8x8_to_f32(wsc, fw);
+        const v8i B0 = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, 0, 0, 0, 0};
+        const v8i B1 = {(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w, 0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < S; ++s) fp8x8_to_f32(ws[s], fw[s]);
-#pragma unroll
-      for (int p = 0; p < MP; ++p) {
-        if (p >= npairs) break;  // uniform
-        const uint8_t* ac = lds_codes + (2 * p + a_mloc) * cbytes;
-        const uint8_t* as = lds_scales + (2 * p + c_mloc) * sbytes;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int c = cg * S + s;
-          if (tail && c >= nsc) break;  // uniform: past the last chunk
+        for (int p = 0; p < MP; ++p) {
+          if (p >= npairs) break;  // uniform
+          const uint8_t* ac = lds_codes + (2 * p + a_mloc) * cbytes + (int64_t)c * 128 + 32 * j +
+                              8 * a_half;
           uint2 q0 = make_uint2(0u, 0u), q1 = make_uint2(0u, 0u), sa = make_uint2(0u, 0u);
           if (aok[p]) {
-            q0 = *(const uint2*)(ac + (int64_t)c * 128 + 32 * j + 8 * a_half);
-            q1 = *(const uint2*)(ac + (int64_t)c * 128 + 32 * j + 8 * a_half + 16);
+            q0 = *(const uint2*)ac;
+            q1 = *(const uint2*)(ac + 16);
           }
-          if (sok[p]) sa = *(const uint2*)(as + (int64_t)c * 16 + 8 * (j & 1));
+          if (sok[p])
+            sa = *(const uint2*)(lds_scales + (2 * p + c_mloc) * sbytes + (int64_t)c * 16 +
+                                 8 * (j & 1));
           const v8i A0 = a_half == 0 ? v8i{(int)q0.x, (int)q0.y, 0, 0, 0, 0, 0, 0}
                                      : v8i{0, 0, (int)q0.x, (int)q0.y, 0, 0, 0, 0};
           const v8i A1 = a_half == 0 ? v8i{(int)q1.x, (int)q1.y, 0, 0, 0, 0, 0, 0}
                                      : v8i{0, 0, (int)q1.x, (int)q1.y, 0, 0, 0, 0};
-          const v8i B0 = {(int)w0[s].x, (int)w0[s].y, (int)w0[s].z, (int)w0[s].w, 0, 0, 0, 0};
-          const v8i B1 = {(int)w1[s].x, (int)w1[s].y, (int)w1[s].z, (int)w1[s].w, 0, 0, 0, 0};
           float fa[8];
           fp8x8_to_f32(sa, fa);
           const float4_t c0 = mfma_fp4(A0, B0);
           const float4_t c1 = mfma_fp4(A1, B1);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int t0 = 4 * (r >> 1) + (r & 1);  // scale byte for MFMA 0
-            const int t1 = t0 + 2;                  // and for MFMA 1
-            acc[p] = fmaf(c0[r], fa[t0] * fw[s][t0], acc[p]);
-            acc[p] = fmaf(c1[r], fa[t1] * fw[s][t1], acc[p]);
+            const int t0 = 4 * (r >> 1) + (r & 1);
+            const int t1 = t0 + 2;
+            acc[p] = fmaf(c0[r], fa[t0] * fw[t0], acc[p]);
+            acc[p] = fmaf(c1[r], fa[t1] * fw[t1], acc[p]);
           }
         }
-      }
-    };
-
-    if (tile_ok) {
-      // Groups alternate between the two buffers, the loads of group cg + 1
-      // issued before group cg is computed.  A counted loop of two groups
-      // per trip with no exit inside keeps each buffer in its registers (an
-      // exit inside makes the compiler copy a buffer at the back edge, which
-      // waits for its loads).
-      const int trips = (ngr - 1) / 2;
-      for (int t = 0; t < trips; ++t) {
-        load_w_group<S, true>(wrow, wsrow, 2 * t + 1, nsc, j, cbytes, sbytes, xb0, xb1, xsb);
-        compute(xa0, xa1, xsa, 2 * t, false);
-        load_w_group<S, true>(wrow, wsrow, 2 * t + 2, nsc, j, cbytes, sbytes, xa0, xa1, xsa);
-        compute(xb0, xb1, xsb, 2 * t + 1, false);
-      }
-      if ((ngr & 1) == 0) {
-        load_w_group<S, true>(wrow, wsrow, ngr - 1, nsc, j, cbytes, sbytes, xb0, xb1, xsb);
-        compute(xa0, xa1, xsa, ngr - 2, false);
-        compute(xb0, xb1, xsb, ngr - 1, true);
-      } else {
-        compute(xa0, xa1, xsa, ngr - 1, true);
+        // refill this slot once its reads have returned
+        if (c + D < nsc) {
+          __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          issue_slot(c + D);
+        }
       }
 
       const float gscale = args.gsa[0] * args.ws2[g];
 #pragma unroll
       for (int p = 0; p < MP; ++p) {
-        // lanes of slices j and j^1 hold the same (row, column): add them
         const float v = acc[p] + __shfl_xor(acc[p], 16, 64);
         const int rl = 2 * p + c_mloc, r = r0 + rl, n = n0 + col;
         const bool ok = (j & 1) == 0 && r < r_end && n < N && __shfl(my_src, rl, 64) >= 0;
@@ -550,6 +590,25 @@ __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_stream_kernel(const GemvArgs
       }
     }
   }
+}
+
+template <int MP, int D, int W>
+static size_t ring_lds_bytes(int64_t K) {
+  return (size_t)(2 * MP) * (size_t)(K / 2 + K / 16) +
+         (size_t)W * (size_t)(K + D * RING_SLOT);
+}
+
+template <int MP, int D, int W>
+static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
+  const size_t lds = ring_lds_bytes<MP, D, W>(a.K);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_ring_kernel<MP, D, W>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)((a.N + 16 * W - 1) / (16 * W)), (unsigned)G);
+  gemv_ring_kernel<MP, D, W><<<grid, W * 64, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- narrow
@@ -771,7 +830,6 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int S_GROUP = 4;
-constexpr int S_STREAM = 2;
 
 static int waves_for(int64_t K, int S = S_GROUP) {
   const int64_t nsc = (K + 255) / 256;
@@ -790,38 +848,23 @@ static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hip
   return hipGetLastError();
 }
 
-template <int S, int MP, int WPE = 1>
-static hipError_t launch_stream_t(const GemvArgs& a, int G, size_t lds, hipStream_t s) {
-  if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_stream_kernel<S, MP, WPE>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const dim3 grid((unsigned)((a.N + 16 * STREAM_WAVES - 1) / (16 * STREAM_WAVES)), (unsigned)G);
-  gemv_stream_kernel<S, MP, WPE><<<grid, STREAM_WAVES * 64, lds, s>>>(a);
-  return hipGetLastError();
+// Grouped linear through the LDS ring: the most activation rows per pass
+// (two workgroups per CU where that fits, else one) whose LDS fits
+// RING_MAX_LDS.  false: K too long to stage.
+constexpr size_t RING_MAX_LDS = 160 * 1024;
+
+template <int MP, int D, int W>
+static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err) {
+  if (ring_lds_bytes<MP, D, W>(a.K) > RING_MAX_LDS) return false;
+  *err = launch_ring_t<MP, D, W>(a, G, s);
+  return true;
 }
 
-// Rows per pass of the streaming kernel: enough for most groups (a group
-// with more rows streams its weights once more per extra pass), within
-// STREAM_MAX_LDS bytes of staged activation.  0: K too long to stage.
-constexpr int64_t STREAM_MAX_LDS = 64 * 1024;
-
-static int stream_pairs(int64_t mean_rows, int64_t K) {
-  const int64_t row_bytes = K / 2 + K / 16;
-  int mp = mean_rows <= 4 ? 4 : 8;
-  while (mp > 0 && 2 * mp * row_bytes > STREAM_MAX_LDS) mp /= 2;
-  return mp;
-}
-
-// at most 256 registers (two workgroups of four waves per CU) where that
-// does not spill
-static hipError_t launch_stream(const GemvArgs& a, int G, int mp, hipStream_t s) {
-  const size_t lds = (size_t)(2 * mp) * (size_t)(a.K / 2 + a.K / 16);
-  if (mp >= 8) return launch_stream_t<S_STREAM, 8, 1>(a, G, lds, s);
-  if (mp >= 4) return launch_stream_t<S_STREAM, 4, 2>(a, G, lds, s);
-  if (mp >= 2) return launch_stream_t<S_STREAM, 2, 2>(a, G, lds, s);
-  return launch_stream_t<S_STREAM, 1, 2>(a, G, lds, s);
+static bool launch_ring(const GemvArgs& a, int G, int64_t mean_rows, hipStream_t s,
+                        hipError_t* err) {
+  if (mean_rows > 4 && ring_try<8, 3, 4>(a, G, s, err)) return true;
+  return ring_try<4, 3, 8>(a, G, s, err) || ring_try<4, 3, 4>(a, G, s, err) ||
+         ring_try<2, 3, 4>(a, G, s, err) || ring_try<1, 3, 2>(a, G, s, err);
 }
 
 template <int MODE>
@@ -974,10 +1017,9 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
   // rows per pass from the mean group size (groups larger than a pass make
   // more passes over the same weight tile, which then comes from L2)
   const int64_t mean_rows = (M_total + G - 1) / G;
-  if (fast) {
-    // activation copy offsets are 32-bit
-    const int mp = stream_pairs(mean_rows, K);
-    if (mp > 0 && a_rows * (K / 2) < ((int64_t)1 << 31)) return launch_stream(a, G, mp, s);
+  if (fast && a_rows * (K / 2) < ((int64_t)1 << 31)) {  // copy offsets are 32-bit
+    hipError_t err = hipSuccess;
+    if (launch_ring(a, G, mean_rows, s, &err)) return err;
   }
   dim3 grid((unsigned)((N + 15) / 16), (unsigned)G);
   if (mean_rows <= 2 && K >= 4096) {

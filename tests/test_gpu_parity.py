@@ -432,16 +432,18 @@ def test_grouped_row_index_bounds(C):
         assert np.array_equal(yh[r], ref[0])
 
 
+@pytest.mark.parametrize("sizes", [[3, 0, 1, 19, 2, 0, 5, 9], [3, 0, 1, 4, 2, 0, 7, 1]],
+                         ids=["large-groups", "small-groups"])
 @pytest.mark.parametrize("K,N", [(256, 72), (768, 64), (1280, 40), (2048, 136)])
-def test_grouped_stream_shapes(C, K, N):
+def test_grouped_ring_shapes(C, K, N, sizes):
     """Grouped linear on 16-byte aligned operands with K % 256 == 0: group
-    sizes 0 .. 19 (several passes of rows), invalid row indices, K giving one,
-    two and three weight groups per wave with a partial last group, N with
-    partial tiles.  Every written row against the oracle; invalid rows and
-    rows past the last group stay unwritten."""
-    say(f"grouped stream K={K} N={N}")
-    rng = np.random.default_rng(K + N)
-    sizes = [3, 0, 1, 19, 2, 0, 5, 9]
+    sizes 0 .. 19 (a mean above 4 rows takes 16 rows per pass, else 8, so
+    the 19-row group makes two passes), invalid row indices, K of 1, 3, 5
+    and 8 super-chunks against a 3-slot ring, N with partial tiles and whole
+    idle waves.  Every written row against the oracle; invalid rows and rows
+    past the last group stay unwritten."""
+    say(f"grouped ring K={K} N={N} sizes={sizes}")
+    rng = np.random.default_rng(K + N + sum(sizes))
     G = len(sizes)
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     P = int(offsets[-1])
