@@ -327,6 +327,182 @@ __device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t voff,
       : "memory");
 }
 
+// N direct loads from one base in a single block: 16 bytes per lane from
+// base + voff[i] into LDS at m0_first + i * stride + 16 * lane.  Every offset
+// sits in its own register while the loads issue; computing them one at a
+// time into one register would make each address wait until the previous
+// load has read it.
+template <int N>
+__device__ __forceinline__ void load_lds16_run(const uint8_t* base, const uint32_t (&voff)[N],
+                                               uint32_t m0_first, uint32_t stride) {
+  static_assert(N >= 1 && N <= 8, "1 to 8 loads");
+  uint32_t saved;
+  if constexpr (N == 1)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %4\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "s"(base)
+        : "memory");
+  else if constexpr (N == 2)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %5\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %5\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "v"(voff[1]), "s"(base)
+        : "memory");
+  else if constexpr (N == 3)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %6\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %6\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %6\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "s"(base)
+        : "memory");
+  else if constexpr (N == 4)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %7\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %7\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %7\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, %7\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(base)
+        : "memory");
+  else if constexpr (N == 5)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %8\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %8\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %8\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, %8\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, %8\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "s"(base)
+        : "memory");
+  else if constexpr (N == 6)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %9\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %9\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %9\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, %9\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, %9\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %8, %9\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "s"(base)
+        : "memory");
+  else if constexpr (N == 7)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %10\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %10\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %10\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, %10\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, %10\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %8, %10\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %9, %10\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]), "s"(base)
+        : "memory");
+  else if constexpr (N == 8)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %11\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %11\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %11\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, %11\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, %11\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %8, %11\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %9, %11\n\t"
+        "s_add_u32 m0, m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %10, %11\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0_first), "s"(stride), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]), "v"(voff[7]), "s"(base)
+        : "memory");
+}
+
 // LDS byte address of a pointer into dynamic shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;

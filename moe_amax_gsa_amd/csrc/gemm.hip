@@ -228,13 +228,18 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const uint32_t ssrc = (srow < TM ? (uint32_t)min(m0 + srow, M - 1) * sbytes
                                    : (uint32_t)min(n0 + srow - TM, N - 1) * sbytes) + spiece;
 
+  // code loads 0 .. NA-1 read A rows, the rest W rows; load i fills LDS at
+  // stage + 1024 (KW i + wave)
+  constexpr int NA = TM / (T::RPL * KW), NB = T::CODE_LOADS - NA;
   auto issue = [&](int chunk, int stage) {
     const uint32_t st = smem_base + stage * T::STAGE_BYTES;
+    uint32_t va[NA], vb[NB];
 #pragma unroll
-    for (int i = 0; i < T::CODE_LOADS; ++i) {
-      const uint8_t* base = (T::RPL * KW * i < TM) ? a_codes : w_codes;  // the same for the load
-      load_lds16(base, csrc[i] + (uint32_t)chunk * T::CB, st + 1024 * (KW * i + wave));
-    }
+    for (int i = 0; i < NA; ++i) va[i] = csrc[i] + (uint32_t)chunk * T::CB;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) vb[i] = csrc[NA + i] + (uint32_t)chunk * T::CB;
+    load_lds16_run<NA>(a_codes, va, st + 1024 * wave, 1024 * KW);
+    load_lds16_run<NB>(w_codes, vb, st + 1024 * (KW * NA + wave), 1024 * KW);
     const uint32_t sdst = st + T::CODE_BYTES + 1024 * wave;
     if (wave < TM / T::SRL)
       load_lds16(a_scales, ssrc + (uint32_t)chunk * T::SB, sdst);
@@ -259,9 +264,15 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, nch - 1), s0);
 
   for (int c = 0; c < nch; ++c) {
-    // chunks c+1 .. c+STAGES-2 may still be in flight (fewest loads per wave)
-    constexpr int PER_CHUNK = T::CODE_LOADS + (T::SCALE_LOADS == KW ? 1 : 0);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * PER_CHUNK) : "memory");
+    // chunks c+1 .. c+STAGES-2 may still be in flight: this wave issues its
+    // code loads per chunk, and one scale load if it is one of the first
+    // SCALE_LOADS waves
+    constexpr int W_SCALE = (STAGES - 2) * (T::CODE_LOADS + 1);
+    constexpr int W_CODE = (STAGES - 2) * T::CODE_LOADS;
+    if (wave < T::SCALE_LOADS)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_SCALE) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_CODE) : "memory");
     lds_barrier();
     issue(min(c + STAGES - 1, nch - 1), (c + STAGES - 1) % STAGES);
 
