@@ -90,6 +90,51 @@ __device__ __forceinline__ uint32_t e2m1_codes8_hw(const float v[8], float sc) {
   return c;
 }
 
+// The same codes as e2m1_codes8_hw without eight divisions.  Each quotient
+// q is formed with the hardware reciprocal: q = v * rcp(sc) lies within
+// 2^-22 |v / sc| of v / sc, and so of the correctly rounded quotient.  q is
+// converted twice, nudged up and down by 2^-20 of itself.  Rounding to E2M1
+// is monotone in the magnitude, so where both conversions agree it is
+// constant over that window, which holds the correctly rounded quotient:
+// its code is the agreed one.  Where they differ a rounding boundary (a
+// tie) is near, and the quotients are divided exactly.  sc > 0, normal.
+__device__ __forceinline__ uint32_t e2m1_codes8(const float v[8], float sc) {
+#pragma clang fp contract(off)
+  const float r = __builtin_amdgcn_rcpf(sc);
+  float u[8], d[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = v[i] * r;
+    u[i] = fmaf(q, 0x1p-20f, q);
+    d[i] = fmaf(q, -0x1p-20f, q);
+  }
+  uint32_t up = 0, dn = 0;
+  up = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(up, u[0], u[1], 1.0f, 0);
+  up = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(up, u[2], u[3], 1.0f, 1);
+  up = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(up, u[4], u[5], 1.0f, 2);
+  up = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(up, u[6], u[7], 1.0f, 3);
+  dn = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dn, d[0], d[1], 1.0f, 0);
+  dn = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dn, d[2], d[3], 1.0f, 1);
+  dn = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dn, d[4], d[5], 1.0f, 2);
+  dn = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dn, d[6], d[7], 1.0f, 3);
+  if (up == dn) return up;
+  return e2m1_codes8_hw(v, sc);
+}
+
+// e4m3_encode_hw(a / b) for a >= 0, b > 0 normal, without the division
+// where it is not needed: as in e2m1_codes8, the quotient from the hardware
+// reciprocal is encoded nudged up and down by 2^-20 of itself (E4M3
+// rounding with saturation is monotone); the exact quotient is formed only
+// where the two encodings differ.
+__device__ __forceinline__ uint32_t e4m3_of_quotient(float a, float b) {
+#pragma clang fp contract(off)
+  const float q = a * __builtin_amdgcn_rcpf(b);
+  const uint32_t up = e4m3_encode_hw(fmaf(q, 0x1p-20f, q));
+  const uint32_t dn = e4m3_encode_hw(fmaf(q, -0x1p-20f, q));
+  if (up == dn) return up;
+  return e4m3_encode_hw(a / b);
+}
+
 // Signs only (the codes of a block whose scale rounded to 0).
 __device__ __forceinline__ uint32_t e2m1_signs8(const float v[8]) {
   uint32_t c = 0;
@@ -208,8 +253,7 @@ __device__ __forceinline__ void quantize_vals16(const float v[16], float gsa, ui
 #pragma clang fp contract(off)
   const float bamax = block_absmax16(v);
   const float six_gsa = gsa * 6.0f;
-  const float sf_raw = bamax / six_gsa;
-  sf = e4m3_encode_hw(sf_raw);
+  sf = e4m3_of_quotient(bamax, six_gsa);
   const float sdec = e4m3_decode(sf);
   const float sc = sdec * gsa;
   if (sdec == 0.0f) {  // every magnitude rounds to 0; signs stay
@@ -217,8 +261,8 @@ __device__ __forceinline__ void quantize_vals16(const float v[16], float gsa, ui
     hi = e2m1_signs8(v + 8);
     return;
   }
-  lo = e2m1_codes8_hw(v, sc);
-  hi = e2m1_codes8_hw(v + 8, sc);
+  lo = e2m1_codes8(v, sc);
+  hi = e2m1_codes8(v + 8, sc);
 }
 
 // Half-block layout: thread h owns elements 8h .. 8h+7 (one 16-byte bf16
@@ -288,11 +332,10 @@ __device__ __forceinline__ void quantize_half8(const float v[8], float bamax, fl
                                                uint32_t& codes, uint32_t& sf) {
 #pragma clang fp contract(off)
   const float six_gsa = gsa * 6.0f;
-  const float sf_raw = bamax / six_gsa;
-  sf = e4m3_encode_hw(sf_raw);
+  sf = e4m3_of_quotient(bamax, six_gsa);
   const float sdec = e4m3_decode(sf);
   const float sc = sdec * gsa;
-  codes = sdec == 0.0f ? e2m1_signs8(v) : e2m1_codes8_hw(v, sc);
+  codes = sdec == 0.0f ? e2m1_signs8(v) : e2m1_codes8(v, sc);
 }
 
 template <bool BF16>

@@ -724,8 +724,10 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     if (lane == 0) amax_red[wave] = mx;
     lds_barrier();
-    float mm = 0.f;
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, amax_red[w]);
+    // every 16 lanes read the (at most 16) wave maxima at once and reduce
+    float mm = (lane & 15) < NW ? amax_red[lane & 15] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
     gsa_v = gsa_from_amax(mm);
     const bool writer = blockIdx.x == 0;
 #pragma unroll
@@ -745,7 +747,12 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
       }
     }
     if (writer && threadIdx.x == 0) args.gsa_out[0] = gsa_v;
-    lds_barrier();
+    // One row, one 512-element set per wave and as many waves as sets: wave
+    // w quantized exactly set w (its threads own elements 512w .. 512w+511),
+    // the only set it multiplies, and a wave's LDS operations complete in
+    // order, so no other wave needs to be waited for.
+    const bool own_set = M == 1 && S == 1 && HPT == 1 && NW == nset;
+    if (!own_set) lds_barrier();
   }
 
   float acc[MR][RQ];
@@ -811,13 +818,17 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
       if (lane < 4) red[wave][m][4 * rq + lane] = t;
     }
   __syncthreads();
+  // output o = e / 16 is summed by 16 lanes at once, lane e % 16 reading the
+  // partial of wave e % 16 (at most 16 waves)
   const float gscale = gsa_v * args.ws2[0];
-  for (int e = threadIdx.x; e < MR * 4 * RQ; e += blockDim.x) {
-    const int m = e / (4 * RQ), rr = e % (4 * RQ);
-    float sum = 0.f;
-    for (int w = 0; w < NW; ++w) sum += red[w][m][rr];
+  for (int base = threadIdx.x & ~63; base < 16 * MR * 4 * RQ; base += blockDim.x) {
+    const int e = base + lane, o = e >> 4, w = e & 15;
+    const int m = o / (4 * RQ), rr = o % (4 * RQ);
+    float sum = (w < NW && o < MR * 4 * RQ) ? red[w][m][rr] : 0.f;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) sum += __shfl_xor(sum, d, 64);
     const int n = n0 + rr;
-    if (m < M && n < N) {
+    if (w == 0 && o < MR * 4 * RQ && m < M && n < N) {
       const float v = sum * gscale;
       if (args.y_bf16)
         ((uint16_t*)args.y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
