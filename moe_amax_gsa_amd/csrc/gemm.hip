@@ -192,7 +192,7 @@ struct LdsTile {
   static_assert(KW * 16 * (TN + 4) * 4 <= LDS_BYTES, "reduction slabs fit in the stages");
 };
 
-template <int WM, int WN, int STAGES, int WPE, int KW>
+template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE>
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
@@ -260,51 +260,58 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const uint32_t piece = (uint32_t)(2 * wave + h);
   const uint32_t slot = (piece ^ (uint32_t)(r32 & 7)) * 16;
 
+  if constexpr (PIPE) {
+    // This wave's code fragments (16 bytes: its 64-element step of the
+    // chunk) and scale pairs of every tile row, from a stage.
+    auto read_frags = [&](int stage, uint4 (&fa)[WM], uint4 (&fb)[WN], uint32_t (&sa)[WM],
+                          uint32_t (&sb)[WN]) {
+      const uint8_t* st = smem + stage * T::STAGE_BYTES;
 #pragma unroll
-  for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, nch - 1), s0);
-
-  for (int c = 0; c < nch; ++c) {
-    // chunks c+1 .. c+STAGES-2 may still be in flight: this wave issues its
-    // code loads per chunk, and one scale load if it is one of the first
-    // SCALE_LOADS waves
-    constexpr int W_SCALE = (STAGES - 2) * (T::CODE_LOADS + 1);
-    constexpr int W_CODE = (STAGES - 2) * T::CODE_LOADS;
-    if (wave < T::SCALE_LOADS)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_SCALE) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_CODE) : "memory");
-    lds_barrier();
-    issue(min(c + STAGES - 1, nch - 1), (c + STAGES - 1) % STAGES);
-
-    const uint8_t* st = smem + (c % STAGES) * T::STAGE_BYTES;
+      for (int i = 0; i < WM; ++i) {
+        const int row = 32 * i + r32;
+        fa[i] = *(const uint4*)(st + row * T::CB + slot);
+        sa[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
+      }
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        const int row = TM + 32 * i + r32;
+        fb[i] = *(const uint4*)(st + row * T::CB + slot);
+        sb[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
+      }
+    };
+    // scale pairs as f16 and the operands of substep 0
+    half2_t sfa[WM], sfb[WN];
+    half8_t A[2][WM], B[2][WN];
+    auto prep = [&](const uint4 (&fa)[WM], const uint4 (&fb)[WN], const uint32_t (&sa)[WM],
+                    const uint32_t (&sb)[WN]) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        sfa[i] = scale_pair2(sa[i]);
+        A[0][i] = dequant8(fa[i].x, half2_t{sfa[i][0], sfa[i][0]});
+      }
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        sfb[i] = scale_pair2(sb[i]);
+        B[0][i] = dequant8(fb[i].x, half2_t{sfb[i][0], sfb[i][0]});
+      }
+    };
+    // Two stages.  The wait and barrier for chunk c + 1 come before the last
+    // substep of chunk c, so that substep's MFMAs run beside the next
+    // chunk's fragment reads, scale conversions and first dequantization;
+    // the loads of chunk c + 2 then refill the stage chunk c was read from.
+    static_assert(STAGES == 2, "the pipelined loop has two stages");
     uint4 fa[WM], fb[WN];
     uint32_t sa[WM], sb[WN];
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    read_frags(0, fa, fb, sa, sb);
+    if (nch > 1) issue(1, 1);
+    prep(fa, fb, sa, sb);
+    for (int c = 0; c < nch; ++c) {
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const int row = 32 * i + r32;
-      fa[i] = *(const uint4*)(st + row * T::CB + slot);
-      sa[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
-    }
-#pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      const int row = TM + 32 * i + r32;
-      fb[i] = *(const uint4*)(st + row * T::CB + slot);
-      sb[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
-    }
-    half2_t sfa[WM], sfb[WN];
-#pragma unroll
-    for (int i = 0; i < WM; ++i) sfa[i] = scale_pair2(sa[i]);
-#pragma unroll
-    for (int i = 0; i < WN; ++i) sfb[i] = scale_pair2(sb[i]);
-    half8_t A[2][WM], B[2][WN];
-#pragma unroll
-    for (int i = 0; i < WM; ++i) A[0][i] = dequant8(fa[i].x, half2_t{sfa[i][0], sfa[i][0]});
-#pragma unroll
-    for (int i = 0; i < WN; ++i) B[0][i] = dequant8(fb[i].x, half2_t{sfb[i][0], sfb[i][0]});
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const int cur = sub & 1, nxt = cur ^ 1;
-      if (sub < 3) {
+      for (int sub = 0; sub < 3; ++sub) {
+        const int cur = sub & 1, nxt = cur ^ 1;
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
           const uint32_t w = sub == 0 ? fa[i].y : sub == 1 ? fa[i].z : fa[i].w;
@@ -317,17 +324,116 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
           const _Float16 sc = sub == 0 ? sfb[i][0] : sfb[i][1];
           B[nxt][i] = dequant8(w, half2_t{sc, sc});
         }
-      }
 #pragma unroll
-      for (int a = 0; a < WM; ++a)
+        for (int a = 0; a < WM; ++a)
 #pragma unroll
-        for (int b = 0; b < WN; ++b) acc[a][b] = mfma_f16(A[cur][a], B[cur][b], acc[a][b]);
-      if (sub < 3) {
-        // one MFMA, then a share of the next substep's dequantization
+          for (int b = 0; b < WN; ++b) acc[a][b] = mfma_f16(A[cur][a], B[cur][b], acc[a][b]);
 #pragma unroll
         for (int g = 0; g < WM * WN; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, (8 * (WM + WN) + WM * WN - 1) / (WM * WN), 0);
+        }
+      }
+      // chunk c + 1 has landed and every wave has read chunk c's stage (at
+      // the last chunk this reads a stale stage whose values are not used)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      if (c + 2 < nch) issue(c + 2, c & 1);
+      uint4 ga[WM], gb[WN];
+      uint32_t ta[WM], tb[WN];
+      read_frags((c + 1) & 1, ga, gb, ta, tb);
+      // substep 3 (operands in buffer 1) beside the next chunk's preparation
+      half8_t A3[WM], B3[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i) A3[i] = A[1][i];
+#pragma unroll
+      for (int i = 0; i < WN; ++i) B3[i] = B[1][i];
+      prep(ga, gb, ta, tb);
+#pragma unroll
+      for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b) acc[a][b] = mfma_f16(A3[a], B3[b], acc[a][b]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (WM + WN), 0);  // the fragment reads first
+#pragma unroll
+      for (int g = 0; g < WM * WN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (12 * (WM + WN) + WM * WN - 1) / (WM * WN), 0);
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i) fa[i] = ga[i];
+#pragma unroll
+      for (int i = 0; i < WN; ++i) fb[i] = gb[i];
+    }
+  } else {
+  #pragma unroll
+    for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, nch - 1), s0);
+
+    for (int c = 0; c < nch; ++c) {
+      // chunks c+1 .. c+STAGES-2 may still be in flight: this wave issues its
+      // code loads per chunk, and one scale load if it is one of the first
+      // SCALE_LOADS waves
+      constexpr int W_SCALE = (STAGES - 2) * (T::CODE_LOADS + 1);
+      constexpr int W_CODE = (STAGES - 2) * T::CODE_LOADS;
+      if (wave < T::SCALE_LOADS)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_SCALE) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_CODE) : "memory");
+      lds_barrier();
+      issue(min(c + STAGES - 1, nch - 1), (c + STAGES - 1) % STAGES);
+
+      const uint8_t* st = smem + (c % STAGES) * T::STAGE_BYTES;
+      uint4 fa[WM], fb[WN];
+      uint32_t sa[WM], sb[WN];
+  #pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const int row = 32 * i + r32;
+        fa[i] = *(const uint4*)(st + row * T::CB + slot);
+        sa[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
+      }
+  #pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        const int row = TM + 32 * i + r32;
+        fb[i] = *(const uint4*)(st + row * T::CB + slot);
+        sb[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
+      }
+      half2_t sfa[WM], sfb[WN];
+  #pragma unroll
+      for (int i = 0; i < WM; ++i) sfa[i] = scale_pair2(sa[i]);
+  #pragma unroll
+      for (int i = 0; i < WN; ++i) sfb[i] = scale_pair2(sb[i]);
+      half8_t A[2][WM], B[2][WN];
+  #pragma unroll
+      for (int i = 0; i < WM; ++i) A[0][i] = dequant8(fa[i].x, half2_t{sfa[i][0], sfa[i][0]});
+  #pragma unroll
+      for (int i = 0; i < WN; ++i) B[0][i] = dequant8(fb[i].x, half2_t{sfb[i][0], sfb[i][0]});
+  #pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const int cur = sub & 1, nxt = cur ^ 1;
+        if (sub < 3) {
+  #pragma unroll
+          for (int i = 0; i < WM; ++i) {
+            const uint32_t w = sub == 0 ? fa[i].y : sub == 1 ? fa[i].z : fa[i].w;
+            const _Float16 sc = sub == 0 ? sfa[i][0] : sfa[i][1];
+            A[nxt][i] = dequant8(w, half2_t{sc, sc});
+          }
+  #pragma unroll
+          for (int i = 0; i < WN; ++i) {
+            const uint32_t w = sub == 0 ? fb[i].y : sub == 1 ? fb[i].z : fb[i].w;
+            const _Float16 sc = sub == 0 ? sfb[i][0] : sfb[i][1];
+            B[nxt][i] = dequant8(w, half2_t{sc, sc});
+          }
+        }
+  #pragma unroll
+        for (int a = 0; a < WM; ++a)
+  #pragma unroll
+          for (int b = 0; b < WN; ++b) acc[a][b] = mfma_f16(A[cur][a], B[cur][b], acc[a][b]);
+        if (sub < 3) {
+          // one MFMA, then a share of the next substep's dequantization
+  #pragma unroll
+          for (int g = 0; g < WM * WN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (8 * (WM + WN) + WM * WN - 1) / (WM * WN), 0);
+          }
         }
       }
     }
@@ -369,20 +475,35 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
-template <int WM, int WN, int STAGES, int WPE, int KW>
+template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE = false>
 hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   using T = LdsTile<WM, WN, STAGES, KW>;
   static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW>,
+      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE>,
       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM));
-  gemm_lds_kernel<WM, WN, STAGES, WPE, KW><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
+  gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
       a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
@@ -392,9 +513,18 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                     (((uintptr_t)a_scales | (uintptr_t)w_scales) & 1u) == 0;
   // the staged kernel takes whole 256-element chunks and 32-bit row offsets
   const bool big = fast && K % 256 == 0 && K >= 256 && M * (K / 2) < (1ll << 31) && N * (K / 2) < (1ll << 31);
-  if (big)  // 128 x 64 tiles, two workgroups per CU, two stages
+  if (big) {
+    // 128 x 64 tiles.  At most one tile per CU: eight waves split each
+    // 512-element chunk (two waves per SIMD) and the next chunk's fragment
+    // reads and first dequantization run under the current chunk's last
+    // MFMAs.  More tiles: four waves, two workgroups per CU.
+    const int64_t tiles = ((N + 63) / 64) * ((M + 127) / 128);
+    if (tiles <= cu_count() && K % 512 == 0)
+      return launch_lds<4, 2, 2, 2, 8, true>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,
+                                             y_bf16, M, N, K, s);
     return launch_lds<4, 2, 2, 2, 4>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M,
                                      N, K, s);
+  }
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
   if (fast)
     gemm_f16_kernel<true><<<grid, 256, 0, s>>>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,

@@ -245,6 +245,7 @@ LINEAR_CASES = [
     (1, 7, 128), (2, 33, 384), (4, 130, 1152),                 # 16-row kernel, ragged K
     (1, 7, 512), (2, 33, 1024), (4, 130, 2048), (3, 64, 7168),  # 4-row kernel
     (128, 64, 256), (200, 100, 768), (129, 65, 1280), (600, 333, 1536),  # LDS-staged tiles
+    (64, 96, 1024),                                            # eight-wave tiles, two chunks
 ]
 
 
