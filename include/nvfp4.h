@@ -87,10 +87,12 @@ extern "C" {
 #define NVFP4_OP_LINEAR 2
 #define NVFP4_OP_GROUPED_LINEAR 3
 #define NVFP4_OP_LINEAR_RUN 4
+#define NVFP4_OP_GROUPED_SWIGLU 5
 
 /* Bytes of workspace an operation needs for the given sizes (0 if none).
  * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored;
- * for NVFP4_OP_LINEAR_RUN, the activation is (M, K). */
+ * for NVFP4_OP_LINEAR_RUN, the activation is (M, K); for
+ * NVFP4_OP_GROUPED_SWIGLU, N is N_inter and G the group count. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
 
 /* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
@@ -172,10 +174,42 @@ int nvfp4_grouped_linear(const uint8_t *a_codes, const uint8_t *a_scales, const 
 int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_inter,
                               int granularity, void *stream);
 
+/* The step between the two expert projections, fused into the first
+ * (NEXT row 1 of the hot path: SwiGLU, de-interleave and the first amax
+ * phase in the grouped gate/up linear's epilogue; the pages' fused SwiGLU
+ * grouped GEMM epilogue, and the de-interleave + amax + quantize kernel that
+ * consumes its output).  Same results as
+ *   nvfp4_grouped_linear(..., l1, FP32, N_inter, K, ...)   l1 (M_total, N_inter)
+ *   nvfp4_swiglu_deinterleave(l1, h, M_total, N_inter, granularity)
+ *   nvfp4_amax_gsa(h, FP32, M_total * N_inter / 2, gsa_h, ...)
+ * without the fp32 l1: h (M_total, N_inter/2) fp32 and gsa_h (device
+ * float32[1]) are written, h bit-identical to the unfused calls.  Rows of
+ * h that nvfp4_grouped_linear would leave unwritten (outside every group,
+ * or whose row_index lies outside [0, a_rows)) are not written and do not
+ * enter the amax.  The amax is a two-phase grid reduction: every workgroup
+ * of the linear writes the largest |h| it wrote into ws, and a second
+ * kernel reduces those and writes gsa_h.
+ * Requires granularity 1, 2, 4 or 8 (a wave's 16 output columns then hold
+ * whole gate/up pairs), N_inter % (2*granularity) == 0, K % 256 == 0, K
+ * short enough for the staged kernel (K <= 48 384), a_rows*K/2 < 2^31, and
+ * 16-byte aligned codes and scales (NVFP4_ERR_SHAPE / NVFP4_ERR_ALIGN
+ * otherwise; then call the three functions above).
+ * ws: nvfp4_workspace_bytes(NVFP4_OP_GROUPED_SWIGLU, 0, N_inter, 0, G)
+ * bytes, 4-byte aligned, overwritten.
+ * M_total == 0 or N_inter == 0 only writes gsa_h (the 1e-8 floor). */
+int nvfp4_grouped_linear_swiglu(const uint8_t *a_codes, const uint8_t *a_scales,
+                                const float *gsa, int64_t a_rows, const int32_t *row_index,
+                                const int32_t *group_offsets, int G, int64_t M_total,
+                                const uint8_t *w_codes, const uint8_t *w_scales,
+                                const float *ws2, float *h, float *gsa_h, int64_t N_inter,
+                                int64_t K, int granularity, void *ws, size_t ws_bytes,
+                                void *stream);
+
 /* Static name of a status code. */
 const char *nvfp4_status_string(int status);
 
-/* Library ABI version (increments on any signature change). */
+/* Library ABI version (increments when an entry point is added or a
+ * signature changes). */
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

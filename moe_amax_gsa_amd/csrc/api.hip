@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 1; }
+NVFP4_API int nvfp4_abi_version(void) { return 2; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -54,6 +54,8 @@ NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, 
   switch (op) {
     case NVFP4_OP_AMAX_GSA: return M > 0 ? amax_ws_bytes(M) : 0;
     case NVFP4_OP_LINEAR_RUN: return (M > 0 && K > 0) ? amax_ws_bytes(M * K) : 0;
+    case NVFP4_OP_GROUPED_SWIGLU:
+      return (N > 0 && G > 0) ? (size_t)grouped_swiglu_parts(N, G) * sizeof(uint32_t) : 0;
     default: return 0;
   }
 }
@@ -171,6 +173,41 @@ NVFP4_API int nvfp4_grouped_linear(const uint8_t* a_codes, const uint8_t* a_scal
   return launched(launch_grouped_gemv(a_codes, a_scales, gsa, a_rows, row_index, group_offsets, G,
                                       M_total, w_codes, w_scales, ws2, y,
                                       y_dtype == NVFP4_DTYPE_BF16, N, K, (hipStream_t)stream));
+}
+
+NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                          const float* gsa, int64_t a_rows,
+                                          const int32_t* row_index, const int32_t* group_offsets,
+                                          int G, int64_t M_total, const uint8_t* w_codes,
+                                          const uint8_t* w_scales, const float* ws2, float* h,
+                                          float* gsa_h, int64_t N_inter, int64_t K,
+                                          int granularity, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  int st = check_gemm_shape(M_total, N_inter, K);
+  if (st != NVFP4_OK) return st;
+  if (G < 1 || G > 65535 || a_rows < 0 || a_rows > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (row_index == nullptr && a_rows < M_total) return NVFP4_ERR_SHAPE;
+  if (granularity < 1 || N_inter % (2 * (int64_t)granularity) != 0) return NVFP4_ERR_SHAPE;
+  if (gsa_h == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned(gsa_h, 4)) return NVFP4_ERR_ALIGN;
+  if (M_total == 0 || N_inter == 0)  // the amax of nothing: gsa_h from the 1e-8 floor
+    return launched(launch_amax_finalize(nullptr, 0, gsa_h, (hipStream_t)stream));
+  if (a_rows == 0) return NVFP4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !gsa || !group_offsets || !w_codes || !w_scales || !ws2 || !h)
+    return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(a_scales, 16) || !aligned(w_codes, 16) ||
+      !aligned(w_scales, 16) || !aligned(gsa, 4) || !aligned(ws2, 4) ||
+      !aligned(group_offsets, 4) || !aligned(row_index, 4) || !aligned(h, 4))
+    return NVFP4_ERR_ALIGN;
+  if (!grouped_swiglu_supported(N_inter, K, granularity, a_rows, a_codes, a_scales, w_codes,
+                                w_scales))
+    return NVFP4_ERR_SHAPE;
+  const size_t need = (size_t)grouped_swiglu_parts(N_inter, G) * sizeof(uint32_t);
+  if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+  return launched(launch_grouped_swiglu(a_codes, a_scales, gsa, a_rows, row_index, group_offsets,
+                                        G, M_total, w_codes, w_scales, ws2, h, gsa_h, N_inter, K,
+                                        granularity, (uint32_t*)ws, (hipStream_t)stream));
 }
 
 NVFP4_API int nvfp4_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t N_inter,

@@ -143,6 +143,19 @@ __device__ __forceinline__ uint32_t e2m1_signs8(const float v[8]) {
   return c;
 }
 
+// silu(g) * u = g / (1 + exp(-g)) * u in fp32 with the hardware exp2 and
+// reciprocal (each within about an ulp; exp(-g) is 2^(-g log2 e), whose
+// argument rounding adds |g| 2^-24 relative): h is within a few 1e-7 of
+// the exact value.  It is the one expression both SwiGLU paths (the
+// standalone kernel and the grouped linear's epilogue) use, so they give
+// identical h.  Large |g| saturates correctly: exp(-g) -> inf gives 0
+// (times the sign of g), exp(-g) -> 0 gives g * u.
+__device__ __forceinline__ float swiglu1(float g, float u) {
+#pragma clang fp contract(off)
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 // ---- wave64 reductions (DPP-friendly xor shuffles)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

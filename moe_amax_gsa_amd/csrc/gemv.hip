@@ -61,6 +61,10 @@ struct GemvArgs {
   float* gsa_out;
   uint8_t* codes_out;
   uint8_t* scales_out;
+  // gemv_ring_kernel with SwiGLU: gate/up group width, and one amax partial
+  // (bits of a non-negative float) per workgroup
+  int gran;
+  uint32_t* partials;
 };
 
 __device__ __forceinline__ float4_t mfma_fp4(v8i a, v8i b) {
@@ -409,7 +413,14 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
-template <int MP, int D, int W>
+// SWIGLU: the output columns are gate/up groups of args.gran columns
+// interleaved (group q is gate when q is even, and gate group 2p pairs with
+// up group 2p+1); instead of those columns the epilogue writes
+// h = silu(gate) * up, (M, N/2) fp32 at args.y, column p*gran + i, and each
+// workgroup writes the largest |h| it wrote to args.partials (the first
+// phase of h's amax).  A wave's 16 columns hold whole pairs (gran divides 8):
+// the up value of gate column c sits in lane c ^ gran.
+template <int MP, int D, int W, bool SWIGLU = false>
 __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) {
   static_assert(2 * (D - 1) <= 14, "wait_vm range");
   constexpr int ROWS = 2 * MP;
@@ -426,7 +437,11 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
     r_begin = max(args.offsets[g], 0);
     r_end = min(args.offsets[g + 1], args.M);
   }
-  if (r_begin >= r_end) return;  // uniform over the workgroup
+  if (r_begin >= r_end) {  // uniform over the workgroup
+    if (SWIGLU && threadIdx.x == 0) args.partials[blockIdx.y * gridDim.x + blockIdx.x] = 0u;
+    return;
+  }
+  float hmax = 0.f;  // SWIGLU: largest |h| this thread wrote
 
   const int n0 = (blockIdx.x * W + wave) * 16;
   const bool tile_ok = n0 < N;  // wave-uniform; a wave past the end only stages
@@ -581,13 +596,34 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
         const float v = acc[p] + __shfl_xor(acc[p], 16, 64);
         const int rl = 2 * p + c_mloc, r = r0 + rl, n = n0 + col;
         const bool ok = (j & 1) == 0 && r < r_end && n < N && __shfl(my_src, rl, 64) >= 0;
-        if (ok) {
+        if (SWIGLU) {
+          const float gv = v * gscale;
+          const float uv = __shfl_xor(gv, args.gran, 64);  // the paired up column
+          if (ok && (col & args.gran) == 0) {  // a gate column (gran is a power of two)
+            const float hv = swiglu1(gv, uv);
+            const int lg = __builtin_ctz(args.gran);
+            const int hcol = ((n >> (lg + 1)) << lg) + (n & (args.gran - 1));
+            ((float*)args.y)[(int64_t)r * (N / 2) + hcol] = hv;
+            hmax = fmaxf(hmax, fabsf(hv));
+          }
+        } else if (ok) {
           if (args.y_bf16)
             ((uint16_t*)args.y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v * gscale);
           else
             ((float*)args.y)[(int64_t)r * N + n] = v * gscale;
         }
       }
+    }
+  }
+  if (SWIGLU) {  // the workgroup's largest |h|
+    __shared__ uint32_t wmax[W];
+    const uint32_t m = wave_max_u32(__float_as_uint(hmax));
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t mm = 0;
+      for (int w = 0; w < W; ++w) mm = max(mm, wmax[w]);
+      args.partials[blockIdx.y * gridDim.x + blockIdx.x] = mm;
     }
   }
 }
@@ -598,16 +634,16 @@ static size_t ring_lds_bytes(int64_t K) {
          (size_t)W * (size_t)(K + D * RING_SLOT);
 }
 
-template <int MP, int D, int W>
+template <int MP, int D, int W, bool SWIGLU>
 static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
   const size_t lds = ring_lds_bytes<MP, D, W>(a.K);
   if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_ring_kernel<MP, D, W>,
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_ring_kernel<MP, D, W, SWIGLU>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)((a.N + 16 * W - 1) / (16 * W)), (unsigned)G);
-  gemv_ring_kernel<MP, D, W><<<grid, W * 64, lds, s>>>(a);
+  gemv_ring_kernel<MP, D, W, SWIGLU><<<grid, W * 64, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -862,21 +898,30 @@ static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hip
 // Grouped linear through the LDS ring: the most activation rows per pass
 // (two workgroups per CU where that fits, else one) whose LDS fits
 // RING_MAX_LDS.  false: K too long to stage.
-constexpr size_t RING_MAX_LDS = 160 * 1024;
+constexpr size_t RING_MAX_LDS = 160 * 1024 - 256;  // room for the kernel's static LDS
 
-template <int MP, int D, int W>
-static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err) {
+// *parts: the grid's workgroup count (SwiGLU amax partials)
+template <int MP, int D, int W, bool SWIGLU>
+static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err, int64_t* parts) {
   if (ring_lds_bytes<MP, D, W>(a.K) > RING_MAX_LDS) return false;
-  *err = launch_ring_t<MP, D, W>(a, G, s);
+  *parts = (int64_t)((a.N + 16 * W - 1) / (16 * W)) * G;
+  *err = launch_ring_t<MP, D, W, SWIGLU>(a, G, s);
   return true;
 }
 
+template <bool SWIGLU>
 static bool launch_ring(const GemvArgs& a, int G, int64_t mean_rows, hipStream_t s,
-                        hipError_t* err) {
-  if (mean_rows > 4 && ring_try<8, 3, 4>(a, G, s, err)) return true;
-  return ring_try<4, 3, 8>(a, G, s, err) || ring_try<4, 3, 4>(a, G, s, err) ||
-         ring_try<2, 3, 4>(a, G, s, err) || ring_try<1, 3, 2>(a, G, s, err);
+                        hipError_t* err, int64_t* parts) {
+  if (mean_rows > 4 && ring_try<8, 3, 4, SWIGLU>(a, G, s, err, parts)) return true;
+  return ring_try<4, 3, 8, SWIGLU>(a, G, s, err, parts) ||
+         ring_try<4, 3, 4, SWIGLU>(a, G, s, err, parts) ||
+         ring_try<2, 3, 4, SWIGLU>(a, G, s, err, parts) ||
+         ring_try<1, 3, 2, SWIGLU>(a, G, s, err, parts);
 }
+
+// Most workgroups any ring configuration launches for (N, G): the size of
+// the SwiGLU amax partials.
+int64_t ring_max_parts(int64_t N, int G) { return ((N + 31) / 32) * (int64_t)G; }
 
 template <int MODE>
 static hipError_t launch_rows(const GemvArgs& a, int64_t rows_per_pass, bool fast, dim3 grid,
@@ -1030,7 +1075,8 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
   const int64_t mean_rows = (M_total + G - 1) / G;
   if (fast && a_rows * (K / 2) < ((int64_t)1 << 31)) {  // copy offsets are 32-bit
     hipError_t err = hipSuccess;
-    if (launch_ring(a, G, mean_rows, s, &err)) return err;
+    int64_t parts = 0;
+    if (launch_ring<false>(a, G, mean_rows, s, &err, &parts)) return err;
   }
   dim3 grid((unsigned)((N + 15) / 16), (unsigned)G);
   if (mean_rows <= 2 && K >= 4096) {
@@ -1040,6 +1086,49 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
   }
   return launch_rows<MODE_GROUPED>(a, mean_rows <= 2 ? 4 : 2 * mean_rows, fast, grid,
                                    waves_for(K), s);
+}
+
+int64_t grouped_swiglu_parts(int64_t N, int G) { return ring_max_parts(N, G); }
+
+bool grouped_swiglu_supported(int64_t N, int64_t K, int gran, int64_t a_rows,
+                              const uint8_t* a_codes, const uint8_t* a_scales,
+                              const uint8_t* w_codes, const uint8_t* w_scales) {
+  const bool gran_ok = gran == 1 || gran == 2 || gran == 4 || gran == 8;
+  return gran_ok && N % (2 * gran) == 0 && K % 256 == 0 && K >= 256 && aligned16(a_codes) &&
+         aligned16(a_scales) && aligned16(w_codes) && aligned16(w_scales) &&
+         a_rows * (K / 2) < ((int64_t)1 << 31) &&
+         ring_lds_bytes<1, 3, 2>(K) <= RING_MAX_LDS;  // the smallest configuration fits
+}
+
+hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const float* gsa, int64_t a_rows, const int32_t* row_index,
+                                 const int32_t* offsets, int G, int64_t M_total,
+                                 const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const float* ws2, float* h, float* gsa_h, int64_t N, int64_t K,
+                                 int gran, uint32_t* partials, hipStream_t s) {
+  GemvArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.gsa = gsa;
+  a.row_index = row_index;
+  a.offsets = offsets;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.ws2 = ws2;
+  a.y = h;
+  a.y_bf16 = 0;
+  a.M = (int)M_total;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.a_rows = (int)a_rows;
+  a.gran = gran;
+  a.partials = partials;
+  const int64_t mean_rows = (M_total + G - 1) / G;
+  hipError_t err = hipSuccess;
+  int64_t parts = 0;
+  if (!launch_ring<true>(a, G, mean_rows, s, &err, &parts)) return hipErrorInvalidValue;
+  if (err != hipSuccess) return err;
+  return launch_amax_finalize(partials, parts, gsa_h, s);
 }
 
 bool gemv_run_supported(int64_t M, int64_t K, const void* x, const uint8_t* w_codes,

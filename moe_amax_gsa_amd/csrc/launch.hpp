@@ -27,6 +27,10 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
 hipError_t launch_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t NI, int gran,
                                       hipStream_t s);
 
+// Phase 2 of an amax over partials (bits of non-negative fp32 maxima): gsa.
+hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float* gsa,
+                                hipStream_t s);
+
 // Weight-streaming linear for few rows (FP4 matrix cores).
 constexpr int64_t GEMV_MAX_M = 16;
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
@@ -39,6 +43,21 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
                                int G, int64_t M_total, const uint8_t* w_codes,
                                const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
                                int64_t N, int64_t K, hipStream_t s);
+
+// Grouped linear with SwiGLU, de-interleave and the first amax phase of h
+// in its epilogue, then the second phase (gsa_h).  ws holds
+// grouped_swiglu_parts(N, G) partials.  false: the operands or shape do not
+// suit the fused kernel (nothing launched).
+bool grouped_swiglu_supported(int64_t N, int64_t K, int gran, int64_t a_rows,
+                              const uint8_t* a_codes, const uint8_t* a_scales,
+                              const uint8_t* w_codes, const uint8_t* w_scales);
+int64_t grouped_swiglu_parts(int64_t N, int G);
+hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const float* gsa, int64_t a_rows, const int32_t* row_index,
+                                 const int32_t* offsets, int G, int64_t M_total,
+                                 const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const float* ws2, float* h, float* gsa_h, int64_t N, int64_t K,
+                                 int gran, uint32_t* partials, hipStream_t s);
 
 // amax -> gsa -> quantize -> linear in one kernel for a few activation rows.
 constexpr int64_t GEMV_RUN_MAX_M = 16;

@@ -54,8 +54,18 @@ __global__ __launch_bounds__(AMAX_THREADS) void amax_partial_kernel(
 template <bool BF16>
 __global__ __launch_bounds__(AMAX_THREADS) void amax_finalize_kernel(
     const uint32_t* __restrict__ partials, int nparts, float* __restrict__ gsa) {
+  // eight independent loads in flight per thread, not one after another
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += AMAX_THREADS) m = max(m, partials[i]);
+  for (int i0 = threadIdx.x; i0 < nparts; i0 += 8 * AMAX_THREADS) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * AMAX_THREADS;
+      v[u] = i < nparts ? partials[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = max(m, v[u]);
+  }
   m = block_max_u32<AMAX_THREADS>(m);
   if (threadIdx.x == 0) gsa[0] = gsa_from_bits<BF16>(m);
 }
@@ -220,7 +230,13 @@ __global__ __launch_bounds__(256) void swiglu_deinterleave_kernel(const float* _
   const int64_t pair = c / gran, off = c - pair * gran;
   const float g = l1[m * NI + 2 * pair * gran + off];
   const float u = l1[m * NI + (2 * pair + 1) * gran + off];
-  h[t] = g / (1.0f + expf(-g)) * u;
+  h[t] = swiglu1(g, u);
+}
+
+hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float* gsa,
+                                hipStream_t s) {
+  amax_finalize_kernel<false><<<1, AMAX_THREADS, 0, s>>>(partials, (int)nparts, gsa);
+  return hipGetLastError();
 }
 
 hipError_t launch_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t NI, int gran,

@@ -4,7 +4,9 @@
 amax -> gsa, quantize from the gsa buffer, block-scaled GEMM; see
 dsv4/_archive/layers/linear.py, _run_impl).  ``Nvfp4MoE`` runs the routed
 expert pair (L1 gate/up with granularity-8 interleave, SwiGLU, re-quantize,
-L2), as README.md's MoE kernel section describes, unfused.  Both keep gsa
+L2), as README.md's MoE kernel section describes; where the shapes allow,
+SwiGLU, the de-interleave and the first amax phase run in the L1 linear's
+epilogue (nvfp4_grouped_linear_swiglu), else as separate calls.  Both keep gsa
 on the device: no host synchronisation, no per-call host-to-device copy
 (deleted PERFORMANCE_AUDIT.md, P0; docs/PERFORMANCE_AUDIT.md, P2).
 
@@ -86,7 +88,7 @@ class Nvfp4MoE:
     """
 
     def __init__(self, w1_codes, w1_scales, w1_ws2, w2_codes, w2_scales, w2_ws2, max_pairs: int,
-                 max_tokens: int, granularity: int = 8):
+                 max_tokens: int, granularity: int = 8, fused: bool = True):
         dev = w1_codes.device
         self.device = dev
         self.E, self.N1, self.K1 = w1_codes.shape[0], w1_codes.shape[1], w1_codes.shape[2] * 2
@@ -104,7 +106,17 @@ class Nvfp4MoE:
         self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
         self.x_codes = torch.empty(max_tokens, self.K1 // 2, dtype=torch.uint8, device=dev)
         self.x_scales = torch.empty(max_tokens, self.K1 // 16, dtype=torch.uint8, device=dev)
-        self.y1 = torch.empty(max_pairs, self.N1, dtype=torch.float32, device=dev)
+        # SwiGLU in the L1 epilogue: the conditions nvfp4_grouped_linear_swiglu
+        # states (the activation buffers below are allocated 16-byte aligned)
+        self.fused = bool(fused and granularity in (1, 2, 4, 8) and self.K1 % 256 == 0
+                          and self.K1 <= 48384 and self.N1 % (2 * granularity) == 0
+                          and self.w1_codes.data_ptr() % 16 == 0
+                          and self.w1_scales.data_ptr() % 16 == 0)
+        self.ws_swiglu = torch.empty(
+            max(C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, 0, self.N1, 0, self.E), 16),
+            dtype=torch.uint8, device=dev)
+        self.y1 = (None if self.fused else
+                   torch.empty(max_pairs, self.N1, dtype=torch.float32, device=dev))
         self.h = torch.empty(max_pairs, self.K2, dtype=torch.float32, device=dev)
         self.h_codes = torch.empty(max_pairs, self.K2 // 2, dtype=torch.uint8, device=dev)
         self.h_scales = torch.empty(max_pairs, self.K2 // 16, dtype=torch.uint8, device=dev)
@@ -115,13 +127,18 @@ class Nvfp4MoE:
         xc, xs = self.x_codes[:T], self.x_scales[:T]
         C.nvfp4_amax_gsa(x, self.gsa1, self.ws, stream)
         C.nvfp4_quantize_from_buffer(x, self.gsa1, xc, xs, stream)
-        y1 = self.y1[:P]
-        C.nvfp4_grouped_linear(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
-                               self.w1_scales, self.w1_ws2, y1, None, stream)
         h = self.h[:P]
-        C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream)
+        if self.fused:
+            C.nvfp4_grouped_linear_swiglu(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
+                                          self.w1_scales, self.w1_ws2, h, self.gsa2,
+                                          self.granularity, self.ws_swiglu, stream)
+        else:
+            y1 = self.y1[:P]
+            C.nvfp4_grouped_linear(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
+                                   self.w1_scales, self.w1_ws2, y1, None, stream)
+            C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream)
+            C.nvfp4_amax_gsa(h, self.gsa2, self.ws, stream)
         hc, hs = self.h_codes[:P], self.h_scales[:P]
-        C.nvfp4_amax_gsa(h, self.gsa2, self.ws, stream)
         C.nvfp4_quantize_from_buffer(h, self.gsa2, hc, hs, stream)
         y2 = self.y2[:P]
         C.nvfp4_grouped_linear(hc, hs, self.gsa2, None, offsets, self.w2_codes, self.w2_scales,

@@ -26,6 +26,7 @@ OP_QUANTIZE = 1
 OP_LINEAR = 2
 OP_GROUPED_LINEAR = 3
 OP_LINEAR_RUN = 4
+OP_GROUPED_SWIGLU = 5
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_amax_gsa_amd.build`")
@@ -55,6 +56,9 @@ lib.nvfp4_linear_run.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _
 lib.nvfp4_grouped_linear.restype = _I
 lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
                                      _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_grouped_linear_swiglu.restype = _I
+lib.nvfp4_grouped_linear_swiglu.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P,
+                                            _P, _I64, _I64, _I, _P, _SZ, _P]
 lib.nvfp4_swiglu_deinterleave.restype = _I
 lib.nvfp4_swiglu_deinterleave.argtypes = [_P, _P, _I64, _I64, _I, _P]
 
@@ -157,6 +161,22 @@ def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: tor
                                     _dtype(y), N, K, _ptr(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)), "nvfp4_grouped_linear")
+
+
+def nvfp4_grouped_linear_swiglu(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,
+                                row_index: Optional[torch.Tensor], group_offsets: torch.Tensor,
+                                w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
+                                h: torch.Tensor, gsa_h: torch.Tensor, granularity: int,
+                                ws: torch.Tensor, stream=None) -> None:
+    """w_codes (G, N_inter, K/2), w_scales (G, N_inter, K/16), ws2 (G,);
+    h (M_total, N_inter/2) fp32 and gsa_h (1,) fp32 are written."""
+    G, NI = w_codes.shape[0], w_codes.shape[1]
+    K = w_codes.shape[2] * 2
+    _check(lib.nvfp4_grouped_linear_swiglu(
+        _ptr(a_codes), _ptr(a_scales), _ptr(gsa), a_codes.shape[0], _ptr(row_index),
+        _ptr(group_offsets), G, h.shape[0], _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(h),
+        _ptr(gsa_h), NI, K, granularity, _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "nvfp4_grouped_linear_swiglu")
 
 
 def nvfp4_swiglu_deinterleave(l1: torch.Tensor, h: torch.Tensor, granularity: int = 8,

@@ -341,14 +341,16 @@ def moe_small(**kw):
     return W.make_moe(**base)
 
 
-def run_moe_stepwise(C, moe, sample=None):
+def run_moe_stepwise(C, moe, sample=None, fused=True):
     """Run the layer; check every step against the oracle on the GPU's own
     input to that step.  sample: number of sampled outputs per GEMM (None =
-    all)."""
+    all).  fused: SwiGLU in the L1 epilogue (then L1 is checked through h,
+    the SwiGLU of the oracle's L1 output), else the separate calls."""
     from moe_amax_gsa_amd.layer import Nvfp4MoE
     P = int(moe.offsets[-1])
     w = W.moe_weights_to(moe, DEV, keep_host=True)
-    layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=moe.granularity)
+    layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=moe.granularity, fused=fused)
+    assert layer.fused == fused
     xd = W.bf16_to_torch(moe.x, DEV)
     ri = to_dev(moe.pair_token)
     off = to_dev(moe.offsets)
@@ -359,13 +361,18 @@ def run_moe_stepwise(C, moe, sample=None):
     oc1, os1 = oracle.quantize(moe.x, g1)
     assert np.array_equal(layer.x_codes[:moe.T].cpu().numpy(), oc1)
     assert np.array_equal(layer.x_scales[:moe.T].cpu().numpy(), os1)
-    y1 = layer.y1[:P].cpu().numpy().astype(np.float64)
+    y1 = None if fused else layer.y1[:P].cpu().numpy().astype(np.float64)
     h = layer.h[:P].cpu().numpy()
     hc = layer.h_codes[:P].cpu().numpy()
     hs = layer.h_scales[:P].cpu().numpy()
     g2 = f32(layer.gsa2)
+    gran = moe.granularity
     rng = np.random.default_rng(0)
-    for layer_id, yg, Ncols in [(0, y1, moe.N1), (1, y2, moe.N2)]:
+
+    def silu_mul(g, u):
+        return g / (1.0 + np.exp(-g)) * u
+
+    for layer_id, Ncols in [(0, moe.N1), (1, moe.N2)]:
         ref_max = 0.0
         err_max = 0.0
         for e in moe.active_experts:
@@ -376,38 +383,103 @@ def run_moe_stepwise(C, moe, sample=None):
                 ac, asf, g = oc1[moe.pair_token[rows]], os1[moe.pair_token[rows]], g1
             else:
                 ac, asf, g = hc[rows], hs[rows], g2
-            if sample is None:
+            if layer_id == 0 and fused:
+                # h against the SwiGLU of the oracle's L1 output (fp32 as the
+                # GPU holds it, SwiGLU in double)
+                if sample is None:
+                    l1 = oracle.linear(ac, asf, g, wc, wsf, w2).astype(np.float32)
+                    ref = oracle.swiglu_deinterleave(l1, gran)
+                    got = h[rows].astype(np.float64)
+                else:
+                    ms = rng.integers(0, len(rows), sample)
+                    cs = rng.integers(0, Ncols // 2, sample)
+                    cs[:2] = [0, Ncols // 2 - 1]
+                    gcol = (cs // gran) * 2 * gran + cs % gran
+                    lg = oracle.linear_at(ac, asf, g, wc, wsf, w2, ms, gcol).astype(np.float32)
+                    lu = oracle.linear_at(ac, asf, g, wc, wsf, w2, ms, gcol + gran).astype(np.float32)
+                    ref = silu_mul(lg.astype(np.float64), lu.astype(np.float64))
+                    got = h[rows[ms], cs].astype(np.float64)
+            elif sample is None:
                 ref = oracle.linear(ac, asf, g, wc, wsf, w2)
-                got = yg[rows]
+                got = (y1 if layer_id == 0 else y2)[rows]
             else:
                 ms = rng.integers(0, len(rows), sample)
                 ns = rng.integers(0, Ncols, sample)
                 ns[:2] = [0, Ncols - 1]
                 ref = oracle.linear_at(ac, asf, g, wc, wsf, w2, ms, ns)
-                got = yg[rows[ms], ns]
+                got = (y1 if layer_id == 0 else y2)[rows[ms], ns]
             ref_max = max(ref_max, float(np.max(np.abs(ref))))
             err_max = max(err_max, float(np.max(np.abs(got - ref))))
         assert err_max / ref_max <= REL_TOL, (layer_id, err_max / ref_max)
         if layer_id == 0:
-            # SwiGLU on the GPU's own L1 output (tolerance only: exp rounding)
-            href = oracle.swiglu_deinterleave(layer.y1[:P].cpu().numpy(), moe.granularity)
-            assert np.max(np.abs(h - href)) <= 1e-6 * np.max(np.abs(href))
+            if not fused:
+                # SwiGLU on the GPU's own L1 output (tolerance only: exp rounding)
+                href = oracle.swiglu_deinterleave(layer.y1[:P].cpu().numpy(), gran)
+                assert np.max(np.abs(h - href)) <= 1e-6 * np.max(np.abs(href))
             # re-quantize of the GPU's own h: bit-exact
             assert g2 == oracle.amax_gsa(h)
             oc2, os2 = oracle.quantize(h, g2)
             assert np.array_equal(hc, oc2) and np.array_equal(hs, os2)
 
 
-def test_moe_small_stepwise(C):
-    say("moe small")
-    run_moe_stepwise(C, moe_small())
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_moe_small_stepwise(C, fused):
+    say("moe small", fused)
+    run_moe_stepwise(C, moe_small(), fused=fused)
 
 
-def test_moe_small_skewed_groups(C):
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+def test_moe_small_skewed_groups(C, fused):
     """One expert takes many rows (more than one pass of the grouped kernel),
     several experts are empty."""
-    say("moe skewed")
-    run_moe_stepwise(C, moe_small(tokens=40, experts=3, topk=2, K1=512, N1=64, N2=24, seed=4))
+    say("moe skewed", fused)
+    run_moe_stepwise(C, moe_small(tokens=40, experts=3, topk=2, K1=512, N1=64, N2=24, seed=4),
+                     fused=fused)
+
+
+@pytest.mark.parametrize("gran", [8, 4, 2, 1])
+@pytest.mark.parametrize("K,N", [(256, 64), (768, 160), (2048, 96)])
+def test_grouped_swiglu_matches_unfused(C, K, N, gran):
+    """nvfp4_grouped_linear_swiglu against the three separate calls on the
+    same inputs: h bit-identical and the same gsa_h.  Group sizes 0 .. 19,
+    invalid row indices (rows left unwritten in both, and out of the amax:
+    both h buffers start at zero), partial column tiles."""
+    say(f"grouped swiglu K={K} N={N} gran={gran}")
+    rng = np.random.default_rng(K + N + gran)
+    sizes = [3, 0, 1, 19, 2, 0, 5, 9]
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    P = int(offsets[-1])
+    a_rows = 11
+    row_index = rng.integers(0, a_rows, P).astype(np.int32)
+    row_index[[4, 10, 20]] = [-1, a_rows, 1 << 20]
+    ac = to_dev(rng.integers(0, 256, (a_rows, K // 2), dtype=np.uint8))
+    asf = to_dev(rng.integers(0x20, 0x48, (a_rows, K // 16), dtype=np.uint8))
+    wc = to_dev(rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8))
+    wsf = to_dev(rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8))
+    ws2 = to_dev(rng.uniform(0.002, 0.01, G).astype(np.float32))
+    gsa = to_dev(np.array([0.37], np.float32))
+    ri, off = to_dev(row_index), to_dev(offsets)
+    # fused
+    h1 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
+    g1 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, 0, N, 0, G), 16),
+                     dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_swiglu(ac, asf, gsa, ri, off, wc, wsf, ws2, h1, g1, gran, ws)
+    # unfused
+    l1 = torch.zeros(P, N, dtype=torch.float32, device=DEV)
+    h2 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
+    g2 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(ac, asf, gsa, ri, off, wc, wsf, ws2, l1)
+    C.nvfp4_swiglu_deinterleave(l1, h2, gran)
+    aws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, P * N // 2), 16),
+                      dtype=torch.uint8, device=DEV)
+    C.nvfp4_amax_gsa(h2, g2, aws)
+    torch.cuda.synchronize()
+    a, b = h1.cpu().numpy(), h2.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert f32(g1) == f32(g2)
+    assert np.all(a[[4, 10]] == 0.0)  # invalid row indices: unwritten
 
 
 def test_grouped_row_index_bounds(C):
