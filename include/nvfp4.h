@@ -88,11 +88,13 @@ extern "C" {
 #define NVFP4_OP_GROUPED_LINEAR 3
 #define NVFP4_OP_LINEAR_RUN 4
 #define NVFP4_OP_GROUPED_SWIGLU 5
+#define NVFP4_OP_QUANTIZE_WEIGHT 6
 
 /* Bytes of workspace an operation needs for the given sizes (0 if none).
  * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored;
  * for NVFP4_OP_LINEAR_RUN, the activation is (M, K); for
- * NVFP4_OP_GROUPED_SWIGLU, N is N_inter and G the group count. */
+ * NVFP4_OP_GROUPED_SWIGLU, N is N_inter and G the group count; for
+ * NVFP4_OP_QUANTIZE_WEIGHT, the weight is (N, K). */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
 
 /* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
@@ -111,6 +113,19 @@ int nvfp4_amax_gsa(const void *x, int x_dtype, int64_t numel, float *gsa, void *
 int nvfp4_quantize_from_buffer(const void *x, int x_dtype, int64_t M, int64_t K,
                                const float *gsa, uint8_t *codes, uint8_t *scales,
                                void *stream);
+
+/* Weight-side quantize at load time (NEXT row 3 of the hot path; the
+ * pages' quantize_weight_to_nvfp4 for the lm_head and router gate, whose
+ * checkpoints hold bf16): w (N, K) bf16/fp32, K % 16 == 0, 16-byte
+ * aligned, becomes codes (N, K/2), scales (N, K/16) and its global scale
+ * ws2[0] = max(max|w|, 1e-8) / 2688 -- the activation recipe of steps 1
+ * and 2 applied to the weight, with the result in the layout nvfp4_linear
+ * takes, and the same results as nvfp4_amax_gsa + nvfp4_quantize_from_buffer
+ * on w.  ws: nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE_WEIGHT, 0, N, K, 0)
+ * bytes (the amax partials). */
+int nvfp4_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, float *ws2,
+                          uint8_t *codes, uint8_t *scales, void *ws, size_t ws_bytes,
+                          void *stream);
 
 /* Step 3: y (M, N) = gsa * ws2 * dequant(A) @ dequant(W)^T, FP32 accumulation.
  * A is codes (M, K/2) + scales (M, K/16) from step 2; W is codes (N, K/2) +

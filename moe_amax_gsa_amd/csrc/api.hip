@@ -54,6 +54,7 @@ NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, 
   switch (op) {
     case NVFP4_OP_AMAX_GSA: return M > 0 ? amax_ws_bytes(M) : 0;
     case NVFP4_OP_LINEAR_RUN: return (M > 0 && K > 0) ? amax_ws_bytes(M * K) : 0;
+    case NVFP4_OP_QUANTIZE_WEIGHT: return (N > 0 && K > 0) ? amax_ws_bytes(N * K) : 0;
     case NVFP4_OP_GROUPED_SWIGLU:
       return (N > 0 && G > 0) ? (size_t)grouped_swiglu_parts(N, G) * sizeof(uint32_t) : 0;
     default: return 0;
@@ -87,6 +88,26 @@ NVFP4_API int nvfp4_quantize_from_buffer(const void* x, int x_dtype, int64_t M, 
   if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gsa, 4)) return NVFP4_ERR_ALIGN;
   return launched(launch_quantize(x, x_dtype == NVFP4_DTYPE_BF16, M, K, gsa, codes, scales,
                                   (hipStream_t)stream));
+}
+
+NVFP4_API int nvfp4_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, float* ws2,
+                                    uint8_t* codes, uint8_t* scales, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (!dtype_ok(w_dtype)) return NVFP4_ERR_DTYPE;
+  if (N <= 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if ((N * (K / 16) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (w == nullptr || ws2 == nullptr || codes == nullptr || scales == nullptr)
+    return NVFP4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(codes, 8) || !aligned(ws2, 4)) return NVFP4_ERR_ALIGN;
+  const size_t need = amax_ws_bytes(N * K);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+  }
+  const bool bf16 = w_dtype == NVFP4_DTYPE_BF16;
+  const hipError_t e = launch_amax_gsa(w, bf16, N * K, ws2, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return launched(e);
+  return launched(launch_quantize(w, bf16, N, K, ws2, codes, scales, (hipStream_t)stream));
 }
 
 NVFP4_API int nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,

@@ -48,6 +48,21 @@ class Nvfp4Linear:
         self.scales = torch.empty(max_tokens, self.K // 16, dtype=torch.uint8, device=dev)
         self.y = torch.empty(max_tokens, self.N, dtype=out_dtype, device=dev)
 
+    @classmethod
+    def from_weight(cls, w: torch.Tensor, max_tokens: int, out_dtype=torch.float32,
+                    x_dtype=torch.bfloat16, stream=None) -> "Nvfp4Linear":
+        """Quantize a bf16/fp32 weight (N, K) at load time (nvfp4_quantize_weight:
+        codes, scales and weight_scale_2 on the device) and build the layer."""
+        w = w.contiguous()
+        N, K = w.shape
+        codes = torch.empty(N, K // 2, dtype=torch.uint8, device=w.device)
+        scales = torch.empty(N, K // 16, dtype=torch.uint8, device=w.device)
+        ws2 = torch.empty(1, dtype=torch.float32, device=w.device)
+        ws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_QUANTIZE_WEIGHT, 0, N, K), 16),
+                         dtype=torch.uint8, device=w.device)
+        C.nvfp4_quantize_weight(w, ws2, codes, scales, ws, stream)
+        return cls(codes, scales, ws2, max_tokens, out_dtype=out_dtype, x_dtype=x_dtype)
+
     def quantize(self, x: torch.Tensor, stream=None):
         M = x.shape[0]
         C.nvfp4_amax_gsa(x, self.gsa, self.ws, stream)

@@ -27,6 +27,7 @@ OP_LINEAR = 2
 OP_GROUPED_LINEAR = 3
 OP_LINEAR_RUN = 4
 OP_GROUPED_SWIGLU = 5
+OP_QUANTIZE_WEIGHT = 6
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_amax_gsa_amd.build`")
@@ -56,6 +57,8 @@ lib.nvfp4_linear_run.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _
 lib.nvfp4_grouped_linear.restype = _I
 lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
                                      _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_quantize_weight.restype = _I
+lib.nvfp4_quantize_weight.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]
 lib.nvfp4_grouped_linear_swiglu.restype = _I
 lib.nvfp4_grouped_linear_swiglu.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P,
                                             _P, _I64, _I64, _I, _P, _SZ, _P]
@@ -161,6 +164,17 @@ def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: tor
                                     _dtype(y), N, K, _ptr(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)), "nvfp4_grouped_linear")
+
+
+def nvfp4_quantize_weight(w: torch.Tensor, ws2: torch.Tensor, codes: torch.Tensor,
+                          scales: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                          stream=None) -> None:
+    """w (N, K) bf16/fp32 -> codes (N, K/2), scales (N, K/16), ws2 (1,) fp32."""
+    N, K = w.shape
+    _check(lib.nvfp4_quantize_weight(_ptr(w), _dtype(w), N, K, _ptr(ws2), _ptr(codes),
+                                     _ptr(scales), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream)), "nvfp4_quantize_weight")
 
 
 def nvfp4_grouped_linear_swiglu(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,

@@ -422,6 +422,32 @@ def run_moe_stepwise(C, moe, sample=None, fused=True):
             assert np.array_equal(hc, oc2) and np.array_equal(hs, os2)
 
 
+@pytest.mark.parametrize("N,K", [(48, 256), (130, 1024), (1024, 7168)])
+def test_quantize_weight(C, N, K):
+    """Weight-side quantize at load time: codes, scales and weight_scale_2
+    bit-exact with the oracle's amax -> gsa -> quantize of the bf16 weight,
+    and the layer built from it gives the oracle's linear of those codes."""
+    from moe_amax_gsa_amd.layer import Nvfp4Linear
+    say(f"quantize weight N={N} K={K}")
+    rng = np.random.default_rng(N + K)
+    w = W.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    w[rng.integers(0, N), rng.integers(0, K)] = W.to_bf16_bits(np.array([0.75]))[0]
+    wd = W.bf16_to_torch(w, DEV)
+    lin = Nvfp4Linear.from_weight(wd, max_tokens=8)
+    torch.cuda.synchronize()
+    g = oracle.amax_gsa(w)
+    assert f32(lin.ws2) == g
+    oc, os_ = oracle.quantize(w, g)
+    assert np.array_equal(lin.w_codes.cpu().numpy(), oc)
+    assert np.array_equal(lin.w_scales.cpu().numpy(), os_)
+    x = W.to_bf16_bits(rng.standard_normal((5, K)))
+    y = lin(W.bf16_to_torch(x, DEV)).cpu().numpy().astype(np.float64)
+    gx = oracle.amax_gsa(x)
+    xc, xs = oracle.quantize(x, gx)
+    ref = oracle.linear(xc, xs, gx, oc, os_, g)
+    assert rel_err(y, ref) <= REL_TOL
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 def test_moe_small_stepwise(C, fused):
     say("moe small", fused)
