@@ -26,6 +26,9 @@
  *           by every group; each group has its own weight global scale).
  *   [MOE]   README.md, "MoE kernel (FusedSwiGLUScaledGroupedGemmKernel)":
  *           granularity-8 interleaved L1 weights, even subtiles gate, odd up.
+ *   [NORM]  archived_plans/CORRECTNESS_BACKLOG.md, "Compressor kv_norm --
+ *           VERIFIED CORRECT" (output = input * inv_rms * norm_weight[c]);
+ *           dsv4/_archive/layers/mhc.py, module constants (EPS_RMSN = 1e-6).
  *
  * Where the pages are silent, each function below states the reading it
  * takes.
@@ -297,5 +300,29 @@ void oracle_swiglu_deinterleave(const float *l1, int64_t M, int64_t N_inter,
             double u = l1[m * N_inter + (2 * pair + 1) * gran + off];
             h[m * H + c] = g / (1.0 + exp(-g)) * u;
         }
+    }
+}
+
+/* RMSNorm of each row [NORM]: inv_rms[m] = 1 / sqrt(mean_k x[m,k]^2 + eps)
+ * and y[m,k] = x[m,k] * inv_rms[m] * w[k], all in binary64 (the sum of
+ * squares in ascending k).  The pages give the product form and the eps;
+ * eps is added to the mean of the squares (the usual RMSNorm; a variant
+ * on the pages adds it to the sum instead, which this does not take).
+ * y may be NULL. */
+void oracle_rmsnorm(const void *x, int x_dtype, const void *w, int w_dtype, double eps,
+                    int64_t M, int64_t K, double *inv_rms, double *y)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)load_elem(x, x_dtype, m * K + k);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        inv_rms[m] = r;
+        if (y)
+            for (int64_t k = 0; k < K; ++k)
+                y[m * K + k] = (double)load_elem(x, x_dtype, m * K + k) * r *
+                               (double)load_elem(w, w_dtype, k);
     }
 }

@@ -64,6 +64,9 @@ def _load():
     lib.oracle_grouped_linear.restype = None
     lib.oracle_grouped_linear.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_int,
                                           P, P, P, I64, I64, P]
+    lib.oracle_rmsnorm.restype = None
+    lib.oracle_rmsnorm.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_double, I64, I64,
+                                   P, P]
     lib.oracle_swiglu_deinterleave.restype = None
     lib.oracle_swiglu_deinterleave.argtypes = [P, I64, I64, ctypes.c_int, P]
     _lib = lib
@@ -187,6 +190,35 @@ def grouped_linear(a_codes, a_scales, gsa, row_index, offsets, w_codes, w_scales
                                   _ptr(offsets), G, _ptr(w_codes), _ptr(w_scales),
                                   _ptr(ws2), N, K, _ptr(y))
     return y
+
+
+def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float = 1e-6):
+    """RMSNorm of each row of x (M, K) (bf16 bits or float32) with weight w
+    (K,) (bf16 bits or float32): inv_rms (M,) and y (M, K), both float64
+    (nvfp4_oracle.c, oracle_rmsnorm)."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    M, K = x.shape
+    assert w.shape == (K,)
+    inv = np.empty(M, np.float64)
+    y = np.empty((M, K), np.float64)
+    _load().oracle_rmsnorm(_ptr(x), _dtype_of(x), _ptr(w), _dtype_of(w), ctypes.c_double(eps),
+                           M, K, _ptr(inv), _ptr(y))
+    return inv, y
+
+
+def quantize_rows(y: np.ndarray):
+    """Quantize each row of y (M, K) float32 with its own global scale
+    gsa[m] = max(max|y[m]|, 1e-8) / 2688: codes, scales, gsa (M,)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    M, K = y.shape
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // 16), np.uint8)
+    gsa = np.zeros(M, np.float32)
+    for m in range(M):
+        gsa[m] = amax_gsa(y[m:m + 1])
+        codes[m:m + 1], scales[m:m + 1] = quantize(y[m:m + 1], gsa[m])
+    return codes, scales, gsa
 
 
 def swiglu_deinterleave(l1: np.ndarray, granularity: int = 8) -> np.ndarray:

@@ -366,3 +366,78 @@ def test_swiglu_matches_torch_silu():
     t = torch.from_numpy(l1.astype(np.float64)).reshape(4, 4, 2, 8)
     ref = (torch.nn.functional.silu(t[:, :, 0]) * t[:, :, 1]).reshape(4, 32).numpy()
     assert np.max(np.abs(h - ref)) <= 1e-14 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_constant_row_closed_form():
+    """A row of equal values c: mean of squares c^2, inv_rms = 1/sqrt(c^2 + eps)."""
+    K, c, eps = 48, 0.75, 1e-6
+    x = np.full((1, K), c, np.float32)
+    w = np.linspace(0.5, 2.0, K).astype(np.float32)
+    inv, y = oracle.rmsnorm(x, w, eps)
+    want = 1.0 / math.sqrt(c * c + eps)
+    assert inv[0] == pytest.approx(want, rel=1e-15)
+    assert np.allclose(y[0], c * want * w.astype(np.float64), rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_worked_vector():
+    """x = (3, 4), eps = 0: mean of squares 12.5; weight (1, 2) scales the
+    second element."""
+    x = np.array([[3.0, 4.0]], np.float32)
+    w = np.array([1.0, 2.0], np.float32)
+    inv, y = oracle.rmsnorm(x, w, 0.0)
+    assert inv[0] == pytest.approx(1.0 / math.sqrt(12.5), rel=1e-15)
+    assert y[0, 0] == pytest.approx(3.0 / math.sqrt(12.5), rel=1e-15)
+    assert y[0, 1] == pytest.approx(8.0 / math.sqrt(12.5), rel=1e-15)
+
+
+def test_rmsnorm_matches_torch_definition():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((6, 160)) * 3).astype(np.float32)
+    w = rng.uniform(0.2, 4.0, 160).astype(np.float32)
+    inv, y = oracle.rmsnorm(x, w, 1e-6)
+    t = torch.from_numpy(x.astype(np.float64))
+    ref = t * torch.rsqrt(t.pow(2).mean(-1, keepdim=True) + 1e-6) * torch.from_numpy(
+        w.astype(np.float64))
+    assert np.max(np.abs(y - ref.numpy())) <= 1e-14 * np.max(np.abs(ref.numpy()))
+
+
+def test_rmsnorm_bf16_inputs_and_properties():
+    """bf16 bits give the same result as their float32 values; with eps = 0
+    and unit weight every row has mean square 1 and scaling a row by a
+    power of two changes nothing."""
+    rng = np.random.default_rng(6)
+    xb = W.to_bf16_bits(rng.standard_normal((4, 64)))
+    wb = W.to_bf16_bits(rng.uniform(0.5, 1.5, 64))
+    xf, wf = W.bf16_bits_to_f32(xb), W.bf16_bits_to_f32(wb)
+    i1, y1 = oracle.rmsnorm(xb, wb)
+    i2, y2 = oracle.rmsnorm(xf, wf)
+    assert np.array_equal(i1, i2) and np.array_equal(y1, y2)
+    ones = np.ones(64, np.float32)
+    _, y = oracle.rmsnorm(xf, ones, 0.0)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-14, atol=0)
+    _, y8 = oracle.rmsnorm(xf * np.float32(8.0), ones, 0.0)
+    assert np.allclose(y8, y, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_eps_bounds_tiny_rows():
+    """A row far below sqrt(eps): inv_rms tends to 1/sqrt(eps)."""
+    x = np.full((1, 32), 1e-9, np.float32)
+    inv, _ = oracle.rmsnorm(x, np.ones(32, np.float32), 1e-6)
+    assert inv[0] == pytest.approx(1e3, rel=1e-9)
+
+
+def test_quantize_rows_uses_each_rows_scale():
+    """Per-row global scales: each row's gsa is its own amax / 2688, and a
+    row scaled by 2^k gets its gsa scaled by 2^k with identical codes and
+    block scales (the per-row form is invariant to a row's scale)."""
+    rng = np.random.default_rng(7)
+    y = (rng.standard_normal((3, 64)) * np.array([[1.0], [40.0], [1e-3]])).astype(np.float32)
+    codes, scales, gsa = oracle.quantize_rows(y)
+    for m in range(3):
+        assert gsa[m] == oracle.amax_gsa(y[m:m + 1])
+        c1, s1 = oracle.quantize(y[m:m + 1], gsa[m])
+        assert np.array_equal(codes[m:m + 1], c1) and np.array_equal(scales[m:m + 1], s1)
+    c2, s2, g2 = oracle.quantize_rows(y * np.float32(16.0))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+    assert np.array_equal(g2, gsa * np.float32(16.0))
