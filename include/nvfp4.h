@@ -89,12 +89,14 @@ extern "C" {
 #define NVFP4_OP_LINEAR_RUN 4
 #define NVFP4_OP_GROUPED_SWIGLU 5
 #define NVFP4_OP_QUANTIZE_WEIGHT 6
+#define NVFP4_OP_RMSNORM_QUANTIZE 7
 
 /* Bytes of workspace an operation needs for the given sizes (0 if none).
  * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored;
  * for NVFP4_OP_LINEAR_RUN, the activation is (M, K); for
  * NVFP4_OP_GROUPED_SWIGLU, N is N_inter and G the group count; for
- * NVFP4_OP_QUANTIZE_WEIGHT, the weight is (N, K). */
+ * NVFP4_OP_QUANTIZE_WEIGHT, the weight is (N, K); for
+ * NVFP4_OP_RMSNORM_QUANTIZE, the activation is (M, K). */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
 
 /* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
@@ -114,8 +116,34 @@ int nvfp4_quantize_from_buffer(const void *x, int x_dtype, int64_t M, int64_t K,
                                const float *gsa, uint8_t *codes, uint8_t *scales,
                                void *stream);
 
-/* Weight-side quantize at load time (NEXT row 3 of the hot path; the
- * pages' quantize_weight_to_nvfp4 for the lm_head and router gate, whose
+/* The producer of the activation fused into steps 1 and 2 (the pages' fused
+ * RMSNorm + NVFP4 quantize feeding run_from_quantized with an optional
+ * per-row gsa; the product form output = input * inv_rms * norm_weight from
+ * archived_plans/CORRECTNESS_BACKLOG.md, "Compressor kv_norm", and
+ * eps = 1e-6 from dsv4/_archive/layers/mhc.py): RMSNorm of each row of
+ * x (M, K) with norm_weight (K,), inv_rms = 1 / sqrt(mean(x^2) + eps), then
+ * steps 1 and 2 on the normalized rows -- without writing them out.
+ * Two kernels (three with one global scale): one workgroup per row forms
+ * inv_rms and the row's largest |y|, then the quantize recomputes y.
+ *   - inv_rms (M,) float32 receives each row's scale.
+ *   - The normalized value is y = (x * inv_rms) * w in float32 (two
+ *     roundings, in that order), and y is what is quantized: codes (M, K/2),
+ *     scales (M, K/16).
+ *   - gsa_per_row == 0: one global scale, gsa[0] = max(max|y|, 1e-8) / 2688
+ *     over the whole tensor (two-phase: row maxima into ws, then one
+ *     workgroup reduces them); ws holds nvfp4_workspace_bytes(
+ *     NVFP4_OP_RMSNORM_QUANTIZE, M, 0, K, 0) bytes.
+ *   - gsa_per_row != 0: gsa (M,), gsa[m] from row m alone (then ws is not
+ *     used); nvfp4_linear_rows takes such a gsa.
+ * x and norm_weight bf16 or fp32, 16-byte aligned; K % 16 == 0; eps > 0
+ * and finite (so a row of zeros normalizes to zeros, not 0 * inf).
+ * M == 0 writes gsa[0] = 1e-8 / 2688 (one scale) or nothing (per row). */
+int nvfp4_rmsnorm_quantize(const void *x, int x_dtype, const void *norm_weight, int w_dtype,
+                           float eps, int64_t M, int64_t K, int gsa_per_row, float *gsa,
+                           float *inv_rms, uint8_t *codes, uint8_t *scales, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Weight-side quantize at load time (the pages' quantize_weight_to_nvfp4 for the lm_head and router gate, whose
  * checkpoints hold bf16): w (N, K) bf16/fp32, K % 16 == 0, 16-byte
  * aligned, becomes codes (N, K/2), scales (N, K/16) and its global scale
  * ws2[0] = max(max|w|, 1e-8) / 2688 -- the activation recipe of steps 1
@@ -139,6 +167,17 @@ int nvfp4_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *g
                  const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
                  void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* Step 3 with one activation global scale per row (the optional per-row gsa
+ * of the pages' run_from_quantized): as nvfp4_linear, but gsa_rows is a
+ * device float32[M] and y[m] = gsa_rows[m] * ws2 * dequant(A[m]) @
+ * dequant(W)^T -- the product nvfp4_rmsnorm_quantize(..., gsa_per_row = 1)
+ * feeds.  Same kernels, same checks and alignment as nvfp4_linear; the
+ * epilogue multiplies by gsa_rows[m] * ws2 in float32.  M == 0 or N == 0 is
+ * a no-op. */
+int nvfp4_linear_rows(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa_rows,
+                      const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
+                      void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *stream);
 
 /* The whole layer on a bf16/fp32 activation, as Nvfp4Linear.run does
  * (dsv4/_archive/layers/linear.py, _run_impl): steps 1, 2 and 3 with the
@@ -190,8 +229,8 @@ int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_in
                               int granularity, void *stream);
 
 /* The step between the two expert projections, fused into the first
- * (NEXT row 1 of the hot path: SwiGLU, de-interleave and the first amax
- * phase in the grouped gate/up linear's epilogue; the pages' fused SwiGLU
+ * (SwiGLU, de-interleave and the first amax phase in the grouped gate/up
+ * linear's epilogue; the pages' fused SwiGLU
  * grouped GEMM epilogue, and the de-interleave + amax + quantize kernel that
  * consumes its output).  Same results as
  *   nvfp4_grouped_linear(..., l1, FP32, N_inter, K, ...)   l1 (M_total, N_inter)

@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 2; }
+NVFP4_API int nvfp4_abi_version(void) { return 3; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -55,6 +55,7 @@ NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, 
     case NVFP4_OP_AMAX_GSA: return M > 0 ? amax_ws_bytes(M) : 0;
     case NVFP4_OP_LINEAR_RUN: return (M > 0 && K > 0) ? amax_ws_bytes(M * K) : 0;
     case NVFP4_OP_QUANTIZE_WEIGHT: return (N > 0 && K > 0) ? amax_ws_bytes(N * K) : 0;
+    case NVFP4_OP_RMSNORM_QUANTIZE: return M > 0 ? (size_t)M * sizeof(uint32_t) : 0;
     case NVFP4_OP_GROUPED_SWIGLU:
       return (N > 0 && G > 0) ? (size_t)grouped_swiglu_parts(N, G) * sizeof(uint32_t) : 0;
     default: return 0;
@@ -90,6 +91,35 @@ NVFP4_API int nvfp4_quantize_from_buffer(const void* x, int x_dtype, int64_t M, 
                                   (hipStream_t)stream));
 }
 
+NVFP4_API int nvfp4_rmsnorm_quantize(const void* x, int x_dtype, const void* norm_weight,
+                                     int w_dtype, float eps, int64_t M, int64_t K,
+                                     int gsa_per_row, float* gsa, float* inv_rms,
+                                     uint8_t* codes, uint8_t* scales, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype)) return NVFP4_ERR_DTYPE;
+  if (M < 0 || K <= 0 || K % 16 != 0 || M > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (!(eps > 0.0f) || eps > 3.0e38f) return NVFP4_ERR_SHAPE;  // a zero row stays finite
+  if (M > 0 && (M * (K / 8) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (gsa == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned(gsa, 4)) return NVFP4_ERR_ALIGN;
+  const bool per_row = gsa_per_row != 0;
+  if (M == 0)  // one scale of nothing: the 1e-8 floor; per-row: nothing to write
+    return per_row ? NVFP4_OK
+                   : launched(launch_amax_finalize(nullptr, 0, gsa, (hipStream_t)stream));
+  if (!x || !norm_weight || !inv_rms || !codes || !scales) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(norm_weight, 16) || !aligned(codes, 8) ||
+      !aligned(inv_rms, 4))
+    return NVFP4_ERR_ALIGN;
+  if (!per_row) {
+    if (ws == nullptr || ws_bytes < (size_t)M * sizeof(uint32_t)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+  }
+  return launched(launch_rmsnorm_quantize(x, x_dtype == NVFP4_DTYPE_BF16, norm_weight,
+                                          w_dtype == NVFP4_DTYPE_BF16, eps, M, K, per_row, gsa,
+                                          inv_rms, codes, scales, (uint32_t*)ws,
+                                          (hipStream_t)stream));
+}
+
 NVFP4_API int nvfp4_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, float* ws2,
                                     uint8_t* codes, uint8_t* scales, void* ws, size_t ws_bytes,
                                     void* stream) {
@@ -110,12 +140,10 @@ NVFP4_API int nvfp4_quantize_weight(const void* w, int w_dtype, int64_t N, int64
   return launched(launch_quantize(w, bf16, N, K, ws2, codes, scales, (hipStream_t)stream));
 }
 
-NVFP4_API int nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
-                           const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                           void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* ws,
-                           size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+static int linear_impl(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
+                       int y_dtype, int64_t M, int64_t N, int64_t K, bool gsa_rows,
+                       void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   int st = check_gemm_shape(M, N, K);
   if (st != NVFP4_OK) return st;
@@ -127,8 +155,28 @@ NVFP4_API int nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, cons
   const bool ybf = y_dtype == NVFP4_DTYPE_BF16;
   hipStream_t s = (hipStream_t)stream;
   if (M <= GEMV_MAX_M)
-    return launched(launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s));
-  return launched(launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s));
+    return launched(
+        launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s, gsa_rows));
+  return launched(
+      launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s, gsa_rows));
+}
+
+NVFP4_API int nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                           void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* ws,
+                           size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return linear_impl(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_dtype, M, N, K, false,
+                     stream);
+}
+
+NVFP4_API int nvfp4_linear_rows(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const float* gsa_rows, const uint8_t* w_codes,
+                                const uint8_t* w_scales, const float* ws2, void* y, int y_dtype,
+                                int64_t M, int64_t N, int64_t K, void* stream) {
+  return linear_impl(a_codes, a_scales, gsa_rows, w_codes, w_scales, ws2, y, y_dtype, M, N, K,
+                     true, stream);
 }
 
 NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* codes,

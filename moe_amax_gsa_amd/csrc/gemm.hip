@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
-    int y_bf16, int M, int N, int K) {
+    int y_bf16, int M, int N, int K, int gsa_rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * 128 + wm * 64, n0 = blockIdx.x * 128 + wn * 64;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(
         const int row = m0 + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         const int col = n0 + b * 32 + r32;
         if (row < M && col < N) {
-          const float v = acc[a][b][r] * gscale;
+          const float v = acc[a][b][r] * (gsa_rows ? gsa_p[row] * ws2_p[0] : gscale);
           if (y_bf16)
             ((uint16_t*)y)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(v);
           else
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
-    int y_bf16, int M, int N, int K) {
+    int y_bf16, int M, int N, int K, int gsa_rows) {
   using T = LdsTile<WM, WN, STAGES, KW>;
   constexpr int TM = T::TM, TN = T::TN, LDT = TN + 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
         for (int w = 1; w < KW; ++w) v += red[(w * 16 + rr) * LDT + cc];
         const int row = m0 + a * 32 + q * 16 + rr, col = n0 + cc;
         if (row < M && col < N) {
-          const float o = v * gscale;
+          const float o = v * (gsa_rows ? gsa_p[row] * ws2_p[0] : gscale);
           if (y_bf16)
             ((uint16_t*)y)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(o);
           else
@@ -478,7 +478,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
 template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE = false>
 hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
-                      bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                      bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                      bool gsa_rows = false) {
   using T = LdsTile<WM, WN, STAGES, KW>;
   static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
   static const hipError_t attr = hipFuncSetAttribute(
@@ -487,7 +488,8 @@ hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM));
   gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
-      a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K);
+      a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K,
+      gsa_rows ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -508,7 +510,8 @@ static int cu_count() {
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                       bool gsa_rows) {
   const bool fast = (K % 64 == 0) && (((uintptr_t)a_codes | (uintptr_t)w_codes) & 15u) == 0 &&
                     (((uintptr_t)a_scales | (uintptr_t)w_scales) & 1u) == 0;
   // the staged kernel takes whole 256-element chunks and 32-bit row offsets
@@ -521,17 +524,19 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     const int64_t tiles = ((N + 63) / 64) * ((M + 127) / 128);
     if (tiles <= cu_count() && K % 512 == 0)
       return launch_lds<4, 2, 2, 2, 8, true>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,
-                                             y_bf16, M, N, K, s);
+                                             y_bf16, M, N, K, s, gsa_rows);
     return launch_lds<4, 2, 2, 2, 4>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M,
-                                     N, K, s);
+                                     N, K, s, gsa_rows);
   }
   dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
   if (fast)
     gemm_f16_kernel<true><<<grid, 256, 0, s>>>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,
-                                               y_bf16 ? 1 : 0, (int)M, (int)N, (int)K);
+                                               y_bf16 ? 1 : 0, (int)M, (int)N, (int)K,
+                                               gsa_rows ? 1 : 0);
   else
     gemm_f16_kernel<false><<<grid, 256, 0, s>>>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,
-                                                y_bf16 ? 1 : 0, (int)M, (int)N, (int)K);
+                                                y_bf16 ? 1 : 0, (int)M, (int)N, (int)K,
+                                                gsa_rows ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -65,6 +65,8 @@ struct GemvArgs {
   // (bits of a non-negative float) per workgroup
   int gran;
   uint32_t* partials;
+  // plain mode: gsa holds one global scale per activation row (gsa[m])
+  int gsa_rows;
 };
 
 __device__ __forceinline__ float4_t mfma_fp4(v8i a, v8i b) {
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
       if (MODE == MODE_GROUPED && args.row_index != nullptr && ok)
         ok = args.row_index[r] >= 0 && args.row_index[r] < args.a_rows;
       if (ok) {
-        const float v = s * gscale;
+        const float v = s * (args.gsa_rows ? args.gsa[r] * args.ws2[g] : gscale);
         if (args.y_bf16)
           ((uint16_t*)args.y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v);
         else
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
     for (int d = 1; d < 16; d <<= 1) sum += __shfl_xor(sum, d, 64);
     const int n = n0 + rr;
     if (w == 0 && o < MR * 4 * RQ && m < M && n < N) {
-      const float v = sum * gscale;
+      const float v = sum * (args.gsa_rows ? args.gsa[m] * args.ws2[0] : gscale);
       if (args.y_bf16)
         ((uint16_t*)args.y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
       else
@@ -1026,8 +1028,10 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
 
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                       bool gsa_rows) {
   GemvArgs a{};
+  a.gsa_rows = gsa_rows ? 1 : 0;
   a.a_codes = a_codes;
   a.a_scales = a_scales;
   a.gsa = gsa;

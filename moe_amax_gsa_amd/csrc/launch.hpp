@@ -27,15 +27,24 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
 hipError_t launch_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t NI, int gran,
                                       hipStream_t s);
 
+// RMSNorm + quantize: per-row gsa (M,) or one gsa (then `partials` holds M
+// row maxima).
+hipError_t launch_rmsnorm_quantize(const void* x, bool x_bf16, const void* w, bool w_bf16,
+                                   float eps, int64_t M, int64_t K, bool per_row, float* gsa,
+                                   float* inv_rms, uint8_t* codes, uint8_t* scales,
+                                   uint32_t* partials, hipStream_t s);
+
 // Phase 2 of an amax over partials (bits of non-negative fp32 maxima): gsa.
 hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float* gsa,
                                 hipStream_t s);
 
 // Weight-streaming linear for few rows (FP4 matrix cores).
 constexpr int64_t GEMV_MAX_M = 16;
+// gsa_rows: gsa holds one global scale per row (gsa[m]).
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s);
+                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                       bool gsa_rows = false);
 
 // Grouped weight-streaming linear (device-side group sizes).
 hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
@@ -83,6 +92,7 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
 // Tiled GEMM for many rows (dequantize to f16, f16 matrix cores).
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s);
+                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                       bool gsa_rows = false);
 
 }  // namespace nvfp4

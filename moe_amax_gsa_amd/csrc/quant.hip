@@ -217,6 +217,126 @@ hipError_t launch_amax_quantize_small(const void* x, bool bf16, int64_t M, int64
               : launch_small_t<false>(x, nhalf, gsa, codes, scales, s);
 }
 
+// ---------------------------------------------------------------- RMSNorm
+// RMSNorm fused into the quantize, in two kernels.  y = (x * r) * w in fp32
+// (two roundings, in that order), r = 1 / sqrt(sum(x^2) / K + eps) per row.
+// Kernel 1, one workgroup per row: the sum of squares, r, then the largest
+// |y| of the row (y is formed as kernel 2 forms it, so the maximum is of
+// the values that are quantized).  Per-row scales: it writes gsa[m]
+// directly.  One scale: it writes the row maximum as a partial, a single
+// workgroup reduces the partials into gsa (the grid-wide phase), and
+// kernel 2 reads gsa[0].  Kernel 2 forms y again per half-block and
+// quantizes it as quantize_kernel does.
+__device__ __forceinline__ float block_sum_f32(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+template <bool XBF16, bool WBF16>
+__device__ __forceinline__ void rms_y8(const void* x, const void* w, int64_t hx, int64_t hw,
+                                       float r, float y[8]) {
+#pragma clang fp contract(off)
+  float xv[8], wv[8];
+  load_half8<XBF16>(x, hx, xv);
+  load_half8<WBF16>(w, hw, wv);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (xv[i] * r) * wv[i];
+}
+
+template <bool XBF16, bool WBF16, bool PER_ROW>
+__global__ __launch_bounds__(256) void rmsnorm_stats_kernel(
+    const void* __restrict__ x, const void* __restrict__ w, float eps, int64_t K,
+    float* __restrict__ inv_rms, float* __restrict__ gsa, uint32_t* __restrict__ partials) {
+#pragma clang fp contract(off)
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x, K8 = K / 8;
+  float ss = 0.f;
+  for (int64_t h = threadIdx.x; h < K8; h += 256) {
+    float v[8];
+    load_half8<XBF16>(x, m * K8 + h, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+  }
+  ss = block_sum_f32(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)K + eps);
+  float mx = 0.f;
+  for (int64_t h = threadIdx.x; h < K8; h += 256) {
+    float y[8];
+    rms_y8<XBF16, WBF16>(x, w, m * K8 + h, h, r, y);
+    mx = fmaxf(mx, half_absmax8(y));
+  }
+  const uint32_t mb = block_max_u32<256>(__float_as_uint(mx));
+  if (threadIdx.x == 0) {
+    inv_rms[m] = r;
+    if (PER_ROW)
+      gsa[m] = gsa_from_amax(__uint_as_float(mb));
+    else
+      partials[m] = mb;
+  }
+}
+
+template <bool XBF16, bool WBF16, bool PER_ROW>
+__global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
+    const void* __restrict__ x, const void* __restrict__ w, int64_t K, int64_t nhalf,
+    const float* __restrict__ inv_rms, const float* __restrict__ gsa_p,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = h < nhalf;  // nhalf is even, so both lanes of a block agree
+  const int64_t K8 = K / 8, hh = ok ? h : 0, m = hh / K8;
+  float y[8];
+  rms_y8<XBF16, WBF16>(x, w, hh, hh - m * K8, inv_rms[m], y);
+  const float gsa = gsa_p[PER_ROW ? m : 0];
+  float bm = half_absmax8(y);
+  bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+  uint32_t c, sf;
+  quantize_half8(y, bm, gsa, c, sf);
+  if (ok) {
+    ((uint32_t*)codes)[h] = c;
+    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sf;
+  }
+}
+
+template <bool XBF16, bool WBF16, bool PER_ROW>
+static hipError_t launch_rmsnorm_t(const void* x, const void* w, float eps, int64_t M, int64_t K,
+                                   float* gsa, float* inv_rms, uint8_t* codes, uint8_t* scales,
+                                   uint32_t* partials, hipStream_t s) {
+  rmsnorm_stats_kernel<XBF16, WBF16, PER_ROW><<<(unsigned)M, 256, 0, s>>>(x, w, eps, K, inv_rms,
+                                                                         gsa, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (!PER_ROW) {
+    amax_finalize_kernel<false><<<1, AMAX_THREADS, 0, s>>>(partials, (int)M, gsa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nhalf = M * (K / 8);
+  rmsnorm_quantize_kernel<XBF16, WBF16, PER_ROW><<<(unsigned)((nhalf + 255) / 256), 256, 0, s>>>(
+      x, w, K, nhalf, inv_rms, gsa, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quantize(const void* x, bool x_bf16, const void* w, bool w_bf16,
+                                   float eps, int64_t M, int64_t K, bool per_row, float* gsa,
+                                   float* inv_rms, uint8_t* codes, uint8_t* scales,
+                                   uint32_t* partials, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+#define RMS_CASE(XB, WB, PR)                                                                   \
+  if (x_bf16 == XB && w_bf16 == WB && per_row == PR)                                           \
+    return launch_rmsnorm_t<XB, WB, PR>(x, w, eps, M, K, gsa, inv_rms, codes, scales, partials, \
+                                        s);
+  RMS_CASE(true, true, true) RMS_CASE(true, true, false) RMS_CASE(true, false, true)
+  RMS_CASE(true, false, false) RMS_CASE(false, true, true) RMS_CASE(false, true, false)
+  RMS_CASE(false, false, true) RMS_CASE(false, false, false)
+#undef RMS_CASE
+  return hipErrorInvalidValue;
+}
+
 // ---------------------------------------------------------------- SwiGLU
 // Thread t handles output column c of row m; gate group 2p and up group 2p+1.
 __global__ __launch_bounds__(256) void swiglu_deinterleave_kernel(const float* __restrict__ l1,

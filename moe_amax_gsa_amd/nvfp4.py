@@ -28,6 +28,7 @@ OP_GROUPED_LINEAR = 3
 OP_LINEAR_RUN = 4
 OP_GROUPED_SWIGLU = 5
 OP_QUANTIZE_WEIGHT = 6
+OP_RMSNORM_QUANTIZE = 7
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_amax_gsa_amd.build`")
@@ -51,12 +52,17 @@ lib.nvfp4_quantize_from_buffer.restype = _I
 lib.nvfp4_quantize_from_buffer.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P]
 lib.nvfp4_linear.restype = _I
 lib.nvfp4_linear.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_linear_rows.restype = _I
+lib.nvfp4_linear_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P]
 lib.nvfp4_linear_run.restype = _I
 lib.nvfp4_linear_run.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ,
                                  _P]
 lib.nvfp4_grouped_linear.restype = _I
 lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
                                      _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_rmsnorm_quantize.restype = _I
+lib.nvfp4_rmsnorm_quantize.argtypes = [_P, _I, _P, _I, ctypes.c_float, _I64, _I64, _I, _P, _P,
+                                       _P, _P, _P, _SZ, _P]
 lib.nvfp4_quantize_weight.restype = _I
 lib.nvfp4_quantize_weight.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]
 lib.nvfp4_grouped_linear_swiglu.restype = _I
@@ -136,6 +142,18 @@ def nvfp4_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tenso
                             _stream(stream)), "nvfp4_linear")
 
 
+def nvfp4_linear_rows(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa_rows: torch.Tensor,
+                      w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
+                      y: torch.Tensor, stream=None) -> None:
+    """y[m] = gsa_rows[m] * ws2 * dequant(A[m]) @ dequant(W)^T; gsa_rows (M,)."""
+    M = a_codes.shape[0]
+    K = a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    _check(lib.nvfp4_linear_rows(_ptr(a_codes), _ptr(a_scales), _ptr(gsa_rows), _ptr(w_codes),
+                                 _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y), M, N, K,
+                                 _stream(stream)), "nvfp4_linear_rows")
+
+
 def nvfp4_linear_run(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
                      scales: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
                      ws2: torch.Tensor, y: torch.Tensor, ws: Optional[torch.Tensor] = None,
@@ -164,6 +182,20 @@ def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: tor
                                     _dtype(y), N, K, _ptr(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)), "nvfp4_grouped_linear")
+
+
+def nvfp4_rmsnorm_quantize(x: torch.Tensor, norm_weight: torch.Tensor, gsa: torch.Tensor,
+                           inv_rms: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                           eps: float = 1e-6, per_row: bool = False,
+                           ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """RMSNorm of x (M, K) with norm_weight (K,), quantized: codes (M, K/2),
+    scales (M, K/16), inv_rms (M,), gsa (1,) or, per_row, (M,)."""
+    M, K = x.shape
+    _check(lib.nvfp4_rmsnorm_quantize(_ptr(x), _dtype(x), _ptr(norm_weight), _dtype(norm_weight),
+                                      eps, M, K, 1 if per_row else 0, _ptr(gsa), _ptr(inv_rms),
+                                      _ptr(codes), _ptr(scales), _ptr(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(),
+                                      _stream(stream)), "nvfp4_rmsnorm_quantize")
 
 
 def nvfp4_quantize_weight(w: torch.Tensor, ws2: torch.Tensor, codes: torch.Tensor,

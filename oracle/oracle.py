@@ -221,6 +221,20 @@ def quantize_rows(y: np.ndarray):
     return codes, scales, gsa
 
 
+def linear_rows(a_codes, a_scales, gsa_rows, w_codes, w_scales, ws2) -> np.ndarray:
+    """The linear with one activation global scale per row: row m is the
+    linear of row m alone with gsa_rows[m] (y (M, N) float64)."""
+    a_codes = np.ascontiguousarray(a_codes)
+    a_scales = np.ascontiguousarray(a_scales)
+    gsa_rows = np.asarray(gsa_rows, dtype=np.float32)
+    M = a_codes.shape[0]
+    y = np.empty((M, w_codes.shape[0]), np.float64)
+    for m in range(M):
+        y[m:m + 1] = linear(a_codes[m:m + 1], a_scales[m:m + 1], gsa_rows[m], w_codes, w_scales,
+                            ws2)
+    return y
+
+
 def swiglu_deinterleave(l1: np.ndarray, granularity: int = 8) -> np.ndarray:
     l1 = np.ascontiguousarray(l1, dtype=np.float32)
     M, NI = l1.shape

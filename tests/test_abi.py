@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(C):
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert C.nvfp4_abi_version() == 2
+    assert C.nvfp4_abi_version() == 3
 
 
 def test_status_strings(C):
@@ -79,3 +79,38 @@ def test_validation_errors_return_before_any_launch(C):
                                   1, 16, 32, None, 0, None) == -2
     assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 24, 8, None) == -2
     assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 32, 0, None) == -2
+
+
+def test_validation_of_the_fused_and_load_time_entries(C):
+    L = C.lib
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation
+    rq = L.nvfp4_rmsnorm_quantize
+    # (x, x_dtype, w, w_dtype, eps, M, K, per_row, gsa, inv_rms, codes, scales, ws, ws_bytes, s)
+    assert rq(fake, 0, fake, 0, 1e-6, 4, 24, 0, fake, fake, fake, fake, fake, 64, None) == -2
+    assert rq(fake, 0, fake, 0, 0.0, 4, 32, 1, fake, fake, fake, fake, None, 0, None) == -2
+    assert rq(fake, 0, fake, 0, -1.0, 4, 32, 1, fake, fake, fake, fake, None, 0, None) == -2
+    assert rq(fake, 0, fake, 0, float("nan"), 4, 32, 1, fake, fake, fake, fake, None, 0,
+              None) == -2
+    assert rq(fake, 3, fake, 0, 1e-6, 4, 32, 1, fake, fake, fake, fake, None, 0, None) == -3
+    assert rq(fake, 0, fake, 0, 1e-6, 4, 32, 1, None, fake, fake, fake, None, 0, None) == -1
+    assert rq(fake, 0, None, 0, 1e-6, 4, 32, 1, fake, fake, fake, fake, None, 0, None) == -1
+    assert rq(ctypes.c_void_p(4104), 0, fake, 0, 1e-6, 4, 32, 1, fake, fake, fake, fake, None,
+              0, None) == -5
+    # one global scale needs M * 4 bytes of workspace for the row maxima
+    assert C.nvfp4_workspace_bytes(C.OP_RMSNORM_QUANTIZE, 4, 0, 32) == 16
+    assert rq(fake, 0, fake, 0, 1e-6, 4, 32, 0, fake, fake, fake, fake, fake, 12, None) == -4
+    assert rq(fake, 0, fake, 0, 1e-6, 4, 32, 0, fake, fake, fake, fake, None, 0, None) == -4
+    assert rq(fake, 0, fake, 0, 1e-6, 0, 32, 1, fake, None, None, None, None, 0, None) == 0
+    lr = L.nvfp4_linear_rows
+    args = [fake] * 7
+    assert lr(*args, 0, 2, 3, 24, None) == -2
+    assert lr(*args, 5, 2, 3, 32, None) == -3
+    assert lr(fake, fake, None, fake, fake, fake, fake, 1, 2, 3, 32, None) == -1
+    assert lr(*args, 1, 0, 3, 32, None) == 0  # M == 0: no-op
+    qw = L.nvfp4_quantize_weight
+    assert qw(fake, 0, 0, 32, fake, fake, fake, None, 0, None) == -2
+    assert qw(fake, 0, 4, 40, fake, fake, fake, None, 0, None) == -2
+    assert qw(fake, 0, 4, 32, None, fake, fake, None, 0, None) == -1
+    big = C.nvfp4_workspace_bytes(C.OP_QUANTIZE_WEIGHT, 0, 4096, 4096)
+    assert big > 0
+    assert qw(fake, 0, 4096, 4096, fake, fake, fake, None, 0, None) == -4

@@ -573,6 +573,117 @@ def test_grouped_ring_shapes(C, K, N, sizes):
             assert err <= REL_TOL, (g, r, err)
 
 
+# ---------------------------------------------------------------- RMSNorm -> quantize
+# inv_rms: the kernel sums K squares in float32 (per-thread runs of K/2048
+# terms, then a 256-way tree) and takes a correctly rounded divide and
+# square root: relative error below (K/2048 + 12) * 2^-24 + 2 ulp, under
+# 4e-6 for K <= 32768.  1e-5 leaves room.
+INV_RMS_TOL = 1e-5
+
+
+def rms_case(M, K, seed, zero_row=False):
+    rng = np.random.default_rng(seed)
+    x64 = rng.standard_normal((M, K)) * np.exp(rng.uniform(-3, 3, (M, 1)))
+    x64[rng.random((M, K)) < 0.002] *= 40.0  # a few outliers per row
+    if zero_row:
+        x64[M // 2] = 0.0
+    w64 = 1.0 + 0.25 * rng.standard_normal(K)
+    return W.to_bf16_bits(x64), W.to_bf16_bits(w64)
+
+
+def gpu_rmsnorm_quantize(C, x, w, per_row, eps=1e-6):
+    M, K = x.shape
+    gsa = torch.full((M if per_row else 1,), -1.0, dtype=torch.float32, device=DEV)
+    inv = torch.full((M,), -1.0, dtype=torch.float32, device=DEV)
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    nws = max(4, C.nvfp4_workspace_bytes(C.OP_RMSNORM_QUANTIZE, M, 0, K))
+    ws = torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV)
+    C.nvfp4_rmsnorm_quantize(x, w, gsa, inv, codes, scales, eps=eps, per_row=per_row, ws=ws)
+    return gsa, inv, codes, scales
+
+
+RMS_CASES = [
+    (1, 16, "bf16", "bf16"), (1, 7168, "bf16", "bf16"), (3, 272, "fp32", "bf16"),
+    (5, 1040, "bf16", "fp32"), (64, 2048, "fp32", "fp32"), (130, 7168, "bf16", "bf16"),
+    (257, 4096, "bf16", "fp32"),
+]
+
+
+@pytest.mark.parametrize("per_row", [False, True], ids=["one_gsa", "gsa_per_row"])
+@pytest.mark.parametrize("M,K,xd,wd", RMS_CASES)
+def test_rmsnorm_quantize(C, M, K, xd, wd, per_row):
+    """inv_rms against the oracle's binary64 RMSNorm; the normalized rows
+    rebuilt on the host from the GPU's inv_rms with the kernel's two float32
+    products, (x * inv_rms) * w, so that the quantize decisions are taken in
+    one precision on both sides: gsa, codes and scales bit-exact with the
+    oracle's quantize of those rows."""
+    say(f"rmsnorm quantize M={M} K={K} x={xd} w={wd} per_row={per_row}")
+    xb, wb = rms_case(M, K, seed=M * 7 + K, zero_row=M >= 3)
+    xh, wh = x_host(xb, xd), x_host(wb, wd)
+    gsa, inv, codes, scales = gpu_rmsnorm_quantize(C, x_dev(xb, xd), x_dev(wb, wd), per_row)
+    inv_g = inv.cpu().numpy()
+    inv_o, y_o = oracle.rmsnorm(xh, wh, 1e-6)
+    assert np.max(np.abs(inv_g / inv_o - 1.0)) <= INV_RMS_TOL
+    x32 = W.bf16_bits_to_f32(xb)
+    w32 = W.bf16_bits_to_f32(wb)
+    y32 = (x32 * inv_g[:, None]).astype(np.float32) * w32[None, :]
+    assert y32.dtype == np.float32
+    assert np.max(np.abs(y32 - y_o)) <= 4 * INV_RMS_TOL * np.max(np.abs(y_o))
+    if per_row:
+        oc, os_, og = oracle.quantize_rows(y32)
+        assert np.array_equal(gsa.cpu().numpy(), og)
+    else:
+        og = oracle.amax_gsa(y32)
+        assert f32(gsa) == og
+        oc, os_ = oracle.quantize(y32, og)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    if M >= 3:  # the zero row: inv_rms = 1/sqrt(eps), codes and scales 0
+        assert np.all(codes.cpu().numpy()[M // 2] == 0) and np.all(scales.cpu().numpy()[M // 2] == 0)
+
+
+def test_rmsnorm_quantize_empty(C):
+    say("rmsnorm quantize M=0")
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(256, dtype=torch.bfloat16, device=DEV)
+    gsa, _, _, _ = gpu_rmsnorm_quantize(C, x, w, per_row=False)
+    assert f32(gsa) == oracle.gsa_from_amax(0.0)
+
+
+LINEAR_ROWS_CASES = [
+    (1, 96, 7168), (3, 130, 1024),            # one-pass kernel
+    (9, 40, 2048), (5, 33, 272),              # 16-row kernel, staged and ragged K
+    (64, 96, 1024), (130, 300, 768),          # LDS-staged tiles (eight / four waves)
+    (40, 70, 320), (33, 50, 272),             # direct tiles, aligned and ragged K
+]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_ROWS_CASES)
+def test_linear_rows(C, M, N, K):
+    """RMSNorm -> quantize with one gsa per row, then the linear that takes
+    that gsa: y[m] against the oracle's linear of row m with gsa[m]; bf16
+    output is the float32 output rounded."""
+    say(f"linear rows M={M} N={N} K={K}")
+    xb, wb = rms_case(M, K, seed=M + N + K)
+    gsa, _, codes, scales = gpu_rmsnorm_quantize(C, x_dev(xb, "bf16"), x_dev(wb, "bf16"), True)
+    inp = W.make_linear(1, K, N, seed=K + 1, sf=(0.125, 8.0), ws2=0.0037)
+    wc, wsc = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=DEV)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_rows(codes, scales, gsa, wc, wsc, ws2, y)
+    ref = oracle.linear_rows(codes.cpu().numpy(), scales.cpu().numpy(), gsa.cpu().numpy(),
+                             inp.w_codes, inp.w_scales, inp.ws2)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(yg))
+    # each row against its own magnitude: the rows' scales differ by up to e^6
+    err = np.max(np.abs(yg - ref), axis=1) / np.maximum(np.max(np.abs(ref), axis=1), 1e-300)
+    assert np.max(err) <= REL_TOL
+    y16 = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    C.nvfp4_linear_rows(codes, scales, gsa, wc, wsc, ws2, y16)
+    assert torch.equal(y16.cpu(), y.cpu().to(torch.bfloat16))
+
+
 def test_swiglu_parity(C):
     say("swiglu")
     rng = np.random.default_rng(1)

@@ -441,3 +441,21 @@ def test_quantize_rows_uses_each_rows_scale():
     c2, s2, g2 = oracle.quantize_rows(y * np.float32(16.0))
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
     assert np.array_equal(g2, gsa * np.float32(16.0))
+
+
+def test_linear_rows_is_the_linear_of_each_row_with_its_scale():
+    """Per-row global scale: equal scales give the one-scale linear; the
+    rows of distinct scales are that linear's rows times gsa[m] / gsa."""
+    rng = np.random.default_rng(31)
+    M, N, K = 5, 7, 64
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asf = rng.integers(0x20, 0x48, (M, K // 16), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wsf = rng.integers(0x20, 0x48, (N, K // 16), dtype=np.uint8)
+    g0 = np.float32(0.0625)
+    base = oracle.linear(ac, asf, g0, wc, wsf, np.float32(0.5))
+    same = oracle.linear_rows(ac, asf, np.full(M, g0, np.float32), wc, wsf, np.float32(0.5))
+    assert np.array_equal(same, base)
+    g = np.float32(2.0) ** rng.integers(-6, 6, M).astype(np.float32)
+    y = oracle.linear_rows(ac, asf, g, wc, wsf, np.float32(0.5))
+    assert np.allclose(y, base * (g / g0)[:, None], rtol=1e-14, atol=0)
