@@ -42,8 +42,11 @@ class Nvfp4Linear:
         self.max_tokens = max_tokens
         dev = self.device
         self.gsa = torch.zeros(1, dtype=torch.float32, device=dev)
-        nws = C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, max_tokens, self.N, self.K)
+        nws = max(C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, max_tokens, self.N, self.K),
+                  C.nvfp4_workspace_bytes(C.OP_RMSNORM_QUANTIZE, max_tokens, 0, self.K))
         self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+        self.gsa_rows = torch.zeros(max_tokens, dtype=torch.float32, device=dev)
+        self.inv_rms = torch.zeros(max_tokens, dtype=torch.float32, device=dev)
         self.codes = torch.empty(max_tokens, self.K // 2, dtype=torch.uint8, device=dev)
         self.scales = torch.empty(max_tokens, self.K // 16, dtype=torch.uint8, device=dev)
         self.y = torch.empty(max_tokens, self.N, dtype=out_dtype, device=dev)
@@ -69,11 +72,32 @@ class Nvfp4Linear:
         C.nvfp4_quantize_from_buffer(x, self.gsa, self.codes[:M], self.scales[:M], stream)
         return self.codes[:M], self.scales[:M], self.gsa
 
-    def run_from_quantized(self, codes, scales, gsa, stream=None) -> torch.Tensor:
+    def run_from_quantized(self, codes, scales, gsa, stream=None,
+                           gsa_per_row: bool = False) -> torch.Tensor:
+        """Step 3 on an already quantized activation; gsa is one scale, or
+        with gsa_per_row one per row (M,)."""
         M = codes.shape[0]
         y = self.y[:M]
-        C.nvfp4_linear(codes, scales, gsa, self.w_codes, self.w_scales, self.ws2, y, None, stream)
+        if gsa_per_row:
+            assert gsa.numel() >= M
+            C.nvfp4_linear_rows(codes, scales, gsa, self.w_codes, self.w_scales, self.ws2, y,
+                                stream)
+        else:
+            C.nvfp4_linear(codes, scales, gsa, self.w_codes, self.w_scales, self.ws2, y, None,
+                           stream)
         return y
+
+    def rmsnorm_forward(self, x: torch.Tensor, norm_weight: torch.Tensor, eps: float = 1e-6,
+                        gsa_per_row: bool = False, stream=None) -> torch.Tensor:
+        """RMSNorm of x fused into the quantize (nvfp4_rmsnorm_quantize), then
+        step 3; with gsa_per_row every row keeps its own global scale."""
+        M = x.shape[0]
+        assert M <= self.max_tokens and x.shape[1] == self.K
+        gsa = self.gsa_rows[:M] if gsa_per_row else self.gsa
+        C.nvfp4_rmsnorm_quantize(x, norm_weight, gsa, self.inv_rms[:M], self.codes[:M],
+                                 self.scales[:M], eps=eps, per_row=gsa_per_row, ws=self.ws,
+                                 stream=stream)
+        return self.run_from_quantized(self.codes[:M], self.scales[:M], gsa, stream, gsa_per_row)
 
     def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
         """The three steps as three calls of the C ABI."""

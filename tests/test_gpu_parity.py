@@ -684,6 +684,32 @@ def test_linear_rows(C, M, N, K):
     assert torch.equal(y16.cpu(), y.cpu().to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("per_row", [False, True], ids=["one_gsa", "gsa_per_row"])
+def test_layer_rmsnorm_forward(C, per_row):
+    """Nvfp4Linear.rmsnorm_forward: the oracle's RMSNorm -> quantize ->
+    linear, row by row against each row's magnitude."""
+    from moe_amax_gsa_amd.layer import Nvfp4Linear
+    M, K, N = 7, 1024, 80
+    say(f"layer rmsnorm_forward per_row={per_row}")
+    xb, wb = rms_case(M, K, seed=77)
+    inp = W.make_linear(1, K, N, seed=78, ws2=0.0041)
+    lin = Nvfp4Linear(to_dev(inp.w_codes), to_dev(inp.w_scales), inp.ws2, max_tokens=16)
+    y = lin.rmsnorm_forward(x_dev(xb, "bf16"), x_dev(wb, "bf16"), gsa_per_row=per_row)
+    yg = y.cpu().numpy().astype(np.float64)
+    y32 = ((W.bf16_bits_to_f32(xb) * lin.inv_rms[:M].cpu().numpy()[:, None]).astype(np.float32)
+           * W.bf16_bits_to_f32(wb)[None, :])
+    if per_row:
+        oc, os_, og = oracle.quantize_rows(y32)
+        ref = oracle.linear_rows(oc, os_, og, inp.w_codes, inp.w_scales, inp.ws2)
+    else:
+        og = oracle.amax_gsa(y32)
+        oc, os_ = oracle.quantize(y32, og)
+        ref = oracle.linear(oc, os_, og, inp.w_codes, inp.w_scales, inp.ws2)
+    assert np.array_equal(lin.codes[:M].cpu().numpy(), oc)
+    err = np.max(np.abs(yg - ref), axis=1) / np.maximum(np.max(np.abs(ref), axis=1), 1e-300)
+    assert np.max(err) <= REL_TOL
+
+
 def test_swiglu_parity(C):
     say("swiglu")
     rng = np.random.default_rng(1)
