@@ -29,6 +29,12 @@
  *   [NORM]  archived_plans/CORRECTNESS_BACKLOG.md, "Compressor kv_norm --
  *           VERIFIED CORRECT" (output = input * inv_rms * norm_weight[c]);
  *           dsv4/_archive/layers/mhc.py, module constants (EPS_RMSN = 1e-6).
+ *   [ROUTE] archived_plans/CORRECTNESS_BACKLOG.md, section 5 "Router",
+ *           "Dense Router" (expert scores sqrt(softplus(X @ W_gate)) plus
+ *           e_bias, then top-k selection); commit 107d62d,
+ *           single_shot_inference.py, commit message on the router gate's
+ *           global scales (the epilogue applies gsa * gsb to the logit
+ *           before sqrt(softplus)).
  *
  * Where the pages are silent, each function below states the reading it
  * takes.
@@ -324,5 +330,55 @@ void oracle_rmsnorm(const void *x, int x_dtype, const void *w, int w_dtype, doub
             for (int64_t k = 0; k < K; ++k)
                 y[m * K + k] = (double)load_elem(x, x_dtype, m * K + k) * r *
                                (double)load_elem(w, w_dtype, k);
+    }
+}
+
+/* Router scores [ROUTE], in binary64: for each logit z (the linear's output,
+ * gsa * gsb already applied), s = sqrt(softplus(z)) with
+ * softplus(z) = log(1 + exp(z)) written as max(z, 0) + log1p(exp(-|z|)),
+ * which is the same function without overflow for large |z|. */
+void oracle_router_scores(const double *logits, int64_t n, double *s)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double z = logits[i];
+        double sp = (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));
+        s[i] = sqrt(sp);
+    }
+}
+
+/* Top-k routing [ROUTE]: per row of logits (M, N), v_j = s_j + bias_j
+ * (bias may be NULL: zero), and the k experts of largest v are chosen, best
+ * first.  The pages do not order equal values; the reading taken is the
+ * lower expert index first.  The bias only steers the choice: score[r] is
+ * s (without the bias) of the r-th chosen expert (the pages do not say what
+ * the selection writes besides the experts; the bias is a per-expert
+ * correction of the choice).  Plain selection: k passes over the row. */
+void oracle_router_topk(const double *logits, const double *bias, int64_t M, int64_t N, int k,
+                        int32_t *idx, double *score)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const double *z = logits + m * N;
+        for (int r = 0; r < k; ++r) {
+            int64_t best = -1;
+            double best_v = 0.0, best_s = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                int taken = 0;
+                for (int q = 0; q < r; ++q)
+                    if (idx[m * k + q] == (int32_t)j)
+                        taken = 1;
+                if (taken)
+                    continue;
+                double sj;
+                oracle_router_scores(&z[j], 1, &sj);
+                double vj = sj + (bias ? bias[j] : 0.0);
+                if (best < 0 || vj > best_v) {  /* strict: the lower index keeps a tie */
+                    best = j;
+                    best_v = vj;
+                    best_s = sj;
+                }
+            }
+            idx[m * k + r] = (int32_t)best;
+            score[m * k + r] = best_s;
+        }
     }
 }

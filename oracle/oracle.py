@@ -67,6 +67,10 @@ def _load():
     lib.oracle_rmsnorm.restype = None
     lib.oracle_rmsnorm.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_double, I64, I64,
                                    P, P]
+    lib.oracle_router_scores.restype = None
+    lib.oracle_router_scores.argtypes = [P, I64, P]
+    lib.oracle_router_topk.restype = None
+    lib.oracle_router_topk.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
     lib.oracle_swiglu_deinterleave.restype = None
     lib.oracle_swiglu_deinterleave.argtypes = [P, I64, I64, ctypes.c_int, P]
     _lib = lib
@@ -242,3 +246,28 @@ def swiglu_deinterleave(l1: np.ndarray, granularity: int = 8) -> np.ndarray:
     h = np.empty((M, NI // 2), np.float64)
     _load().oracle_swiglu_deinterleave(_ptr(l1), M, NI, granularity, _ptr(h))
     return h
+
+
+def router_scores(logits: np.ndarray) -> np.ndarray:
+    """sqrt(softplus(z)) of every logit, float64 (nvfp4_oracle.c,
+    oracle_router_scores)."""
+    z = np.ascontiguousarray(logits, dtype=np.float64)
+    s = np.empty_like(z)
+    _load().oracle_router_scores(_ptr(z), z.size, _ptr(s))
+    return s
+
+
+def router_topk(logits: np.ndarray, bias, k: int):
+    """Top-k experts of each row of logits (M, N) by sqrt(softplus(z)) + bias:
+    idx (M, k) int32 best first (lower index on ties) and their scores
+    sqrt(softplus(z)) (M, k) float64, bias excluded (nvfp4_oracle.c,
+    oracle_router_topk)."""
+    z = np.ascontiguousarray(logits, dtype=np.float64)
+    M, N = z.shape
+    assert 1 <= k <= N
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    idx = np.zeros((M, k), np.int32)
+    sc = np.zeros((M, k), np.float64)
+    _load().oracle_router_topk(_ptr(z), None if b is None else _ptr(b), M, N, k, _ptr(idx),
+                               _ptr(sc))
+    return idx, sc

@@ -459,3 +459,88 @@ def test_linear_rows_is_the_linear_of_each_row_with_its_scale():
     g = np.float32(2.0) ** rng.integers(-6, 6, M).astype(np.float32)
     y = oracle.linear_rows(ac, asf, g, wc, wsf, np.float32(0.5))
     assert np.allclose(y, base * (g / g0)[:, None], rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------- router
+def test_router_score_closed_forms():
+    """sqrt(softplus(z)): s(0) = sqrt(ln 2); softplus(z) - softplus(-z) = z
+    (catches a dropped sqrt or a flipped sign); softplus(z) ~ exp(z) far
+    below 0 and = z far above (catches log(1 + exp(z)) losing the tail or
+    overflowing)."""
+    assert oracle.router_scores(np.array([0.0]))[0] == pytest.approx(math.sqrt(math.log(2.0)),
+                                                                     rel=1e-15)
+    z = np.linspace(-30.0, 30.0, 241)
+    sp, sn = oracle.router_scores(z), oracle.router_scores(-z)
+    assert np.allclose(sp ** 2 - sn ** 2, z, rtol=0, atol=1e-12)
+    for t in [-40.0, -100.0, -700.0]:
+        assert oracle.router_scores(np.array([t]))[0] ** 2 / math.exp(t) == pytest.approx(1.0,
+                                                                                        rel=1e-12)
+    assert oracle.router_scores(np.array([800.0]))[0] == pytest.approx(math.sqrt(800.0), rel=1e-15)
+    # against the library's softplus, log(exp(0) + exp(z))
+    zz = np.random.default_rng(5).standard_normal(1000) * 8
+    assert np.allclose(oracle.router_scores(zz), np.sqrt(np.logaddexp(0.0, zz)), rtol=1e-14,
+                       atol=0)
+
+
+def test_router_topk_matches_a_stable_sort():
+    """Top-k by s + bias, best first, the lower expert first among equal
+    values: the first k of numpy's lexsort on (index, -value)."""
+    rng = np.random.default_rng(8)
+    M, N = 40, 96
+    z = rng.integers(-6, 7, (M, N)) * 0.5          # many equal logits
+    bias = rng.integers(-2, 3, N) * 0.25
+    for b in [None, bias]:
+        v = oracle.router_scores(z) + (0.0 if b is None else b)
+        for k in [1, 6, 8, N]:
+            idx, sc = oracle.router_topk(z, b, k)
+            for m in range(M):
+                ref = np.lexsort((np.arange(N), -v[m]))[:k]
+                assert np.array_equal(idx[m], ref)
+                assert np.array_equal(sc[m], oracle.router_scores(z[m, ref]))
+    idx, _ = oracle.router_topk(z, bias, N)
+    assert all(sorted(r) == list(range(N)) for r in idx)
+
+
+def test_router_bias_steers_the_choice_only():
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((3, 64))
+    bias = np.zeros(64)
+    forced = [40, 3, 17]
+    bias[forced] = 100.0
+    idx, sc = oracle.router_topk(z, bias, 5)
+    s = oracle.router_scores(z)
+    for m in range(3):
+        head = sorted(forced, key=lambda j: (-s[m, j], j))
+        assert list(idx[m, :3]) == head
+        rest = [j for j in np.lexsort((np.arange(64), -s[m])) if j not in forced][:2]
+        assert list(idx[m, 3:]) == rest
+        assert np.array_equal(sc[m], s[m, idx[m]])      # scores carry no bias
+
+
+def test_router_integer_case_reduces_to_library_routines():
+    """Scales 1.0 and gsa = gsb = 2^-4: the logits are an integer matmul of
+    the decoded codes divided by 256, exact in binary64; the scores are
+    sqrt(logaddexp(0, z)) and the choice is a stable sort."""
+    rng = np.random.default_rng(10)
+    M, N, K, k = 6, 48, 128, 6
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    one = np.full((M, K // 16), 0x38, np.uint8)
+    onew = np.full((N, K // 16), 0x38, np.uint8)
+    g = np.float32(2.0 ** -4)
+    z = oracle.linear(ac, one, g, wc, onew, g)
+    lut2 = np.array([0, 1, 2, 3, 4, 6, 8, 12], np.int64)    # 2 * E2M1 magnitude
+
+    def dec2(c):
+        lo, hi = c & 15, c >> 4
+        nib = np.stack([lo, hi], axis=-1).reshape(c.shape[0], -1)
+        return np.where(nib & 8, -1, 1) * lut2[nib & 7]
+
+    zi = dec2(ac) @ dec2(wc).T                                  # 4 * sum of products
+    assert np.array_equal(z, zi / 4.0 / 256.0)
+    idx, sc = oracle.router_topk(z, None, k)
+    s = np.sqrt(np.logaddexp(0.0, z))
+    for m in range(M):
+        ref = np.lexsort((np.arange(N), -s[m]))[:k]
+        assert np.array_equal(idx[m], ref)
+        assert np.allclose(sc[m], s[m, ref], rtol=1e-14, atol=0)
