@@ -165,7 +165,7 @@ class LinearBench:
 
     def linear(self, i):
         wc, wsf = self.w[i % self.ncopies]
-        self.C.nvfp4_linear(self.codes, self.scales, self.gsa, wc, wsf, self.ws2, self.y)
+        self.C.nvfp4_linear(self.codes, self.scales, self.gsa, wc, wsf, self.ws2, self.y, self.ws)
 
     def step3(self, i):  # the three ABI calls
         self.quantize()
@@ -218,6 +218,48 @@ def bench_moe(C, dev, steps, warmup):
             "step_GBps": wbytes / (us * 1e-6) / 1e9,
             "step_frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "step_TFLOPs": flops / (us * 1e-6) / 1e12}
+
+
+def bench_router(C, name, dev, steps, warmup):
+    """The dense router on an already quantized activation: gate linear and
+    expert choice (nvfp4_router_topk), gate weights rotated."""
+    from moe_amax_gsa_amd import workloads as W
+    r = W.make(name)
+    M, K, N, k = r.M, r.K, r.N, r.topk
+    w = W.bf16_to_torch(r.w, dev)
+    wc = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+    wsf = torch.empty(N, K // 16, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(1, dtype=torch.float32, device=dev)
+    qws = torch.empty(max(16, C.nvfp4_workspace_bytes(C.OP_QUANTIZE_WEIGHT, 0, N, K)),
+                      dtype=torch.uint8, device=dev)
+    C.nvfp4_quantize_weight(w, ws2, wc, wsf, qws)
+    wbytes = N * K // 2 + N * K // 16
+    ncopies = max(1, min(512, -(-ROTATE_BYTES // wbytes)))
+    ws_ = [(wc, wsf)] + [(wc.clone(), wsf.clone()) for _ in range(ncopies - 1)]
+    x = W.bf16_to_torch(r.x, dev)
+    gsa = torch.empty(1, dtype=torch.float32, device=dev)
+    aws = torch.empty(max(16, C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, M * K)), dtype=torch.uint8,
+                      device=dev)
+    C.nvfp4_amax_gsa(x, gsa, aws)
+    codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
+    C.nvfp4_quantize_from_buffer(x, gsa, codes, scales)
+    bias = torch.from_numpy(r.bias).to(dev)
+    idx = torch.empty(M, k, dtype=torch.int32, device=dev)
+    sc = torch.empty(M, k, dtype=torch.float32, device=dev)
+    rws = torch.empty(max(16, C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, M, N, K)),
+                      dtype=torch.uint8, device=dev)
+
+    def step(i):
+        c, s_ = ws_[i % ncopies]
+        C.nvfp4_router_topk(codes, scales, gsa, c, s_, ws2, bias, idx, sc, rws)
+
+    us = 1e3 * graph_ms_per_step(step, steps, warmup)
+    # weights + quantized activation + bias + logits written and read + choice
+    nbytes = wbytes + M * K * 9 // 16 + N * 4 + M * N * 8 + M * k * 8
+    return {"step_us": us, "rotated_weight_copies": ncopies, "bytes_per_step": nbytes,
+            "step_GBps": nbytes / (us * 1e-6) / 1e9,
+            "step_frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
 # ------------------------------------------------------------------ oracle
@@ -288,6 +330,11 @@ def main():
             log("workload", name)
             workloads[name] = bench_linear(C, name, dev, steps, min(args.warmup, 10),
                                            min(kiters, steps))[2]
+        for name in ["router_m1_k7168_e384_top6", "router_m64_k7168_e384_top6"]:
+            if args.only and args.only != name:
+                continue
+            log("workload", name)
+            workloads[name] = bench_router(C, name, dev, args.steps, min(args.warmup, 10))
         if not args.only or args.only == "moe_t64_e256_top8":
             log("workload moe_t64_e256_top8")
             workloads["moe_t64_e256_top8"] = bench_moe(C, dev, max(10, args.steps // 10),

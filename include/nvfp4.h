@@ -90,13 +90,15 @@ extern "C" {
 #define NVFP4_OP_GROUPED_SWIGLU 5
 #define NVFP4_OP_QUANTIZE_WEIGHT 6
 #define NVFP4_OP_RMSNORM_QUANTIZE 7
+#define NVFP4_OP_ROUTER_TOPK 8
 
 /* Bytes of workspace an operation needs for the given sizes (0 if none).
  * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored;
  * for NVFP4_OP_LINEAR_RUN, the activation is (M, K); for
  * NVFP4_OP_GROUPED_SWIGLU, N is N_inter and G the group count; for
  * NVFP4_OP_QUANTIZE_WEIGHT, the weight is (N, K); for
- * NVFP4_OP_RMSNORM_QUANTIZE, the activation is (M, K). */
+ * NVFP4_OP_RMSNORM_QUANTIZE, the activation is (M, K); for
+ * NVFP4_OP_ROUTER_TOPK, M rows and N experts. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
 
 /* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
@@ -161,8 +163,16 @@ int nvfp4_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, floa
  * 8-byte aligned.  M <= 16 runs a weight-streaming kernel on FP4 matrix
  * cores; larger M runs a tiled kernel that dequantizes both operands
  * exactly to f16 (every E2M1 x E4M3 product fits) and accumulates on f16
- * matrix cores in FP32.  M == 0 or N == 0 is a no-op.  ws is unused (may be
- * NULL). */
+ * matrix cores in FP32.  M == 0 or N == 0 is a no-op.
+ * ws is optional.  With few output tiles (a 128 x 64 tile each; at most
+ * half as many tiles as the device has compute units) and K a multiple of
+ * 256 the tiled kernel can split K across workgroups: each split writes its
+ * fp32 partial sums into ws and a second kernel adds them in split order
+ * (deterministic) and applies the epilogue.  That needs
+ * nvfp4_workspace_bytes(NVFP4_OP_LINEAR, M, N, K, 0) bytes (0 when the
+ * shape does not split on the current device), 16-byte aligned; with a
+ * NULL or smaller ws the kernel runs unsplit, with the same results up to
+ * the fp32 summation order. */
 int nvfp4_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa,
                  const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
                  void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *ws,
@@ -172,12 +182,42 @@ int nvfp4_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *g
  * of the pages' run_from_quantized): as nvfp4_linear, but gsa_rows is a
  * device float32[M] and y[m] = gsa_rows[m] * ws2 * dequant(A[m]) @
  * dequant(W)^T -- the product nvfp4_rmsnorm_quantize(..., gsa_per_row = 1)
- * feeds.  Same kernels, same checks and alignment as nvfp4_linear; the
- * epilogue multiplies by gsa_rows[m] * ws2 in float32.  M == 0 or N == 0 is
- * a no-op. */
+ * feeds.  Same kernels, checks, alignment and optional split-K workspace
+ * as nvfp4_linear; the epilogue multiplies by gsa_rows[m] * ws2 in
+ * float32.  M == 0 or N == 0 is a no-op. */
 int nvfp4_linear_rows(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa_rows,
                       const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
-                      void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *stream);
+                      void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* The dense router's gate projection and expert choice (the pages'
+ * "Dense Router": sqrt(softplus(X @ W_gate)) + e_bias and top-k selection,
+ * archived_plans/CORRECTNESS_BACKLOG.md section 5; the gsa * gsb factor on
+ * the logit before sqrt(softplus) from the router gate commit message of
+ * single_shot_inference.py, commit 107d62d; shipped there as the NVFP4 GEMM
+ * followed by an activation + top-k kernel).
+ *   logit[m, j] = gsa * ws2 * dequant(A[m]) . dequant(W[j])   (step 3; W is
+ *                 the gate weight, one row per expert, e.g. quantized at
+ *                 load time by nvfp4_quantize_weight)
+ *   s[m, j]     = sqrt(softplus(logit[m, j])),  softplus(z) = log(1 + e^z)
+ *   v[m, j]     = s[m, j] + bias[j]             (bias (N,) fp32, or NULL: 0)
+ * topk_idx (M, topk) int32 receives the topk experts of largest v, best
+ * first, the lower expert index first among equal v; topk_score (M, topk)
+ * fp32 receives their s (the bias steers the choice only).  The scores are
+ * float32: softplus and sqrt from the device math library (a few ulp).
+ * N <= 1024 experts; 1 <= topk <= min(N, 64); other checks as nvfp4_linear.
+ * ws: nvfp4_workspace_bytes(NVFP4_OP_ROUTER_TOPK, M, N, K, 0) bytes,
+ * 16-byte aligned (at least M * N * 4: the logits; what follows them, rounded
+ * up to 16 bytes, serves the linear's split K); on return it starts with the
+ * fp32 logits (M, N) row-major.
+ * Two kernels: the linear of nvfp4_linear, whose epilogue writes the logits
+ * into ws, then one wave per row for the activation, bias and choice.
+ * M == 0 is a no-op. */
+int nvfp4_router_topk(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa,
+                      const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
+                      const float *bias, int64_t M, int64_t N, int64_t K, int topk,
+                      int32_t *topk_idx, float *topk_score, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* The whole layer on a bf16/fp32 activation, as Nvfp4Linear.run does
  * (dsv4/_archive/layers/linear.py, _run_impl): steps 1, 2 and 3 with the
@@ -194,7 +234,8 @@ int nvfp4_linear_rows(const uint8_t *a_codes, const uint8_t *a_scales, const flo
  * another), quantizes it into LDS and streams its weight rows; workgroup 0
  * also writes gsa, codes and scales.  Otherwise the separate kernels run in
  * order (then ws must hold nvfp4_workspace_bytes(NVFP4_OP_LINEAR_RUN, M, N,
- * K, 1) bytes).
+ * K, 1) bytes: the amax partials, and after them the optional split K of
+ * nvfp4_linear).
  * N == 0 only quantizes. */
 int nvfp4_linear_run(const void *x, int x_dtype, float *gsa, uint8_t *codes, uint8_t *scales,
                      const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2, void *y,

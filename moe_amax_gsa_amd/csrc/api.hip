@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 3; }
+NVFP4_API int nvfp4_abi_version(void) { return 4; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -47,15 +47,30 @@ NVFP4_API const char* nvfp4_status_string(int status) {
   }
 }
 
+// split-K partials of the tiled kernel (shapes with few output tiles)
+static size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  return (M > GEMV_MAX_M && N > 0 && K > 0) ? gemm_ws_bytes(M, N, K) : 0;
+}
+
+static size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
+
 NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G) {
   (void)N;
   (void)K;
   (void)G;
   switch (op) {
     case NVFP4_OP_AMAX_GSA: return M > 0 ? amax_ws_bytes(M) : 0;
-    case NVFP4_OP_LINEAR_RUN: return (M > 0 && K > 0) ? amax_ws_bytes(M * K) : 0;
+    case NVFP4_OP_LINEAR: return linear_ws_bytes(M, N, K);
+    case NVFP4_OP_LINEAR_RUN: {
+      const size_t a = (M > 0 && K > 0) ? amax_ws_bytes(M * K) : 0;
+      const size_t l = linear_ws_bytes(M, N, K);
+      return a > l ? a : l;
+    }
     case NVFP4_OP_QUANTIZE_WEIGHT: return (N > 0 && K > 0) ? amax_ws_bytes(N * K) : 0;
     case NVFP4_OP_RMSNORM_QUANTIZE: return M > 0 ? (size_t)M * sizeof(uint32_t) : 0;
+    case NVFP4_OP_ROUTER_TOPK:
+      return (M > 0 && N > 0) ? round16((size_t)M * N * sizeof(float)) + linear_ws_bytes(M, N, K)
+                              : 0;
     case NVFP4_OP_GROUPED_SWIGLU:
       return (N > 0 && G > 0) ? (size_t)grouped_swiglu_parts(N, G) * sizeof(uint32_t) : 0;
     default: return 0;
@@ -142,8 +157,8 @@ NVFP4_API int nvfp4_quantize_weight(const void* w, int w_dtype, int64_t N, int64
 
 static int linear_impl(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
-                       int y_dtype, int64_t M, int64_t N, int64_t K, bool gsa_rows,
-                       void* stream) {
+                       int y_dtype, int64_t M, int64_t N, int64_t K, bool gsa_rows, void* ws,
+                       size_t ws_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   int st = check_gemm_shape(M, N, K);
   if (st != NVFP4_OK) return st;
@@ -157,26 +172,62 @@ static int linear_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   if (M <= GEMV_MAX_M)
     return launched(
         launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s, gsa_rows));
-  return launched(
-      launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s, gsa_rows));
+  return launched(launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s,
+                              gsa_rows, ws, ws_bytes));
 }
 
 NVFP4_API int nvfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* ws,
                            size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   return linear_impl(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_dtype, M, N, K, false,
-                     stream);
+                     ws, ws_bytes, stream);
 }
 
 NVFP4_API int nvfp4_linear_rows(const uint8_t* a_codes, const uint8_t* a_scales,
                                 const float* gsa_rows, const uint8_t* w_codes,
                                 const uint8_t* w_scales, const float* ws2, void* y, int y_dtype,
-                                int64_t M, int64_t N, int64_t K, void* stream) {
+                                int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                                void* stream) {
   return linear_impl(a_codes, a_scales, gsa_rows, w_codes, w_scales, ws2, y, y_dtype, M, N, K,
-                     true, stream);
+                     true, ws, ws_bytes, stream);
+}
+
+NVFP4_API int nvfp4_router_topk(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const float* gsa, const uint8_t* w_codes, const uint8_t* w_scales,
+                                const float* ws2, const float* bias, int64_t M, int64_t N,
+                                int64_t K, int topk, int32_t* topk_idx, float* topk_score,
+                                void* ws, size_t ws_bytes, void* stream) {
+  int st = check_gemm_shape(M, N, K);
+  if (st != NVFP4_OK) return st;
+  if (N < 1 || N > ROUTER_MAX_N || topk < 1 || topk > N || topk > ROUTER_MAX_K)
+    return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !gsa || !w_codes || !w_scales || !ws2 || !topk_idx ||
+      !topk_score)
+    return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 8) || !aligned(w_codes, 8) || !aligned(gsa, 4) || !aligned(ws2, 4) ||
+      !aligned(topk_idx, 4) || !aligned(topk_score, 4) || (bias && !aligned(bias, 4)))
+    return NVFP4_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < (size_t)M * N * sizeof(float)) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+  float* logits = (float*)ws;
+  // the bytes after the logits, if any, take the linear's split-K partials
+  const size_t lbytes = round16((size_t)M * N * sizeof(float));
+  void* lws = ws_bytes > lbytes ? (void*)((uint8_t*)ws + lbytes) : nullptr;
+  const size_t lws_bytes = ws_bytes > lbytes ? ws_bytes - lbytes : 0;
+  hipStream_t s = (hipStream_t)stream;
+  // a split-K gate linear leaves its partials after the logits: the choice
+  // kernel adds and scales them (and writes the logits) itself
+  int nsplit = 0;
+  const hipError_t e =
+      M <= GEMV_MAX_M
+          ? launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, logits, false, M, N, K, s)
+          : launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, logits, false, M, N, K, s,
+                        false, lws, lws_bytes, &nsplit);
+  if (e != hipSuccess) return launched(e);
+  return launched(launch_router_topk(nsplit ? (const float*)lws : logits, nsplit, gsa, ws2,
+                                     logits, bias, M, N, topk, topk_idx, topk_score, s));
 }
 
 NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* codes,
@@ -212,8 +263,9 @@ NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* 
   if (e == hipSuccess && N > 0) {
     if (M <= GEMV_MAX_M)
       e = launch_gemv(codes, scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s);
-    else
-      e = launch_gemm(codes, scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s);
+    else  // the amax partials are consumed by now: the workspace takes the split K
+      e = launch_gemm(codes, scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s, false, ws,
+                      ws_bytes);
   }
   return launched(e);
 }

@@ -192,12 +192,12 @@ struct LdsTile {
   static_assert(KW * 16 * (TN + 4) * 4 <= LDS_BYTES, "reduction slabs fit in the stages");
 };
 
-template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE>
+template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE, bool SPLIT>
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
-    int y_bf16, int M, int N, int K, int gsa_rows) {
+    int y_bf16, int M, int N, int K, int gsa_rows, int cps, float* __restrict__ part) {
   using T = LdsTile<WM, WN, STAGES, KW>;
   constexpr int TM = T::TM, TN = T::TN, LDT = TN + 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -207,7 +207,9 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const uint32_t cbytes = (uint32_t)K / 2, sbytes = (uint32_t)K / 16;
-  const int nch = K / T::CHUNK;
+  // split z of the K range: chunks c0 .. c0 + nch - 1 (cps per split)
+  const int c0 = SPLIT ? (int)blockIdx.z * cps : 0;
+  const int nch = SPLIT ? min(K / T::CHUNK - c0, cps) : K / T::CHUNK;
 
   // code load i of wave w fills LDS rows RPL (KW i + w) .. + RPL-1: lane l
   // the row RPL (KW i + w) + l / PPR, slot l % PPR, which holds piece
@@ -221,12 +223,14 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
       csrc[i] = (uint32_t)min(m0 + row, M - 1) * cbytes + piece * 16;  // clamped: discarded
     else
       csrc[i] = (uint32_t)min(n0 + row - TM, N - 1) * cbytes + piece * 16;
+    csrc[i] += (uint32_t)c0 * T::CB;
   }
   // scale load of wave w < SCALE_LOADS: rows SRL w + l / (SB/16), piece l % (SB/16)
   const int srow = T::SRL * min(wave, T::SCALE_LOADS - 1) + lane / (T::SB / 16);
   const uint32_t spiece = (uint32_t)(lane % (T::SB / 16)) * 16;
   const uint32_t ssrc = (srow < TM ? (uint32_t)min(m0 + srow, M - 1) * sbytes
-                                   : (uint32_t)min(n0 + srow - TM, N - 1) * sbytes) + spiece;
+                                   : (uint32_t)min(n0 + srow - TM, N - 1) * sbytes) + spiece +
+                        (uint32_t)c0 * T::SB;
 
   // code loads 0 .. NA-1 read A rows, the rest W rows; load i fills LDS at
   // stage + 1024 (KW i + wave)
@@ -462,7 +466,9 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
         for (int w = 1; w < KW; ++w) v += red[(w * 16 + rr) * LDT + cc];
         const int row = m0 + a * 32 + q * 16 + rr, col = n0 + cc;
-        if (row < M && col < N) {
+        if (SPLIT) {  // the raw partial sum of this split
+          if (row < M && col < N) part[((int64_t)blockIdx.z * M + row) * N + col] = v;
+        } else if (row < M && col < N) {
           const float o = v * (gsa_rows ? gsa_p[row] * ws2_p[0] : gscale);
           if (y_bf16)
             ((uint16_t*)y)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(o);
@@ -475,21 +481,68 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
+// Sum of the split-K partials in split order (deterministic), times the
+// epilogue scale: one output per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int64_t MN, int N,
+                                                            const float* __restrict__ gsa_p,
+                                                            const float* __restrict__ ws2_p,
+                                                            int gsa_rows, void* __restrict__ y,
+                                                            int y_bf16) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= MN) return;
+  // every split's load in flight at once, then the sum in split order
+  float p[GEMM_MAX_SPLITS];
+#pragma unroll
+  for (int z = 0; z < GEMM_MAX_SPLITS; ++z) p[z] = z < splits ? part[(int64_t)z * MN + e] : 0.0f;
+  float v = p[0];
+#pragma unroll
+  for (int z = 1; z < GEMM_MAX_SPLITS; ++z)
+    if (z < splits) v += p[z];
+  const float sc = (gsa_rows ? gsa_p[e / N] : gsa_p[0]) * ws2_p[0];
+  const float o = v * sc;
+  if (y_bf16)
+    ((uint16_t*)y)[e] = (uint16_t)f32_to_bf16_rne(o);
+  else
+    ((float*)y)[e] = o;
+}
+
 template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE = false>
 hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                      bool gsa_rows = false) {
+                      bool gsa_rows = false, int splits = 1, float* part = nullptr,
+                      bool reduce = true) {
   using T = LdsTile<WM, WN, STAGES, KW>;
   static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+  const int nch = (int)(K / T::CHUNK);
+  const int cps = (nch + splits - 1) / splits;
+  splits = (nch + cps - 1) / cps;  // every split has at least one chunk
+  const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM),
+                  (unsigned)splits);
+  if (splits == 1 || part == nullptr) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, false>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, false>
+        <<<dim3(grid.x, grid.y), T::THREADS, T::LDS_BYTES, s>>>(
+            a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N,
+            (int)K, gsa_rows ? 1 : 0, nch, nullptr);
+    return hipGetLastError();
+  }
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE>,
+      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, true>,
       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM));
-  gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
+  gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, true><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
       a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K,
-      gsa_rows ? 1 : 0);
+      gsa_rows ? 1 : 0, cps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !reduce) return e;
+  const int64_t MN = M * N;
+  splitk_reduce_kernel<<<(unsigned)((MN + 255) / 256), 256, 0, s>>>(
+      part, splits, MN, (int)N, gsa, ws2, gsa_rows ? 1 : 0, y, y_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -508,15 +561,53 @@ static int cu_count() {
   return cached[dev];
 }
 
-hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
-                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
-                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                       bool gsa_rows) {
+// Split-K plan for the staged kernel: with few output tiles (at most half a
+// tile per CU) the K range is cut into up to 16 splits so that the grid
+// covers the chip.  Returns the split count (1: none).
+static int gemm_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((N + 63) / 64) * ((M + 127) / 128);
+  const int64_t nch = K / 256;
+  if (2 * tiles > cu_count() || nch < 2) return 1;
+  int64_t sp = (2 * cu_count()) / tiles;
+  sp = sp < GEMM_MAX_SPLITS ? sp : GEMM_MAX_SPLITS;
+  sp = sp < nch ? sp : nch;
+  const int64_t cps = (nch + sp - 1) / sp;
+  return (int)((nch + cps - 1) / cps);
+}
+
+static bool gemm_staged_ok(const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t M, int64_t N,
+                           int64_t K) {
   const bool fast = (K % 64 == 0) && (((uintptr_t)a_codes | (uintptr_t)w_codes) & 15u) == 0 &&
                     (((uintptr_t)a_scales | (uintptr_t)w_scales) & 1u) == 0;
   // the staged kernel takes whole 256-element chunks and 32-bit row offsets
-  const bool big = fast && K % 256 == 0 && K >= 256 && M * (K / 2) < (1ll << 31) && N * (K / 2) < (1ll << 31);
+  return fast && K % 256 == 0 && K >= 256 && M * (K / 2) < (1ll << 31) &&
+         N * (K / 2) < (1ll << 31);
+}
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K % 256 != 0 || K < 256) return 0;
+  const int sp = gemm_splits(M, N, K);
+  return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                       void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                       bool gsa_rows, void* ws, size_t ws_bytes, int* partial_splits) {
+  if (partial_splits) *partial_splits = 0;
+  const bool fast = (K % 64 == 0) && (((uintptr_t)a_codes | (uintptr_t)w_codes) & 15u) == 0 &&
+                    (((uintptr_t)a_scales | (uintptr_t)w_scales) & 1u) == 0;
+  const bool big = gemm_staged_ok(a_codes, a_scales, w_codes, w_scales, M, N, K);
   if (big) {
+    const int sp = gemm_splits(M, N, K);
+    if (sp > 1 && ws != nullptr && ((uintptr_t)ws & 15u) == 0 &&
+        ws_bytes >= (size_t)sp * M * N * sizeof(float)) {
+      if (partial_splits) *partial_splits = sp;  // the caller adds the partials
+      return launch_lds<4, 2, 2, 2, 4>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16,
+                                       M, N, K, s, gsa_rows, sp, (float*)ws,
+                                       partial_splits == nullptr);
+    }
     // 128 x 64 tiles.  At most one tile per CU: eight waves split each
     // 512-element chunk (two waves per SIMD) and the next chunk's fragment
     // reads and first dequantization run under the current chunk's last

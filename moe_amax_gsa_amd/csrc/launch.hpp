@@ -34,6 +34,18 @@ hipError_t launch_rmsnorm_quantize(const void* x, bool x_bf16, const void* w, bo
                                    float* inv_rms, uint8_t* codes, uint8_t* scales,
                                    uint32_t* partials, hipStream_t s);
 
+// Router expert choice on fp32 logits (M, N), N <= ROUTER_MAX_N,
+// 1 <= k <= min(N, ROUTER_MAX_K):
+// idx (M, k) and score (M, k) = sqrt(softplus(logit)) of the chosen experts.
+constexpr int64_t ROUTER_MAX_N = 1024;
+constexpr int ROUTER_MAX_K = 64;
+// The logits are src (nsrc == 0), or the sum of nsrc split-K partials
+// (split z at src + z * M * N) times gsa[0] * ws2[0], then also written to
+// logits.
+hipError_t launch_router_topk(const float* src, int nsrc, const float* gsa, const float* ws2,
+                              float* logits, const float* bias, int64_t M, int64_t N, int k,
+                              int32_t* idx, float* score, hipStream_t s);
+
 // Phase 2 of an amax over partials (bits of non-negative fp32 maxima): gsa.
 hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float* gsa,
                                 hipStream_t s);
@@ -90,9 +102,18 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
                              int64_t K, hipStream_t s);
 
 // Tiled GEMM for many rows (dequantize to f16, f16 matrix cores).
+// Workspace for split K (fp32 partials) when the shape has few output tiles
+// on the current device; 0 when it does not split.  Without it (ws NULL or
+// smaller) launch_gemm runs unsplit.  With partial_splits, a split launch
+// leaves its raw partial sums (split z at ws + z * M * N floats) for the
+// caller to add and scale, and reports the split count there (0: y was
+// written).
+constexpr int GEMM_MAX_SPLITS = 16;
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
                        void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                       bool gsa_rows = false);
+                       bool gsa_rows = false, void* ws = nullptr, size_t ws_bytes = 0,
+                       int* partial_splits = nullptr);
 
 }  // namespace nvfp4

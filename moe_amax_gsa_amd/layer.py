@@ -22,6 +22,13 @@ import torch
 from . import nvfp4 as C
 
 
+def _max_ws(op: int, max_rows: int, N: int, K: int) -> int:
+    """Workspace for any row count up to max_rows: within a block of 128 rows
+    the split-K partials grow with the rows, so the block ends bound it."""
+    ms = sorted({min(128 * j, max_rows) for j in range(1, (max_rows + 127) // 128 + 1)})
+    return max(C.nvfp4_workspace_bytes(op, m, N, K) for m in ms)
+
+
 def _f32_scalar(v, device) -> torch.Tensor:
     if isinstance(v, torch.Tensor):
         return v.to(device=device, dtype=torch.float32).reshape(1).contiguous()
@@ -42,8 +49,10 @@ class Nvfp4Linear:
         self.max_tokens = max_tokens
         dev = self.device
         self.gsa = torch.zeros(1, dtype=torch.float32, device=dev)
+        # the largest row count needs the most split-K partials: size for it
         nws = max(C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, max_tokens, self.N, self.K),
                   C.nvfp4_workspace_bytes(C.OP_RMSNORM_QUANTIZE, max_tokens, 0, self.K))
+        nws = max(nws, _max_ws(C.OP_LINEAR, max_tokens, self.N, self.K))
         self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
         self.gsa_rows = torch.zeros(max_tokens, dtype=torch.float32, device=dev)
         self.inv_rms = torch.zeros(max_tokens, dtype=torch.float32, device=dev)
@@ -81,9 +90,9 @@ class Nvfp4Linear:
         if gsa_per_row:
             assert gsa.numel() >= M
             C.nvfp4_linear_rows(codes, scales, gsa, self.w_codes, self.w_scales, self.ws2, y,
-                                stream)
+                                self.ws, stream)
         else:
-            C.nvfp4_linear(codes, scales, gsa, self.w_codes, self.w_scales, self.ws2, y, None,
+            C.nvfp4_linear(codes, scales, gsa, self.w_codes, self.w_scales, self.ws2, y, self.ws,
                            stream)
         return y
 
@@ -113,6 +122,45 @@ class Nvfp4Linear:
         C.nvfp4_linear_run(x, self.gsa, self.codes[:M], self.scales[:M], self.w_codes,
                            self.w_scales, self.ws2, y, self.ws, stream)
         return y
+
+    __call__ = forward
+
+
+class Nvfp4Router:
+    """The dense router: (idx, score) = Nvfp4Router(x) for x (M, K) bf16/fp32.
+
+    The gate projection is an NVFP4 linear against the gate weight (N
+    experts, quantized at load time when it comes as bf16); the expert
+    choice is the top k of sqrt(softplus(logit)) + bias (nvfp4_router_topk).
+    idx (M, k) int32, best first; score (M, k) fp32 = sqrt(softplus(logit)).
+    """
+
+    def __init__(self, gate: Nvfp4Linear, bias: Optional[torch.Tensor], topk: int):
+        self.gate, self.topk = gate, topk
+        dev = gate.device
+        self.bias = None if bias is None else bias.to(device=dev, dtype=torch.float32).contiguous()
+        M, N, K = gate.max_tokens, gate.N, gate.K
+        nws = max(16, _max_ws(C.OP_ROUTER_TOPK, M, N, K))
+        self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(M, topk, dtype=torch.int32, device=dev)
+        self.score = torch.empty(M, topk, dtype=torch.float32, device=dev)
+
+    @classmethod
+    def from_weight(cls, w_gate: torch.Tensor, bias: Optional[torch.Tensor], topk: int,
+                    max_tokens: int, stream=None) -> "Nvfp4Router":
+        return cls(Nvfp4Linear.from_weight(w_gate, max_tokens, stream=stream), bias, topk)
+
+    def route_quantized(self, codes, scales, gsa, stream=None):
+        M = codes.shape[0]
+        g = self.gate
+        C.nvfp4_router_topk(codes, scales, gsa, g.w_codes, g.w_scales, g.ws2, self.bias,
+                            self.idx[:M], self.score[:M], self.ws, stream)
+        return self.idx[:M], self.score[:M]
+
+    def forward(self, x: torch.Tensor, stream=None):
+        assert x.shape[0] <= self.gate.max_tokens and x.shape[1] == self.gate.K
+        codes, scales, gsa = self.gate.quantize(x, stream)
+        return self.route_quantized(codes, scales, gsa, stream)
 
     __call__ = forward
 

@@ -29,6 +29,7 @@ OP_LINEAR_RUN = 4
 OP_GROUPED_SWIGLU = 5
 OP_QUANTIZE_WEIGHT = 6
 OP_RMSNORM_QUANTIZE = 7
+OP_ROUTER_TOPK = 8
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_amax_gsa_amd.build`")
@@ -53,7 +54,10 @@ lib.nvfp4_quantize_from_buffer.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P]
 lib.nvfp4_linear.restype = _I
 lib.nvfp4_linear.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]
 lib.nvfp4_linear_rows.restype = _I
-lib.nvfp4_linear_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P]
+lib.nvfp4_linear_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_router_topk.restype = _I
+lib.nvfp4_router_topk.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P,
+                                  _SZ, _P]
 lib.nvfp4_linear_run.restype = _I
 lib.nvfp4_linear_run.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ,
                                  _P]
@@ -144,14 +148,32 @@ def nvfp4_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tenso
 
 def nvfp4_linear_rows(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa_rows: torch.Tensor,
                       w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
-                      y: torch.Tensor, stream=None) -> None:
+                      y: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None) -> None:
     """y[m] = gsa_rows[m] * ws2 * dequant(A[m]) @ dequant(W)^T; gsa_rows (M,)."""
     M = a_codes.shape[0]
     K = a_codes.shape[1] * 2
     N = w_codes.shape[0]
     _check(lib.nvfp4_linear_rows(_ptr(a_codes), _ptr(a_scales), _ptr(gsa_rows), _ptr(w_codes),
                                  _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y), M, N, K,
+                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                  _stream(stream)), "nvfp4_linear_rows")
+
+
+def nvfp4_router_topk(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,
+                      w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
+                      bias: Optional[torch.Tensor], topk_idx: torch.Tensor,
+                      topk_score: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """Gate logits of A (M, K) against W (N, K), then the top k experts of
+    sqrt(softplus(logit)) + bias: topk_idx (M, k) int32, topk_score (M, k)."""
+    M = a_codes.shape[0]
+    K = a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    k = topk_idx.shape[1]
+    _check(lib.nvfp4_router_topk(_ptr(a_codes), _ptr(a_scales), _ptr(gsa), _ptr(w_codes),
+                                 _ptr(w_scales), _ptr(ws2), _ptr(bias), M, N, K, k,
+                                 _ptr(topk_idx), _ptr(topk_score), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)),
+           "nvfp4_router_topk")
 
 
 def nvfp4_linear_run(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,

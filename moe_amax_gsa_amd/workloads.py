@@ -43,6 +43,9 @@ WORKLOADS = {
                               sf=(0.25, 4.0), ws2=(0.002, 0.01)),
     "stress_m2048_k7168_n7168": dict(kind="linear", M=2048, K=7168, N=7168, seed=4,
                                      x="student_t", sf=(0.125, 8.0), ws2=0.003),
+    # the dense router: hidden 7168, 384 routed experts, 6 chosen per token
+    "router_m1_k7168_e384_top6": dict(kind="router", M=1, K=7168, N=384, topk=6, seed=5),
+    "router_m64_k7168_e384_top6": dict(kind="router", M=64, K=7168, N=384, topk=6, seed=6),
 }
 
 
@@ -181,6 +184,29 @@ def make_moe(tokens=64, experts=256, topk=8, K1=7168, N1=4096, K2=2048, N2=7168,
                      K1, N1, K2, N2, granularity, seed, tuple(sf), tuple(ws2))
 
 
+@dataclass
+class RouterInputs:
+    name: str
+    x: np.ndarray        # (M, K) bf16 bits
+    w: np.ndarray        # (N, K) bf16 bits: the gate weight, one row per expert
+    bias: np.ndarray     # (N,) float32 per-expert bias
+    M: int
+    K: int
+    N: int
+    topk: int
+
+
+def make_router(M: int, K: int, N: int, topk: int, seed: int,
+                name: str = "custom") -> RouterInputs:
+    """x ~ N(0, 1); gate weight ~ N(0, (2 / sqrt(K))^2), so the logits spread
+    about N(0, 4); bias ~ N(0, 0.05^2) in float32.  Draw order: x, w, bias."""
+    rng = np.random.default_rng(seed)
+    x = to_bf16_bits(rng.standard_normal((M, K)))
+    w = to_bf16_bits(rng.standard_normal((N, K)) * (2.0 / np.sqrt(K)))
+    bias = (rng.standard_normal(N) * 0.05).astype(np.float32)
+    return RouterInputs(name, x, w, bias, M, K, N, topk)
+
+
 def make(name: str):
     """Build the named workload at its full size."""
     c = dict(WORKLOADS[name])
@@ -188,6 +214,8 @@ def make(name: str):
     if kind == "linear":
         return make_linear(c["M"], c["K"], c["N"], c["seed"], c["x"], c["sf"], c["ws2"],
                            name=name)
+    if kind == "router":
+        return make_router(c["M"], c["K"], c["N"], c["topk"], c["seed"], name=name)
     return make_moe(c["tokens"], c["experts"], c["topk"], c["K1"], c["N1"], c["K2"],
                     c["N2"], c["granularity"], c["seed"], c["sf"], c["ws2"], name=name)
 

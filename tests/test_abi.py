@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(C):
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert C.nvfp4_abi_version() == 3
+    assert C.nvfp4_abi_version() == 4
 
 
 def test_status_strings(C):
@@ -103,10 +103,20 @@ def test_validation_of_the_fused_and_load_time_entries(C):
     assert rq(fake, 0, fake, 0, 1e-6, 0, 32, 1, fake, None, None, None, None, 0, None) == 0
     lr = L.nvfp4_linear_rows
     args = [fake] * 7
-    assert lr(*args, 0, 2, 3, 24, None) == -2
-    assert lr(*args, 5, 2, 3, 32, None) == -3
-    assert lr(fake, fake, None, fake, fake, fake, fake, 1, 2, 3, 32, None) == -1
-    assert lr(*args, 1, 0, 3, 32, None) == 0  # M == 0: no-op
+    assert lr(*args, 0, 2, 3, 24, None, 0, None) == -2
+    assert lr(*args, 5, 2, 3, 32, None, 0, None) == -3
+    assert lr(fake, fake, None, fake, fake, fake, fake, 1, 2, 3, 32, None, 0, None) == -1
+    assert lr(*args, 1, 0, 3, 32, None, 0, None) == 0  # M == 0: no-op
+    rt = L.nvfp4_router_topk
+    # (a_codes, a_scales, gsa, w_codes, w_scales, ws2, bias, M, N, K, k, idx, score, ws, bytes, s)
+    assert rt(*[fake] * 7, 2, 1025, 64, 8, fake, fake, fake, 1 << 20, None) == -2  # N > 1024
+    assert rt(*[fake] * 7, 2, 64, 64, 0, fake, fake, fake, 1 << 20, None) == -2     # k < 1
+    assert rt(*[fake] * 7, 2, 64, 64, 65, fake, fake, fake, 1 << 20, None) == -2    # k > N
+    assert rt(*[fake] * 7, 2, 64, 40, 8, fake, fake, fake, 1 << 20, None) == -2     # K % 16
+    assert rt(*[fake] * 6, None, 2, 64, 64, 8, None, fake, fake, 1 << 20, None) == -1
+    assert rt(*[fake] * 6, None, 2, 64, 64, 8, fake, fake, fake, 2 * 64 * 4 - 4, None) == -4
+    assert rt(*[fake] * 6, None, 2, 64, 64, 8, fake, fake, None, 0, None) == -4
+    assert rt(*[fake] * 6, None, 0, 64, 64, 8, None, None, None, 0, None) == 0   # M == 0
     qw = L.nvfp4_quantize_weight
     assert qw(fake, 0, 0, 32, fake, fake, fake, None, 0, None) == -2
     assert qw(fake, 0, 4, 40, fake, fake, fake, None, 0, None) == -2
@@ -114,3 +124,14 @@ def test_validation_of_the_fused_and_load_time_entries(C):
     big = C.nvfp4_workspace_bytes(C.OP_QUANTIZE_WEIGHT, 0, 4096, 4096)
     assert big > 0
     assert qw(fake, 0, 4096, 4096, fake, fake, fake, None, 0, None) == -4
+
+
+def test_linear_workspace_is_optional_and_sized_by_shape(C):
+    # one output tile per device's worth of compute units: no split, no bytes
+    assert C.nvfp4_workspace_bytes(C.OP_LINEAR, 4096, 4096, 7168) == 0
+    assert C.nvfp4_workspace_bytes(C.OP_LINEAR, 8, 64, 7168) == 0      # weight-streaming kernel
+    assert C.nvfp4_workspace_bytes(C.OP_LINEAR, 64, 96, 1000) == 0     # K not in 256-chunks
+    n = C.nvfp4_workspace_bytes(C.OP_LINEAR, 64, 96, 1024)
+    assert n > 0 and n % (64 * 96 * 4) == 0
+    r = C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, 64, 96, 1024)
+    assert r == 64 * 96 * 4 + n

@@ -262,6 +262,52 @@ def test_linear_parity(C, M, N, K):
     assert rel_err(yg, ref) <= REL_TOL
 
 
+SPLIT_CASES = [(17, 64, 512), (64, 96, 1024), (130, 300, 768), (256, 256, 7168),
+               (100, 40, 2304), (129, 65, 1280)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_CASES)
+def test_linear_split_k(C, M, N, K):
+    """Few output tiles: with the workspace the tiled kernel splits K and a
+    second kernel adds the partials in split order.  Against the oracle,
+    and against the unsplit kernel (the same sums in another fp32 order)."""
+    say("linear split K", M, N, K)
+    need = C.nvfp4_workspace_bytes(C.OP_LINEAR, M, N, K)
+    assert need > 0
+    inp = W.make_linear(M, K, N, seed=M + 2 * N + K, x="outliers", sf=(0.125, 8.0), ws2=0.0037)
+    xd = x_dev(inp.x, "bf16")
+    g = gpu_gsa(C, xd)
+    codes, scales = gpu_quantize(C, xd, g)
+    wc, wsf = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=DEV)
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=DEV)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(codes, scales, g, wc, wsf, ws2, y, ws)
+    y1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(codes, scales, g, wc, wsf, ws2, y1)          # no workspace: unsplit
+    oc, os_ = oracle.quantize(inp.x, f32(g))
+    ref = oracle.linear(oc, os_, f32(g), inp.w_codes, inp.w_scales, inp.ws2)
+    yg, y1g = y.cpu().numpy().astype(np.float64), y1.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(yg))
+    assert rel_err(yg, ref) <= REL_TOL
+    assert rel_err(yg, y1g) <= 1e-5
+    # deterministic: a second call gives the same bits
+    y2 = torch.empty_like(y)
+    C.nvfp4_linear(codes, scales, g, wc, wsf, ws2, y2, ws)
+    assert torch.equal(y2, y)
+    # bf16 output and per-row gsa through the same split
+    y16 = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    C.nvfp4_linear(codes, scales, g, wc, wsf, ws2, y16, ws)
+    assert torch.equal(y16.cpu(), y.cpu().to(torch.bfloat16))
+    grow = torch.full((M,), float(f32(g)), dtype=torch.float32, device=DEV)
+    grow[::3] *= 2.0
+    yr = torch.empty_like(y)
+    C.nvfp4_linear_rows(codes, scales, grow, wc, wsf, ws2, yr, ws)
+    scale = np.ones(M)
+    scale[::3] = 2.0
+    assert torch.equal(yr.cpu(), torch.from_numpy((yg * scale[:, None]).astype(np.float32)))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 7168), (3, 100, 256), (40, 96, 1024), (200, 160, 7168)])
 def test_linear_integer_case_bitexact(C, M, N, K):
     """All block scales 1.0, gsa = ws2 = 1: outputs are multiples of 1/4 below
@@ -274,10 +320,12 @@ def test_linear_integer_case_bitexact(C, M, N, K):
     asf = np.full((M, K // 16), 0x38, np.uint8)
     wsf = np.full((N, K // 16), 0x38, np.uint8)
     one = torch.ones(1, dtype=torch.float32, device=DEV)
-    y = torch.empty(M, N, dtype=torch.float32, device=DEV)
-    C.nvfp4_linear(to_dev(ac), to_dev(asf), one, to_dev(wc), to_dev(wsf), one, y)
     ref = oracle.linear(ac, asf, 1.0, wc, wsf, 1.0)
-    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+    need = C.nvfp4_workspace_bytes(C.OP_LINEAR, M, N, K)
+    for ws in [None] + ([torch.empty(need, dtype=torch.uint8, device=DEV)] if need else []):
+        y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+        C.nvfp4_linear(to_dev(ac), to_dev(asf), one, to_dev(wc), to_dev(wsf), one, y, ws)
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
 @pytest.mark.parametrize("M", [1, 64])
@@ -708,6 +756,128 @@ def test_layer_rmsnorm_forward(C, per_row):
     assert np.array_equal(lin.codes[:M].cpu().numpy(), oc)
     err = np.max(np.abs(yg - ref), axis=1) / np.maximum(np.max(np.abs(ref), axis=1), 1e-300)
     assert np.max(err) <= REL_TOL
+
+
+# ---------------------------------------------------------------- router
+def router_inputs(M, K, N, k, seed):
+    """Router operands quantized by the oracle: A from x, the gate weight
+    with its own global scale (the load-time recipe)."""
+    r = W.make_router(M, K, N, k, seed)
+    ga = oracle.amax_gsa(r.x)
+    ac, as_ = oracle.quantize(r.x, ga)
+    gw = oracle.amax_gsa(r.w)
+    wc, wsf = oracle.quantize(r.w, gw)
+    return r, ga, ac, as_, gw, wc, wsf
+
+
+def gpu_router(C, ac, as_, ga, wc, wsf, gw, bias, k):
+    M, N = ac.shape[0], wc.shape[0]
+    idx = torch.full((M, k), -7, dtype=torch.int32, device=DEV)
+    sc = torch.full((M, k), float("nan"), dtype=torch.float32, device=DEV)
+    K = ac.shape[1] * 2
+    ws = torch.full((max(16, C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, M, N, K)),), 0xAB,
+                    dtype=torch.uint8, device=DEV)
+    C.nvfp4_router_topk(to_dev(ac), to_dev(as_), torch.tensor([ga], device=DEV), to_dev(wc),
+                        to_dev(wsf), torch.tensor([gw], device=DEV),
+                        None if bias is None else to_dev(bias), idx, sc, ws)
+    logits = ws[:M * N * 4].view(torch.float32).view(M, N).cpu().numpy()
+    return idx.cpu().numpy(), sc.cpu().numpy(), logits
+
+
+def check_choice(idx_g, sc_g, z, bias, k, eps):
+    """The GPU's choice on its own logits z, against the oracle's choice on
+    the same logits: identical, or different only among values within eps
+    of each other (fp32 scores on the GPU, binary64 in the oracle)."""
+    idx_o, sc_o = oracle.router_topk(z, bias, k)
+    v = oracle.router_scores(z) + (0.0 if bias is None else bias.astype(np.float64))
+    for m in range(z.shape[0]):
+        assert len(set(idx_g[m])) == k and np.all((idx_g[m] >= 0) & (idx_g[m] < z.shape[1]))
+        if not np.array_equal(idx_g[m], idx_o[m]):
+            assert np.all(np.abs(v[m, idx_g[m]] - v[m, idx_o[m]]) <= eps), m
+    # the scores: sqrt(softplus) of the chosen logits, to a few fp32 ulp
+    ref = oracle.router_scores(np.take_along_axis(z.astype(np.float64), idx_g.astype(np.int64),
+                                                  axis=1))
+    assert np.allclose(sc_g, ref, rtol=2e-6, atol=0)
+    return idx_o
+
+
+ROUTER_CASES = [
+    (1, 384, 7168, 6), (1, 256, 7168, 8), (3, 256, 1024, 8),   # weight-streaming kernels
+    (16, 384, 2048, 6), (5, 33, 272, 1),
+    (17, 256, 512, 8), (64, 384, 7168, 6), (130, 96, 768, 4),   # tiled kernels
+    (2, 1024, 256, 32), (4, 64, 256, 64),                       # 1024 experts; k = N
+]
+
+
+@pytest.mark.parametrize("M,N,K,k", ROUTER_CASES)
+def test_router_topk(C, M, N, K, k):
+    """Gate logits against the oracle's linear (1e-3 of the largest); the
+    choice against the oracle's on the GPU's own logits (equal up to fp32
+    near-ties); and, where the oracle's own logits leave a clear gap after
+    the k-th expert, the same set of experts as the oracle end to end."""
+    say(f"router M={M} N={N} K={K} k={k}")
+    r, ga, ac, as_, gw, wc, wsf = router_inputs(M, K, N, k, seed=M * 31 + N + K + k)
+    idx_g, sc_g, z = gpu_router(C, ac, as_, ga, wc, wsf, gw, r.bias, k)
+    zo = oracle.linear(ac, as_, ga, wc, wsf, gw)
+    dz = np.max(np.abs(z - zo))
+    assert dz <= REL_TOL * np.max(np.abs(zo))
+    vmax = np.max(np.abs(oracle.router_scores(z))) + np.max(np.abs(r.bias))
+    check_choice(idx_g, sc_g, z, r.bias, k, eps=1e-6 * vmax)
+    # end to end: |d s / d z| <= 0.6, so the GPU's values are within
+    # 0.6 dz (+ fp32 rounding) of the oracle's
+    vo = oracle.router_scores(zo) + r.bias.astype(np.float64)
+    delta = 0.6 * dz + 1e-6 * vmax
+    idx_e, _ = oracle.router_topk(zo, r.bias, k)
+    checked = 0
+    for m in range(M):
+        srt = np.sort(vo[m])[::-1]
+        if k < N and srt[k - 1] - srt[k] <= 2 * delta:
+            continue
+        assert set(idx_g[m]) == set(idx_e[m]), m
+        checked += 1
+    assert checked >= (M + 1) // 2
+
+
+@pytest.mark.parametrize("M,N,K,k", [(1, 384, 1024, 6), (9, 256, 1024, 8), (40, 128, 1024, 8)])
+def test_router_integer_case_exact(C, M, N, K, k):
+    """Scales 1.0 and gsa = gsb = 2^-4: the logits are exact on both sides,
+    so the choice (no bias) is the oracle's exactly, ties included."""
+    say(f"router integer M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asf = np.full((M, K // 16), 0x38, np.uint8)
+    wsf = np.full((N, K // 16), 0x38, np.uint8)
+    g = np.float32(2.0 ** -4)
+    idx_g, sc_g, z = gpu_router(C, ac, asf, g, wc, wsf, g, None, k)
+    zo = oracle.linear(ac, asf, g, wc, wsf, g)
+    assert np.array_equal(z.astype(np.float64), zo)
+    idx_o, sc_o = oracle.router_topk(zo, None, k)
+    assert np.array_equal(idx_g, idx_o)
+    assert np.allclose(sc_g, sc_o, rtol=2e-6, atol=0)
+
+
+def test_router_layer(C):
+    """Nvfp4Router: gate weight quantized at load time, activation quantized
+    per call, then the choice -- against the oracle's chain on the same
+    bf16 inputs."""
+    from moe_amax_gsa_amd.layer import Nvfp4Router
+    say("router layer")
+    r = W.make_router(3, 2048, 256, 8, seed=12)
+    router = Nvfp4Router.from_weight(W.bf16_to_torch(r.w, DEV), to_dev(r.bias), topk=8,
+                                     max_tokens=4)
+    idx, sc = router(W.bf16_to_torch(r.x, DEV))
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    gw = oracle.amax_gsa(r.w)
+    assert f32(router.gate.ws2) == gw
+    ga = oracle.amax_gsa(r.x)
+    ac, as_ = oracle.quantize(r.x, ga)
+    wc, wsf = oracle.quantize(r.w, gw)
+    z = router.ws[:3 * 256 * 4].view(torch.float32).view(3, 256).cpu().numpy()
+    zo = oracle.linear(ac, as_, ga, wc, wsf, gw)
+    assert np.max(np.abs(z - zo)) <= REL_TOL * np.max(np.abs(zo))
+    vmax = np.max(np.abs(oracle.router_scores(z))) + np.max(np.abs(r.bias))
+    check_choice(idx, sc, z, r.bias, 8, eps=1e-6 * vmax)
 
 
 def test_swiglu_parity(C):
