@@ -262,6 +262,55 @@ def bench_router(C, name, dev, steps, warmup):
             "step_frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_rmsnorm(C, name, dev, steps, warmup):
+    """RMSNorm fused into the quantize (nvfp4_rmsnorm_quantize), with one
+    global scale and with one per row."""
+    from moe_amax_gsa_amd import workloads as W
+    r = W.make(name)
+    M, K = r.M, r.K
+    x, w = W.bf16_to_torch(r.x, dev), W.bf16_to_torch(r.w, dev)
+    gsa = torch.empty(M, dtype=torch.float32, device=dev)
+    inv = torch.empty(M, dtype=torch.float32, device=dev)
+    codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(16, C.nvfp4_workspace_bytes(C.OP_RMSNORM_QUANTIZE, M, 0, K)),
+                     dtype=torch.uint8, device=dev)
+    res = {}
+    for key, per_row in [("one_gsa", False), ("gsa_per_row", True)]:
+        def step(i, per_row=per_row):
+            C.nvfp4_rmsnorm_quantize(x, w, gsa, inv, codes, scales, per_row=per_row, ws=ws)
+        res[key + "_us"] = 1e3 * graph_ms_per_step(step, steps, warmup)
+    # x and the norm weight read once, codes + scales + inv_rms + gsa written
+    nbytes = M * K * 2 + K * 2 + M * K * 9 // 16 + M * 8
+    res["bytes_per_step"] = nbytes
+    for key in ["one_gsa", "gsa_per_row"]:
+        res[key + "_GBps"] = nbytes / (res[key + "_us"] * 1e-6) / 1e9
+    return res
+
+
+def bench_quantize_weight(C, dev, steps, warmup, N=129280, K=7168):
+    """Load-time quantize of a bf16 weight the size of the lm_head (vocab
+    129280 x hidden 7168): amax -> weight_scale_2 -> codes and scales.  The
+    weight is drawn on the device (torch's seeded generator): a numpy draw
+    of 0.9 G values would dominate the run."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    w = (torch.randn(N, K, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    ws2 = torch.empty(1, dtype=torch.float32, device=dev)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(N, K // 16, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(16, C.nvfp4_workspace_bytes(C.OP_QUANTIZE_WEIGHT, 0, N, K)),
+                     dtype=torch.uint8, device=dev)
+    us = 1e3 * graph_ms_per_step(lambda i: C.nvfp4_quantize_weight(w, ws2, codes, scales, ws),
+                                 steps, warmup)
+    # the two-phase amax reads w once, the quantize reads it again and writes
+    nbytes = 2 * (N * K * 2) + N * K * 9 // 16
+    del w
+    return {"step_us": us, "N": N, "K": K, "bytes_per_step": nbytes,
+            "step_GBps": nbytes / (us * 1e-6) / 1e9,
+            "step_frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 # ------------------------------------------------------------------ oracle
 def cpu_baseline(inp, budget_s=12.0):
     """The oracle's step (amax, quantize, FP64 linear) for the same workload
@@ -335,6 +384,15 @@ def main():
                 continue
             log("workload", name)
             workloads[name] = bench_router(C, name, dev, args.steps, min(args.warmup, 10))
+        for name in ["rmsnorm_m1_k7168", "rmsnorm_m512_k7168"]:
+            if args.only and args.only != name:
+                continue
+            log("workload", name)
+            workloads[name] = bench_rmsnorm(C, name, dev, args.steps, min(args.warmup, 10))
+        if not args.only or args.only == "quantize_weight_n129280_k7168":
+            log("workload quantize_weight_n129280_k7168")
+            workloads["quantize_weight_n129280_k7168"] = bench_quantize_weight(
+                C, dev, max(5, args.steps // 40), 2)
         if not args.only or args.only == "moe_t64_e256_top8":
             log("workload moe_t64_e256_top8")
             workloads["moe_t64_e256_top8"] = bench_moe(C, dev, max(10, args.steps // 10),

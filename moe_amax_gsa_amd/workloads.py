@@ -46,6 +46,9 @@ WORKLOADS = {
     # the dense router: hidden 7168, 384 routed experts, 6 chosen per token
     "router_m1_k7168_e384_top6": dict(kind="router", M=1, K=7168, N=384, topk=6, seed=5),
     "router_m64_k7168_e384_top6": dict(kind="router", M=64, K=7168, N=384, topk=6, seed=6),
+    # RMSNorm -> quantize of the hidden state, one token and a prefill batch
+    "rmsnorm_m1_k7168": dict(kind="rmsnorm", M=1, K=7168, seed=7),
+    "rmsnorm_m512_k7168": dict(kind="rmsnorm", M=512, K=7168, seed=8),
 }
 
 
@@ -207,6 +210,30 @@ def make_router(M: int, K: int, N: int, topk: int, seed: int,
     return RouterInputs(name, x, w, bias, M, K, N, topk)
 
 
+@dataclass
+class RMSNormInputs:
+    name: str
+    x: np.ndarray        # (M, K) bf16 bits
+    w: np.ndarray        # (K,) bf16 bits: the norm weight
+    M: int
+    K: int
+
+
+def make_rmsnorm(M: int, K: int, seed: int, zero_row: bool = False,
+                 name: str = "custom") -> RMSNormInputs:
+    """Rows of N(0, 1) times a per-row magnitude exp(U[-3, 3]) (hidden states
+    of very different sizes), 0.2% of the entries times 40 (outliers), and
+    optionally row M // 2 all zero; norm weight 1 + 0.25 N(0, 1).  Draw
+    order: x, the row magnitudes, the outlier mask, w."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)) * np.exp(rng.uniform(-3, 3, (M, 1)))
+    x[rng.random((M, K)) < 0.002] *= 40.0
+    if zero_row:
+        x[M // 2] = 0.0
+    w = 1.0 + 0.25 * rng.standard_normal(K)
+    return RMSNormInputs(name, to_bf16_bits(x), to_bf16_bits(w), M, K)
+
+
 def make(name: str):
     """Build the named workload at its full size."""
     c = dict(WORKLOADS[name])
@@ -216,6 +243,8 @@ def make(name: str):
                            name=name)
     if kind == "router":
         return make_router(c["M"], c["K"], c["N"], c["topk"], c["seed"], name=name)
+    if kind == "rmsnorm":
+        return make_rmsnorm(c["M"], c["K"], c["seed"], name=name)
     return make_moe(c["tokens"], c["experts"], c["topk"], c["K1"], c["N1"], c["K2"],
                     c["N2"], c["granularity"], c["seed"], c["sf"], c["ws2"], name=name)
 

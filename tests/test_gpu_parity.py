@@ -630,13 +630,8 @@ INV_RMS_TOL = 1e-5
 
 
 def rms_case(M, K, seed, zero_row=False):
-    rng = np.random.default_rng(seed)
-    x64 = rng.standard_normal((M, K)) * np.exp(rng.uniform(-3, 3, (M, 1)))
-    x64[rng.random((M, K)) < 0.002] *= 40.0  # a few outliers per row
-    if zero_row:
-        x64[M // 2] = 0.0
-    w64 = 1.0 + 0.25 * rng.standard_normal(K)
-    return W.to_bf16_bits(x64), W.to_bf16_bits(w64)
+    r = W.make_rmsnorm(M, K, seed, zero_row=zero_row)
+    return r.x, r.w
 
 
 def gpu_rmsnorm_quantize(C, x, w, per_row, eps=1e-6):
