@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--pmc-probe", action="store_true",
                    help="run only a 256 MiB copy and the headline kernel (for counter runs)")
+    p.add_argument("--pmc-probe-prefill", action="store_true",
+                   help="run only a 256 MiB copy, then the prefill quantize and linear "
+                        "(for counter runs)")
     return p.parse_args()
 
 
@@ -352,6 +355,46 @@ def pmc_probe(C, dev, launches=20):
                       "source_hash": kernel_source_hash()}))
 
 
+def pmc_probe_prefill(C, dev, launches=10):
+    """A 256 MiB device copy (three times), then `launches` rounds of the
+    prefill workload's amax + quantize and its linear, on rotated weights."""
+    from moe_amax_gsa_amd import workloads as W
+    name = "prefill_m512_k7168_n4096"
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    b = LinearBench(C, W.make(name), dev)
+    for i in range(launches):
+        b.quantize(i)
+        b.linear(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": name, "copy_bytes": src.numel(), "copies": 3,
+                      "launches": launches, "quant_bytes": b.quant_bytes, "flops": b.flops,
+                      "source_hash": kernel_source_hash()}))
+
+
+def torch_bf16_matmul_us(M, N, K, dev, iters=20):
+    """Context only: torch's bf16 matmul (hipBLASLt) on random operands of
+    the same shape, timed eagerly between events (not captured)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    a = torch.randn(M, K, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    bt = torch.randn(K, N, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, bt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        torch.matmul(a, bt)
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / iters
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -364,6 +407,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.pmc_probe:
         pmc_probe(C, dev)
+        return
+    if args.pmc_probe_prefill:
+        pmc_probe_prefill(C, dev)
         return
     kiters = 50
 
@@ -379,6 +425,12 @@ def main():
             log("workload", name)
             workloads[name] = bench_linear(C, name, dev, steps, min(args.warmup, 10),
                                            min(kiters, steps))[2]
+            if name != "tiny_m1_k256_n256":
+                c = __import__("moe_amax_gsa_amd.workloads", fromlist=["WORKLOADS"]).WORKLOADS[name]
+                us = torch_bf16_matmul_us(c["M"], c["N"], c["K"], dev)
+                workloads[name]["context_torch_bf16_matmul_us"] = us
+                workloads[name]["context_torch_bf16_matmul_TFLOPs"] = (
+                    workloads[name]["flops"] / (us * 1e-6) / 1e12)
         for name in ["router_m1_k7168_e384_top6", "router_m64_k7168_e384_top6"]:
             if args.only and args.only != name:
                 continue
