@@ -156,15 +156,67 @@ __device__ __forceinline__ float swiglu1(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-// ---- wave64 reductions (DPP-friendly xor shuffles)
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
-    v = v > w ? v : w;
-  }
-  return v;
+// ---- wave64 cross-lane steps on DPP (no LDS round trip, unlike the
+// bpermute that a general shuffle compiles to).  Within each row of 16
+// lanes: quad_perm [1,0,3,2] pairs lane i with i ^ 1 and [2,3,0,1] with
+// i ^ 2, so two steps leave every lane with its quad's result; then
+// row_half_mirror pairs lane i of each 8-lane half with 7 - i (a lane of the
+// other quad) and row_mirror pairs lane i with 15 - i (a lane of the other
+// half).  Four steps leave the row's result in all 16 lanes, associated as
+// ((l0 . l1) . (l2 . l3)) . ((l4 . l5) . (l6 . l7)) ... like an xor
+// butterfly.  row_ror:4 / row_ror:8 rotate a row by 4 / 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+constexpr int DPP_ROR4 = 0x124, DPP_ROR8 = 0x128;
+
+__device__ __forceinline__ float row16_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f32<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f32<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f32<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum_f32(float v) {
+  v += dpp_f32<DPP_XOR1>(v);
+  v += dpp_f32<DPP_XOR2>(v);
+  v += dpp_f32<DPP_HALF_MIRROR>(v);
+  return v + dpp_f32<DPP_MIRROR>(v);
+}
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_XOR1>(v));
+  v = max(v, dpp_u32<DPP_XOR2>(v));
+  v = max(v, dpp_u32<DPP_HALF_MIRROR>(v));
+  return max(v, dpp_u32<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// The whole wave's result, uniform (the four rows' results read out).
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = row16_max_f32(v);
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+               fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = row16_sum_f32(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row16_max_u32(v);
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+// lane ^ 1 (the other half of a 16-element block in the quantize kernels)
+__device__ __forceinline__ float xor1_f32(float v) { return dpp_f32<DPP_XOR1>(v); }
 
 }  // namespace nvfp4
 

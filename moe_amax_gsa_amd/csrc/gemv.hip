@@ -229,8 +229,7 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
 #pragma unroll
       for (int q = 0; q < BPT; ++q)
         if (xok[q]) m = fmaxf(m, block_absmax16(xv[q]));
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      m = wave_max_f32(m);
       if (lane == 0) amax_red[wave] = m;
       lds_barrier();
       float mm = 0.f;
@@ -758,21 +757,18 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
 #pragma unroll
     for (int u = 0; u < HPT; ++u)
       if (xok[u]) mx = fmaxf(mx, half_absmax8(xv[u]));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx = wave_max_f32(mx);
     if (lane == 0) amax_red[wave] = mx;
     lds_barrier();
-    // every 16 lanes read the (at most 16) wave maxima at once and reduce
-    float mm = (lane & 15) < NW ? amax_red[lane & 15] : 0.f;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
+    // every row of 16 lanes reads the (at most 16) wave maxima at once
+    const float mm = row16_max_f32((lane & 15) < NW ? amax_red[lane & 15] : 0.f);
     gsa_v = gsa_from_amax(mm);
     const bool writer = blockIdx.x == 0;
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
       const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
       float bm = xok[u] ? half_absmax8(xv[u]) : 0.f;
-      bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+      bm = fmaxf(bm, xor1_f32(bm));
       uint32_t c, sf;
       quantize_half8(xv[u], bm, gsa_v, c, sf);
       if (xok[u]) {
@@ -851,8 +847,10 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
       const float v = useful ? acc[m][rq] : 0.f;
       const int src = 20 * (lane >> 2) + (lane & 3);  // lanes 0..15 read the 16 useful lanes
       float t = __shfl(v, src & 63, 64);
-      t += __shfl_down(t, 4, 64);
-      t += __shfl_down(t, 8, 64);
+      // lanes r, r+4, r+8, r+12 of row 0 hold row r's four parts: two
+      // rotations by 4 and 8 lanes add them (either direction covers them)
+      t += dpp_f32<DPP_ROR4>(t);
+      t += dpp_f32<DPP_ROR8>(t);
       if (lane < 4) red[wave][m][4 * rq + lane] = t;
     }
   __syncthreads();
@@ -863,8 +861,7 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
     const int e = base + lane, o = e >> 4, w = e & 15;
     const int m = o / (4 * RQ), rr = o % (4 * RQ);
     float sum = (w < NW && o < MR * 4 * RQ) ? red[w][m][rr] : 0.f;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) sum += __shfl_xor(sum, d, 64);
+    sum = row16_sum_f32(sum);
     const int n = n0 + rr;
     if (w == 0 && o < MR * 4 * RQ && m < M && n < N) {
       const float v = sum * (args.gsa_rows ? args.gsa[m] * args.ws2[0] : gscale);

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   load_half8<BF16>(x, ok ? h : 0, v);
   const float gsa = gsa_p[0];
   float m = half_absmax8(v);
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, xor1_f32(m));
   uint32_t c, sf;
   quantize_half8(v, m, gsa, c, sf);
   if (ok) {
@@ -169,8 +169,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void amax_quantize_small_kernel(
 #pragma unroll
   for (int q = 0; q < HPT; ++q)
     if (ok[q]) m = fmaxf(m, half_absmax8(v[q]));
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = wave_max_f32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   float mm = 0.f;
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void amax_quantize_small_kernel(
   for (int q = 0; q < HPT; ++q) {
     const int64_t h = threadIdx.x + (int64_t)q * SMALL_THREADS;
     float bm = ok[q] ? half_absmax8(v[q]) : 0.f;
-    bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+    bm = fmaxf(bm, xor1_f32(bm));
     uint32_t c, sf;
     quantize_half8(v[q], bm, gsa, c, sf);
     if (ok[q]) {
@@ -228,8 +227,7 @@ hipError_t launch_amax_quantize_small(const void* x, bool bf16, int64_t M, int64
 // kernel 2 reads gsa[0].  Kernel 2 forms y again per half-block and
 // quantizes it as quantize_kernel does.
 __device__ __forceinline__ float block_sum_f32(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_f32(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float t = 0.f;
@@ -293,7 +291,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
   rms_y8<XBF16, WBF16>(x, w, hh, hh - m * K8, inv_rms[m], y);
   const float gsa = gsa_p[PER_ROW ? m : 0];
   float bm = half_absmax8(y);
-  bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+  bm = fmaxf(bm, xor1_f32(bm));
   uint32_t c, sf;
   quantize_half8(y, bm, gsa, c, sf);
   if (ok) {
