@@ -300,10 +300,120 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
   }
 }
 
+// One row per workgroup, the whole row in registers: thread t owns
+// half-blocks t, t + T, ... (HPT of them) of the row.  The sum of squares,
+// inv_rms, y = (x * inv_rms) * w, the row's largest |y| -- its gsa, the
+// row's own (per-row scales, or one row) -- and the codes and scales, all
+// from one read of x and w.  The two reductions over the row go through DPP
+// within waves and LDS across them, each followed by one barrier.
+template <bool XBF16, bool WBF16, int HPT>
+__global__ __launch_bounds__(1024) void rmsnorm_quantize_row_kernel(
+    const void* __restrict__ x, const void* __restrict__ w, float eps, int K,
+    float* __restrict__ inv_rms, float* __restrict__ gsa_p, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+#pragma clang fp contract(off)
+  __shared__ float red_s[16], red_m[16];
+  const int64_t m = blockIdx.x;
+  const int T = blockDim.x, nw = T >> 6, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nh = K / 8;  // half-blocks in the row
+  float v[HPT][8];
+  bool ok[HPT];
+  uint4 xr[HPT][2], wr[HPT][2];
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {  // every load first
+    const int h = threadIdx.x + u * T;
+    ok[u] = h < nh;
+    const int hc = ok[u] ? h : 0;
+    load_half8_raw<XBF16>(x, m * nh + hc, xr[u]);
+    load_half8_raw<WBF16>(w, hc, wr[u]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    unpack_half8<XBF16>(xr[u], v[u]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (!ok[u]) v[u][i] = 0.f;
+      ss += v[u][i] * v[u][i];
+    }
+  }
+  ss = wave_sum_f32(ss);
+  if (lane == 0) red_s[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int i = 0; i < nw; ++i) tot += red_s[i];
+  const float r = 1.0f / sqrtf(tot / (float)K + eps);
+  float mx = 0.f;
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    float wv[8];
+    unpack_half8<WBF16>(wr[u], wv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[u][i] = (v[u][i] * r) * wv[i];
+    mx = fmaxf(mx, half_absmax8(v[u]));  // masked half-blocks are 0
+  }
+  mx = wave_max_f32(mx);
+  if (lane == 0) red_m[wave] = mx;
+  __syncthreads();
+  float rm = 0.f;
+  for (int i = 0; i < nw; ++i) rm = fmaxf(rm, red_m[i]);
+  const float gsa = gsa_from_amax(rm);
+  if (threadIdx.x == 0) {
+    inv_rms[m] = r;
+    gsa_p[m] = gsa;
+  }
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    const int h = threadIdx.x + u * T;
+    float bm = half_absmax8(v[u]);
+    bm = fmaxf(bm, xor1_f32(bm));  // T is a multiple of 64: h ^ 1 is the next lane
+    uint32_t c, sf;
+    quantize_half8(v[u], bm, gsa, c, sf);
+    if (ok[u]) {
+      ((uint32_t*)codes)[m * nh + h] = c;
+      if ((h & 1) == 0) scales[m * nh / 2 + h / 2] = (uint8_t)sf;
+    }
+  }
+}
+
+// Threads and half-blocks per thread of the one-row kernel, or false when a
+// row is too long for registers (more than 4096 half-blocks: K > 32768).
+static bool rms_row_plan(int64_t K, int& threads, int& hpt) {
+  const int64_t nh = K / 8;
+  if (nh > 4096) return false;
+  hpt = nh <= 1024 ? 1 : nh <= 2048 ? 2 : 4;
+  const int64_t t = (nh + hpt - 1) / hpt;
+  threads = (int)(((t + 63) / 64) * 64);
+  return true;
+}
+
+template <bool XBF16, bool WBF16>
+static hipError_t launch_rms_row_t(const void* x, const void* w, float eps, int64_t M, int64_t K,
+                                   float* gsa, float* inv_rms, uint8_t* codes, uint8_t* scales,
+                                   int threads, int hpt, hipStream_t s) {
+#define RMS_ROW(H)                                                                       \
+  rmsnorm_quantize_row_kernel<XBF16, WBF16, H><<<(unsigned)M, threads, 0, s>>>(x, w, eps, (int)K, \
+                                                                       inv_rms, gsa, codes, \
+                                                                       scales)
+  if (hpt == 1)
+    RMS_ROW(1);
+  else if (hpt == 2)
+    RMS_ROW(2);
+  else
+    RMS_ROW(4);
+#undef RMS_ROW
+  return hipGetLastError();
+}
+
 template <bool XBF16, bool WBF16, bool PER_ROW>
 static hipError_t launch_rmsnorm_t(const void* x, const void* w, float eps, int64_t M, int64_t K,
                                    float* gsa, float* inv_rms, uint8_t* codes, uint8_t* scales,
                                    uint32_t* partials, hipStream_t s) {
+  // per-row scales, or a single row: every scale is one row's own -- one kernel
+  int threads = 0, hpt = 0;
+  if ((PER_ROW || M == 1) && rms_row_plan(K, threads, hpt))
+    return launch_rms_row_t<XBF16, WBF16>(x, w, eps, M, K, gsa, inv_rms, codes, scales, threads,
+                                          hpt, s);
   rmsnorm_stats_kernel<XBF16, WBF16, PER_ROW><<<(unsigned)M, 256, 0, s>>>(x, w, eps, K, inv_rms,
                                                                          gsa, partials);
   hipError_t e = hipGetLastError();

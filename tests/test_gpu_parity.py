@@ -650,6 +650,8 @@ RMS_CASES = [
     (1, 16, "bf16", "bf16"), (1, 7168, "bf16", "bf16"), (3, 272, "fp32", "bf16"),
     (5, 1040, "bf16", "fp32"), (64, 2048, "fp32", "fp32"), (130, 7168, "bf16", "bf16"),
     (257, 4096, "bf16", "fp32"),
+    (1, 32768, "bf16", "fp32"), (3, 12288, "fp32", "bf16"),   # four, two half-blocks a thread
+    (2, 33024, "fp32", "bf16"),                               # too long for one row kernel
 ]
 
 
