@@ -521,9 +521,9 @@ hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM),
                   (unsigned)splits);
   if (splits == 1 || part == nullptr) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, false>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+    static unsigned char done[64];
+    const hipError_t attr = allow_dynamic_lds(
+        (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, false>, T::LDS_BYTES, done);
     if (attr != hipSuccess) return attr;
     gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, false>
         <<<dim3(grid.x, grid.y), T::THREADS, T::LDS_BYTES, s>>>(
@@ -531,9 +531,9 @@ hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const flo
             (int)K, gsa_rows ? 1 : 0, nch, nullptr);
     return hipGetLastError();
   }
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, true>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  static unsigned char done[64];
+  const hipError_t attr = allow_dynamic_lds(
+      (const void*)gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, true>, T::LDS_BYTES, done);
   if (attr != hipSuccess) return attr;
   gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, true><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
       a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K,

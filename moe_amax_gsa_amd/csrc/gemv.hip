@@ -629,6 +629,9 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
   }
 }
 
+// Dynamic LDS the ring kernel may take (the rest is its static LDS).
+constexpr size_t RING_MAX_LDS = 160 * 1024 - 256;
+
 template <int MP, int D, int W>
 static size_t ring_lds_bytes(int64_t K) {
   return (size_t)(2 * MP) * (size_t)(K / 2 + K / 16) +
@@ -638,9 +641,10 @@ static size_t ring_lds_bytes(int64_t K) {
 template <int MP, int D, int W, bool SWIGLU>
 static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
   const size_t lds = ring_lds_bytes<MP, D, W>(a.K);
-  if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_ring_kernel<MP, D, W, SWIGLU>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds > 64 * 1024) {  // the largest any launch may ask for (callers keep lds below it)
+    static unsigned char done[64];
+    const hipError_t e = allow_dynamic_lds((const void*)gemv_ring_kernel<MP, D, W, SWIGLU>,
+                                           RING_MAX_LDS, done);
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)((a.N + 16 * W - 1) / (16 * W)), (unsigned)G);
@@ -894,12 +898,9 @@ static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hip
   return hipGetLastError();
 }
 
-// Grouped linear through the LDS ring: the most activation rows per pass
-// (two workgroups per CU where that fits, else one) whose LDS fits
-// RING_MAX_LDS.  false: K too long to stage.
-constexpr size_t RING_MAX_LDS = 160 * 1024 - 256;  // room for the kernel's static LDS
-
-// *parts: the grid's workgroup count (SwiGLU amax partials)
+// Grouped linear through the LDS ring with one configuration, if its LDS
+// fits RING_MAX_LDS (false: K too long to stage).  *parts: the grid's
+// workgroup count (SwiGLU amax partials).
 template <int MP, int D, int W, bool SWIGLU>
 static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err, int64_t* parts) {
   if (ring_lds_bytes<MP, D, W>(a.K) > RING_MAX_LDS) return false;
@@ -908,6 +909,9 @@ static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err, i
   return true;
 }
 
+// The first configuration that fits: 16 activation rows a pass when groups
+// average more than 4 rows, else 8 rows with 8 waves (one workgroup per CU),
+// then smaller footprints for longer K.
 template <bool SWIGLU>
 static bool launch_ring(const GemvArgs& a, int G, int64_t mean_rows, hipStream_t s,
                         hipError_t* err, int64_t* parts) {

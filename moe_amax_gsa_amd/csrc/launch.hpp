@@ -7,6 +7,21 @@
 
 namespace nvfp4 {
 
+// Allow `bytes` of dynamic LDS for kernel f on the current device.  The
+// attribute belongs to the device, so it is set once per device; `done` is
+// the calling launcher's record for that kernel (setting it twice from two
+// threads is harmless).
+inline hipError_t allow_dynamic_lds(const void* f, int bytes, unsigned char (&done)[64]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool track = dev >= 0 && dev < 64;
+  if (track && done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && track) done[dev] = 1;
+  return e;
+}
+
 // amax -> gsa
 constexpr int64_t AMAX_SMALL_NUMEL = 65536;  // one workgroup, one kernel
 constexpr int AMAX_MAX_PARTS = 1024;         // phase-1 workgroups at most
