@@ -279,17 +279,29 @@ __global__ __launch_bounds__(256) void rmsnorm_stats_kernel(
   }
 }
 
-template <bool XBF16, bool WBF16, bool PER_ROW>
+// FINALIZE (one scale over several rows): every workgroup first reduces the
+// nparts row maxima itself -- the second amax phase -- and workgroup 0
+// writes gsa[0]; otherwise gsa is read (per row, or the finalized one).
+template <bool XBF16, bool WBF16, bool PER_ROW, bool FINALIZE>
 __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
     const void* __restrict__ x, const void* __restrict__ w, int64_t K, int64_t nhalf,
-    const float* __restrict__ inv_rms, const float* __restrict__ gsa_p,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const float* __restrict__ inv_rms, float* __restrict__ gsa_p,
+    const uint32_t* __restrict__ partials, int nparts, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
   const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool ok = h < nhalf;  // nhalf is even, so both lanes of a block agree
   const int64_t K8 = K / 8, hh = ok ? h : 0, m = hh / K8;
   float y[8];
   rms_y8<XBF16, WBF16>(x, w, hh, hh - m * K8, inv_rms[m], y);
-  const float gsa = gsa_p[PER_ROW ? m : 0];
+  float gsa;
+  if (FINALIZE) {
+    uint32_t mb = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) mb = max(mb, partials[i]);
+    gsa = gsa_from_amax(__uint_as_float(block_max_u32<256>(mb)));
+    if (blockIdx.x == 0 && threadIdx.x == 0) gsa_p[0] = gsa;
+  } else {
+    gsa = gsa_p[PER_ROW ? m : 0];
+  }
   float bm = half_absmax8(y);
   bm = fmaxf(bm, xor1_f32(bm));
   uint32_t c, sf;
@@ -299,6 +311,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
     if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sf;
   }
 }
+
+constexpr int64_t RMS_INLINE_ROWS = 4096;
 
 // One row per workgroup, the whole row in registers: thread t owns
 // half-blocks t, t + T, ... (HPT of them) of the row.  The sum of squares,
@@ -418,14 +432,22 @@ static hipError_t launch_rmsnorm_t(const void* x, const void* w, float eps, int6
                                                                          gsa, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int64_t nhalf = M * (K / 8);
+  const unsigned grid = (unsigned)((nhalf + 255) / 256);
+  // one scale over up to RMS_INLINE_ROWS rows: the quantize reduces the row
+  // maxima itself (two kernels); more rows: a finalize kernel between
+  if (!PER_ROW && M <= RMS_INLINE_ROWS) {
+    rmsnorm_quantize_kernel<XBF16, WBF16, false, true><<<grid, 256, 0, s>>>(
+        x, w, K, nhalf, inv_rms, gsa, partials, (int)M, codes, scales);
+    return hipGetLastError();
+  }
   if (!PER_ROW) {
     amax_finalize_kernel<false><<<1, AMAX_THREADS, 0, s>>>(partials, (int)M, gsa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t nhalf = M * (K / 8);
-  rmsnorm_quantize_kernel<XBF16, WBF16, PER_ROW><<<(unsigned)((nhalf + 255) / 256), 256, 0, s>>>(
-      x, w, K, nhalf, inv_rms, gsa, codes, scales);
+  rmsnorm_quantize_kernel<XBF16, WBF16, PER_ROW, false><<<grid, 256, 0, s>>>(
+      x, w, K, nhalf, inv_rms, gsa, partials, (int)M, codes, scales);
   return hipGetLastError();
 }
 

@@ -652,6 +652,7 @@ RMS_CASES = [
     (257, 4096, "bf16", "fp32"),
     (1, 32768, "bf16", "fp32"), (3, 12288, "fp32", "bf16"),   # four, two half-blocks a thread
     (2, 33024, "fp32", "bf16"),                               # too long for one row kernel
+    (4100, 32, "bf16", "bf16"),           # one scale over > 4096 rows: separate finalize
 ]
 
 
