@@ -352,6 +352,7 @@ RUN_CASES = [
     (1, 256, 64, "bf16"), (1, 7168, 1536, "bf16"), (1, 7168, 100, "fp32"), (2, 2048, 48, "bf16"),
     (3, 4096, 40, "fp32"), (5, 512, 33, "bf16"), (16, 1024, 64, "bf16"),  # one kernel
     (1, 272, 40, "bf16"), (4, 7168, 40, "bf16"), (20, 512, 64, "fp32"),    # separate kernels
+    (100, 7168, 96, "bf16"),  # amax partials, then the same workspace for a 14-way split K
 ]
 
 
@@ -855,15 +856,37 @@ def test_router_integer_case_exact(C, M, N, K, k):
     assert np.allclose(sc_g, sc_o, rtol=2e-6, atol=0)
 
 
+@pytest.mark.parametrize("M", [1, 64, 200])
+def test_layer_linear_sizes_its_workspace(C, M):
+    """Nvfp4Linear sized for 256 tokens: one token (weight-streaming
+    kernel), 64 and 200 tokens (few tiles: split K through the layer's own
+    workspace) -- against the oracle."""
+    from moe_amax_gsa_amd.layer import Nvfp4Linear
+    K, N = 2048, 96
+    say(f"layer linear M={M}")
+    inp = W.make_linear(M, K, N, seed=M + 5, ws2=0.006)
+    lin = Nvfp4Linear(to_dev(inp.w_codes), to_dev(inp.w_scales), inp.ws2, max_tokens=256)
+    y = lin(W.bf16_to_torch(inp.x, DEV)).cpu().numpy().astype(np.float64)
+    g = f32(lin.gsa)
+    oc, os_ = oracle.quantize(inp.x, g)
+    ref = oracle.linear(oc, os_, g, inp.w_codes, inp.w_scales, inp.ws2)
+    assert rel_err(y, ref) <= REL_TOL
+
+
 def test_router_layer(C):
     """Nvfp4Router: gate weight quantized at load time, activation quantized
     per call, then the choice -- against the oracle's chain on the same
     bf16 inputs."""
     from moe_amax_gsa_amd.layer import Nvfp4Router
     say("router layer")
-    r = W.make_router(3, 2048, 256, 8, seed=12)
-    router = Nvfp4Router.from_weight(W.bf16_to_torch(r.w, DEV), to_dev(r.bias), topk=8,
-                                     max_tokens=4)
+    for M in [3, 40]:  # 40 rows: the gate linear splits K inside the router's workspace
+        r = W.make_router(M, 2048, 256, 8, seed=12 + M)
+        router = Nvfp4Router.from_weight(W.bf16_to_torch(r.w, DEV), to_dev(r.bias), topk=8,
+                                         max_tokens=64)
+        check_router_layer(router, r, M)
+
+
+def check_router_layer(router, r, M):
     idx, sc = router(W.bf16_to_torch(r.x, DEV))
     idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
     gw = oracle.amax_gsa(r.w)
@@ -871,7 +894,7 @@ def test_router_layer(C):
     ga = oracle.amax_gsa(r.x)
     ac, as_ = oracle.quantize(r.x, ga)
     wc, wsf = oracle.quantize(r.w, gw)
-    z = router.ws[:3 * 256 * 4].view(torch.float32).view(3, 256).cpu().numpy()
+    z = router.ws[:M * 256 * 4].view(torch.float32).view(M, 256).cpu().numpy()
     zo = oracle.linear(ac, as_, ga, wc, wsf, gw)
     assert np.max(np.abs(z - zo)) <= REL_TOL * np.max(np.abs(zo))
     vmax = np.max(np.abs(oracle.router_scores(z))) + np.max(np.abs(r.bias))
