@@ -5,6 +5,10 @@
  *   1. amax -> gsa:  gsa = max(max_i |x_i|, 1e-8) / (6 * 448)
  *   2. quantize:     per 16-element block an E4M3 scale and 16 E2M1 codes
  *   3. linear:       y = gsa * ws2 * sum_k (lut[a]*sfa) * (lut[w]*sfw)
+ * with a grouped form of step 3 for routed experts (and SwiGLU fused into
+ * the gate/up projection), and around it the producer and consumers of the
+ * same data: RMSNorm fused into steps 1-2, steps 1-2 on a weight at load
+ * time, and the dense router's expert choice after a gate linear.
  *
  * Sources (pages of the nvfp4-megamoe-kernel repository on sweetapi.com):
  *   - commit 107d62d, single_shot_inference.py, commit message on computing
