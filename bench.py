@@ -217,10 +217,21 @@ def bench_moe(C, dev, steps, warmup):
     wbytes = nact * per_expert
     flops = 2.0 * P * (moe.N1 * moe.K1 + moe.N2 * moe.K2)
     us = 1e3 * graph_ms_per_step(lambda i: layer(x, ri, off), steps, warmup)
-    return {"step_us": us, "active_experts": nact, "weight_bytes": wbytes,
-            "step_GBps": wbytes / (us * 1e-6) / 1e9,
-            "step_frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "step_TFLOPs": flops / (us * 1e-6) / 1e12}
+    res = {"step_us": us, "active_experts": nact, "weight_bytes": wbytes,
+           "step_GBps": wbytes / (us * 1e-6) / 1e9,
+           "step_frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "step_TFLOPs": flops / (us * 1e-6) / 1e12}
+    # the same experts (the weights depend on the seed alone) for one decoded
+    # token routed to 8 of them: context for the decode shape
+    m1 = W.make_moe(tokens=1, experts=moe.E, topk=moe.topk, seed=moe.seed, name="moe_t1")
+    x1 = W.bf16_to_torch(m1.x, dev)
+    ri1 = torch.from_numpy(m1.pair_token).to(dev)
+    off1 = torch.from_numpy(m1.offsets).to(dev)
+    b1 = len(m1.active_experts) * per_expert
+    us1 = 1e3 * graph_ms_per_step(lambda i: layer(x1, ri1, off1), steps, warmup)
+    res.update({"one_token_step_us": us1, "one_token_weight_bytes": b1,
+                "one_token_GBps": b1 / (us1 * 1e-6) / 1e9})
+    return res
 
 
 def bench_router(C, name, dev, steps, warmup):

@@ -67,6 +67,10 @@ struct GemvArgs {
   uint32_t* partials;
   // plain mode: gsa holds one global scale per activation row (gsa[m])
   int gsa_rows;
+  // grouped ring: G groups in all; when the grid has fewer rows of
+  // workgroups than groups, workgroup row y serves the y-th group that has
+  // rows (found on the device from the offsets)
+  int groups;
 };
 
 __device__ __forceinline__ float4_t mfma_fp4(v8i a, v8i b) {
@@ -432,7 +436,33 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, j = lane >> 4;
   const int N = args.N, K = args.K;
-  const int g = blockIdx.y;
+  int g = blockIdx.y;
+  if (args.offsets != nullptr && (int)gridDim.y < args.groups) {
+    // compacted grid: the blockIdx.y-th group with rows (in group order)
+    __shared__ int sel, wcnt[W];
+    if (threadIdx.x == 0) sel = -1;
+    int base = 0;  // groups with rows before this pass
+    for (int t0 = 0; t0 < args.groups; t0 += W * 64) {
+      const int t = t0 + (int)threadIdx.x;
+      bool act = false;
+      if (t < args.groups)
+        act = min(args.offsets[t + 1], args.M) > max(args.offsets[t], 0);
+      const uint64_t b = __ballot(act);
+      if (lane == 0) wcnt[wave] = __popcll(b);
+      __syncthreads();
+      int before = base;
+      for (int w = 0; w < wave; ++w) before += wcnt[w];
+      const int rank = before + __popcll(b & ((1ull << lane) - 1ull));
+      if (act && rank == (int)blockIdx.y) sel = t;
+      for (int w = 0; w < W; ++w) base += wcnt[w];
+      __syncthreads();
+    }
+    g = __builtin_amdgcn_readfirstlane(sel);  // uniform after the barrier
+    if (g < 0) {  // fewer groups with rows than workgroup rows
+      if (SWIGLU && threadIdx.x == 0) args.partials[blockIdx.y * gridDim.x + blockIdx.x] = 0u;
+      return;
+    }
+  }
   int r_begin = 0, r_end = args.M;
   if (args.offsets != nullptr) {
     r_begin = max(args.offsets[g], 0);
@@ -647,8 +677,13 @@ static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
                                            RING_MAX_LDS, done);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)((a.N + 16 * W - 1) / (16 * W)), (unsigned)G);
-  gemv_ring_kernel<MP, D, W, SWIGLU><<<grid, W * 64, lds, s>>>(a);
+  // at most M groups have rows: with fewer rows than groups, launch a row of
+  // workgroups per possible group with rows instead of one per group
+  GemvArgs b = a;
+  b.groups = G;
+  const int gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
+  const dim3 grid((unsigned)((a.N + 16 * W - 1) / (16 * W)), (unsigned)gy);
+  gemv_ring_kernel<MP, D, W, SWIGLU><<<grid, W * 64, lds, s>>>(b);
   return hipGetLastError();
 }
 
@@ -904,7 +939,8 @@ static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hip
 template <int MP, int D, int W, bool SWIGLU>
 static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err, int64_t* parts) {
   if (ring_lds_bytes<MP, D, W>(a.K) > RING_MAX_LDS) return false;
-  *parts = (int64_t)((a.N + 16 * W - 1) / (16 * W)) * G;
+  const int64_t gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
+  *parts = (int64_t)((a.N + 16 * W - 1) / (16 * W)) * gy;
   *err = launch_ring_t<MP, D, W, SWIGLU>(a, G, s);
   return true;
 }

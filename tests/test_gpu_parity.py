@@ -557,6 +557,54 @@ def test_grouped_swiglu_matches_unfused(C, K, N, gran):
     assert np.all(a[[4, 10]] == 0.0)  # invalid row indices: unwritten
 
 
+@pytest.mark.parametrize("G,rows", [(64, {0: 1, 17: 2, 63: 1}), (100, {5: 3, 6: 1, 99: 2}),
+                                    (700, {3: 1, 511: 2, 512: 1, 699: 1})])
+def test_grouped_sparse_groups(C, G, rows):
+    """Fewer rows than groups (one decoded token over many experts): the
+    ring launches one row of workgroups per possible group with rows and
+    each finds its group on the device (700 groups: a scan over more
+    groups than threads).  Linear against the oracle; fused SwiGLU
+    bit-identical with the unfused calls."""
+    K, N, gran = 512, 64, 8
+    say(f"grouped sparse G={G} rows={rows}")
+    rng = np.random.default_rng(G)
+    sizes = np.zeros(G, np.int64)
+    for g, n in rows.items():
+        sizes[g] = n
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    P = int(offsets[-1])
+    assert P < G
+    a_rows = 3
+    row_index = rng.integers(0, a_rows, P).astype(np.int32)
+    ac = rng.integers(0, 256, (a_rows, K // 2), dtype=np.uint8)
+    asf = rng.integers(0x20, 0x48, (a_rows, K // 16), dtype=np.uint8)
+    wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    wsf = rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8)
+    ws2 = rng.uniform(0.002, 0.01, G).astype(np.float32)
+    gsa = np.float32(0.37)
+    d = dict(ac=to_dev(ac), asf=to_dev(asf), gsa=to_dev(np.array([gsa], np.float32)),
+             ri=to_dev(row_index), off=to_dev(offsets), wc=to_dev(wc), wsf=to_dev(wsf),
+             ws2=to_dev(ws2))
+    y = torch.full((P, N), -7.0, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(d["ac"], d["asf"], d["gsa"], d["ri"], d["off"], d["wc"], d["wsf"],
+                           d["ws2"], y)
+    ref = oracle.grouped_linear(ac, asf, gsa, row_index, offsets, wc, wsf, ws2, P)
+    assert rel_err(y.cpu().numpy().astype(np.float64), ref) <= REL_TOL
+    h1 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
+    g1 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    ws = torch.full((max(C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, 0, N, 0, G), 16),), 0xAB,
+                    dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_swiglu(d["ac"], d["asf"], d["gsa"], d["ri"], d["off"], d["wc"],
+                                  d["wsf"], d["ws2"], h1, g1, gran, ws)
+    h2 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
+    g2 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    C.nvfp4_swiglu_deinterleave(y, h2, gran)
+    C.nvfp4_amax_gsa(h2, g2, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(h1.cpu().numpy().view(np.uint32), h2.cpu().numpy().view(np.uint32))
+    assert f32(g1) == f32(g2)
+
+
 def test_grouped_row_index_bounds(C):
     """Row indices outside the activation rows and rows past the last group
     are left unwritten."""
