@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 4; }
+NVFP4_API int nvfp4_abi_version(void) { return 5; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -104,6 +104,32 @@ NVFP4_API int nvfp4_quantize_from_buffer(const void* x, int x_dtype, int64_t M, 
   if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gsa, 4)) return NVFP4_ERR_ALIGN;
   return launched(launch_quantize(x, x_dtype == NVFP4_DTYPE_BF16, M, K, gsa, codes, scales,
                                   (hipStream_t)stream));
+}
+
+NVFP4_API int nvfp4_amax_quantize(const void* x, int x_dtype, int64_t M, int64_t K, float* gsa,
+                                  uint8_t* codes, uint8_t* scales, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (!dtype_ok(x_dtype)) return NVFP4_ERR_DTYPE;
+  if (M < 0 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (M > 0 && (M * (K / 16) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (gsa == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned(gsa, 4)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (M == 0)  // the amax of nothing: the 1e-8 floor
+    return launched(launch_amax_finalize(nullptr, 0, gsa, s));
+  if (x == nullptr || codes == nullptr || scales == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_ERR_ALIGN;
+  const bool bf16 = x_dtype == NVFP4_DTYPE_BF16;
+  if (amax_quantize_small_ok(M, K))  // one workgroup: amax, gsa and codes in one kernel
+    return launched(launch_amax_quantize_small(x, bf16, M, K, gsa, codes, scales, s));
+  const size_t need = amax_ws_bytes(M * K);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+  }
+  const hipError_t e = launch_amax_gsa(x, bf16, M * K, gsa, ws, s);
+  if (e != hipSuccess) return launched(e);
+  return launched(launch_quantize(x, bf16, M, K, gsa, codes, scales, s));
 }
 
 NVFP4_API int nvfp4_rmsnorm_quantize(const void* x, int x_dtype, const void* norm_weight,
@@ -254,12 +280,17 @@ NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* 
   if (N > 0 && gemv_run_supported(M, K, x, w_codes, w_scales))
     return launched(launch_gemv_run(x, xbf, gsa, codes, scales, w_codes, w_scales, ws2, y, ybf, M,
                                     N, K, s));
-  // general case: the three steps as separate kernels
-  const size_t need = amax_ws_bytes(M * K);
-  if (need > 0 && (ws == nullptr || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
-  if (need > 0 && !aligned(ws, 4)) return NVFP4_ERR_ALIGN;
-  hipError_t e = launch_amax_gsa(x, xbf, M * K, gsa, ws, s);
-  if (e == hipSuccess) e = launch_quantize(x, xbf, M, K, gsa, codes, scales, s);
+  // general case: steps 1-2 (one kernel for a small activation), then step 3
+  hipError_t e = hipSuccess;
+  if (amax_quantize_small_ok(M, K)) {
+    e = launch_amax_quantize_small(x, xbf, M, K, gsa, codes, scales, s);
+  } else {
+    const size_t need = amax_ws_bytes(M * K);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+    e = launch_amax_gsa(x, xbf, M * K, gsa, ws, s);
+    if (e == hipSuccess) e = launch_quantize(x, xbf, M, K, gsa, codes, scales, s);
+  }
   if (e == hipSuccess && N > 0) {
     if (M <= GEMV_MAX_M)
       e = launch_gemv(codes, scales, gsa, w_codes, w_scales, ws2, y, ybf, M, N, K, s);

@@ -77,8 +77,7 @@ class Nvfp4Linear:
 
     def quantize(self, x: torch.Tensor, stream=None):
         M = x.shape[0]
-        C.nvfp4_amax_gsa(x, self.gsa, self.ws, stream)
-        C.nvfp4_quantize_from_buffer(x, self.gsa, self.codes[:M], self.scales[:M], stream)
+        C.nvfp4_amax_quantize(x, self.gsa, self.codes[:M], self.scales[:M], self.ws, stream)
         return self.codes[:M], self.scales[:M], self.gsa
 
     def run_from_quantized(self, codes, scales, gsa, stream=None,
@@ -212,8 +211,7 @@ class Nvfp4MoE:
     def forward(self, x, row_index, offsets, stream=None) -> torch.Tensor:
         T, P = x.shape[0], row_index.shape[0]
         xc, xs = self.x_codes[:T], self.x_scales[:T]
-        C.nvfp4_amax_gsa(x, self.gsa1, self.ws, stream)
-        C.nvfp4_quantize_from_buffer(x, self.gsa1, xc, xs, stream)
+        C.nvfp4_amax_quantize(x, self.gsa1, xc, xs, self.ws, stream)
         h = self.h[:P]
         if self.fused:
             C.nvfp4_grouped_linear_swiglu(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,

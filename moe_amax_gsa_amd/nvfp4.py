@@ -64,6 +64,8 @@ lib.nvfp4_linear_run.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _
 lib.nvfp4_grouped_linear.restype = _I
 lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
                                      _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_amax_quantize.restype = _I
+lib.nvfp4_amax_quantize.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]
 lib.nvfp4_rmsnorm_quantize.restype = _I
 lib.nvfp4_rmsnorm_quantize.argtypes = [_P, _I, _P, _I, ctypes.c_float, _I64, _I64, _I, _P, _P,
                                        _P, _P, _P, _SZ, _P]
@@ -204,6 +206,17 @@ def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: tor
                                     _dtype(y), N, K, _ptr(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)), "nvfp4_grouped_linear")
+
+
+def nvfp4_amax_quantize(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
+                        scales: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """Steps 1 and 2: gsa, codes (M, K/2), scales (M, K/16) of x (M, K)."""
+    M, K = x.shape
+    _check(lib.nvfp4_amax_quantize(_ptr(x), _dtype(x), M, K, _ptr(gsa), _ptr(codes),
+                                   _ptr(scales), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(stream)), "nvfp4_amax_quantize")
 
 
 def nvfp4_rmsnorm_quantize(x: torch.Tensor, norm_weight: torch.Tensor, gsa: torch.Tensor,

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(C):
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert C.nvfp4_abi_version() == 4
+    assert C.nvfp4_abi_version() == 5
 
 
 def test_status_strings(C):
@@ -135,3 +135,17 @@ def test_linear_workspace_is_optional_and_sized_by_shape(C):
     assert n > 0 and n % (64 * 96 * 4) == 0
     r = C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, 64, 96, 1024)
     assert r == 64 * 96 * 4 + n
+
+
+def test_validation_of_amax_quantize(C):
+    L = C.lib
+    fake = ctypes.c_void_p(4096)
+    aq = L.nvfp4_amax_quantize
+    assert aq(fake, 2, 4, 32, fake, fake, fake, None, 0, None) == -3     # dtype
+    assert aq(fake, 0, 4, 40, fake, fake, fake, None, 0, None) == -2     # K % 16
+    assert aq(fake, 0, -1, 32, fake, fake, fake, None, 0, None) == -2    # M < 0
+    assert aq(fake, 0, 4, 32, None, fake, fake, None, 0, None) == -1     # gsa
+    assert aq(None, 0, 4, 32, fake, fake, fake, None, 0, None) == -1     # x
+    assert aq(ctypes.c_void_p(4104), 0, 4, 32, fake, fake, fake, None, 0, None) == -5
+    # beyond one workgroup the two-phase amax needs its workspace
+    assert aq(fake, 0, 1024, 1024, fake, fake, fake, None, 0, None) == -4

@@ -133,6 +133,40 @@ def test_quantize_bitexact(C, M, K, dist, dtype):
     assert np.array_equal(codes.cpu().numpy(), oc)
 
 
+AMAXQ_CASES = [
+    (1, 256, "bf16"), (1, 7168, "bf16"), (3, 4096, "fp32"), (9, 3072, "bf16"),
+    (16, 4096, "bf16"),                       # one workgroup, 1 .. 8 half-blocks a thread
+    (17, 4096, "bf16"), (512, 7168, "fp32"),  # two-phase amax, then the quantize
+]
+
+
+@pytest.mark.parametrize("M,K,dtype", AMAXQ_CASES)
+def test_amax_quantize_bitexact(C, M, K, dtype):
+    """nvfp4_amax_quantize: gsa, codes and scales bit-exact with the oracle's
+    amax -> gsa -> quantize, on both of its paths."""
+    say("amax_quantize", M, K, dtype)
+    inp = W.make_linear(M, K, 16, seed=M * 3 + K, x="outliers")
+    xd = x_dev(inp.x, dtype)
+    gsa = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    ws = torch.full((max(16, C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, M * K)),), 0xAB,
+                    dtype=torch.uint8, device=DEV)
+    C.nvfp4_amax_quantize(xd, gsa, codes, scales, ws)
+    g = oracle.amax_gsa(x_host(inp.x, dtype))
+    assert f32(gsa) == g
+    oc, os_ = oracle.quantize(x_host(inp.x, dtype), g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+
+
+def test_amax_quantize_empty(C):
+    gsa = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    e = torch.empty(0, 32, dtype=torch.uint8, device=DEV)
+    C.nvfp4_amax_quantize(x, gsa, e, e[:, :4])
+    assert f32(gsa) == oracle.gsa_from_amax(0.0)
+
+
 def test_quantize_small_gsa_saturates(C):
     """A caller gsa far too small (the pages' input_scale bug) saturates
     block scales at 448 on both sides."""
