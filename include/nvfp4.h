@@ -310,14 +310,22 @@ int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_in
  * otherwise; then call the three functions above).
  * ws: nvfp4_workspace_bytes(NVFP4_OP_GROUPED_SWIGLU, 0, N_inter, 0, G)
  * bytes, 4-byte aligned, overwritten.
+ * h_codes (M_total, N_inter/4) and h_scales (M_total, N_inter/32), both or
+ * neither (NULL): also step 2 on h with gsa_h, as
+ *   nvfp4_quantize_from_buffer(h, FP32, M_total, N_inter/2, gsa_h, ...)
+ * writes it -- every row of h, including rows left unwritten above (they
+ * carry whatever h held) -- the pages' fused de-interleave + amax +
+ * quantize.  With at most 2048 amax partials each quantize workgroup
+ * reduces them itself, so the second amax phase and the quantize are one
+ * kernel.  Needs (N_inter/2) % 16 == 0; h_codes 8-byte aligned.
  * M_total == 0 or N_inter == 0 only writes gsa_h (the 1e-8 floor). */
 int nvfp4_grouped_linear_swiglu(const uint8_t *a_codes, const uint8_t *a_scales,
                                 const float *gsa, int64_t a_rows, const int32_t *row_index,
                                 const int32_t *group_offsets, int G, int64_t M_total,
                                 const uint8_t *w_codes, const uint8_t *w_scales,
-                                const float *ws2, float *h, float *gsa_h, int64_t N_inter,
-                                int64_t K, int granularity, void *ws, size_t ws_bytes,
-                                void *stream);
+                                const float *ws2, float *h, float *gsa_h, uint8_t *h_codes,
+                                uint8_t *h_scales, int64_t N_inter, int64_t K, int granularity,
+                                void *ws, size_t ws_bytes, void *stream);
 
 /* Static name of a status code. */
 const char *nvfp4_status_string(int status);

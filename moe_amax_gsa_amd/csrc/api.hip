@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 5; }
+NVFP4_API int nvfp4_abi_version(void) { return 6; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -332,9 +332,9 @@ NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t*
                                           const int32_t* row_index, const int32_t* group_offsets,
                                           int G, int64_t M_total, const uint8_t* w_codes,
                                           const uint8_t* w_scales, const float* ws2, float* h,
-                                          float* gsa_h, int64_t N_inter, int64_t K,
-                                          int granularity, void* ws, size_t ws_bytes,
-                                          void* stream) {
+                                          float* gsa_h, uint8_t* h_codes, uint8_t* h_scales,
+                                          int64_t N_inter, int64_t K, int granularity, void* ws,
+                                          size_t ws_bytes, void* stream) {
   int st = check_gemm_shape(M_total, N_inter, K);
   if (st != NVFP4_OK) return st;
   if (G < 1 || G > 65535 || a_rows < 0 || a_rows > I32_MAX) return NVFP4_ERR_SHAPE;
@@ -342,6 +342,9 @@ NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t*
   if (granularity < 1 || N_inter % (2 * (int64_t)granularity) != 0) return NVFP4_ERR_SHAPE;
   if (gsa_h == nullptr) return NVFP4_ERR_NULL;
   if (!aligned(gsa_h, 4)) return NVFP4_ERR_ALIGN;
+  if ((h_codes == nullptr) != (h_scales == nullptr)) return NVFP4_ERR_NULL;  // both or neither
+  if (h_codes != nullptr && (N_inter / 2) % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (h_codes != nullptr && !aligned(h_codes, 8)) return NVFP4_ERR_ALIGN;
   if (M_total == 0 || N_inter == 0)  // the amax of nothing: gsa_h from the 1e-8 floor
     return launched(launch_amax_finalize(nullptr, 0, gsa_h, (hipStream_t)stream));
   if (a_rows == 0) return NVFP4_ERR_SHAPE;
@@ -359,7 +362,8 @@ NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t*
   if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
   return launched(launch_grouped_swiglu(a_codes, a_scales, gsa, a_rows, row_index, group_offsets,
                                         G, M_total, w_codes, w_scales, ws2, h, gsa_h, N_inter, K,
-                                        granularity, (uint32_t*)ws, (hipStream_t)stream));
+                                        granularity, (uint32_t*)ws, h_codes, h_scales,
+                                        (hipStream_t)stream));
 }
 
 NVFP4_API int nvfp4_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t N_inter,

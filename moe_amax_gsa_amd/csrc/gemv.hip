@@ -1131,6 +1131,9 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
 
 int64_t grouped_swiglu_parts(int64_t N, int G) { return ring_max_parts(N, G); }
 
+// Most amax partials a quantize workgroup reduces by itself (8 KB of reads).
+constexpr int64_t SWIGLU_INLINE_PARTS = 2048;
+
 bool grouped_swiglu_supported(int64_t N, int64_t K, int gran, int64_t a_rows,
                               const uint8_t* a_codes, const uint8_t* a_scales,
                               const uint8_t* w_codes, const uint8_t* w_scales) {
@@ -1146,7 +1149,8 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
                                  const int32_t* offsets, int G, int64_t M_total,
                                  const uint8_t* w_codes, const uint8_t* w_scales,
                                  const float* ws2, float* h, float* gsa_h, int64_t N, int64_t K,
-                                 int gran, uint32_t* partials, hipStream_t s) {
+                                 int gran, uint32_t* partials, uint8_t* h_codes,
+                                 uint8_t* h_scales, hipStream_t s) {
   GemvArgs a{};
   a.a_codes = a_codes;
   a.a_scales = a_scales;
@@ -1169,7 +1173,15 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
   int64_t parts = 0;
   if (!launch_ring<true>(a, G, mean_rows, s, &err, &parts)) return hipErrorInvalidValue;
   if (err != hipSuccess) return err;
-  return launch_amax_finalize(partials, parts, gsa_h, s);
+  if (h_codes == nullptr) return launch_amax_finalize(partials, parts, gsa_h, s);
+  // h's quantize as well: with few partials each quantize workgroup reduces
+  // them itself (one launch), else the finalize runs first
+  if (parts <= SWIGLU_INLINE_PARTS)
+    return launch_quantize_finalize(h, M_total, N / 2, partials, parts, gsa_h, h_codes, h_scales,
+                                    s);
+  err = launch_amax_finalize(partials, parts, gsa_h, s);
+  if (err != hipSuccess) return err;
+  return launch_quantize(h, false, M_total, N / 2, gsa_h, h_codes, h_scales, s);
 }
 
 bool gemv_run_supported(int64_t M, int64_t K, const void* x, const uint8_t* w_codes,

@@ -61,6 +61,13 @@ hipError_t launch_router_topk(const float* src, int nsrc, const float* gsa, cons
                               float* logits, const float* bias, int64_t M, int64_t N, int k,
                               int32_t* idx, float* score, hipStream_t s);
 
+// Phase 2 of an amax over partials fused into the quantize of fp32 x (M, K):
+// every workgroup reduces the partials itself (keep nparts small), workgroup
+// 0 writes gsa.
+hipError_t launch_quantize_finalize(const float* x, int64_t M, int64_t K,
+                                    const uint32_t* partials, int64_t nparts, float* gsa,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // Phase 2 of an amax over partials (bits of non-negative fp32 maxima): gsa.
 hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float* gsa,
                                 hipStream_t s);
@@ -93,7 +100,8 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
                                  const int32_t* offsets, int G, int64_t M_total,
                                  const uint8_t* w_codes, const uint8_t* w_scales,
                                  const float* ws2, float* h, float* gsa_h, int64_t N, int64_t K,
-                                 int gran, uint32_t* partials, hipStream_t s);
+                                 int gran, uint32_t* partials, uint8_t* h_codes,
+                                 uint8_t* h_scales, hipStream_t s);
 
 // amax -> gsa -> quantize -> linear in one kernel for a few activation rows.
 constexpr int64_t GEMV_RUN_MAX_M = 16;

@@ -115,16 +115,29 @@ hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, 
 // exchange their maxima with one shuffle.  Row-major (M, K) with K % 16 == 0
 // makes half-block h start at element 8h, its 4 code bytes at byte 4h and
 // its block's scale at byte h/2.
-template <bool BF16>
+// FINALIZE: gsa is not read but formed -- every workgroup reduces the
+// nparts amax partials (bits of non-negative fp32 maxima) itself, the second
+// amax phase, and workgroup 0 writes it to gsa_p[0].
+template <bool BF16, bool FINALIZE = false>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t nhalf,
-                                                       const float* __restrict__ gsa_p,
+                                                       float* __restrict__ gsa_p,
                                                        uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales,
+                                                       const uint32_t* __restrict__ partials,
+                                                       int nparts) {
   const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool ok = h < nhalf;  // nhalf is even, so both lanes of a block agree
   float v[8];
   load_half8<BF16>(x, ok ? h : 0, v);
-  const float gsa = gsa_p[0];
+  float gsa;
+  if (FINALIZE) {
+    uint32_t mb = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) mb = max(mb, partials[i]);
+    gsa = gsa_from_amax(__uint_as_float(block_max_u32<256>(mb)));
+    if (blockIdx.x == 0 && threadIdx.x == 0) gsa_p[0] = gsa;
+  } else {
+    gsa = gsa_p[0];
+  }
   float m = half_absmax8(v);
   m = fmaxf(m, xor1_f32(m));
   uint32_t c, sf;
@@ -140,10 +153,22 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
   const int64_t nhalf = M * (K / 8);
   if (nhalf == 0) return hipSuccess;
   const int64_t grid = (nhalf + 255) / 256;
+  float* g = const_cast<float*>(gsa);  // read only: FINALIZE is off
   if (bf16)
-    quantize_kernel<true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales);
+    quantize_kernel<true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, g, codes, scales, nullptr, 0);
   else
-    quantize_kernel<false><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales);
+    quantize_kernel<false><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, g, codes, scales, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_finalize(const float* x, int64_t M, int64_t K,
+                                    const uint32_t* partials, int64_t nparts, float* gsa,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t nhalf = M * (K / 8);
+  if (nhalf == 0) return launch_amax_finalize(partials, nparts, gsa, s);
+  const int64_t grid = (nhalf + 255) / 256;
+  quantize_kernel<false, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
+                                                              partials, (int)nparts);
   return hipGetLastError();
 }
 

@@ -213,18 +213,19 @@ class Nvfp4MoE:
         xc, xs = self.x_codes[:T], self.x_scales[:T]
         C.nvfp4_amax_quantize(x, self.gsa1, xc, xs, self.ws, stream)
         h = self.h[:P]
-        if self.fused:
+        hc, hs = self.h_codes[:P], self.h_scales[:P]
+        if self.fused:  # SwiGLU, amax and h's quantize with the gate/up projection
             C.nvfp4_grouped_linear_swiglu(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
                                           self.w1_scales, self.w1_ws2, h, self.gsa2,
-                                          self.granularity, self.ws_swiglu, stream)
+                                          self.granularity, self.ws_swiglu, stream,
+                                          h_codes=hc, h_scales=hs)
         else:
             y1 = self.y1[:P]
             C.nvfp4_grouped_linear(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
                                    self.w1_scales, self.w1_ws2, y1, None, stream)
             C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream)
             C.nvfp4_amax_gsa(h, self.gsa2, self.ws, stream)
-        hc, hs = self.h_codes[:P], self.h_scales[:P]
-        C.nvfp4_quantize_from_buffer(h, self.gsa2, hc, hs, stream)
+            C.nvfp4_quantize_from_buffer(h, self.gsa2, hc, hs, stream)
         y2 = self.y2[:P]
         C.nvfp4_grouped_linear(hc, hs, self.gsa2, None, offsets, self.w2_codes, self.w2_scales,
                                self.w2_ws2, y2, None, stream)

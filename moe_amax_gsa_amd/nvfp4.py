@@ -73,7 +73,7 @@ lib.nvfp4_quantize_weight.restype = _I
 lib.nvfp4_quantize_weight.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]
 lib.nvfp4_grouped_linear_swiglu.restype = _I
 lib.nvfp4_grouped_linear_swiglu.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P,
-                                            _P, _I64, _I64, _I, _P, _SZ, _P]
+                                            _P, _P, _P, _I64, _I64, _I, _P, _SZ, _P]
 lib.nvfp4_swiglu_deinterleave.restype = _I
 lib.nvfp4_swiglu_deinterleave.argtypes = [_P, _P, _I64, _I64, _I, _P]
 
@@ -248,16 +248,19 @@ def nvfp4_grouped_linear_swiglu(a_codes: torch.Tensor, a_scales: torch.Tensor, g
                                 row_index: Optional[torch.Tensor], group_offsets: torch.Tensor,
                                 w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
                                 h: torch.Tensor, gsa_h: torch.Tensor, granularity: int,
-                                ws: torch.Tensor, stream=None) -> None:
+                                ws: torch.Tensor, stream=None,
+                                h_codes: Optional[torch.Tensor] = None,
+                                h_scales: Optional[torch.Tensor] = None) -> None:
     """w_codes (G, N_inter, K/2), w_scales (G, N_inter, K/16), ws2 (G,);
-    h (M_total, N_inter/2) fp32 and gsa_h (1,) fp32 are written."""
+    h (M_total, N_inter/2) fp32 and gsa_h (1,) fp32 are written, and with
+    h_codes / h_scales also h's codes and scales."""
     G, NI = w_codes.shape[0], w_codes.shape[1]
     K = w_codes.shape[2] * 2
     _check(lib.nvfp4_grouped_linear_swiglu(
         _ptr(a_codes), _ptr(a_scales), _ptr(gsa), a_codes.shape[0], _ptr(row_index),
         _ptr(group_offsets), G, h.shape[0], _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(h),
-        _ptr(gsa_h), NI, K, granularity, _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(stream)), "nvfp4_grouped_linear_swiglu")
+        _ptr(gsa_h), _ptr(h_codes), _ptr(h_scales), NI, K, granularity, _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "nvfp4_grouped_linear_swiglu")
 
 
 def nvfp4_swiglu_deinterleave(l1: torch.Tensor, h: torch.Tensor, granularity: int = 8,

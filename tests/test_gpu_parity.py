@@ -574,7 +574,10 @@ def test_grouped_swiglu_matches_unfused(C, K, N, gran):
     g1 = torch.zeros(1, dtype=torch.float32, device=DEV)
     ws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, 0, N, 0, G), 16),
                      dtype=torch.uint8, device=DEV)
-    C.nvfp4_grouped_linear_swiglu(ac, asf, gsa, ri, off, wc, wsf, ws2, h1, g1, gran, ws)
+    hc1 = torch.full((P, N // 4), 0x5A, dtype=torch.uint8, device=DEV)
+    hs1 = torch.full((P, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_swiglu(ac, asf, gsa, ri, off, wc, wsf, ws2, h1, g1, gran, ws,
+                                  h_codes=hc1, h_scales=hs1)
     # unfused
     l1 = torch.zeros(P, N, dtype=torch.float32, device=DEV)
     h2 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
@@ -584,11 +587,14 @@ def test_grouped_swiglu_matches_unfused(C, K, N, gran):
     aws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, P * N // 2), 16),
                       dtype=torch.uint8, device=DEV)
     C.nvfp4_amax_gsa(h2, g2, aws)
+    hc2, hs2 = gpu_quantize(C, h2, g2)
     torch.cuda.synchronize()
     a, b = h1.cpu().numpy(), h2.cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert f32(g1) == f32(g2)
     assert np.all(a[[4, 10]] == 0.0)  # invalid row indices: unwritten
+    # h's quantize in the same call (the partials reduced by the quantize)
+    assert torch.equal(hc1, hc2) and torch.equal(hs1, hs2)
 
 
 @pytest.mark.parametrize("G,rows", [(64, {0: 1, 17: 2, 63: 1}), (100, {5: 3, 6: 1, 99: 2}),
@@ -628,15 +634,53 @@ def test_grouped_sparse_groups(C, G, rows):
     g1 = torch.zeros(1, dtype=torch.float32, device=DEV)
     ws = torch.full((max(C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, 0, N, 0, G), 16),), 0xAB,
                     dtype=torch.uint8, device=DEV)
+    hc1 = torch.full((P, N // 4), 0x5A, dtype=torch.uint8, device=DEV)
+    hs1 = torch.full((P, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
     C.nvfp4_grouped_linear_swiglu(d["ac"], d["asf"], d["gsa"], d["ri"], d["off"], d["wc"],
-                                  d["wsf"], d["ws2"], h1, g1, gran, ws)
+                                  d["wsf"], d["ws2"], h1, g1, gran, ws, h_codes=hc1, h_scales=hs1)
     h2 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
     g2 = torch.zeros(1, dtype=torch.float32, device=DEV)
     C.nvfp4_swiglu_deinterleave(y, h2, gran)
     C.nvfp4_amax_gsa(h2, g2, None)
+    hc2, hs2 = gpu_quantize(C, h2, g2)
     torch.cuda.synchronize()
     assert np.array_equal(h1.cpu().numpy().view(np.uint32), h2.cpu().numpy().view(np.uint32))
     assert f32(g1) == f32(g2)
+    assert torch.equal(hc1, hc2) and torch.equal(hs1, hs2)
+
+
+def test_grouped_swiglu_quantize_many_partials(C):
+    """More amax partials than one quantize workgroup reduces (128 groups x
+    17 workgroups of 128 columns = 2176): the finalize runs as its own kernel
+    before h's quantize.  h's codes and scales against the oracle's quantize
+    of the GPU's h."""
+    K, N, gran, G = 256, 2112, 8, 128
+    say("grouped swiglu quantize, 2176 partials")
+    rng = np.random.default_rng(5)
+    sizes = rng.integers(1, 4, G)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    P = int(offsets[-1])
+    a_rows = 5
+    row_index = rng.integers(0, a_rows, P).astype(np.int32)
+    ac = to_dev(rng.integers(0, 256, (a_rows, K // 2), dtype=np.uint8))
+    asf = to_dev(rng.integers(0x20, 0x48, (a_rows, K // 16), dtype=np.uint8))
+    wc = to_dev(rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8))
+    wsf = to_dev(rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8))
+    ws2 = to_dev(rng.uniform(0.002, 0.01, G).astype(np.float32))
+    gsa = to_dev(np.array([0.37], np.float32))
+    nws = C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, 0, N, 0, G)
+    assert nws >= 2176 * 4
+    ws = torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV)
+    h = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
+    gh = torch.zeros(1, dtype=torch.float32, device=DEV)
+    hc = torch.full((P, N // 4), 0x5A, dtype=torch.uint8, device=DEV)
+    hs = torch.full((P, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_swiglu(ac, asf, gsa, to_dev(row_index), to_dev(offsets), wc, wsf, ws2,
+                                  h, gh, gran, ws, h_codes=hc, h_scales=hs)
+    hh = h.cpu().numpy()
+    assert f32(gh) == oracle.amax_gsa(hh)
+    oc, os_ = oracle.quantize(hh, f32(gh))
+    assert np.array_equal(hc.cpu().numpy(), oc) and np.array_equal(hs.cpu().numpy(), os_)
 
 
 def test_grouped_row_index_bounds(C):
