@@ -209,19 +209,26 @@ class Nvfp4MoE:
         self.y2 = torch.empty(max_pairs, self.N2, dtype=torch.float32, device=dev)
 
     def forward(self, x, row_index, offsets, stream=None) -> torch.Tensor:
-        T, P = x.shape[0], row_index.shape[0]
+        T = x.shape[0]
         xc, xs = self.x_codes[:T], self.x_scales[:T]
         C.nvfp4_amax_quantize(x, self.gsa1, xc, xs, self.ws, stream)
+        return self.forward_quantized(xc, xs, self.gsa1, row_index, offsets, stream)
+
+    def forward_quantized(self, xc, xs, gsa, row_index, offsets, stream=None) -> torch.Tensor:
+        """The expert pair on an already quantized activation (codes (T, K1/2),
+        scales (T, K1/16), one device gsa) -- e.g. nvfp4_rmsnorm_quantize's
+        output, which the router consumes too."""
+        P = row_index.shape[0]
         h = self.h[:P]
         hc, hs = self.h_codes[:P], self.h_scales[:P]
         if self.fused:  # SwiGLU, amax and h's quantize with the gate/up projection
-            C.nvfp4_grouped_linear_swiglu(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
+            C.nvfp4_grouped_linear_swiglu(xc, xs, gsa, row_index, offsets, self.w1_codes,
                                           self.w1_scales, self.w1_ws2, h, self.gsa2,
                                           self.granularity, self.ws_swiglu, stream,
                                           h_codes=hc, h_scales=hs)
         else:
             y1 = self.y1[:P]
-            C.nvfp4_grouped_linear(xc, xs, self.gsa1, row_index, offsets, self.w1_codes,
+            C.nvfp4_grouped_linear(xc, xs, gsa, row_index, offsets, self.w1_codes,
                                    self.w1_scales, self.w1_ws2, y1, None, stream)
             C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream)
             C.nvfp4_amax_gsa(h, self.gsa2, self.ws, stream)

@@ -531,6 +531,25 @@ def test_quantize_weight(C, N, K):
     assert rel_err(y, ref) <= REL_TOL
 
 
+def test_moe_forward_quantized_matches_forward(C):
+    """Nvfp4MoE.forward_quantized on the codes that forward itself made
+    gives the same output bits."""
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
+    say("moe forward_quantized")
+    moe = moe_small()
+    w = W.moe_weights_to(moe, DEV)
+    P = int(moe.offsets[-1])
+    layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=moe.granularity)
+    x = W.bf16_to_torch(moe.x, DEV)
+    ri = torch.from_numpy(moe.pair_token).to(DEV)
+    off = torch.from_numpy(moe.offsets).to(DEV)
+    y1 = layer(x, ri, off).clone()
+    xc, xs = layer.x_codes[:moe.T].clone(), layer.x_scales[:moe.T].clone()
+    g = layer.gsa1.clone()
+    y2 = layer.forward_quantized(xc, xs, g, ri, off)
+    assert torch.equal(y1, y2)
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 def test_moe_small_stepwise(C, fused):
     say("moe small", fused)
