@@ -28,18 +28,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// E4M3 encode of v >= 0: round to nearest even on the E4M3 grid, values
-// above 448 saturate to 448 (0x7E).  Below 2^-6 the grid is uniform with
-// step 2^-9, so the code is rint(v * 512); above it the fp32 mantissa is
-// rounded to 3 bits at bit 20 and the exponent rebased from 127 to 7.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  v = fminf(v, 448.0f);
-  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  return (u >> 20) - ((127u - 7u) << 3);
-}
-
 // E4M3 decode of a non-negative finite code (0..0x7E) to float.
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   uint32_t e = c >> 3, m = c & 7u;
@@ -48,28 +36,14 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return e == 0 ? sub : nrm;
 }
 
-// E2M1 magnitude index of q >= 0: nearest of {0,.5,1,1.5,2,3,4,6}, ties to
-// the even mantissa bit, beyond 6 -> 6.  Below 1 the grid is uniform with
-// step 1/2, so the index is rint(2q) (0, 1 or 2; rint ties to even).  From
-// 1 up it is a float with one mantissa bit: round the fp32 mantissa to one
-// bit at bit 22 (ties to even), then index = 2 + 2*exponent + mantissa bit,
-// saturated at 7.  Equal to the midpoint-threshold form for every fp32 q >= 0.
-__device__ __forceinline__ uint32_t e2m1_magnitude(float q) {
-  if (q < 1.0f) return (uint32_t)__builtin_rintf(q * 2.0f);
-  uint32_t u = __float_as_uint(q);
-  u += 0x1FFFFFu + ((u >> 22) & 1u);
-  const uint32_t mag = 2u + 2u * ((u >> 23) - 127u) + ((u >> 22) & 1u);
-  return mag < 7u ? mag : 7u;
-}
-
-// gfx950's converters give the same codes as the two encoders above:
+// gfx950's converters round as the scale convention asks:
 // v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds fp32 to E2M1 to nearest,
 // ties to even, saturating at 6, keeping the sign (-0 -> 0x8); it packs
 // its two inputs into one byte, the first in the low nibble.
 // v_cvt_scalef32_pk_fp8_f32 with scale 1 rounds to E4M3 to nearest even
-// (NaN above 448, so the input is clamped first).  Both were compared with
-// the encoders above on every input they see here (every non-negative
-// finite fp32; every fp32 in [0, 448]).
+// (NaN above 448, so the input is clamped first).  Both were compared on
+// the device with bit-level round-to-nearest-even encoders on every input
+// they see here (every non-negative finite fp32; every fp32 in [0, 448]).
 typedef short short2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t e4m3_encode_hw(float v) {
@@ -401,14 +375,6 @@ __device__ __forceinline__ void quantize_half8(const float v[8], float bamax, fl
   const float sdec = e4m3_decode(sf);
   const float sc = sdec * gsa;
   codes = sdec == 0.0f ? e2m1_signs8(v) : e2m1_codes8(v, sc);
-}
-
-template <bool BF16>
-__device__ __forceinline__ void quantize_block16(const void* __restrict__ x, int64_t b, float gsa,
-                                                 uint32_t& lo, uint32_t& hi, uint32_t& sf) {
-  float v[16];
-  load_block16<BF16>(x, b, v);
-  quantize_vals16(v, gsa, lo, hi, sf);
 }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
