@@ -751,12 +751,21 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
   }
 
   const int64_t nhalf = (int64_t)M * (K / 8);
+  // One activation row with one set group per wave (HPT == S, NW * S sets
+  // cover the row): lane l of wave w quantizes half-block l of sets S w ..
+  // S w + S - 1 -- exactly the sets the wave multiplies, so the wave needs
+  // no other wave's codes.  Otherwise half-blocks go round the workgroup.
+  const bool own_sets = RUN && M == 1 && HPT == S && NW * S >= nset;
+  auto half_of = [&](int u) -> int64_t {
+    return own_sets ? (int64_t)(lane + 64 * (S * wave + u))
+                    : (int64_t)threadIdx.x + (int64_t)u * blockDim.x;
+  };
   uint4 xr[HPT][2];
   bool xok[HPT];
   if (RUN) {  // the activation first: its loads complete before the weights'
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
-      const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
+      const int64_t h = half_of(u);
       xok[u] = h < nhalf;
       load_half8_raw<XBF16>(args.x, xok[u] ? h : 0, xr[u]);
     }
@@ -805,7 +814,7 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
     const bool writer = blockIdx.x == 0;
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
-      const int64_t h = threadIdx.x + (int64_t)u * blockDim.x;
+      const int64_t h = half_of(u);
       float bm = xok[u] ? half_absmax8(xv[u]) : 0.f;
       bm = fmaxf(bm, xor1_f32(bm));
       uint32_t c, sf;
@@ -820,12 +829,9 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
       }
     }
     if (writer && threadIdx.x == 0) args.gsa_out[0] = gsa_v;
-    // One row, one 512-element set per wave and as many waves as sets: wave
-    // w quantized exactly set w (its threads own elements 512w .. 512w+511),
-    // the only set it multiplies, and a wave's LDS operations complete in
-    // order, so no other wave needs to be waited for.
-    const bool own_set = M == 1 && S == 1 && HPT == 1 && NW == nset;
-    if (!own_set) lds_barrier();
+    // With own_sets a wave quantized exactly the sets it multiplies and a
+    // wave's LDS operations complete in order: no other wave is waited for.
+    if (!own_sets) lds_barrier();
   }
 
   float acc[MR][RQ];
@@ -1047,12 +1053,25 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
   a.a_rows = (int)M;
   const int64_t nhalf = M * (K / 8);
   const bool one = M <= 1;
+  const size_t lds = (size_t)(M * (K / 2 + K / 16));
+  if (one && K >= 1024) {
+    // two 512-element sets per wave, each wave quantizing its own two:
+    // half the waves of one set each, and no barrier after the quantize
+    const int nw2 = narrow_waves(K, 2, NARROW_MAXW1);
+    dim3 grid((unsigned)((a.N + 4 * NARROW_RQ - 1) / (4 * NARROW_RQ)));
+    if (x_bf16)
+      gemv_narrow_kernel<2, 1, true, true, 2, NARROW_RQ, NARROW_MAXW1>
+          <<<grid, nw2 * 64, lds, s>>>(a);
+    else
+      gemv_narrow_kernel<2, 1, true, false, 2, NARROW_RQ, NARROW_MAXW1>
+          <<<grid, nw2 * 64, lds, s>>>(a);
+    return hipGetLastError();
+  }
   const int maxw = one ? NARROW_MAXW1 : GEMV_MAX_WAVES;
   int nw = narrow_waves(K, one ? 1 : 2, maxw);
   while ((int64_t)nw * 64 * 4 < nhalf && nw < maxw) ++nw;
   const int64_t per = ((int64_t)nw * 64);
   const int hpt = nhalf <= per ? 1 : (nhalf <= 2 * per ? 2 : 4);
-  const size_t lds = (size_t)(M * (K / 2 + K / 16));
   if (x_bf16) {
     if (one) return launch_narrow_run_t<1, 1, true, NARROW_MAXW1>(a, nw, hpt, lds, s);
     if (M <= 2) return launch_narrow_run_t<2, 2, true, GEMV_MAX_WAVES>(a, nw, hpt, lds, s);
