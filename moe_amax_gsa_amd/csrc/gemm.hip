@@ -46,16 +46,17 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t sf) {
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Both E4M3 scale bytes of a fragment's two blocks (low byte first) as f16.
+// Both E4M3 scale bytes of a fragment's two blocks (low byte first) as f16,
+// in one conversion (every E4M3FN value is an f16 value).
 __device__ __forceinline__ half2_t scale_pair2(uint32_t two) {
-  const _Float16 f0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)two, 0);
-  const _Float16 f1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)two, 1);
-  return half2_t{f0, f1};
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two, 1.0f, false);
 }
 
-__device__ __forceinline__ half2_t scale_pair(uint32_t byte) {
-  const _Float16 f = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
-  return half2_t{f, f};
+// {s[I], s[I]}: the packed multiply selects the half through its operand
+// selectors, so this costs no instruction.
+template <int I>
+__device__ __forceinline__ half2_t splat(half2_t s) {
+  return __builtin_shufflevector(s, s, I, I);
 }
 
 // 16 code bytes and 2 scale bytes of one fragment row for K step ks.
@@ -124,8 +125,9 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(
     half8_t A[2][4], B[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const half2_t fa0 = scale_pair(sa[i] & 0xFFu), fa1 = scale_pair(sa[i] >> 8);
-      const half2_t fb0 = scale_pair(sb[i] & 0xFFu), fb1 = scale_pair(sb[i] >> 8);
+      const half2_t pa = scale_pair2(sa[i]), pb = scale_pair2(sb[i]);
+      const half2_t fa0 = splat<0>(pa), fa1 = splat<1>(pa);
+      const half2_t fb0 = splat<0>(pb), fb1 = splat<1>(pb);
       A[i][0] = dequant8(ca[i].x, fa0);
       A[i][1] = dequant8(ca[i].y, fa0);
       A[i][2] = dequant8(ca[i].z, fa1);
@@ -235,20 +237,23 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // code loads 0 .. NA-1 read A rows, the rest W rows; load i fills LDS at
   // stage + 1024 (KW i + wave)
   constexpr int NA = TM / (T::RPL * KW), NB = T::CODE_LOADS - NA;
+  // The chunk advances the (uniform) base pointers; the per-lane offsets
+  // stay as computed above, so issuing costs no vector instruction.
+  uint32_t va[NA], vb[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) va[i] = csrc[i];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) vb[i] = csrc[NA + i];
   auto issue = [&](int chunk, int stage) {
     const uint32_t st = smem_base + stage * T::STAGE_BYTES;
-    uint32_t va[NA], vb[NB];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) va[i] = csrc[i] + (uint32_t)chunk * T::CB;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) vb[i] = csrc[NA + i] + (uint32_t)chunk * T::CB;
-    load_lds16_run<NA>(a_codes, va, st + 1024 * wave, 1024 * KW);
-    load_lds16_run<NB>(w_codes, vb, st + 1024 * (KW * NA + wave), 1024 * KW);
+    load_lds16_run<NA>(a_codes + (size_t)chunk * T::CB, va, st + 1024 * wave, 1024 * KW);
+    load_lds16_run<NB>(w_codes + (size_t)chunk * T::CB, vb, st + 1024 * (KW * NA + wave),
+                       1024 * KW);
     const uint32_t sdst = st + T::CODE_BYTES + 1024 * wave;
     if (wave < TM / T::SRL)
-      load_lds16(a_scales, ssrc + (uint32_t)chunk * T::SB, sdst);
+      load_lds16(a_scales + (size_t)chunk * T::SB, ssrc, sdst);
     else if (wave < T::SCALE_LOADS)
-      load_lds16(w_scales, ssrc + (uint32_t)chunk * T::SB, sdst);
+      load_lds16(w_scales + (size_t)chunk * T::SB, ssrc, sdst);
   };
 
   f32x16 acc[WM][WN];
@@ -267,20 +272,23 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   if constexpr (PIPE) {
     // This wave's code fragments (16 bytes: its 64-element step of the
     // chunk) and scale pairs of every tile row, from a stage.
+    // One address per stage and lane; the fragments sit at constant offsets
+    // from it (folded into the LDS reads' offset fields).
+    const uint32_t lane_c = (uint32_t)r32 * T::CB + slot;
+    const uint32_t lane_s = T::CODE_BYTES + (uint32_t)r32 * T::SB + 4 * wave + 2 * h;
     auto read_frags = [&](int stage, uint4 (&fa)[WM], uint4 (&fb)[WN], uint32_t (&sa)[WM],
                           uint32_t (&sb)[WN]) {
-      const uint8_t* st = smem + stage * T::STAGE_BYTES;
+      const uint8_t* pc = smem + stage * T::STAGE_BYTES + lane_c;
+      const uint8_t* ps = smem + stage * T::STAGE_BYTES + lane_s;
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
-        const int row = 32 * i + r32;
-        fa[i] = *(const uint4*)(st + row * T::CB + slot);
-        sa[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
+        fa[i] = *(const uint4*)(pc + 32 * i * T::CB);
+        sa[i] = *(const uint16_t*)(ps + 32 * i * T::SB);
       }
 #pragma unroll
       for (int i = 0; i < WN; ++i) {
-        const int row = TM + 32 * i + r32;
-        fb[i] = *(const uint4*)(st + row * T::CB + slot);
-        sb[i] = *(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * wave + 2 * h);
+        fb[i] = *(const uint4*)(pc + (TM + 32 * i) * T::CB);
+        sb[i] = *(const uint16_t*)(ps + (TM + 32 * i) * T::SB);
       }
     };
     // scale pairs as f16 and the operands of substep 0
@@ -291,12 +299,12 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         sfa[i] = scale_pair2(sa[i]);
-        A[0][i] = dequant8(fa[i].x, half2_t{sfa[i][0], sfa[i][0]});
+        A[0][i] = dequant8(fa[i].x, splat<0>(sfa[i]));
       }
 #pragma unroll
       for (int i = 0; i < WN; ++i) {
         sfb[i] = scale_pair2(sb[i]);
-        B[0][i] = dequant8(fb[i].x, half2_t{sfb[i][0], sfb[i][0]});
+        B[0][i] = dequant8(fb[i].x, splat<0>(sfb[i]));
       }
     };
     // Two stages.  The wait and barrier for chunk c + 1 come before the last
@@ -319,14 +327,12 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
           const uint32_t w = sub == 0 ? fa[i].y : sub == 1 ? fa[i].z : fa[i].w;
-          const _Float16 sc = sub == 0 ? sfa[i][0] : sfa[i][1];
-          A[nxt][i] = dequant8(w, half2_t{sc, sc});
+          A[nxt][i] = dequant8(w, sub == 0 ? splat<0>(sfa[i]) : splat<1>(sfa[i]));
         }
 #pragma unroll
         for (int i = 0; i < WN; ++i) {
           const uint32_t w = sub == 0 ? fb[i].y : sub == 1 ? fb[i].z : fb[i].w;
-          const _Float16 sc = sub == 0 ? sfb[i][0] : sfb[i][1];
-          B[nxt][i] = dequant8(w, half2_t{sc, sc});
+          B[nxt][i] = dequant8(w, sub == 0 ? splat<0>(sfb[i]) : splat<1>(sfb[i]));
         }
 #pragma unroll
         for (int a = 0; a < WM; ++a)
@@ -407,9 +413,9 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int i = 0; i < WN; ++i) sfb[i] = scale_pair2(sb[i]);
       half8_t A[2][WM], B[2][WN];
   #pragma unroll
-      for (int i = 0; i < WM; ++i) A[0][i] = dequant8(fa[i].x, half2_t{sfa[i][0], sfa[i][0]});
+      for (int i = 0; i < WM; ++i) A[0][i] = dequant8(fa[i].x, splat<0>(sfa[i]));
   #pragma unroll
-      for (int i = 0; i < WN; ++i) B[0][i] = dequant8(fb[i].x, half2_t{sfb[i][0], sfb[i][0]});
+      for (int i = 0; i < WN; ++i) B[0][i] = dequant8(fb[i].x, splat<0>(sfb[i]));
   #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         const int cur = sub & 1, nxt = cur ^ 1;
@@ -417,14 +423,12 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   #pragma unroll
           for (int i = 0; i < WM; ++i) {
             const uint32_t w = sub == 0 ? fa[i].y : sub == 1 ? fa[i].z : fa[i].w;
-            const _Float16 sc = sub == 0 ? sfa[i][0] : sfa[i][1];
-            A[nxt][i] = dequant8(w, half2_t{sc, sc});
+            A[nxt][i] = dequant8(w, sub == 0 ? splat<0>(sfa[i]) : splat<1>(sfa[i]));
           }
   #pragma unroll
           for (int i = 0; i < WN; ++i) {
             const uint32_t w = sub == 0 ? fb[i].y : sub == 1 ? fb[i].z : fb[i].w;
-            const _Float16 sc = sub == 0 ? sfb[i][0] : sfb[i][1];
-            B[nxt][i] = dequant8(w, half2_t{sc, sc});
+            B[nxt][i] = dequant8(w, sub == 0 ? splat<0>(sfb[i]) : splat<1>(sfb[i]));
           }
         }
   #pragma unroll
@@ -516,6 +520,9 @@ hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   using T = LdsTile<WM, WN, STAGES, KW>;
   static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
   const int nch = (int)(K / T::CHUNK);
+  // the prologue loads chunk 0 (and chunk min(s, nch - 1) for deeper
+  // stages) unconditionally: K must hold whole chunks, at least one
+  if (nch < 1 || K % T::CHUNK != 0) return hipErrorInvalidValue;
   const int cps = (nch + splits - 1) / splits;
   splits = (nch + cps - 1) / cps;  // every split has at least one chunk
   const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM),

@@ -362,6 +362,59 @@ def test_linear_integer_case_bitexact(C, M, N, K):
         assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
+E4M3_FINITE = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)  # 254 bytes
+
+
+def every_scale_byte_operands(M, N, K, side, seed):
+    """Operands on which every finite E4M3 byte (both signs, subnormals,
+    zero) is a block scale of `side` ('a' or 'w') and every output is exact
+    in FP32 on any summation order.  That side's scale of block b in row r
+    is E4M3_FINITE[(r + b) % 254]; the other side has unit scales and
+    nonzero codes in a single block per row, so an output is one decoded
+    scale times a 16-term sum of E2M1 products (a multiple of 1/4 of
+    magnitude <= 576): at most 16 significant bits."""
+    rng = np.random.default_rng(seed)
+    nb = K // 16
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asf = np.full((M, nb), 0x38, np.uint8)
+    wsf = np.full((N, nb), 0x38, np.uint8)
+    block_of_byte = np.arange(K // 2)[None, :] // 8
+    if side == "a":
+        asf = E4M3_FINITE[(np.arange(M)[:, None] + np.arange(nb)[None, :]) % 254]
+        wc = np.where(block_of_byte == (np.arange(N) % nb)[:, None], wc, 0).astype(np.uint8)
+    else:
+        wsf = E4M3_FINITE[(np.arange(N)[:, None] + np.arange(nb)[None, :]) % 254]
+        ac = np.where(block_of_byte == ((7 * np.arange(M)) % nb)[:, None], ac, 0).astype(np.uint8)
+    return ac, asf, wc, wsf
+
+
+@pytest.mark.parametrize("side", ["a", "w"])
+@pytest.mark.parametrize("M", [1, 3, 16, 200])
+def test_linear_every_scale_byte_exact(C, M, side):
+    """Every finite E4M3 scale byte on either operand, through each linear
+    kernel (one row, a few rows, many rows) and the grouped form: outputs
+    bit-identical to the oracle.  Pins the kernels' scale decoding over its
+    whole domain (E4M3FN as the pages define the scale format)."""
+    say("linear every scale byte", M, side)
+    N, K = 256, 4096
+    ac, asf, wc, wsf = every_scale_byte_operands(M, N, K, side, seed=M + (side == "w"))
+    ref = oracle.linear(ac, asf, 1.0, wc, wsf, 1.0)
+    one = torch.ones(2, dtype=torch.float32, device=DEV)
+    need = C.nvfp4_workspace_bytes(C.OP_LINEAR, M, N, K)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV) if need else None
+    y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(to_dev(ac), to_dev(asf), one[:1], to_dev(wc), to_dev(wsf), one[:1], y, ws)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+    # grouped: two experts with the same weights, the rows split between them
+    wc2, wsf2 = np.stack([wc, wc]), np.stack([wsf, wsf])
+    offsets = np.array([0, M // 2, M], np.int32)
+    yg = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(to_dev(ac), to_dev(asf), one[:1], None, to_dev(offsets),
+                           to_dev(wc2), to_dev(wsf2), one, yg)
+    assert np.array_equal(yg.cpu().numpy().astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("M", [1, 64])
 def test_linear_bf16_output_is_rounded_fp32(C, M):
     say("linear bf16 out", M)
