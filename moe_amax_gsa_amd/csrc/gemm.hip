@@ -511,6 +511,186 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     ((float*)y)[e] = o;
 }
 
+// ------------------------------------------------------- wide tiles
+// Workgroup tile 256 x 256 for shapes with enough such tiles to fill the
+// chip.  Eight waves in a 2 (rows) x 4 (columns) arrangement each own a
+// 128 x 64 output block over the whole K range, so no partial tiles are
+// summed across waves.  Both operands' 256-element chunks (one 128-byte code
+// line and 16 scale bytes per row, 512 rows) are staged through LDS as in
+// the kernel above, two stages; a wave reads and dequantizes its own 4 + 2
+// fragments per 64-element step and runs 8 MFMAs per 16 elements.  Per flop
+// this moves a third of the bytes of the 128 x 64 tile.
+struct WideTile {
+  static constexpr int TM = 256, TN = 256, ROWS = TM + TN, KW = 8, THREADS = 64 * KW;
+  static constexpr int CHUNK = 256, CB = 128, SB = 16;
+  static constexpr int CODE_BYTES = ROWS * CB;                // 64 KiB
+  static constexpr int STAGE_BYTES = CODE_BYTES + ROWS * SB;  // + 8 KiB of scales
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int CODE_LOADS = ROWS / (8 * KW);  // a load covers 8 rows: 8 per wave
+  static constexpr int NA = TM / (8 * KW);             // the first 4 read A rows
+};
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_wide_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
+    const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
+    int y_bf16, int M, int N, int K, int gsa_rows) {
+  using T = WideTile;
+  constexpr int WM = 4, WN = 2, NA = T::NA, NB = T::CODE_LOADS - T::NA;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int m0 = blockIdx.y * T::TM, n0 = blockIdx.x * T::TN;
+  const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t cbytes = (uint32_t)K / 2, sbytes = (uint32_t)K / 16;
+  const int nch = K / T::CHUNK;
+
+  // code load i of wave w: LDS rows 8 (KW i + w) + l / 8, lane l filling
+  // slot l % 8 with piece (l % 8) ^ (row & 7) of the row's chunk line
+  uint32_t va[NA], vb[NB];
+#pragma unroll
+  for (int i = 0; i < T::CODE_LOADS; ++i) {
+    const int row = 8 * (T::KW * i + wave) + lane / 8;
+    const uint32_t off = (uint32_t)((lane % 8) ^ (row & 7)) * 16;
+    if (i < NA)
+      va[i] = (uint32_t)min(m0 + row, M - 1) * cbytes + off;  // clamped rows: discarded
+    else
+      vb[i - NA] = (uint32_t)min(n0 + row - T::TM, N - 1) * cbytes + off;
+  }
+  // scale load of wave w: rows 64 w + l (A rows for w < 4), 16 bytes each
+  const int srow = 64 * wave + lane;
+  const uint32_t ssrc = srow < T::TM ? (uint32_t)min(m0 + srow, M - 1) * sbytes
+                                     : (uint32_t)min(n0 + srow - T::TM, N - 1) * sbytes;
+  auto issue = [&](int chunk, int stage) {
+    const uint32_t st = smem_base + stage * T::STAGE_BYTES;
+    load_lds16_run<NA>(a_codes + (size_t)chunk * T::CB, va, st + 1024 * wave, 1024 * T::KW);
+    load_lds16_run<NB>(w_codes + (size_t)chunk * T::CB, vb, st + 1024 * (T::KW * NA + wave),
+                       1024 * T::KW);
+    const uint32_t sdst = st + T::CODE_BYTES + 1024 * wave;
+    if (wave < T::TM / 64)
+      load_lds16(a_scales + (size_t)chunk * T::SB, ssrc, sdst);
+    else
+      load_lds16(w_scales + (size_t)chunk * T::SB, ssrc, sdst);
+  };
+
+  f32x16 acc[WM][WN];
+#pragma unroll
+  for (int a = 0; a < WM; ++a)
+#pragma unroll
+    for (int b = 0; b < WN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // this lane's rows of the stage: A rows 128 wm + 32 i + r32, W rows
+  // 256 + 64 wn + 32 j + r32 (all with row & 7 == r32 & 7)
+  const uint32_t a_row0 = (uint32_t)(128 * wm + r32), b_row0 = (uint32_t)(T::TM + 64 * wn + r32);
+
+  issue(0, 0);
+  for (int c = 0; c < nch; ++c) {
+    // chunk c has landed everywhere, and every wave is done with the stage
+    // chunk c + 1 will refill
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (c + 1 < nch) issue(c + 1, (c + 1) & 1);
+    const uint8_t* st = smem + (c & 1) * T::STAGE_BYTES;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // step s of the chunk: lane half h owns its pieces 2s + h
+      const uint32_t slot = (uint32_t)(((2 * s + h) ^ (r32 & 7)) * 16);
+      uint4 fa[WM], fb[WN];
+      half2_t sfa[WM], sfb[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const uint32_t row = a_row0 + 32 * i;
+        fa[i] = *(const uint4*)(st + row * T::CB + slot);
+        sfa[i] = scale_pair2(*(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * s + 2 * h));
+      }
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const uint32_t row = b_row0 + 32 * j;
+        fb[j] = *(const uint4*)(st + row * T::CB + slot);
+        sfb[j] = scale_pair2(*(const uint16_t*)(st + T::CODE_BYTES + row * T::SB + 4 * s + 2 * h));
+      }
+      half8_t A[2][WM], B[2][WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i) A[0][i] = dequant8(fa[i].x, splat<0>(sfa[i]));
+#pragma unroll
+      for (int j = 0; j < WN; ++j) B[0][j] = dequant8(fb[j].x, splat<0>(sfb[j]));
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const int cur = sub & 1, nxt = cur ^ 1;
+        if (sub < 3) {
+#pragma unroll
+          for (int i = 0; i < WM; ++i) {
+            const uint32_t w = sub == 0 ? fa[i].y : sub == 1 ? fa[i].z : fa[i].w;
+            A[nxt][i] = dequant8(w, sub == 0 ? splat<0>(sfa[i]) : splat<1>(sfa[i]));
+          }
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const uint32_t w = sub == 0 ? fb[j].y : sub == 1 ? fb[j].z : fb[j].w;
+            B[nxt][j] = dequant8(w, sub == 0 ? splat<0>(sfb[j]) : splat<1>(sfb[j]));
+          }
+        }
+#pragma unroll
+        for (int a = 0; a < WM; ++a)
+#pragma unroll
+          for (int b = 0; b < WN; ++b) acc[a][b] = mfma_f16(A[cur][a], B[cur][b], acc[a][b]);
+        if (sub < 3) {
+#pragma unroll
+          for (int g = 0; g < WM * WN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (8 * (WM + WN) + WM * WN - 1) / (WM * WN), 0);
+          }
+        }
+      }
+    }
+  }
+
+  // each wave stores its own block: result register r of MFMA tile (a, b)
+  // is row 32a + 8(r/4) + 4h + r%4, column 32b + r32 of the block
+  const float gscale = gsa_p[0] * ws2_p[0];
+  const float w2 = ws2_p[0];
+#pragma unroll
+  for (int a = 0; a < WM; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + 128 * wm + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row >= M) continue;
+      const float sc = gsa_rows ? gsa_p[row] * w2 : gscale;
+#pragma unroll
+      for (int b = 0; b < WN; ++b) {
+        const int col = n0 + 64 * wn + 32 * b + r32;
+        if (col >= N) continue;
+        const float o = acc[a][b][r] * sc;
+        if (y_bf16)
+          ((uint16_t*)y)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(o);
+        else
+          ((float*)y)[(int64_t)row * N + col] = o;
+      }
+    }
+}
+
+static hipError_t launch_wide(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                              const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                              void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                              bool gsa_rows) {
+  using T = WideTile;
+  static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+  // the loop loads chunk 0 unconditionally: K must hold whole chunks
+  if (K < T::CHUNK || K % T::CHUNK != 0) return hipErrorInvalidValue;
+  static unsigned char done[64];
+  const hipError_t attr = allow_dynamic_lds((const void*)gemm_wide_kernel, T::LDS_BYTES, done);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM));
+  gemm_wide_kernel<<<grid, T::THREADS, T::LDS_BYTES, s>>>(a_codes, a_scales, gsa, w_codes,
+                                                          w_scales, ws2, y, y_bf16 ? 1 : 0,
+                                                          (int)M, (int)N, (int)K,
+                                                          gsa_rows ? 1 : 0);
+  return hipGetLastError();
+}
+
 template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE = false>
 hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                       const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2, void* y,
@@ -619,6 +799,11 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     // 512-element chunk (two waves per SIMD) and the next chunk's fragment
     // reads and first dequantization run under the current chunk's last
     // MFMAs.  More tiles: four waves, two workgroups per CU.
+    // 256 x 256 tiles where they keep at least three quarters of the CUs busy
+    const int64_t wide = ((N + 255) / 256) * ((M + 255) / 256);
+    if (4 * wide >= 3 * (int64_t)cu_count())
+      return launch_wide(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M, N, K, s,
+                         gsa_rows);
     const int64_t tiles = ((N + 63) / 64) * ((M + 127) / 128);
     if (tiles <= cu_count() && K % 512 == 0)
       return launch_lds<4, 2, 2, 2, 8, true>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,

@@ -415,6 +415,61 @@ def test_linear_every_scale_byte_exact(C, M, side):
     assert np.array_equal(yg.cpu().numpy().astype(np.float64), ref)
 
 
+WIDE_SHAPES = [(2000, 6600, 512), (2048, 7168, 256), (1800, 7000, 768)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_SHAPES)
+def test_linear_wide_tiles_integer_exact(C, M, N, K):
+    """Shapes with enough 256 x 256 tiles to fill the chip (ragged in both
+    dimensions, one to three 256-element chunks): all block scales 1.0 and
+    gsa = ws2 = 1, so every output is a multiple of 1/4 below 2^15 and exact
+    on any summation order.  The whole output is compared bit for bit with
+    the FP64 product of the oracle's dequantized operands; bf16 output is
+    that value rounded to nearest even."""
+    say("linear wide integer", M, N, K)
+    rng = np.random.default_rng(M + N + K)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asf = np.full((M, K // 16), 0x38, np.uint8)
+    wsf = np.full((N, K // 16), 0x38, np.uint8)
+    ref = oracle.dequantize(ac, asf, 1.0) @ oracle.dequantize(wc, wsf, 1.0).T
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(to_dev(ac), to_dev(asf), one, to_dev(wc), to_dev(wsf), one, y)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+    y16 = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    C.nvfp4_linear(to_dev(ac), to_dev(asf), one, to_dev(wc), to_dev(wsf), one, y16)
+    assert torch.equal(y16.cpu(), torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_SHAPES[:2])
+def test_linear_wide_tiles_parity(C, M, N, K):
+    """The same shapes with scales over the E4M3 range and a quantized
+    activation: sampled outputs (tile corners and edges included) within
+    1e-3 of the oracle, also with one gsa per row."""
+    say("linear wide parity", M, N, K)
+    inp = W.make_linear(M, K, N, seed=K, x="outliers", sf=(0.125, 8.0), ws2=0.003)
+    g, codes, scales, y = run_linear(C, inp)
+    oc, os_ = oracle.quantize(inp.x, f32(g))
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    ms, ns = sample_positions(M, N, 4096, 3)
+    edge = np.array([255, 256, 511, 512, M - 1, M - 2] * 2)[:12] % M
+    ms = np.concatenate([ms, edge, np.full(6, M // 2)])
+    ns = np.concatenate([ns, np.array([0, 255, 256, N - 1, N - 2, 4095] * 2)[:12] % N,
+                         np.array([63, 64, 127, 128, 191, 192]) % N])
+    ref = oracle.linear_at(oc, os_, f32(g), inp.w_codes, inp.w_scales, inp.ws2, ms, ns)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert rel_err(yg[ms, ns], ref) <= REL_TOL
+    # one gsa per row: row m scaled by 2^(m % 3) exactly
+    grow = torch.full((M,), float(f32(g)), dtype=torch.float32, device=DEV)
+    grow *= torch.tensor([1.0, 2.0, 4.0], device=DEV).repeat(M // 3 + 1)[:M]
+    yr = torch.empty_like(y)
+    ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_rows(codes, scales, grow, to_dev(inp.w_codes), to_dev(inp.w_scales), ws2, yr)
+    mult = np.array([1.0, 2.0, 4.0])[np.arange(M) % 3]
+    assert np.array_equal(yr.cpu().numpy(), (yg * mult[:, None]).astype(np.float32))
+
+
 @pytest.mark.parametrize("M", [1, 64])
 def test_linear_bf16_output_is_rounded_fp32(C, M):
     say("linear bf16 out", M)
