@@ -284,9 +284,13 @@ int nvfp4_grouped_linear(const uint8_t *a_codes, const uint8_t *a_scales, const 
  * q = j / granularity is gate when q is even, up when odd, gate group 2p
  * pairs with up group 2p+1); h (M, N_inter/2) fp32 receives
  * h[m, p*granularity + i] = silu(gate) * up, silu(g) = g / (1 + exp(-g)).
- * N_inter % (2*granularity) == 0. */
+ * N_inter % (2*granularity) == 0.
+ * limit: <= 0 applies none.  > 0 first caps the gate at limit and clamps the
+ * up value to [-limit, limit] (archived_plans/CORRECTNESS_BACKLOG.md
+ * section 6, Nvfp4MoE, lists a SwiGLU limit of 10 without its formula; this
+ * clamp is the reading taken).  NaN: NVFP4_ERR_SHAPE. */
 int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_inter,
-                              int granularity, void *stream);
+                              int granularity, float limit, void *stream);
 
 /* The step between the two expert projections, fused into the first
  * (SwiGLU, de-interleave and the first amax phase in the grouped gate/up
@@ -318,6 +322,7 @@ int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_in
  * quantize.  With at most 2048 amax partials each quantize workgroup
  * reduces them itself, so the second amax phase and the quantize are one
  * kernel.  Needs (N_inter/2) % 16 == 0; h_codes 8-byte aligned.
+ * limit: the SwiGLU limit, as in nvfp4_swiglu_deinterleave.
  * M_total == 0 or N_inter == 0 only writes gsa_h (the 1e-8 floor). */
 int nvfp4_grouped_linear_swiglu(const uint8_t *a_codes, const uint8_t *a_scales,
                                 const float *gsa, int64_t a_rows, const int32_t *row_index,
@@ -325,7 +330,7 @@ int nvfp4_grouped_linear_swiglu(const uint8_t *a_codes, const uint8_t *a_scales,
                                 const uint8_t *w_codes, const uint8_t *w_scales,
                                 const float *ws2, float *h, float *gsa_h, uint8_t *h_codes,
                                 uint8_t *h_scales, int64_t N_inter, int64_t K, int granularity,
-                                void *ws, size_t ws_bytes, void *stream);
+                                float limit, void *ws, size_t ws_bytes, void *stream);
 
 /* Static name of a status code. */
 const char *nvfp4_status_string(int status);

@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 6; }
+NVFP4_API int nvfp4_abi_version(void) { return 7; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -333,10 +333,11 @@ NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t*
                                           int G, int64_t M_total, const uint8_t* w_codes,
                                           const uint8_t* w_scales, const float* ws2, float* h,
                                           float* gsa_h, uint8_t* h_codes, uint8_t* h_scales,
-                                          int64_t N_inter, int64_t K, int granularity, void* ws,
-                                          size_t ws_bytes, void* stream) {
+                                          int64_t N_inter, int64_t K, int granularity,
+                                          float limit, void* ws, size_t ws_bytes, void* stream) {
   int st = check_gemm_shape(M_total, N_inter, K);
   if (st != NVFP4_OK) return st;
+  if (limit != limit) return NVFP4_ERR_SHAPE;  // NaN limit
   if (G < 1 || G > 65535 || a_rows < 0 || a_rows > I32_MAX) return NVFP4_ERR_SHAPE;
   if (row_index == nullptr && a_rows < M_total) return NVFP4_ERR_SHAPE;
   if (granularity < 1 || N_inter % (2 * (int64_t)granularity) != 0) return NVFP4_ERR_SHAPE;
@@ -362,17 +363,19 @@ NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t*
   if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
   return launched(launch_grouped_swiglu(a_codes, a_scales, gsa, a_rows, row_index, group_offsets,
                                         G, M_total, w_codes, w_scales, ws2, h, gsa_h, N_inter, K,
-                                        granularity, (uint32_t*)ws, h_codes, h_scales,
+                                        granularity, limit, (uint32_t*)ws, h_codes, h_scales,
                                         (hipStream_t)stream));
 }
 
 NVFP4_API int nvfp4_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t N_inter,
-                                        int granularity, void* stream) {
+                                        int granularity, float limit, void* stream) {
   if (M < 0 || granularity < 1 || N_inter < 0 || N_inter % (2 * (int64_t)granularity) != 0)
     return NVFP4_ERR_SHAPE;
+  if (limit != limit) return NVFP4_ERR_SHAPE;  // NaN limit
   if ((M * (N_inter / 2) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
   if (M == 0 || N_inter == 0) return NVFP4_OK;
   if (l1 == nullptr || h == nullptr) return NVFP4_ERR_NULL;
   if (!aligned(l1, 4) || !aligned(h, 4)) return NVFP4_ERR_ALIGN;
-  return launched(launch_swiglu_deinterleave(l1, h, M, N_inter, granularity, (hipStream_t)stream));
+  return launched(
+      launch_swiglu_deinterleave(l1, h, M, N_inter, granularity, limit, (hipStream_t)stream));
 }

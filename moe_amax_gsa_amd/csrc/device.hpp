@@ -124,8 +124,15 @@ __device__ __forceinline__ uint32_t e2m1_signs8(const float v[8]) {
 // standalone kernel and the grouped linear's epilogue) use, so they give
 // identical h.  Large |g| saturates correctly: exp(-g) -> inf gives 0
 // (times the sign of g), exp(-g) -> 0 gives g * u.
-__device__ __forceinline__ float swiglu1(float g, float u) {
+// limit > 0 first caps the gate from above and clamps the up value to
+// [-limit, limit] (the pages name a SwiGLU limit without its formula; this
+// is the reading taken).  Clamping is exact, so both paths still agree.
+__device__ __forceinline__ float swiglu1(float g, float u, float limit) {
 #pragma clang fp contract(off)
+  if (limit > 0.f) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
   const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }

@@ -61,9 +61,11 @@ struct GemvArgs {
   float* gsa_out;
   uint8_t* codes_out;
   uint8_t* scales_out;
-  // gemv_ring_kernel with SwiGLU: gate/up group width, and one amax partial
-  // (bits of a non-negative float) per workgroup
+  // gemv_ring_kernel with SwiGLU: gate/up group width, the SwiGLU limit
+  // (<= 0: none), and one amax partial (bits of a non-negative float) per
+  // workgroup
   int gran;
+  float limit;
   uint32_t* partials;
   // plain mode: gsa holds one global scale per activation row (gsa[m])
   int gsa_rows;
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
           const float gv = v * gscale;
           const float uv = __shfl_xor(gv, args.gran, 64);  // the paired up column
           if (ok && (col & args.gran) == 0) {  // a gate column (gran is a power of two)
-            const float hv = swiglu1(gv, uv);
+            const float hv = swiglu1(gv, uv, args.limit);
             const int lg = __builtin_ctz(args.gran);
             const int hcol = ((n >> (lg + 1)) << lg) + (n & (args.gran - 1));
             ((float*)args.y)[(int64_t)r * (N / 2) + hcol] = hv;
@@ -1168,7 +1170,7 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
                                  const int32_t* offsets, int G, int64_t M_total,
                                  const uint8_t* w_codes, const uint8_t* w_scales,
                                  const float* ws2, float* h, float* gsa_h, int64_t N, int64_t K,
-                                 int gran, uint32_t* partials, uint8_t* h_codes,
+                                 int gran, float limit, uint32_t* partials, uint8_t* h_codes,
                                  uint8_t* h_scales, hipStream_t s) {
   GemvArgs a{};
   a.a_codes = a_codes;
@@ -1186,6 +1188,7 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
   a.K = (int)K;
   a.a_rows = (int)a_rows;
   a.gran = gran;
+  a.limit = limit;
   a.partials = partials;
   const int64_t mean_rows = (M_total + G - 1) / G;
   hipError_t err = hipSuccess;

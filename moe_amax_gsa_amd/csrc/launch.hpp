@@ -38,9 +38,9 @@ hipError_t launch_amax_quantize_small(const void* x, bool bf16, int64_t M, int64
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const float* gsa,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
 
-// SwiGLU de-interleave
+// SwiGLU de-interleave (limit > 0: gate capped at limit, up clamped to +-limit)
 hipError_t launch_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t NI, int gran,
-                                      hipStream_t s);
+                                      float limit, hipStream_t s);
 
 // RMSNorm + quantize: per-row gsa (M,) or one gsa (then `partials` holds M
 // row maxima).
@@ -100,7 +100,7 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
                                  const int32_t* offsets, int G, int64_t M_total,
                                  const uint8_t* w_codes, const uint8_t* w_scales,
                                  const float* ws2, float* h, float* gsa_h, int64_t N, int64_t K,
-                                 int gran, uint32_t* partials, uint8_t* h_codes,
+                                 int gran, float limit, uint32_t* partials, uint8_t* h_codes,
                                  uint8_t* h_scales, hipStream_t s);
 
 // amax -> gsa -> quantize -> linear in one kernel for a few activation rows.

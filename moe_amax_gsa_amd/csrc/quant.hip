@@ -497,7 +497,7 @@ hipError_t launch_rmsnorm_quantize(const void* x, bool x_bf16, const void* w, bo
 __global__ __launch_bounds__(256) void swiglu_deinterleave_kernel(const float* __restrict__ l1,
                                                                   float* __restrict__ h,
                                                                   int64_t M, int64_t NI,
-                                                                  int gran) {
+                                                                  int gran, float limit) {
   const int64_t H = NI / 2;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= M * H) return;
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256) void swiglu_deinterleave_kernel(const float* _
   const int64_t pair = c / gran, off = c - pair * gran;
   const float g = l1[m * NI + 2 * pair * gran + off];
   const float u = l1[m * NI + (2 * pair + 1) * gran + off];
-  h[t] = swiglu1(g, u);
+  h[t] = swiglu1(g, u, limit);
 }
 
 hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float* gsa,
@@ -515,10 +515,11 @@ hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float*
 }
 
 hipError_t launch_swiglu_deinterleave(const float* l1, float* h, int64_t M, int64_t NI, int gran,
-                                      hipStream_t s) {
+                                      float limit, hipStream_t s) {
   const int64_t n = M * (NI / 2);
   if (n == 0) return hipSuccess;
-  swiglu_deinterleave_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(l1, h, M, NI, gran);
+  swiglu_deinterleave_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(l1, h, M, NI, gran,
+                                                                        limit);
   return hipGetLastError();
 }
 

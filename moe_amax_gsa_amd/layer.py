@@ -170,13 +170,17 @@ class Nvfp4MoE:
     x (T, K1) bf16; row_index (P,) int32 = token of each pair; offsets (E+1,)
     int32 = first pair of each expert.  L1 weights (E, N1, K1/2) hold
     gate/up column groups interleaved at ``granularity``; L2 weights
-    (E, N2, N1/4) consume the SwiGLU output of width N1/2.
+    (E, N2, N1/4) consume the SwiGLU output of width N1/2.  swiglu_limit > 0
+    caps the gate at the limit and clamps up to [-limit, limit] before
+    silu(gate) * up (0: no clamp).
     """
 
     def __init__(self, w1_codes, w1_scales, w1_ws2, w2_codes, w2_scales, w2_ws2, max_pairs: int,
-                 max_tokens: int, granularity: int = 8, fused: bool = True):
+                 max_tokens: int, granularity: int = 8, fused: bool = True,
+                 swiglu_limit: float = 0.0):
         dev = w1_codes.device
         self.device = dev
+        self.swiglu_limit = float(swiglu_limit)
         self.E, self.N1, self.K1 = w1_codes.shape[0], w1_codes.shape[1], w1_codes.shape[2] * 2
         self.N2, self.K2 = w2_codes.shape[1], w2_codes.shape[2] * 2
         assert self.K2 * 2 == self.N1, "L2 input width must be half the L1 output width"
@@ -225,12 +229,12 @@ class Nvfp4MoE:
             C.nvfp4_grouped_linear_swiglu(xc, xs, gsa, row_index, offsets, self.w1_codes,
                                           self.w1_scales, self.w1_ws2, h, self.gsa2,
                                           self.granularity, self.ws_swiglu, stream,
-                                          h_codes=hc, h_scales=hs)
+                                          h_codes=hc, h_scales=hs, limit=self.swiglu_limit)
         else:
             y1 = self.y1[:P]
             C.nvfp4_grouped_linear(xc, xs, gsa, row_index, offsets, self.w1_codes,
                                    self.w1_scales, self.w1_ws2, y1, None, stream)
-            C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream)
+            C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream, limit=self.swiglu_limit)
             C.nvfp4_amax_gsa(h, self.gsa2, self.ws, stream)
             C.nvfp4_quantize_from_buffer(h, self.gsa2, hc, hs, stream)
         y2 = self.y2[:P]

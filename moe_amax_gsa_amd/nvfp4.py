@@ -73,9 +73,10 @@ lib.nvfp4_quantize_weight.restype = _I
 lib.nvfp4_quantize_weight.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]
 lib.nvfp4_grouped_linear_swiglu.restype = _I
 lib.nvfp4_grouped_linear_swiglu.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P,
-                                            _P, _P, _P, _I64, _I64, _I, _P, _SZ, _P]
+                                            _P, _P, _P, _I64, _I64, _I, ctypes.c_float, _P, _SZ,
+                                            _P]
 lib.nvfp4_swiglu_deinterleave.restype = _I
-lib.nvfp4_swiglu_deinterleave.argtypes = [_P, _P, _I64, _I64, _I, _P]
+lib.nvfp4_swiglu_deinterleave.argtypes = [_P, _P, _I64, _I64, _I, ctypes.c_float, _P]
 
 
 class Nvfp4Error(RuntimeError):
@@ -250,22 +251,25 @@ def nvfp4_grouped_linear_swiglu(a_codes: torch.Tensor, a_scales: torch.Tensor, g
                                 h: torch.Tensor, gsa_h: torch.Tensor, granularity: int,
                                 ws: torch.Tensor, stream=None,
                                 h_codes: Optional[torch.Tensor] = None,
-                                h_scales: Optional[torch.Tensor] = None) -> None:
+                                h_scales: Optional[torch.Tensor] = None,
+                                limit: float = 0.0) -> None:
     """w_codes (G, N_inter, K/2), w_scales (G, N_inter, K/16), ws2 (G,);
     h (M_total, N_inter/2) fp32 and gsa_h (1,) fp32 are written, and with
-    h_codes / h_scales also h's codes and scales."""
+    h_codes / h_scales also h's codes and scales.  limit: the SwiGLU limit
+    (<= 0: none)."""
     G, NI = w_codes.shape[0], w_codes.shape[1]
     K = w_codes.shape[2] * 2
     _check(lib.nvfp4_grouped_linear_swiglu(
         _ptr(a_codes), _ptr(a_scales), _ptr(gsa), a_codes.shape[0], _ptr(row_index),
         _ptr(group_offsets), G, h.shape[0], _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(h),
-        _ptr(gsa_h), _ptr(h_codes), _ptr(h_scales), NI, K, granularity, _ptr(ws),
+        _ptr(gsa_h), _ptr(h_codes), _ptr(h_scales), NI, K, granularity, limit, _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "nvfp4_grouped_linear_swiglu")
 
 
 def nvfp4_swiglu_deinterleave(l1: torch.Tensor, h: torch.Tensor, granularity: int = 8,
-                              stream=None) -> None:
-    """h (M, N/2) = silu(gate) * up from granularity-interleaved l1 (M, N), fp32."""
+                              stream=None, limit: float = 0.0) -> None:
+    """h (M, N/2) = silu(gate) * up from granularity-interleaved l1 (M, N),
+    fp32; limit > 0 caps the gate at limit and clamps up to [-limit, limit]."""
     M, NI = l1.shape
-    _check(lib.nvfp4_swiglu_deinterleave(_ptr(l1), _ptr(h), M, NI, granularity,
+    _check(lib.nvfp4_swiglu_deinterleave(_ptr(l1), _ptr(h), M, NI, granularity, limit,
                                          _stream(stream)), "nvfp4_swiglu_deinterleave")

@@ -294,9 +294,13 @@ void oracle_grouped_linear(const uint8_t *a_codes, const uint8_t *a_scales, floa
 /* Column j of the interleaved gate/up output belongs to group q = j / gran;
  * even q are gate columns and odd q up columns, pairing gate group q with
  * up group q+1 [MOE].  h[:, (q/2)*gran + j%gran] = silu(gate) * up with
- * silu(g) = g / (1 + exp(-g)), in double. */
+ * silu(g) = g / (1 + exp(-g)), in double.
+ * limit > 0: the pages name a SwiGLU limit (10 for the model) without its
+ * formula; the reading taken here caps the gate from above,
+ * g = min(g, limit), and clamps the up value to [-limit, limit] before the
+ * product.  limit <= 0: no clamp. */
 void oracle_swiglu_deinterleave(const float *l1, int64_t M, int64_t N_inter,
-                                int gran, double *h)
+                                int gran, double limit, double *h)
 {
     int64_t H = N_inter / 2;
     for (int64_t m = 0; m < M; ++m) {
@@ -304,6 +308,10 @@ void oracle_swiglu_deinterleave(const float *l1, int64_t M, int64_t N_inter,
             int64_t pair = c / gran, off = c % gran;
             double g = l1[m * N_inter + (2 * pair) * gran + off];
             double u = l1[m * N_inter + (2 * pair + 1) * gran + off];
+            if (limit > 0.0) {
+                g = fmin(g, limit);
+                u = fmin(fmax(u, -limit), limit);
+            }
             h[m * H + c] = g / (1.0 + exp(-g)) * u;
         }
     }

@@ -72,7 +72,7 @@ def _load():
     lib.oracle_router_topk.restype = None
     lib.oracle_router_topk.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
     lib.oracle_swiglu_deinterleave.restype = None
-    lib.oracle_swiglu_deinterleave.argtypes = [P, I64, I64, ctypes.c_int, P]
+    lib.oracle_swiglu_deinterleave.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_double, P]
     _lib = lib
     return lib
 
@@ -239,12 +239,14 @@ def linear_rows(a_codes, a_scales, gsa_rows, w_codes, w_scales, ws2) -> np.ndarr
     return y
 
 
-def swiglu_deinterleave(l1: np.ndarray, granularity: int = 8) -> np.ndarray:
+def swiglu_deinterleave(l1: np.ndarray, granularity: int = 8, limit: float = 0.0) -> np.ndarray:
+    """h = silu(gate) * up, de-interleaved (nvfp4_oracle.c,
+    oracle_swiglu_deinterleave); limit > 0 clamps as documented there."""
     l1 = np.ascontiguousarray(l1, dtype=np.float32)
     M, NI = l1.shape
     assert NI % (2 * granularity) == 0
     h = np.empty((M, NI // 2), np.float64)
-    _load().oracle_swiglu_deinterleave(_ptr(l1), M, NI, granularity, _ptr(h))
+    _load().oracle_swiglu_deinterleave(_ptr(l1), M, NI, granularity, float(limit), _ptr(h))
     return h
 
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(C):
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert C.nvfp4_abi_version() == 6
+    assert C.nvfp4_abi_version() == 7
 
 
 def test_status_strings(C):
@@ -77,8 +77,15 @@ def test_validation_errors_return_before_any_launch(C):
                                   1, 16, 32, None, 0, None) == -2
     assert L.nvfp4_grouped_linear(fake, fake, fake, 8, None, fake, 0, 8, fake, fake, fake, fake,
                                   1, 16, 32, None, 0, None) == -2
-    assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 24, 8, None) == -2
-    assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 32, 0, None) == -2
+    assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 24, 8, 0.0, None) == -2
+    assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 32, 0, 0.0, None) == -2
+    assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 32, 8, float("nan"), None) == -2
+    assert L.nvfp4_swiglu_deinterleave(fake, fake, 0, 32, 8, 10.0, None) == 0  # M == 0
+    gs = L.nvfp4_grouped_linear_swiglu
+    # (a_codes, a_scales, gsa, a_rows, row_index, offsets, G, M_total, w_codes, w_scales, ws2,
+    #  h, gsa_h, h_codes, h_scales, N_inter, K, granularity, limit, ws, ws_bytes, stream)
+    assert gs(fake, fake, fake, 4, None, fake, 1, 4, fake, fake, fake, fake, fake, None, None,
+              32, 256, 8, float("nan"), fake, 1 << 20, None) == -2
 
 
 def test_validation_of_the_fused_and_load_time_entries(C):

@@ -673,14 +673,16 @@ def test_moe_small_skewed_groups(C, fused):
                      fused=fused)
 
 
+@pytest.mark.parametrize("lim", ["off", "median"])
 @pytest.mark.parametrize("gran", [8, 4, 2, 1])
 @pytest.mark.parametrize("K,N", [(256, 64), (768, 160), (2048, 96)])
-def test_grouped_swiglu_matches_unfused(C, K, N, gran):
+def test_grouped_swiglu_matches_unfused(C, K, N, gran, lim):
     """nvfp4_grouped_linear_swiglu against the three separate calls on the
     same inputs: h bit-identical and the same gsa_h.  Group sizes 0 .. 19,
     invalid row indices (rows left unwritten in both, and out of the amax:
-    both h buffers start at zero), partial column tiles."""
-    say(f"grouped swiglu K={K} N={N} gran={gran}")
+    both h buffers start at zero), partial column tiles; without a SwiGLU
+    limit and with one at the median |l1| (so both clamps act)."""
+    say(f"grouped swiglu K={K} N={N} gran={gran} limit={lim}")
     rng = np.random.default_rng(K + N + gran)
     sizes = [3, 0, 1, 19, 2, 0, 5, 9]
     G = len(sizes)
@@ -696,6 +698,9 @@ def test_grouped_swiglu_matches_unfused(C, K, N, gran):
     ws2 = to_dev(rng.uniform(0.002, 0.01, G).astype(np.float32))
     gsa = to_dev(np.array([0.37], np.float32))
     ri, off = to_dev(row_index), to_dev(offsets)
+    l1 = torch.zeros(P, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(ac, asf, gsa, ri, off, wc, wsf, ws2, l1)
+    limit = 0.0 if lim == "off" else float(torch.median(torch.abs(l1[l1 != 0])))
     # fused
     h1 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
     g1 = torch.zeros(1, dtype=torch.float32, device=DEV)
@@ -704,13 +709,11 @@ def test_grouped_swiglu_matches_unfused(C, K, N, gran):
     hc1 = torch.full((P, N // 4), 0x5A, dtype=torch.uint8, device=DEV)
     hs1 = torch.full((P, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
     C.nvfp4_grouped_linear_swiglu(ac, asf, gsa, ri, off, wc, wsf, ws2, h1, g1, gran, ws,
-                                  h_codes=hc1, h_scales=hs1)
+                                  h_codes=hc1, h_scales=hs1, limit=limit)
     # unfused
-    l1 = torch.zeros(P, N, dtype=torch.float32, device=DEV)
     h2 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
     g2 = torch.zeros(1, dtype=torch.float32, device=DEV)
-    C.nvfp4_grouped_linear(ac, asf, gsa, ri, off, wc, wsf, ws2, l1)
-    C.nvfp4_swiglu_deinterleave(l1, h2, gran)
+    C.nvfp4_swiglu_deinterleave(l1, h2, gran, limit=limit)
     aws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, P * N // 2), 16),
                       dtype=torch.uint8, device=DEV)
     C.nvfp4_amax_gsa(h2, g2, aws)
@@ -722,6 +725,11 @@ def test_grouped_swiglu_matches_unfused(C, K, N, gran):
     assert np.all(a[[4, 10]] == 0.0)  # invalid row indices: unwritten
     # h's quantize in the same call (the partials reduced by the quantize)
     assert torch.equal(hc1, hc2) and torch.equal(hs1, hs2)
+    # and h against the oracle's SwiGLU of the same l1 (written rows)
+    href = oracle.swiglu_deinterleave(l1.cpu().numpy(), gran, limit)
+    keep = np.ones(P, bool)
+    keep[[4, 10, 20]] = False
+    assert np.max(np.abs(a[keep] - href[keep])) <= 1e-6 * max(np.max(np.abs(href[keep])), 1e-30)
 
 
 @pytest.mark.parametrize("G,rows", [(64, {0: 1, 17: 2, 63: 1}), (100, {5: 3, 6: 1, 99: 2}),
@@ -1154,13 +1162,17 @@ def check_router_layer(router, r, M):
     check_choice(idx, sc, z, r.bias, 8, eps=1e-6 * vmax)
 
 
-def test_swiglu_parity(C):
-    say("swiglu")
+@pytest.mark.parametrize("limit", [0.0, 6.0, 1e30])
+def test_swiglu_parity(C, limit):
+    """The unfused SwiGLU against the oracle within 1e-6 relative, without a
+    limit, with one that clamps gate and up values on both sides (|l1| up
+    to ~25), and with one that clamps nothing."""
+    say("swiglu", limit)
     rng = np.random.default_rng(1)
     l1 = (rng.standard_normal((37, 96)) * 5).astype(np.float32)
     h = torch.empty(37, 48, dtype=torch.float32, device=DEV)
-    C.nvfp4_swiglu_deinterleave(to_dev(l1), h, 8)
-    href = oracle.swiglu_deinterleave(l1, 8)
+    C.nvfp4_swiglu_deinterleave(to_dev(l1), h, 8, limit=limit)
+    href = oracle.swiglu_deinterleave(l1, 8, limit)
     assert np.max(np.abs(h.cpu().numpy() - href)) <= 1e-6 * np.max(np.abs(href))
 
 

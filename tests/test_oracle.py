@@ -368,6 +368,40 @@ def test_swiglu_matches_torch_silu():
     assert np.max(np.abs(h - ref)) <= 1e-14 * np.max(np.abs(ref))
 
 
+def test_swiglu_limit_off_or_wide_is_plain():
+    """limit <= 0 is off, and a limit above every |gate| and |up| clamps
+    nothing: both give the plain SwiGLU bit for bit."""
+    rng = np.random.default_rng(4)
+    l1 = (rng.standard_normal((3, 64)) * 5).astype(np.float32)
+    plain = oracle.swiglu_deinterleave(l1, 8)
+    for lim in (0.0, -1.0, float(np.max(np.abs(l1))) * 1.01, 1e30):
+        assert np.array_equal(oracle.swiglu_deinterleave(l1, 8, lim), plain)
+
+
+def test_swiglu_limit_matches_torch_clamp():
+    """The limit's reading (gate capped from above, up clamped to
+    [-limit, limit]) against torch's own clamp and silu in FP64, on values
+    well beyond the limit of 10 on both sides; parity of the reading with
+    the pages is unpinned (they name the limit, not its formula)."""
+    rng = np.random.default_rng(5)
+    l1 = (rng.standard_normal((5, 128)) * 15).astype(np.float32)
+    lim = 10.0
+    h = oracle.swiglu_deinterleave(l1, 8, lim)
+    t = torch.from_numpy(l1.astype(np.float64)).reshape(5, 8, 2, 8)
+    g = torch.clamp(t[:, :, 0], max=lim)
+    u = torch.clamp(t[:, :, 1], min=-lim, max=lim)
+    ref = (torch.nn.functional.silu(g) * u).reshape(5, 64).numpy()
+    assert np.max(np.abs(h - ref)) <= 1e-14 * np.max(np.abs(ref))
+    # saturation: a huge gate gives silu(limit) * up, a huge up gives silu(g) * limit
+    one = np.zeros((1, 16), np.float32)
+    one[0, 0], one[0, 8] = 1e6, 3.0
+    one[0, 1], one[0, 9] = -2.0, -1e6
+    hh = oracle.swiglu_deinterleave(one, 8, lim)
+    silu = lambda v: v / (1.0 + math.exp(-v))
+    assert hh[0, 0] == pytest.approx(silu(lim) * 3.0, rel=1e-15)
+    assert hh[0, 1] == pytest.approx(silu(-2.0) * -lim, rel=1e-15)
+
+
 # ---------------------------------------------------------------- RMSNorm
 def test_rmsnorm_constant_row_closed_form():
     """A row of equal values c: mean of squares c^2, inv_rms = 1/sqrt(c^2 + eps)."""
