@@ -22,6 +22,11 @@ namespace nvfp4 {
 
 constexpr int AMAX_THREADS = 256;
 constexpr int SMALL_THREADS = 1024;
+// From this many half-blocks (256 MiB of bf16, beyond what the Infinity
+// Cache keeps from the amax pass) a quantize thread takes four: the tensor
+// then streams from HBM and more bytes in flight pay; below it one a
+// thread is faster (measured at 1.85 GB and at 29 MB).
+constexpr int64_t QUANTIZE_WIDE_HALVES = 1ll << 24;
 
 // Block-wide max; every thread gets the result.
 template <int THREADS>
@@ -118,17 +123,23 @@ hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, 
 // FINALIZE: gsa is not read but formed -- every workgroup reduces the
 // nparts amax partials (bits of non-negative fp32 maxima) itself, the second
 // amax phase, and workgroup 0 writes it to gsa_p[0].
-template <bool BF16, bool FINALIZE = false>
+// HPT > 1: a workgroup covers 256 HPT half-blocks, thread t the half-blocks
+// t + 256 u, every load issued before the first quantize (more bytes in
+// flight per CU for large tensors).
+template <bool BF16, bool FINALIZE = false, int HPT = 1>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t nhalf,
                                                        float* __restrict__ gsa_p,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
                                                        const uint32_t* __restrict__ partials,
                                                        int nparts) {
-  const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool ok = h < nhalf;  // nhalf is even, so both lanes of a block agree
-  float v[8];
-  load_half8<BF16>(x, ok ? h : 0, v);
+  const int64_t h0 = (int64_t)blockIdx.x * 256 * HPT + threadIdx.x;
+  float v[HPT][8];
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    const int64_t h = h0 + 256 * u;
+    load_half8<BF16>(x, h < nhalf ? h : 0, v[u]);
+  }
   float gsa;
   if (FINALIZE) {
     uint32_t mb = 0;
@@ -138,13 +149,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   } else {
     gsa = gsa_p[0];
   }
-  float m = half_absmax8(v);
-  m = fmaxf(m, xor1_f32(m));
-  uint32_t c, sf;
-  quantize_half8(v, m, gsa, c, sf);
-  if (ok) {
-    ((uint32_t*)codes)[h] = c;
-    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sf;
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    const int64_t h = h0 + 256 * u;
+    const bool ok = h < nhalf;  // nhalf is even, so both lanes of a block agree
+    float m = half_absmax8(v[u]);
+    m = fmaxf(m, xor1_f32(m));
+    uint32_t c, sf;
+    quantize_half8(v[u], m, gsa, c, sf);
+    if (ok) {
+      ((uint32_t*)codes)[h] = c;
+      if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sf;
+    }
   }
 }
 
@@ -152,8 +168,18 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const int64_t nhalf = M * (K / 8);
   if (nhalf == 0) return hipSuccess;
-  const int64_t grid = (nhalf + 255) / 256;
   float* g = const_cast<float*>(gsa);  // read only: FINALIZE is off
+  if (nhalf >= QUANTIZE_WIDE_HALVES) {  // four half-blocks a thread
+    const int64_t grid = (nhalf + 1023) / 1024;
+    if (bf16)
+      quantize_kernel<true, false, 4><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, g, codes, scales,
+                                                                      nullptr, 0);
+    else
+      quantize_kernel<false, false, 4><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, g, codes, scales,
+                                                                       nullptr, 0);
+    return hipGetLastError();
+  }
+  const int64_t grid = (nhalf + 255) / 256;
   if (bf16)
     quantize_kernel<true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, g, codes, scales, nullptr, 0);
   else

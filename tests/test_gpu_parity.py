@@ -116,6 +116,7 @@ QUANT_CASES = [
     (1, 16, "normal", "bf16"), (3, 48, "normal", "fp32"), (7, 256, "outliers", "bf16"),
     (33, 1040, "zero_blocks", "fp32"), (16, 7168, "student_t", "bf16"), (300, 512, "normal", "bf16"),
     (5, 2048, "student_t", "fp32"),
+    (1171, 7200, "outliers", "bf16"), (1100, 7632, "zero_blocks", "fp32"),  # ragged, ~1M halves
 ]
 
 
@@ -131,6 +132,43 @@ def test_quantize_bitexact(C, M, K, dist, dtype):
     oc, os_ = oracle.quantize(x_host(bits, dtype), f32(g))
     assert np.array_equal(scales.cpu().numpy(), os_)
     assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+@pytest.mark.parametrize("M,K,dtype", [(18003, 7504, "bf16"), (18003, 7504, "fp32")])
+def test_quantize_large_tensor_rows(C, M, K, dtype):
+    """Tensors of more than 2^24 half-blocks (the quantize then gives each
+    thread four, and the last workgroup is ragged): gsa from the oracle's
+    amax of the whole tensor, codes and scales of sampled rows (first, last,
+    and 60 more) bit-exact with the oracle's quantize of those rows.  The
+    input is drawn on the device by torch's seeded generator: N(0, 1) with
+    every 97th row scaled by 50."""
+    say("quantize large", M, K, dtype)
+    assert M * K // 8 >= 1 << 24 and (M * K // 8) % 1024 != 0
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M + K)
+    xf = torch.randn(M, K, generator=g, device=DEV, dtype=torch.float32)
+    xf[::97] *= 50.0
+    xb = xf.to(torch.bfloat16)
+    xd = xb if dtype == "bf16" else xb.to(torch.float32)
+    del xf
+    gsa = gpu_gsa(C, xd)
+    codes, scales = gpu_quantize(C, xd, gsa)
+    # the oracle's gsa: its amax over the whole tensor (rows in slices)
+    bits = xb.view(torch.int16)
+    amax_bits = 0
+    for r0 in range(0, M, 2048):
+        part = bits[r0:r0 + 2048].cpu().numpy().view(np.uint16)
+        amax_bits = max(amax_bits, int(np.max(part & 0x7FFF)))
+    row_max = np.zeros((1, 8), np.uint16)
+    row_max[0, 0] = amax_bits
+    assert f32(gsa) == oracle.amax_gsa(row_max)
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], np.arange(0, M, 97)[:8],
+                                     np.random.default_rng(M).integers(0, M, 50)]))
+    rows_t = torch.from_numpy(rows).to(DEV)
+    sub = bits[rows_t].cpu().numpy().view(np.uint16)
+    oc, os_ = oracle.quantize(x_host(sub, dtype), f32(gsa))
+    assert np.array_equal(codes[rows_t].cpu().numpy(), oc)
+    assert np.array_equal(scales[rows_t].cpu().numpy(), os_)
 
 
 AMAXQ_CASES = [
