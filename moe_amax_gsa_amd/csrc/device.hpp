@@ -220,7 +220,16 @@ __device__ __forceinline__ uint32_t absbits_vec(uint4 v) {
 
 // Max of |x| bits over elements tid, tid + nthreads, ... (16-byte vectors,
 // scalar tail).  x must be 16-byte aligned.
-template <bool BF16>
+// A 16-byte load that is not kept in the caches (for streams larger than
+// they are).
+__device__ __forceinline__ uint4 load_nt16(const uint4* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// NT: nontemporal loads, for tensors larger than the Infinity Cache.
+template <bool BF16, bool NT = false>
 __device__ __forceinline__ uint32_t thread_absmax(const void* __restrict__ x, int64_t numel,
                                                   int64_t tid, int64_t nthreads) {
   constexpr int EPV = BF16 ? 8 : 4;
@@ -228,8 +237,9 @@ __device__ __forceinline__ uint32_t thread_absmax(const void* __restrict__ x, in
   const int64_t nvec = numel / EPV;
   uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
   int64_t i = tid;
+  auto ld = [&](int64_t k) { return NT ? load_nt16(xv + k) : xv[k]; };
   for (; i + 3 * nthreads < nvec; i += 4 * nthreads) {
-    uint4 v0 = xv[i], v1 = xv[i + nthreads], v2 = xv[i + 2 * nthreads], v3 = xv[i + 3 * nthreads];
+    uint4 v0 = ld(i), v1 = ld(i + nthreads), v2 = ld(i + 2 * nthreads), v3 = ld(i + 3 * nthreads);
     m0 = max(m0, absbits_vec<BF16>(v0));
     m1 = max(m1, absbits_vec<BF16>(v1));
     m2 = max(m2, absbits_vec<BF16>(v2));

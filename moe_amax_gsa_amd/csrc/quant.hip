@@ -22,11 +22,14 @@ namespace nvfp4 {
 
 constexpr int AMAX_THREADS = 256;
 constexpr int SMALL_THREADS = 1024;
-// From this many half-blocks (256 MiB of bf16, beyond what the Infinity
-// Cache keeps from the amax pass) a quantize thread takes four: the tensor
-// then streams from HBM and more bytes in flight pay; below it one a
-// thread is faster (measured at 1.85 GB and at 29 MB).
-constexpr int64_t QUANTIZE_WIDE_HALVES = 1ll << 24;
+// Tensors of at least 256 MiB outgrow the Infinity Cache: the quantize pass
+// reads them from HBM again whatever the amax pass does.  For them the amax
+// loads are nontemporal, and a quantize thread takes four half-blocks (more
+// bytes in flight); smaller tensors stay cached between the two passes,
+// where plain loads and one half-block a thread are faster (measured at
+// 1.85 GB and at 29 MB).
+constexpr int64_t STREAM_BYTES = 256ll << 20;
+constexpr int64_t QUANTIZE_WIDE_HALVES = 1ll << 24;  // 256 MiB of bf16
 
 // Block-wide max; every thread gets the result.
 template <int THREADS>
@@ -42,13 +45,14 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
   return r;
 }
 
-// Phase 1: one partial maximum per workgroup.
-template <bool BF16>
+// Phase 1: one partial maximum per workgroup.  NT: nontemporal loads (a
+// tensor the caches cannot keep for the quantize pass anyway).
+template <bool BF16, bool NT = false>
 __global__ __launch_bounds__(AMAX_THREADS) void amax_partial_kernel(
     const void* __restrict__ x, int64_t numel, uint32_t* __restrict__ partials) {
   const int64_t nthreads = (int64_t)gridDim.x * AMAX_THREADS;
-  uint32_t m = thread_absmax<BF16>(x, numel, (int64_t)blockIdx.x * AMAX_THREADS + threadIdx.x,
-                                   nthreads);
+  uint32_t m = thread_absmax<BF16, NT>(x, numel, (int64_t)blockIdx.x * AMAX_THREADS + threadIdx.x,
+                                       nthreads);
   m = block_max_u32<AMAX_THREADS>(m);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
@@ -104,11 +108,18 @@ hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, 
   }
   const int parts = amax_parts_for(numel);
   uint32_t* partials = (uint32_t*)ws;
+  const bool nt = numel * (bf16 ? 2 : 4) >= STREAM_BYTES;
   if (bf16) {
-    amax_partial_kernel<true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    if (nt)
+      amax_partial_kernel<true, true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    else
+      amax_partial_kernel<true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
     amax_finalize_kernel<true><<<1, AMAX_THREADS, 0, s>>>(partials, parts, gsa);
   } else {
-    amax_partial_kernel<false><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    if (nt)
+      amax_partial_kernel<false, true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    else
+      amax_partial_kernel<false><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
     amax_finalize_kernel<false><<<1, AMAX_THREADS, 0, s>>>(partials, parts, gsa);
   }
   return hipGetLastError();
