@@ -206,6 +206,14 @@ namespace nvfp4 {
 // ---- |x| maximum as an ordered integer (bf16: 15 bits, fp32: 31 bits).
 // For non-negative finite floats the bit pattern orders like the value, so
 // the integer max is the exact, order-free maximum.
+// A 16-byte load that is not kept in the caches (for streams larger than
+// they are).
+__device__ __forceinline__ uint4 load_nt16(const uint4* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint32_t absbits_vec(uint4 v) {
   if (BF16) {
@@ -220,14 +228,6 @@ __device__ __forceinline__ uint32_t absbits_vec(uint4 v) {
 
 // Max of |x| bits over elements tid, tid + nthreads, ... (16-byte vectors,
 // scalar tail).  x must be 16-byte aligned.
-// A 16-byte load that is not kept in the caches (for streams larger than
-// they are).
-__device__ __forceinline__ uint4 load_nt16(const uint4* p) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // NT: nontemporal loads, for tensors larger than the Infinity Cache.
 template <bool BF16, bool NT = false>
 __device__ __forceinline__ uint32_t thread_absmax(const void* __restrict__ x, int64_t numel,
@@ -412,6 +412,22 @@ __device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t voff,
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_wave_base), "v"(voff), "s"(base)
+      : "memory");
+}
+
+// The same load, nontemporal: for data read once (an expert's weight stream),
+// which should not displace what the caches hold.
+__device__ __forceinline__ void load_lds16_nt(const uint8_t* base, uint32_t voff,
+                                              uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds_wave_base), "v"(voff), "s"(base)

@@ -511,8 +511,10 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
   }
   auto issue_slot = [&](int c) {
     const uint32_t slot = ring_lds + (uint32_t)(c % D) * SLOT;
-    load_lds16(wbase, ring_off[0] + 128u * (uint32_t)c, slot);
-    load_lds16(wbase, ring_off[1] + 128u * (uint32_t)c, slot + 1024u);
+    // nontemporal: a weight line is read once per pass of activation rows,
+    // and decode-sized routing makes one pass
+    load_lds16_nt(wbase, ring_off[0] + 128u * (uint32_t)c, slot);
+    load_lds16_nt(wbase, ring_off[1] + 128u * (uint32_t)c, slot + 1024u);
   };
 
   for (int r0 = r_begin; r0 < r_end; r0 += ROWS) {
