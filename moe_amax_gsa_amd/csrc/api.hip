@@ -127,9 +127,7 @@ NVFP4_API int nvfp4_amax_quantize(const void* x, int x_dtype, int64_t M, int64_t
     if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
   }
-  const hipError_t e = launch_amax_gsa(x, bf16, M * K, gsa, ws, s);
-  if (e != hipSuccess) return launched(e);
-  return launched(launch_quantize(x, bf16, M, K, gsa, codes, scales, s));
+  return launched(launch_amax_then_quantize(x, bf16, M, K, gsa, codes, scales, ws, s));
 }
 
 NVFP4_API int nvfp4_rmsnorm_quantize(const void* x, int x_dtype, const void* norm_weight,
@@ -288,8 +286,7 @@ NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* 
     const size_t need = amax_ws_bytes(M * K);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
     if (need > 0 && !aligned(ws, 4)) return NVFP4_ERR_ALIGN;
-    e = launch_amax_gsa(x, xbf, M * K, gsa, ws, s);
-    if (e == hipSuccess) e = launch_quantize(x, xbf, M, K, gsa, codes, scales, s);
+    e = launch_amax_then_quantize(x, xbf, M, K, gsa, codes, scales, ws, s);
   }
   if (e == hipSuccess && N > 0) {
     if (M <= GEMV_MAX_M)

@@ -34,6 +34,11 @@ bool amax_quantize_small_ok(int64_t M, int64_t K);
 hipError_t launch_amax_quantize_small(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
                                       uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+// steps 1-2 past the one-workgroup size: two-phase amax, then the quantize
+// (which reduces few partials itself); ws holds amax_parts_for(M K) partials
+hipError_t launch_amax_then_quantize(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
+                                     uint8_t* codes, uint8_t* scales, void* ws, hipStream_t s);
+
 // quantize from a device gsa
 hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const float* gsa,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);

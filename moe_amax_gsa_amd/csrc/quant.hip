@@ -30,6 +30,8 @@ constexpr int SMALL_THREADS = 1024;
 // 1.85 GB and at 29 MB).
 constexpr int64_t STREAM_BYTES = 256ll << 20;
 constexpr int64_t QUANTIZE_WIDE_HALVES = 1ll << 24;  // 256 MiB of bf16
+// at most this many amax partials are reduced inside every quantize workgroup
+constexpr int QUANTIZE_INLINE_PARTS = 512;
 
 // Block-wide max; every thread gets the result.
 template <int THREADS>
@@ -132,8 +134,10 @@ hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, 
 // makes half-block h start at element 8h, its 4 code bytes at byte 4h and
 // its block's scale at byte h/2.
 // FINALIZE: gsa is not read but formed -- every workgroup reduces the
-// nparts amax partials (bits of non-negative fp32 maxima) itself, the second
-// amax phase, and workgroup 0 writes it to gsa_p[0].
+// nparts amax partials itself (the second amax phase; the partials hold
+// the bits of non-negative maxima in the input's own format: bf16 bits for
+// a bf16 input, fp32 bits otherwise), and workgroup 0 writes it to
+// gsa_p[0].
 // HPT > 1: a workgroup covers 256 HPT half-blocks, thread t the half-blocks
 // t + 256 u, every load issued before the first quantize (more bytes in
 // flight per CU for large tensors).
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   if (FINALIZE) {
     uint32_t mb = 0;
     for (int i = threadIdx.x; i < nparts; i += 256) mb = max(mb, partials[i]);
-    gsa = gsa_from_amax(__uint_as_float(block_max_u32<256>(mb)));
+    gsa = gsa_from_bits<BF16>(block_max_u32<256>(mb));
     if (blockIdx.x == 0 && threadIdx.x == 0) gsa_p[0] = gsa;
   } else {
     gsa = gsa_p[0];
@@ -195,6 +199,32 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
     quantize_kernel<true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, g, codes, scales, nullptr, 0);
   else
     quantize_kernel<false><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, g, codes, scales, nullptr, 0);
+  return hipGetLastError();
+}
+
+// Steps 1 and 2 on a tensor past the one-workgroup size.  With few amax
+// partials the quantize reduces them itself (two launches instead of
+// three); large tensors take the separate finalize and the wide quantize.
+hipError_t launch_amax_then_quantize(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
+                                     uint8_t* codes, uint8_t* scales, void* ws, hipStream_t s) {
+  const int64_t numel = M * K, nhalf = M * (K / 8);
+  const int parts = amax_parts_for(numel);
+  if (numel <= AMAX_SMALL_NUMEL || nhalf >= QUANTIZE_WIDE_HALVES || parts > QUANTIZE_INLINE_PARTS) {
+    const hipError_t e = launch_amax_gsa(x, bf16, numel, gsa, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_quantize(x, bf16, M, K, gsa, codes, scales, s);
+  }
+  uint32_t* partials = (uint32_t*)ws;
+  const int64_t grid = (nhalf + 255) / 256;
+  if (bf16) {
+    amax_partial_kernel<true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    quantize_kernel<true, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
+                                                               partials, parts);
+  } else {
+    amax_partial_kernel<false><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    quantize_kernel<false, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
+                                                                partials, parts);
+  }
   return hipGetLastError();
 }
 

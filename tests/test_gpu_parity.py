@@ -174,7 +174,9 @@ def test_quantize_large_tensor_rows(C, M, K, dtype):
 AMAXQ_CASES = [
     (1, 256, "bf16"), (1, 7168, "bf16"), (3, 4096, "fp32"), (9, 3072, "bf16"),
     (16, 4096, "bf16"),                       # one workgroup, 1 .. 8 half-blocks a thread
-    (17, 4096, "bf16"), (512, 7168, "fp32"),  # two-phase amax, then the quantize
+    (17, 4096, "bf16"), (512, 7168, "fp32"),  # two-phase amax, the quantize reducing the
+    (512, 7168, "bf16"), (499, 7184, "bf16"),  # partials itself (9 to 448 of them)
+    (600, 7168, "bf16"), (1000, 7168, "fp32"),  # more than 512 partials: a separate finalize
 ]
 
 
