@@ -535,6 +535,7 @@ RUN_CASES = [
     (3, 4096, 40, "fp32"), (5, 512, 33, "bf16"), (16, 1024, 64, "bf16"),  # one kernel
     (1, 272, 40, "bf16"), (4, 7168, 40, "bf16"), (20, 512, 64, "fp32"),    # separate kernels
     (100, 7168, 96, "bf16"),  # amax partials, then the same workspace for a 14-way split K
+    (700, 7168, 64, "bf16"),  # more than 512 amax partials: a separate finalize
 ]
 
 
