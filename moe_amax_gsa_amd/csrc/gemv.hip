@@ -538,14 +538,15 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
     __syncthreads();  // the previous pass has finished reading LDS
 
     if (tile_ok) {
-      // the tile's weight scales (once), then the first D slots
+      // the tile's weight scales (once, nontemporal: read once per call), then
+      // the first D slots
       if (r0 == r_begin) {
         for (int e0 = 0; e0 < 16 * spr; e0 += 64) {
           const int e = e0 + lane;
           const int r = e / spr, q = e - r * spr;
           const int rc = (n0 + r < N) ? r : N - 1 - n0;
           if (e < 16 * spr)
-            load_lds16(wsbase, (uint32_t)(rc * sbytes + 16 * q), ws_lds + 16u * (uint32_t)e0);
+            load_lds16_nt(wsbase, (uint32_t)(rc * sbytes + 16 * q), ws_lds + 16u * (uint32_t)e0);
         }
       }
       for (int c = 0; c < D && c < nsc; ++c) issue_slot(c);
