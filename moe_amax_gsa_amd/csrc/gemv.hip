@@ -144,6 +144,14 @@ __device__ __forceinline__ uint4 ldg_nt16(const uint8_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 8 bytes, nontemporal: a weight row's scales, read once per call like its
+// codes.
+__device__ __forceinline__ uint2 ldg_nt8(const uint8_t* p) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+  return make_uint2(v.x, v.y);
+}
+
 // Weight codes and scales of S super-chunks (group cg) for this lane.  FAST:
 // unconditional loads of a clamped, always valid chunk -- chunks past the
 // end are skipped by the (wave-uniform) compute loop.  A branch around the
@@ -162,7 +170,8 @@ __device__ __forceinline__ void load_w_group(const uint8_t* wrow, const uint8_t*
     } else {
       load32<FAST>(wrow, (int64_t)c * 128 + 32 * j, cbytes, ok, wb0[s], wb1[s]);
     }
-    wsb[s] = load8<FAST>(wsrow, (int64_t)c * 16 + 8 * (j & 1), sbytes, ok);
+    wsb[s] = FAST ? ldg_nt8(wsrow + (int64_t)c * 16 + 8 * (j & 1))
+                  : load8<FAST>(wsrow, (int64_t)c * 16 + 8 * (j & 1), sbytes, ok);
   }
 }
 
@@ -788,7 +797,7 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
 #pragma unroll
       for (int rq = 0; rq < RQ; ++rq) {
         wv[s2][rq] = ldg_nt16(wrow[rq] + (int64_t)(4 * set + q) * 64 + 16 * j);
-        fwv[s2][rq] = *(const uint2*)(wsrow[rq] + (4 * set + j) * 8);
+        fwv[s2][rq] = ldg_nt8(wsrow[rq] + (4 * set + j) * 8);
       }
       if (!RUN) {
 #pragma unroll
