@@ -1009,6 +1009,13 @@ static hipError_t launch_narrow(const GemvArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.N + 4 * NARROW_RQ - 1) / (4 * NARROW_RQ)));
   if (a.M <= 1) {
     const int th = narrow_waves(a.K, 1, NARROW_MAXW1) * 64;
+    // few weight rows (a router gate): one quad a workgroup, so twice as
+    // many CUs stream them
+    if ((int)grid.x < 128) {
+      gemv_narrow_kernel<1, 1, false, true, 1, 1, NARROW_MAXW1>
+          <<<dim3((unsigned)((a.N + 3) / 4)), th, 0, s>>>(a);
+      return hipGetLastError();
+    }
     gemv_narrow_kernel<1, 1, false, true, 1, NARROW_RQ, NARROW_MAXW1><<<grid, th, 0, s>>>(a);
   } else {
     const int th = narrow_waves(a.K, 2, GEMV_MAX_WAVES) * 64;
