@@ -115,6 +115,201 @@ def test_gsa_zero_tensor_uses_floor():
     assert oracle.amax(neg0) == 0.0
 
 
+def _page_gsa_torch(a32: np.ndarray) -> np.ndarray:
+    """The page's expression run as the page runs it: an fp32 torch tensor
+    clamped at 1e-8, divided by the Python float 6.0 * 448.0."""
+    t = torch.from_numpy(np.ascontiguousarray(a32, np.float32))
+    return (t.clamp(min=1e-8) / (6.0 * 448.0)).numpy()
+
+
+def _gsa_sweep_values() -> np.ndarray:
+    """Every positive finite bf16 value (bit patterns 0x0001..0x7F7F, the
+    subnormals included), plus float32 values around the 1e-8 floor, zero,
+    the smallest subnormal and the largest finite float32."""
+    bf = (np.arange(1, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    assert bf.size == 32639
+    floor = np.float32(1e-8)
+    near = [floor]
+    lo = hi = floor
+    for _ in range(8):
+        lo = np.nextafter(lo, np.float32(0))
+        hi = np.nextafter(hi, np.float32(1))
+        near += [lo, hi]
+    edges = np.array(near + [0.0, np.float32(1.4e-45), np.float32(3.4028235e38),
+                             np.float32(2688.0), np.float32(1.0)], np.float32)
+    return np.concatenate([bf, edges])
+
+
+def test_gsa_matches_page_expression_on_every_bf16_amax():
+    """gsa = max(amax, 1e-8) / (6 * 448) for every positive finite bf16 amax
+    and for float32 values straddling the floor, against the page's own
+    expression evaluated by torch in float32, and against the same expression
+    in binary64 rounded once to float32 (the two agree: a binary64 quotient
+    rounded to float32 is the correctly rounded float32 quotient)."""
+    a = _gsa_sweep_values()
+    got = np.array([oracle.gsa_from_amax(float(v)) for v in a], np.float32)
+    want = _page_gsa_torch(a)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, [(float(a[i]), float(got[i]), float(want[i])) for i in bad[:5]]
+    clamped = np.maximum(a.astype(np.float64), float(np.float32(1e-8)))
+    want64 = (clamped / 2688.0).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want64.view(np.uint32))
+
+
+def test_gsa_sweep_tells_the_reciprocal_reading_apart():
+    """The sweep above discriminates: the plausible misreading
+    amax * fp32(1 / 2688) differs from the page's division on thousands of
+    bf16 amax values, so an oracle computing it would fail that test."""
+    a = _gsa_sweep_values()
+    want = _page_gsa_torch(a)
+    recip = (np.maximum(a, np.float32(1e-8)) * np.float32(1.0 / 2688.0)).astype(np.float32)
+    assert np.count_nonzero(recip.view(np.uint32) != want.view(np.uint32)) > 1000
+
+
+# Block scales: sf = E4M3_rne_satfinite(bamax / (gsa * 6)), the quotient one
+# correctly rounded float32 division by the float32 product gsa * 6.
+def _scale_quotient(bamax: np.ndarray, gsa) -> np.ndarray:
+    return (np.asarray(bamax, np.float32) / (np.float32(gsa) * np.float32(6.0))).astype(np.float32)
+
+
+def _torch_e4m3_bytes(q32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> float8_e4m3fn (round to nearest even), after the
+    saturation at 448 that the scale convention asks for (torch gives NaN
+    from 464 up)."""
+    q = np.minimum(np.asarray(q32, np.float32), np.float32(448.0))
+    return torch.from_numpy(np.ascontiguousarray(q)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+# gsa values (amax / 2688 for a few amax) whose float32 reciprocal of gsa * 6
+# is off by a sizeable fraction of an ulp, so operation-order slips show.
+NEAR_TIE_GSA = [np.float32(np.float32(a) / np.float32(2688.0))
+                for a in (3.71875, 3.28125, 2.90625, 11.375, 9.5625)]
+
+
+def _near_tie_scale_blocks(gsa: np.float32, width: int = 3) -> np.ndarray:
+    """float32 blocks whose maximum puts bamax / (gsa * 6) within `width` ulp
+    of every E4M3 rounding tie (the midpoints between consecutive finite
+    codes up to 448) and of 464 (the saturation edge); the other 15 elements
+    are smaller values of both signs."""
+    finite = np.array([oracle.e4m3_value(c) for c in range(0x7F)], np.float64)
+    ties = np.concatenate([(finite[:-1] + finite[1:]) / 2, [464.0]])
+    six = np.float32(gsa) * np.float32(6.0)
+    rows = []
+    rng = np.random.default_rng(31)
+    for t in ties:
+        centre = np.float32(t * float(six))
+        v = centre
+        cands = [centre]
+        for _ in range(width):
+            v = np.nextafter(v, np.float32(np.inf))
+            cands.append(v)
+        v = centre
+        for _ in range(width):
+            v = np.nextafter(v, np.float32(0))
+            cands.append(v)
+        for bm in cands:
+            blk = (rng.uniform(-1, 1, 16) * float(bm)).astype(np.float32)
+            blk = np.clip(blk, -bm, bm)
+            blk[rng.integers(0, 16)] = bm if rng.integers(0, 2) else -bm
+            rows.append(blk)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", ["normal", "student_t", "near_ties"])
+def test_block_scale_is_torch_e4m3_of_the_float32_quotient(case):
+    """Every block's scale byte equals torch's float8_e4m3fn of
+    float32(bamax) / (float32(gsa) * float32(6)), clamped at 448 -- on random
+    data and on blocks whose quotient sits within 3 ulp of every E4M3 tie."""
+    rng = np.random.default_rng(17)
+    if case == "near_ties":
+        cases = [(_near_tie_scale_blocks(g).reshape(-1, 16 * 7), g)  # 7 candidates per tie
+                 for g in NEAR_TIE_GSA]
+    else:
+        x = W.bf16_bits_to_f32(W.to_bf16_bits(W.draw_activation(rng, 32, 512, case)))
+        x = np.ascontiguousarray(x)
+        cases = [(x, oracle.amax_gsa(x))]
+    for x, g in cases:
+        codes, scales = oracle.quantize(x, g)
+        bamax = np.max(np.abs(x.reshape(x.shape[0], -1, 16)), axis=-1)
+        want = _torch_e4m3_bytes(_scale_quotient(bamax, g))
+        bad = np.argwhere(scales != want)
+        assert bad.size == 0, [(float(g), tuple(i), int(scales[tuple(i)]), int(want[tuple(i)]))
+                               for i in bad[:5]]
+
+
+def test_block_scale_pin_tells_other_operation_orders_apart():
+    """On the near-tie blocks, the other plausible orders -- (bamax / gsa) / 6
+    and bamax * (1 / (gsa * 6)) -- round to a different scale byte for some
+    block, so the test above fails an oracle that uses either of them."""
+    n_chained = n_recip = 0
+    for g in NEAR_TIE_GSA:
+        x = _near_tie_scale_blocks(g)
+        bamax = np.max(np.abs(x), axis=-1).astype(np.float32)
+        want = _torch_e4m3_bytes(_scale_quotient(bamax, g))
+        chained = ((bamax / g).astype(np.float32) / np.float32(6.0)).astype(np.float32)
+        recip = (bamax * (np.float32(1.0) / (g * np.float32(6.0))).astype(np.float32))
+        n_chained += np.count_nonzero(_torch_e4m3_bytes(chained) != want)
+        n_recip += np.count_nonzero(_torch_e4m3_bytes(recip.astype(np.float32)) != want)
+    assert n_chained > 0 and n_recip > 0, (n_chained, n_recip)
+
+
+def _e2m1_nearest_even(q: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 magnitude index to each float32 quotient, ties to the
+    even index, beyond 6 to 6 (numpy brute force over the page's table)."""
+    grid = np.array([float(v) for _, v in golden("e2m1_table.txt")], np.float64)
+    d = np.abs(q.astype(np.float64)[..., None] - grid)
+    cand = d == d.min(axis=-1, keepdims=True)  # one grid point, or the two of a tie
+    even = cand[..., ::2]
+    idx = np.where(even.any(axis=-1), 2 * np.argmax(even, axis=-1),
+                   2 * np.argmax(cand[..., 1::2], axis=-1) + 1)
+    return np.where(q >= 6.0, 7, idx)
+
+
+def _near_tie_code_blocks(g: np.float32, sf_byte: int):
+    """float32 blocks whose elements sit within 2 ulp of every E2M1 tie
+    (|x| / s = 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) for s = dec(sf) * gsa,
+    each block completed by the element that makes its scale byte sf_byte."""
+    sdec = np.float32(oracle.e4m3_value(sf_byte))
+    s = np.float32(sdec * g)
+    bm = np.float32(sdec * np.float32(g * np.float32(6.0)))
+    vals = []
+    for t in [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]:
+        c = np.float32(t) * s
+        vals.append(c)
+        for d in (np.float32(np.inf), np.float32(0)):
+            v = c
+            for _ in range(2):
+                v = np.nextafter(v, d)
+                vals.append(v)
+    vals = np.array(vals, np.float32)
+    vals = np.concatenate([vals, np.zeros((-vals.size) % 15, np.float32)]).reshape(-1, 15)
+    x = np.concatenate([vals, np.full((vals.shape[0], 1), bm, np.float32)], axis=1)
+    return np.ascontiguousarray(x.reshape(1, -1)), bm
+
+
+def test_codes_are_nearest_to_the_float32_quotient_near_ties():
+    """Elements within 2 ulp of every E2M1 tie, in blocks whose decoded scale
+    is not a power of two: each code is the nearest magnitude, ties to even,
+    to the float32 quotient |x| / (dec(sf) * gsa); the reciprocal reading
+    |x| * (1 / s) picks another code for some of them, so this test fails an
+    oracle that uses it."""
+    n_recip = 0
+    for g in NEAR_TIE_GSA:
+        for sf_byte in (0x5B, 0x3D, 0x4F, 0x2A):  # 22, 1.625, 7.5, 0.3125
+            x, bm = _near_tie_code_blocks(g, sf_byte)
+            codes, scales = oracle.quantize(x, g)
+            assert np.all(scales == _torch_e4m3_bytes(_scale_quotient(np.full(scales.shape, bm),
+                                                                       g)))
+            dec = np.array([oracle.e4m3_value(int(b)) for b in scales.ravel()], np.float32)
+            s_el = np.repeat((dec * g).astype(np.float32), 16)
+            q = (np.abs(x.ravel()) / s_el).astype(np.float32)
+            mag = bruteforce.unpack(codes).ravel() & 7
+            assert np.array_equal(mag, _e2m1_nearest_even(q)), (float(g), sf_byte)
+            q_recip = (np.abs(x.ravel()) * (np.float32(1.0) / s_el).astype(np.float32))
+            n_recip += np.count_nonzero(_e2m1_nearest_even(q_recip.astype(np.float32)) != mag)
+    assert n_recip > 0
+
+
 @pytest.mark.parametrize("dist", ["normal", "outliers", "student_t", "zero_blocks"])
 def test_amax_block_gets_max_scale(dist):
     """Runtime gsa makes x/gsa <= 6*448: the block holding max|x| gets the
