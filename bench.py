@@ -6,11 +6,14 @@ A step is one pass of the layer's hot path over one batch of synthetic,
 seeded input already resident in HBM: amax -> gsa, quantize from the gsa
 buffer and the block-scaled linear (for the MoE workload also SwiGLU,
 re-quantize and the second grouped linear).  Timing: W untimed eager steps,
-then the K steps are captured once in a HIP graph (launch cost off the
-critical path, as a decode loop runs), replayed once untimed, and replayed
-once more bracketed by synchronisation and events: ms_per_step = that
-replay / K.  Weight copies rotate over more than 512 MB so the 256 MB
-Infinity Cache cannot serve repeats.
+then two HIP graphs of K steps each (launch cost off the critical path, as
+a decode loop runs): the first covers steps 0..K-1 and is replayed once
+untimed; then 512 MiB are copied to another buffer (1 GiB of other
+traffic, so neither the 256 MB Infinity Cache nor any L2 holds a step's
+weights), and the second graph, steps K..2K-1, is replayed once bracketed
+by synchronisation and events: ms_per_step = that replay / K.  Step i reads
+weight copy i mod C, where the C copies span at least 512 MB: within a
+replay a copy is read again only after 512 MB of others, at any K.
 
 Headline: the decode projection (M=1, K=7168, N=1536), step = one
 nvfp4_linear_run call (amax, gsa, quantize and the weight-streaming linear
@@ -21,10 +24,16 @@ other workloads are reported under "workloads".
 
 roofline: the dominant kernel's average duration, from events around a
 graph of K back-to-back launches of that kernel alone (at M=1 the whole step
-is that one kernel).  traffic: HBM bytes per launch from the rocprofv3
-FETCH_SIZE and WRITE_SIZE summary kept under profiles/, scaled by what the
-same counters read for a copy of known size; reported only while the kernel
-sources still hash to the value recorded there.
+is that one kernel).  Beside it, two measured floors of the same launch
+shape: floor_us, an empty kernel with the same grid in a graph of K
+launches, and stream_us, a read-only pass of the same weight bytes with the
+same grid (libnvfp4_probe.so).  traffic: HBM bytes per launch from the
+rocprofv3 FETCH_SIZE and WRITE_SIZE summary kept under profiles/, scaled by
+what the same counters read for a copy of known size; reported only while
+the kernel sources still hash to the value recorded there.
+
+cpu_baseline: the oracle's step on every host core and on one, each for a
+bounded time, with the CPU model.
 
     python bench.py --pmc-probe     (the program those counter runs profile)
 
@@ -73,24 +82,44 @@ def log(*a):
 
 
 # ------------------------------------------------------------------ timing
+FLUSH_BYTES = 512 << 20
+_flush_bufs = []
+
+
+def flush_caches() -> None:
+    """Copy 512 MiB to another buffer on the current stream: 1 GiB of other
+    traffic, after which the 256 MB Infinity Cache and the L2s hold none of
+    a benchmark's inputs."""
+    if not _flush_bufs:
+        src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda").fill_(3)
+        _flush_bufs.extend([src, torch.empty_like(src)])
+    _flush_bufs[1].copy_(_flush_bufs[0])
+
+
 def graph_ms_per_step(step, steps: int, warmup: int) -> float:
-    """step(i) enqueues step i.  W eager warmup steps, then K steps captured
-    in one graph, one untimed replay, one timed replay."""
+    """step(i) enqueues step i.  W eager warmup steps; a graph of steps
+    0..K-1 replayed once untimed; the caches flushed; a graph of steps
+    K..2K-1 replayed once between events (ms per step)."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        for i in range(steps):
-            step(i)
-    graph.replay()
+    graphs = []
+    for base in (0, steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                step(base + i)
+        graphs.append(g)
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    flush_caches()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    graph.replay()
+    graphs[1].replay()
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
@@ -98,8 +127,8 @@ def graph_ms_per_step(step, steps: int, warmup: int) -> float:
 
 def kernel_us(launch, iters: int, pre=None) -> float:
     """Average duration of launch(i) alone: `iters` launches captured back to
-    back in a graph (after pre(0), which prepares the inputs), replayed once
-    untimed and once between events on the replay stream."""
+    back in a graph (after pre(0), which prepares the inputs), timed as
+    graph_ms_per_step times a step."""
     if pre is not None:
         pre(0)
     return 1e3 * graph_ms_per_step(launch, iters, 2)
@@ -326,27 +355,83 @@ def bench_quantize_weight(C, dev, steps, warmup, N=129280, K=7168):
 
 
 # ------------------------------------------------------------------ oracle
-def cpu_baseline(inp, budget_s=12.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, budget_s=10.0):
     """The oracle's step (amax, quantize, FP64 linear) for the same workload
-    on the host cores, repeated within a time budget."""
-    threads = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    on every host core this process may use, then on one core, each repeated
+    within a time budget.  Returns [(seconds per step, steps, threads)]."""
     from oracle import oracle
-    oracle._load()
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        g = oracle.amax_gsa(inp.x)
-        c, s = oracle.quantize(inp.x, g)
-        oracle.linear(c, s, g, inp.w_codes, inp.w_scales, inp.ws2)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 1000:
-            break
-    return el / n, n, int(os.environ["OMP_NUM_THREADS"])
+    legs = []
+    for threads in (len(os.sched_getaffinity(0)), 1):
+        used = oracle.set_threads(threads)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            g = oracle.amax_gsa(inp.x)
+            c, s = oracle.quantize(inp.x, g)
+            oracle.linear(c, s, g, inp.w_codes, inp.w_scales, inp.ws2)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 1000:
+                break
+        legs.append((el / n, n, used))
+    return legs
 
 
 # ------------------------------------------------------------------ probe
+_probe_lib = None
+
+
+def probe_lib():
+    """libnvfp4_probe.so: an empty kernel and a read-only stream, for the
+    measured floors of a launch shape."""
+    global _probe_lib
+    if _probe_lib is None:
+        import ctypes
+        from moe_amax_gsa_amd import build as B
+        lib = ctypes.CDLL(B.PROBE_LIB)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.probe_empty.restype = I
+        lib.probe_empty.argtypes = [I, I, P]
+        lib.probe_stream.restype = I
+        lib.probe_stream.argtypes = [P, I64, P, I64, I, I, P, P]
+        _probe_lib = lib
+    return _probe_lib
+
+
+def launch_floors(b, grid: int, threads: int, steps: int):
+    """floor_us: an empty kernel of the given grid; stream_us: a read-only
+    pass of a step's weight codes and scales (rotated copies) with that grid;
+    both as graph_ms_per_step times them."""
+    import ctypes
+    lib = probe_lib()
+    out = torch.empty(grid * (threads // 64), dtype=torch.int32, device="cuda")
+
+    def stream_of():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def empty(i):
+        assert lib.probe_empty(grid, threads, stream_of()) == 0
+
+    def stream(i):
+        wc, wsf = b.w[i % b.ncopies]
+        assert lib.probe_stream(ctypes.c_void_p(wc.data_ptr()), wc.numel(),
+                                ctypes.c_void_p(wsf.data_ptr()), wsf.numel(), grid, threads,
+                                ctypes.c_void_p(out.data_ptr()), stream_of()) == 0
+
+    return (1e3 * graph_ms_per_step(empty, steps, 2), 1e3 * graph_ms_per_step(stream, steps, 2))
+
+
 def pmc_probe(C, dev, launches=20):
     """A 256 MiB device copy (three times, to calibrate the byte counters),
     then `launches` launches of the headline step on rotated weights."""
@@ -464,16 +549,25 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        per_step_s, nrep, cores = cpu_baseline(inp)
-        cpu = {"value": b.step_bytes / per_step_s / 1e9, "unit": "GB/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"{nrep} whole oracle steps (amax, quantize, FP64 linear) of {HEAD}, "
-                         f"{per_step_s * 1e3:.1f} ms each"}
+        (t_all, n_all, c_all), (t_one, n_one, _) = cpu_baseline(inp)
+        cpu = {"value": b.step_bytes / t_all / 1e9, "unit": "GB/s", "cores": c_all,
+               "kind": "oracle", "cpu_model": cpu_model(),
+               "sample": f"{n_all} whole oracle steps (amax, quantize, FP64 linear) of {HEAD} "
+                         f"on {c_all} threads, {t_all * 1e3:.1f} ms each",
+               "one_core": {"value": b.step_bytes / t_one / 1e9, "unit": "GB/s", "cores": 1,
+                            "sample": f"{n_one} oracle steps of {HEAD} on 1 thread, "
+                                      f"{t_one * 1e3:.1f} ms each"}}
 
     # at M=1 the step is one launch of the fused kernel: its average
     # duration is the step time of the graph of K launches
     kern_us = r["step_us"]
     run_gbps = b.step_bytes / (kern_us * 1e-6) / 1e9
+    # the decode kernel's launch shape: 8 weight rows and K / 1024 waves
+    # (two 512-element sets each) per workgroup
+    grid, threads = -(-inp.N // 8), 64 * min(16, -(-inp.K // 1024))
+    log("launch floors", grid, threads)
+    floor_us, stream_us = launch_floors(b, grid, threads, args.steps)
+    wbytes = inp.w_codes.nbytes + inp.w_scales.nbytes
     traffic = recorded_traffic(os.path.join(ROOT, "profiles", "traffic_gemv_narrow_run_decode_m1_k7168_n1536.md"))
     line = {
         "metric": "NVFP4 linear decode weight-stream GB/s (M=1, K=7168, N=1536)",
@@ -495,7 +589,17 @@ def main():
                      "frac": run_gbps / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gemv_narrow_kernel, run mode (amax, gsa, quantize and linear "
                                "for one activation row in one launch)",
-                     "kernel_us": kern_us, "bytes_per_launch": b.step_bytes},
+                     "kernel_us": kern_us, "bytes_per_launch": b.step_bytes,
+                     "floor_us": floor_us, "stream_us": stream_us,
+                     "stream_GBps": wbytes / (stream_us * 1e-6) / 1e9,
+                     "floors": f"floor_us: an empty kernel of the same grid ({grid} x {threads} "
+                               f"threads); stream_us: a read-only pass of the {wbytes} weight "
+                               "bytes with that grid; each in a graph of K launches"},
+        "timing": {"graph_launches_per_replay": args.steps,
+                   "weight_copies": b.ncopies,
+                   "reuse_distance_bytes": b.ncopies * wbytes,
+                   "distinct_weight_bytes_per_replay": min(args.steps, b.ncopies) * wbytes,
+                   "flush_bytes_before_timed_replay": 2 * FLUSH_BYTES},
         "cpu_baseline": cpu,
         "workloads": workloads,
         "context": "the pages' whole-model decode on B200 took about 1.45 s per token "

@@ -321,7 +321,8 @@ int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_in
  * carry whatever h held) -- the pages' fused de-interleave + amax +
  * quantize.  With at most 2048 amax partials each quantize workgroup
  * reduces them itself, so the second amax phase and the quantize are one
- * kernel.  Needs (N_inter/2) % 16 == 0; h_codes 8-byte aligned.
+ * kernel.  Needs (N_inter/2) % 16 == 0; h_codes 8-byte aligned and h
+ * 16-byte aligned.
  * limit: the SwiGLU limit, as in nvfp4_swiglu_deinterleave.
  * M_total == 0 or N_inter == 0 only writes gsa_h (the 1e-8 floor). */
 int nvfp4_grouped_linear_swiglu(const uint8_t *a_codes, const uint8_t *a_scales,

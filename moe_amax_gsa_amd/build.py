@@ -3,7 +3,8 @@
     python -m moe_amax_gsa_amd.build
 
 Compiles every csrc/*.hip with hipcc into objects and links one shared
-library next to this file.  No JIT at import time.
+library next to this file, and the benchmark's measurement probes
+(probe/probe.hip) into a second one.  No JIT at import time.
 """
 from __future__ import annotations
 
@@ -17,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4.so")
+PROBE_SRC = os.path.join(HERE, "probe", "probe.hip")
+PROBE_LIB = os.path.join(HERE, "libnvfp4_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -39,8 +42,9 @@ def sources():
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -52,19 +56,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        objs = list(ex.map(_compile, srcs + [PROBE_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {', '.join(srcs)}")
+        print(f"built {LIB} from {', '.join(srcs)}; {PROBE_LIB} from probe/probe.hip")
     return LIB
 
 

@@ -270,8 +270,8 @@ NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* 
     return NVFP4_ERR_ALIGN;
   const bool xbf = x_dtype == NVFP4_DTYPE_BF16, ybf = y_dtype == NVFP4_DTYPE_BF16;
   hipStream_t s = (hipStream_t)stream;
-  // decode shapes: one kernel, 4 weight rows per workgroup, every workgroup
-  // quantizes the activation itself
+  // decode shapes: one kernel, 8 weight rows per workgroup (4 when N is
+  // small), every workgroup quantizes the activation itself
   if (N > 0 && gemv_narrow_run_supported(M, K, x, w_codes, w_scales))
     return launched(launch_narrow_run(x, xbf, gsa, codes, scales, w_codes, w_scales, ws2, y, ybf,
                                       M, N, K, s));
@@ -343,6 +343,8 @@ NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t*
   if ((h_codes == nullptr) != (h_scales == nullptr)) return NVFP4_ERR_NULL;  // both or neither
   if (h_codes != nullptr && (N_inter / 2) % 16 != 0) return NVFP4_ERR_SHAPE;
   if (h_codes != nullptr && !aligned(h_codes, 8)) return NVFP4_ERR_ALIGN;
+  // h's quantize reads h in 16-byte vectors
+  if (h_codes != nullptr && h != nullptr && !aligned(h, 16)) return NVFP4_ERR_ALIGN;
   if (M_total == 0 || N_inter == 0)  // the amax of nothing: gsa_h from the 1e-8 floor
     return launched(launch_amax_finalize(nullptr, 0, gsa_h, (hipStream_t)stream));
   if (a_rows == 0) return NVFP4_ERR_SHAPE;

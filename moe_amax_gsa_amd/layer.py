@@ -232,6 +232,10 @@ class Nvfp4MoE:
                                           h_codes=hc, h_scales=hs, limit=self.swiglu_limit)
         else:
             y1 = self.y1[:P]
+            # rows that belong to no group (or carry an out-of-range token) are
+            # not written by the grouped linear: zero them first, so that they
+            # give h = 0 and stay out of h's amax, as in the fused path
+            y1.zero_()
             C.nvfp4_grouped_linear(xc, xs, gsa, row_index, offsets, self.w1_codes,
                                    self.w1_scales, self.w1_ws2, y1, None, stream)
             C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream, limit=self.swiglu_limit)

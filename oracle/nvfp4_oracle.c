@@ -47,6 +47,7 @@
 #include <stddef.h>
 #include <string.h>
 #include <math.h>
+#include <omp.h>
 
 #define ORACLE_BF16 0
 #define ORACLE_FP32 1
@@ -389,4 +390,17 @@ void oracle_router_topk(const double *logits, const double *bias, int64_t M, int
             score[m * k + r] = best_s;
         }
     }
+}
+
+/* Threads of the parallel loops above (the benchmark's CPU baseline times
+ * the oracle on every host core and on one). */
+void oracle_set_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}
+
+int oracle_max_threads(void)
+{
+    return omp_get_max_threads();
 }

@@ -73,8 +73,20 @@ def _load():
     lib.oracle_router_topk.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
     lib.oracle_swiglu_deinterleave.restype = None
     lib.oracle_swiglu_deinterleave.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_double, P]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
     _lib = lib
     return lib
+
+
+def set_threads(n: int) -> int:
+    """Threads the oracle's parallel loops use from now on; returns the
+    count in effect."""
+    lib = _load()
+    lib.oracle_set_threads(int(n))
+    return lib.oracle_max_threads()
 
 
 def _ptr(a: np.ndarray) -> ctypes.c_void_p:

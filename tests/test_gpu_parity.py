@@ -699,6 +699,38 @@ def test_moe_forward_quantized_matches_forward(C):
     assert torch.equal(y1, y2)
 
 
+def test_moe_fused_and_unfused_agree_with_rows_outside_groups(C):
+    """The last three pairs belong to no expert (offsets[E] < P) and the
+    intermediate buffers hold large garbage: the grouped linear leaves those
+    rows unwritten, yet both paths keep them out of h's amax, so gsa_h and
+    every grouped row's output agree bit for bit, and gsa_h is the oracle's
+    amax over the grouped rows of h only."""
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
+    say("moe rows outside groups")
+    moe = moe_small()
+    P = int(moe.offsets[-1])
+    off_h = np.minimum(moe.offsets, P - 3).astype(np.int32)
+    w = W.moe_weights_to(moe, DEV)
+    xd = W.bf16_to_torch(moe.x, DEV)
+    ri, off = to_dev(moe.pair_token), to_dev(off_h)
+    outs = []
+    for fused in (True, False):
+        layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=moe.granularity,
+                         fused=fused)
+        assert layer.fused == fused
+        layer.h.fill_(1.0e6)
+        layer.y2.fill_(7.0)
+        if layer.y1 is not None:
+            layer.y1.fill_(-3.0e5)
+        y2 = layer(xd, ri, off).clone()
+        torch.cuda.synchronize()
+        outs.append((f32(layer.gsa2), y2[:P - 3].cpu().numpy(), layer.h[:P - 3].cpu().numpy()))
+    (gf, yf, hf), (gu, yu, hu) = outs
+    assert np.array_equal(hf, hu)
+    assert gf == gu == oracle.amax_gsa(np.ascontiguousarray(hf))
+    assert np.array_equal(yf, yu)
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 def test_moe_small_stepwise(C, fused):
     say("moe small", fused)
