@@ -81,6 +81,7 @@ extern "C" {
 #define NVFP4_ERR_WORKSPACE (-4) /* workspace NULL or smaller than needed  */
 #define NVFP4_ERR_ALIGN (-5)     /* a pointer is not aligned as required   */
 #define NVFP4_ERR_LAUNCH (-6)    /* the HIP runtime reported an error      */
+#define NVFP4_ERR_SCRATCH (-7)   /* needs more than the static scratch     */
 
 #define NVFP4_DTYPE_BF16 0
 #define NVFP4_DTYPE_FP32 1
@@ -260,6 +261,24 @@ int nvfp4_linear_run(const void *x, int x_dtype, float *gsa, uint8_t *codes, uin
                      const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2, void *y,
                      int y_dtype, int64_t M, int64_t N, int64_t K, void *ws, size_t ws_bytes,
                      void *stream);
+
+/* nvfp4_linear_run for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks, kernels and results, without the
+ * workspace.  Its scratch (the amax partials and the linear's split-K
+ * partials) is a device array of NVFP4_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; the call allocates
+ * nothing and calls no allocating routine.  A shape whose workspace,
+ * nvfp4_workspace_bytes(NVFP4_OP_LINEAR_RUN, M, N, K, 1), exceeds that size
+ * returns NVFP4_ERR_SCRATCH and launches nothing.  Every call on one GPU
+ * shares the array: calls that overlap on a GPU (other streams, other
+ * threads) race and must be ordered by the caller.  The stream must belong
+ * to the calling thread's current device. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (16u << 20)
+int nvfp4_linear_run_noalloc(const void *x, int x_dtype, float *gsa, uint8_t *codes,
+                             uint8_t *scales, const uint8_t *w_codes, const uint8_t *w_scales,
+                             const float *ws2, void *y, int y_dtype, int64_t M, int64_t N,
+                             int64_t K, void *stream);
 
 /* Grouped linear (MoE experts, or any set of G weight matrices sharing one
  * activation gsa).  Output row r, 0 <= r < M_total, belongs to group g when

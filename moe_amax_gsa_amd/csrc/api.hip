@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 7; }
+NVFP4_API int nvfp4_abi_version(void) { return 8; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -43,6 +43,8 @@ NVFP4_API const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case NVFP4_ERR_ALIGN: return "pointer not aligned as required";
     case NVFP4_ERR_LAUNCH: return "HIP launch failed";
+    case NVFP4_ERR_SCRATCH:
+      return "the call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -254,10 +256,13 @@ NVFP4_API int nvfp4_router_topk(const uint8_t* a_codes, const uint8_t* a_scales,
                                      logits, bias, M, N, topk, topk_idx, topk_score, s));
 }
 
-NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* codes,
-                               uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
-                               const float* ws2, void* y, int y_dtype, int64_t M, int64_t N,
-                               int64_t K, void* ws, size_t ws_bytes, void* stream) {
+namespace nvfp4 {
+// The argument checks of nvfp4_linear_run that come before any launch (the
+// workspace is checked where a path needs it).
+int linear_run_check(const void* x, int x_dtype, const float* gsa, const uint8_t* codes,
+                     const uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                     const float* ws2, const void* y, int y_dtype, int64_t M, int64_t N,
+                     int64_t K) {
   if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   int st = check_gemm_shape(M, N, K);
   if (st != NVFP4_OK) return st;
@@ -268,6 +273,17 @@ NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* 
   if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gsa, 4) || !aligned(w_codes, 8) ||
       !aligned(ws2, 4) || !aligned(y, y_dtype == NVFP4_DTYPE_FP32 ? 4 : 2))
     return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+}  // namespace nvfp4
+
+NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* codes,
+                               uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* ws2, void* y, int y_dtype, int64_t M, int64_t N,
+                               int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  const int st = linear_run_check(x, x_dtype, gsa, codes, scales, w_codes, w_scales, ws2, y,
+                                  y_dtype, M, N, K);
+  if (st != NVFP4_OK || M == 0) return st;
   const bool xbf = x_dtype == NVFP4_DTYPE_BF16, ybf = y_dtype == NVFP4_DTYPE_BF16;
   hipStream_t s = (hipStream_t)stream;
   // decode shapes: one kernel, 8 weight rows per workgroup (4 when N is

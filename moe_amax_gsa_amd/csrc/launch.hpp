@@ -129,6 +129,12 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
                              const float* ws2, void* y, bool y_bf16, int64_t M, int64_t N,
                              int64_t K, hipStream_t s);
 
+// The checks nvfp4_linear_run makes before any launch (an NVFP4_* status).
+int linear_run_check(const void* x, int x_dtype, const float* gsa, const uint8_t* codes,
+                     const uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                     const float* ws2, const void* y, int y_dtype, int64_t M, int64_t N,
+                     int64_t K);
+
 // Tiled GEMM for many rows (dequantize to f16, f16 matrix cores).
 // Workspace for split K (fp32 partials) when the shape has few output tiles
 // on the current device; 0 when it does not split.  Without it (ws NULL or

@@ -30,6 +30,8 @@ OP_GROUPED_SWIGLU = 5
 OP_QUANTIZE_WEIGHT = 6
 OP_RMSNORM_QUANTIZE = 7
 OP_ROUTER_TOPK = 8
+ERR_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_amax_gsa_amd.build`")
@@ -61,6 +63,9 @@ lib.nvfp4_router_topk.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, 
 lib.nvfp4_linear_run.restype = _I
 lib.nvfp4_linear_run.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ,
                                  _P]
+lib.nvfp4_linear_run_noalloc.restype = _I
+lib.nvfp4_linear_run_noalloc.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64,
+                                         _P]
 lib.nvfp4_grouped_linear.restype = _I
 lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
                                      _I64, _I64, _P, _SZ, _P]
@@ -191,6 +196,19 @@ def nvfp4_linear_run(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
                                 M, N, K, _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
                                 _stream(stream)), "nvfp4_linear_run")
+
+
+def nvfp4_linear_run_noalloc(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
+                             scales: torch.Tensor, w_codes: torch.Tensor,
+                             w_scales: torch.Tensor, ws2: torch.Tensor, y: torch.Tensor,
+                             stream=None) -> None:
+    """nvfp4_linear_run without a workspace: the library's static scratch."""
+    M, K = x.shape
+    N = w_codes.shape[0]
+    _check(lib.nvfp4_linear_run_noalloc(_ptr(x), _dtype(x), _ptr(gsa), _ptr(codes), _ptr(scales),
+                                        _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(y),
+                                        _dtype(y), M, N, K, _stream(stream)),
+           "nvfp4_linear_run_noalloc")
 
 
 def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,

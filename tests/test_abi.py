@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(C):
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert C.nvfp4_abi_version() == 7
+    assert C.nvfp4_abi_version() == 8
 
 
 def test_status_strings(C):
