@@ -394,6 +394,82 @@ __device__ __forceinline__ void quantize_half8(const float v[8], float bamax, fl
   codes = sdec == 0.0f ? e2m1_signs8(v) : e2m1_codes8(v, sc);
 }
 
+// Largest |v| of a half-block as the bits of a non-negative float (for such
+// floats the integer order is the value order, so no NaN-quieting max).
+__device__ __forceinline__ uint32_t half_absmax8_bits(const float v[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  return m;
+}
+
+// quantize_half8 for H half-blocks of one thread at once, with the same
+// results: the reciprocal-based fast paths of all H scales, then of all H
+// code words, each followed by ONE branch into the exact division for the
+// (rare) lanes near a rounding tie -- so the H independent chains
+// interleave instead of being cut apart by a branch per half-block.  The
+// E4M3 scale decodes on gfx950's fp8 converter (OCP E4M3FN, exact).
+// bamax[h]: the maximum of half-block h's whole block.
+template <int H>
+__device__ __forceinline__ void quantize_halves(const float (&v)[H][8], const float (&bamax)[H],
+                                                float gsa, uint32_t (&codes)[H],
+                                                uint32_t (&sf)[H]) {
+#pragma clang fp contract(off)
+  const float six_gsa = gsa * 6.0f;
+  const float r6 = __builtin_amdgcn_rcpf(six_gsa);
+  uint32_t dn[H];
+  bool near = false;
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const float q = bamax[h] * r6;
+    sf[h] = e4m3_encode_hw(fmaf(q, 0x1p-20f, q));
+    dn[h] = e4m3_encode_hw(fmaf(q, -0x1p-20f, q));
+    near |= sf[h] != dn[h];
+  }
+  if (near) {
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+      if (sf[h] != dn[h]) sf[h] = e4m3_encode_hw(bamax[h] / six_gsa);
+  }
+  float sc[H];
+  bool zero[H];
+  uint32_t up8[H], dn8[H];
+  near = false;
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const float sdec = __builtin_amdgcn_cvt_f32_fp8((int)sf[h], 0);
+    zero[h] = sdec == 0.0f;
+    sc[h] = zero[h] ? 1.0f : sdec * gsa;  // a zero scale keeps signs only (below)
+    const float r = __builtin_amdgcn_rcpf(sc[h]);
+    float u[8], d[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = v[h][i] * r;
+      u[i] = fmaf(q, 0x1p-20f, q);
+      d[i] = fmaf(q, -0x1p-20f, q);
+    }
+    uint32_t a = 0, b = 0;
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, u[0], u[1], 1.0f, 0);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, u[2], u[3], 1.0f, 1);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, u[4], u[5], 1.0f, 2);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, u[6], u[7], 1.0f, 3);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, d[0], d[1], 1.0f, 0);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, d[2], d[3], 1.0f, 1);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, d[4], d[5], 1.0f, 2);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, d[6], d[7], 1.0f, 3);
+    up8[h] = a;
+    dn8[h] = b;
+    near |= !zero[h] && a != b;
+  }
+  if (near) {
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+      if (!zero[h] && up8[h] != dn8[h]) up8[h] = e2m1_codes8_hw(v[h], sc[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < H; ++h) codes[h] = zero[h] ? e2m1_signs8(v[h]) : up8[h];
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations (lgkmcnt 0) but leaves vector-memory loads in flight, unlike
 // __syncthreads(), whose release fence also drains them.

@@ -785,6 +785,10 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
     }
   }
 
+  // Every wave's activation loads enter the memory pipeline before any
+  // weight load: the activation's amax and quantize are the critical path.
+  if (RUN) __builtin_amdgcn_s_barrier();
+
   int sg = wave;
   uint4 wv[S][RQ];
   uint2 fwv[S][RQ];
@@ -809,30 +813,36 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
     }
   };
   load_group(sg);
+  // all weight loads are issued before the activation is first used
+  if (RUN) __builtin_amdgcn_sched_barrier(0);
 
   float gsa_v = RUN ? 0.f : args.gsa[0];
   if (RUN) {  // quantize the activation into LDS
     float xv[HPT][8];
 #pragma unroll
     for (int u = 0; u < HPT; ++u) unpack_half8<XBF16>(xr[u], xv[u]);
-    float mx = 0.f;
+    uint32_t hb[HPT], mx = 0;  // |x| maxima as float bits
 #pragma unroll
-    for (int u = 0; u < HPT; ++u)
-      if (xok[u]) mx = fmaxf(mx, half_absmax8(xv[u]));
-    mx = wave_max_f32(mx);
-    if (lane == 0) amax_red[wave] = mx;
+    for (int u = 0; u < HPT; ++u) {
+      hb[u] = xok[u] ? half_absmax8_bits(xv[u]) : 0u;
+      mx = max(mx, hb[u]);
+    }
+    mx = wave_max_u32(mx);
+    if (lane == 0) amax_red[wave] = __uint_as_float(mx);
     lds_barrier();
     // every row of 16 lanes reads the (at most 16) wave maxima at once
-    const float mm = row16_max_f32((lane & 15) < NW ? amax_red[lane & 15] : 0.f);
-    gsa_v = gsa_from_amax(mm);
+    const uint32_t mm = row16_max_u32((lane & 15) < NW ? __float_as_uint(amax_red[lane & 15]) : 0u);
+    gsa_v = gsa_from_amax(__uint_as_float(mm));
     const bool writer = blockIdx.x == 0;
+    float bm[HPT];
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) bm[u] = __uint_as_float(max(hb[u], dpp_u32<DPP_XOR1>(hb[u])));
+    uint32_t cw[HPT], sfw[HPT];
+    quantize_halves<HPT>(xv, bm, gsa_v, cw, sfw);
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
       const int64_t h = half_of(u);
-      float bm = xok[u] ? half_absmax8(xv[u]) : 0.f;
-      bm = fmaxf(bm, xor1_f32(bm));
-      uint32_t c, sf;
-      quantize_half8(xv[u], bm, gsa_v, c, sf);
+      const uint32_t c = cw[u], sf = sfw[u];
       if (xok[u]) {
         ((uint32_t*)acl)[h] = c;
         if ((h & 1) == 0) asl[h >> 1] = (uint8_t)sf;

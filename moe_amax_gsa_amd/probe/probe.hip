@@ -22,9 +22,17 @@ __device__ __forceinline__ uint32_t xor_slice(const uint4* __restrict__ p, int64
   const int64_t b = (int64_t)blockIdx.x * per_wg;
   const int64_t e = b + per_wg < n16 ? b + per_wg : n16;
   uint32_t acc = 0;
-  for (int64_t i = b + threadIdx.x; i < e; i += blockDim.x) {
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(p + i));
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  // eight loads a thread in flight before any is used
+  for (int64_t i0 = b + threadIdx.x; i0 < e; i0 += 8 * (int64_t)blockDim.x) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * (int64_t)blockDim.x;
+      v[u] = __builtin_nontemporal_load((const u32x4*)(p + (i < e ? i : b)));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * (int64_t)blockDim.x < e) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   return acc;
 }

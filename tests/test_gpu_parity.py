@@ -271,11 +271,13 @@ def near_tie_activation(M=4, K=4096, seed=11):
     return np.ascontiguousarray(x)
 
 
-def test_quantize_near_rounding_ties(C):
+@pytest.mark.parametrize("M,K", [(4, 4096), (1, 7168), (2, 2048)])
+def test_quantize_near_rounding_ties(C, M, K):
     """Codes and scales at and around every rounding tie, through
-    quantize_from_buffer and through the one-launch decode path."""
-    say("quantize near ties")
-    x = near_tie_activation()
+    quantize_from_buffer and through the one-launch decode path (one row
+    with K = 7168 is the decode kernel's two half-blocks a lane)."""
+    say("quantize near ties", M, K)
+    x = near_tie_activation(M, K)
     M, K = x.shape
     xd = to_dev(x)
     g = gpu_gsa(C, xd)
