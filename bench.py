@@ -250,17 +250,79 @@ def bench_moe(C, dev, steps, warmup):
            "step_GBps": wbytes / (us * 1e-6) / 1e9,
            "step_frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
            "step_TFLOPs": flops / (us * 1e-6) / 1e12}
-    # the same experts (the weights depend on the seed alone) for one decoded
-    # token routed to 8 of them: context for the decode shape
-    m1 = W.make_moe(tokens=1, experts=moe.E, topk=moe.topk, seed=moe.seed, name="moe_t1")
-    x1 = W.bf16_to_torch(m1.x, dev)
-    ri1 = torch.from_numpy(m1.pair_token).to(dev)
-    off1 = torch.from_numpy(m1.offsets).to(dev)
-    b1 = len(m1.active_experts) * per_expert
-    us1 = 1e3 * graph_ms_per_step(lambda i: layer(x1, ri1, off1), steps, warmup)
+    # One decoded token routed to 8 experts.  Step i decodes token i mod 64
+    # of the same workload with its own 8 experts, so consecutive steps read
+    # different expert weights (one token's 198 MB would fit the Infinity
+    # Cache).  nvfp4_moe_run: two launches; beside it the separate calls.
+    ex = moe.pair_expert
+    singles = []
+    for t in range(moe.T):
+        es = np.sort(ex[moe.pair_token == t])
+        off1 = np.zeros(moe.E + 1, np.int32)
+        off1[es + 1] = 1
+        off1 = np.cumsum(off1).astype(np.int32)
+        singles.append((W.bf16_to_torch(moe.x[t:t + 1], dev),
+                        torch.zeros(len(es), dtype=torch.int32, device=dev),
+                        torch.from_numpy(off1).to(dev)))
+    b1 = moe.topk * per_expert
+    layer1 = Nvfp4MoE(*w, max_pairs=moe.topk, max_tokens=1, granularity=moe.granularity)
+    layer1s = Nvfp4MoE(*w, max_pairs=moe.topk, max_tokens=1, granularity=moe.granularity,
+                       run_entry=False)
+    assert layer1.run_entry
+    us1 = 1e3 * graph_ms_per_step(lambda i: layer1(*singles[i % moe.T]), steps, warmup)
+    us1s = 1e3 * graph_ms_per_step(lambda i: layer1s(*singles[i % moe.T]), steps, warmup)
     res.update({"one_token_step_us": us1, "one_token_weight_bytes": b1,
-                "one_token_GBps": b1 / (us1 * 1e-6) / 1e9})
+                "one_token_GBps": b1 / (us1 * 1e-6) / 1e9,
+                "one_token_frac_hbm": b1 / (us1 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                "one_token_launches": 2,
+                "one_token_separate_calls_us": us1s,
+                "one_token_rotation": "step i decodes token i mod 64 with its own 8 experts"})
     return res
+
+
+def bench_grouped(C, name, dev, steps, warmup):
+    """The dense grouped linear of one decoded token (nvfp4_grouped_linear_run
+    through Nvfp4GroupedLinear), weight copies rotated over 512 MB."""
+    from moe_amax_gsa_amd import workloads as W
+    from moe_amax_gsa_amd.layer import Nvfp4GroupedLinear
+    gi = W.make(name)
+    wc = torch.from_numpy(gi.w_codes).to(dev)
+    wsf = torch.from_numpy(gi.w_scales).to(dev)
+    wbytes = gi.w_codes.nbytes + gi.w_scales.nbytes
+    ncopies = max(1, min(64, -(-ROTATE_BYTES // wbytes)))
+    layers = [Nvfp4GroupedLinear(wc if k == 0 else wc.clone(), wsf if k == 0 else wsf.clone(),
+                                 torch.from_numpy(gi.ws2), max_tokens=gi.T)
+              for k in range(ncopies)]
+    o = W.bf16_to_torch(gi.x, dev).reshape(gi.T, gi.G * gi.K)
+    us = 1e3 * graph_ms_per_step(lambda i: layers[i % ncopies](o), steps, warmup)
+    nbytes = wbytes + gi.x.nbytes + gi.x.nbytes * 9 // 32 + gi.T * gi.G * gi.N * 4
+    launches = 1 if gi.T * gi.G * gi.K <= 16384 else 2
+    return {"step_us": us, "rotated_weight_copies": ncopies, "bytes_per_step": nbytes,
+            "launches": launches, "step_GBps": nbytes / (us * 1e-6) / 1e9,
+            "step_frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_big_decode(C, name, dev, steps, warmup):
+    """A one-row decode with a long weight stream (the lm_head's shape):
+    nvfp4_linear_run, and the grouped run with one group (G = 1)."""
+    from moe_amax_gsa_amd import workloads as W
+    inp = W.make(name)
+    b = LinearBench(C, inp, dev)
+    M, K, N = inp.M, inp.K, inp.N
+    off = torch.tensor([0, M], dtype=torch.int32, device=dev)
+
+    def grouped(i):
+        wc, wsf = b.w[i % b.ncopies]
+        C.nvfp4_grouped_linear_run(b.x, b.gsa, b.codes, b.scales, None, off, wc.view(1, N, K // 2),
+                                   wsf.view(1, N, K // 16), b.ws2, b.y, b.ws)
+
+    r = {"rotated_weight_copies": b.ncopies, "bytes_per_step": b.step_bytes}
+    for key, fn in [("linear_run", b.run), ("grouped_run_g1", grouped)]:
+        us = 1e3 * graph_ms_per_step(fn, steps, warmup)
+        r[key + "_us"] = us
+        r[key + "_GBps"] = b.step_bytes / (us * 1e-6) / 1e9
+        r[key + "_frac_hbm"] = r[key + "_GBps"] / HBM_PEAK_GBS
+    return r
 
 
 def bench_router(C, name, dev, steps, warmup):
@@ -541,6 +603,17 @@ def main():
             log("workload quantize_weight_n129280_k7168")
             workloads["quantize_weight_n129280_k7168"] = bench_quantize_weight(
                 C, dev, max(5, args.steps // 40), 2)
+        for name in ["grouped_wo_a_t1_g8_k8192_n1536"]:
+            if args.only and args.only != name:
+                continue
+            log("workload", name)
+            workloads[name] = bench_grouped(C, name, dev, args.steps, min(args.warmup, 10))
+        for name in ["lm_head_m1_k7168_n129280"]:
+            if args.only and args.only != name:
+                continue
+            log("workload", name)
+            workloads[name] = bench_big_decode(C, name, dev, max(10, args.steps // 4),
+                                               min(args.warmup, 3))
         if not args.only or args.only == "moe_t64_e256_top8":
             log("workload moe_t64_e256_top8")
             workloads["moe_t64_e256_top8"] = bench_moe(C, dev, max(10, args.steps // 10),

@@ -96,6 +96,8 @@ extern "C" {
 #define NVFP4_OP_QUANTIZE_WEIGHT 6
 #define NVFP4_OP_RMSNORM_QUANTIZE 7
 #define NVFP4_OP_ROUTER_TOPK 8
+#define NVFP4_OP_GROUPED_RUN 9
+#define NVFP4_OP_MOE_RUN 10
 
 /* Bytes of workspace an operation needs for the given sizes (0 if none).
  * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored;
@@ -103,7 +105,9 @@ extern "C" {
  * NVFP4_OP_GROUPED_SWIGLU, N is N_inter and G the group count; for
  * NVFP4_OP_QUANTIZE_WEIGHT, the weight is (N, K); for
  * NVFP4_OP_RMSNORM_QUANTIZE, the activation is (M, K); for
- * NVFP4_OP_ROUTER_TOPK, M rows and N experts. */
+ * NVFP4_OP_ROUTER_TOPK, M rows and N experts; for NVFP4_OP_GROUPED_RUN, x is
+ * (M, K); for NVFP4_OP_MOE_RUN, M tokens, N = N1 and K = K1 of the first
+ * projection and G experts. */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
 
 /* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
@@ -297,6 +301,71 @@ int nvfp4_grouped_linear(const uint8_t *a_codes, const uint8_t *a_scales, const 
                          const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
                          void *y, int y_dtype, int64_t N, int64_t K, void *ws,
                          size_t ws_bytes, void *stream);
+
+/* The grouped linear on a bf16/fp32 activation, steps 1-3 in as few
+ * launches as the sizes allow (the decode of G weight matrices that share
+ * one activation's global scale: the pages' dense grouped linear for wo_a,
+ * where token t's slice for group g is row t*G + g of x -- or the routed
+ * experts of a decoded token).  Same results as
+ *   nvfp4_amax_quantize(x (x_rows, K)) -> gsa, x_codes, x_scales
+ *   nvfp4_grouped_linear(x_codes, x_scales, gsa, x_rows, row_index, ...)
+ * (dsv4/_archive/layers/grouped_linear.py, _run_impl: one gsa over the whole
+ * activation, then the grouped GEMM; README.md's MoE kernel section for the
+ * routed case).  gsa, x_codes (x_rows, K/2) and x_scales (x_rows, K/16)
+ * are written as those calls write them, except that rows of x no output
+ * row reads may be left unwritten when x has more than 16384 elements.
+ * When x, w_codes and w_scales are 16-byte aligned and K % 256 == 0:
+ *   - x of at most 16384 elements: ONE launch.  Every workgroup reduces all
+ *     of x itself (so none waits on another), forms gsa, quantizes the rows
+ *     it reads into its LDS and streams its weight tiles;
+ *   - larger x: two launches, the amax partials (ws) and then the grouped
+ *     linear, every workgroup of which reduces the partials itself.
+ * Otherwise the two calls above.  ws: nvfp4_workspace_bytes(
+ * NVFP4_OP_GROUPED_RUN, x_rows, N, K, G) bytes (0 for the one-launch case),
+ * 4-byte aligned.  Row conventions and other checks as nvfp4_grouped_linear
+ * (x_codes 8-byte aligned).  x_rows == 0 writes gsa = 1e-8 / 2688 and
+ * needs M_total == 0 or N == 0. */
+int nvfp4_grouped_linear_run(const void *x, int x_dtype, int64_t x_rows, float *gsa,
+                             uint8_t *x_codes, uint8_t *x_scales, const int32_t *row_index,
+                             const int32_t *group_offsets, int G, int64_t M_total,
+                             const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
+                             void *y, int y_dtype, int64_t N, int64_t K, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* The routed-expert pair on a bf16/fp32 activation x (T, K1), the pages'
+ * Nvfp4MoE (README.md, "MoE kernel": granularity-interleaved gate/up first
+ * projection, SwiGLU, second projection; dsv4/ops/quantize.py's commit
+ * message on the fused de-interleave + amax + quantize between them).  Same
+ * results as
+ *   nvfp4_amax_quantize(x) -> gsa_x, x_codes (T, K1/2), x_scales (T, K1/16)
+ *   nvfp4_grouped_linear_swiglu(x_codes, ..., row_index, group_offsets, E, P,
+ *       w1 (E, N1, K1), ..., h (P, N1/2), gsa_h, h_codes, h_scales, ...)
+ *   nvfp4_grouped_linear(h_codes, h_scales, gsa_h, P, NULL, group_offsets,
+ *       E, P, w2 (E, N2, N1/2), ..., y (P, N2))
+ * with the same rules for rows outside every group (h, h_codes, h_scales and
+ * y are written only for rows some expert reads; h's amax covers only
+ * those rows).  Launches:
+ *   - the first projection, whose workgroups quantize x themselves when x
+ *     has at most 16384 elements (a decoded token); else x's amax and
+ *     quantize come first (one or two launches);
+ *   - the second projection, whose workgroups reduce the first's amax
+ *     partials and quantize the rows of h they read themselves, when the
+ *     first projection had at most 2048 workgroups; else h's finalize and
+ *     quantize come first.
+ * One decoded token routed to 8 experts is two launches.
+ * Requires row_index (token of each pair), granularity 1, 2, 4 or 8,
+ * N1 % (2 granularity) == 0, K1 and N1/2 multiples of 256 (short enough to
+ * stage), and every buffer but y and the scalars 16-byte aligned.
+ * ws: nvfp4_workspace_bytes(NVFP4_OP_MOE_RUN, T, N1, K1, E) bytes.
+ * limit: the SwiGLU limit, as in nvfp4_swiglu_deinterleave.  P == 0 only
+ * quantizes x and writes gsa_h = 1e-8 / 2688. */
+int nvfp4_moe_run(const void *x, int x_dtype, int64_t T, float *gsa_x, uint8_t *x_codes,
+                  uint8_t *x_scales, const int32_t *row_index, const int32_t *group_offsets,
+                  int E, int64_t P, const uint8_t *w1_codes, const uint8_t *w1_scales,
+                  const float *w1_ws2, int64_t N1, int64_t K1, int granularity, float limit,
+                  float *h, float *gsa_h, uint8_t *h_codes, uint8_t *h_scales,
+                  const uint8_t *w2_codes, const uint8_t *w2_scales, const float *w2_ws2,
+                  int64_t N2, void *y, int y_dtype, void *ws, size_t ws_bytes, void *stream);
 
 /* SwiGLU between the two expert projections, unfused: l1 (M, N_inter) fp32
  * holds gate/up column groups of `granularity` columns interleaved (group

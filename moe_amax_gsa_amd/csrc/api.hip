@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 8; }
+NVFP4_API int nvfp4_abi_version(void) { return 9; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -56,6 +56,11 @@ static size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
 
 static size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
 
+// workspace of the grouped run (the amax partials, past the one-launch size;
+// the fallback path's amax partials are never more) and of the MoE run
+static size_t grouped_run_ws_bytes_any(int64_t rows, int64_t K);
+static size_t moe_ws_bytes_any(int64_t T, int64_t N1, int64_t K1, int E);
+
 NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G) {
   (void)N;
   (void)K;
@@ -75,6 +80,8 @@ NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, 
                               : 0;
     case NVFP4_OP_GROUPED_SWIGLU:
       return (N > 0 && G > 0) ? (size_t)grouped_swiglu_parts(N, G) * sizeof(uint32_t) : 0;
+    case NVFP4_OP_GROUPED_RUN: return (M > 0 && K > 0) ? grouped_run_ws_bytes_any(M, K) : 0;
+    case NVFP4_OP_MOE_RUN: return moe_ws_bytes_any(M, N, K, G);
     default: return 0;
   }
 }
@@ -393,4 +400,176 @@ NVFP4_API int nvfp4_swiglu_deinterleave(const float* l1, float* h, int64_t M, in
   if (!aligned(l1, 4) || !aligned(h, 4)) return NVFP4_ERR_ALIGN;
   return launched(
       launch_swiglu_deinterleave(l1, h, M, N_inter, granularity, limit, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- runs
+// Activations of at most this many elements are reduced by every workgroup
+// of a grouped run itself (one launch); larger ones take a phase-1 launch.
+constexpr int64_t GROUPED_RUN_X_NUMEL = 16384;
+// At most this many amax partials are reduced by every workgroup of the
+// second expert projection itself.
+constexpr int64_t RUN_INLINE_PARTS = 2048;
+
+static size_t grouped_run_ws_bytes(int64_t rows, int64_t K) {
+  return rows * K > GROUPED_RUN_X_NUMEL ? (size_t)amax_parts_for(rows * K) * sizeof(uint32_t) : 0;
+}
+
+static int check_grouped(int64_t a_rows, const int32_t* row_index, int G, int64_t M_total,
+                         int64_t N, int64_t K) {
+  int st = check_gemm_shape(M_total, N, K);
+  if (st != NVFP4_OK) return st;
+  if (G < 1 || G > 65535 || a_rows < 0 || a_rows > I32_MAX) return NVFP4_ERR_SHAPE;
+  if (row_index == nullptr && a_rows < M_total) return NVFP4_ERR_SHAPE;
+  if (a_rows > 0 && (a_rows * (K / 16) + 255) / 256 > I32_MAX) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+NVFP4_API int nvfp4_grouped_linear_run(const void* x, int x_dtype, int64_t x_rows, float* gsa,
+                                       uint8_t* x_codes, uint8_t* x_scales,
+                                       const int32_t* row_index, const int32_t* group_offsets,
+                                       int G, int64_t M_total, const uint8_t* w_codes,
+                                       const uint8_t* w_scales, const float* ws2, void* y,
+                                       int y_dtype, int64_t N, int64_t K, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  int st = check_grouped(x_rows, row_index, G, M_total, N, K);
+  if (st != NVFP4_OK) return st;
+  if (gsa == nullptr) return NVFP4_ERR_NULL;
+  if (!aligned(gsa, 4)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (x_rows == 0)  // the amax of nothing: the 1e-8 floor; no row to read
+    return M_total == 0 || N == 0 ? launched(launch_amax_finalize(nullptr, 0, gsa, s))
+                                  : NVFP4_ERR_SHAPE;
+  if (!x || !x_codes || !x_scales || !group_offsets || !w_codes || !w_scales || !ws2 ||
+      (M_total > 0 && N > 0 && !y))
+    return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_codes, 8) || !aligned(w_codes, 8) || !aligned(ws2, 4) ||
+      !aligned(group_offsets, 4) || !aligned(row_index, 4) ||
+      !aligned(y, y_dtype == NVFP4_DTYPE_FP32 ? 4 : 2))
+    return NVFP4_ERR_ALIGN;
+  const bool xbf = x_dtype == NVFP4_DTYPE_BF16, ybf = y_dtype == NVFP4_DTYPE_BF16;
+  const int64_t numel = x_rows * K;
+  if (M_total > 0 && N > 0 && grouped_run_supported(x_rows, K, x, w_codes, w_scales)) {
+    if (numel <= GROUPED_RUN_X_NUMEL)  // one launch: every workgroup takes the amax of x
+      return launched(launch_grouped_run(x, xbf, x_rows, nullptr, 0, gsa, x_codes, x_scales,
+                                         row_index, group_offsets, G, M_total, w_codes, w_scales,
+                                         ws2, y, ybf, N, K, false, 0, 0.f, nullptr, nullptr, s));
+    // two launches: the amax partials, then the grouped linear, every
+    // workgroup of which reduces them
+    const size_t need = grouped_run_ws_bytes(x_rows, K);
+    if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+    int64_t np = 0;
+    hipError_t e = launch_amax_partials(x, xbf, numel, (uint32_t*)ws, &np, s);
+    if (e != hipSuccess) return launched(e);
+    return launched(launch_grouped_run(x, xbf, x_rows, (const uint32_t*)ws, np, gsa, x_codes,
+                                       x_scales, row_index, group_offsets, G, M_total, w_codes,
+                                       w_scales, ws2, y, ybf, N, K, false, 0, 0.f, nullptr,
+                                       nullptr, s));
+  }
+  // otherwise steps 1-2 as nvfp4_amax_quantize, then nvfp4_grouped_linear
+  hipError_t e;
+  if (amax_quantize_small_ok(x_rows, K)) {
+    e = launch_amax_quantize_small(x, xbf, x_rows, K, gsa, x_codes, x_scales, s);
+  } else {
+    const size_t need = amax_ws_bytes(numel);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+    e = launch_amax_then_quantize(x, xbf, x_rows, K, gsa, x_codes, x_scales, ws, s);
+  }
+  if (e != hipSuccess || M_total == 0 || N == 0) return launched(e);
+  return launched(launch_grouped_gemv(x_codes, x_scales, gsa, x_rows, row_index, group_offsets, G,
+                                      M_total, w_codes, w_scales, ws2, y, ybf, N, K, s));
+}
+
+static size_t moe_ws_bytes(int64_t T, int64_t N1, int64_t K1, int E) {
+  const size_t a = T > 0 ? amax_ws_bytes(T * K1) : 0;
+  const size_t b = (N1 > 0 && E > 0) ? (size_t)grouped_swiglu_parts(N1, E) * sizeof(uint32_t) : 0;
+  return a > b ? a : b;
+}
+
+NVFP4_API int nvfp4_moe_run(const void* x, int x_dtype, int64_t T, float* gsa_x,
+                            uint8_t* x_codes, uint8_t* x_scales, const int32_t* row_index,
+                            const int32_t* group_offsets, int E, int64_t P,
+                            const uint8_t* w1_codes, const uint8_t* w1_scales,
+                            const float* w1_ws2, int64_t N1, int64_t K1, int granularity,
+                            float limit, float* h, float* gsa_h, uint8_t* h_codes,
+                            uint8_t* h_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                            const float* w2_ws2, int64_t N2, void* y, int y_dtype, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
+  if (limit != limit) return NVFP4_ERR_SHAPE;  // NaN limit
+  if (T < 1 || P < 0 || N1 <= 0 || N2 <= 0) return NVFP4_ERR_SHAPE;
+  if (row_index == nullptr) return NVFP4_ERR_NULL;
+  int st = check_grouped(T, row_index, E, P, N1, K1);
+  if (st != NVFP4_OK) return st;
+  const int64_t K2 = N1 / 2;
+  if (K2 % 256 != 0) return NVFP4_ERR_SHAPE;
+  if (check_gemm_shape(P, N2, K2) != NVFP4_OK) return NVFP4_ERR_SHAPE;
+  if (!x || !gsa_x || !x_codes || !x_scales || !group_offsets || !w1_codes || !w1_scales ||
+      !w1_ws2 || !h || !gsa_h || !h_codes || !h_scales || !w2_codes || !w2_scales || !w2_ws2 ||
+      !y || !ws)
+    return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_codes, 16) || !aligned(x_scales, 16) ||
+      !aligned(w1_codes, 16) || !aligned(w1_scales, 16) || !aligned(w2_codes, 16) ||
+      !aligned(w2_scales, 16) || !aligned(h, 16) || !aligned(h_codes, 16) ||
+      !aligned(h_scales, 16) || !aligned(gsa_x, 4) || !aligned(gsa_h, 4) ||
+      !aligned(w1_ws2, 4) || !aligned(w2_ws2, 4) || !aligned(group_offsets, 4) ||
+      !aligned(row_index, 4) || !aligned(ws, 4) ||
+      !aligned(y, y_dtype == NVFP4_DTYPE_FP32 ? 4 : 2))
+    return NVFP4_ERR_ALIGN;
+  if (!grouped_swiglu_supported(N1, K1, granularity, T, x_codes, x_scales, w1_codes, w1_scales) ||
+      !grouped_run_supported(T, K1, x, w1_codes, w1_scales) ||
+      !grouped_run_supported(P > 0 ? P : 1, K2, h, w2_codes, w2_scales))
+    return NVFP4_ERR_SHAPE;
+  if (ws_bytes < moe_ws_bytes(T, N1, K1, E)) return NVFP4_ERR_WORKSPACE;
+  const bool xbf = x_dtype == NVFP4_DTYPE_BF16, ybf = y_dtype == NVFP4_DTYPE_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* parts = (uint32_t*)ws;
+  if (P == 0) {  // no pair: x is still quantized; h's amax is of nothing
+    hipError_t e = amax_quantize_small_ok(T, K1)
+                       ? launch_amax_quantize_small(x, xbf, T, K1, gsa_x, x_codes, x_scales, s)
+                       : launch_amax_then_quantize(x, xbf, T, K1, gsa_x, x_codes, x_scales, ws, s);
+    if (e != hipSuccess) return launched(e);
+    return launched(launch_amax_finalize(nullptr, 0, gsa_h, s));
+  }
+  // first projection with SwiGLU: its workgroups quantize x themselves when
+  // x is small, else x is quantized first
+  int64_t np = 0;
+  hipError_t e;
+  if (T * K1 <= GROUPED_RUN_X_NUMEL) {
+    e = launch_grouped_run(x, xbf, T, nullptr, 0, gsa_x, x_codes, x_scales, row_index,
+                           group_offsets, E, P, w1_codes, w1_scales, w1_ws2, h, false, N1, K1,
+                           true, granularity, limit, parts, &np, s);
+  } else {
+    e = amax_quantize_small_ok(T, K1)
+            ? launch_amax_quantize_small(x, xbf, T, K1, gsa_x, x_codes, x_scales, s)
+            : launch_amax_then_quantize(x, xbf, T, K1, gsa_x, x_codes, x_scales, ws, s);
+    if (e == hipSuccess)
+      e = launch_grouped_swiglu_l1(x_codes, x_scales, gsa_x, T, row_index, group_offsets, E, P,
+                                   w1_codes, w1_scales, w1_ws2, h, N1, K1, granularity, limit,
+                                   parts, &np, s);
+  }
+  if (e != hipSuccess) return launched(e);
+  // second projection: with few partials its workgroups reduce them and
+  // quantize their rows of h themselves; else h is quantized first
+  if (np <= RUN_INLINE_PARTS)
+    return launched(launch_grouped_run(h, false, P, parts, np, gsa_h, h_codes, h_scales, nullptr,
+                                       group_offsets, E, P, w2_codes, w2_scales, w2_ws2, y, ybf,
+                                       N2, K2, false, 0, 0.f, nullptr, nullptr, s));
+  e = launch_amax_finalize(parts, np, gsa_h, s);
+  if (e == hipSuccess) e = launch_quantize(h, false, P, K2, gsa_h, h_codes, h_scales, s);
+  if (e == hipSuccess)
+    e = launch_grouped_gemv(h_codes, h_scales, gsa_h, P, nullptr, group_offsets, E, P, w2_codes,
+                            w2_scales, w2_ws2, y, ybf, N2, K2, s);
+  return launched(e);
+}
+
+static size_t grouped_run_ws_bytes_any(int64_t rows, int64_t K) {
+  const size_t a = grouped_run_ws_bytes(rows, K), b = amax_ws_bytes(rows * K);
+  return a > b ? a : b;
+}
+
+static size_t moe_ws_bytes_any(int64_t T, int64_t N1, int64_t K1, int E) {
+  return moe_ws_bytes(T, N1, K1, E);
 }

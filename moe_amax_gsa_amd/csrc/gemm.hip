@@ -734,7 +734,7 @@ hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const flo
 }
 
 // Compute units of the current device (cached per device).
-static int cu_count() {
+int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -754,8 +754,8 @@ static int cu_count() {
 static int gemm_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((N + 63) / 64) * ((M + 127) / 128);
   const int64_t nch = K / 256;
-  if (2 * tiles > cu_count() || nch < 2) return 1;
-  int64_t sp = (2 * cu_count()) / tiles;
+  if (2 * tiles > device_cu_count() || nch < 2) return 1;
+  int64_t sp = (2 * device_cu_count()) / tiles;
   sp = sp < GEMM_MAX_SPLITS ? sp : GEMM_MAX_SPLITS;
   sp = sp < nch ? sp : nch;
   const int64_t cps = (nch + sp - 1) / sp;
@@ -801,11 +801,11 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     // MFMAs.  More tiles: four waves, two workgroups per CU.
     // 256 x 256 tiles where they keep at least three quarters of the CUs busy
     const int64_t wide = ((N + 255) / 256) * ((M + 255) / 256);
-    if (4 * wide >= 3 * (int64_t)cu_count())
+    if (4 * wide >= 3 * (int64_t)device_cu_count())
       return launch_wide(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M, N, K, s,
                          gsa_rows);
     const int64_t tiles = ((N + 63) / 64) * ((M + 127) / 128);
-    if (tiles <= cu_count() && K % 512 == 0)
+    if (tiles <= device_cu_count() && K % 512 == 0)
       return launch_lds<4, 2, 2, 2, 8, true>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y,
                                              y_bf16, M, N, K, s, gsa_rows);
     return launch_lds<4, 2, 2, 2, 4>(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M,

@@ -73,6 +73,19 @@ struct GemvArgs {
   // workgroups than groups, workgroup row y serves the y-th group that has
   // rows (found on the device from the offsets)
   int groups;
+  // gemv_ring_kernel quantizing its own activation rows from x (RING_Q_*):
+  // the amax partials of an earlier launch whose maximum gives gsa
+  const uint32_t* parts_in;
+  int nparts_in;
+};
+
+// Where gemv_ring_kernel's activation rows come from.
+enum {
+  RING_Q_CODES = 0,  // codes and scales in memory (a_codes, a_scales, gsa)
+  RING_Q_X = 1,      // quantized in the workgroup from x (a_rows x K), gsa
+                     // from the amax of all of x, which every workgroup takes
+  RING_Q_PARTS = 2,  // quantized in the workgroup from x, gsa from the maximum
+                     // of parts_in (an earlier launch's first amax phase)
 };
 
 __device__ __forceinline__ float4_t mfma_fp4(v8i a, v8i b) {
@@ -429,6 +442,77 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
+// ---- a ring workgroup that quantizes its own activation rows (RING_Q_X,
+// RING_Q_PARTS).  The amax is still a grid-wide maximum reached without any
+// workgroup waiting on another: with RING_Q_X every workgroup reduces all of
+// the (small) x itself; with RING_Q_PARTS it reduces the partial maxima that
+// an earlier launch wrote, which stream order completes first.
+
+// gsa for every thread; partial maxima are bits of non-negative floats in the
+// format of x (bf16 or fp32).  Ends with a workgroup barrier.
+template <int QIN, bool XBF16, int W>
+__device__ __forceinline__ float ring_gsa(const GemvArgs& args) {
+  __shared__ uint32_t qred[W];
+  uint32_t m = 0;
+  if (QIN == RING_Q_X) {
+    m = thread_absmax<XBF16>(args.x, (int64_t)args.a_rows * args.K, threadIdx.x, W * 64);
+  } else {
+    for (int t = threadIdx.x; t < args.nparts_in; t += W * 64) m = max(m, args.parts_in[t]);
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) qred[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t mm = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) mm = max(mm, qred[w]);
+  return gsa_from_bits<XBF16>(mm);
+}
+
+// Quantize half-blocks [0, nh) of rows whose half-block i lies in row
+// src_of(i / hpr) of x, at position i % hpr (hpr = K / 8 half-blocks a row):
+// put(i, row, hh, code word, scale byte) stores each one.  The loop runs a
+// uniform number of trips so that every lane takes part in src_of's shuffle;
+// half-blocks 2b and 2b+1 of a block sit in adjacent lanes (W * 64 and hpr
+// are even).
+template <bool XBF16, int W, typename SrcOf, typename Put>
+__device__ __forceinline__ void ring_quantize(const GemvArgs& args, int nh, float gsa,
+                                              SrcOf src_of, Put put) {
+  const int hpr = args.K / 8;
+  const int trips = (nh + W * 64 - 1) / (W * 64);
+  for (int it = 0; it < trips; ++it) {
+    const int i = (int)threadIdx.x + it * W * 64;
+    const bool in = i < nh;
+    const int rl = in ? i / hpr : 0;
+    const int hh = in ? i - rl * hpr : 0;
+    const int src = src_of(rl);
+    const bool ok = in && src >= 0;
+    uint4 raw[2];
+    load_half8_raw<XBF16>(args.x, ok ? (int64_t)src * hpr + hh : 0, raw);
+    float v[1][8];
+    unpack_half8<XBF16>(raw, v[0]);
+    const uint32_t hb = ok ? half_absmax8_bits(v[0]) : 0u;
+    const float bm[1] = {__uint_as_float(max(hb, dpp_u32<DPP_XOR1>(hb)))};
+    uint32_t c[1], sf[1];
+    quantize_halves<1>(v, bm, gsa, c, sf);
+    if (ok) put(rl, src, hh, c[0], sf[0]);
+  }
+}
+
+// Workgroup (0, 0)'s extra duty: gsa to gsa_out and, with RING_Q_X, every
+// row of x quantized to codes_out / scales_out (when given).
+template <int QIN, bool XBF16, int W>
+__device__ __forceinline__ void ring_write_x(const GemvArgs& args, float gsa) {
+  if (threadIdx.x == 0 && args.gsa_out != nullptr) args.gsa_out[0] = gsa;
+  if (QIN != RING_Q_X || args.codes_out == nullptr) return;
+  const int64_t cbytes = args.K / 2, sbytes = args.K / 16;
+  ring_quantize<XBF16, W>(
+      args, args.a_rows * (args.K / 8), gsa, [](int rl) { return rl; },
+      [&](int, int src, int hh, uint32_t c, uint32_t sf) {
+        ((uint32_t*)(args.codes_out + src * cbytes))[hh] = c;
+        if ((hh & 1) == 0) args.scales_out[src * sbytes + hh / 2] = (uint8_t)sf;
+      });
+}
+
 // SWIGLU: the output columns are gate/up groups of args.gran columns
 // interleaved (group q is gate when q is even, and gate group 2p pairs with
 // up group 2p+1); instead of those columns the epilogue writes
@@ -436,7 +520,9 @@ __device__ __forceinline__ void wait_vm(int n) {
 // workgroup writes the largest |h| it wrote to args.partials (the first
 // phase of h's amax).  A wave's 16 columns hold whole pairs (gran divides 8):
 // the up value of gate column c sits in lane c ^ gran.
-template <int MP, int D, int W, bool SWIGLU = false>
+// QIN: where the activation rows come from (RING_Q_*); XBF16: x's format
+// when the workgroup quantizes them.
+template <int MP, int D, int W, bool SWIGLU = false, int QIN = RING_Q_CODES, bool XBF16 = true>
 __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) {
   static_assert(2 * (D - 1) <= 14, "wait_vm range");
   constexpr int ROWS = 2 * MP;
@@ -471,6 +557,8 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
     g = __builtin_amdgcn_readfirstlane(sel);  // uniform after the barrier
     if (g < 0) {  // fewer groups with rows than workgroup rows
       if (SWIGLU && threadIdx.x == 0) args.partials[blockIdx.y * gridDim.x + blockIdx.x] = 0u;
+      if (QIN != RING_Q_CODES && blockIdx.x == 0 && blockIdx.y == 0)
+        ring_write_x<QIN, XBF16, W>(args, ring_gsa<QIN, XBF16, W>(args));
       return;
     }
   }
@@ -481,8 +569,11 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
   }
   if (r_begin >= r_end) {  // uniform over the workgroup
     if (SWIGLU && threadIdx.x == 0) args.partials[blockIdx.y * gridDim.x + blockIdx.x] = 0u;
+    if (QIN != RING_Q_CODES && blockIdx.x == 0 && blockIdx.y == 0)
+      ring_write_x<QIN, XBF16, W>(args, ring_gsa<QIN, XBF16, W>(args));
     return;
   }
+  float gsa_q = 0.f;  // QIN: the gsa this workgroup forms
   float hmax = 0.f;  // SWIGLU: largest |h| this thread wrote
 
   const int n0 = (blockIdx.x * W + wave) * 16;
@@ -560,24 +651,48 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
       }
       for (int c = 0; c < D && c < nsc; ++c) issue_slot(c);
     }
-    // the pass rows' activation codes and scales (a missing row copies row 0
-    // and is masked below)
-    const int ncp = ROWS * cpr, nsp = ROWS * spr;
-    for (int base = wave * 64; base < ncp; base += W * 64) {
-      const int e = base + lane;
-      const int rl = e / cpr, q = e - rl * cpr;
-      const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
-      if (e < ncp)
-        load_lds16(args.a_codes, (uint32_t)((int64_t)max(src, 0) * cbytes + 16 * q),
-                   lds0 + 16 * (uint32_t)base);
-    }
-    for (int base = wave * 64; base < nsp; base += W * 64) {
-      const int e = base + lane;
-      const int rl = e / spr, q = e - rl * spr;
-      const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
-      if (e < nsp)
-        load_lds16(args.a_scales, (uint32_t)((int64_t)max(src, 0) * sbytes + 16 * q),
-                   lds0 + (uint32_t)(ROWS * cbytes) + 16 * (uint32_t)base);
+    if (QIN == RING_Q_CODES) {
+      // the pass rows' activation codes and scales (a missing row copies row
+      // 0 and is masked below)
+      const int ncp = ROWS * cpr, nsp = ROWS * spr;
+      for (int base = wave * 64; base < ncp; base += W * 64) {
+        const int e = base + lane;
+        const int rl = e / cpr, q = e - rl * cpr;
+        const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
+        if (e < ncp)
+          load_lds16(args.a_codes, (uint32_t)((int64_t)max(src, 0) * cbytes + 16 * q),
+                     lds0 + 16 * (uint32_t)base);
+      }
+      for (int base = wave * 64; base < nsp; base += W * 64) {
+        const int e = base + lane;
+        const int rl = e / spr, q = e - rl * spr;
+        const int src = __shfl(my_src, rl < ROWS ? rl : 0, 64);
+        if (e < nsp)
+          load_lds16(args.a_scales, (uint32_t)((int64_t)max(src, 0) * sbytes + 16 * q),
+                     lds0 + (uint32_t)(ROWS * cbytes) + 16 * (uint32_t)base);
+      }
+    } else {
+      // the workgroup quantizes the pass rows itself, after the weight loads
+      // above are on their way
+      if (r0 == r_begin) {
+        gsa_q = ring_gsa<QIN, XBF16, W>(args);
+        if (blockIdx.x == 0 && blockIdx.y == 0) ring_write_x<QIN, XBF16, W>(args, gsa_q);
+      }
+      // with RING_Q_PARTS the first tile's workgroup of a group also stores
+      // the codes of the rows it reads
+      const bool out = QIN == RING_Q_PARTS && blockIdx.x == 0 && args.codes_out != nullptr;
+      uint8_t* act = lds;
+      ring_quantize<XBF16, W>(
+          args, min(ROWS, r_end - r0) * (K / 8), gsa_q,
+          [&](int rl) { return __shfl(my_src, rl, 64); },
+          [&](int rl, int src, int hh, uint32_t c, uint32_t sf) {
+            ((uint32_t*)(act + rl * cbytes))[hh] = c;
+            if ((hh & 1) == 0) act[ROWS * cbytes + rl * sbytes + hh / 2] = (uint8_t)sf;
+            if (out) {
+              ((uint32_t*)(args.codes_out + src * cbytes))[hh] = c;
+              if ((hh & 1) == 0) args.scales_out[src * sbytes + hh / 2] = (uint8_t)sf;
+            }
+          });
     }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -635,7 +750,7 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
         }
       }
 
-      const float gscale = args.gsa[0] * args.ws2[g];
+      const float gscale = (QIN == RING_Q_CODES ? args.gsa[0] : gsa_q) * args.ws2[g];
 #pragma unroll
       for (int p = 0; p < MP; ++p) {
         const float v = acc[p] + __shfl_xor(acc[p], 16, 64);
@@ -682,13 +797,13 @@ static size_t ring_lds_bytes(int64_t K) {
          (size_t)W * (size_t)(K + D * RING_SLOT);
 }
 
-template <int MP, int D, int W, bool SWIGLU>
+template <int MP, int D, int W, bool SWIGLU, int QIN = RING_Q_CODES, bool XBF16 = true>
 static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
   const size_t lds = ring_lds_bytes<MP, D, W>(a.K);
   if (lds > 64 * 1024) {  // the largest any launch may ask for (callers keep lds below it)
     static unsigned char done[64];
-    const hipError_t e = allow_dynamic_lds((const void*)gemv_ring_kernel<MP, D, W, SWIGLU>,
-                                           RING_MAX_LDS, done);
+    const hipError_t e = allow_dynamic_lds(
+        (const void*)gemv_ring_kernel<MP, D, W, SWIGLU, QIN, XBF16>, RING_MAX_LDS, done);
     if (e != hipSuccess) return e;
   }
   // at most M groups have rows: with fewer rows than groups, launch a row of
@@ -697,7 +812,7 @@ static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
   b.groups = G;
   const int gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
   const dim3 grid((unsigned)((a.N + 16 * W - 1) / (16 * W)), (unsigned)gy);
-  gemv_ring_kernel<MP, D, W, SWIGLU><<<grid, W * 64, lds, s>>>(b);
+  gemv_ring_kernel<MP, D, W, SWIGLU, QIN, XBF16><<<grid, W * 64, lds, s>>>(b);
   return hipGetLastError();
 }
 
@@ -966,12 +1081,12 @@ static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hip
 // Grouped linear through the LDS ring with one configuration, if its LDS
 // fits RING_MAX_LDS (false: K too long to stage).  *parts: the grid's
 // workgroup count (SwiGLU amax partials).
-template <int MP, int D, int W, bool SWIGLU>
+template <int MP, int D, int W, bool SWIGLU, int QIN = RING_Q_CODES, bool XBF16 = true>
 static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err, int64_t* parts) {
   if (ring_lds_bytes<MP, D, W>(a.K) > RING_MAX_LDS) return false;
   const int64_t gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
   *parts = (int64_t)((a.N + 16 * W - 1) / (16 * W)) * gy;
-  *err = launch_ring_t<MP, D, W, SWIGLU>(a, G, s);
+  *err = launch_ring_t<MP, D, W, SWIGLU, QIN, XBF16>(a, G, s);
   return true;
 }
 
@@ -986,6 +1101,79 @@ static bool launch_ring(const GemvArgs& a, int G, int64_t mean_rows, hipStream_t
          ring_try<4, 3, 4, SWIGLU>(a, G, s, err, parts) ||
          ring_try<2, 3, 4, SWIGLU>(a, G, s, err, parts) ||
          ring_try<1, 3, 2, SWIGLU>(a, G, s, err, parts);
+}
+
+// The ring with workgroups that quantize their own activation rows (QIN):
+// eight waves of 16 weight rows a workgroup where that still gives a
+// workgroup per CU, else two waves (four times the workgroups); two rows a
+// pass for decode-sized groups, eight otherwise.
+template <bool SWIGLU, int QIN, bool XBF16>
+static bool launch_ring_q(const GemvArgs& a, int G, int64_t mean_rows, hipStream_t s,
+                          hipError_t* err, int64_t* parts) {
+  const int64_t gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
+  const bool wide = ((a.N + 127) / 128) * gy >= device_cu_count();
+  if (mean_rows <= 2) {
+    if (wide && ring_try<1, 3, 8, SWIGLU, QIN, XBF16>(a, G, s, err, parts)) return true;
+    return ring_try<1, 3, 2, SWIGLU, QIN, XBF16>(a, G, s, err, parts);
+  }
+  if (wide && ring_try<4, 3, 8, SWIGLU, QIN, XBF16>(a, G, s, err, parts)) return true;
+  return ring_try<4, 3, 2, SWIGLU, QIN, XBF16>(a, G, s, err, parts) ||
+         ring_try<1, 3, 2, SWIGLU, QIN, XBF16>(a, G, s, err, parts);
+}
+
+bool grouped_run_supported(int64_t x_rows, int64_t K, const void* x, const uint8_t* w_codes,
+                           const uint8_t* w_scales) {
+  return K % 256 == 0 && K >= 256 && x_rows >= 1 && x_rows * (K / 2) < ((int64_t)1 << 31) &&
+         aligned16(x) && aligned16(w_codes) && aligned16(w_scales) &&
+         ring_lds_bytes<1, 3, 2>(K) <= RING_MAX_LDS;
+}
+
+hipError_t launch_grouped_run(const void* x, bool x_bf16, int64_t x_rows, const uint32_t* parts,
+                              int64_t nparts, float* gsa_out, uint8_t* codes_out,
+                              uint8_t* scales_out, const int32_t* row_index,
+                              const int32_t* offsets, int G, int64_t M_total,
+                              const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                              void* y, bool y_bf16, int64_t N, int64_t K, bool swiglu, int gran,
+                              float limit, uint32_t* partials_out, int64_t* nparts_out,
+                              hipStream_t s) {
+  GemvArgs a{};
+  a.x = x;
+  a.parts_in = parts;
+  a.nparts_in = (int)nparts;
+  a.gsa_out = gsa_out;
+  a.codes_out = codes_out;
+  a.scales_out = scales_out;
+  a.row_index = row_index;
+  a.offsets = offsets;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.ws2 = ws2;
+  a.y = y;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.M = (int)M_total;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.a_rows = (int)x_rows;
+  a.gran = gran;
+  a.limit = limit;
+  a.partials = partials_out;
+  const int64_t mean_rows = (M_total + G - 1) / G;
+  hipError_t err = hipSuccess;
+  int64_t np = 0;
+  bool ok;
+  if (parts != nullptr) {
+    ok = x_bf16 ? (swiglu ? launch_ring_q<true, RING_Q_PARTS, true>(a, G, mean_rows, s, &err, &np)
+                          : launch_ring_q<false, RING_Q_PARTS, true>(a, G, mean_rows, s, &err, &np))
+                : (swiglu ? launch_ring_q<true, RING_Q_PARTS, false>(a, G, mean_rows, s, &err, &np)
+                          : launch_ring_q<false, RING_Q_PARTS, false>(a, G, mean_rows, s, &err, &np));
+  } else {
+    ok = x_bf16 ? (swiglu ? launch_ring_q<true, RING_Q_X, true>(a, G, mean_rows, s, &err, &np)
+                          : launch_ring_q<false, RING_Q_X, true>(a, G, mean_rows, s, &err, &np))
+                : (swiglu ? launch_ring_q<true, RING_Q_X, false>(a, G, mean_rows, s, &err, &np)
+                          : launch_ring_q<false, RING_Q_X, false>(a, G, mean_rows, s, &err, &np));
+  }
+  if (nparts_out) *nparts_out = np;
+  return ok ? err : hipErrorInvalidValue;
 }
 
 // Most workgroups any ring configuration launches for (N, G): the size of
@@ -1233,6 +1421,35 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
   err = launch_amax_finalize(partials, parts, gsa_h, s);
   if (err != hipSuccess) return err;
   return launch_quantize(h, false, M_total, N / 2, gsa_h, h_codes, h_scales, s);
+}
+
+hipError_t launch_grouped_swiglu_l1(const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const float* gsa, int64_t a_rows, const int32_t* row_index,
+                                    const int32_t* offsets, int G, int64_t M_total,
+                                    const uint8_t* w_codes, const uint8_t* w_scales,
+                                    const float* ws2, float* h, int64_t N, int64_t K, int gran,
+                                    float limit, uint32_t* partials, int64_t* nparts,
+                                    hipStream_t s) {
+  GemvArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.gsa = gsa;
+  a.row_index = row_index;
+  a.offsets = offsets;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.ws2 = ws2;
+  a.y = h;
+  a.M = (int)M_total;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.a_rows = (int)a_rows;
+  a.gran = gran;
+  a.limit = limit;
+  a.partials = partials;
+  hipError_t err = hipSuccess;
+  if (!launch_ring<true>(a, G, (M_total + G - 1) / G, s, &err, nparts)) return hipErrorInvalidValue;
+  return err;
 }
 
 bool gemv_run_supported(int64_t M, int64_t K, const void* x, const uint8_t* w_codes,

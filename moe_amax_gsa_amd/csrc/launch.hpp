@@ -29,6 +29,11 @@ int amax_parts_for(int64_t numel);
 hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, void* ws,
                            hipStream_t s);
 
+// Phase 1 alone: amax_parts_for(numel) partial maxima (bits in x's format)
+// into partials; their count in *nparts.
+hipError_t launch_amax_partials(const void* x, bool bf16, int64_t numel, uint32_t* partials,
+                                int64_t* nparts, hipStream_t s);
+
 // amax -> gsa -> quantize in one workgroup (at most 4096 blocks)
 bool amax_quantize_small_ok(int64_t M, int64_t K);
 hipError_t launch_amax_quantize_small(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
@@ -108,6 +113,17 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
                                  int gran, float limit, uint32_t* partials, uint8_t* h_codes,
                                  uint8_t* h_scales, hipStream_t s);
 
+// The gate/up linear with SwiGLU, de-interleave and the first amax phase of
+// h (one partial per workgroup into partials, their count in *nparts), and
+// nothing after it.
+hipError_t launch_grouped_swiglu_l1(const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const float* gsa, int64_t a_rows, const int32_t* row_index,
+                                    const int32_t* offsets, int G, int64_t M_total,
+                                    const uint8_t* w_codes, const uint8_t* w_scales,
+                                    const float* ws2, float* h, int64_t N, int64_t K, int gran,
+                                    float limit, uint32_t* partials, int64_t* nparts,
+                                    hipStream_t s);
+
 // amax -> gsa -> quantize -> linear in one kernel for a few activation rows.
 constexpr int64_t GEMV_RUN_MAX_M = 16;
 constexpr int64_t GEMV_RUN_MAX_LDS = 65536;  // activation codes + scales held in LDS
@@ -128,6 +144,30 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
                              uint8_t* scales, const uint8_t* w_codes, const uint8_t* w_scales,
                              const float* ws2, void* y, bool y_bf16, int64_t M, int64_t N,
                              int64_t K, hipStream_t s);
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count();
+
+// Grouped linear (or one projection: offsets NULL, G = 1) whose workgroups
+// quantize their activation rows themselves from x (x_rows, K), bf16 or
+// fp32, in ONE launch.  gsa: parts == NULL, from the amax of all of x, which
+// every workgroup takes (keep x small); else from the maximum of the nparts
+// partial maxima an earlier launch wrote (bits in x's format).  Workgroup
+// (0, 0) writes gsa_out; codes_out / scales_out (or NULL) receive every row
+// of x (parts == NULL) or the rows some group reads.  swiglu: the epilogue
+// of nvfp4_grouped_linear_swiglu (y = h, partials_out gets one partial per
+// workgroup, *nparts_out their count).  false from grouped_run_supported:
+// not for these operands.
+bool grouped_run_supported(int64_t x_rows, int64_t K, const void* x, const uint8_t* w_codes,
+                           const uint8_t* w_scales);
+hipError_t launch_grouped_run(const void* x, bool x_bf16, int64_t x_rows, const uint32_t* parts,
+                              int64_t nparts, float* gsa_out, uint8_t* codes_out,
+                              uint8_t* scales_out, const int32_t* row_index,
+                              const int32_t* offsets, int G, int64_t M_total,
+                              const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
+                              void* y, bool y_bf16, int64_t N, int64_t K, bool swiglu, int gran,
+                              float limit, uint32_t* partials_out, int64_t* nparts_out,
+                              hipStream_t s);
 
 // The checks nvfp4_linear_run makes before any launch (an NVFP4_* status).
 int linear_run_check(const void* x, int x_dtype, const float* gsa, const uint8_t* codes,

@@ -99,6 +99,25 @@ int amax_parts_for(int64_t numel) {
   return (int)p;
 }
 
+hipError_t launch_amax_partials(const void* x, bool bf16, int64_t numel, uint32_t* partials,
+                                int64_t* nparts, hipStream_t s) {
+  const int parts = amax_parts_for(numel);
+  *nparts = parts;
+  const bool nt = numel * (bf16 ? 2 : 4) >= STREAM_BYTES;
+  if (bf16) {
+    if (nt)
+      amax_partial_kernel<true, true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    else
+      amax_partial_kernel<true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+  } else {
+    if (nt)
+      amax_partial_kernel<false, true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+    else
+      amax_partial_kernel<false><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_amax_gsa(const void* x, bool bf16, int64_t numel, float* gsa, void* ws,
                            hipStream_t s) {
   if (numel <= AMAX_SMALL_NUMEL) {

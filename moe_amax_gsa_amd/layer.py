@@ -172,12 +172,14 @@ class Nvfp4MoE:
     gate/up column groups interleaved at ``granularity``; L2 weights
     (E, N2, N1/4) consume the SwiGLU output of width N1/2.  swiglu_limit > 0
     caps the gate at the limit and clamps up to [-limit, limit] before
-    silu(gate) * up (0: no clamp).
+    silu(gate) * up (0: no clamp).  forward runs the pair through
+    nvfp4_moe_run where its conditions hold (run_entry), else as separate
+    calls; forward_quantized always takes the separate calls.
     """
 
     def __init__(self, w1_codes, w1_scales, w1_ws2, w2_codes, w2_scales, w2_ws2, max_pairs: int,
                  max_tokens: int, granularity: int = 8, fused: bool = True,
-                 swiglu_limit: float = 0.0):
+                 swiglu_limit: float = 0.0, run_entry: bool = True):
         dev = w1_codes.device
         self.device = dev
         self.swiglu_limit = float(swiglu_limit)
@@ -211,10 +213,26 @@ class Nvfp4MoE:
         self.h_codes = torch.empty(max_pairs, self.K2 // 2, dtype=torch.uint8, device=dev)
         self.h_scales = torch.empty(max_pairs, self.K2 // 16, dtype=torch.uint8, device=dev)
         self.y2 = torch.empty(max_pairs, self.N2, dtype=torch.float32, device=dev)
+        # the whole pair through nvfp4_moe_run (two launches for a decoded
+        # token): its conditions on top of the fused path's
+        self.run_entry = bool(run_entry and self.fused and self.K2 % 256 == 0
+                              and self.w2_codes.data_ptr() % 16 == 0
+                              and self.w2_scales.data_ptr() % 16 == 0)
+        self.ws_run = torch.empty(
+            max(C.nvfp4_workspace_bytes(C.OP_MOE_RUN, max_tokens, self.N1, self.K1, self.E), 16),
+            dtype=torch.uint8, device=dev)
 
     def forward(self, x, row_index, offsets, stream=None) -> torch.Tensor:
         T = x.shape[0]
         xc, xs = self.x_codes[:T], self.x_scales[:T]
+        if self.run_entry and x.data_ptr() % 16 == 0:
+            P = row_index.shape[0]
+            y2 = self.y2[:P]
+            C.nvfp4_moe_run(x, self.gsa1, xc, xs, row_index, offsets, self.w1_codes,
+                            self.w1_scales, self.w1_ws2, self.granularity, self.h[:P], self.gsa2,
+                            self.h_codes[:P], self.h_scales[:P], self.w2_codes, self.w2_scales,
+                            self.w2_ws2, y2, self.ws_run, limit=self.swiglu_limit, stream=stream)
+            return y2
         C.nvfp4_amax_quantize(x, self.gsa1, xc, xs, self.ws, stream)
         return self.forward_quantized(xc, xs, self.gsa1, row_index, offsets, stream)
 
@@ -245,5 +263,57 @@ class Nvfp4MoE:
         C.nvfp4_grouped_linear(hc, hs, self.gsa2, None, offsets, self.w2_codes, self.w2_scales,
                                self.w2_ws2, y2, None, stream)
         return y2
+
+    __call__ = forward
+
+
+class Nvfp4GroupedLinear:
+    """The dense grouped linear (the pages' wo_a): z = Nvfp4GroupedLinear(o)
+    for o (T, G * K) bf16/fp32 -> z (G, T, N), z[g, t] = token t's slice
+    o[t, g*K:(g+1)*K] through group g's weight, with one gsa over all of o
+    (dsv4/_archive/layers/grouped_linear.py, _run_impl).  Weights are stacked
+    (G, N, K/2) and (G, N, K/16) with ws2 (G,).  One launch
+    (nvfp4_grouped_linear_run) while o has at most 16384 elements, two
+    beyond."""
+
+    def __init__(self, w_codes: torch.Tensor, w_scales: torch.Tensor, ws2, max_tokens: int,
+                 out_dtype=torch.float32):
+        dev = w_codes.device
+        self.device = dev
+        self.G, self.N, self.K = w_codes.shape[0], w_codes.shape[1], w_codes.shape[2] * 2
+        self.w_codes, self.w_scales = w_codes.contiguous(), w_scales.contiguous()
+        self.ws2 = ws2.to(device=dev, dtype=torch.float32).contiguous()
+        self.max_tokens = max_tokens
+        rows = max_tokens * self.G
+        self.gsa = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.codes = torch.empty(rows, self.K // 2, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(rows, self.K // 16, dtype=torch.uint8, device=dev)
+        self.y = torch.empty(rows, self.N, dtype=out_dtype, device=dev)
+        self.ws = torch.empty(
+            max(C.nvfp4_workspace_bytes(C.OP_GROUPED_RUN, rows, self.N, self.K, self.G), 16),
+            dtype=torch.uint8, device=dev)
+        self._routes = {}
+
+    def routes(self, T: int):
+        """(row_index, offsets) for T tokens: group g's rows g*T .. g*T+T-1
+        read slices t*G + g (built once per T, on the device)."""
+        if T not in self._routes:
+            G = self.G
+            ri = (torch.arange(T, device=self.device)[None, :] * G +
+                  torch.arange(G, device=self.device)[:, None]).reshape(-1).to(torch.int32)
+            off = (torch.arange(G + 1, device=self.device) * T).to(torch.int32)
+            self._routes[T] = (ri.contiguous(), off.contiguous())
+        return self._routes[T]
+
+    def forward(self, o: torch.Tensor, stream=None) -> torch.Tensor:
+        T = o.shape[0]
+        assert T <= self.max_tokens and o.shape[1] == self.G * self.K
+        x = o.reshape(T * self.G, self.K)
+        ri, off = self.routes(T)
+        rows = T * self.G
+        y = self.y[:rows]
+        C.nvfp4_grouped_linear_run(x, self.gsa, self.codes[:rows], self.scales[:rows], ri, off,
+                                   self.w_codes, self.w_scales, self.ws2, y, self.ws, stream)
+        return y.view(self.G, T, self.N)
 
     __call__ = forward

@@ -30,6 +30,8 @@ OP_GROUPED_SWIGLU = 5
 OP_QUANTIZE_WEIGHT = 6
 OP_RMSNORM_QUANTIZE = 7
 OP_ROUTER_TOPK = 8
+OP_GROUPED_RUN = 9
+OP_MOE_RUN = 10
 ERR_SCRATCH = -7
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -80,6 +82,13 @@ lib.nvfp4_grouped_linear_swiglu.restype = _I
 lib.nvfp4_grouped_linear_swiglu.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P,
                                             _P, _P, _P, _I64, _I64, _I, ctypes.c_float, _P, _SZ,
                                             _P]
+lib.nvfp4_grouped_linear_run.restype = _I
+lib.nvfp4_grouped_linear_run.argtypes = [_P, _I, _I64, _P, _P, _P, _P, _P, _I, _I64, _P, _P, _P,
+                                         _P, _I, _I64, _I64, _P, _SZ, _P]
+lib.nvfp4_moe_run.restype = _I
+lib.nvfp4_moe_run.argtypes = [_P, _I, _I64, _P, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _I64, _I64,
+                              _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _I, _P,
+                              _SZ, _P]
 lib.nvfp4_swiglu_deinterleave.restype = _I
 lib.nvfp4_swiglu_deinterleave.argtypes = [_P, _P, _I64, _I64, _I, ctypes.c_float, _P]
 
@@ -291,3 +300,45 @@ def nvfp4_swiglu_deinterleave(l1: torch.Tensor, h: torch.Tensor, granularity: in
     M, NI = l1.shape
     _check(lib.nvfp4_swiglu_deinterleave(_ptr(l1), _ptr(h), M, NI, granularity, limit,
                                          _stream(stream)), "nvfp4_swiglu_deinterleave")
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def nvfp4_grouped_linear_run(x: torch.Tensor, gsa: torch.Tensor, x_codes: torch.Tensor,
+                             x_scales: torch.Tensor, row_index: Optional[torch.Tensor],
+                             group_offsets: torch.Tensor, w_codes: torch.Tensor,
+                             w_scales: torch.Tensor, ws2: torch.Tensor, y: torch.Tensor,
+                             ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Steps 1-3 of the grouped linear on x (x_rows, K): w_codes (G, N, K/2),
+    w_scales (G, N, K/16), ws2 (G,), y (M_total, N); gsa, x_codes and
+    x_scales receive x's quantization."""
+    G, N = w_codes.shape[0], w_codes.shape[1]
+    K = w_codes.shape[2] * 2
+    _check(lib.nvfp4_grouped_linear_run(_ptr(x), _dtype(x), x.shape[0], _ptr(gsa), _ptr(x_codes),
+                                        _ptr(x_scales), _ptr(row_index), _ptr(group_offsets), G,
+                                        y.shape[0], _ptr(w_codes), _ptr(w_scales), _ptr(ws2),
+                                        _ptr(y), _dtype(y), N, K, _ptr(ws), _nbytes(ws),
+                                        _stream(stream)), "nvfp4_grouped_linear_run")
+
+
+def nvfp4_moe_run(x: torch.Tensor, gsa_x: torch.Tensor, x_codes: torch.Tensor,
+                  x_scales: torch.Tensor, row_index: torch.Tensor, group_offsets: torch.Tensor,
+                  w1_codes: torch.Tensor, w1_scales: torch.Tensor, w1_ws2: torch.Tensor,
+                  granularity: int, h: torch.Tensor, gsa_h: torch.Tensor, h_codes: torch.Tensor,
+                  h_scales: torch.Tensor, w2_codes: torch.Tensor, w2_scales: torch.Tensor,
+                  w2_ws2: torch.Tensor, y: torch.Tensor, ws: torch.Tensor, limit: float = 0.0,
+                  stream=None) -> None:
+    """The routed-expert pair on x (T, K1): w1 (E, N1, K1/2 | K1/16), w2 (E,
+    N2, N1/4 | N1/32), h (P, N1/2), y (P, N2) for the P pairs."""
+    E, N1 = w1_codes.shape[0], w1_codes.shape[1]
+    K1 = w1_codes.shape[2] * 2
+    N2 = w2_codes.shape[1]
+    _check(lib.nvfp4_moe_run(_ptr(x), _dtype(x), x.shape[0], _ptr(gsa_x), _ptr(x_codes),
+                             _ptr(x_scales), _ptr(row_index), _ptr(group_offsets), E,
+                             row_index.shape[0], _ptr(w1_codes), _ptr(w1_scales), _ptr(w1_ws2),
+                             N1, K1, granularity, limit, _ptr(h), _ptr(gsa_h), _ptr(h_codes),
+                             _ptr(h_scales), _ptr(w2_codes), _ptr(w2_scales), _ptr(w2_ws2), N2,
+                             _ptr(y), _dtype(y), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "nvfp4_moe_run")

@@ -46,6 +46,13 @@ WORKLOADS = {
     # the dense router: hidden 7168, 384 routed experts, 6 chosen per token
     "router_m1_k7168_e384_top6": dict(kind="router", M=1, K=7168, N=384, topk=6, seed=5),
     "router_m64_k7168_e384_top6": dict(kind="router", M=64, K=7168, N=384, topk=6, seed=6),
+    # the dense grouped linear (wo_a): one decoded token's 8 slices of 8192
+    # (heads_per_group * head_dim) against 8 weights of 1536 (o_lora_rank) rows
+    "grouped_wo_a_t1_g8_k8192_n1536": dict(kind="grouped", T=1, G=8, K=8192, N=1536, seed=10,
+                                           sf=(0.25, 4.0), ws2=(0.002, 0.01)),
+    # a decode projection with the lm_head's shape (vocab 129280, hidden 7168)
+    "lm_head_m1_k7168_n129280": dict(kind="linear", M=1, K=7168, N=129280, seed=11,
+                                     x="normal", sf=(0.25, 4.0), ws2=0.005),
     # RMSNorm -> quantize of the hidden state, one token and a prefill batch
     "rmsnorm_m1_k7168": dict(kind="rmsnorm", M=1, K=7168, seed=7),
     "rmsnorm_m512_k7168": dict(kind="rmsnorm", M=512, K=7168, seed=8),
@@ -188,6 +195,36 @@ def make_moe(tokens=64, experts=256, topk=8, K1=7168, N1=4096, K2=2048, N2=7168,
 
 
 @dataclass
+class GroupedInputs:
+    """The dense grouped linear: x (T, G*K) bf16 bits, token t's slice g is
+    row t*G + g of x viewed as (T*G, K); group g's output rows are
+    g*T .. g*T + T - 1 (row_index maps them to their slices)."""
+    name: str
+    x: np.ndarray            # (T * G, K) bf16 bits
+    row_index: np.ndarray    # (G * T,) int32
+    offsets: np.ndarray      # (G + 1,) int32
+    w_codes: np.ndarray      # (G, N, K/2) uint8
+    w_scales: np.ndarray     # (G, N, K/16) uint8
+    ws2: np.ndarray          # (G,) float32
+    T: int
+    G: int
+    K: int
+    N: int
+
+
+def make_grouped(T: int, G: int, K: int, N: int, seed: int, sf=(0.25, 4.0),
+                 ws2=(0.002, 0.01), x: str = "normal", name: str = "custom") -> GroupedInputs:
+    rng = np.random.default_rng(seed)
+    xb = to_bf16_bits(draw_activation(rng, T, G * K, x)).reshape(T * G, K)
+    row_index = (np.arange(T)[None, :] * G + np.arange(G)[:, None]).reshape(-1).astype(np.int32)
+    offsets = (np.arange(G + 1) * T).astype(np.int32)
+    ws = [draw_weight(seed, 0, g, N, K, sf[0], sf[1], ws2) for g in range(G)]
+    return GroupedInputs(name, np.ascontiguousarray(xb), row_index, offsets,
+                         np.stack([w[0] for w in ws]), np.stack([w[1] for w in ws]),
+                         np.array([w[2] for w in ws], np.float32), T, G, K, N)
+
+
+@dataclass
 class RouterInputs:
     name: str
     x: np.ndarray        # (M, K) bf16 bits
@@ -245,6 +282,9 @@ def make(name: str):
         return make_router(c["M"], c["K"], c["N"], c["topk"], c["seed"], name=name)
     if kind == "rmsnorm":
         return make_rmsnorm(c["M"], c["K"], c["seed"], name=name)
+    if kind == "grouped":
+        return make_grouped(c["T"], c["G"], c["K"], c["N"], c["seed"], c["sf"], c["ws2"],
+                            name=name)
     return make_moe(c["tokens"], c["experts"], c["topk"], c["K1"], c["N1"], c["K2"],
                     c["N2"], c["granularity"], c["seed"], c["sf"], c["ws2"], name=name)
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(C):
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert C.nvfp4_abi_version() == 8
+    assert C.nvfp4_abi_version() == 9
 
 
 def test_status_strings(C):
@@ -156,3 +156,39 @@ def test_validation_of_amax_quantize(C):
     assert aq(ctypes.c_void_p(4104), 0, 4, 32, fake, fake, fake, None, 0, None) == -5
     # beyond one workgroup the two-phase amax needs its workspace
     assert aq(fake, 0, 1024, 1024, fake, fake, fake, None, 0, None) == -4
+
+
+def test_validation_of_the_run_entries(C):
+    L = C.lib
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation
+    gr = L.nvfp4_grouped_linear_run
+    # (x, x_dtype, x_rows, gsa, x_codes, x_scales, row_index, offsets, G, M_total, w_codes,
+    #  w_scales, ws2, y, y_dtype, N, K, ws, ws_bytes, stream)
+    assert gr(fake, 3, 2, fake, fake, fake, fake, fake, 2, 2, fake, fake, fake, fake, 1, 16, 256,
+              None, 0, None) == -3                                           # dtype
+    assert gr(fake, 0, 2, fake, fake, fake, fake, fake, 2, 2, fake, fake, fake, fake, 1, 16, 40,
+              None, 0, None) == -2                                           # K % 16
+    assert gr(fake, 0, 1, fake, fake, fake, None, fake, 2, 2, fake, fake, fake, fake, 1, 16, 256,
+              None, 0, None) == -2                                           # rows without index
+    assert gr(fake, 0, 2, None, fake, fake, fake, fake, 2, 2, fake, fake, fake, fake, 1, 16, 256,
+              None, 0, None) == -1                                           # gsa
+    assert gr(fake, 0, 2, fake, None, fake, fake, fake, 2, 2, fake, fake, fake, fake, 1, 16, 256,
+              None, 0, None) == -1                                           # x_codes
+    assert gr(fake, 0, 8, fake, fake, fake, fake, fake, 2, 8, fake, fake, fake, fake, 1, 16, 8192,
+              None, 0, None) == -4                                           # 65536 elements: ws
+    assert C.nvfp4_workspace_bytes(C.OP_GROUPED_RUN, 8, 16, 8192, 2) > 0
+    assert C.nvfp4_workspace_bytes(C.OP_GROUPED_RUN, 1, 16, 8192, 2) == 0
+    mr = L.nvfp4_moe_run
+    # (x, x_dtype, T, gsa_x, x_codes, x_scales, row_index, offsets, E, P, w1_codes, w1_scales,
+    #  w1_ws2, N1, K1, gran, limit, h, gsa_h, h_codes, h_scales, w2_codes, w2_scales, w2_ws2,
+    #  N2, y, y_dtype, ws, ws_bytes, stream)
+    f = [fake] * 3
+    assert mr(fake, 0, 1, *f, fake, fake, 8, 8, *f, 512, 512, 8, float("nan"), *[fake] * 4, *f,
+              40, fake, 1, fake, 1 << 20, None) == -2                        # NaN limit
+    assert mr(fake, 0, 1, *f, None, fake, 8, 8, *f, 512, 512, 8, 0.0, *[fake] * 4, *f, 40, fake,
+              1, fake, 1 << 20, None) == -1                                  # row_index
+    assert mr(fake, 0, 1, *f, fake, fake, 8, 8, *f, 384, 512, 8, 0.0, *[fake] * 4, *f, 40, fake,
+              1, fake, 1 << 20, None) == -2                                  # N1 / 2 % 256
+    assert mr(fake, 0, 1, *f, fake, fake, 8, 8, *f, 512, 512, 8, 0.0, *[fake] * 4, *f, 40, fake,
+              1, fake, 4, None) in (-4, -5)                                   # workspace
+    assert C.nvfp4_workspace_bytes(C.OP_MOE_RUN, 1, 4096, 7168, 256) >= 4 * 128 * 256

@@ -1287,6 +1287,134 @@ def test_workload_moe(C):
     run_moe_stepwise(C, W.make("moe_t64_e256_top8"), sample=64)
 
 
+# ---------------------------------------------------------------- grouped runs
+def run_grouped(C, gi, dtype):
+    """nvfp4_grouped_linear_run on a make_grouped input; the GPU's outputs."""
+    rows = gi.T * gi.G
+    xd = x_dev(gi.x, dtype)
+    gsa = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    codes = torch.full((rows, gi.K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((rows, gi.K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    y = torch.full((rows, gi.N), float("nan"), dtype=torch.float32, device=DEV)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_GROUPED_RUN, rows, gi.N, gi.K, gi.G))
+    ws = torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_run(xd, gsa, codes, scales, to_dev(gi.row_index), to_dev(gi.offsets),
+                               to_dev(gi.w_codes), to_dev(gi.w_scales), to_dev(gi.ws2), y, ws)
+    torch.cuda.synchronize()
+    return (f32(gsa), codes.cpu().numpy(), scales.cpu().numpy(),
+            y.cpu().numpy().astype(np.float64))
+
+
+GROUPED_RUN_CASES = [
+    # (T, G, K, N, dtype); token t's slice g is row t*G + g of x
+    (1, 8, 1024, 96, "bf16"),    # 8192 elements: one launch
+    (2, 4, 2048, 40, "fp32"),    # 16384 elements, fp32: one launch
+    (1, 8, 8192, 64, "bf16"),    # the pages' wo_a slices: amax partials, then one launch
+    (3, 2, 7168, 130, "bf16"),   # 43008 elements, N not a multiple of 16
+    (1, 2, 272, 32, "bf16"),     # K % 256 != 0: the two ABI calls
+    (1, 1, 7168, 4096, "bf16"),  # one projection (G = 1)
+]
+
+
+@pytest.mark.parametrize("T,G,K,N,dtype", GROUPED_RUN_CASES)
+def test_grouped_linear_run(C, T, G, K, N, dtype):
+    """gsa and every row's codes and scales bit-exact with the oracle's
+    quantize of the whole activation; outputs within 1e-3 of the oracle's
+    grouped linear on those codes."""
+    say("grouped run", T, G, K, N, dtype)
+    gi = W.make_grouped(T, G, K, N, seed=T + G + K + N, x="outliers")
+    g, codes, scales, y = run_grouped(C, gi, dtype)
+    xh = x_host(gi.x, dtype)
+    assert g == oracle.amax_gsa(xh)
+    oc, os_ = oracle.quantize(xh, g)
+    assert np.array_equal(codes, oc) and np.array_equal(scales, os_)
+    ref = oracle.grouped_linear(oc, os_, g, gi.row_index, gi.offsets, gi.w_codes, gi.w_scales,
+                                gi.ws2, T * G)
+    assert not np.any(np.isnan(y))
+    assert rel_err(y, ref) <= REL_TOL
+
+
+def test_grouped_linear_run_routed_token(C):
+    """One token routed to 6 of 16 experts (the decode of routed experts),
+    plus two output rows past the last group (left unwritten)."""
+    say("grouped run routed")
+    moe = W.make_moe(tokens=1, experts=16, topk=6, K1=1024, N1=64, K2=32, N2=8, seed=7)
+    w1c, w1s, w1w, _, _, _ = W.moe_weights_to(moe, DEV, keep_host=True)
+    P = int(moe.offsets[-1])
+    ri = np.concatenate([moe.pair_token, [0, 0]]).astype(np.int32)
+    xd = W.bf16_to_torch(moe.x, DEV)
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes = torch.full((1, moe.K1 // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((1, moe.K1 // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    y = torch.full((P + 2, moe.N1), 7.0, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear_run(xd, gsa, codes, scales, to_dev(ri), to_dev(moe.offsets), w1c, w1s,
+                               w1w, y)
+    g = f32(gsa)
+    assert g == oracle.amax_gsa(moe.x)
+    oc, os_ = oracle.quantize(moe.x, g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    wc = np.stack([moe.weight(0, e)[0] for e in range(moe.E)])
+    wsf = np.stack([moe.weight(0, e)[1] for e in range(moe.E)])
+    w2 = np.array([moe.weight(0, e)[2] for e in range(moe.E)], np.float32)
+    ref = oracle.grouped_linear(oc, os_, g, moe.pair_token, moe.offsets, wc, wsf, w2, P)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert rel_err(yg[:P], ref) <= REL_TOL
+    assert np.all(yg[P:] == 7.0)
+
+
+@pytest.mark.parametrize("tokens,experts,topk,K1,N1,N2", [
+    (1, 8, 4, 512, 512, 40),      # a decoded token: two launches
+    (2, 16, 8, 1024, 512, 64),    # two tokens (2048 elements): two launches
+    (40, 6, 2, 512, 512, 24),     # x past 16384 elements: x quantized first
+])
+def test_moe_run(C, tokens, experts, topk, K1, N1, N2):
+    """nvfp4_moe_run: every step against the oracle on the GPU's own input to
+    it, and every output bit-equal to the separate calls'."""
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
+    say("moe run", tokens, experts, topk, K1, N1, N2)
+    moe = W.make_moe(tokens=tokens, experts=experts, topk=topk, K1=K1, N1=N1, K2=N1 // 2, N2=N2,
+                     granularity=8, seed=tokens + experts)
+    run_moe_stepwise(C, moe, fused=True)
+    P = int(moe.offsets[-1])
+    w = W.moe_weights_to(moe, DEV)
+    xd = W.bf16_to_torch(moe.x, DEV)
+    ri, off = to_dev(moe.pair_token), to_dev(moe.offsets)
+    outs = []
+    for run_entry in (True, False):
+        layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=8, run_entry=run_entry)
+        assert layer.run_entry == run_entry
+        y2 = layer(xd, ri, off).clone()
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (layer.gsa1, layer.x_codes[:moe.T],
+                                               layer.x_scales[:moe.T], layer.h[:P], layer.gsa2,
+                                               layer.h_codes[:P], layer.h_scales[:P], y2)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_workload_moe_one_token(C):
+    """One decoded token of the MoE workload's experts (K1 = 7168, N1 = 4096,
+    K2 = 2048, N2 = 7168, 8 of 256 experts) through nvfp4_moe_run."""
+    say("workload moe one token")
+    c = W.WORKLOADS["moe_t64_e256_top8"]
+    moe = W.make_moe(tokens=1, experts=c["experts"], topk=c["topk"], seed=c["seed"])
+    run_moe_stepwise(C, moe, sample=64)
+
+
+def test_workload_grouped_wo_a(C):
+    """The dense grouped linear at the pages' wo_a size (one token, 8 slices
+    of 8192 against 8 weights of 1536 rows): every output."""
+    say("workload grouped wo_a")
+    gi = W.make("grouped_wo_a_t1_g8_k8192_n1536")
+    g, codes, scales, y = run_grouped(C, gi, "bf16")
+    assert g == oracle.amax_gsa(gi.x)
+    oc, os_ = oracle.quantize(gi.x, g)
+    assert np.array_equal(codes, oc) and np.array_equal(scales, os_)
+    ref = oracle.grouped_linear(oc, os_, g, gi.row_index, gi.offsets, gi.w_codes, gi.w_scales,
+                                gi.ws2, gi.T * gi.G)
+    assert rel_err(y, ref) <= REL_TOL
+
+
 def test_graph_capture_replays_match_eager(C):
     """The whole step (amax, quantize, linear) captured once and replayed,
     with eager work in between; every replay equals the eager result."""
