@@ -248,7 +248,10 @@ int nvfp4_router_topk(const uint8_t *a_codes, const uint8_t *a_scales, const flo
  * nvfp4_linear in turn -- gsa, codes (M, K/2) and scales (M, K/16) are
  * written as those calls would write them, and y (M, N).
  * When x, w_codes and w_scales are 16-byte aligned it is ONE kernel for
- *   - up to 4 rows with K % 512 == 0, K <= 16384 and M*K <= 16384 (4 weight
+ *   - up to 2 rows with N >= 24576, K % 256 == 0 and M*K <= 16384 (the
+ *     weight-streaming ring of nvfp4_grouped_linear_run, 128 weight rows per
+ *     workgroup: a long weight stream such as the lm_head's), or
+ *   - up to 4 rows with K % 512 == 0, K <= 16384 and M*K <= 16384 (8 weight
  *     rows per workgroup), or
  *   - up to 16 rows with K % 256 == 0, M*K/16 <= 1024 and
  *     M*(K/2 + K/16) <= 65536 (16 weight rows per workgroup):

@@ -474,27 +474,39 @@ __device__ __forceinline__ float ring_gsa(const GemvArgs& args) {
 // uniform number of trips so that every lane takes part in src_of's shuffle;
 // half-blocks 2b and 2b+1 of a block sit in adjacent lanes (W * 64 and hpr
 // are even).
+// U trips at a time: all U loads are in flight before the first is used.
 template <bool XBF16, int W, typename SrcOf, typename Put>
 __device__ __forceinline__ void ring_quantize(const GemvArgs& args, int nh, float gsa,
                                               SrcOf src_of, Put put) {
+  constexpr int U = 4;
   const int hpr = args.K / 8;
   const int trips = (nh + W * 64 - 1) / (W * 64);
-  for (int it = 0; it < trips; ++it) {
-    const int i = (int)threadIdx.x + it * W * 64;
-    const bool in = i < nh;
-    const int rl = in ? i / hpr : 0;
-    const int hh = in ? i - rl * hpr : 0;
-    const int src = src_of(rl);
-    const bool ok = in && src >= 0;
-    uint4 raw[2];
-    load_half8_raw<XBF16>(args.x, ok ? (int64_t)src * hpr + hh : 0, raw);
-    float v[1][8];
-    unpack_half8<XBF16>(raw, v[0]);
-    const uint32_t hb = ok ? half_absmax8_bits(v[0]) : 0u;
-    const float bm[1] = {__uint_as_float(max(hb, dpp_u32<DPP_XOR1>(hb)))};
-    uint32_t c[1], sf[1];
-    quantize_halves<1>(v, bm, gsa, c, sf);
-    if (ok) put(rl, src, hh, c[0], sf[0]);
+  for (int it0 = 0; it0 < trips; it0 += U) {
+    int rl[U], hh[U], src[U];
+    bool ok[U];
+    uint4 raw[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (int)threadIdx.x + (it0 + u) * W * 64;
+      const bool in = it0 + u < trips && i < nh;
+      rl[u] = in ? i / hpr : 0;
+      hh[u] = in ? i - rl[u] * hpr : 0;
+      src[u] = src_of(rl[u]);
+      ok[u] = in && src[u] >= 0;
+      load_half8_raw<XBF16>(args.x, ok[u] ? (int64_t)src[u] * hpr + hh[u] : 0, raw[u]);
+    }
+    float v[U][8], bm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      unpack_half8<XBF16>(raw[u], v[u]);
+      const uint32_t hb = ok[u] ? half_absmax8_bits(v[u]) : 0u;
+      bm[u] = __uint_as_float(max(hb, dpp_u32<DPP_XOR1>(hb)));
+    }
+    uint32_t c[U], sf[U];
+    quantize_halves<U>(v, bm, gsa, c, sf);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) put(rl[u], src[u], hh[u], c[u], sf[u]);
   }
 }
 

@@ -538,6 +538,7 @@ RUN_CASES = [
     (1, 272, 40, "bf16"), (4, 7168, 40, "bf16"), (20, 512, 64, "fp32"),    # separate kernels
     (100, 7168, 96, "bf16"),  # amax partials, then the same workspace for a 14-way split K
     (700, 7168, 64, "bf16"),  # more than 512 amax partials: a separate finalize
+    (1, 7168, 32768, "bf16"), (2, 2048, 24576, "fp32"),  # long weight streams: the ring
 ]
 
 
@@ -1280,6 +1281,30 @@ def test_workload_linear(C, name):
         ms, ns = sample_positions(inp.M, inp.N, 4096, 1)
         ref = oracle.linear_at(oc, os_, f32(g), inp.w_codes, inp.w_scales, inp.ws2, ms, ns)
         assert rel_err(yg[ms, ns], ref) <= REL_TOL
+
+
+def test_workload_lm_head_decode(C):
+    """A one-row decode with the lm_head's shape through nvfp4_linear_run (the
+    ring, 128 weight rows a workgroup): gsa, codes and scales bit-exact, 4096
+    sampled outputs within 1e-3."""
+    say("workload lm_head decode")
+    inp = W.make("lm_head_m1_k7168_n129280")
+    xd = W.bf16_to_torch(inp.x, DEV)
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes = torch.full((1, inp.K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((1, inp.K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    y = torch.full((1, inp.N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_run(xd, gsa, codes, scales, to_dev(inp.w_codes), to_dev(inp.w_scales),
+                       torch.tensor([inp.ws2], dtype=torch.float32, device=DEV), y)
+    g = f32(gsa)
+    assert g == oracle.amax_gsa(inp.x)
+    oc, os_ = oracle.quantize(inp.x, g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(yg))
+    ms, ns = sample_positions(1, inp.N, 4096, 2)
+    ref = oracle.linear_at(oc, os_, g, inp.w_codes, inp.w_scales, inp.ws2, ms, ns)
+    assert rel_err(yg[ms, ns], ref) <= REL_TOL
 
 
 def test_workload_moe(C):
