@@ -352,7 +352,8 @@ def bench_router(C, name, dev, steps, warmup):
     bias = torch.from_numpy(r.bias).to(dev)
     idx = torch.empty(M, k, dtype=torch.int32, device=dev)
     sc = torch.empty(M, k, dtype=torch.float32, device=dev)
-    rws = torch.empty(max(16, C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, M, N, K)),
+    # zeroed: the one-launch path's ticket counter starts at zero
+    rws = torch.zeros(max(16, C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, M, N, K)),
                       dtype=torch.uint8, device=dev)
 
     def step(i):

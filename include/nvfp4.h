@@ -230,11 +230,20 @@ int nvfp4_linear_rows(const uint8_t *a_codes, const uint8_t *a_scales, const flo
  * float32: softplus and sqrt from the device math library (a few ulp).
  * N <= 1024 experts; 1 <= topk <= min(N, 64); other checks as nvfp4_linear.
  * ws: nvfp4_workspace_bytes(NVFP4_OP_ROUTER_TOPK, M, N, K, 0) bytes,
- * 16-byte aligned (at least M * N * 4: the logits; what follows them, rounded
- * up to 16 bytes, serves the linear's split K); on return it starts with the
- * fp32 logits (M, N) row-major.
- * Two kernels: the linear of nvfp4_linear, whose epilogue writes the logits
- * into ws, then one wave per row for the activation, bias and choice.
+ * 16-byte aligned; on return it starts with the fp32 logits (M, N)
+ * row-major.  What follows them (from byte L = M * N * 4 rounded up to 16):
+ *   - M <= 16: ONE kernel (the pages' single-kernel gate GEMM with the
+ *     sqrt(softplus) + bias + top-k epilogue, commit db07d17's message).
+ *     The weight-streaming linear's workgroups write the logits; each then
+ *     takes a ticket from a counter, the uint32 at byte L (a device-scope
+ *     atomic after a release fence), and the workgroup with the last ticket
+ *     chooses the experts of every row and sets the counter back to zero.
+ *     No workgroup waits for another.  That word must be ZERO before the
+ *     first call with a given workspace (allocate it zeroed); every call
+ *     leaves it zero.  Calls that share a workspace must be ordered.
+ *   - M > 16: the linear's split-K partials; two kernels, the linear and
+ *     one wave per row for the activation, bias and choice (which also adds
+ *     the split-K partials).
  * M == 0 is a no-op. */
 int nvfp4_router_topk(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa,
                       const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,

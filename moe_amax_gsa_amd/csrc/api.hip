@@ -76,7 +76,10 @@ NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, 
     case NVFP4_OP_QUANTIZE_WEIGHT: return (N > 0 && K > 0) ? amax_ws_bytes(N * K) : 0;
     case NVFP4_OP_RMSNORM_QUANTIZE: return M > 0 ? (size_t)M * sizeof(uint32_t) : 0;
     case NVFP4_OP_ROUTER_TOPK:
-      return (M > 0 && N > 0) ? round16((size_t)M * N * sizeof(float)) + linear_ws_bytes(M, N, K)
+      // the logits, then the one-launch path's ticket counter (M <= 16) or
+      // the linear's split-K partials
+      return (M > 0 && N > 0) ? round16((size_t)M * N * sizeof(float)) +
+                                    (M <= GEMV_MAX_M ? 16 : linear_ws_bytes(M, N, K))
                               : 0;
     case NVFP4_OP_GROUPED_SWIGLU:
       return (N > 0 && G > 0) ? (size_t)grouped_swiglu_parts(N, G) * sizeof(uint32_t) : 0;
@@ -245,19 +248,24 @@ NVFP4_API int nvfp4_router_topk(const uint8_t* a_codes, const uint8_t* a_scales,
   if (ws == nullptr || ws_bytes < (size_t)M * N * sizeof(float)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
   float* logits = (float*)ws;
-  // the bytes after the logits, if any, take the linear's split-K partials
   const size_t lbytes = round16((size_t)M * N * sizeof(float));
+  hipStream_t s = (hipStream_t)stream;
+  if (M <= GEMV_MAX_M) {
+    // one launch: the gate linear's last workgroup chooses the experts; its
+    // ticket counter is the word after the logits
+    if (ws_bytes < lbytes + 16) return NVFP4_ERR_WORKSPACE;
+    RouterEpilogue r{topk, bias, topk_idx, topk_score, (uint32_t*)((uint8_t*)ws + lbytes)};
+    return launched(launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, logits, false, M,
+                                N, K, s, false, &r));
+  }
+  // the bytes after the logits, if any, take the linear's split-K partials
   void* lws = ws_bytes > lbytes ? (void*)((uint8_t*)ws + lbytes) : nullptr;
   const size_t lws_bytes = ws_bytes > lbytes ? ws_bytes - lbytes : 0;
-  hipStream_t s = (hipStream_t)stream;
   // a split-K gate linear leaves its partials after the logits: the choice
   // kernel adds and scales them (and writes the logits) itself
   int nsplit = 0;
-  const hipError_t e =
-      M <= GEMV_MAX_M
-          ? launch_gemv(a_codes, a_scales, gsa, w_codes, w_scales, ws2, logits, false, M, N, K, s)
-          : launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, logits, false, M, N, K, s,
-                        false, lws, lws_bytes, &nsplit);
+  const hipError_t e = launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, logits, false,
+                                   M, N, K, s, false, lws, lws_bytes, &nsplit);
   if (e != hipSuccess) return launched(e);
   return launched(launch_router_topk(nsplit ? (const float*)lws : logits, nsplit, gsa, ws2,
                                      logits, bias, M, N, topk, topk_idx, topk_score, s));

@@ -37,6 +37,7 @@
 // Workgroup (0, 0) also writes gsa, codes and scales to memory.
 #include "device.hpp"
 #include "launch.hpp"
+#include "router.hpp"
 
 namespace nvfp4 {
 
@@ -77,7 +78,46 @@ struct GemvArgs {
   // the amax partials of an earlier launch whose maximum gives gsa
   const uint32_t* parts_in;
   int nparts_in;
+  // the dense router's choice after the gate linear, in the same launch
+  // (the kernels' ROUTER flag): k experts per row, the bias (or NULL), the
+  // outputs, and the ticket counter in the workspace
+  int router_k;
+  const float* router_bias;
+  int32_t* router_idx;
+  float* router_score;
+  uint32_t* router_count;
 };
+
+// The gate linear's last workgroup chooses the experts.  Every workgroup
+// writes its logits to args.y with device-coherent stores (written through
+// past its XCD's L2, store_logit), waits until they have completed, and then
+// takes a ticket from a counter (a device-scope vector atomic); the one that
+// takes the last ticket reads every logit with device-coherent loads, runs
+// the choice for every row and sets the counter back to zero for the next
+// call.  No workgroup waits for another: each exits once it has its ticket.
+// (A device-scope fence would write back and invalidate whole L2s in every
+// workgroup instead.)
+__device__ __forceinline__ void store_logit(const GemvArgs& args, int64_t e, float v) {
+  __hip_atomic_store((float*)args.y + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void router_finish(const GemvArgs& args) {
+  __shared__ int last;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's logits are written
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t n = gridDim.x * gridDim.y * gridDim.z;
+    const uint32_t t = __hip_atomic_fetch_add(args.router_count, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    last = t == n - 1;
+  }
+  __syncthreads();
+  if (!last) return;  // uniform over the workgroup
+  router_choose_rows<true>((const float*)args.y, args.M, args.N, args.router_k,
+                           args.router_bias, args.router_idx, args.router_score);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(args.router_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Where gemv_ring_kernel's activation rows come from.
 enum {
@@ -192,7 +232,7 @@ __device__ __forceinline__ void load_w_group(const uint8_t* wrow, const uint8_t*
 // past the last row are skipped); BPT activation blocks per thread in
 // MODE_RUN (the activation is held in registers between its amax and its
 // quantization).
-template <int S, int MP, bool FAST, int MODE, bool XBF16, int BPT>
+template <int S, int MP, bool FAST, int MODE, bool XBF16, int BPT, bool ROUTER = false>
 __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const GemvArgs args) {
   constexpr int ROWS = 2 * MP;
   __shared__ float red[GEMV_MAX_WAVES][ROWS][16];
@@ -393,7 +433,9 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
         ok = args.row_index[r] >= 0 && args.row_index[r] < args.a_rows;
       if (ok) {
         const float v = s * (args.gsa_rows ? args.gsa[r] * args.ws2[g] : gscale);
-        if (args.y_bf16)
+        if (ROUTER)
+          store_logit(args, (int64_t)r * N + n, v);
+        else if (args.y_bf16)
           ((uint16_t*)args.y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v);
         else
           ((float*)args.y)[(int64_t)r * N + n] = v;
@@ -401,6 +443,7 @@ __global__ __launch_bounds__(GEMV_MAX_WAVES * 64) void gemv_fp4_kernel(const Gem
     }
     __syncthreads();
   }
+  if constexpr (ROUTER) router_finish(args);
 }
 
 // ---------------------------------------------------------------- ring
@@ -850,7 +893,7 @@ static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
 // over every element, gsa, codes and scales into LDS, HPT half-blocks per
 // thread -- while its weight loads are in flight.  No workgroup depends on
 // another; workgroup 0 also writes gsa, codes and scales out.
-template <int S, int MR, bool RUN, bool XBF16, int HPT, int RQ, int MAXW>
+template <int S, int MR, bool RUN, bool XBF16, int HPT, int RQ, int MAXW, bool ROUTER = false>
 __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs args) {
   __shared__ float red[MAXW][MR][4 * RQ];
   __shared__ float amax_red[MAXW];
@@ -1061,12 +1104,15 @@ __global__ __launch_bounds__(MAXW * 64) void gemv_narrow_kernel(const GemvArgs a
     const int n = n0 + rr;
     if (w == 0 && o < MR * 4 * RQ && m < M && n < N) {
       const float v = sum * (args.gsa_rows ? args.gsa[m] * args.ws2[0] : gscale);
-      if (args.y_bf16)
+      if (ROUTER)
+        store_logit(args, (int64_t)m * N + n, v);
+      else if (args.y_bf16)
         ((uint16_t*)args.y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
       else
         ((float*)args.y)[(int64_t)m * N + n] = v;
     }
   }
+  if constexpr (ROUTER) router_finish(args);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -1081,12 +1127,12 @@ static int waves_for(int64_t K, int S = S_GROUP) {
   return (int)nw;
 }
 
-template <int MP, int MODE, int S = S_GROUP>
+template <int MP, int MODE, int S = S_GROUP, bool ROUTER = false>
 static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hipStream_t s) {
   if (fast)
-    gemv_fp4_kernel<S, MP, true, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
+    gemv_fp4_kernel<S, MP, true, MODE, true, 1, ROUTER><<<grid, nw * 64, 0, s>>>(a);
   else
-    gemv_fp4_kernel<S, MP, false, MODE, true, 1><<<grid, nw * 64, 0, s>>>(a);
+    gemv_fp4_kernel<S, MP, false, MODE, true, 1, ROUTER><<<grid, nw * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1192,12 +1238,12 @@ hipError_t launch_grouped_run(const void* x, bool x_bf16, int64_t x_rows, const 
 // the SwiGLU amax partials.
 int64_t ring_max_parts(int64_t N, int G) { return ((N + 31) / 32) * (int64_t)G; }
 
-template <int MODE>
+template <int MODE, bool ROUTER = false>
 static hipError_t launch_rows(const GemvArgs& a, int64_t rows_per_pass, bool fast, dim3 grid,
                               int nw, hipStream_t s) {
-  if (rows_per_pass <= 2) return launch_mp<1, MODE>(a, fast, grid, nw, s);
-  if (rows_per_pass <= 4) return launch_mp<2, MODE>(a, fast, grid, nw, s);
-  return launch_mp<8, MODE>(a, fast, grid, nw, s);
+  if (rows_per_pass <= 2) return launch_mp<1, MODE, S_GROUP, ROUTER>(a, fast, grid, nw, s);
+  if (rows_per_pass <= 4) return launch_mp<2, MODE, S_GROUP, ROUTER>(a, fast, grid, nw, s);
+  return launch_mp<8, MODE, S_GROUP, ROUTER>(a, fast, grid, nw, s);
 }
 
 // One activation row: one 512-element set per wave and up to 16 waves (the
@@ -1215,6 +1261,7 @@ static int narrow_waves(int64_t K, int S, int maxw) {
 // the activation in RUN mode, and a decode-sized N still spreads over the CUs
 constexpr int NARROW_RQ = 2;
 
+template <bool ROUTER = false>
 static hipError_t launch_narrow(const GemvArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.N + 4 * NARROW_RQ - 1) / (4 * NARROW_RQ)));
   if (a.M <= 1) {
@@ -1222,17 +1269,20 @@ static hipError_t launch_narrow(const GemvArgs& a, hipStream_t s) {
     // few weight rows (a router gate): one quad a workgroup, so twice as
     // many CUs stream them
     if ((int)grid.x < 128) {
-      gemv_narrow_kernel<1, 1, false, true, 1, 1, NARROW_MAXW1>
+      gemv_narrow_kernel<1, 1, false, true, 1, 1, NARROW_MAXW1, ROUTER>
           <<<dim3((unsigned)((a.N + 3) / 4)), th, 0, s>>>(a);
       return hipGetLastError();
     }
-    gemv_narrow_kernel<1, 1, false, true, 1, NARROW_RQ, NARROW_MAXW1><<<grid, th, 0, s>>>(a);
+    gemv_narrow_kernel<1, 1, false, true, 1, NARROW_RQ, NARROW_MAXW1, ROUTER>
+        <<<grid, th, 0, s>>>(a);
   } else {
     const int th = narrow_waves(a.K, 2, GEMV_MAX_WAVES) * 64;
     if (a.M <= 2)
-      gemv_narrow_kernel<2, 2, false, true, 1, NARROW_RQ, GEMV_MAX_WAVES><<<grid, th, 0, s>>>(a);
+      gemv_narrow_kernel<2, 2, false, true, 1, NARROW_RQ, GEMV_MAX_WAVES, ROUTER>
+          <<<grid, th, 0, s>>>(a);
     else
-      gemv_narrow_kernel<2, 4, false, true, 1, NARROW_RQ, GEMV_MAX_WAVES><<<grid, th, 0, s>>>(a);
+      gemv_narrow_kernel<2, 4, false, true, 1, NARROW_RQ, GEMV_MAX_WAVES, ROUTER>
+          <<<grid, th, 0, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -1316,8 +1366,15 @@ hipError_t launch_narrow_run(const void* x, bool x_bf16, float* gsa, uint8_t* co
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
                        void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                       bool gsa_rows) {
+                       bool gsa_rows, const RouterEpilogue* router) {
   GemvArgs a{};
+  if (router != nullptr) {
+    a.router_k = router->k;
+    a.router_bias = router->bias;
+    a.router_idx = router->idx;
+    a.router_score = router->score;
+    a.router_count = router->count;
+  }
   a.gsa_rows = gsa_rows ? 1 : 0;
   a.a_codes = a_codes;
   a.a_scales = a_scales;
@@ -1331,11 +1388,16 @@ hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   a.N = (int)N;
   a.K = (int)K;
   a.a_rows = (int)M;
-  if (gemv_narrow_supported(M, K, a_codes, a_scales, w_codes, w_scales))
-    return launch_narrow(a, s);
   const bool fast = (K % 256 == 0) && aligned16(a_codes) && aligned16(a_scales) &&
                     aligned16(w_codes) && aligned16(w_scales);
   dim3 grid((unsigned)((N + 15) / 16), 1u);
+  if (router != nullptr) {
+    if (gemv_narrow_supported(M, K, a_codes, a_scales, w_codes, w_scales))
+      return launch_narrow<true>(a, s);
+    return launch_rows<MODE_PLAIN, true>(a, M, fast, grid, waves_for(K), s);
+  }
+  if (gemv_narrow_supported(M, K, a_codes, a_scales, w_codes, w_scales))
+    return launch_narrow(a, s);
   return launch_rows<MODE_PLAIN>(a, M, fast, grid, waves_for(K), s);
 }
 

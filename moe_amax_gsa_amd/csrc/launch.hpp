@@ -84,11 +84,23 @@ hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float*
 
 // Weight-streaming linear for few rows (FP4 matrix cores).
 constexpr int64_t GEMV_MAX_M = 16;
-// gsa_rows: gsa holds one global scale per row (gsa[m]).
+// The dense router's choice run by the linear's last workgroup: k experts
+// per row of the fp32 logits the linear writes to y (M, N <= 1024), bias
+// (N,) or NULL, outputs idx / score (M, k), and a ticket counter that is
+// zero before the launch and left zero after it.
+struct RouterEpilogue {
+  int k;
+  const float* bias;
+  int32_t* idx;
+  float* score;
+  uint32_t* count;
+};
+// gsa_rows: gsa holds one global scale per row (gsa[m]).  router: the choice
+// in the same launch (y fp32).
 hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* ws2,
                        void* y, bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                       bool gsa_rows = false);
+                       bool gsa_rows = false, const RouterEpilogue* router = nullptr);
 
 // Grouped weight-streaming linear (device-side group sizes).
 hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,

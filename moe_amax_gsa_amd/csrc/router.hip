@@ -16,22 +16,9 @@
 #include <stdint.h>
 
 #include "launch.hpp"
+#include "router.hpp"
 
 namespace nvfp4 {
-
-// softplus(z) = max(z, 0) + log1p(exp(-|z|)): log(1 + exp(z)) without
-// overflow for large z and without losing the tail for very negative z.
-__device__ __forceinline__ float sqrt_softplus(float z) {
-  const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
-  return sqrtf(sp);
-}
-
-// Order-preserving map of a finite float to a nonzero u32 (key 0 marks a
-// retired or absent expert); -0 and +0 map to one key.
-__device__ __forceinline__ uint32_t order_key(float v) {
-  const uint32_t b = __float_as_uint(v + 0.0f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
 
 template <int NV>
 __global__ __launch_bounds__(256) void router_topk_kernel(
@@ -76,44 +63,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
   __syncthreads();
   if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  uint32_t key[NV];
-#pragma unroll
-  for (int t = 0; t < NV; ++t) key[t] = key_lds[lane + 64 * t];
-  int mine = 0;  // lane r keeps the expert of round r
-  for (int r = 0; r < k; ++r) {
-    // the largest live key: each lane's own, then the max within rows of 16
-    // lanes (DPP: swap neighbours, swap pairs, mirror halves, mirror the
-    // row), then across the four rows on the scalar unit
-    uint32_t x = 0u;
-#pragma unroll
-    for (int t = 0; t < NV; ++t) x = max(x, key[t]);
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
-    const uint32_t w = max(max((uint32_t)__builtin_amdgcn_readlane((int)x, 0),
-                               (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
-                           max((uint32_t)__builtin_amdgcn_readlane((int)x, 32),
-                               (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
-    // the lowest expert index holding it: expert j = lane + 64 t, so the
-    // first t with a hit and the lowest lane in that t's ballot.  k <= N, so
-    // a live key (nonzero) is left in every round.
-    int jw = 0;
-#pragma unroll
-    for (int t = NV - 1; t >= 0; --t) {
-      const uint64_t b = __ballot(key[t] == w);
-      if (b) jw = 64 * t + __builtin_ctzll(b);
-    }
-#pragma unroll
-    for (int t = 0; t < NV; ++t)
-      if (64 * t + lane == jw) key[t] = 0u;
-    if (lane == r) mine = jw;
-  }
-  if (lane < k) {
-    idx[(int64_t)m * k + lane] = mine;
-    score[(int64_t)m * k + lane] = s_lds[mine];
-  }
+  router_rounds<NV>(key_lds, s_lds, k, idx + (int64_t)m * k, score + (int64_t)m * k);
 }
 
 hipError_t launch_router_topk(const float* src, int nsrc, const float* gsa, const float* ws2,

@@ -139,8 +139,11 @@ class Nvfp4Router:
         dev = gate.device
         self.bias = None if bias is None else bias.to(device=dev, dtype=torch.float32).contiguous()
         M, N, K = gate.max_tokens, gate.N, gate.K
-        nws = max(16, _max_ws(C.OP_ROUTER_TOPK, M, N, K))
-        self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        nws = max(16, _max_ws(C.OP_ROUTER_TOPK, M, N, K),
+                  *[C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, m, N, K) for m in range(1, 17)])
+        # zeroed: for up to 16 rows the call's ticket counter (the word after
+        # the logits) must start at zero; every call leaves it zero
+        self.ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
         self.idx = torch.empty(M, topk, dtype=torch.int32, device=dev)
         self.score = torch.empty(M, topk, dtype=torch.float32, device=dev)
 
