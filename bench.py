@@ -302,6 +302,52 @@ def bench_grouped(C, name, dev, steps, warmup):
             "step_frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_routed(C, name, dev, steps, warmup):
+    """The routed experts' first projection over a prefill batch (512 tokens,
+    top 8 of 32 experts): the grouped linear on the tiled kernel from
+    quantized codes (linear_us), and nvfp4_grouped_linear_run from the bf16
+    activation (step_us: amax, quantize, grouped linear).  The stacked
+    weights (about 530 MB) are one copy: a step reads them all, more than
+    the Infinity Cache holds, before reading any again."""
+    from moe_amax_gsa_amd import workloads as W
+    moe = W.make(name)
+    P = int(moe.offsets[-1])
+    w1c, w1s, w1w, _, _, _ = W.moe_weights_to(moe, dev, first_only=True)
+    x = W.bf16_to_torch(moe.x, dev)
+    ri = torch.from_numpy(moe.pair_token).to(dev)
+    off = torch.from_numpy(moe.offsets).to(dev)
+    gsa = torch.zeros(1, dtype=torch.float32, device=dev)
+    codes = torch.zeros(moe.T, moe.K1 // 2, dtype=torch.uint8, device=dev)
+    scales = torch.zeros(moe.T, moe.K1 // 16, dtype=torch.uint8, device=dev)
+    y = torch.empty(P, moe.N1, dtype=torch.float32, device=dev)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_GROUPED_RUN, moe.T, moe.N1, moe.K1, moe.E))
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+
+    def run(i):
+        C.nvfp4_grouped_linear_run(x, gsa, codes, scales, ri, off, w1c, w1s, w1w, y, ws)
+
+    def linear(i):
+        C.nvfp4_grouped_linear(codes, scales, gsa, ri, off, w1c, w1s, w1w, y)
+
+    step_us = 1e3 * graph_ms_per_step(run, steps, warmup)
+    lin_us = 1e3 * graph_ms_per_step(linear, steps, warmup)
+    flops = 2.0 * P * moe.N1 * moe.K1
+    sizes = np.diff(moe.offsets)
+    wbytes = int(moe.E * moe.N1 * (moe.K1 // 2 + moe.K1 // 16))
+    abytes = P * (moe.K1 // 2 + moe.K1 // 16) + P * moe.N1 * 4
+    tf = flops / (lin_us * 1e-6) / 1e12
+    return {"pairs": P, "rows_per_expert_min_mean_max": [int(sizes.min()), float(sizes.mean()),
+                                                         int(sizes.max())],
+            "step_us": step_us, "linear_us": lin_us, "flops": flops,
+            "linear_TFLOPs": tf, "linear_frac_mfma": tf / MFMA_F16_PEAK_TFLOPS,
+            "step_TFLOPs": flops / (step_us * 1e-6) / 1e12,
+            "weight_bytes": wbytes,
+            "linear_GBps_weights_and_rows": (wbytes + abytes) / (lin_us * 1e-6) / 1e9,
+            "roofline_us": max(flops / (MFMA_F16_PEAK_TFLOPS * 1e12),
+                               (wbytes + abytes) / (HBM_PEAK_GBS * 1e9)) * 1e6,
+            "kernel": "gemm_lds_kernel, grouped (128 x 64 tiles over every group's rows)"}
+
+
 def bench_big_decode(C, name, dev, steps, warmup):
     """A one-row decode with a long weight stream (the lm_head's shape):
     nvfp4_linear_run, and the grouped run with one group (G = 1)."""
@@ -615,6 +661,12 @@ def main():
             log("workload", name)
             workloads[name] = bench_big_decode(C, name, dev, max(10, args.steps // 4),
                                                min(args.warmup, 3))
+        for name in ["moe_l1_t512_e32_top8_k7168_n4096", "moe_l1_t512_e32_top8_k7168_n4096_zipf"]:
+            if args.only and args.only != name:
+                continue
+            log("workload", name)
+            workloads[name] = bench_routed(C, name, dev, max(5, args.steps // 4),
+                                           min(args.warmup, 3))
         if not args.only or args.only == "moe_t64_e256_top8":
             log("workload moe_t64_e256_top8")
             workloads["moe_t64_e256_top8"] = bench_moe(C, dev, max(10, args.steps // 10),

@@ -306,13 +306,18 @@ int nvfp4_linear_run_noalloc(const void *x, int x_dtype, float *gsa, uint8_t *co
  * (N, K/2) at w_codes + g*N*K/2 and scales (N, K/16) at w_scales + g*N*K/16;
  * ws2 is a device float32[G].  The group sizes are read on the device only.
  * Rows of y outside every group, rows at or beyond M_total, and rows whose
- * row_index lies outside [0, a_rows) are not written. */
+ * row_index lies outside [0, a_rows) are not written.  group_offsets must
+ * be non-decreasing; rows of groups that break that may be left unwritten.
+ * Kernels: with at least 32 rows per group on average (M_total / G), 16-byte
+ * aligned codes, 2-byte aligned scales and K % 256 == 0, one launch of
+ * 64 x 128 output tiles over every group's rows on the f16 matrix cores
+ * (the pages' grouped block-scaled GEMM); otherwise one launch that streams
+ * each group's weights once per 8 or 16 of its rows. */
 int nvfp4_grouped_linear(const uint8_t *a_codes, const uint8_t *a_scales, const float *gsa,
                          int64_t a_rows, const int32_t *row_index,
                          const int32_t *group_offsets, int G, int64_t M_total,
                          const uint8_t *w_codes, const uint8_t *w_scales, const float *ws2,
-                         void *y, int y_dtype, int64_t N, int64_t K, void *ws,
-                         size_t ws_bytes, void *stream);
+                         void *y, int y_dtype, int64_t N, int64_t K, void *stream);
 
 /* The grouped linear on a bf16/fp32 activation, steps 1-3 in as few
  * launches as the sizes allow (the decode of G weight matrices that share

@@ -32,7 +32,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-NVFP4_API int nvfp4_abi_version(void) { return 9; }
+NVFP4_API int nvfp4_abi_version(void) { return 10; }
 
 NVFP4_API const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -350,9 +350,7 @@ NVFP4_API int nvfp4_grouped_linear(const uint8_t* a_codes, const uint8_t* a_scal
                                    const int32_t* group_offsets, int G, int64_t M_total,
                                    const uint8_t* w_codes, const uint8_t* w_scales,
                                    const float* ws2, void* y, int y_dtype, int64_t N, int64_t K,
-                                   void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+                                   void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_DTYPE;
   int st = check_gemm_shape(M_total, N, K);
   if (st != NVFP4_OK) return st;
@@ -476,17 +474,20 @@ NVFP4_API int nvfp4_grouped_linear_run(const void* x, int x_dtype, int64_t x_row
                                          row_index, group_offsets, G, M_total, w_codes, w_scales,
                                          ws2, y, ybf, N, K, false, 0, 0.f, nullptr, nullptr, s));
     // two launches: the amax partials, then the grouped linear, every
-    // workgroup of which reduces them
-    const size_t need = grouped_run_ws_bytes(x_rows, K);
-    if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
-    if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
-    int64_t np = 0;
-    hipError_t e = launch_amax_partials(x, xbf, numel, (uint32_t*)ws, &np, s);
-    if (e != hipSuccess) return launched(e);
-    return launched(launch_grouped_run(x, xbf, x_rows, (const uint32_t*)ws, np, gsa, x_codes,
-                                       x_scales, row_index, group_offsets, G, M_total, w_codes,
-                                       w_scales, ws2, y, ybf, N, K, false, 0, 0.f, nullptr,
-                                       nullptr, s));
+    // workgroup of which reduces them -- unless the groups are large enough
+    // for the tiled kernel, which reads codes quantized beforehand
+    if ((M_total + G - 1) / G < GROUPED_MFMA_MIN_ROWS) {
+      const size_t need = grouped_run_ws_bytes(x_rows, K);
+      if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+      if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+      int64_t np = 0;
+      hipError_t e = launch_amax_partials(x, xbf, numel, (uint32_t*)ws, &np, s);
+      if (e != hipSuccess) return launched(e);
+      return launched(launch_grouped_run(x, xbf, x_rows, (const uint32_t*)ws, np, gsa, x_codes,
+                                         x_scales, row_index, group_offsets, G, M_total, w_codes,
+                                         w_scales, ws2, y, ybf, N, K, false, 0, 0.f, nullptr,
+                                         nullptr, s));
+    }
   }
   // otherwise steps 1-2 as nvfp4_amax_quantize, then nvfp4_grouped_linear
   hipError_t e;

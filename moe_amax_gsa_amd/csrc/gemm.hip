@@ -194,19 +194,128 @@ struct LdsTile {
   static_assert(KW * 16 * (TN + 4) * 4 <= LDS_BYTES, "reduction slabs fit in the stages");
 };
 
-template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE, bool SPLIT>
+// Grouped launches: output row r belongs to group g when offsets[g] <= r <
+// offsets[g + 1]; its activation row is row_index[r] (r when NULL), and
+// group g's weights sit at w_codes + g N K/2, w_scales + g N K/16 with
+// scale ws2[g] (dsv4/_archive/layers/grouped_linear.py, _run_impl: one
+// block-scaled GEMM per group over the rows routed to it).
+struct GroupArgs {
+  const int32_t* row_index;
+  const int32_t* offsets;
+  int G;
+  int a_rows;
+};
+
+// gfx950 hands consecutive workgroups of a launch to its 8 XCDs in turn.
+constexpr int GFX950_XCDS = 8;
+
+// The tile of grouped workgroup b (1-D grid).  Work units: for each group
+// g, each column tile nt and each of the group's row tiles t (ceil(rows /
+// TM) of them, rows clamped to [0, M)), t fastest; they are numbered so
+// that each XCD takes one contiguous run of them.  Consecutive workgroups
+// on an XCD then share a weight tile -- read from HBM once, the group's
+// other row tiles find it in that XCD's L2 -- and the activation rows
+// (gathered, re-read by every column tile) come from L2 as well.  Every
+// wave computes the same answer from the offsets, so a workgroup without a
+// unit leaves as a whole.  Returns false for none; else group g, first
+// output row m0, the group's end rend and column tile nt.
+template <int TM>
+__device__ __forceinline__ bool group_tile(const GroupArgs& ga, int M, int ntn, int& g, int& m0,
+                                           int& rend, int& nt) {
+  const int lane = threadIdx.x & 63;
+  // the row tiles of all groups
+  int total = 0;
+  for (int g0 = 0; g0 < ga.G; g0 += 64) {
+    const int gi = g0 + lane;
+    int nti = 0;
+    if (gi < ga.G) {
+      const int lo = min(max(ga.offsets[gi], 0), M), hi = min(max(ga.offsets[gi + 1], 0), M);
+      nti = hi > lo ? (hi - lo + TM - 1) / TM : 0;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) nti += __shfl_xor(nti, d);
+    total += __builtin_amdgcn_readfirstlane(nti);
+  }
+  const int64_t work = (int64_t)total * ntn;
+  const int64_t per = (work + GFX950_XCDS - 1) / GFX950_XCDS;
+  const int64_t b = blockIdx.x, j = b / GFX950_XCDS;
+  if (j >= per) return false;
+  const int64_t w = (b % GFX950_XCDS) * per + j;
+  if (w >= work) return false;
+  // group g holds units [first * ntn, (first + nti) * ntn): the group whose
+  // row-tile range holds w / ntn, from an inclusive scan of the counts
+  const int slot = (int)(w / ntn);
+  int base = 0;
+  for (int g0 = 0; g0 < ga.G; g0 += 64) {
+    const int gi = g0 + lane;
+    int lo = 0, nti = 0;
+    if (gi < ga.G) {
+      lo = min(max(ga.offsets[gi], 0), M);
+      const int hi = min(max(ga.offsets[gi + 1], 0), M);
+      nti = hi > lo ? (hi - lo + TM - 1) / TM : 0;
+    }
+    int inc = nti;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(inc, d);
+      if (lane >= d) inc += up;
+    }
+    const uint64_t hit = __ballot(base + inc > slot);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      g = g0 + f;
+      const int n_g = __builtin_amdgcn_readlane(nti, f);
+      const int first = base + __builtin_amdgcn_readlane(inc, f) - n_g;
+      const int local = (int)(w - (int64_t)first * ntn);
+      nt = local / n_g;
+      m0 = __builtin_amdgcn_readlane(lo, f) + (local % n_g) * TM;
+      rend = __builtin_amdgcn_readfirstlane(min(max(ga.offsets[g + 1], 0), M));
+      return true;
+    }
+    base += __builtin_amdgcn_readlane(inc, 63);
+  }
+  return false;  // not reached: slot < total
+}
+
+template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE, bool SPLIT, bool GROUPED = false>
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ ws2_p, void* __restrict__ y,
-    int y_bf16, int M, int N, int K, int gsa_rows, int cps, float* __restrict__ part) {
+    int y_bf16, int M, int N, int K, int gsa_rows, int cps, float* __restrict__ part,
+    GroupArgs grp) {
   using T = LdsTile<WM, WN, STAGES, KW>;
   constexpr int TM = T::TM, TN = T::TN, LDT = TN + 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, h = lane >> 5;
-  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  // rows m0 .. rend - 1 of the output are this tile's (grouped: the rest of
+  // the group; else all of them)
+  int rend = M;
+  if constexpr (GROUPED) {
+    int g = 0, nt = 0;
+    if (!group_tile<TM>(grp, M, (N + TN - 1) / TN, g, m0, rend, nt)) return;
+    g = __builtin_amdgcn_readfirstlane(g);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    rend = __builtin_amdgcn_readfirstlane(rend);
+    n0 = __builtin_amdgcn_readfirstlane(nt) * TN;
+    w_codes += (size_t)g * N * (K / 2);
+    w_scales += (size_t)g * N * (K / 16);
+    ws2_p += g;
+  }
+  // activation row of tile row r (clamped rows: results discarded; a
+  // row_index outside [0, a_rows) reads row 0 and its output is skipped)
+  auto a_row = [&](int r) -> uint32_t {
+    const int o = min(m0 + r, rend - 1);
+    if constexpr (GROUPED) {
+      if (grp.row_index == nullptr) return (uint32_t)o;
+      const int ix = grp.row_index[o];
+      return (ix >= 0 && ix < grp.a_rows) ? (uint32_t)ix : 0u;
+    }
+    return (uint32_t)o;
+  };
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const uint32_t cbytes = (uint32_t)K / 2, sbytes = (uint32_t)K / 16;
   // split z of the K range: chunks c0 .. c0 + nch - 1 (cps per split)
@@ -222,7 +331,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int row = T::RPL * (KW * i + wave) + lane / T::PPR;
     const uint32_t piece = (uint32_t)((lane % T::PPR) ^ (row & 7));
     if (row < TM)
-      csrc[i] = (uint32_t)min(m0 + row, M - 1) * cbytes + piece * 16;  // clamped: discarded
+      csrc[i] = a_row(row) * cbytes + piece * 16;
     else
       csrc[i] = (uint32_t)min(n0 + row - TM, N - 1) * cbytes + piece * 16;
     csrc[i] += (uint32_t)c0 * T::CB;
@@ -230,7 +339,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // scale load of wave w < SCALE_LOADS: rows SRL w + l / (SB/16), piece l % (SB/16)
   const int srow = T::SRL * min(wave, T::SCALE_LOADS - 1) + lane / (T::SB / 16);
   const uint32_t spiece = (uint32_t)(lane % (T::SB / 16)) * 16;
-  const uint32_t ssrc = (srow < TM ? (uint32_t)min(m0 + srow, M - 1) * sbytes
+  const uint32_t ssrc = (srow < TM ? a_row(srow) * sbytes
                                    : (uint32_t)min(n0 + srow - TM, N - 1) * sbytes) + spiece +
                         (uint32_t)c0 * T::SB;
 
@@ -470,9 +579,16 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
         for (int w = 1; w < KW; ++w) v += red[(w * 16 + rr) * LDT + cc];
         const int row = m0 + a * 32 + q * 16 + rr, col = n0 + cc;
+        bool live = row < rend && col < N;
+        if constexpr (GROUPED) {
+          if (live && grp.row_index != nullptr) {
+            const int ix = grp.row_index[row];
+            live = ix >= 0 && ix < grp.a_rows;
+          }
+        }
         if (SPLIT) {  // the raw partial sum of this split
-          if (row < M && col < N) part[((int64_t)blockIdx.z * M + row) * N + col] = v;
-        } else if (row < M && col < N) {
+          if (live) part[((int64_t)blockIdx.z * M + row) * N + col] = v;
+        } else if (live) {
           const float o = v * (gsa_rows ? gsa_p[row] * ws2_p[0] : gscale);
           if (y_bf16)
             ((uint16_t*)y)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(o);
@@ -715,7 +831,7 @@ hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const flo
     gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, false>
         <<<dim3(grid.x, grid.y), T::THREADS, T::LDS_BYTES, s>>>(
             a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N,
-            (int)K, gsa_rows ? 1 : 0, nch, nullptr);
+            (int)K, gsa_rows ? 1 : 0, nch, nullptr, GroupArgs{});
     return hipGetLastError();
   }
   static unsigned char done[64];
@@ -724,7 +840,7 @@ hipError_t launch_lds(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   if (attr != hipSuccess) return attr;
   gemm_lds_kernel<WM, WN, STAGES, WPE, KW, PIPE, true><<<grid, T::THREADS, T::LDS_BYTES, s>>>(
       a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M, (int)N, (int)K,
-      gsa_rows ? 1 : 0, cps, part);
+      gsa_rows ? 1 : 0, cps, part, GroupArgs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !reduce) return e;
   const int64_t MN = M * N;
@@ -821,6 +937,62 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                                                 y_bf16 ? 1 : 0, (int)M, (int)N, (int)K,
                                                 gsa_rows ? 1 : 0);
   return hipGetLastError();
+}
+
+}  // namespace nvfp4
+
+namespace nvfp4 {
+
+// Grouped tiled linear for groups of many rows: the staged kernel over the
+// row tiles of every group (the tile count is known on the device only, so
+// the grid covers the most there can be, ceil(M_total / TM) + G row tiles,
+// and the workgroups past the real count leave at once).
+bool grouped_gemm_supported(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* w_codes, const uint8_t* w_scales, int64_t a_rows,
+                            int64_t M_total, int G, int64_t N, int64_t K) {
+  if (!gemm_staged_ok(a_codes, a_scales, w_codes, w_scales, a_rows, N, K)) return false;
+  const int64_t blocks = ((M_total + 31) / 32 + G) * ((N + 63) / 64);
+  return blocks + GFX950_XCDS <= 2147483647ll;
+}
+
+template <int WM, int WN, int KW, bool PIPE>
+static hipError_t launch_grouped_tiles(const uint8_t* a_codes, const uint8_t* a_scales,
+                                       const float* gsa, const GroupArgs& ga, int64_t M_total,
+                                       const uint8_t* w_codes, const uint8_t* w_scales,
+                                       const float* ws2, void* y, bool y_bf16, int64_t N,
+                                       int64_t K, hipStream_t s) {
+  using T = LdsTile<WM, WN, 2, KW>;
+  static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+  int64_t blocks = ((M_total + T::TM - 1) / T::TM + ga.G) * ((N + T::TN - 1) / T::TN);
+  blocks = (blocks + GFX950_XCDS - 1) / GFX950_XCDS * GFX950_XCDS;
+  static unsigned char done[64];
+  const hipError_t attr = allow_dynamic_lds(
+      (const void*)gemm_lds_kernel<WM, WN, 2, 2, KW, PIPE, false, true>, T::LDS_BYTES, done);
+  if (attr != hipSuccess) return attr;
+  gemm_lds_kernel<WM, WN, 2, 2, KW, PIPE, false, true>
+      <<<dim3((unsigned)blocks), T::THREADS, T::LDS_BYTES, s>>>(
+          a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M_total,
+          (int)N, (int)K, 0, (int)(K / T::CHUNK), nullptr, ga);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                               int64_t a_rows, const int32_t* row_index, const int32_t* offsets,
+                               int G, int64_t M_total, const uint8_t* w_codes,
+                               const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
+                               int64_t N, int64_t K, hipStream_t s) {
+  const GroupArgs ga{row_index, offsets, G, (int)a_rows};
+  // 64 x 128 tiles: a group's last row tile is on average half empty (the
+  // group sizes are known on the device only), and 64-row tiles waste half
+  // as many rows as 128-row ones.  As launch_gemm: eight waves per tile
+  // while the tiles are no more than the CUs, else four (two workgroups
+  // per CU).
+  const int64_t tiles = ((M_total + 63) / 64) * ((N + 127) / 128);
+  if (tiles <= device_cu_count() && K % 512 == 0)
+    return launch_grouped_tiles<2, 4, 8, true>(a_codes, a_scales, gsa, ga, M_total, w_codes,
+                                               w_scales, ws2, y, y_bf16, N, K, s);
+  return launch_grouped_tiles<2, 4, 4, false>(a_codes, a_scales, gsa, ga, M_total, w_codes,
+                                              w_scales, ws2, y, y_bf16, N, K, s);
 }
 
 }  // namespace nvfp4

@@ -1426,6 +1426,11 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
   // rows per pass from the mean group size (groups larger than a pass make
   // more passes over the same weight tile, which then comes from L2)
   const int64_t mean_rows = (M_total + G - 1) / G;
+  // many rows per group: tiles on the matrix cores
+  if (mean_rows >= GROUPED_MFMA_MIN_ROWS &&
+      grouped_gemm_supported(a_codes, a_scales, w_codes, w_scales, a_rows, M_total, G, N, K))
+    return launch_grouped_gemm(a_codes, a_scales, gsa, a_rows, row_index, offsets, G, M_total,
+                               w_codes, w_scales, ws2, y, y_bf16, N, K, s);
   if (fast && a_rows * (K / 2) < ((int64_t)1 << 31)) {  // copy offsets are 32-bit
     hipError_t err = hipSuccess;
     int64_t parts = 0;

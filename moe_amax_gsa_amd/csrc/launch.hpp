@@ -202,4 +202,17 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                        bool gsa_rows = false, void* ws = nullptr, size_t ws_bytes = 0,
                        int* partial_splits = nullptr);
 
+// Grouped linear on the tiled GEMM (groups of many rows; arguments as
+// launch_grouped_gemv).  Needs 16-byte aligned codes, 2-byte aligned
+// scales, K % 256 == 0 and 32-bit code offsets of A and of one group's W.
+constexpr int64_t GROUPED_MFMA_MIN_ROWS = 32;  // mean rows per group that take it
+bool grouped_gemm_supported(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* w_codes, const uint8_t* w_scales, int64_t a_rows,
+                            int64_t M_total, int G, int64_t N, int64_t K);
+hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
+                               int64_t a_rows, const int32_t* row_index, const int32_t* offsets,
+                               int G, int64_t M_total, const uint8_t* w_codes,
+                               const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
+                               int64_t N, int64_t K, hipStream_t s);
+
 }  // namespace nvfp4

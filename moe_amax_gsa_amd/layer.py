@@ -258,13 +258,13 @@ class Nvfp4MoE:
             # give h = 0 and stay out of h's amax, as in the fused path
             y1.zero_()
             C.nvfp4_grouped_linear(xc, xs, gsa, row_index, offsets, self.w1_codes,
-                                   self.w1_scales, self.w1_ws2, y1, None, stream)
+                                   self.w1_scales, self.w1_ws2, y1, stream)
             C.nvfp4_swiglu_deinterleave(y1, h, self.granularity, stream, limit=self.swiglu_limit)
             C.nvfp4_amax_gsa(h, self.gsa2, self.ws, stream)
             C.nvfp4_quantize_from_buffer(h, self.gsa2, hc, hs, stream)
         y2 = self.y2[:P]
         C.nvfp4_grouped_linear(hc, hs, self.gsa2, None, offsets, self.w2_codes, self.w2_scales,
-                               self.w2_ws2, y2, None, stream)
+                               self.w2_ws2, y2, stream)
         return y2
 
     __call__ = forward

@@ -70,7 +70,7 @@ lib.nvfp4_linear_run_noalloc.argtypes = [_P, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                                          _P]
 lib.nvfp4_grouped_linear.restype = _I
 lib.nvfp4_grouped_linear.argtypes = [_P, _P, _P, _I64, _P, _P, _I, _I64, _P, _P, _P, _P, _I,
-                                     _I64, _I64, _P, _SZ, _P]
+                                     _I64, _I64, _P]
 lib.nvfp4_amax_quantize.restype = _I
 lib.nvfp4_amax_quantize.argtypes = [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]
 lib.nvfp4_rmsnorm_quantize.restype = _I
@@ -223,17 +223,14 @@ def nvfp4_linear_run_noalloc(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Te
 def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tensor,
                          row_index: Optional[torch.Tensor], group_offsets: torch.Tensor,
                          w_codes: torch.Tensor, w_scales: torch.Tensor, ws2: torch.Tensor,
-                         y: torch.Tensor, ws: Optional[torch.Tensor] = None,
-                         stream=None) -> None:
+                         y: torch.Tensor, stream=None) -> None:
     """w_codes (G, N, K/2), w_scales (G, N, K/16), ws2 (G,), y (M_total, N)."""
     G, N = w_codes.shape[0], w_codes.shape[1]
     K = w_codes.shape[2] * 2
     _check(lib.nvfp4_grouped_linear(_ptr(a_codes), _ptr(a_scales), _ptr(gsa), a_codes.shape[0],
                                     _ptr(row_index), _ptr(group_offsets), G, y.shape[0],
                                     _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(y),
-                                    _dtype(y), N, K, _ptr(ws),
-                                    0 if ws is None else ws.numel() * ws.element_size(),
-                                    _stream(stream)), "nvfp4_grouped_linear")
+                                    _dtype(y), N, K, _stream(stream)), "nvfp4_grouped_linear")
 
 
 def nvfp4_amax_quantize(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,

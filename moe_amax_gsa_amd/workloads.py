@@ -53,6 +53,15 @@ WORKLOADS = {
     # a decode projection with the lm_head's shape (vocab 129280, hidden 7168)
     "lm_head_m1_k7168_n129280": dict(kind="linear", M=1, K=7168, N=129280, seed=11,
                                      x="normal", sf=(0.25, 4.0), ws2=0.005),
+    # a prefill batch through the routed experts' first projection: 512
+    # tokens, top 8 of 32 experts (128 rows per expert on average), routed
+    # uniformly, or with expert e drawn with weight (e + 1)^-1.2 (a few
+    # experts take most tokens)
+    "moe_l1_t512_e32_top8_k7168_n4096": dict(kind="routed", tokens=512, experts=32, topk=8,
+                                             K=7168, N=4096, seed=12, routing="uniform"),
+    "moe_l1_t512_e32_top8_k7168_n4096_zipf": dict(kind="routed", tokens=512, experts=32,
+                                                  topk=8, K=7168, N=4096, seed=13,
+                                                  routing="zipf"),
     # RMSNorm -> quantize of the hidden state, one token and a prefill batch
     "rmsnorm_m1_k7168": dict(kind="rmsnorm", M=1, K=7168, seed=7),
     "rmsnorm_m512_k7168": dict(kind="rmsnorm", M=512, K=7168, seed=8),
@@ -173,12 +182,20 @@ class MoEInputs:
 
 def make_moe(tokens=64, experts=256, topk=8, K1=7168, N1=4096, K2=2048, N2=7168,
              granularity=8, seed=3, sf=(0.25, 4.0), ws2=(0.002, 0.01),
-             name="custom_moe") -> MoEInputs:
+             name="custom_moe", routing: str = "uniform") -> MoEInputs:
+    """routing "uniform": each token's topk distinct experts uniformly at
+    random; "zipf": drawn without replacement with weights (e + 1)^-1.2."""
     rng = np.random.default_rng(seed)
     xb = to_bf16_bits(draw_activation(rng, tokens, K1, "normal"))
+    p = None
+    if routing == "zipf":
+        p = (np.arange(experts) + 1.0) ** -1.2
+        p /= p.sum()
+    elif routing != "uniform":
+        raise ValueError(routing)
     tok, exp_ = [], []
     for t in range(tokens):
-        chosen = rng.choice(experts, topk, replace=False)
+        chosen = rng.choice(experts, topk, replace=False, p=p)
         for e in chosen:
             tok.append(t)
             exp_.append(int(e))
@@ -282,6 +299,9 @@ def make(name: str):
         return make_router(c["M"], c["K"], c["N"], c["topk"], c["seed"], name=name)
     if kind == "rmsnorm":
         return make_rmsnorm(c["M"], c["K"], c["seed"], name=name)
+    if kind == "routed":  # the first projection only: K2, N2 are never drawn
+        return make_moe(c["tokens"], c["experts"], c["topk"], c["K"], c["N"], 256, 16, 8,
+                        c["seed"], name=name, routing=c["routing"])
     if kind == "grouped":
         return make_grouped(c["T"], c["G"], c["K"], c["N"], c["seed"], c["sf"], c["ws2"],
                             name=name)
@@ -296,18 +316,21 @@ def bf16_to_torch(bits: np.ndarray, device) -> torch.Tensor:
     return t.to(device)
 
 
-def moe_weights_to(moe: MoEInputs, device, experts=None, keep_host: bool = False):
+def moe_weights_to(moe: MoEInputs, device, experts=None, keep_host: bool = False,
+                   first_only: bool = False):
     """Stacked expert weights on the device: (w1_codes, w1_scales, w1_ws2,
     w2_codes, w2_scales, w2_ws2).  Experts outside ``experts`` (default:
     the experts that receive at least one token) are left zero -- the
-    grouped kernels never read an empty group's weights."""
+    grouped kernels never read an empty group's weights.  first_only: the
+    second projection's tensors are empty and never drawn."""
     E = moe.E
     if experts is None:
         experts = moe.active_experts
+    N2, K2 = (0, 16) if first_only else (moe.N2, moe.K2)
     w1c = torch.zeros(E, moe.N1, moe.K1 // 2, dtype=torch.uint8, device=device)
     w1s = torch.zeros(E, moe.N1, moe.K1 // 16, dtype=torch.uint8, device=device)
-    w2c = torch.zeros(E, moe.N2, moe.K2 // 2, dtype=torch.uint8, device=device)
-    w2s = torch.zeros(E, moe.N2, moe.K2 // 16, dtype=torch.uint8, device=device)
+    w2c = torch.zeros(E, N2, K2 // 2, dtype=torch.uint8, device=device)
+    w2s = torch.zeros(E, N2, K2 // 16, dtype=torch.uint8, device=device)
     w1_ws2 = np.zeros(E, np.float32)
     w2_ws2 = np.zeros(E, np.float32)
     for e in experts:
@@ -315,6 +338,10 @@ def moe_weights_to(moe: MoEInputs, device, experts=None, keep_host: bool = False
         w1c[e].copy_(torch.from_numpy(c))
         w1s[e].copy_(torch.from_numpy(s))
         w1_ws2[e] = w
+        if first_only:
+            if not keep_host:
+                moe.drop_cache()
+            continue
         c, s, w = moe.weight(1, int(e))
         w2c[e].copy_(torch.from_numpy(c))
         w2s[e].copy_(torch.from_numpy(s))

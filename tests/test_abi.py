@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(C):
     lib = ctypes.CDLL(C.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert C.nvfp4_abi_version() == 9
+    assert C.nvfp4_abi_version() == 10
 
 
 def test_status_strings(C):
@@ -74,9 +74,9 @@ def test_validation_errors_return_before_any_launch(C):
     assert L.nvfp4_linear(*args, 1, 0, 3, 32, None, 0, None) == 0  # M == 0: no-op
     # grouped: no row_index needs a_rows >= M_total; G must be positive
     assert L.nvfp4_grouped_linear(fake, fake, fake, 4, None, fake, 2, 8, fake, fake, fake, fake,
-                                  1, 16, 32, None, 0, None) == -2
+                                  1, 16, 32, None) == -2
     assert L.nvfp4_grouped_linear(fake, fake, fake, 8, None, fake, 0, 8, fake, fake, fake, fake,
-                                  1, 16, 32, None, 0, None) == -2
+                                  1, 16, 32, None) == -2
     assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 24, 8, 0.0, None) == -2
     assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 32, 0, 0.0, None) == -2
     assert L.nvfp4_swiglu_deinterleave(fake, fake, 2, 32, 8, float("nan"), None) == -2

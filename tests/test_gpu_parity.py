@@ -1325,6 +1325,164 @@ def test_workload_moe(C):
     run_moe_stepwise(C, W.make("moe_t64_e256_top8"), sample=64)
 
 
+
+# ------------------------------------------------------- grouped, tiled
+def grouped_case(seed, sizes, K, N, start=0, tail=0, a_rows=64, bad=()):
+    """Random grouped operands: groups of the given sizes starting at output
+    row `start` (rows before it and `tail` rows after the last group are in
+    no group), row_index uniform over a_rows with the entries in `bad`
+    pointing outside [0, a_rows)."""
+    rng = np.random.default_rng(seed)
+    G = len(sizes)
+    offsets = (start + np.concatenate([[0], np.cumsum(sizes)])).astype(np.int32)
+    M_total = int(offsets[-1]) + tail
+    row_index = rng.integers(0, a_rows, M_total).astype(np.int32)
+    for r, v in bad:
+        row_index[r] = v
+    ac = rng.integers(0, 256, (a_rows, K // 2), dtype=np.uint8)
+    asf = rng.integers(0x20, 0x48, (a_rows, K // 16), dtype=np.uint8)
+    wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    wsf = rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8)
+    ws2 = rng.uniform(0.002, 0.01, G).astype(np.float32)
+    return dict(G=G, offsets=offsets, M_total=M_total, row_index=row_index, ac=ac, asf=asf,
+                wc=wc, wsf=wsf, ws2=ws2, gsa=np.float32(0.37), a_rows=a_rows)
+
+
+def grouped_gpu(C, c, y_dtype=torch.float32):
+    y = torch.full((c["M_total"], c["wc"].shape[1]), -7.0, dtype=y_dtype, device=DEV)
+    C.nvfp4_grouped_linear(to_dev(c["ac"]), to_dev(c["asf"]),
+                           to_dev(np.array([c["gsa"]], np.float32)), to_dev(c["row_index"]),
+                           to_dev(c["offsets"]), to_dev(c["wc"]), to_dev(c["wsf"]),
+                           to_dev(c["ws2"]), y)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def grouped_expected_rows(c):
+    """Output rows the grouped linear writes: inside a group, with a valid
+    row_index."""
+    live = np.zeros(c["M_total"], bool)
+    live[c["offsets"][0]:c["offsets"][-1]] = True
+    ri = c["row_index"]
+    return live & (ri >= 0) & (ri < c["a_rows"])
+
+
+TILED_CASES = [
+    # (sizes, K, N): mean rows per group >= 32 takes the tiled kernel.
+    # 128 x 64 tiles: a 129-row group makes two row tiles (the second one
+    # row), empty groups make none; N not a multiple of 64
+    ([37, 0, 128, 129, 5, 203], 512, 200),    # few tiles: eight waves per tile
+    ([37, 0, 128, 129, 5, 203], 768, 64),     # K % 512 != 0: four waves per tile
+    ([37, 0, 128, 129, 5, 203], 7168, 136),   # long K, 14 chunks of 512
+    ([300], 1024, 40),                        # one group (G = 1)
+    ([33] * 40, 256, 72),                     # 40 groups of 33 rows: scan over 40 groups
+    ([2, 0, 0, 90, 1, 1, 1, 1, 300], 512, 64),  # skewed: mean 44, most groups tiny
+]
+
+
+@pytest.mark.parametrize("sizes,K,N", TILED_CASES)
+def test_grouped_tiled_shapes(C, sizes, K, N):
+    """The grouped linear on the tiled kernel (mean rows per group >= 32):
+    every written row against the oracle's grouped linear, rows before the
+    first group, after the last and with an invalid row_index unwritten."""
+    say(f"grouped tiled sizes={sizes[:9]} K={K} N={N}")
+    c = grouped_case(K + N + len(sizes), sizes, K, N, start=3, tail=4,
+                     bad=[(5, -1), (40, 64), (100, 1 << 20)])
+    y = grouped_gpu(C, c)
+    live = grouped_expected_rows(c)
+    assert np.all(y[~live] == -7.0)
+    ri = np.where(live, c["row_index"], 0).astype(np.int32)
+    ref = oracle.grouped_linear(c["ac"], c["asf"], c["gsa"], ri, c["offsets"], c["wc"], c["wsf"],
+                                c["ws2"], c["M_total"])
+    assert not np.any(np.isnan(y[live]))
+    assert rel_err(y[live], ref[live]) <= REL_TOL
+
+
+def test_grouped_tiled_bf16_is_rounded_fp32(C):
+    """bf16 output of the tiled grouped kernel: the fp32 output rounded to
+    nearest even, bit for bit."""
+    say("grouped tiled bf16")
+    c = grouped_case(77, [64, 100, 3, 150], 512, 96, start=1, tail=2)
+    y32 = grouped_gpu(C, c)
+    y16 = grouped_gpu(C, c, torch.bfloat16)
+    live = grouped_expected_rows(c)
+    r = torch.from_numpy(y32[live].astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(r, y16[live].astype(np.float32))
+
+
+def test_grouped_tiled_many_tiles(C):
+    """More row x column tiles than CUs (four waves per tile, two workgroups
+    per CU, the tiles spread over the XCDs in runs): 4096 rows over 32
+    groups of skewed sizes; sampled outputs against the oracle, every row
+    of every group sampled at least once."""
+    say("grouped tiled many tiles")
+    rng = np.random.default_rng(11)
+    sizes = rng.multinomial(4096 - 32, np.linspace(3.0, 0.2, 32) / np.linspace(3.0, 0.2, 32).sum())
+    sizes = sizes + 1
+    K, N = 512, 1088
+    c = grouped_case(11, list(sizes), K, N, a_rows=512)
+    y = grouped_gpu(C, c)
+    off = c["offsets"]
+    errs, refmax = 0.0, 0.0
+    for g in range(c["G"]):
+        rows = np.arange(off[g], off[g + 1])
+        ns = rng.integers(0, N, rows.size)
+        if rows.size >= 2:
+            ns[:2] = [0, N - 1]
+        ms = c["row_index"][rows]
+        ref = oracle.linear_at(c["ac"], c["asf"], c["gsa"], c["wc"][g], c["wsf"][g],
+                               c["ws2"][g], ms, ns)
+        errs = max(errs, float(np.max(np.abs(y[rows, ns] - ref))))
+        refmax = max(refmax, float(np.max(np.abs(ref))))
+    assert errs / refmax <= REL_TOL
+
+
+@pytest.mark.parametrize("name", ["moe_l1_t512_e32_top8_k7168_n4096",
+                                  "moe_l1_t512_e32_top8_k7168_n4096_zipf"])
+def test_workload_routed_first_projection(C, name):
+    """512 tokens, top 8 of 32 experts, the first expert projection through
+    nvfp4_grouped_linear_run: gsa, codes and scales bit-exact with the
+    oracle's quantize; 32 sampled outputs of every expert (its first and
+    last rows, first and last columns among them) within 1e-3 of the
+    oracle's linear of those codes."""
+    say("workload", name)
+    moe = W.make(name)
+    P = int(moe.offsets[-1])
+    w1c, w1s, w1w, _, _, _ = W.moe_weights_to(moe, DEV, first_only=True)
+    xd = W.bf16_to_torch(moe.x, DEV)
+    gsa = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    codes = torch.full((moe.T, moe.K1 // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((moe.T, moe.K1 // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    y = torch.full((P, moe.N1), float("nan"), dtype=torch.float32, device=DEV)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_GROUPED_RUN, moe.T, moe.N1, moe.K1, moe.E))
+    ws = torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_run(xd, gsa, codes, scales, to_dev(moe.pair_token),
+                               to_dev(moe.offsets), w1c, w1s, w1w, y, ws)
+    torch.cuda.synchronize()
+    del w1c, w1s
+    g = f32(gsa)
+    assert g == oracle.amax_gsa(moe.x)
+    oc, os_ = oracle.quantize(moe.x, g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    yh = y.cpu().numpy()
+    assert not np.any(np.isnan(yh))
+    rng = np.random.default_rng(0)
+    errs, refmax = 0.0, 0.0
+    for e in moe.active_experts:
+        r0, r1 = int(moe.offsets[e]), int(moe.offsets[e + 1])
+        wc, wsf, w2 = moe.weight(0, int(e))
+        moe.drop_cache()
+        rows = rng.integers(r0, r1, 32)
+        rows[:2] = [r0, r1 - 1]
+        ns = rng.integers(0, moe.N1, 32)
+        ns[:2] = [0, moe.N1 - 1]
+        ref = oracle.linear_at(oc, os_, g, wc, wsf, w2, moe.pair_token[rows], ns)
+        got = yh[rows, ns].astype(np.float64)
+        errs = max(errs, float(np.max(np.abs(got - ref))))
+        refmax = max(refmax, float(np.max(np.abs(ref))))
+    assert errs / refmax <= REL_TOL
+
+
 # ---------------------------------------------------------------- grouped runs
 def run_grouped(C, gi, dtype):
     """nvfp4_grouped_linear_run on a make_grouped input; the GPU's outputs."""
