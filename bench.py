@@ -280,6 +280,31 @@ def bench_moe(C, dev, steps, warmup):
     return res
 
 
+def bench_moe_prefill(C, dev, steps, warmup, name="moe_t512_e32_top8"):
+    """The MoE pair over a prefill batch (512 tokens, top 8 of 32 experts)
+    through nvfp4_moe_run: x's amax and quantize, the gate/up projection
+    with SwiGLU and h's amax in its epilogue, h's finalize and quantize, the
+    second projection -- both projections on the tiled kernel.  All 32
+    experts' weights (about 790 MB) are read every step."""
+    from moe_amax_gsa_amd import workloads as W
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
+    moe = W.make(name)
+    P = int(moe.offsets[-1])
+    w = W.moe_weights_to(moe, dev)
+    layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=moe.granularity)
+    assert layer.run_entry
+    x = W.bf16_to_torch(moe.x, dev)
+    ri = torch.from_numpy(moe.pair_token).to(dev)
+    off = torch.from_numpy(moe.offsets).to(dev)
+    flops = 2.0 * P * (moe.N1 * moe.K1 + moe.N2 * moe.K2)
+    us = 1e3 * graph_ms_per_step(lambda i: layer(x, ri, off), steps, warmup)
+    tf = flops / (us * 1e-6) / 1e12
+    return {"pairs": P, "step_us": us, "flops": flops, "step_TFLOPs": tf,
+            "step_frac_mfma": tf / MFMA_F16_PEAK_TFLOPS, "launches": 6,
+            "steps_in_the_launches": "x amax partials, x quantize, gate/up + SwiGLU + h amax "
+                                     "partials, h finalize, h quantize, second projection"}
+
+
 def bench_grouped(C, name, dev, steps, warmup):
     """The dense grouped linear of one decoded token (nvfp4_grouped_linear_run
     through Nvfp4GroupedLinear), weight copies rotated over 512 MB."""
@@ -667,6 +692,10 @@ def main():
             log("workload", name)
             workloads[name] = bench_routed(C, name, dev, max(5, args.steps // 4),
                                            min(args.warmup, 3))
+        if not args.only or args.only == "moe_t512_e32_top8":
+            log("workload moe_t512_e32_top8")
+            workloads["moe_t512_e32_top8"] = bench_moe_prefill(C, dev, max(5, args.steps // 4),
+                                                              min(args.warmup, 3))
         if not args.only or args.only == "moe_t64_e256_top8":
             log("workload moe_t64_e256_top8")
             workloads["moe_t64_e256_top8"] = bench_moe(C, dev, max(10, args.steps // 10),

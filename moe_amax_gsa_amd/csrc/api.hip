@@ -82,7 +82,9 @@ NVFP4_API size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, 
                                     (M <= GEMV_MAX_M ? 16 : linear_ws_bytes(M, N, K))
                               : 0;
     case NVFP4_OP_GROUPED_SWIGLU:
-      return (N > 0 && G > 0) ? (size_t)grouped_swiglu_parts(N, G) * sizeof(uint32_t) : 0;
+      return (N > 0 && G > 0)
+                 ? (size_t)grouped_swiglu_parts_bound(M > 0 ? M : 0, N, G) * sizeof(uint32_t)
+                 : 0;
     case NVFP4_OP_GROUPED_RUN: return (M > 0 && K > 0) ? grouped_run_ws_bytes_any(M, K) : 0;
     case NVFP4_OP_MOE_RUN: return moe_ws_bytes_any(M, N, K, G);
     default: return 0;
@@ -402,7 +404,9 @@ NVFP4_API int nvfp4_grouped_linear_swiglu(const uint8_t* a_codes, const uint8_t*
   if (!grouped_swiglu_supported(N_inter, K, granularity, a_rows, a_codes, a_scales, w_codes,
                                 w_scales))
     return NVFP4_ERR_SHAPE;
-  const size_t need = (size_t)grouped_swiglu_parts(N_inter, G) * sizeof(uint32_t);
+  const size_t need = (size_t)grouped_swiglu_parts_for(a_codes, a_scales, w_codes, w_scales,
+                                                       a_rows, M_total, G, N_inter, K) *
+                      sizeof(uint32_t);
   if (ws == nullptr || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
   return launched(launch_grouped_swiglu(a_codes, a_scales, gsa, a_rows, row_index, group_offsets,
@@ -504,9 +508,14 @@ NVFP4_API int nvfp4_grouped_linear_run(const void* x, int x_dtype, int64_t x_row
                                       M_total, w_codes, w_scales, ws2, y, ybf, N, K, s));
 }
 
+// The amax partials of x, or of h after the first projection: the
+// weight-streaming kernel's, or the tiled kernel's for up to T * E pairs
+// (every token at most once per expert); a call checks its own pair count.
 static size_t moe_ws_bytes(int64_t T, int64_t N1, int64_t K1, int E) {
   const size_t a = T > 0 ? amax_ws_bytes(T * K1) : 0;
-  const size_t b = (N1 > 0 && E > 0) ? (size_t)grouped_swiglu_parts(N1, E) * sizeof(uint32_t) : 0;
+  const size_t b = (N1 > 0 && E > 0 && T > 0)
+                       ? (size_t)grouped_swiglu_parts_bound(T * E, N1, E) * sizeof(uint32_t)
+                       : 0;
   return a > b ? a : b;
 }
 
@@ -544,7 +553,11 @@ NVFP4_API int nvfp4_moe_run(const void* x, int x_dtype, int64_t T, float* gsa_x,
       !grouped_run_supported(T, K1, x, w1_codes, w1_scales) ||
       !grouped_run_supported(P > 0 ? P : 1, K2, h, w2_codes, w2_scales))
     return NVFP4_ERR_SHAPE;
-  if (ws_bytes < moe_ws_bytes(T, N1, K1, E)) return NVFP4_ERR_WORKSPACE;
+  if (ws_bytes < moe_ws_bytes(T, N1, K1, E) ||
+      ws_bytes < (size_t)grouped_swiglu_parts_for(x_codes, x_scales, w1_codes, w1_scales, T, P, E,
+                                                  N1, K1) *
+                     sizeof(uint32_t))
+    return NVFP4_ERR_WORKSPACE;
   const bool xbf = x_dtype == NVFP4_DTYPE_BF16, ybf = y_dtype == NVFP4_DTYPE_BF16;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* parts = (uint32_t*)ws;
@@ -574,8 +587,9 @@ NVFP4_API int nvfp4_moe_run(const void* x, int x_dtype, int64_t T, float* gsa_x,
   }
   if (e != hipSuccess) return launched(e);
   // second projection: with few partials its workgroups reduce them and
-  // quantize their rows of h themselves; else h is quantized first
-  if (np <= RUN_INLINE_PARTS)
+  // quantize their rows of h themselves; else, or when the groups are large
+  // enough for the tiled kernel, h is quantized first
+  if (np <= RUN_INLINE_PARTS && (P + E - 1) / E < GROUPED_MFMA_MIN_ROWS)
     return launched(launch_grouped_run(h, false, P, parts, np, gsa_h, h_codes, h_scales, nullptr,
                                        group_offsets, E, P, w2_codes, w2_scales, w2_ws2, y, ybf,
                                        N2, K2, false, 0, 0.f, nullptr, nullptr, s));

@@ -204,6 +204,11 @@ struct GroupArgs {
   const int32_t* offsets;
   int G;
   int a_rows;
+  // SwiGLU epilogue: gate/up column groups of `gran` columns, the limit, and
+  // one amax partial per workgroup (bits of the largest |h| it wrote)
+  int gran;
+  float limit;
+  uint32_t* partials;
 };
 
 // gfx950 hands consecutive workgroups of a launch to its 8 XCDs in turn.
@@ -277,7 +282,8 @@ __device__ __forceinline__ bool group_tile(const GroupArgs& ga, int M, int ntn, 
   return false;  // not reached: slot < total
 }
 
-template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE, bool SPLIT, bool GROUPED = false>
+template <int WM, int WN, int STAGES, int WPE, int KW, bool PIPE, bool SPLIT, bool GROUPED = false,
+          bool SWIGLU = false>
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ gsa_p, const uint8_t* __restrict__ w_codes,
@@ -296,7 +302,10 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   int rend = M;
   if constexpr (GROUPED) {
     int g = 0, nt = 0;
-    if (!group_tile<TM>(grp, M, (N + TN - 1) / TN, g, m0, rend, nt)) return;
+    if (!group_tile<TM>(grp, M, (N + TN - 1) / TN, g, m0, rend, nt)) {
+      if (SWIGLU && threadIdx.x == 0) grp.partials[blockIdx.x] = 0u;  // wrote no h
+      return;
+    }
     g = __builtin_amdgcn_readfirstlane(g);
     m0 = __builtin_amdgcn_readfirstlane(m0);
     rend = __builtin_amdgcn_readfirstlane(rend);
@@ -563,6 +572,18 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
   float* red = (float*)smem;
   const float gscale = gsa_p[0] * ws2_p[0];
   float* slab = red + (size_t)wave * 16 * LDT;
+  float hmax = 0.f;  // SWIGLU: the largest |h| this thread wrote
+  // is output row `row` written (inside the tile's group, valid row_index)
+  auto live_row = [&](int row) -> bool {
+    bool live = row < rend;
+    if constexpr (GROUPED) {
+      if (live && grp.row_index != nullptr) {
+        const int ix = grp.row_index[row];
+        live = ix >= 0 && ix < grp.a_rows;
+      }
+    }
+    return live;
+  };
 #pragma unroll
   for (int a = 0; a < WM; ++a) {
 #pragma unroll
@@ -573,30 +594,58 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(WPE, WP
         for (int r = 8 * q; r < 8 * q + 8; ++r)
           slab[(8 * ((r >> 2) & 1) + 4 * h + (r & 3)) * LDT + b * 32 + r32] = acc[a][b][r];
       __syncthreads();
-      for (int e = threadIdx.x; e < 16 * TN; e += T::THREADS) {
-        const int rr = e / TN, cc = e % TN;
-        float v = red[rr * LDT + cc];
+      if constexpr (SWIGLU) {
+        // h column n0 / 2 + hc pairs the tile's gate column cg with the up
+        // column cg + gran (the tile starts on a whole number of pairs)
+        const int lg = __builtin_ctz(grp.gran);
+        for (int e = threadIdx.x; e < 16 * (TN / 2); e += T::THREADS) {
+          const int rr = e / (TN / 2), hc = e % (TN / 2);
+          const int cg = ((hc >> lg) << (lg + 1)) + (hc & (grp.gran - 1)), cu = cg + grp.gran;
+          float vg = red[rr * LDT + cg], vu = red[rr * LDT + cu];
 #pragma unroll
-        for (int w = 1; w < KW; ++w) v += red[(w * 16 + rr) * LDT + cc];
-        const int row = m0 + a * 32 + q * 16 + rr, col = n0 + cc;
-        bool live = row < rend && col < N;
-        if constexpr (GROUPED) {
-          if (live && grp.row_index != nullptr) {
-            const int ix = grp.row_index[row];
-            live = ix >= 0 && ix < grp.a_rows;
+          for (int w = 1; w < KW; ++w) {
+            vg += red[(w * 16 + rr) * LDT + cg];
+            vu += red[(w * 16 + rr) * LDT + cu];
+          }
+          const int row = m0 + a * 32 + q * 16 + rr;
+          if (n0 + cg < N && live_row(row)) {
+            const float hv = swiglu1(vg * gscale, vu * gscale, grp.limit);
+            ((float*)y)[(int64_t)row * (N / 2) + n0 / 2 + hc] = hv;
+            hmax = fmaxf(hmax, fabsf(hv));
           }
         }
-        if (SPLIT) {  // the raw partial sum of this split
-          if (live) part[((int64_t)blockIdx.z * M + row) * N + col] = v;
-        } else if (live) {
-          const float o = v * (gsa_rows ? gsa_p[row] * ws2_p[0] : gscale);
-          if (y_bf16)
-            ((uint16_t*)y)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(o);
-          else
-            ((float*)y)[(int64_t)row * N + col] = o;
+      } else {
+        for (int e = threadIdx.x; e < 16 * TN; e += T::THREADS) {
+          const int rr = e / TN, cc = e % TN;
+          float v = red[rr * LDT + cc];
+#pragma unroll
+          for (int w = 1; w < KW; ++w) v += red[(w * 16 + rr) * LDT + cc];
+          const int row = m0 + a * 32 + q * 16 + rr, col = n0 + cc;
+          if (col < N && live_row(row)) {
+            if (SPLIT) {  // the raw partial sum of this split
+              part[((int64_t)blockIdx.z * M + row) * N + col] = v;
+            } else {
+              const float o = v * (gsa_rows ? gsa_p[row] * ws2_p[0] : gscale);
+              if (y_bf16)
+                ((uint16_t*)y)[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(o);
+              else
+                ((float*)y)[(int64_t)row * N + col] = o;
+            }
+          }
         }
       }
       __syncthreads();
+    }
+  }
+  if constexpr (SWIGLU) {  // the workgroup's largest |h| (reusing the slab LDS)
+    uint32_t* wmax = (uint32_t*)smem;
+    const uint32_t m = wave_max_u32(__float_as_uint(hmax));
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t mm = 0;
+      for (int w = 0; w < KW; ++w) mm = max(mm, wmax[w]);
+      grp.partials[blockIdx.x] = mm;
     }
   }
 }
@@ -950,12 +999,11 @@ namespace nvfp4 {
 bool grouped_gemm_supported(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* w_codes, const uint8_t* w_scales, int64_t a_rows,
                             int64_t M_total, int G, int64_t N, int64_t K) {
-  if (!gemm_staged_ok(a_codes, a_scales, w_codes, w_scales, a_rows, N, K)) return false;
-  const int64_t blocks = ((M_total + 31) / 32 + G) * ((N + 63) / 64);
-  return blocks + GFX950_XCDS <= 2147483647ll;
+  return gemm_staged_ok(a_codes, a_scales, w_codes, w_scales, a_rows, N, K) &&
+         grouped_tile_blocks(M_total, G, N) <= 2147483647ll;
 }
 
-template <int WM, int WN, int KW, bool PIPE>
+template <int WM, int WN, int KW, bool PIPE, bool SWIGLU>
 static hipError_t launch_grouped_tiles(const uint8_t* a_codes, const uint8_t* a_scales,
                                        const float* gsa, const GroupArgs& ga, int64_t M_total,
                                        const uint8_t* w_codes, const uint8_t* w_scales,
@@ -963,17 +1011,40 @@ static hipError_t launch_grouped_tiles(const uint8_t* a_codes, const uint8_t* a_
                                        int64_t K, hipStream_t s) {
   using T = LdsTile<WM, WN, 2, KW>;
   static_assert(T::LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
-  int64_t blocks = ((M_total + T::TM - 1) / T::TM + ga.G) * ((N + T::TN - 1) / T::TN);
-  blocks = (blocks + GFX950_XCDS - 1) / GFX950_XCDS * GFX950_XCDS;
+  const int64_t blocks = grouped_tile_blocks(M_total, ga.G, N);
   static unsigned char done[64];
   const hipError_t attr = allow_dynamic_lds(
-      (const void*)gemm_lds_kernel<WM, WN, 2, 2, KW, PIPE, false, true>, T::LDS_BYTES, done);
+      (const void*)gemm_lds_kernel<WM, WN, 2, 2, KW, PIPE, false, true, SWIGLU>, T::LDS_BYTES,
+      done);
   if (attr != hipSuccess) return attr;
-  gemm_lds_kernel<WM, WN, 2, 2, KW, PIPE, false, true>
+  gemm_lds_kernel<WM, WN, 2, 2, KW, PIPE, false, true, SWIGLU>
       <<<dim3((unsigned)blocks), T::THREADS, T::LDS_BYTES, s>>>(
           a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16 ? 1 : 0, (int)M_total,
           (int)N, (int)K, 0, (int)(K / T::CHUNK), nullptr, ga);
   return hipGetLastError();
+}
+
+// 64 x 128 tiles: a group's last row tile is on average half empty (the
+// group sizes are known on the device only), and 64-row tiles waste half as
+// many rows as 128-row ones.  As launch_gemm: eight waves per tile while the
+// tiles are no more than the CUs, else four (two workgroups per CU).
+template <bool SWIGLU>
+static hipError_t launch_grouped_any(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const float* gsa, const GroupArgs& ga, int64_t M_total,
+                                     const uint8_t* w_codes, const uint8_t* w_scales,
+                                     const float* ws2, void* y, bool y_bf16, int64_t N, int64_t K,
+                                     hipStream_t s) {
+  const int64_t tiles = ((M_total + 63) / 64) * ((N + 127) / 128);
+  if (tiles <= device_cu_count() && K % 512 == 0)
+    return launch_grouped_tiles<2, 4, 8, true, SWIGLU>(a_codes, a_scales, gsa, ga, M_total,
+                                                       w_codes, w_scales, ws2, y, y_bf16, N, K, s);
+  return launch_grouped_tiles<2, 4, 4, false, SWIGLU>(a_codes, a_scales, gsa, ga, M_total,
+                                                      w_codes, w_scales, ws2, y, y_bf16, N, K, s);
+}
+
+int64_t grouped_tile_blocks(int64_t M_total, int G, int64_t N) {
+  const int64_t b = ((M_total + 63) / 64 + G) * ((N + 127) / 128);
+  return (b + GFX950_XCDS - 1) / GFX950_XCDS * GFX950_XCDS;
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gsa,
@@ -981,18 +1052,20 @@ hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, 
                                int G, int64_t M_total, const uint8_t* w_codes,
                                const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
                                int64_t N, int64_t K, hipStream_t s) {
-  const GroupArgs ga{row_index, offsets, G, (int)a_rows};
-  // 64 x 128 tiles: a group's last row tile is on average half empty (the
-  // group sizes are known on the device only), and 64-row tiles waste half
-  // as many rows as 128-row ones.  As launch_gemm: eight waves per tile
-  // while the tiles are no more than the CUs, else four (two workgroups
-  // per CU).
-  const int64_t tiles = ((M_total + 63) / 64) * ((N + 127) / 128);
-  if (tiles <= device_cu_count() && K % 512 == 0)
-    return launch_grouped_tiles<2, 4, 8, true>(a_codes, a_scales, gsa, ga, M_total, w_codes,
-                                               w_scales, ws2, y, y_bf16, N, K, s);
-  return launch_grouped_tiles<2, 4, 4, false>(a_codes, a_scales, gsa, ga, M_total, w_codes,
-                                              w_scales, ws2, y, y_bf16, N, K, s);
+  const GroupArgs ga{row_index, offsets, G, (int)a_rows, 0, 0.f, nullptr};
+  return launch_grouped_any<false>(a_codes, a_scales, gsa, ga, M_total, w_codes, w_scales, ws2, y,
+                                   y_bf16, N, K, s);
+}
+
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const float* gsa, int64_t a_rows, const int32_t* row_index,
+                                      const int32_t* offsets, int G, int64_t M_total,
+                                      const uint8_t* w_codes, const uint8_t* w_scales,
+                                      const float* ws2, float* h, int64_t N, int64_t K, int gran,
+                                      float limit, uint32_t* partials, hipStream_t s) {
+  const GroupArgs ga{row_index, offsets, G, (int)a_rows, gran, limit, partials};
+  return launch_grouped_any<true>(a_codes, a_scales, gsa, ga, M_total, w_codes, w_scales, ws2, h,
+                                  false, N, K, s);
 }
 
 }  // namespace nvfp4

@@ -1448,6 +1448,29 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
 
 int64_t grouped_swiglu_parts(int64_t N, int G) { return ring_max_parts(N, G); }
 
+// Groups of many rows take the tiled kernel (as launch_grouped_gemv).
+static bool swiglu_tiled(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                         const uint8_t* w_scales, int64_t a_rows, int64_t M_total, int G,
+                         int64_t N, int64_t K) {
+  return (M_total + G - 1) / G >= GROUPED_MFMA_MIN_ROWS &&
+         grouped_gemm_supported(a_codes, a_scales, w_codes, w_scales, a_rows, M_total, G, N, K);
+}
+
+int64_t grouped_swiglu_parts_for(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t a_rows,
+                                 int64_t M_total, int G, int64_t N, int64_t K) {
+  return swiglu_tiled(a_codes, a_scales, w_codes, w_scales, a_rows, M_total, G, N, K)
+             ? grouped_tile_blocks(M_total, G, N)
+             : ring_max_parts(N, G);
+}
+
+int64_t grouped_swiglu_parts_bound(int64_t M_total, int64_t N, int G) {
+  const int64_t r = ring_max_parts(N, G);
+  if ((M_total + G - 1) / G < GROUPED_MFMA_MIN_ROWS) return r;
+  const int64_t t = grouped_tile_blocks(M_total, G, N);
+  return t > r ? t : r;
+}
+
 // Most amax partials a quantize workgroup reduces by itself (8 KB of reads).
 constexpr int64_t SWIGLU_INLINE_PARTS = 2048;
 
@@ -1489,7 +1512,14 @@ hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
   const int64_t mean_rows = (M_total + G - 1) / G;
   hipError_t err = hipSuccess;
   int64_t parts = 0;
-  if (!launch_ring<true>(a, G, mean_rows, s, &err, &parts)) return hipErrorInvalidValue;
+  if (swiglu_tiled(a_codes, a_scales, w_codes, w_scales, a_rows, M_total, G, N, K)) {
+    err = launch_grouped_gemm_swiglu(a_codes, a_scales, gsa, a_rows, row_index, offsets, G,
+                                     M_total, w_codes, w_scales, ws2, h, N, K, gran, limit,
+                                     partials, s);
+    parts = grouped_tile_blocks(M_total, G, N);
+  } else if (!launch_ring<true>(a, G, mean_rows, s, &err, &parts)) {
+    return hipErrorInvalidValue;
+  }
   if (err != hipSuccess) return err;
   if (h_codes == nullptr) return launch_amax_finalize(partials, parts, gsa_h, s);
   // h's quantize as well: with few partials each quantize workgroup reduces
@@ -1526,6 +1556,12 @@ hipError_t launch_grouped_swiglu_l1(const uint8_t* a_codes, const uint8_t* a_sca
   a.gran = gran;
   a.limit = limit;
   a.partials = partials;
+  if (swiglu_tiled(a_codes, a_scales, w_codes, w_scales, a_rows, M_total, G, N, K)) {
+    *nparts = grouped_tile_blocks(M_total, G, N);
+    return launch_grouped_gemm_swiglu(a_codes, a_scales, gsa, a_rows, row_index, offsets, G,
+                                      M_total, w_codes, w_scales, ws2, h, N, K, gran, limit,
+                                      partials, s);
+  }
   hipError_t err = hipSuccess;
   if (!launch_ring<true>(a, G, (M_total + G - 1) / G, s, &err, nparts)) return hipErrorInvalidValue;
   return err;

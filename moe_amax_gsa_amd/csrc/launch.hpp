@@ -111,12 +111,19 @@ hipError_t launch_grouped_gemv(const uint8_t* a_codes, const uint8_t* a_scales, 
 
 // Grouped linear with SwiGLU, de-interleave and the first amax phase of h
 // in its epilogue, then the second phase (gsa_h).  ws holds
-// grouped_swiglu_parts(N, G) partials.  false: the operands or shape do not
-// suit the fused kernel (nothing launched).
+// grouped_swiglu_parts_for(...) partials: grouped_swiglu_parts(N, G) for the
+// weight-streaming kernel, grouped_tile_blocks(M_total, G, N) when the
+// groups are large enough for the tiled one; grouped_swiglu_parts_bound is
+// the larger of the two where the tiled one may run.  false: the operands
+// or shape do not suit the fused kernels (nothing launched).
 bool grouped_swiglu_supported(int64_t N, int64_t K, int gran, int64_t a_rows,
                               const uint8_t* a_codes, const uint8_t* a_scales,
                               const uint8_t* w_codes, const uint8_t* w_scales);
 int64_t grouped_swiglu_parts(int64_t N, int G);
+int64_t grouped_swiglu_parts_for(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t a_rows,
+                                 int64_t M_total, int G, int64_t N, int64_t K);
+int64_t grouped_swiglu_parts_bound(int64_t M_total, int64_t N, int G);
 hipError_t launch_grouped_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
                                  const float* gsa, int64_t a_rows, const int32_t* row_index,
                                  const int32_t* offsets, int G, int64_t M_total,
@@ -214,5 +221,16 @@ hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, 
                                int G, int64_t M_total, const uint8_t* w_codes,
                                const uint8_t* w_scales, const float* ws2, void* y, bool y_bf16,
                                int64_t N, int64_t K, hipStream_t s);
+// Workgroups (and so amax partials, with SwiGLU) of a grouped tiled launch.
+int64_t grouped_tile_blocks(int64_t M_total, int G, int64_t N);
+// The same with the SwiGLU epilogue of the gate/up projection (as
+// launch_grouped_swiglu's kernel): h (M_total, N/2) fp32 and one partial per
+// workgroup, grouped_tile_blocks of them.  N % (2 gran) == 0.
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const float* gsa, int64_t a_rows, const int32_t* row_index,
+                                      const int32_t* offsets, int G, int64_t M_total,
+                                      const uint8_t* w_codes, const uint8_t* w_scales,
+                                      const float* ws2, float* h, int64_t N, int64_t K, int gran,
+                                      float limit, uint32_t* partials, hipStream_t s);
 
 }  // namespace nvfp4

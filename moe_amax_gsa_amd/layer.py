@@ -208,7 +208,7 @@ class Nvfp4MoE:
                           and self.w1_codes.data_ptr() % 16 == 0
                           and self.w1_scales.data_ptr() % 16 == 0)
         self.ws_swiglu = torch.empty(
-            max(C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, 0, self.N1, 0, self.E), 16),
+            max(C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, max_pairs, self.N1, 0, self.E), 16),
             dtype=torch.uint8, device=dev)
         self.y1 = (None if self.fused else
                    torch.empty(max_pairs, self.N1, dtype=torch.float32, device=dev))
@@ -222,7 +222,8 @@ class Nvfp4MoE:
                               and self.w2_codes.data_ptr() % 16 == 0
                               and self.w2_scales.data_ptr() % 16 == 0)
         self.ws_run = torch.empty(
-            max(C.nvfp4_workspace_bytes(C.OP_MOE_RUN, max_tokens, self.N1, self.K1, self.E), 16),
+            max(C.nvfp4_workspace_bytes(C.OP_MOE_RUN, max_tokens, self.N1, self.K1, self.E),
+                C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, max_pairs, self.N1, 0, self.E), 16),
             dtype=torch.uint8, device=dev)
 
     def forward(self, x, row_index, offsets, stream=None) -> torch.Tensor:

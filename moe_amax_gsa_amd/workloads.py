@@ -41,6 +41,11 @@ WORKLOADS = {
     "moe_t64_e256_top8": dict(kind="moe", tokens=64, experts=256, topk=8, K1=7168,
                               N1=4096, K2=2048, N2=7168, granularity=8, seed=3,
                               sf=(0.25, 4.0), ws2=(0.002, 0.01)),
+    # the MoE pair at prefill: 512 tokens, top 8 of 32 experts (128 pairs per
+    # expert on average)
+    "moe_t512_e32_top8": dict(kind="moe", tokens=512, experts=32, topk=8, K1=7168, N1=4096,
+                              K2=2048, N2=7168, granularity=8, seed=14, sf=(0.25, 4.0),
+                              ws2=(0.002, 0.01)),
     "stress_m2048_k7168_n7168": dict(kind="linear", M=2048, K=7168, N=7168, seed=4,
                                      x="student_t", sf=(0.125, 8.0), ws2=0.003),
     # the dense router: hidden 7168, 384 routed experts, 6 chosen per token

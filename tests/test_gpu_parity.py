@@ -1437,6 +1437,58 @@ def test_grouped_tiled_many_tiles(C):
     assert errs / refmax <= REL_TOL
 
 
+
+@pytest.mark.parametrize("lim", ["off", "median"])
+@pytest.mark.parametrize("gran", [8, 1])
+@pytest.mark.parametrize("K,N", [(512, 256), (768, 416)])
+def test_grouped_swiglu_tiled_matches_unfused(C, K, N, gran, lim):
+    """The fused SwiGLU epilogue of the tiled grouped kernel (groups of 32 or
+    more rows on average) against the separate calls, which take the same
+    tiled kernel for the linear: h bit-identical, the same gsa_h, h's codes
+    and scales identical; rows outside every group and with an invalid
+    row_index unwritten in both and outside the amax.  h against the
+    oracle's SwiGLU of the GPU's l1, codes and scales against the oracle's
+    quantize of the GPU's h.  N = 416: a partial last column tile."""
+    say(f"grouped swiglu tiled K={K} N={N} gran={gran} limit={lim}")
+    c = grouped_case(K + N + gran, [37, 0, 128, 129, 5, 203], K, N, start=3, tail=4,
+                     bad=[(5, -1), (40, 64), (100, 1 << 20)])
+    P = c["M_total"]
+    live = grouped_expected_rows(c)
+    d = {k: to_dev(c[k]) for k in ("ac", "asf", "row_index", "offsets", "wc", "wsf", "ws2")}
+    gsa = to_dev(np.array([c["gsa"]], np.float32))
+    l1 = torch.zeros(P, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(d["ac"], d["asf"], gsa, d["row_index"], d["offsets"], d["wc"],
+                           d["wsf"], d["ws2"], l1)
+    limit = 0.0 if lim == "off" else float(torch.median(torch.abs(l1[l1 != 0])))
+    h1 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
+    g1 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    nws = C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, P, N, 0, c["G"])
+    ws = torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV)
+    hc1 = torch.full((P, N // 4), 0x5A, dtype=torch.uint8, device=DEV)
+    hs1 = torch.full((P, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_swiglu(d["ac"], d["asf"], gsa, d["row_index"], d["offsets"], d["wc"],
+                                  d["wsf"], d["ws2"], h1, g1, gran, ws, h_codes=hc1,
+                                  h_scales=hs1, limit=limit)
+    h2 = torch.zeros(P, N // 2, dtype=torch.float32, device=DEV)
+    g2 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    C.nvfp4_swiglu_deinterleave(l1, h2, gran, limit=limit)
+    C.nvfp4_amax_gsa(h2, g2, torch.empty(max(C.nvfp4_workspace_bytes(C.OP_AMAX_GSA,
+                                                                      P * N // 2), 16),
+                                         dtype=torch.uint8, device=DEV))
+    hc2, hs2 = gpu_quantize(C, h2, g2)
+    torch.cuda.synchronize()
+    a, b = h1.cpu().numpy(), h2.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.all(a[~live] == 0.0)
+    assert f32(g1) == f32(g2)
+    assert torch.equal(hc1, hc2) and torch.equal(hs1, hs2)
+    href = oracle.swiglu_deinterleave(l1.cpu().numpy(), gran, limit)
+    assert np.max(np.abs(a[live] - href[live])) <= 1e-6 * np.max(np.abs(href[live]))
+    assert f32(g1) == oracle.amax_gsa(a)
+    oc, os_ = oracle.quantize(a, f32(g1))
+    assert np.array_equal(hc1.cpu().numpy(), oc) and np.array_equal(hs1.cpu().numpy(), os_)
+
+
 @pytest.mark.parametrize("name", ["moe_l1_t512_e32_top8_k7168_n4096",
                                   "moe_l1_t512_e32_top8_k7168_n4096_zipf"])
 def test_workload_routed_first_projection(C, name):
@@ -1562,6 +1614,8 @@ def test_grouped_linear_run_routed_token(C):
     (1, 8, 4, 512, 512, 40),      # a decoded token: two launches
     (2, 16, 8, 1024, 512, 64),    # two tokens (2048 elements): two launches
     (40, 6, 2, 512, 512, 24),     # x past 16384 elements: x quantized first
+    (256, 8, 2, 512, 512, 64),    # 64 pairs per expert: both projections tiled
+    (96, 3, 1, 1024, 512, 136),   # 32 pairs per expert, N2 a partial column tile
 ])
 def test_moe_run(C, tokens, experts, topk, K1, N1, N2):
     """nvfp4_moe_run: every step against the oracle on the GPU's own input to
@@ -1586,6 +1640,16 @@ def test_moe_run(C, tokens, experts, topk, K1, N1, N2):
                                                layer.h_codes[:P], layer.h_scales[:P], y2)])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_workload_moe_prefill(C):
+    """A prefill batch through the routed experts (512 tokens, top 8 of 32,
+    about 128 pairs per expert, the MoE workload's projection sizes) through
+    nvfp4_moe_run, both projections on the tiled kernel: every step against
+    the oracle on the GPU's own input to it, 32 sampled outputs per expert
+    and projection."""
+    say("workload moe_t512_e32_top8")
+    run_moe_stepwise(C, W.make("moe_t512_e32_top8"), sample=32)
 
 
 def test_workload_moe_one_token(C):
