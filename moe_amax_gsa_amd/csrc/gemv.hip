@@ -1171,7 +1171,12 @@ static bool launch_ring_q(const GemvArgs& a, int G, int64_t mean_rows, hipStream
   const int64_t gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
   const bool wide = ((a.N + 127) / 128) * gy >= device_cu_count();
   if (mean_rows <= 2) {
+    // eight waves a workgroup where 128-row tiles fill the chip; otherwise
+    // four, with a 4-slot ring (one token over 8 x 1536 rows of K = 8192:
+    // 23.6 us against 28.6 us with two waves and 3 slots; 8 slots with two
+    // waves: 30.5 us)
     if (wide && ring_try<1, 3, 8, SWIGLU, QIN, XBF16>(a, G, s, err, parts)) return true;
+    if (ring_try<1, 4, 4, SWIGLU, QIN, XBF16>(a, G, s, err, parts)) return true;
     return ring_try<1, 3, 2, SWIGLU, QIN, XBF16>(a, G, s, err, parts);
   }
   if (wide && ring_try<4, 3, 8, SWIGLU, QIN, XBF16>(a, G, s, err, parts)) return true;
