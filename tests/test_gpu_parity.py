@@ -1398,6 +1398,34 @@ def test_grouped_tiled_shapes(C, sizes, K, N):
     assert rel_err(y[live], ref[live]) <= REL_TOL
 
 
+def test_grouped_tiled_many_groups_and_identity_rows(C):
+    """150 groups (the tile search scans the offsets 64 groups at a time,
+    three passes), a third of them empty, 40 rows per group on average;
+    once with a row gather and once with row_index NULL (output row r reads
+    activation row r).  Every written row against the oracle."""
+    say("grouped tiled 150 groups")
+    rng = np.random.default_rng(150)
+    sizes = rng.integers(0, 121, 150)
+    sizes[rng.random(150) < 0.33] = 0
+    K, N = 256, 136
+    c = grouped_case(150, list(sizes), K, N, a_rows=int(sizes.sum()) + 8)
+    assert c["M_total"] / c["G"] >= 32
+    for gather in (True, False):
+        if not gather:
+            c["row_index"] = np.arange(c["M_total"], dtype=np.int32)
+        y = torch.full((c["M_total"], N), -7.0, dtype=torch.float32, device=DEV)
+        C.nvfp4_grouped_linear(to_dev(c["ac"]), to_dev(c["asf"]),
+                               to_dev(np.array([c["gsa"]], np.float32)),
+                               to_dev(c["row_index"]) if gather else None,
+                               to_dev(c["offsets"]), to_dev(c["wc"]), to_dev(c["wsf"]),
+                               to_dev(c["ws2"]), y)
+        yh = y.cpu().numpy().astype(np.float64)
+        ref = oracle.grouped_linear(c["ac"], c["asf"], c["gsa"], c["row_index"], c["offsets"],
+                                    c["wc"], c["wsf"], c["ws2"], c["M_total"])
+        assert not np.any(np.isnan(yh))
+        assert rel_err(yh, ref) <= REL_TOL, gather
+
+
 def test_grouped_tiled_bf16_is_rounded_fp32(C):
     """bf16 output of the tiled grouped kernel: the fp32 output rounded to
     nearest even, bit for bit."""
