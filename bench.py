@@ -503,22 +503,28 @@ def cpu_model() -> str:
 def cpu_baseline(inp, budget_s=10.0):
     """The oracle's step (amax, quantize, FP64 linear) for the same workload
     on every host core this process may use, then on one core, each repeated
-    within a time budget.  Returns [(seconds per step, steps, threads)]."""
+    within a time budget.  Returns [(seconds per step, steps, threads,
+    seconds per step in amax + quantize, seconds per step in the linear)]."""
     from oracle import oracle
     legs = []
     for threads in (len(os.sched_getaffinity(0)), 1):
         used = oracle.set_threads(threads)
         n = 0
+        tq = tl = 0.0
         t0 = time.perf_counter()
         while True:
+            a = time.perf_counter()
             g = oracle.amax_gsa(inp.x)
             c, s = oracle.quantize(inp.x, g)
+            b = time.perf_counter()
             oracle.linear(c, s, g, inp.w_codes, inp.w_scales, inp.ws2)
+            tq += b - a
+            tl += time.perf_counter() - b
             n += 1
             el = time.perf_counter() - t0
             if el >= budget_s or n >= 1000:
                 break
-        legs.append((el / n, n, used))
+        legs.append((el / n, n, used, tq / n, tl / n))
     return legs
 
 
@@ -704,14 +710,16 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        (t_all, n_all, c_all), (t_one, n_one, _) = cpu_baseline(inp)
+        (t_all, n_all, c_all, q_all, l_all), (t_one, n_one, _, q_one, l_one) = cpu_baseline(inp)
         cpu = {"value": b.step_bytes / t_all / 1e9, "unit": "GB/s", "cores": c_all,
                "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"{n_all} whole oracle steps (amax, quantize, FP64 linear) of {HEAD} "
                          f"on {c_all} threads, {t_all * 1e3:.1f} ms each",
+               "ms_amax_quantize": q_all * 1e3, "ms_linear": l_all * 1e3,
                "one_core": {"value": b.step_bytes / t_one / 1e9, "unit": "GB/s", "cores": 1,
                             "sample": f"{n_one} oracle steps of {HEAD} on 1 thread, "
-                                      f"{t_one * 1e3:.1f} ms each"}}
+                                      f"{t_one * 1e3:.1f} ms each",
+                            "ms_amax_quantize": q_one * 1e3, "ms_linear": l_one * 1e3}}
 
     # at M=1 the step is one launch of the fused kernel: its average
     # duration is the step time of the graph of K launches
