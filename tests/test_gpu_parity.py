@@ -1589,6 +1589,8 @@ GROUPED_RUN_CASES = [
     (3, 2, 7168, 130, "bf16"),   # 43008 elements, N not a multiple of 16
     (1, 2, 272, 32, "bf16"),     # K % 256 != 0: the two ABI calls
     (1, 1, 7168, 4096, "bf16"),  # one projection (G = 1)
+    (64, 8, 512, 96, "bf16"),    # 64 tokens: quantize first, then the tiled kernel
+    (40, 3, 1024, 130, "fp32"),  # 40 rows per group, fp32 activation, ragged N
 ]
 
 
