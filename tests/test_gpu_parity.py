@@ -1705,6 +1705,70 @@ def test_workload_grouped_wo_a(C):
     assert rel_err(y, ref) <= REL_TOL
 
 
+def _graph_scenario(name):
+    """(step, outputs): step() enqueues one call of the named path on the
+    current stream; outputs() are the tensors it writes."""
+    from moe_amax_gsa_amd.layer import Nvfp4GroupedLinear, Nvfp4MoE, Nvfp4Router
+    if name == "router_one_launch":
+        r = W.make_router(1, 1024, 64, topk=6, seed=3)
+        router = Nvfp4Router.from_weight(W.bf16_to_torch(r.w, DEV), to_dev(r.bias), r.topk,
+                                         max_tokens=1)
+        x = W.bf16_to_torch(r.x, DEV)
+        return (lambda: router(x)), (lambda: [router.idx, router.score])
+    if name in ("moe_run_one_token", "moe_run_tiled"):
+        tokens, experts, topk = (1, 16, 4) if name == "moe_run_one_token" else (128, 4, 2)
+        moe = W.make_moe(tokens=tokens, experts=experts, topk=topk, K1=512, N1=512, K2=256,
+                         N2=136, granularity=8, seed=9)
+        P = int(moe.offsets[-1])
+        layer = Nvfp4MoE(*W.moe_weights_to(moe, DEV), max_pairs=P, max_tokens=moe.T)
+        assert layer.run_entry
+        x = W.bf16_to_torch(moe.x, DEV)
+        ri, off = to_dev(moe.pair_token), to_dev(moe.offsets)
+        return ((lambda: layer(x, ri, off)),
+                (lambda: [layer.y2[:P], layer.h[:P], layer.gsa1, layer.gsa2]))
+    T = 1 if name == "grouped_run_one_token" else 64
+    gi = W.make_grouped(T, 4, 1024, 96, seed=5)
+    g = Nvfp4GroupedLinear(to_dev(gi.w_codes), to_dev(gi.w_scales), to_dev(gi.ws2),
+                           max_tokens=T)
+    o = W.bf16_to_torch(gi.x, DEV).reshape(T, 4 * 1024)
+    return (lambda: g(o)), (lambda: [g.y, g.gsa])
+
+
+@pytest.mark.parametrize("name", ["router_one_launch", "moe_run_one_token", "moe_run_tiled",
+                                  "grouped_run_one_token", "grouped_run_tiled"])
+def test_graph_capture_replays_of_the_run_paths(C, name):
+    """Each one-call path captured once in a HIP graph and replayed four
+    times, with its outputs overwritten and eager work in between; every
+    replay's outputs equal the eager call's bit for bit (the router's
+    ticket counter is left at zero by every call, so replays keep
+    working)."""
+    say("graph replay", name)
+    step, outs = _graph_scenario(name)
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(4):
+        for t in outs():
+            if t.dtype.is_floating_point:
+                t.fill_(float("nan"))
+            else:
+                t.fill_(-7)
+        _ = torch.randn(1000, device=DEV).sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), eager):
+            assert torch.equal(a.view(torch.uint8) if a.dtype.is_floating_point else a,
+                               b.view(torch.uint8) if b.dtype.is_floating_point else b), (name, i)
+
+
 def test_graph_capture_replays_match_eager(C):
     """The whole step (amax, quantize, linear) captured once and replayed,
     with eager work in between; every replay equals the eager result."""
