@@ -134,7 +134,8 @@ def kernel_us(launch, iters: int, pre=None) -> float:
     return 1e3 * graph_ms_per_step(launch, iters, 2)
 
 
-KERNEL_SOURCES = ["device.hpp", "launch.hpp", "api.hip", "gemv.hip", "gemm.hip", "quant.hip"]
+KERNEL_SOURCES = ["device.hpp", "launch.hpp", "router.hpp", "api.hip", "gemv.hip", "gemm.hip",
+                  "quant.hip", "router.hip", "noalloc.hip"]
 
 
 def kernel_source_hash() -> str:
