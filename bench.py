@@ -744,7 +744,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1 codes with e4m3 block scales, exact f16 operands, f32 accumulate",
+        "dtype": "fp4",
+        "dtype_detail": "e2m1 x e2m1 block sums on the fp4 matrix cores, e4m3 block scales and "
+                        "the global scales applied in f32, f32 accumulation",
         "data": "synthetic, seeded",
         "config": {"workload": HEAD, "M": 1, "K": 7168, "N": 1536,
                    "step": "nvfp4_linear_run (amax, gsa, quantize, linear)",
