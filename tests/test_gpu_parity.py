@@ -1672,6 +1672,41 @@ def test_moe_run(C, tokens, experts, topk, K1, N1, N2):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+@pytest.mark.parametrize("limit", [0.0, 2.0])
+def test_moe_run_tiled_skewed_matches_separate_calls(C, limit):
+    """nvfp4_moe_run with Zipf routing (128 tokens, 2 of 8 experts: the first
+    experts take most pairs, the last few under 32), both projections on the
+    tiled kernel, without and with a SwiGLU limit that clamps: every output
+    bit-equal to the separate calls (which take the same kernels for the
+    projections), and y against the oracle on the GPU's own h codes."""
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
+    say("moe run tiled zipf", limit)
+    moe = W.make_moe(tokens=128, experts=8, topk=2, K1=512, N1=512, K2=256, N2=136,
+                     granularity=8, seed=21, routing="zipf")
+    P = int(moe.offsets[-1])
+    assert P / moe.E >= 32
+    w = W.moe_weights_to(moe, DEV, keep_host=True)
+    xd = W.bf16_to_torch(moe.x, DEV)
+    ri, off = to_dev(moe.pair_token), to_dev(moe.offsets)
+    outs = []
+    for run_entry in (True, False):
+        layer = Nvfp4MoE(*w, max_pairs=P, max_tokens=moe.T, granularity=8,
+                         swiglu_limit=limit, run_entry=run_entry)
+        assert layer.run_entry == run_entry
+        y2 = layer(xd, ri, off).clone()
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (layer.gsa1, layer.h[:P], layer.gsa2,
+                                               layer.h_codes[:P], layer.h_scales[:P], y2)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    g2, hc, hs, y = outs[0][2][0], outs[0][3], outs[0][4], outs[0][5].astype(np.float64)
+    w2c = np.stack([moe.weight(1, e)[0] for e in range(moe.E)])
+    w2s = np.stack([moe.weight(1, e)[1] for e in range(moe.E)])
+    w2w = np.array([moe.weight(1, e)[2] for e in range(moe.E)], np.float32)
+    ref = oracle.grouped_linear(hc, hs, g2, None, moe.offsets, w2c, w2s, w2w, P)
+    assert rel_err(y, ref) <= REL_TOL
+
+
 def test_workload_moe_prefill(C):
     """A prefill batch through the routed experts (512 tokens, top 8 of 32,
     about 128 pairs per expert, the MoE workload's projection sizes) through
