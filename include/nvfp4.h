@@ -58,8 +58,10 @@
  *     names a status.
  *   - Stateless and reentrant; the workspace is scratch that the call may
  *     overwrite (its size comes from nvfp4_workspace_bytes; no initial
- *     contents are required).  Calls that share a workspace must be ordered
- *     on one stream.
+ *     contents are required, except nvfp4_router_topk's ticket counter,
+ *     which must be zero before the first call and which every call leaves
+ *     at zero).  Calls that share a workspace must be ordered on one
+ *     stream.
  *   - Inputs must be finite.  A caller-supplied gsa must be positive and
  *     finite.
  */
@@ -102,12 +104,15 @@ extern "C" {
 /* Bytes of workspace an operation needs for the given sizes (0 if none).
  * For NVFP4_OP_AMAX_GSA, M is the element count and N, K, G are ignored;
  * for NVFP4_OP_LINEAR_RUN, the activation is (M, K); for
- * NVFP4_OP_GROUPED_SWIGLU, N is N_inter and G the group count; for
+ * NVFP4_OP_GROUPED_SWIGLU, M is M_total, N is N_inter and G the group count
+ * (with M = 0 the size covers groups averaging fewer than 32 rows only);
+ * for
  * NVFP4_OP_QUANTIZE_WEIGHT, the weight is (N, K); for
  * NVFP4_OP_RMSNORM_QUANTIZE, the activation is (M, K); for
  * NVFP4_OP_ROUTER_TOPK, M rows and N experts; for NVFP4_OP_GROUPED_RUN, x is
  * (M, K); for NVFP4_OP_MOE_RUN, M tokens, N = N1 and K = K1 of the first
- * projection and G experts. */
+ * projection and G experts (enough for up to M * G pairs: every token at
+ * most once per expert; a call checks its own pair count). */
 size_t nvfp4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int G);
 
 /* Step 1: gsa[0] = max(max_i |x_i|, 1e-8) / 2688.
@@ -359,17 +364,20 @@ int nvfp4_grouped_linear_run(const void *x, int x_dtype, int64_t x_rows, float *
  *       w1 (E, N1, K1), ..., h (P, N1/2), gsa_h, h_codes, h_scales, ...)
  *   nvfp4_grouped_linear(h_codes, h_scales, gsa_h, P, NULL, group_offsets,
  *       E, P, w2 (E, N2, N1/2), ..., y (P, N2))
- * with the same rules for rows outside every group (h, h_codes, h_scales and
- * y are written only for rows some expert reads; h's amax covers only
- * those rows).  Launches:
+ * with the same rules for rows outside every group (h and y are written
+ * only for rows some expert reads, and h's amax covers only those rows;
+ * when h is quantized by a launch of its own, h_codes and h_scales are
+ * written for every row, from whatever h holds in the others).  Launches:
  *   - the first projection, whose workgroups quantize x themselves when x
  *     has at most 16384 elements (a decoded token); else x's amax and
  *     quantize come first (one or two launches);
  *   - the second projection, whose workgroups reduce the first's amax
  *     partials and quantize the rows of h they read themselves, when the
- *     first projection had at most 2048 workgroups; else h's finalize and
- *     quantize come first.
- * One decoded token routed to 8 experts is two launches.
+ *     first projection had at most 2048 workgroups and the experts average
+ *     fewer than 32 pairs; else h's finalize and quantize come first.
+ * With 32 pairs or more per expert on average both projections run on the
+ * 64 x 128 tiles of nvfp4_grouped_linear.  One decoded token routed to 8
+ * experts is two launches.
  * Requires row_index (token of each pair), granularity 1, 2, 4 or 8,
  * N1 % (2 granularity) == 0, K1 and N1/2 multiples of 256 (short enough to
  * stage), and every buffer but y and the scalars 16-byte aligned.
@@ -411,13 +419,16 @@ int nvfp4_swiglu_deinterleave(const float *l1, float *h, int64_t M, int64_t N_in
  * or whose row_index lies outside [0, a_rows)) are not written and do not
  * enter the amax.  The amax is a two-phase grid reduction: every workgroup
  * of the linear writes the largest |h| it wrote into ws, and a second
- * kernel reduces those and writes gsa_h.
- * Requires granularity 1, 2, 4 or 8 (a wave's 16 output columns then hold
- * whole gate/up pairs), N_inter % (2*granularity) == 0, K % 256 == 0, K
+ * kernel reduces those and writes gsa_h.  The linear is the weight ring
+ * for few rows per group, or with 32 rows or more per group on average the
+ * 64 x 128 tiles of nvfp4_grouped_linear (the same kernels the unfused
+ * call takes, so h stays bit-identical).
+ * Requires granularity 1, 2, 4 or 8 (a wave's 16 output columns, and a
+ * tile's 128, then hold whole gate/up pairs), N_inter % (2*granularity) == 0, K % 256 == 0, K
  * short enough for the staged kernel (K <= 48 384), a_rows*K/2 < 2^31, and
  * 16-byte aligned codes and scales (NVFP4_ERR_SHAPE / NVFP4_ERR_ALIGN
  * otherwise; then call the three functions above).
- * ws: nvfp4_workspace_bytes(NVFP4_OP_GROUPED_SWIGLU, 0, N_inter, 0, G)
+ * ws: nvfp4_workspace_bytes(NVFP4_OP_GROUPED_SWIGLU, M_total, N_inter, 0, G)
  * bytes, 4-byte aligned, overwritten.
  * h_codes (M_total, N_inter/4) and h_scales (M_total, N_inter/32), both or
  * neither (NULL): also step 2 on h with gsa_h, as
