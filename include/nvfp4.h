@@ -239,10 +239,12 @@ int nvfp4_linear_rows(const uint8_t *a_codes, const uint8_t *a_scales, const flo
  * row-major.  What follows them (from byte L = M * N * 4 rounded up to 16):
  *   - M <= 16: ONE kernel (the pages' single-kernel gate GEMM with the
  *     sqrt(softplus) + bias + top-k epilogue, commit db07d17's message).
- *     The weight-streaming linear's workgroups write the logits; each then
- *     takes a ticket from a counter, the uint32 at byte L (a device-scope
- *     atomic after a release fence), and the workgroup with the last ticket
- *     chooses the experts of every row and sets the counter back to zero.
+ *     The weight-streaming linear's workgroups write the logits with
+ *     device-coherent (agent-scope atomic) stores and wait for them; each
+ *     then takes a ticket from a counter, the uint32 at byte L (a
+ *     device-scope atomic add), and the workgroup with the last ticket reads
+ *     the logits with device-coherent loads, chooses the experts of every
+ *     row and sets the counter back to zero.
  *     No workgroup waits for another.  That word must be ZERO before the
  *     first call with a given workspace (allocate it zeroed); every call
  *     leaves it zero.  Calls that share a workspace must be ordered.
