@@ -1644,6 +1644,7 @@ def test_grouped_linear_run_routed_token(C):
     (1, 8, 4, 512, 512, 40),      # a decoded token: two launches
     (2, 16, 8, 1024, 512, 64),    # two tokens (2048 elements): two launches
     (40, 6, 2, 512, 512, 24),     # x past 16384 elements: x quantized first
+    (1, 16, 12, 1024, 6144, 6144),  # 576 ring workgroups each: the split prologue
     (256, 8, 2, 512, 512, 64),    # 64 pairs per expert: both projections tiled
     (96, 3, 1, 1024, 512, 136),   # 32 pairs per expert, N2 a partial column tile
 ])
