@@ -218,6 +218,18 @@ def bench_linear(C, name, dev, steps, warmup, kiters):
     r["step_us"] = 1e3 * graph_ms_per_step(b.run, steps, warmup)
     r["step3_us"] = 1e3 * graph_ms_per_step(b.step3, steps, warmup)
     r["linear_us"] = kernel_us(b.linear, kiters, pre=b.quantize)
+    if inp.M > 16:
+        # the same linear with bf16 output (the pages' layer returns bf16;
+        # parity is checked on the fp32 output, whose RNE rounding the bf16
+        # output equals bit for bit)
+        y16 = torch.empty(inp.M, inp.N, dtype=torch.bfloat16, device=dev)
+
+        def lin16(i):
+            wc, wsf = b.w[i % b.ncopies]
+            C.nvfp4_linear(b.codes, b.scales, b.gsa, wc, wsf, b.ws2, y16, b.ws)
+
+        r["linear_bf16_out_us"] = kernel_us(lin16, kiters)
+        del y16
     r["quant_us"] = kernel_us(lambda i: b.quantize(), kiters)
     r["step_GBps"] = b.step_bytes / (r["step_us"] * 1e-6) / 1e9
     r["step_TFLOPs"] = b.flops / (r["step_us"] * 1e-6) / 1e12
