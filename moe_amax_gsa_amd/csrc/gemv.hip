@@ -577,7 +577,13 @@ __device__ __forceinline__ void ring_write_x(const GemvArgs& args, float gsa) {
 // the up value of gate column c sits in lane c ^ gran.
 // QIN: where the activation rows come from (RING_Q_*); XBF16: x's format
 // when the workgroup quantizes them.
-template <int MP, int D, int W, bool SWIGLU = false, int QIN = RING_Q_CODES, bool XBF16 = true>
+// KS > 1: KS consecutive waves share a tile of 16 rows, wave k streaming
+// super-chunks [k nsc/KS, (k+1) nsc/KS) through its own ring; after the
+// loop the partial sums are added in k order (through the now idle ring
+// slots) and the first wave of the tile stores.  More waves stream at once
+// for the same rows.  nsc % KS == 0.
+template <int MP, int D, int W, bool SWIGLU = false, int QIN = RING_Q_CODES, bool XBF16 = true,
+          int KS = 1>
 __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) {
   static_assert(2 * (D - 1) <= 14, "wait_vm range");
   constexpr int ROWS = 2 * MP;
@@ -631,10 +637,13 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
   float gsa_q = 0.f;  // QIN: the gsa this workgroup forms
   float hmax = 0.f;  // SWIGLU: largest |h| this thread wrote
 
-  const int n0 = (blockIdx.x * W + wave) * 16;
+  static_assert(W % KS == 0, "whole tiles per workgroup");
+  const int kp = wave % KS;  // this wave's part of the K range
+  const int n0 = (blockIdx.x * (W / KS) + wave / KS) * 16;
   const bool tile_ok = n0 < N;  // wave-uniform; a wave past the end only stages
   const int64_t cbytes = K / 2, sbytes = K / 16;
   const int nsc = K / 256;
+  const int cb = kp * (nsc / KS), ce = cb + nsc / KS;  // this wave's super-chunks
 
   const int a_mloc = col >> 3, a_half = col & 1;
   const bool a_has = ((col & 7) >> 1) == j;
@@ -698,13 +707,13 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
       if (r0 == r_begin) {
         for (int e0 = 0; e0 < 16 * spr; e0 += 64) {
           const int e = e0 + lane;
-          const int r = e / spr, q = e - r * spr;
+          const int r = e / spr, q = e - r * spr;  // piece q: the scales of super-chunk q
           const int rc = (n0 + r < N) ? r : N - 1 - n0;
-          if (e < 16 * spr)
+          if (e < 16 * spr && q >= cb && q < ce)
             load_lds16_nt(wsbase, (uint32_t)(rc * sbytes + 16 * q), ws_lds + 16u * (uint32_t)e0);
         }
       }
-      for (int c = 0; c < D && c < nsc; ++c) issue_slot(c);
+      for (int c = cb; c < cb + D && c < ce; ++c) issue_slot(c);
     }
     if (QIN == RING_Q_CODES) {
       // the pass rows' activation codes and scales (a missing row copies row
@@ -758,9 +767,9 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
     for (int p = 0; p < MP; ++p) acc[p] = 0.f;
 
     if (tile_ok) {
-      for (int c = 0; c < nsc; ++c) {
+      for (int c = cb; c < ce; ++c) {
         // slots c + 1 .. c + D - 1 may still be in flight
-        wait_vm(2 * min(D - 1, nsc - 1 - c));
+        wait_vm(2 * min(D - 1, ce - 1 - c));
         const uint8_t* sl = ring + (c % D) * SLOT + col * 128;
         const uint4 w0 = *(const uint4*)(sl + 16 * ((2 * j) ^ (col & 7)));
         const uint4 w1 = *(const uint4*)(sl + 16 * ((2 * j + 1) ^ (col & 7)));
@@ -799,12 +808,31 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
           }
         }
         // refill this slot once its reads have returned
-        if (c + D < nsc) {
+        if (c + D < ce) {
           __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           issue_slot(c + D);
         }
       }
-
+    }
+    if constexpr (KS > 1) {
+      // the tile's partial sums, in k order, through the waves' idle slots
+      float* xch = (float*)(lds + wave_off + K);
+      if (tile_ok && kp != 0) {
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // last slot reads done
+#pragma unroll
+        for (int p = 0; p < MP; ++p) xch[p * 64 + lane] = acc[p];
+      }
+      __syncthreads();
+      if (tile_ok && kp == 0) {
+#pragma unroll
+        for (int k = 1; k < KS; ++k) {
+          const float* px = (const float*)(lds + wave_off + (uint32_t)k * (uint32_t)(K + D * SLOT) + K);
+#pragma unroll
+          for (int p = 0; p < MP; ++p) acc[p] += px[p * 64 + lane];
+        }
+      }
+    }
+    if (tile_ok && kp == 0) {
       const float gscale = (QIN == RING_Q_CODES ? args.gsa[0] : gsa_q) * args.ws2[g];
 #pragma unroll
       for (int p = 0; p < MP; ++p) {
@@ -852,13 +880,14 @@ static size_t ring_lds_bytes(int64_t K) {
          (size_t)W * (size_t)(K + D * RING_SLOT);
 }
 
-template <int MP, int D, int W, bool SWIGLU, int QIN = RING_Q_CODES, bool XBF16 = true>
+template <int MP, int D, int W, bool SWIGLU, int QIN = RING_Q_CODES, bool XBF16 = true,
+          int KS = 1>
 static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
   const size_t lds = ring_lds_bytes<MP, D, W>(a.K);
   if (lds > 64 * 1024) {  // the largest any launch may ask for (callers keep lds below it)
     static unsigned char done[64];
     const hipError_t e = allow_dynamic_lds(
-        (const void*)gemv_ring_kernel<MP, D, W, SWIGLU, QIN, XBF16>, RING_MAX_LDS, done);
+        (const void*)gemv_ring_kernel<MP, D, W, SWIGLU, QIN, XBF16, KS>, RING_MAX_LDS, done);
     if (e != hipSuccess) return e;
   }
   // at most M groups have rows: with fewer rows than groups, launch a row of
@@ -866,8 +895,9 @@ static hipError_t launch_ring_t(const GemvArgs& a, int G, hipStream_t s) {
   GemvArgs b = a;
   b.groups = G;
   const int gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
-  const dim3 grid((unsigned)((a.N + 16 * W - 1) / (16 * W)), (unsigned)gy);
-  gemv_ring_kernel<MP, D, W, SWIGLU, QIN, XBF16><<<grid, W * 64, lds, s>>>(b);
+  constexpr int TW = W / KS;  // tiles of 16 rows per workgroup
+  const dim3 grid((unsigned)((a.N + 16 * TW - 1) / (16 * TW)), (unsigned)gy);
+  gemv_ring_kernel<MP, D, W, SWIGLU, QIN, XBF16, KS><<<grid, W * 64, lds, s>>>(b);
   return hipGetLastError();
 }
 
@@ -1139,21 +1169,36 @@ static hipError_t launch_mp(const GemvArgs& a, bool fast, dim3 grid, int nw, hip
 // Grouped linear through the LDS ring with one configuration, if its LDS
 // fits RING_MAX_LDS (false: K too long to stage).  *parts: the grid's
 // workgroup count (SwiGLU amax partials).
-template <int MP, int D, int W, bool SWIGLU, int QIN = RING_Q_CODES, bool XBF16 = true>
+template <int MP, int D, int W, bool SWIGLU, int QIN = RING_Q_CODES, bool XBF16 = true,
+          int KS = 1>
 static bool ring_try(const GemvArgs& a, int G, hipStream_t s, hipError_t* err, int64_t* parts) {
   if (ring_lds_bytes<MP, D, W>(a.K) > RING_MAX_LDS) return false;
+  if ((a.K / 256) % KS != 0) return false;
   const int64_t gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
-  *parts = (int64_t)((a.N + 16 * W - 1) / (16 * W)) * gy;
-  *err = launch_ring_t<MP, D, W, SWIGLU, QIN, XBF16>(a, G, s);
+  constexpr int TW = W / KS;
+  *parts = (int64_t)((a.N + 16 * TW - 1) / (16 * TW)) * gy;
+  *err = launch_ring_t<MP, D, W, SWIGLU, QIN, XBF16, KS>(a, G, s);
   return true;
 }
 
-// The first configuration that fits: 16 activation rows a pass when groups
-// average more than 4 rows, else 8 rows with 8 waves (one workgroup per CU),
-// then smaller footprints for longer K.
+// Decode-sized groups on a grid that 128-row tiles do not fill: two waves
+// share each 16-row tile, splitting its K range (twice the waves streaming
+// at once).  The same rule in both launchers keeps the self-quantizing
+// ring's sums bit-identical to the codes ring's.
+static bool ring_narrow_decode(const GemvArgs& a, int G, int64_t mean_rows) {
+  const int64_t gy = (a.offsets != nullptr && a.M < G) ? (a.M > 0 ? a.M : 1) : G;
+  return mean_rows <= 2 && ((a.N + 127) / 128) * gy < device_cu_count();
+}
+
+// The first configuration that fits: the K split above; then 16 activation
+// rows a pass when groups average more than 4 rows, else 8 rows with 8 waves
+// (one workgroup per CU), then smaller footprints for longer K.
 template <bool SWIGLU>
 static bool launch_ring(const GemvArgs& a, int G, int64_t mean_rows, hipStream_t s,
                         hipError_t* err, int64_t* parts) {
+  if (ring_narrow_decode(a, G, mean_rows) &&
+      ring_try<1, 4, 8, SWIGLU, RING_Q_CODES, true, 2>(a, G, s, err, parts))
+    return true;
   if (mean_rows > 4 && ring_try<8, 3, 4, SWIGLU>(a, G, s, err, parts)) return true;
   return ring_try<4, 3, 8, SWIGLU>(a, G, s, err, parts) ||
          ring_try<4, 3, 4, SWIGLU>(a, G, s, err, parts) ||
@@ -1172,10 +1217,15 @@ static bool launch_ring_q(const GemvArgs& a, int G, int64_t mean_rows, hipStream
   const bool wide = ((a.N + 127) / 128) * gy >= device_cu_count();
   if (mean_rows <= 2) {
     // eight waves a workgroup where 128-row tiles fill the chip; otherwise
-    // four, with a 4-slot ring (one token over 8 x 1536 rows of K = 8192:
-    // 23.6 us against 28.6 us with two waves and 3 slots; 8 slots with two
-    // waves: 30.5 us)
+    // eight waves on four tiles, two waves splitting each tile's K range,
+    // with a 4-slot ring (one token over 8 x 1536 rows of K = 8192: 18.7 us,
+    // against 23.7 us with four waves on four tiles and 28.6 us with two
+    // waves and 3 slots; K split four ways: 26.0 us; the split on the
+    // 128-row-tile grids: one token over 8 experts 45.5 -> 60.9 us)
     if (wide && ring_try<1, 3, 8, SWIGLU, QIN, XBF16>(a, G, s, err, parts)) return true;
+    if (ring_narrow_decode(a, G, mean_rows) &&
+        ring_try<1, 4, 8, SWIGLU, QIN, XBF16, 2>(a, G, s, err, parts))
+      return true;
     if (ring_try<1, 4, 4, SWIGLU, QIN, XBF16>(a, G, s, err, parts)) return true;
     return ring_try<1, 3, 2, SWIGLU, QIN, XBF16>(a, G, s, err, parts);
   }

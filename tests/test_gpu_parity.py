@@ -917,16 +917,19 @@ def test_grouped_row_index_bounds(C):
         assert np.array_equal(yh[r], ref[0])
 
 
-@pytest.mark.parametrize("sizes", [[3, 0, 1, 19, 2, 0, 5, 9], [3, 0, 1, 4, 2, 0, 7, 1]],
-                         ids=["large-groups", "small-groups"])
-@pytest.mark.parametrize("K,N", [(256, 72), (768, 64), (1280, 40), (2048, 136)])
+@pytest.mark.parametrize("sizes", [[3, 0, 1, 19, 2, 0, 5, 9], [3, 0, 1, 4, 2, 0, 7, 1],
+                                   [1, 0, 2, 1, 2, 0, 1, 1]],
+                         ids=["large-groups", "small-groups", "decode-groups"])
+@pytest.mark.parametrize("K,N", [(256, 72), (768, 64), (1280, 40), (2048, 136), (1024, 200)])
 def test_grouped_ring_shapes(C, K, N, sizes):
     """Grouped linear on 16-byte aligned operands with K % 256 == 0: group
     sizes 0 .. 19 (a mean above 4 rows takes 16 rows per pass, else 8, so
-    the 19-row group makes two passes), invalid row indices, K of 1, 3, 5
-    and 8 super-chunks against a 3-slot ring, N with partial tiles and whole
-    idle waves.  Every written row against the oracle; invalid rows and rows
-    past the last group stay unwritten."""
+    the 19-row group makes two passes; a mean of 2 rows or fewer splits
+    each tile's K range between two waves where the super-chunk count is
+    even), invalid row indices, K of 1, 3, 4, 5 and 8 super-chunks against
+    a 3- or 4-slot ring, N with partial tiles and whole idle waves.  Every
+    written row against the oracle; invalid rows and rows past the last
+    group stay unwritten."""
     say(f"grouped ring K={K} N={N} sizes={sizes}")
     rng = np.random.default_rng(K + N + sum(sizes))
     G = len(sizes)
@@ -934,7 +937,8 @@ def test_grouped_ring_shapes(C, K, N, sizes):
     P = int(offsets[-1])
     a_rows = 11
     row_index = rng.integers(0, a_rows, P + 3).astype(np.int32)
-    row_index[[4, 10, 20]] = [-1, a_rows, 1 << 20]  # invalid: not written
+    bad = [i for i in (4, 10, 20) if i < P]
+    row_index[bad] = [-1, a_rows, 1 << 20][:len(bad)]  # invalid: not written
     ac = rng.integers(0, 256, (a_rows, K // 2), dtype=np.uint8)
     asf = rng.integers(0x20, 0x48, (a_rows, K // 16), dtype=np.uint8)
     wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
