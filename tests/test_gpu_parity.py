@@ -918,15 +918,16 @@ def test_grouped_row_index_bounds(C):
 
 
 @pytest.mark.parametrize("sizes", [[3, 0, 1, 19, 2, 0, 5, 9], [3, 0, 1, 4, 2, 0, 7, 1],
-                                   [1, 0, 2, 1, 2, 0, 1, 1]],
-                         ids=["large-groups", "small-groups", "decode-groups"])
+                                   [1, 0, 2, 1, 2, 0, 1, 1], [1, 0, 5, 0, 0, 1, 0, 1]],
+                         ids=["large-groups", "small-groups", "decode-groups", "decode-uneven"])
 @pytest.mark.parametrize("K,N", [(256, 72), (768, 64), (1280, 40), (2048, 136), (1024, 200)])
 def test_grouped_ring_shapes(C, K, N, sizes):
     """Grouped linear on 16-byte aligned operands with K % 256 == 0: group
     sizes 0 .. 19 (a mean above 4 rows takes 16 rows per pass, else 8, so
     the 19-row group makes two passes; a mean of 2 rows or fewer splits
     each tile's K range between two waves where the super-chunk count is
-    even), invalid row indices, K of 1, 3, 4, 5 and 8 super-chunks against
+    even, and passes two rows at a time, so the 5-row group makes three),
+    invalid row indices, K of 1, 3, 4, 5 and 8 super-chunks against
     a 3- or 4-slot ring, N with partial tiles and whole idle waves.  Every
     written row against the oracle; invalid rows and rows past the last
     group stay unwritten."""
@@ -1655,10 +1656,31 @@ def test_grouped_linear_run_routed_token(C):
 def test_moe_run(C, tokens, experts, topk, K1, N1, N2):
     """nvfp4_moe_run: every step against the oracle on the GPU's own input to
     it, and every output bit-equal to the separate calls'."""
-    from moe_amax_gsa_amd.layer import Nvfp4MoE
     say("moe run", tokens, experts, topk, K1, N1, N2)
     moe = W.make_moe(tokens=tokens, experts=experts, topk=topk, K1=K1, N1=N1, K2=N1 // 2, N2=N2,
                      granularity=8, seed=tokens + experts)
+    moe_run_matches_separate_calls(C, moe)
+
+
+def test_moe_run_decode_skewed_groups(C):
+    """Six tokens, 2 of 32 experts each with Zipf routing: one pair per
+    expert on average (both projections split each weight tile's K range
+    between two waves), while the first expert holds 5 pairs, so its tiles
+    make three passes of two rows.  Every step against the oracle, every
+    output bit-equal to the separate calls."""
+    say("moe run decode zipf")
+    moe = W.make_moe(tokens=6, experts=32, topk=2, K1=1024, N1=1024, K2=512, N2=64,
+                     granularity=8, seed=5, routing="zipf")
+    counts = np.diff(moe.offsets)
+    assert counts.max() == 5 and -(-int(counts.sum()) // moe.E) == 1
+    moe_run_matches_separate_calls(C, moe)
+
+
+def moe_run_matches_separate_calls(C, moe):
+    """The MoE pair stepwise against the oracle, then the layer through
+    nvfp4_moe_run and through the separate calls: gsa, codes, scales, h and
+    y bit-equal between the two."""
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
     run_moe_stepwise(C, moe, fused=True)
     P = int(moe.offsets[-1])
     w = W.moe_weights_to(moe, DEV)
