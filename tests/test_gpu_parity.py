@@ -484,6 +484,22 @@ def test_linear_wide_tiles_integer_exact(C, M, N, K):
     assert torch.equal(y16.cpu(), torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("side", ["a", "w"])
+def test_linear_wide_tiles_every_scale_byte_exact(C, side):
+    """Every finite E4M3 scale byte on either operand through the 256 x 256
+    tiles (3072 x 4096: 192 tiles, K = 256: both step pairs of a chunk's
+    scale layout): the whole output bit-identical to the FP64 product of the
+    oracle's dequantized operands (exact on any summation order here)."""
+    say("linear wide every scale byte", side)
+    M, N, K = 3072, 4096, 256
+    ac, asf, wc, wsf = every_scale_byte_operands(M, N, K, side, seed=5 + (side == "w"))
+    ref = oracle.dequantize(ac, asf, 1.0) @ oracle.dequantize(wc, wsf, 1.0).T
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(to_dev(ac), to_dev(asf), one, to_dev(wc), to_dev(wsf), one, y)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("M,N,K", WIDE_SHAPES[:2])
 def test_linear_wide_tiles_parity(C, M, N, K):
     """The same shapes with scales over the E4M3 range and a quantized
