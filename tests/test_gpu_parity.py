@@ -1398,6 +1398,12 @@ TILED_CASES = [
     ([300], 1024, 40),                        # one group (G = 1)
     ([33] * 40, 256, 72),                     # 40 groups of 33 rows: scan over 40 groups
     ([2, 0, 0, 90, 1, 1, 1, 1, 300], 512, 64),  # skewed: mean 44, most groups tiny
+    # larger groups: ragged row tiles, partial column tiles
+    ([130, 0, 128, 255, 97, 301], 512, 200),  # groups of 2 to 5 row tiles, one empty
+    ([130, 0, 128, 255, 97, 301], 768, 520),  # K % 512 != 0; the last column tile 8 wide
+    ([200, 200, 200], 7168, 256),             # long K, 14 chunks of 512
+    ([96] * 20, 256, 64),                     # 20 groups of 96 rows, one chunk of 256
+    ([1, 0, 0, 500, 3, 2, 1, 300], 512, 136),  # skewed: mean 101, most groups tiny
 ]
 
 
@@ -1447,11 +1453,13 @@ def test_grouped_tiled_many_groups_and_identity_rows(C):
         assert rel_err(yh, ref) <= REL_TOL, gather
 
 
-def test_grouped_tiled_bf16_is_rounded_fp32(C):
+@pytest.mark.parametrize("sizes", [[64, 100, 3, 150], [100, 200, 3, 150]],
+                         ids=["mean-80", "mean-114"])
+def test_grouped_tiled_bf16_is_rounded_fp32(C, sizes):
     """bf16 output of the tiled grouped kernel: the fp32 output rounded to
     nearest even, bit for bit."""
-    say("grouped tiled bf16")
-    c = grouped_case(77, [64, 100, 3, 150], 512, 96, start=1, tail=2)
+    say("grouped tiled bf16", sizes)
+    c = grouped_case(77, sizes, 512, 96, start=1, tail=2)
     y32 = grouped_gpu(C, c)
     y16 = grouped_gpu(C, c, torch.bfloat16)
     live = grouped_expected_rows(c)
@@ -1491,15 +1499,31 @@ def test_grouped_tiled_many_tiles(C):
 @pytest.mark.parametrize("gran", [8, 1])
 @pytest.mark.parametrize("K,N", [(512, 256), (768, 416)])
 def test_grouped_swiglu_tiled_matches_unfused(C, K, N, gran, lim):
-    """The fused SwiGLU epilogue of the tiled grouped kernel (groups of 32 or
-    more rows on average) against the separate calls, which take the same
-    tiled kernel for the linear: h bit-identical, the same gsa_h, h's codes
-    and scales identical; rows outside every group and with an invalid
-    row_index unwritten in both and outside the amax.  h against the
-    oracle's SwiGLU of the GPU's l1, codes and scales against the oracle's
-    quantize of the GPU's h.  N = 416: a partial last column tile."""
-    say(f"grouped swiglu tiled K={K} N={N} gran={gran} limit={lim}")
-    c = grouped_case(K + N + gran, [37, 0, 128, 129, 5, 203], K, N, start=3, tail=4,
+    """The fused SwiGLU epilogue of the tiled grouped kernel (groups of 32
+    or more rows on average) against the separate calls.  N = 416: a partial
+    last column tile."""
+    grouped_swiglu_fused_matches_unfused(C, [37, 0, 128, 129, 5, 203], K, N, gran, lim)
+
+
+@pytest.mark.parametrize("lim", ["off", "median"])
+@pytest.mark.parametrize("gran", [1, 2, 4, 8])
+@pytest.mark.parametrize("K,N", [(512, 512), (768, 384)])
+def test_grouped_swiglu_large_groups_match_unfused(C, K, N, gran, lim):
+    """The same with groups of 2 to 5 row tiles and every granularity the
+    entry point takes (gate and up columns 1 to 8 apart).  N = 384: a
+    partial last column tile."""
+    grouped_swiglu_fused_matches_unfused(C, [130, 0, 128, 255, 97, 301], K, N, gran, lim)
+
+
+def grouped_swiglu_fused_matches_unfused(C, sizes, K, N, gran, lim):
+    """The fused SwiGLU epilogue of a tiled grouped kernel against the
+    separate calls, which take the same tiled kernel for the linear: h
+    bit-identical, the same gsa_h, h's codes and scales identical; rows
+    outside every group and with an invalid row_index unwritten in both and
+    outside the amax.  h against the oracle's SwiGLU of the GPU's l1, codes
+    and scales against the oracle's quantize of the GPU's h."""
+    say(f"grouped swiglu tiled sizes={sizes} K={K} N={N} gran={gran} limit={lim}")
+    c = grouped_case(K + N + gran, sizes, K, N, start=3, tail=4,
                      bad=[(5, -1), (40, 64), (100, 1 << 20)])
     P = c["M_total"]
     live = grouped_expected_rows(c)
@@ -1668,6 +1692,7 @@ def test_grouped_linear_run_routed_token(C):
     (1, 16, 12, 1024, 6144, 6144),  # 576 ring workgroups each: the split prologue
     (256, 8, 2, 512, 512, 64),    # 64 pairs per expert: both projections tiled
     (96, 3, 1, 1024, 512, 136),   # 32 pairs per expert, N2 a partial column tile
+    (384, 8, 2, 512, 512, 136),   # 96 pairs per expert, both projections tiled
 ])
 def test_moe_run(C, tokens, experts, topk, K1, N1, N2):
     """nvfp4_moe_run: every step against the oracle on the GPU's own input to
