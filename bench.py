@@ -210,11 +210,16 @@ class LinearBench:
                                 self.y, self.ws)
 
 
-def bench_linear(C, name, dev, steps, warmup, kiters):
+def bench_linear(C, name, dev, steps, warmup, kiters, settle=False):
+    """settle: one untimed pass of the step graph before the timed ones (on
+    the GEMM shapes the first timed pass of a workload ran 5-15% slower than
+    the same pass repeated)."""
     from moe_amax_gsa_amd import workloads as W
     inp = W.make(name)
     b = LinearBench(C, inp, dev)
     r = {"rotated_weight_copies": b.ncopies}
+    if settle:
+        graph_ms_per_step(b.run, steps, warmup)
     r["step_us"] = 1e3 * graph_ms_per_step(b.run, steps, warmup)
     r["step3_us"] = 1e3 * graph_ms_per_step(b.step3, steps, warmup)
     r["linear_us"] = kernel_us(b.linear, kiters, pre=b.quantize)
@@ -673,7 +678,7 @@ def main():
                 continue
             log("workload", name)
             workloads[name] = bench_linear(C, name, dev, steps, min(args.warmup, 10),
-                                           min(kiters, steps))[2]
+                                           min(kiters, steps), settle=name != "tiny_m1_k256_n256")[2]
             if name != "tiny_m1_k256_n256":
                 c = __import__("moe_amax_gsa_amd.workloads", fromlist=["WORKLOADS"]).WORKLOADS[name]
                 us = torch_bf16_matmul_us(c["M"], c["N"], c["K"], dev)

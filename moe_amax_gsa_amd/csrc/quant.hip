@@ -221,14 +221,17 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
   return hipGetLastError();
 }
 
-// Steps 1 and 2 on a tensor past the one-workgroup size.  With few amax
-// partials the quantize reduces them itself (two launches instead of
-// three); large tensors take the separate finalize and the wide quantize.
+// Steps 1 and 2 on a tensor past the one-workgroup size: at most
+// QUANTIZE_INLINE_PARTS amax partials (each amax workgroup takes a larger
+// slice past that size), which every quantize workgroup reduces itself (two
+// launches instead of three); tensors of 256 MiB or more take the separate
+// finalize and the wide quantize.
 hipError_t launch_amax_then_quantize(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
                                      uint8_t* codes, uint8_t* scales, void* ws, hipStream_t s) {
   const int64_t numel = M * K, nhalf = M * (K / 8);
-  const int parts = amax_parts_for(numel);
-  if (numel <= AMAX_SMALL_NUMEL || nhalf >= QUANTIZE_WIDE_HALVES || parts > QUANTIZE_INLINE_PARTS) {
+  const int parts = amax_parts_for(numel) < QUANTIZE_INLINE_PARTS ? amax_parts_for(numel)
+                                                                   : QUANTIZE_INLINE_PARTS;
+  if (numel <= AMAX_SMALL_NUMEL || nhalf >= QUANTIZE_WIDE_HALVES) {
     const hipError_t e = launch_amax_gsa(x, bf16, numel, gsa, ws, s);
     if (e != hipSuccess) return e;
     return launch_quantize(x, bf16, M, K, gsa, codes, scales, s);
