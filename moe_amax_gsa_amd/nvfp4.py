@@ -125,6 +125,55 @@ def _dtype(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _room(t: Optional[torch.Tensor], nbytes: int, what: str, dtype=None,
+          optional: bool = False) -> None:
+    """The kernels address raw device pointers: refuse a buffer smaller than
+    what the call reads or writes (or of the wrong element type) before any
+    pointer reaches the library."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{what} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{what} holds {_nbytes(t)} bytes, the call needs {nbytes}")
+
+
+def _out(t: torch.Tensor, n: int, what: str) -> None:
+    """An output of n elements in bf16 or fp32."""
+    _dtype(t)
+    _room(t, n * t.element_size(), what)
+
+
+_U8, _F32, _I32 = torch.uint8, torch.float32, torch.int32
+
+
+def _linear_operands(a_codes, a_scales, gsa, n_gsa, w_codes, w_scales, ws2, n_ws2, M, N, K):
+    _room(a_codes, M * (K // 2), "activation codes", _U8)
+    _room(a_scales, M * (K // 16), "activation scales", _U8)
+    _room(gsa, 4 * n_gsa, "gsa", _F32)
+    _room(w_codes, N * (K // 2), "w_codes", _U8)
+    _room(w_scales, N * (K // 16), "w_scales", _U8)
+    _room(ws2, 4 * n_ws2, "ws2", _F32)
+
+
+def _grouped_operands(a_codes, a_scales, a_rows, gsa, row_index, offsets, G, M_total, w_codes,
+                      w_scales, ws2, N, K):
+    _room(a_codes, a_rows * (K // 2), "activation codes", _U8)
+    _room(a_scales, a_rows * (K // 16), "activation scales", _U8)
+    _room(gsa, 4, "gsa", _F32)
+    _room(row_index, 4 * M_total, "row_index", _I32, optional=True)
+    _room(offsets, 4 * (G + 1), "group_offsets", _I32)
+    _room(w_codes, G * N * (K // 2), "w_codes", _U8)
+    _room(w_scales, G * N * (K // 16), "w_scales", _U8)
+    _room(ws2, 4 * G, "ws2", _F32)
+
+
 def nvfp4_abi_version() -> int:
     return lib.nvfp4_abi_version()
 
@@ -136,6 +185,7 @@ def nvfp4_workspace_bytes(op: int, M: int, N: int = 0, K: int = 0, G: int = 0) -
 def nvfp4_amax_gsa(x: torch.Tensor, gsa: torch.Tensor, ws: Optional[torch.Tensor] = None,
                    stream=None) -> None:
     """gsa[0] = max(max|x|, 1e-8) / 2688 on the device (x bf16 or fp32)."""
+    _room(gsa, 4, "gsa", _F32)
     _check(lib.nvfp4_amax_gsa(_ptr(x), _dtype(x), x.numel(), _ptr(gsa), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(),
                               _stream(stream)), "nvfp4_amax_gsa")
@@ -145,6 +195,9 @@ def nvfp4_quantize_from_buffer(x: torch.Tensor, gsa: torch.Tensor, codes: torch.
                                scales: torch.Tensor, stream=None) -> None:
     """x (M, K) -> codes (M, K/2) uint8, scales (M, K/16) uint8 with device gsa."""
     M, K = x.shape
+    _room(gsa, 4, "gsa", _F32)
+    _room(codes, M * (K // 2), "codes", _U8)
+    _room(scales, M * (K // 16), "scales", _U8)
     _check(lib.nvfp4_quantize_from_buffer(_ptr(x), _dtype(x), M, K, _ptr(gsa), _ptr(codes),
                                           _ptr(scales), _stream(stream)),
            "nvfp4_quantize_from_buffer")
@@ -157,6 +210,8 @@ def nvfp4_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.Tenso
     M = a_codes.shape[0]
     K = a_codes.shape[1] * 2
     N = w_codes.shape[0]
+    _linear_operands(a_codes, a_scales, gsa, 1, w_codes, w_scales, ws2, 1, M, N, K)
+    _out(y, M * N, "y")
     _check(lib.nvfp4_linear(_ptr(a_codes), _ptr(a_scales), _ptr(gsa), _ptr(w_codes),
                             _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y), M, N, K, _ptr(ws),
                             0 if ws is None else ws.numel() * ws.element_size(),
@@ -170,6 +225,8 @@ def nvfp4_linear_rows(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa_rows: t
     M = a_codes.shape[0]
     K = a_codes.shape[1] * 2
     N = w_codes.shape[0]
+    _linear_operands(a_codes, a_scales, gsa_rows, M, w_codes, w_scales, ws2, 1, M, N, K)
+    _out(y, M * N, "y")
     _check(lib.nvfp4_linear_rows(_ptr(a_codes), _ptr(a_scales), _ptr(gsa_rows), _ptr(w_codes),
                                  _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y), M, N, K,
                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
@@ -186,6 +243,10 @@ def nvfp4_router_topk(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: torch.
     K = a_codes.shape[1] * 2
     N = w_codes.shape[0]
     k = topk_idx.shape[1]
+    _linear_operands(a_codes, a_scales, gsa, 1, w_codes, w_scales, ws2, 1, M, N, K)
+    _room(bias, 4 * N, "bias", _F32, optional=True)
+    _room(topk_idx, 4 * M * k, "topk_idx", _I32)
+    _room(topk_score, 4 * M * k, "topk_score", _F32)
     _check(lib.nvfp4_router_topk(_ptr(a_codes), _ptr(a_scales), _ptr(gsa), _ptr(w_codes),
                                  _ptr(w_scales), _ptr(ws2), _ptr(bias), M, N, K, k,
                                  _ptr(topk_idx), _ptr(topk_score), _ptr(ws),
@@ -200,6 +261,8 @@ def nvfp4_linear_run(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
     """amax -> gsa -> quantize -> linear on x (M, K); writes gsa, codes, scales, y."""
     M, K = x.shape
     N = w_codes.shape[0]
+    _linear_operands(codes, scales, gsa, 1, w_codes, w_scales, ws2, 1, M, N, K)
+    _out(y, M * N, "y")
     _check(lib.nvfp4_linear_run(_ptr(x), _dtype(x), _ptr(gsa), _ptr(codes), _ptr(scales),
                                 _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(y), _dtype(y),
                                 M, N, K, _ptr(ws),
@@ -214,6 +277,8 @@ def nvfp4_linear_run_noalloc(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Te
     """nvfp4_linear_run without a workspace: the library's static scratch."""
     M, K = x.shape
     N = w_codes.shape[0]
+    _linear_operands(codes, scales, gsa, 1, w_codes, w_scales, ws2, 1, M, N, K)
+    _out(y, M * N, "y")
     _check(lib.nvfp4_linear_run_noalloc(_ptr(x), _dtype(x), _ptr(gsa), _ptr(codes), _ptr(scales),
                                         _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(y),
                                         _dtype(y), M, N, K, _stream(stream)),
@@ -227,6 +292,9 @@ def nvfp4_grouped_linear(a_codes: torch.Tensor, a_scales: torch.Tensor, gsa: tor
     """w_codes (G, N, K/2), w_scales (G, N, K/16), ws2 (G,), y (M_total, N)."""
     G, N = w_codes.shape[0], w_codes.shape[1]
     K = w_codes.shape[2] * 2
+    _grouped_operands(a_codes, a_scales, a_codes.shape[0], gsa, row_index, group_offsets, G,
+                      y.shape[0], w_codes, w_scales, ws2, N, K)
+    _out(y, y.shape[0] * N, "y")
     _check(lib.nvfp4_grouped_linear(_ptr(a_codes), _ptr(a_scales), _ptr(gsa), a_codes.shape[0],
                                     _ptr(row_index), _ptr(group_offsets), G, y.shape[0],
                                     _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(y),
@@ -238,6 +306,9 @@ def nvfp4_amax_quantize(x: torch.Tensor, gsa: torch.Tensor, codes: torch.Tensor,
                         stream=None) -> None:
     """Steps 1 and 2: gsa, codes (M, K/2), scales (M, K/16) of x (M, K)."""
     M, K = x.shape
+    _room(gsa, 4, "gsa", _F32)
+    _room(codes, M * (K // 2), "codes", _U8)
+    _room(scales, M * (K // 16), "scales", _U8)
     _check(lib.nvfp4_amax_quantize(_ptr(x), _dtype(x), M, K, _ptr(gsa), _ptr(codes),
                                    _ptr(scales), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(),
@@ -251,6 +322,11 @@ def nvfp4_rmsnorm_quantize(x: torch.Tensor, norm_weight: torch.Tensor, gsa: torc
     """RMSNorm of x (M, K) with norm_weight (K,), quantized: codes (M, K/2),
     scales (M, K/16), inv_rms (M,), gsa (1,) or, per_row, (M,)."""
     M, K = x.shape
+    _room(norm_weight, K * norm_weight.element_size(), "norm_weight")
+    _room(gsa, 4 * (M if per_row else 1), "gsa", _F32)
+    _room(inv_rms, 4 * M, "inv_rms", _F32)
+    _room(codes, M * (K // 2), "codes", _U8)
+    _room(scales, M * (K // 16), "scales", _U8)
     _check(lib.nvfp4_rmsnorm_quantize(_ptr(x), _dtype(x), _ptr(norm_weight), _dtype(norm_weight),
                                       eps, M, K, 1 if per_row else 0, _ptr(gsa), _ptr(inv_rms),
                                       _ptr(codes), _ptr(scales), _ptr(ws),
@@ -263,6 +339,9 @@ def nvfp4_quantize_weight(w: torch.Tensor, ws2: torch.Tensor, codes: torch.Tenso
                           stream=None) -> None:
     """w (N, K) bf16/fp32 -> codes (N, K/2), scales (N, K/16), ws2 (1,) fp32."""
     N, K = w.shape
+    _room(ws2, 4, "ws2", _F32)
+    _room(codes, N * (K // 2), "codes", _U8)
+    _room(scales, N * (K // 16), "scales", _U8)
     _check(lib.nvfp4_quantize_weight(_ptr(w), _dtype(w), N, K, _ptr(ws2), _ptr(codes),
                                      _ptr(scales), _ptr(ws),
                                      0 if ws is None else ws.numel() * ws.element_size(),
@@ -283,6 +362,13 @@ def nvfp4_grouped_linear_swiglu(a_codes: torch.Tensor, a_scales: torch.Tensor, g
     (<= 0: none)."""
     G, NI = w_codes.shape[0], w_codes.shape[1]
     K = w_codes.shape[2] * 2
+    P = h.shape[0]
+    _grouped_operands(a_codes, a_scales, a_codes.shape[0], gsa, row_index, group_offsets, G, P,
+                      w_codes, w_scales, ws2, NI, K)
+    _room(h, 4 * P * (NI // 2), "h", _F32)
+    _room(gsa_h, 4, "gsa_h", _F32)
+    _room(h_codes, P * (NI // 4), "h_codes", _U8, optional=True)
+    _room(h_scales, P * (NI // 32), "h_scales", _U8, optional=True)
     _check(lib.nvfp4_grouped_linear_swiglu(
         _ptr(a_codes), _ptr(a_scales), _ptr(gsa), a_codes.shape[0], _ptr(row_index),
         _ptr(group_offsets), G, h.shape[0], _ptr(w_codes), _ptr(w_scales), _ptr(ws2), _ptr(h),
@@ -295,12 +381,10 @@ def nvfp4_swiglu_deinterleave(l1: torch.Tensor, h: torch.Tensor, granularity: in
     """h (M, N/2) = silu(gate) * up from granularity-interleaved l1 (M, N),
     fp32; limit > 0 caps the gate at limit and clamps up to [-limit, limit]."""
     M, NI = l1.shape
+    _room(l1, 4 * M * NI, "l1", _F32)
+    _room(h, 4 * M * (NI // 2), "h", _F32)
     _check(lib.nvfp4_swiglu_deinterleave(_ptr(l1), _ptr(h), M, NI, granularity, limit,
                                          _stream(stream)), "nvfp4_swiglu_deinterleave")
-
-
-def _nbytes(t: Optional[torch.Tensor]) -> int:
-    return 0 if t is None else t.numel() * t.element_size()
 
 
 def nvfp4_grouped_linear_run(x: torch.Tensor, gsa: torch.Tensor, x_codes: torch.Tensor,
@@ -313,6 +397,10 @@ def nvfp4_grouped_linear_run(x: torch.Tensor, gsa: torch.Tensor, x_codes: torch.
     x_scales receive x's quantization."""
     G, N = w_codes.shape[0], w_codes.shape[1]
     K = w_codes.shape[2] * 2
+    R = x.shape[0]
+    _grouped_operands(x_codes, x_scales, R, gsa, row_index, group_offsets, G, y.shape[0],
+                      w_codes, w_scales, ws2, N, K)
+    _out(y, y.shape[0] * N, "y")
     _check(lib.nvfp4_grouped_linear_run(_ptr(x), _dtype(x), x.shape[0], _ptr(gsa), _ptr(x_codes),
                                         _ptr(x_scales), _ptr(row_index), _ptr(group_offsets), G,
                                         y.shape[0], _ptr(w_codes), _ptr(w_scales), _ptr(ws2),
@@ -332,6 +420,17 @@ def nvfp4_moe_run(x: torch.Tensor, gsa_x: torch.Tensor, x_codes: torch.Tensor,
     E, N1 = w1_codes.shape[0], w1_codes.shape[1]
     K1 = w1_codes.shape[2] * 2
     N2 = w2_codes.shape[1]
+    T, P = x.shape[0], row_index.shape[0]
+    _grouped_operands(x_codes, x_scales, T, gsa_x, row_index, group_offsets, E, P, w1_codes,
+                      w1_scales, w1_ws2, N1, K1)
+    _room(h, 4 * P * (N1 // 2), "h", _F32)
+    _room(gsa_h, 4, "gsa_h", _F32)
+    _room(h_codes, P * (N1 // 4), "h_codes", _U8)
+    _room(h_scales, P * (N1 // 32), "h_scales", _U8)
+    _room(w2_codes, E * N2 * (N1 // 4), "w2_codes", _U8)
+    _room(w2_scales, E * N2 * (N1 // 32), "w2_scales", _U8)
+    _room(w2_ws2, 4 * E, "w2_ws2", _F32)
+    _out(y, P * N2, "y")
     _check(lib.nvfp4_moe_run(_ptr(x), _dtype(x), x.shape[0], _ptr(gsa_x), _ptr(x_codes),
                              _ptr(x_scales), _ptr(row_index), _ptr(group_offsets), E,
                              row_index.shape[0], _ptr(w1_codes), _ptr(w1_scales), _ptr(w1_ws2),

@@ -192,3 +192,45 @@ def test_validation_of_the_run_entries(C):
     assert mr(fake, 0, 1, *f, fake, fake, 8, 8, *f, 512, 512, 8, 0.0, *[fake] * 4, *f, 40, fake,
               1, fake, 4, None) in (-4, -5)                                   # workspace
     assert C.nvfp4_workspace_bytes(C.OP_MOE_RUN, 1, 4096, 7168, 256) >= 4 * 128 * 256
+
+
+def test_binding_refuses_undersized_buffers_before_the_library(C):
+    """The kernels address raw pointers, so the binding checks every buffer's
+    size and element type against what the call touches before any pointer
+    reaches the library: an undersized or mistyped buffer raises ValueError
+    naming it; well-sized host tensors get as far as the device check."""
+    import torch
+    M, N, K = 3, 32, 64
+    ok = dict(a_codes=torch.zeros(M, K // 2, dtype=torch.uint8),
+              a_scales=torch.zeros(M, K // 16, dtype=torch.uint8),
+              gsa=torch.zeros(1), w_codes=torch.zeros(N, K // 2, dtype=torch.uint8),
+              w_scales=torch.zeros(N, K // 16, dtype=torch.uint8), ws2=torch.zeros(1),
+              y=torch.zeros(M, N))
+    with pytest.raises(ValueError, match="on the GPU"):
+        C.nvfp4_linear(**ok)
+    for name, bad, msg in [("a_scales", torch.zeros(M, K // 16 - 1, dtype=torch.uint8), "holds"),
+                           ("w_scales", torch.zeros(N - 1, K // 16, dtype=torch.uint8), "holds"),
+                           ("gsa", torch.zeros(1, dtype=torch.float64), "must be"),
+                           ("y", torch.zeros(M, N - 1), "holds")]:
+        with pytest.raises(ValueError, match=msg):
+            C.nvfp4_linear(**{**ok, name: bad})
+    # grouped: offsets need G + 1 int32 entries, row_index one per output row
+    G = 2
+    g = dict(a_codes=ok["a_codes"], a_scales=ok["a_scales"], gsa=ok["gsa"],
+             row_index=torch.zeros(4, dtype=torch.int32),
+             group_offsets=torch.zeros(G + 1, dtype=torch.int32),
+             w_codes=torch.zeros(G, N, K // 2, dtype=torch.uint8),
+             w_scales=torch.zeros(G, N, K // 16, dtype=torch.uint8), ws2=torch.zeros(G),
+             y=torch.zeros(4, N))
+    with pytest.raises(ValueError, match="on the GPU"):
+        C.nvfp4_grouped_linear(**g)
+    for name, bad, msg in [("group_offsets", torch.zeros(G, dtype=torch.int32), "holds"),
+                           ("group_offsets", torch.zeros(G + 1, dtype=torch.int64), "must be"),
+                           ("row_index", torch.zeros(3, dtype=torch.int32), "holds"),
+                           ("ws2", torch.zeros(G - 1), "holds")]:
+        with pytest.raises(ValueError, match=msg):
+            C.nvfp4_grouped_linear(**{**g, name: bad})
+    with pytest.raises(ValueError, match="holds"):
+        C.nvfp4_quantize_from_buffer(torch.zeros(M, K, dtype=torch.bfloat16), ok["gsa"],
+                                     torch.zeros(M, K // 2 - 1, dtype=torch.uint8),
+                                     ok["a_scales"])
