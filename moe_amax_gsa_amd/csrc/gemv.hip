@@ -838,7 +838,10 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
       for (int p = 0; p < MP; ++p) {
         const float v = acc[p] + __shfl_xor(acc[p], 16, 64);
         const int rl = 2 * p + c_mloc, r = r0 + rl, n = n0 + col;
-        const bool ok = (j & 1) == 0 && r < r_end && n < N && __shfl(my_src, rl, 64) >= 0;
+        // every lane takes part in the shuffle: a lane left out of it (its
+        // column past N) would hand its readers an undefined row index
+        const int rsrc = __shfl(my_src, rl, 64);
+        const bool ok = (j & 1) == 0 && r < r_end && n < N && rsrc >= 0;
         if (SWIGLU) {
           const float gv = v * gscale;
           const float uv = __shfl_xor(gv, args.gran, 64);  // the paired up column

@@ -936,7 +936,8 @@ def test_grouped_row_index_bounds(C):
 @pytest.mark.parametrize("sizes", [[3, 0, 1, 19, 2, 0, 5, 9], [3, 0, 1, 4, 2, 0, 7, 1],
                                    [1, 0, 2, 1, 2, 0, 1, 1], [1, 0, 5, 0, 0, 1, 0, 1]],
                          ids=["large-groups", "small-groups", "decode-groups", "decode-uneven"])
-@pytest.mark.parametrize("K,N", [(256, 72), (768, 64), (1280, 40), (2048, 136), (1024, 200)])
+@pytest.mark.parametrize("K,N", [(256, 72), (768, 64), (1280, 40), (2048, 136), (1024, 200),
+                                 (512, 273)])
 def test_grouped_ring_shapes(C, K, N, sizes):
     """Grouped linear on 16-byte aligned operands with K % 256 == 0: group
     sizes 0 .. 19 (a mean above 4 rows takes 16 rows per pass, else 8, so
@@ -944,9 +945,10 @@ def test_grouped_ring_shapes(C, K, N, sizes):
     each tile's K range between two waves where the super-chunk count is
     even, and passes two rows at a time, so the 5-row group makes three),
     invalid row indices, K of 1, 3, 4, 5 and 8 super-chunks against
-    a 3- or 4-slot ring, N with partial tiles and whole idle waves.  Every
-    written row against the oracle; invalid rows and rows past the last
-    group stay unwritten."""
+    a 3- or 4-slot ring, N with partial tiles and whole idle waves (N = 273:
+    one valid column in the last tile, so an invalid row's mask comes from
+    lanes whose own column is past N).  Every written row against the
+    oracle; invalid rows and rows past the last group stay unwritten."""
     say(f"grouped ring K={K} N={N} sizes={sizes}")
     rng = np.random.default_rng(K + N + sum(sizes))
     G = len(sizes)
