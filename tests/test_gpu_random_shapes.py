@@ -191,3 +191,161 @@ def test_random_grouped_linear_run(C, case):
     if M_total:
         ref = oracle.grouped_linear(oc, os_, g, row_index, offsets, wc, wsf, ws2, M_total)
         assert rel_err(y[:M_total].cpu().numpy().astype(np.float64), ref) <= REL_TOL
+
+
+# ---------------------------------------------------------------- more entry points
+import test_gpu_parity as P  # noqa: E402  (shared GPU helpers of the parity tests)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_amax_quantize(C, case):
+    """nvfp4_amax_quantize across the one-workgroup size (65 536 elements)
+    and the inline-partials size: gsa, codes and scales bit-exact."""
+    rng = np.random.default_rng(7000 + case)
+    band = case % 3
+    numel_hi = [65536, 4 << 20, 16 << 20][band]
+    K = 16 * int(rng.integers(1, 600))
+    M = max(1, int(rng.integers(numel_hi // 8, numel_hi)) // K)
+    dtype = "bf16" if rng.integers(0, 2) == 0 else "fp32"
+    say("random amax quantize", case, M, K, dtype)
+    inp = W.make_linear(M, K, 1, seed=7100 + case, x="outliers")
+    xh = inp.x if dtype == "bf16" else np.ascontiguousarray(W.bf16_bits_to_f32(inp.x))
+    x = W.bf16_to_torch(inp.x, DEV) if dtype == "bf16" else to_dev(xh)
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    nws = C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, M * K)
+    ws = torch.full((max(nws, 16),), 0xAB, dtype=torch.uint8, device=DEV)
+    C.nvfp4_amax_quantize(x, gsa, codes, scales, ws)
+    g = np.float32(gsa.cpu().numpy()[0])
+    assert g == oracle.amax_gsa(xh)
+    oc, os_ = oracle.quantize(xh, g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_rmsnorm_quantize(C, case):
+    """nvfp4_rmsnorm_quantize on random (M, K), one scale or one per row:
+    inv_rms within 1e-5 of the binary64 oracle, codes, scales and gsa
+    bit-exact with the oracle's quantize of the rows rebuilt from the GPU's
+    inv_rms (as the parity test does)."""
+    rng = np.random.default_rng(8000 + case)
+    M = int(rng.choice(M_CHOICES))
+    K = 16 * int(rng.integers(1, 520))
+    per_row = bool(rng.integers(0, 2))
+    xd = "bf16" if rng.integers(0, 2) == 0 else "fp32"
+    say("random rmsnorm", case, M, K, per_row, xd)
+    r = W.make_rmsnorm(M, K, 8100 + case)
+    xh = r.x if xd == "bf16" else np.ascontiguousarray(W.bf16_bits_to_f32(r.x))
+    x = W.bf16_to_torch(r.x, DEV) if xd == "bf16" else to_dev(xh)
+    w = W.bf16_to_torch(r.w, DEV)
+    gsa, inv, codes, scales = P.gpu_rmsnorm_quantize(C, x, w, per_row)
+    inv_g = inv.cpu().numpy()
+    inv_o, _ = oracle.rmsnorm(xh, r.w, 1e-6)
+    assert np.max(np.abs(inv_g / inv_o - 1.0)) <= P.INV_RMS_TOL
+    y32 = (W.bf16_bits_to_f32(r.x) * inv_g[:, None]).astype(np.float32) * \
+        W.bf16_bits_to_f32(r.w)[None, :]
+    if per_row:
+        oc, os_, og = oracle.quantize_rows(y32)
+        assert np.array_equal(gsa.cpu().numpy(), og)
+    else:
+        og = oracle.amax_gsa(y32)
+        assert np.float32(gsa.cpu().numpy()[0]) == og
+        oc, os_ = oracle.quantize(y32, og)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_router_topk(C, case):
+    """nvfp4_router_topk on random (M, N, K, k): logits within 1e-3 of the
+    oracle's linear, the choice equal to the oracle's on the GPU's own
+    logits up to fp32 near-ties (as the parity test checks)."""
+    rng = np.random.default_rng(9000 + case)
+    M = int(rng.choice([1, 2, 3, 7, 16, 17, 40]))
+    N = int(rng.integers(8, 1025))
+    k = int(rng.integers(1, min(N, 16) + 1))
+    K = 16 * int(rng.integers(1, 200))
+    say("random router", case, M, N, K, k)
+    r, ga, ac, as_, gw, wc, wsf = P.router_inputs(M, K, N, k, seed=9100 + case)
+    idx_g, sc_g, z = P.gpu_router(C, ac, as_, ga, wc, wsf, gw, r.bias, k)
+    zo = oracle.linear(ac, as_, ga, wc, wsf, gw)
+    assert np.max(np.abs(z - zo)) <= REL_TOL * np.max(np.abs(zo))
+    vmax = np.max(np.abs(oracle.router_scores(z))) + np.max(np.abs(r.bias))
+    P.check_choice(idx_g, sc_g, z, r.bias, k, eps=1e-6 * vmax)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_grouped_swiglu(C, case):
+    """nvfp4_grouped_linear_swiglu on random groups, granularities and
+    limits against the separate calls: h bit-identical, the same gsa_h, h's
+    codes and scales identical, rows outside the groups or with an invalid
+    row_index unwritten; h against the oracle's SwiGLU of the GPU's l1."""
+    rng = np.random.default_rng(10000 + case)
+    G, sizes = random_groups(rng)
+    gran = int(rng.choice([1, 2, 4, 8]))
+    N = 32 * int(rng.integers(1, 12))
+    K = 256 * int(rng.integers(1, 5))
+    start, tail = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+    offsets = (start + np.concatenate([[0], np.cumsum(sizes)])).astype(np.int32)
+    P_rows = int(offsets[-1]) + tail
+    a_rows = int(rng.integers(1, 30))
+    row_index = rng.integers(0, a_rows, max(P_rows, 1)).astype(np.int32)[:P_rows]
+    if P_rows:
+        row_index[int(rng.integers(0, P_rows))] = -1
+    say("random grouped swiglu", case, G, sizes, N, K, gran)
+    ac, asf = operands(rng, a_rows, K)
+    wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    wsf = rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8)
+    ws2 = rng.uniform(0.002, 0.01, G).astype(np.float32)
+    d = dict(ac=to_dev(ac), asf=to_dev(asf), gsa=to_dev(np.array([np.float32(0.37)])),
+             ri=to_dev(row_index), off=to_dev(offsets), wc=to_dev(wc), wsf=to_dev(wsf),
+             ws2=to_dev(ws2))
+    l1 = torch.zeros(P_rows, N, dtype=torch.float32, device=DEV)
+    C.nvfp4_grouped_linear(d["ac"], d["asf"], d["gsa"], d["ri"], d["off"], d["wc"], d["wsf"],
+                           d["ws2"], l1)
+    nz = l1[l1 != 0]
+    limit = float(torch.median(torch.abs(nz))) if (case % 2 and nz.numel()) else 0.0
+    h1 = torch.zeros(P_rows, N // 2, dtype=torch.float32, device=DEV)
+    g1 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    nws = C.nvfp4_workspace_bytes(C.OP_GROUPED_SWIGLU, P_rows, N, 0, G)
+    ws = torch.full((max(nws, 16),), 0xAB, dtype=torch.uint8, device=DEV)
+    hc1 = torch.full((P_rows, N // 4), 0x5A, dtype=torch.uint8, device=DEV)
+    hs1 = torch.full((P_rows, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
+    C.nvfp4_grouped_linear_swiglu(d["ac"], d["asf"], d["gsa"], d["ri"], d["off"], d["wc"],
+                                  d["wsf"], d["ws2"], h1, g1, gran, ws, h_codes=hc1,
+                                  h_scales=hs1, limit=limit)
+    h2 = torch.zeros(P_rows, N // 2, dtype=torch.float32, device=DEV)
+    g2 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    C.nvfp4_swiglu_deinterleave(l1, h2, gran, limit=limit)
+    C.nvfp4_amax_gsa(h2, g2, torch.empty(max(C.nvfp4_workspace_bytes(C.OP_AMAX_GSA,
+                                                                      P_rows * N // 2), 16),
+                                         dtype=torch.uint8, device=DEV))
+    hc2, hs2 = P.gpu_quantize(C, h2, g2)
+    torch.cuda.synchronize()
+    a, b = h1.cpu().numpy(), h2.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.float32(g1.cpu().numpy()[0]) == np.float32(g2.cpu().numpy()[0])
+    assert torch.equal(hc1, hc2) and torch.equal(hs1, hs2)
+    if P_rows:
+        href = oracle.swiglu_deinterleave(l1.cpu().numpy(), gran, limit)
+        assert np.max(np.abs(a - href)) <= 1e-6 * max(np.max(np.abs(href)), 1e-30)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_moe_run(C, case):
+    """nvfp4_moe_run on random token counts, expert counts, top-k, sizes and
+    routing: every step against the oracle on the GPU's own input to it,
+    every output bit-equal to the separate calls (as the parity test
+    checks)."""
+    rng = np.random.default_rng(11000 + case)
+    experts = int(rng.integers(2, 33))
+    topk = int(rng.integers(1, min(8, experts) + 1))
+    tokens = int(rng.choice([1, 2, 3, 5, 9, 17, 40, 80]))
+    K1 = 256 * int(rng.integers(1, 9))
+    N1 = 512 * int(rng.integers(1, 3))
+    N2 = int(rng.integers(1, 300))
+    routing = "zipf" if rng.integers(0, 2) else "uniform"
+    say("random moe run", case, tokens, experts, topk, K1, N1, N2, routing)
+    moe = W.make_moe(tokens=tokens, experts=experts, topk=topk, K1=K1, N1=N1, K2=N1 // 2,
+                     N2=N2, granularity=8, seed=11100 + case, routing=routing)
+    P.moe_run_matches_separate_calls(C, moe)
