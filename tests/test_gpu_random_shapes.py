@@ -349,3 +349,94 @@ def test_random_moe_run(C, case):
     moe = W.make_moe(tokens=tokens, experts=experts, topk=topk, K1=K1, N1=N1, K2=N1 // 2,
                      N2=N2, granularity=8, seed=11100 + case, routing=routing)
     P.moe_run_matches_separate_calls(C, moe)
+
+
+def rne_bf16(a: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_bf16_outputs_are_rounded_fp32(C, case):
+    """The bf16 output of nvfp4_linear, nvfp4_linear_rows and
+    nvfp4_grouped_linear on random shapes is the same call's fp32 output
+    rounded to nearest even, bit for bit (the output type changes the store
+    only); the per-row-gsa linear with every row's gsa equal matches the
+    one-gsa linear, and it is within 1e-3 of the oracle row by row."""
+    rng = np.random.default_rng(12000 + case)
+    M = int(rng.choice(M_CHOICES))
+    N = int(rng.integers(1, 400))
+    K = random_k(rng, 80)
+    say("random bf16 outputs", case, M, N, K)
+    ac, asf = operands(rng, M, K)
+    wc, wsf = operands(rng, N, K)
+    gsa_rows = rng.uniform(0.01, 1.0, M).astype(np.float32)
+    ws2 = np.float32(0.004)
+    nws = C.nvfp4_workspace_bytes(C.OP_LINEAR, M, N, K)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+    d = [to_dev(v) for v in (ac, asf)] + [to_dev(gsa_rows)] + [to_dev(v) for v in (wc, wsf)] + \
+        [to_dev(np.array([ws2]))]
+    outs = {}
+    for name, fn in [("rows", C.nvfp4_linear_rows), ("one", C.nvfp4_linear)]:
+        for dt in (torch.float32, torch.bfloat16):
+            y = torch.full((M, N), -7.0, dtype=dt, device=DEV)
+            args = list(d)
+            if name == "one":
+                args[2] = to_dev(np.full(1, gsa_rows[0], np.float32))
+            fn(*args, y, ws)
+            outs[name, dt] = y.float().cpu().numpy()
+        assert np.array_equal(rne_bf16(outs[name, torch.float32]), outs[name, torch.bfloat16])
+    ref = np.stack([oracle.linear(ac[m:m + 1], asf[m:m + 1], gsa_rows[m], wc, wsf, ws2)[0]
+                    for m in range(M)])
+    assert rel_err(outs["rows", torch.float32].astype(np.float64), ref) <= REL_TOL
+    # the first row's scale for every row: the one-gsa linear's result
+    args = list(d)
+    args[2] = to_dev(np.full(M, gsa_rows[0], np.float32))
+    y = torch.full((M, N), -7.0, dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_rows(*args, y, ws)
+    assert np.array_equal(y.cpu().numpy(), outs["one", torch.float32])
+    # grouped, bf16 against fp32 of the same call
+    G = int(rng.integers(1, 5))
+    cut = np.sort(rng.integers(0, M + 1, G - 1))
+    offsets = np.concatenate([[0], cut, [M]]).astype(np.int32)
+    wg = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    sg = rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8)
+    w2 = rng.uniform(0.002, 0.01, G).astype(np.float32)
+    g_out = {}
+    for dt in (torch.float32, torch.bfloat16):
+        y = torch.full((M, N), -7.0, dtype=dt, device=DEV)
+        C.nvfp4_grouped_linear(d[0], d[1], to_dev(np.array([np.float32(0.3)])), None,
+                               to_dev(offsets), to_dev(wg), to_dev(sg), to_dev(w2), y)
+        g_out[dt] = y.float().cpu().numpy()
+    assert np.array_equal(rne_bf16(g_out[torch.float32]), g_out[torch.bfloat16])
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_noalloc_matches_linear_run(C, case):
+    """nvfp4_linear_run_noalloc on random shapes that fit its static
+    scratch: gsa, codes, scales and y bit-equal to nvfp4_linear_run's."""
+    rng = np.random.default_rng(13000 + case)
+    M = int(rng.choice(M_CHOICES))
+    N = int(rng.integers(1, 1500))
+    K = random_k(rng, 128)
+    need = max(C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, N, K), 0)
+    if need > C.NOALLOC_SCRATCH_BYTES:
+        pytest.skip("larger than the static scratch")
+    say("random noalloc", case, M, N, K)
+    inp = W.make_linear(M, K, N, seed=13100 + case, x="outliers")
+    x = W.bf16_to_torch(inp.x, DEV)
+    wc, wsf = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    w2 = to_dev(np.array([inp.ws2], np.float32))
+    res = []
+    for noalloc in (False, True):
+        gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+        codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+        scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+        y = torch.full((M, N), -7.0, dtype=torch.float32, device=DEV)
+        if noalloc:
+            C.nvfp4_linear_run_noalloc(x, gsa, codes, scales, wc, wsf, w2, y)
+        else:
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+            C.nvfp4_linear_run(x, gsa, codes, scales, wc, wsf, w2, y, ws)
+        res.append([t.cpu().numpy() for t in (gsa, codes, scales, y)])
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
