@@ -440,3 +440,101 @@ def test_random_noalloc_matches_linear_run(C, case):
         res.append([t.cpu().numpy() for t in (gsa, codes, scales, y)])
     for a, b in zip(*res):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def _random_graph_step(C, kind, rng):
+    """(step, outputs) for one entry point on random sizes: step() enqueues
+    the call on the current stream, outputs() lists what it writes."""
+    if kind == "linear_run":
+        M = int(rng.choice([1, 3, 16, 17, 100]))
+        N, K = int(rng.integers(1, 600)), random_k(rng, 64)
+        inp = W.make_linear(M, K, N, seed=int(rng.integers(1 << 30)), x="outliers")
+        x = W.bf16_to_torch(inp.x, DEV)
+        wc, wsf = to_dev(inp.w_codes), to_dev(inp.w_scales)
+        w2 = to_dev(np.array([inp.ws2], np.float32))
+        gsa = torch.zeros(1, device=DEV)
+        codes = torch.zeros(M, K // 2, dtype=torch.uint8, device=DEV)
+        scales = torch.zeros(M, K // 16, dtype=torch.uint8, device=DEV)
+        y = torch.zeros(M, N, device=DEV)
+        ws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, N, K), 16),
+                         dtype=torch.uint8, device=DEV)
+        return (lambda: C.nvfp4_linear_run(x, gsa, codes, scales, wc, wsf, w2, y, ws),
+                lambda: [gsa, codes, scales, y])
+    if kind == "grouped_run":
+        G, sizes = random_groups(rng)
+        N, K = int(rng.integers(1, 300)), random_k(rng, 64)
+        x_rows = int(rng.integers(1, 20))
+        offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        P_rows = int(offsets[-1])
+        inp = W.make_linear(x_rows, K, 1, seed=int(rng.integers(1 << 30)))
+        x = W.bf16_to_torch(inp.x, DEV)
+        ri = to_dev(rng.integers(0, x_rows, max(P_rows, 1)).astype(np.int32))
+        off = to_dev(offsets)
+        wc = to_dev(rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8))
+        wsf = to_dev(rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8))
+        w2 = to_dev(rng.uniform(0.002, 0.01, G).astype(np.float32))
+        gsa = torch.zeros(1, device=DEV)
+        codes = torch.zeros(x_rows, K // 2, dtype=torch.uint8, device=DEV)
+        scales = torch.zeros(x_rows, K // 16, dtype=torch.uint8, device=DEV)
+        y = torch.zeros(max(P_rows, 1), N, device=DEV)
+        ws = torch.empty(max(C.nvfp4_workspace_bytes(C.OP_GROUPED_RUN, x_rows, N, K, G), 16),
+                         dtype=torch.uint8, device=DEV)
+        return (lambda: C.nvfp4_grouped_linear_run(x, gsa, codes, scales, ri[:P_rows], off, wc,
+                                                   wsf, w2, y[:P_rows], ws),
+                lambda: [gsa, codes, scales, y[:P_rows]])
+    if kind == "router":
+        M = int(rng.choice([1, 5, 16, 17, 40]))
+        N = int(rng.integers(8, 513))
+        k = int(rng.integers(1, min(N, 8) + 1))
+        K = 16 * int(rng.integers(1, 100))
+        r, ga, ac, as_, gw, wc, wsf = P.router_inputs(M, K, N, k, seed=int(rng.integers(1 << 30)))
+        idx = torch.zeros(M, k, dtype=torch.int32, device=DEV)
+        sc = torch.zeros(M, k, device=DEV)
+        ws = torch.zeros(max(C.nvfp4_workspace_bytes(C.OP_ROUTER_TOPK, M, N, K), 16),
+                         dtype=torch.uint8, device=DEV)  # the ticket counter starts at zero
+        args = (to_dev(ac), to_dev(as_), torch.tensor([ga], device=DEV), to_dev(wc), to_dev(wsf),
+                torch.tensor([gw], device=DEV), to_dev(r.bias), idx, sc, ws)
+        return (lambda: C.nvfp4_router_topk(*args), lambda: [idx, sc])
+    from moe_amax_gsa_amd.layer import Nvfp4MoE
+    tokens = int(rng.choice([1, 3, 40]))
+    experts = int(rng.integers(2, 17))
+    topk = int(rng.integers(1, min(4, experts) + 1))
+    moe = W.make_moe(tokens=tokens, experts=experts, topk=topk, K1=256 * int(rng.integers(1, 4)),
+                     N1=512, K2=256, N2=int(rng.integers(1, 200)), granularity=8,
+                     seed=int(rng.integers(1 << 30)))
+    Pn = int(moe.offsets[-1])
+    layer = Nvfp4MoE(*W.moe_weights_to(moe, DEV), max_pairs=Pn, max_tokens=moe.T)
+    x = W.bf16_to_torch(moe.x, DEV)
+    ri, off = to_dev(moe.pair_token), to_dev(moe.offsets)
+    return (lambda: layer(x, ri, off),
+            lambda: [layer.y2[:Pn], layer.h[:Pn], layer.gsa1, layer.gsa2])
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_graph_replays(C, case):
+    """A random entry point on random sizes captured in a HIP graph and
+    replayed three times, its outputs overwritten and eager work in
+    between: every replay equal to the eager call bit for bit."""
+    rng = np.random.default_rng(14000 + case)
+    kind = ["linear_run", "grouped_run", "router", "moe_run"][case % 4]
+    say("random graph replay", case, kind)
+    step, outs = _random_graph_step(C, kind, rng)
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for t in outs():
+            t.fill_(float("nan") if t.dtype.is_floating_point else 0x5A)
+        _ = torch.randn(1000, device=DEV).sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), eager):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
