@@ -538,3 +538,52 @@ def test_random_graph_replays(C, case):
         torch.cuda.synchronize()
         for a, b in zip(outs(), eager):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_quantize_weight_and_amax(C, case):
+    """nvfp4_quantize_weight on a random bf16 weight (N, K): weight_scale_2,
+    codes and scales bit-exact with the oracle's amax, gsa and quantize; and
+    nvfp4_amax_gsa on a random-length tensor equal to the oracle's gsa."""
+    rng = np.random.default_rng(15000 + case)
+    N = int(rng.integers(1, 3000))
+    K = 16 * int(rng.integers(1, 700))
+    say("random quantize weight", case, N, K)
+    w = W.to_bf16_bits(rng.standard_normal((N, K)) * rng.uniform(0.001, 1.0))
+    ws2 = torch.zeros(1, device=DEV)
+    codes = torch.full((N, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((N, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    nws = C.nvfp4_workspace_bytes(C.OP_QUANTIZE_WEIGHT, 0, N, K)
+    ws = torch.full((max(nws, 16),), 0xAB, dtype=torch.uint8, device=DEV)
+    C.nvfp4_quantize_weight(W.bf16_to_torch(w, DEV), ws2, codes, scales, ws)
+    g = oracle.amax_gsa(w)
+    assert np.float32(ws2.cpu().numpy()[0]) == g
+    oc, os_ = oracle.quantize(w, g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    n = int(rng.integers(1, 3_000_000))
+    x = rng.standard_normal(n).astype(np.float32) * np.float32(rng.uniform(0.1, 100.0))
+    x[int(rng.integers(0, n))] = -np.float32(rng.uniform(100.0, 1e4))
+    gsa = torch.zeros(1, device=DEV)
+    nws = C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, n)
+    C.nvfp4_amax_gsa(to_dev(x), gsa, torch.full((max(nws, 16),), 0xAB, dtype=torch.uint8,
+                                                device=DEV))
+    assert np.float32(gsa.cpu().numpy()[0]) == oracle.amax_gsa(x.reshape(1, -1)[:, :n])
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_swiglu_deinterleave(C, case):
+    """nvfp4_swiglu_deinterleave on random (M, N) and granularity, with and
+    without a limit: within 1e-6 of the oracle's binary64 SwiGLU."""
+    rng = np.random.default_rng(16000 + case)
+    gran = int(rng.choice([1, 2, 4, 8, 16]))
+    M = int(rng.integers(0, 400))
+    N = 2 * gran * int(rng.integers(1, 200))
+    limit = float(rng.choice([0.0, 0.5, 3.0]))
+    say("random swiglu", case, M, N, gran, limit)
+    l1 = (rng.standard_normal((M, N)) * 3.0).astype(np.float32)
+    h = torch.full((M, N // 2), -7.0, device=DEV)
+    C.nvfp4_swiglu_deinterleave(to_dev(l1), h, gran, limit=limit)
+    if M:
+        ref = oracle.swiglu_deinterleave(l1, gran, limit)
+        hh = h.cpu().numpy()
+        assert np.max(np.abs(hh - ref)) <= 1e-6 * max(np.max(np.abs(ref)), 1e-30)
