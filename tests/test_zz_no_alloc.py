@@ -66,13 +66,17 @@ def one_call(C, M, K, N, seed, y_dtype):
 #  - 512 x 7168 -> 1024 uses the amax partials; then one decode row, which
 #    needs no scratch at all;
 #  - 64 x 7168 -> 384 (the router gate's shape, split 14 ways), then
-#    17 x 1024 -> 96 just past the weight-streaming kernel's row limit.
+#    17 x 1024 -> 96 just past the weight-streaming kernel's row limit;
+#  - 2048 x 7168 -> 7168 (224 tiles of 256 x 256, the amax partials of a
+#    14.7 M-element activation), then 128 x 7168 -> 2048 (split K).
 CASES = [((128, 7168, 2048), (40, 2048, 384)),
          ((512, 7168, 1024), (1, 7168, 1536)),
-         ((64, 7168, 384), (17, 1024, 96))]
+         ((64, 7168, 384), (17, 1024, 96)),
+         ((2048, 7168, 7168), (128, 7168, 2048))]
 
 
-@pytest.mark.parametrize("first,second", CASES, ids=["split", "amax_then_decode", "router"])
+@pytest.mark.parametrize("first,second", CASES,
+                         ids=["split", "amax_then_decode", "router", "wide_then_split"])
 def test_noalloc_matches_linear_run(C, first, second):
     for i, (M, K, N) in enumerate((first, second)):
         y_dtype = torch.float32 if i == 0 else torch.bfloat16
