@@ -35,7 +35,9 @@ the kernel sources still hash to the value recorded there.
 cpu_baseline: the oracle's step on every host core and on one, each for a
 bounded time, with the CPU model.
 
-    python bench.py --pmc-probe     (the program those counter runs profile)
+    python bench.py --pmc-probe     (the program those counter runs profile;
+                                     --pmc-probe-prefill, --pmc-probe-stress for
+                                     the GEMM workloads)
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -74,6 +76,9 @@ def parse():
     p.add_argument("--pmc-probe-prefill", action="store_true",
                    help="run only a 256 MiB copy, then the prefill quantize and linear "
                         "(for counter runs)")
+    p.add_argument("--pmc-probe-stress", action="store_true",
+                   help="run only a 256 MiB copy, then the stress quantize and linear, then "
+                        "torch's bf16 matmul of the same shape (for counter runs)")
     return p.parse_args()
 
 
@@ -609,11 +614,12 @@ def pmc_probe(C, dev, launches=20):
                       "source_hash": kernel_source_hash()}))
 
 
-def pmc_probe_prefill(C, dev, launches=10):
+def pmc_probe_prefill(C, dev, launches=10, name="prefill_m512_k7168_n4096", matmul=False):
     """A 256 MiB device copy (three times), then `launches` rounds of the
-    prefill workload's amax + quantize and its linear, on rotated weights."""
+    workload's amax + quantize and its linear, on rotated weights; with
+    matmul, then `launches` of torch's bf16 matmul of the same shape (its
+    counters as context)."""
     from moe_amax_gsa_amd import workloads as W
-    name = "prefill_m512_k7168_n4096"
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -625,9 +631,18 @@ def pmc_probe_prefill(C, dev, launches=10):
         b.quantize(i)
         b.linear(i)
     torch.cuda.synchronize()
+    if matmul:
+        inp = b.inp
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        a = torch.randn(inp.M, inp.K, generator=g, device=dev).to(torch.bfloat16)
+        bt = torch.randn(inp.K, inp.N, generator=g, device=dev).to(torch.bfloat16)
+        for _ in range(launches):
+            torch.matmul(a, bt)
+        torch.cuda.synchronize()
     print(json.dumps({"pmc_probe": name, "copy_bytes": src.numel(), "copies": 3,
                       "launches": launches, "quant_bytes": b.quant_bytes, "flops": b.flops,
-                      "source_hash": kernel_source_hash()}))
+                      "torch_bf16_matmul": matmul, "source_hash": kernel_source_hash()}))
 
 
 def torch_bf16_matmul_us(M, N, K, dev, iters=20):
@@ -664,6 +679,9 @@ def main():
         return
     if args.pmc_probe_prefill:
         pmc_probe_prefill(C, dev)
+        return
+    if args.pmc_probe_stress:
+        pmc_probe_prefill(C, dev, name="stress_m2048_k7168_n7168", matmul=True)
         return
     kiters = 50
 
