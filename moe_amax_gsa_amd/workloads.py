@@ -110,6 +110,20 @@ def draw_activation(rng: np.random.Generator, M: int, K: int, kind: str) -> np.n
         n_zero = int(round(0.01 * nblk))
         idx = rng.choice(nblk, n_zero, replace=False)
         x.reshape(-1, 16)[idx] = 0.0
+    # the edges of the formats' ranges
+    elif kind == "tiny":
+        # bf16 subnormals (|x| < 2^-126): the amax floor sets gsa
+        x *= 1e-39
+    elif kind == "huge":
+        x *= 1e30
+    elif kind == "block_range":
+        # each 16-element block its own magnitude, log-uniform over the
+        # eight decades below 1 (zero, subnormal and normal E4M3 scales)
+        mag = 10.0 ** rng.uniform(-8.0, 0.0, size=(M, K // 16))
+        x *= np.repeat(mag, 16, axis=1)
+    elif kind == "elem_range":
+        # each element its own magnitude, log-uniform over 1e-20 .. 1e20
+        x *= 10.0 ** rng.uniform(-20.0, 20.0, size=(M, K))
     else:
         raise ValueError(kind)
     return x

@@ -134,6 +134,70 @@ def test_quantize_bitexact(C, M, K, dist, dtype):
     assert np.array_equal(codes.cpu().numpy(), oc)
 
 
+EXTREME = ["tiny", "huge", "block_range", "elem_range"]
+
+
+@pytest.mark.parametrize("kind", EXTREME)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("M,K", [(3, 512), (40, 2048)])
+def test_quantize_extreme_magnitudes_bitexact(C, M, K, dtype, kind):
+    """Activations at the edges of the formats' ranges (bf16 subnormals under
+    the gsa floor, values near 1e30, blocks spread over eight decades so
+    that zero, subnormal and normal E4M3 scales sit side by side, elements
+    spread over forty decades): gsa, codes and scales bit-exact with the
+    oracle through nvfp4_amax_gsa + nvfp4_quantize_from_buffer and through
+    nvfp4_amax_quantize (one workgroup at 3 x 512, two phases at 40 x 2048)."""
+    say("quantize extreme", M, K, dtype, kind)
+    rng = np.random.default_rng(M * 11 + K + len(kind))
+    bits = W.to_bf16_bits(W.draw_activation(rng, M, K, kind))
+    xd = x_dev(bits, dtype)
+    want = oracle.amax_gsa(x_host(bits, dtype))
+    oc, os_ = oracle.quantize(x_host(bits, dtype), want)
+    g = gpu_gsa(C, xd)
+    assert f32(g) == want
+    codes, scales = gpu_quantize(C, xd, g)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    g2 = torch.zeros(1, dtype=torch.float32, device=DEV)
+    c2 = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    s2 = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, 0, K))
+    C.nvfp4_amax_quantize(xd, g2, c2, s2, torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV))
+    assert f32(g2) == want
+    assert np.array_equal(s2.cpu().numpy(), os_) and np.array_equal(c2.cpu().numpy(), oc)
+
+
+@pytest.mark.parametrize("kind", EXTREME)
+@pytest.mark.parametrize("M,K,N", [(1, 7168, 256), (3, 1024, 96), (64, 1024, 256)])
+def test_linear_run_extreme_magnitudes(C, M, K, N, kind):
+    """nvfp4_linear_run (the one-row kernel quantizing in LDS, the few-row
+    kernel, the amax + quantize + tiled linear) on those activations: gsa,
+    codes and scales bit-exact with the oracle, y within 1e-3 of the
+    oracle's (all zero where every activation scale rounds to zero)."""
+    say("linear run extreme", M, K, N, kind)
+    inp = W.make_linear(M, K, N, seed=500 + M + len(kind), x=kind)
+    x = W.bf16_to_torch(inp.x, DEV)
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, N, K))
+    ws = torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV)
+    C.nvfp4_linear_run(x, gsa, codes, scales, to_dev(inp.w_codes), to_dev(inp.w_scales),
+                       torch.tensor([inp.ws2], dtype=torch.float32, device=DEV), y, ws)
+    g = f32(gsa)
+    assert g == oracle.amax_gsa(inp.x)
+    oc, os_ = oracle.quantize(inp.x, g)
+    assert np.array_equal(scales.cpu().numpy(), os_) and np.array_equal(codes.cpu().numpy(), oc)
+    ref = oracle.linear(oc, os_, g, inp.w_codes, inp.w_scales, inp.ws2)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(yg))
+    if not np.any(ref):
+        assert not np.any(yg)
+    else:
+        assert rel_err(yg, ref) <= REL_TOL
+
+
 @pytest.mark.parametrize("M,K,dtype", [(18003, 7504, "bf16"), (18003, 7504, "fp32")])
 def test_quantize_large_tensor_rows(C, M, K, dtype):
     """Tensors of more than 2^24 half-blocks (the quantize then gives each
@@ -1657,6 +1721,29 @@ def test_grouped_linear_run(C, T, G, K, N, dtype):
                                 gi.ws2, T * G)
     assert not np.any(np.isnan(y))
     assert rel_err(y, ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("kind", EXTREME)
+@pytest.mark.parametrize("T,G,K,N", [(1, 8, 1024, 96), (1, 8, 8192, 64), (64, 8, 512, 96)])
+def test_grouped_linear_run_extreme_magnitudes(C, T, G, K, N, kind):
+    """The grouped run's three paths (every workgroup reducing and
+    quantizing x itself; amax partials, then the ring quantizing its rows;
+    quantize, then the tiled kernel) on activations at the edges of the
+    formats' ranges: gsa, codes and scales bit-exact, outputs within 1e-3
+    of the oracle's (all zero where every activation scale is zero)."""
+    say("grouped run extreme", T, G, K, N, kind)
+    gi = W.make_grouped(T, G, K, N, seed=T + G + K + N + len(kind), x=kind)
+    g, codes, scales, y = run_grouped(C, gi, "bf16")
+    assert g == oracle.amax_gsa(gi.x)
+    oc, os_ = oracle.quantize(gi.x, g)
+    assert np.array_equal(codes, oc) and np.array_equal(scales, os_)
+    ref = oracle.grouped_linear(oc, os_, g, gi.row_index, gi.offsets, gi.w_codes, gi.w_scales,
+                                gi.ws2, T * G)
+    assert np.all(np.isfinite(y))
+    if not np.any(ref):
+        assert not np.any(y)
+    else:
+        assert rel_err(y, ref) <= REL_TOL
 
 
 def test_grouped_linear_run_routed_token(C):
