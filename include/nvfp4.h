@@ -166,7 +166,10 @@ int nvfp4_amax_quantize(const void *x, int x_dtype, int64_t M, int64_t K, float 
  *   - gsa_per_row != 0: gsa (M,), gsa[m] from row m alone (then ws is not
  *     used); nvfp4_linear_rows takes such a gsa.
  * x and norm_weight bf16 or fp32, 16-byte aligned; K % 16 == 0; eps > 0
- * and finite (so a row of zeros normalizes to zeros, not 0 * inf).
+ * and finite (so a row of zeros normalizes to zeros, not 0 * inf).  The
+ * mean of squares is a float32 sum, as a float32 RMSNorm forms it: a row
+ * whose squares overflow float32 (|x| beyond about 1.8e19 / sqrt(K)) gets
+ * inv_rms 0 and normalizes to zeros.
  * M == 0 writes gsa[0] = 1e-8 / 2688 (one scale) or nothing (per row). */
 int nvfp4_rmsnorm_quantize(const void *x, int x_dtype, const void *norm_weight, int w_dtype,
                            float eps, int64_t M, int64_t K, int gsa_per_row, float *gsa,
