@@ -30,6 +30,13 @@ constexpr int SMALL_THREADS = 1024;
 // 1.85 GB and at 29 MB).
 constexpr int64_t STREAM_BYTES = 256ll << 20;
 constexpr int64_t QUANTIZE_WIDE_HALVES = 1ll << 24;  // 256 MiB of bf16
+// From 2^21 half-blocks (32 MiB of bf16) the quantize that reduces the
+// amax partials itself also takes four half-blocks a thread (measured on
+// MI355X, amax + quantize of (M, 7168) bf16, alternating builds: M = 4096
+// 32-34 against 31-37 us, M = 8192 49-57 against 59-64 us, M = 12288 68-73
+// against 82-96 us; at M = 2048 one a thread is faster, 17-19 against
+// 21-22 us).
+constexpr int64_t QUANTIZE_INLINE_WIDE_HALVES = 1ll << 21;
 // at most this many amax partials are reduced inside every quantize workgroup
 constexpr int QUANTIZE_INLINE_PARTS = 512;
 
@@ -221,6 +228,31 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
   return hipGetLastError();
 }
 
+// The quantize that reduces nparts amax partials itself (and writes gsa):
+// one half-block a thread, four from QUANTIZE_INLINE_WIDE_HALVES on.
+static hipError_t launch_quantize_parts(const void* x, bool bf16, int64_t nhalf,
+                                        const uint32_t* partials, int nparts, float* gsa,
+                                        uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (nhalf >= QUANTIZE_INLINE_WIDE_HALVES) {
+    const unsigned grid = (unsigned)((nhalf + 1023) / 1024);
+    if (bf16)
+      quantize_kernel<true, true, 4><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales, partials,
+                                                          nparts);
+    else
+      quantize_kernel<false, true, 4><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
+                                                           partials, nparts);
+  } else {
+    const unsigned grid = (unsigned)((nhalf + 255) / 256);
+    if (bf16)
+      quantize_kernel<true, true><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales, partials,
+                                                       nparts);
+    else
+      quantize_kernel<false, true><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales, partials,
+                                                        nparts);
+  }
+  return hipGetLastError();
+}
+
 // Steps 1 and 2 on a tensor past the one-workgroup size: at most
 // QUANTIZE_INLINE_PARTS amax partials (each amax workgroup takes a larger
 // slice past that size), which every quantize workgroup reduces itself (two
@@ -237,17 +269,13 @@ hipError_t launch_amax_then_quantize(const void* x, bool bf16, int64_t M, int64_
     return launch_quantize(x, bf16, M, K, gsa, codes, scales, s);
   }
   uint32_t* partials = (uint32_t*)ws;
-  const int64_t grid = (nhalf + 255) / 256;
-  if (bf16) {
+  if (bf16)
     amax_partial_kernel<true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
-    quantize_kernel<true, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
-                                                               partials, parts);
-  } else {
+  else
     amax_partial_kernel<false><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
-    quantize_kernel<false, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
-                                                                partials, parts);
-  }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_quantize_parts(x, bf16, nhalf, partials, parts, gsa, codes, scales, s);
 }
 
 hipError_t launch_quantize_finalize(const float* x, int64_t M, int64_t K,
@@ -255,10 +283,7 @@ hipError_t launch_quantize_finalize(const float* x, int64_t M, int64_t K,
                                     uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const int64_t nhalf = M * (K / 8);
   if (nhalf == 0) return launch_amax_finalize(partials, nparts, gsa, s);
-  const int64_t grid = (nhalf + 255) / 256;
-  quantize_kernel<false, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
-                                                              partials, (int)nparts);
-  return hipGetLastError();
+  return launch_quantize_parts(x, false, nhalf, partials, (int)nparts, gsa, codes, scales, s);
 }
 
 // ---------------------------------------------------------------- small

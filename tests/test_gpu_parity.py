@@ -134,6 +134,31 @@ def test_quantize_bitexact(C, M, K, dist, dtype):
     assert np.array_equal(codes.cpu().numpy(), oc)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_amax_quantize_inline_partials_four_halves(C, dtype):
+    """nvfp4_amax_quantize past 2^21 half-blocks (2341 x 7184: the amax
+    partials, then the quantize that reduces them itself with four
+    half-blocks a thread, its last workgroup ragged): gsa, codes and scales
+    of the whole tensor bit-exact with the oracle."""
+    M, K = 2341, 7184
+    assert M * K // 8 >= 1 << 21 and (M * K // 8) % 1024 != 0
+    say("amax quantize four halves", M, K, dtype)
+    rng = np.random.default_rng(2341)
+    bits = W.to_bf16_bits(W.draw_activation(rng, M, K, "outliers"))
+    xd = x_dev(bits, dtype)
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    nws = max(16, C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, 0, K))
+    C.nvfp4_amax_quantize(xd, gsa, codes, scales,
+                          torch.full((nws,), 0xAB, dtype=torch.uint8, device=DEV))
+    g = oracle.amax_gsa(x_host(bits, dtype))
+    assert f32(gsa) == g
+    oc, os_ = oracle.quantize(x_host(bits, dtype), g)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
 EXTREME = ["tiny", "huge", "block_range", "elem_range"]
 
 
