@@ -104,6 +104,57 @@ def test_noalloc_matches_linear_run(C, first, second):
         assert np.max(np.abs(got - ref)) / np.max(np.abs(ref)) <= tol
 
 
+def test_noalloc_graph_replays(C):
+    """Three calls captured in one HIP graph on one stream, sharing the
+    static scratch: 512 x 7168 -> 1024 (amax partials, tiled linear), one
+    decode row 1 x 7168 -> 1536 (one kernel) and 128 x 7168 -> 2048 (split K,
+    its partials in the scratch).  Replayed three times with the outputs
+    overwritten and eager work in between: every replay equal to the eager
+    calls bit for bit."""
+    say("noalloc graph replays")
+    calls = []
+    for i, (M, K, N) in enumerate([(512, 7168, 1024), (1, 7168, 1536), (128, 7168, 2048)]):
+        inp = W.make_linear(M, K, N, 900 + i, "outliers", (0.25, 4.0), 0.005)
+        t = dict(x=W.bf16_to_torch(inp.x, DEV),
+                 gsa=torch.zeros(1, dtype=torch.float32, device=DEV),
+                 codes=torch.empty(M, K // 2, dtype=torch.uint8, device=DEV),
+                 scales=torch.empty(M, K // 16, dtype=torch.uint8, device=DEV),
+                 wc=torch.from_numpy(inp.w_codes).to(DEV),
+                 wsf=torch.from_numpy(inp.w_scales).to(DEV),
+                 ws2=torch.tensor([inp.ws2], dtype=torch.float32, device=DEV),
+                 y=torch.empty(M, N, dtype=torch.bfloat16 if i == 1 else torch.float32,
+                               device=DEV))
+        calls.append(t)
+
+    def step():
+        for t in calls:
+            C.nvfp4_linear_run_noalloc(t["x"], t["gsa"], t["codes"], t["scales"], t["wc"],
+                                       t["wsf"], t["ws2"], t["y"])
+
+    def outs():
+        return [t[k] for t in calls for k in ("gsa", "codes", "scales", "y")]
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for o in outs():
+            o.fill_(float("nan") if o.dtype.is_floating_point else 0x5A)
+        _ = torch.randn(1000, device=DEV).sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), eager):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 def test_noalloc_rejects_bad_arguments_before_touching_the_device(C):
     L = C.lib
     fake = ctypes.c_void_p(4096)  # never dereferenced
