@@ -71,9 +71,10 @@ hipError_t launch_router_topk(const float* src, int nsrc, const float* gsa, cons
                               float* logits, const float* bias, int64_t M, int64_t N, int k,
                               int32_t* idx, float* score, hipStream_t s);
 
-// Phase 2 of an amax over partials fused into the quantize of fp32 x (M, K):
-// every workgroup reduces the partials itself (keep nparts small), workgroup
-// 0 writes gsa.
+// Phase 2 of an amax over partials, then the quantize of fp32 x (M, K):
+// below 2^20 half-blocks fused (every quantize workgroup reduces the
+// partials itself, workgroup 0 writes gsa), from there a finalize launch
+// and the quantize.
 hipError_t launch_quantize_finalize(const float* x, int64_t M, int64_t K,
                                     const uint32_t* partials, int64_t nparts, float* gsa,
                                     uint8_t* codes, uint8_t* scales, hipStream_t s);

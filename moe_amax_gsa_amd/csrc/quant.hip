@@ -30,13 +30,14 @@ constexpr int SMALL_THREADS = 1024;
 // 1.85 GB and at 29 MB).
 constexpr int64_t STREAM_BYTES = 256ll << 20;
 constexpr int64_t QUANTIZE_WIDE_HALVES = 1ll << 24;  // 256 MiB of bf16
-// From 2^21 half-blocks (32 MiB of bf16) the quantize that reduces the
-// amax partials itself also takes four half-blocks a thread (measured on
-// MI355X, amax + quantize of (M, 7168) bf16, alternating builds: M = 4096
-// 32-34 against 31-37 us, M = 8192 49-57 against 59-64 us, M = 12288 68-73
-// against 82-96 us; at M = 2048 one a thread is faster, 17-19 against
-// 21-22 us).
-constexpr int64_t QUANTIZE_INLINE_WIDE_HALVES = 1ll << 21;
+// From 2^20 half-blocks (16 MiB of bf16) the amax partials take their own
+// finalize launch and the quantize reads gsa; below, every quantize
+// workgroup reduces the partials itself, one launch fewer.  Measured on
+// MI355X, amax + quantize of (M, 7168) bf16, partials reduced in the
+// quantize against a finalize launch: M = 512 8.5 against 9.5 us, 1024
+// 12.0 / 12.3, 1536 13.9 / 13.7, 2048 18.6 / 17.8, 3072 26.8 / 24.5 (four
+// half-blocks a thread in the quantize), 8192 50.6 / 50.6.
+constexpr int64_t QUANTIZE_INLINE_MAX_HALVES = 1ll << 20;
 // at most this many amax partials are reduced inside every quantize workgroup
 constexpr int QUANTIZE_INLINE_PARTS = 512;
 
@@ -228,54 +229,33 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t M, int64_t K, const
   return hipGetLastError();
 }
 
-// The quantize that reduces nparts amax partials itself (and writes gsa):
-// one half-block a thread, four from QUANTIZE_INLINE_WIDE_HALVES on.
-static hipError_t launch_quantize_parts(const void* x, bool bf16, int64_t nhalf,
-                                        const uint32_t* partials, int nparts, float* gsa,
-                                        uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  if (nhalf >= QUANTIZE_INLINE_WIDE_HALVES) {
-    const unsigned grid = (unsigned)((nhalf + 1023) / 1024);
-    if (bf16)
-      quantize_kernel<true, true, 4><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales, partials,
-                                                          nparts);
-    else
-      quantize_kernel<false, true, 4><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
-                                                           partials, nparts);
-  } else {
-    const unsigned grid = (unsigned)((nhalf + 255) / 256);
-    if (bf16)
-      quantize_kernel<true, true><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales, partials,
-                                                       nparts);
-    else
-      quantize_kernel<false, true><<<grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales, partials,
-                                                        nparts);
-  }
-  return hipGetLastError();
-}
-
-// Steps 1 and 2 on a tensor past the one-workgroup size: at most
-// QUANTIZE_INLINE_PARTS amax partials (each amax workgroup takes a larger
-// slice past that size), which every quantize workgroup reduces itself (two
-// launches instead of three); tensors of 256 MiB or more take the separate
-// finalize and the wide quantize.
+// Steps 1 and 2 on a tensor past the one-workgroup size.  Below
+// QUANTIZE_INLINE_MAX_HALVES half-blocks: at most QUANTIZE_INLINE_PARTS amax
+// partials (each amax workgroup takes a larger slice past that size), which
+// every quantize workgroup reduces itself (two launches instead of three);
+// from there on the separate finalize, and from 256 MiB the wide quantize.
 hipError_t launch_amax_then_quantize(const void* x, bool bf16, int64_t M, int64_t K, float* gsa,
                                      uint8_t* codes, uint8_t* scales, void* ws, hipStream_t s) {
   const int64_t numel = M * K, nhalf = M * (K / 8);
   const int parts = amax_parts_for(numel) < QUANTIZE_INLINE_PARTS ? amax_parts_for(numel)
                                                                    : QUANTIZE_INLINE_PARTS;
-  if (numel <= AMAX_SMALL_NUMEL || nhalf >= QUANTIZE_WIDE_HALVES) {
+  if (numel <= AMAX_SMALL_NUMEL || nhalf >= QUANTIZE_INLINE_MAX_HALVES) {
     const hipError_t e = launch_amax_gsa(x, bf16, numel, gsa, ws, s);
     if (e != hipSuccess) return e;
     return launch_quantize(x, bf16, M, K, gsa, codes, scales, s);
   }
   uint32_t* partials = (uint32_t*)ws;
-  if (bf16)
+  const int64_t grid = (nhalf + 255) / 256;
+  if (bf16) {
     amax_partial_kernel<true><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
-  else
+    quantize_kernel<true, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
+                                                               partials, parts);
+  } else {
     amax_partial_kernel<false><<<parts, AMAX_THREADS, 0, s>>>(x, numel, partials);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_quantize_parts(x, bf16, nhalf, partials, parts, gsa, codes, scales, s);
+    quantize_kernel<false, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
+                                                                partials, parts);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_finalize(const float* x, int64_t M, int64_t K,
@@ -283,7 +263,15 @@ hipError_t launch_quantize_finalize(const float* x, int64_t M, int64_t K,
                                     uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const int64_t nhalf = M * (K / 8);
   if (nhalf == 0) return launch_amax_finalize(partials, nparts, gsa, s);
-  return launch_quantize_parts(x, false, nhalf, partials, (int)nparts, gsa, codes, scales, s);
+  if (nhalf >= QUANTIZE_INLINE_MAX_HALVES) {  // the finalize launch, then the quantize
+    const hipError_t e = launch_amax_finalize(partials, nparts, gsa, s);
+    if (e != hipSuccess) return e;
+    return launch_quantize(x, false, M, K, gsa, codes, scales, s);
+  }
+  const int64_t grid = (nhalf + 255) / 256;
+  quantize_kernel<false, true><<<(unsigned)grid, 256, 0, s>>>(x, nhalf, gsa, codes, scales,
+                                                              partials, (int)nparts);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- small

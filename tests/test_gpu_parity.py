@@ -135,14 +135,14 @@ def test_quantize_bitexact(C, M, K, dist, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_amax_quantize_inline_partials_four_halves(C, dtype):
-    """nvfp4_amax_quantize past 2^21 half-blocks (2341 x 7184: the amax
-    partials, then the quantize that reduces them itself with four
-    half-blocks a thread, its last workgroup ragged): gsa, codes and scales
-    of the whole tensor bit-exact with the oracle."""
+def test_amax_quantize_past_inline_limit(C, dtype):
+    """nvfp4_amax_quantize well past 2^20 half-blocks (2341 x 7184: the amax
+    partials, a finalize launch, then the quantize reading gsa, its last
+    workgroup ragged): gsa, codes and scales of the whole tensor bit-exact
+    with the oracle."""
     M, K = 2341, 7184
-    assert M * K // 8 >= 1 << 21 and (M * K // 8) % 1024 != 0
-    say("amax quantize four halves", M, K, dtype)
+    assert M * K // 8 >= 1 << 21 and (M * K // 8) % 256 != 0
+    say("amax quantize past the inline limit", M, K, dtype)
     rng = np.random.default_rng(2341)
     bits = W.to_bf16_bits(W.draw_activation(rng, M, K, "outliers"))
     xd = x_dev(bits, dtype)
@@ -265,7 +265,8 @@ AMAXQ_CASES = [
     (16, 4096, "bf16"),                       # one workgroup, 1 .. 8 half-blocks a thread
     (17, 4096, "bf16"), (512, 7168, "fp32"),  # two-phase amax, the quantize reducing the
     (512, 7168, "bf16"), (499, 7184, "bf16"),  # partials itself (9 to 448 of them)
-    (600, 7168, "bf16"), (1000, 7168, "fp32"),  # more than 512 partials: a separate finalize
+    (600, 7168, "bf16"), (1000, 7168, "fp32"),  # 512 partials, each a larger slice
+    (1200, 7168, "fp32"),                      # 2^20 half-blocks and more: a finalize launch
 ]
 
 
@@ -1604,6 +1605,13 @@ def test_grouped_swiglu_large_groups_match_unfused(C, K, N, gran, lim):
     entry point takes (gate and up columns 1 to 8 apart).  N = 384: a
     partial last column tile."""
     grouped_swiglu_fused_matches_unfused(C, [130, 0, 128, 255, 97, 301], K, N, gran, lim)
+
+
+def test_grouped_swiglu_large_h_finalize_launch(C):
+    """An h of 2^20 half-blocks and more (16 groups of 260 rows, N = 4096):
+    its amax partials go through a finalize launch before the quantize;
+    the same checks as the other fused SwiGLU cases."""
+    grouped_swiglu_fused_matches_unfused(C, [260] * 16, 256, 4096, 8, "off")
 
 
 def grouped_swiglu_fused_matches_unfused(C, sizes, K, N, gran, lim):
