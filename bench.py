@@ -668,8 +668,8 @@ def torch_bf16_matmul_us(M, N, K, dev, iters=20):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU (got --gpus {args.gpus}): the layer is not sharded "
-              "across GPUs in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU (got --gpus {args.gpus}): the layer runs on one GPU "
+              "and is not sharded across several", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench needs a GPU"
     from moe_amax_gsa_amd import nvfp4 as C
