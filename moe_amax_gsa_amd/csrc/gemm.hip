@@ -914,13 +914,17 @@ int device_cu_count() {
 }
 
 // Split-K plan for the staged kernel: with few output tiles (at most half a
-// tile per CU) the K range is cut into up to 16 splits so that the grid
-// covers the chip.  Returns the split count (1: none).
+// tile per CU) the K range is cut into up to 16 splits, about one
+// workgroup per CU.  (Measured on MI355X at K = 7168, M = 64 to 128: about
+// two workgroups per CU took 10-21% longer from 24 tiles up, 64 x 1536
+// 13.9 against 16.1 us, 128 x 2048 17.5 against 22.1 us, 128 x 4096 21.6
+// against 24.3 us, and the same at 6 tiles, where both take 16.)  Returns
+// the split count (1: none).
 static int gemm_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((N + 63) / 64) * ((M + 127) / 128);
   const int64_t nch = K / 256;
   if (2 * tiles > device_cu_count() || nch < 2) return 1;
-  int64_t sp = (2 * device_cu_count()) / tiles;
+  int64_t sp = device_cu_count() / tiles;
   sp = sp < GEMM_MAX_SPLITS ? sp : GEMM_MAX_SPLITS;
   sp = sp < nch ? sp : nch;
   const int64_t cps = (nch + sp - 1) / sp;

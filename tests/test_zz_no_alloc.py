@@ -61,7 +61,7 @@ def one_call(C, M, K, N, seed, y_dtype):
 
 
 # Two calls in a row per case, the second smaller:
-#  - 128 x 7168 -> 2048 splits K 14 ways, its partials filling 14.7 MB of
+#  - 128 x 7168 -> 2048 splits K 7 ways, its partials filling 7.3 MB of
 #    the scratch; then 40 x 2048 -> 384, also split, on what that left;
 #  - 512 x 7168 -> 1024 uses the amax partials; then one decode row, which
 #    needs no scratch at all;
