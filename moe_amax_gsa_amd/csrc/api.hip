@@ -321,10 +321,11 @@ NVFP4_API int nvfp4_linear_run(const void* x, int x_dtype, float* gsa, uint8_t* 
                                        0, 0.f, nullptr, nullptr, s));
   // other decode shapes: one kernel, 8 weight rows per workgroup (4 when N
   // is small), every workgroup quantizes the activation itself
-  if (N > 0 && gemv_narrow_run_supported(M, K, x, w_codes, w_scales))
+  const bool one_kernel = N > 0 && !linear_run_prefers_two_launches(M, N);
+  if (one_kernel && gemv_narrow_run_supported(M, K, x, w_codes, w_scales))
     return launched(launch_narrow_run(x, xbf, gsa, codes, scales, w_codes, w_scales, ws2, y, ybf,
                                       M, N, K, s));
-  if (N > 0 && gemv_run_supported(M, K, x, w_codes, w_scales))
+  if (one_kernel && gemv_run_supported(M, K, x, w_codes, w_scales))
     return launched(launch_gemv_run(x, xbf, gsa, codes, scales, w_codes, w_scales, ws2, y, ybf, M,
                                     N, K, s));
   // general case: steps 1-2 (one kernel for a small activation), then step 3

@@ -1454,6 +1454,16 @@ hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const fl
       return launch_narrow<true>(a, s);
     return launch_rows<MODE_PLAIN, true>(a, M, fast, grid, waves_for(K), s);
   }
+  if (gemv_ring_preferred(M, N) && !gsa_rows && fast && M * (K / 2) < ((int64_t)1 << 31)) {
+    // the weight ring, all M rows one group (its epilogue takes one gsa)
+    hipError_t err = hipSuccess;
+    int64_t parts = 0;
+    if (launch_ring<false>(a, 1, M, s, &err, &parts)) return err;
+  }
+  // the staged tiles (32-bit weight offsets); no split K at these widths, so no workspace
+  if (gemv_tiled_preferred(M, N) && fast && N * (K / 2) < ((int64_t)1 << 31))
+    return launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M, N, K, s,
+                       gsa_rows);
   if (gemv_narrow_supported(M, K, a_codes, a_scales, w_codes, w_scales))
     return launch_narrow(a, s);
   return launch_rows<MODE_PLAIN>(a, M, fast, grid, waves_for(K), s);

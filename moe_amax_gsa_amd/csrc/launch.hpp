@@ -85,6 +85,30 @@ hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float*
 
 // Weight-streaming linear for few rows (FP4 matrix cores).
 constexpr int64_t GEMV_MAX_M = 16;
+// Up to GEMV_MAX_M rows against many weight rows.  Measured on MI355X with
+// cold weights, K = 7168: up to 4 rows from 8192 weight rows stream faster
+// through the weight ring (one group) than through the few-row kernels
+// (4 x 16384: 24.1 against 47.4 us; 1 x 12288: 13.2 against 16.7 us; at 4096
+// rows the few-row kernels win, 6.2 against 10.6 us), and the tiled GEMM is
+// faster from 8 rows and 12288 weight rows (12 x 12288: 30.2 against 37.9 us;
+// 16 x 16384: 32.8 against 57.4 us; 8 x 8192: 25.3 against 22.0, so not
+// there) and from 5 rows and 16384 weight rows (5 x 16384: 33 against 37.3
+// us; 5 x 12288: 30 against 28.6, so not there).
+constexpr int64_t GEMV_RING_MIN_N = 8192, GEMV_RING_MAX_M = 4;
+inline bool gemv_ring_preferred(int64_t M, int64_t N) {
+  return M <= GEMV_RING_MAX_M && N >= GEMV_RING_MIN_N;
+}
+inline bool gemv_tiled_preferred(int64_t M, int64_t N) {
+  return (M >= 8 && N >= 12288) || (M >= 5 && N >= 16384);
+}
+// The linear run of so few rows: its one-kernel forms (every workgroup
+// quantizes the activation itself) lose to a quantize launch followed by the
+// ring or the tiles above, except for one row against under 12288 weight rows
+// (2 x 12288: 16.9 against 28.7 us; 2 x 8192: 15.4 against 20.5 us;
+// 1 x 8192: 15.7 against 13.4 us).
+inline bool linear_run_prefers_two_launches(int64_t M, int64_t N) {
+  return (gemv_ring_preferred(M, N) && (M > 1 || N >= 12288)) || gemv_tiled_preferred(M, N);
+}
 // The dense router's choice run by the linear's last workgroup: k experts
 // per row of the fp32 logits the linear writes to y (M, N <= 1024), bias
 // (N,) or NULL, outputs idx / score (M, k), and a ticket counter that is

@@ -494,6 +494,71 @@ def test_linear_integer_case_bitexact(C, M, N, K):
         assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
+FEW_ROWS_WIDE = [(1, 8192 + 40), (2, 8192), (3, 12288 + 8), (4, 16384 + 24), (5, 8192 + 40),
+                 (7, 12288 + 8), (8, 12288 + 72), (12, 16384 + 8), (16, 12288), (6, 16384 + 40)]
+
+
+def linear_by_column_chunks(ac, asf, g, wc, wsf, ws2, cols, chunk=2048):
+    """The oracle's linear on the weight rows `cols`, a chunk at a time."""
+    return np.concatenate([oracle.linear(ac, asf, g, wc[cols[i:i + chunk]], wsf[cols[i:i + chunk]],
+                                         ws2) for i in range(0, len(cols), chunk)], axis=1)
+
+
+@pytest.mark.parametrize("M,N", FEW_ROWS_WIDE)
+def test_linear_few_rows_many_columns_integer_exact(C, M, N):
+    """Up to 16 rows against thousands of weight rows (the weight ring for up
+    to 4 rows, the tiled kernels from 8 rows and 12288 weight rows or 5 rows
+    and 16384, the few-row kernels between): the integer case of the linear, exact on any
+    summation order, on every output, ragged N included."""
+    K = 2048
+    say("linear few rows, many columns, integer", M, N, K)
+    rng = np.random.default_rng(M * 7 + N)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asf = np.full((M, K // 16), 0x38, np.uint8)
+    wsf = np.full((N, K // 16), 0x38, np.uint8)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    ref = linear_by_column_chunks(ac, asf, 1.0, wc, wsf, 1.0, np.arange(N))
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(to_dev(ac), to_dev(asf), one, to_dev(wc), to_dev(wsf), one, y)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("M,N", FEW_ROWS_WIDE)
+def test_linear_few_rows_many_columns_parity(C, M, N):
+    """The same shapes at K = 7168 with random codes and scales: sampled
+    columns (both ends and the ragged tail, and a random spread) against the
+    oracle, the bf16 output as the float32 one rounded, and one gsa per row
+    (nvfp4_linear_rows) as the one-gsa output scaled per row."""
+    K = 7168
+    say("linear few rows, many columns", M, N, K)
+    inp = W.make_linear(M, K, N, seed=M + N, x="outliers", sf=(0.125, 8.0), ws2=0.0037)
+    g, codes, scales, y = run_linear(C, inp)
+    oc, os_ = codes.cpu().numpy(), scales.cpu().numpy()
+    rng = np.random.default_rng(N)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 80, N),
+                                     rng.choice(N, 256, replace=False)]))
+    ref = linear_by_column_chunks(oc, os_, f32(g), inp.w_codes, inp.w_scales, inp.ws2, cols)
+    yg = y.cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(yg))
+    assert rel_err(yg[:, cols], ref) <= REL_TOL
+    wc, wsc = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    ws2 = torch.tensor([inp.ws2], dtype=torch.float32, device=DEV)
+    y16 = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    C.nvfp4_linear(codes, scales, g, wc, wsc, ws2, y16)
+    assert torch.equal(y16.cpu(), y.cpu().to(torch.bfloat16))
+    grow = torch.full((M,), float(f32(g)), dtype=torch.float32, device=DEV)
+    grow[::3] *= 2.0
+    yr = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_rows(codes, scales, grow, wc, wsc, ws2, yr)
+    scale = np.ones(M)
+    scale[::3] = 2.0
+    ry = yr.cpu().numpy().astype(np.float64)
+    assert rel_err(ry[:, cols], ref * scale[:, None]) <= REL_TOL
+    err = np.max(np.abs(ry - yg * scale[:, None]), axis=1) / np.max(np.abs(yg * scale[:, None]), axis=1)
+    assert np.max(err) <= 1e-4
+
+
 E4M3_FINITE = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)  # 254 bytes
 
 
@@ -645,6 +710,10 @@ RUN_CASES = [
     (100, 7168, 96, "bf16"),  # amax partials, then the same workspace for a 14-way split K
     (700, 7168, 64, "bf16"),  # more than 512 amax partials: a separate finalize
     (1, 7168, 32768, "bf16"), (2, 2048, 24576, "fp32"),  # long weight streams: the ring
+    (2, 4096, 12288 + 8, "bf16"), (4, 2048, 16384 + 24, "fp32"),  # quantize, then the ring
+    (1, 7168, 12288, "bf16"),
+    (6, 2048, 16384 + 40, "bf16"), (8, 1024, 12288, "fp32"),      # quantize, then the tiles
+    (1, 2048, 8192 + 40, "bf16"),                                 # one kernel
 ]
 
 
