@@ -134,12 +134,12 @@ int nvfp4_quantize_from_buffer(const void *x, int x_dtype, int64_t M, int64_t K,
 
 /* Steps 1 and 2 in one call: gsa, codes (M, K/2) and scales (M, K/16) as
  * nvfp4_amax_gsa followed by nvfp4_quantize_from_buffer write them.  A
- * tensor of at most 65536 elements is done by ONE workgroup in one kernel
+ * tensor of at most 16384 elements is done by ONE workgroup in one kernel
  * (its barrier spans every element, so the maximum is complete before any
  * block is quantized -- the cross-workgroup race of a single-pass kernel
- * that the pages record cannot occur); larger tensors run the two-phase
- * amax, then the quantize.  ws: nvfp4_workspace_bytes(NVFP4_OP_AMAX_GSA,
- * M * K, 0, 0, 0) bytes (0 for the one-kernel case).  x bf16 or fp32,
+ * that the pages record cannot occur); larger tensors run the amax as
+ * nvfp4_amax_gsa does, then the quantize.  ws: nvfp4_workspace_bytes(
+ * NVFP4_OP_AMAX_GSA, M * K, 0, 0, 0) bytes (0 up to 65536 elements).  x bf16 or fp32,
  * 16-byte aligned; codes 8-byte aligned; K % 16 == 0.  M == 0 writes
  * gsa = 1e-8 / 2688. */
 int nvfp4_amax_quantize(const void *x, int x_dtype, int64_t M, int64_t K, float *gsa,
@@ -278,7 +278,7 @@ int nvfp4_router_topk(const uint8_t *a_codes, const uint8_t *a_scales, const flo
  * itself (no reduction across workgroups, so no workgroup waits on
  * another), quantizes it into LDS and streams its weight rows; workgroup 0
  * also writes gsa, codes and scales.  Otherwise steps 1-2 run as
- * nvfp4_amax_quantize does (one kernel up to 65536 elements), then step 3
+ * nvfp4_amax_quantize does (one kernel up to 16384 elements), then step 3
  * (ws must hold nvfp4_workspace_bytes(NVFP4_OP_LINEAR_RUN, M, N, K, 1)
  * bytes: the amax partials, and after them the optional split K of
  * nvfp4_linear).

@@ -261,8 +261,10 @@ def test_quantize_large_tensor_rows(C, M, K, dtype):
 
 
 AMAXQ_CASES = [
-    (1, 256, "bf16"), (1, 7168, "bf16"), (3, 4096, "fp32"), (9, 3072, "bf16"),
-    (16, 4096, "bf16"),                       # one workgroup, 1 .. 8 half-blocks a thread
+    (1, 256, "bf16"), (1, 7168, "bf16"), (2, 8192, "fp32"),  # one workgroup, 1 or 2
+    (1, 16384, "bf16"),                                     # half-blocks a thread
+    (3, 4096, "fp32"), (9, 3072, "bf16"), (1, 16400, "bf16"),  # one-workgroup amax, then
+    (8, 7168, "bf16"), (16, 4096, "bf16"),                   # the quantize
     (17, 4096, "bf16"), (512, 7168, "fp32"),  # two-phase amax, the quantize reducing the
     (512, 7168, "bf16"), (499, 7184, "bf16"),  # partials itself (9 to 448 of them)
     (600, 7168, "bf16"), (1000, 7168, "fp32"),  # 512 partials, each a larger slice
@@ -287,6 +289,14 @@ def test_amax_quantize_bitexact(C, M, K, dtype):
     assert f32(gsa) == g
     oc, os_ = oracle.quantize(x_host(inp.x, dtype), g)
     assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    if M * K <= 65536:  # no workspace up to 65536 elements
+        assert C.nvfp4_workspace_bytes(C.OP_AMAX_GSA, M * K) == 0
+        codes.fill_(0x5A)
+        scales.fill_(0x5A)
+        gsa.fill_(-1.0)
+        C.nvfp4_amax_quantize(xd, gsa, codes, scales)
+        assert f32(gsa) == g
+        assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
 
 
 def test_amax_quantize_empty(C):
