@@ -1464,7 +1464,8 @@ hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   if (gemv_tiled_preferred(M, N) && fast && N * (K / 2) < ((int64_t)1 << 31))
     return launch_gemm(a_codes, a_scales, gsa, w_codes, w_scales, ws2, y, y_bf16, M, N, K, s,
                        gsa_rows);
-  if (gemv_narrow_supported(M, K, a_codes, a_scales, w_codes, w_scales))
+  if (gemv_narrow_preferred(M, N) &&
+      gemv_narrow_supported(M, K, a_codes, a_scales, w_codes, w_scales))
     return launch_narrow(a, s);
   return launch_rows<MODE_PLAIN>(a, M, fast, grid, waves_for(K), s);
 }

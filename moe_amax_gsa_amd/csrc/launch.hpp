@@ -86,18 +86,24 @@ hipError_t launch_amax_finalize(const uint32_t* partials, int64_t nparts, float*
 // Weight-streaming linear for few rows (FP4 matrix cores).
 constexpr int64_t GEMV_MAX_M = 16;
 // Up to GEMV_MAX_M rows against many weight rows.  Measured on MI355X with
-// cold weights, K = 7168: up to 4 rows from 8192 weight rows stream faster
-// through the weight ring (one group) than through the few-row kernels
-// (4 x 16384: 24.1 against 47.4 us; 1 x 12288: 13.2 against 16.7 us; at 4096
-// rows the few-row kernels win, 6.2 against 10.6 us), and the tiled GEMM is
+// cold weights, K = 7168: one or two rows from 8192 weight rows, and three
+// or four from 10240, stream faster through the weight ring (one group) than
+// through the few-row kernels (4 x 16384: 24.1 against 47.4 us; 1 x 12288:
+// 13.2 against 16.7 us; 2 x 8192: 11.2 against 13.2 us; at 4096 rows the
+// few-row kernels win, 6.2 against 10.6 us), and the tiled GEMM is
 // faster from 8 rows and 12288 weight rows (12 x 12288: 30.2 against 37.9 us;
 // 16 x 16384: 32.8 against 57.4 us; 8 x 8192: 25.3 against 22.0, so not
 // there) and from 5 rows and 16384 weight rows (5 x 16384: 33 against 37.3
 // us; 5 x 12288: 30 against 28.6, so not there).
-constexpr int64_t GEMV_RING_MIN_N = 8192, GEMV_RING_MAX_M = 4;
+// Three or four rows take the 16-row kernel from 3072 weight rows up to the
+// ring's range, which for them starts at 10240 (4 x 3072: 9.3 against 13.1
+// us on the 4-row kernel; 4 x 8192: 17.0 against 25.3, and 22.3 on the ring;
+// 4 x 1536: 8.9 against 7.4, so not there; 4 x 10240: 23.6 against 22.8 on
+// the ring).
 inline bool gemv_ring_preferred(int64_t M, int64_t N) {
-  return M <= GEMV_RING_MAX_M && N >= GEMV_RING_MIN_N;
+  return (M <= 2 && N >= 8192) || (M <= 4 && N >= 10240);
 }
+inline bool gemv_narrow_preferred(int64_t M, int64_t N) { return M <= 2 || N < 3072; }
 inline bool gemv_tiled_preferred(int64_t M, int64_t N) {
   return (M >= 8 && N >= 12288) || (M >= 5 && N >= 16384);
 }

@@ -504,7 +504,8 @@ def test_linear_integer_case_bitexact(C, M, N, K):
         assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
-FEW_ROWS_WIDE = [(1, 8192 + 40), (2, 8192), (3, 12288 + 8), (4, 16384 + 24), (5, 8192 + 40),
+FEW_ROWS_WIDE = [(1, 8192 + 40), (2, 8192), (3, 12288 + 8), (4, 16384 + 24), (4, 10240),
+                 (3, 4096 + 40), (4, 8192 + 8), (4, 3072), (5, 8192 + 40),
                  (7, 12288 + 8), (8, 12288 + 72), (12, 16384 + 8), (16, 12288), (6, 16384 + 40)]
 
 
@@ -518,7 +519,8 @@ def linear_by_column_chunks(ac, asf, g, wc, wsf, ws2, cols, chunk=2048):
 def test_linear_few_rows_many_columns_integer_exact(C, M, N):
     """Up to 16 rows against thousands of weight rows (the weight ring for up
     to 4 rows, the tiled kernels from 8 rows and 12288 weight rows or 5 rows
-    and 16384, the few-row kernels between): the integer case of the linear, exact on any
+    and 16384, the 16-row kernel for 3 or 4 rows below the ring's range, the
+    few-row kernels between): the integer case of the linear, exact on any
     summation order, on every output, ragged N included."""
     K = 2048
     say("linear few rows, many columns, integer", M, N, K)
