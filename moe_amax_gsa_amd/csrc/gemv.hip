@@ -68,7 +68,8 @@ struct GemvArgs {
   int gran;
   float limit;
   uint32_t* partials;
-  // plain mode: gsa holds one global scale per activation row (gsa[m])
+  // plain mode, and the ring over one group of all rows on given codes:
+  // gsa holds one global scale per activation row (gsa[m])
   int gsa_rows;
   // grouped ring: G groups in all; when the grid has fewer rows of
   // workgroups than groups, workgroup row y serves the y-th group that has
@@ -853,10 +854,12 @@ __global__ __launch_bounds__(W * 64) void gemv_ring_kernel(const GemvArgs args) 
             hmax = fmaxf(hmax, fabsf(hv));
           }
         } else if (ok) {
+          // one gsa per row (one group of all rows, codes given)
+          const float sc = args.gsa_rows ? args.gsa[r] * args.ws2[g] : gscale;
           if (args.y_bf16)
-            ((uint16_t*)args.y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v * gscale);
+            ((uint16_t*)args.y)[(int64_t)r * N + n] = (uint16_t)f32_to_bf16_rne(v * sc);
           else
-            ((float*)args.y)[(int64_t)r * N + n] = v * gscale;
+            ((float*)args.y)[(int64_t)r * N + n] = v * sc;
         }
       }
     }
@@ -1454,8 +1457,8 @@ hipError_t launch_gemv(const uint8_t* a_codes, const uint8_t* a_scales, const fl
       return launch_narrow<true>(a, s);
     return launch_rows<MODE_PLAIN, true>(a, M, fast, grid, waves_for(K), s);
   }
-  if (gemv_ring_preferred(M, N) && !gsa_rows && fast && M * (K / 2) < ((int64_t)1 << 31)) {
-    // the weight ring, all M rows one group (its epilogue takes one gsa)
+  if (gemv_ring_preferred(M, N) && fast && M * (K / 2) < ((int64_t)1 << 31)) {
+    // the weight ring, all M rows one group
     hipError_t err = hipSuccess;
     int64_t parts = 0;
     if (launch_ring<false>(a, 1, M, s, &err, &parts)) return err;

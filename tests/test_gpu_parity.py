@@ -569,6 +569,9 @@ def test_linear_few_rows_many_columns_parity(C, M, N):
     assert rel_err(ry[:, cols], ref * scale[:, None]) <= REL_TOL
     err = np.max(np.abs(ry - yg * scale[:, None]), axis=1) / np.max(np.abs(yg * scale[:, None]), axis=1)
     assert np.max(err) <= 1e-4
+    yr16 = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    C.nvfp4_linear_rows(codes, scales, grow, wc, wsc, ws2, yr16)
+    assert torch.equal(yr16.cpu(), yr.cpu().to(torch.bfloat16))
 
 
 E4M3_FINITE = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)  # 254 bytes
