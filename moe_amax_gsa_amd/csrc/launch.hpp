@@ -90,11 +90,14 @@ constexpr int64_t GEMV_MAX_M = 16;
 // or four from 10240, stream faster through the weight ring (one group) than
 // through the few-row kernels (4 x 16384: 24.1 against 47.4 us; 1 x 12288:
 // 13.2 against 16.7 us; 2 x 8192: 11.2 against 13.2 us; at 4096 rows the
-// few-row kernels win, 6.2 against 10.6 us), and the tiled GEMM is
-// faster from 8 rows and 12288 weight rows (12 x 12288: 30.2 against 37.9 us;
-// 16 x 16384: 32.8 against 57.4 us; 8 x 8192: 25.3 against 22.0, so not
-// there) and from 5 rows and 16384 weight rows (5 x 16384: 33 against 37.3
-// us; 5 x 12288: 30 against 28.6, so not there).
+// few-row kernels win, 6.2 against 10.6 us).  The tiled GEMM (unsplit: its
+// time hardly moves from 5 to 16 rows) is faster from 8 rows and 10240
+// weight rows (12 x 10240: 29.4 against 36.7 us; 16 x 16384: 32.8 against
+// 57.4 us; 8 x 8192: 23.4 against 21.6 on the rows kernel, so not there),
+// from 15 rows and 6144 weight rows (16 x 6144: 27.4 against 29.2 us; 12 x
+// 8192: 28.7 against 25.8, so not there) and from 5 rows and 16384 weight
+// rows (5 x 16384: 32.4 against 37.3 us; 5 x 12288: 30 against 28.6, so not
+// there).
 // Three or four rows take the 16-row kernel from 3072 weight rows up to the
 // ring's range, which for them starts at 10240 (4 x 3072: 9.3 against 13.1
 // us on the 4-row kernel; 4 x 8192: 17.0 against 25.3, and 22.3 on the ring;
@@ -105,7 +108,7 @@ inline bool gemv_ring_preferred(int64_t M, int64_t N) {
 }
 inline bool gemv_narrow_preferred(int64_t M, int64_t N) { return M <= 2 || N < 3072; }
 inline bool gemv_tiled_preferred(int64_t M, int64_t N) {
-  return (M >= 8 && N >= 12288) || (M >= 5 && N >= 16384);
+  return (M >= 15 && N >= 6144) || (M >= 8 && N >= 10240) || (M >= 5 && N >= 16384);
 }
 // The linear run of so few rows: its one-kernel forms (every workgroup
 // quantizes the activation itself) lose to a quantize launch followed by the

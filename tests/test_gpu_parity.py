@@ -506,7 +506,8 @@ def test_linear_integer_case_bitexact(C, M, N, K):
 
 FEW_ROWS_WIDE = [(1, 8192 + 40), (2, 8192), (3, 12288 + 8), (4, 16384 + 24), (4, 10240),
                  (3, 4096 + 40), (4, 8192 + 8), (4, 3072), (5, 8192 + 40),
-                 (7, 12288 + 8), (8, 12288 + 72), (12, 16384 + 8), (16, 12288), (6, 16384 + 40)]
+                 (7, 12288 + 8), (8, 12288 + 72), (12, 16384 + 8), (16, 12288), (6, 16384 + 40),
+                 (16, 6144 + 8), (14, 6144), (8, 10240), (12, 10240 + 40), (7, 10240)]
 
 
 def linear_by_column_chunks(ac, asf, g, wc, wsf, ws2, cols, chunk=2048):
@@ -518,8 +519,8 @@ def linear_by_column_chunks(ac, asf, g, wc, wsf, ws2, cols, chunk=2048):
 @pytest.mark.parametrize("M,N", FEW_ROWS_WIDE)
 def test_linear_few_rows_many_columns_integer_exact(C, M, N):
     """Up to 16 rows against thousands of weight rows (the weight ring for up
-    to 4 rows, the tiled kernels from 8 rows and 12288 weight rows or 5 rows
-    and 16384, the 16-row kernel for 3 or 4 rows below the ring's range, the
+    to 4 rows, the tiled kernels from 8 rows and 10240 weight rows, 15 rows
+    and 6144 or 5 rows and 16384, the 16-row kernel for 3 or 4 rows below the ring's range, the
     few-row kernels between): the integer case of the linear, exact on any
     summation order, on every output, ragged N included."""
     K = 2048
@@ -728,6 +729,7 @@ RUN_CASES = [
     (2, 4096, 12288 + 8, "bf16"), (4, 2048, 16384 + 24, "fp32"),  # quantize, then the ring
     (1, 7168, 12288, "bf16"),
     (6, 2048, 16384 + 40, "bf16"), (8, 1024, 12288, "fp32"),      # quantize, then the tiles
+    (16, 1024, 6144 + 8, "bf16"),
     (1, 2048, 8192 + 40, "bf16"),                                 # one kernel
 ]
 
