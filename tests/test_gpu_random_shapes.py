@@ -109,6 +109,53 @@ def test_random_linear_run(C, case):
     assert rel_err(y.cpu().numpy().astype(np.float64), ref) <= REL_TOL, (M, N, K)
 
 
+@pytest.mark.parametrize("case", range(40))
+def test_random_few_rows_many_columns(C, case):
+    """Up to 16 rows against 2000 to 20000 weight rows, K any multiple of 16
+    (the weight ring, the tiles and the few-row kernels meet here):
+    nvfp4_linear_run's gsa, codes and scales bit-exact with the oracle, y of
+    linear_run, linear and linear_rows (gsa per row) within 1e-3 of the
+    oracle on sampled columns (both ends and a random spread), and the bf16
+    output the float32 one rounded."""
+    rng = np.random.default_rng(6000 + case)
+    M = int(rng.integers(1, 17))
+    N = int(rng.integers(2000, 20001))
+    K = int(rng.choice([256, 1024, 2048, 7168])) if rng.integers(0, 2) else random_k(rng, 256)
+    say("random few rows, many columns", case, M, N, K)
+    inp = W.make_linear(M, K, N, seed=7000 + case, x="outliers", sf=(0.125, 8.0), ws2=0.004)
+    x = W.bf16_to_torch(inp.x, DEV)
+    gsa = torch.zeros(1, dtype=torch.float32, device=DEV)
+    codes = torch.full((M, K // 2), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((M, K // 16), 0x5A, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(16, C.nvfp4_workspace_bytes(C.OP_LINEAR_RUN, M, N, K)),
+                     dtype=torch.uint8, device=DEV)
+    wc, wsf = to_dev(inp.w_codes), to_dev(inp.w_scales)
+    ws2 = to_dev(np.array([inp.ws2], np.float32))
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_run(x, gsa, codes, scales, wc, wsf, ws2, y, ws)
+    g = np.float32(gsa.cpu().numpy()[0])
+    assert g == oracle.amax_gsa(inp.x)
+    oc, os_ = oracle.quantize(inp.x, g)
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), os_)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 40, N),
+                                     rng.choice(N, 96, replace=False)]))
+    ref = oracle.linear(oc, os_, g, inp.w_codes[cols], inp.w_scales[cols], inp.ws2)
+    assert rel_err(y.cpu().numpy().astype(np.float64)[:, cols], ref) <= REL_TOL, (M, N, K)
+    y2 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear(codes, scales, gsa, wc, wsf, ws2, y2)
+    assert rel_err(y2.cpu().numpy().astype(np.float64)[:, cols], ref) <= REL_TOL, (M, N, K)
+    y16 = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    C.nvfp4_linear(codes, scales, gsa, wc, wsf, ws2, y16)
+    assert torch.equal(y16.cpu(), y2.cpu().to(torch.bfloat16))
+    grow = torch.full((M,), float(g), dtype=torch.float32, device=DEV)
+    grow[::2] *= 4.0
+    y3 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    C.nvfp4_linear_rows(codes, scales, grow, wc, wsf, ws2, y3)
+    sc = np.ones(M)
+    sc[::2] = 4.0
+    assert rel_err(y3.cpu().numpy().astype(np.float64)[:, cols], ref * sc[:, None]) <= REL_TOL
+
+
 def random_groups(rng):
     G = int(rng.integers(1, 13))
     big = rng.integers(0, 3) == 0  # a third of the cases: groups for the tiles
