@@ -192,9 +192,13 @@ int nvfp4_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, floa
  * A is codes (M, K/2) + scales (M, K/16) from step 2; W is codes (N, K/2) +
  * scales (N, K/16); gsa and ws2 are device float32 scalars.  Code buffers
  * 8-byte aligned.  M <= 16 runs a weight-streaming kernel on FP4 matrix
- * cores; larger M runs a tiled kernel that dequantizes both operands
- * exactly to f16 (every E2M1 x E4M3 product fits) and accumulates on f16
- * matrix cores in FP32.  M == 0 or N == 0 is a no-op.
+ * cores (with 16-byte aligned operands and K % 256 == 0, the weight ring of
+ * nvfp4_grouped_linear for 1-2 rows from N = 8192 and 3-4 rows from 10240,
+ * and the tiled kernel, unsplit, for 8-16 rows from N = 10240, 15-16 rows
+ * from 6144 and 5-16 rows from 16384, where those measured faster); larger
+ * M runs a tiled kernel that dequantizes both operands exactly to f16
+ * (every E2M1 x E4M3 product fits) and accumulates on f16 matrix cores in
+ * FP32.  M == 0 or N == 0 is a no-op.
  * ws is optional.  With few output tiles (a 128 x 64 tile each; at most
  * half as many tiles as the device has compute units) and K a multiple of
  * 256 the tiled kernel can split K across workgroups: each split writes its
@@ -269,7 +273,9 @@ int nvfp4_router_topk(const uint8_t *a_codes, const uint8_t *a_scales, const flo
  * When x, w_codes and w_scales are 16-byte aligned it is ONE kernel for
  *   - up to 2 rows with N >= 24576, K % 256 == 0 and M*K <= 16384 (the
  *     weight-streaming ring of nvfp4_grouped_linear_run, 128 weight rows per
- *     workgroup: a long weight stream such as the lm_head's), or
+ *     workgroup: a long weight stream such as the lm_head's), or, where
+ *     nvfp4_linear would not take its ring or tiles for the shape (one row
+ *     below N = 12288 excepted; the others run steps 1-2, then that path),
  *   - up to 4 rows with K % 512 == 0, K <= 16384 and M*K <= 16384 (8 weight
  *     rows per workgroup), or
  *   - up to 16 rows with K % 256 == 0, M*K/16 <= 1024 and
